@@ -1,0 +1,59 @@
+"""Build libflashkm.so (HIP kernels + C-ABI) for gfx950 with hipcc, in-tree.
+
+Usage: python -m exact_lloyd_means_02_amd.build [--force]
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libflashkm.so")
+SOURCES = ["api.hip", "k_assign.hip", "k_sort.hip", "k_update.hip", "k_misc.hip", "plan.cpp"]
+HEADERS = ["common.h", "plan.h", os.path.join("..", "..", "include", "flashkm.h")]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    # packed fp32 VALU ops stay off (only plain fp32 instructions in the device code)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    lang = ["-x", "hip"] if src.endswith(".cpp") else []
+    cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
+    return obj
+
+
+def build(force: bool = True, verbose: bool = False) -> str:
+    """Compile every source for gfx950 and link libflashkm.so (always recompiles when force)."""
+    os.makedirs(BUILD, exist_ok=True)
+    if not force and os.path.exists(LIB):
+        newest = max(os.path.getmtime(os.path.join(CSRC, f)) for f in SOURCES + HEADERS)
+        if os.path.getmtime(LIB) >= newest:
+            return LIB
+    jobs = max(1, min(len(SOURCES), os.cpu_count() or 1))
+    with ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
+    os.replace(tmp, LIB)
+    if verbose:
+        print("built", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(force="--force" in sys.argv or True, verbose=True)

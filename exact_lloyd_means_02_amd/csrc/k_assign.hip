@@ -1,0 +1,488 @@
+// FlashAssign on gfx950: centroid preparation, small-D and split-D assign kernels.
+//
+// Method (paper summary, "Method"; paper digest, "核心方法" and "方法步骤详情" step (1)):
+// points are tiled, centroids are scanned tile by tile, each tile's block of scores is
+// computed on chip and folded into a running (min, index) per point; the N x K matrix of
+// distances is never written.  The decomposition ||x-c||^2 = ||x||^2 + ||c||^2 - 2 x.c
+// (paper digest, "核心方法") means the arg-min only needs ||c||^2 - 2 x.c.
+//
+// gfx950 mapping:
+//   * v_mfma_f32_32x32x16_{bf16,f16} (fp32: v_mfma_f32_32x32x2_f32).  Operand A = 32
+//     centroids, operand B = 32 points, so each lane's 16 accumulators hold 16 centroid
+//     scores of ONE point: the arg-min runs inside the lane, with one cross-lane merge per
+//     point at the very end.
+//   * Scores are halved: the accumulator starts at ||c~||^2/2 and A holds -c~ (negation is
+//     exact), so acc = ||c~||^2/2 - x.c~ = (||c~||^2 - 2 x.c~)/2 with no add per score and
+//     no risk of overflowing -2c~ in fp16.  Halving commutes with rounding, so comparisons
+//     are those of the full scores.
+//   * Per 32-centroid tile and lane: one min over the 16 scores, one compare with the
+//     running min, and (selects) a copy of the tile's 16 scores when it improves.  The slot
+//     inside the winning tile is found once at the end by equality with the running min.
+//     Result: the exact arg-min of the fp32 scores with ties to the lowest index (strict
+//     '<' over tiles in increasing order, lowest slot, lexicographic lane merge).
+//   * Centroid tiles are pre-laid-out in "MFMA-fragment" order (see prep kernel) so a stage
+//     is one contiguous copy and each A fragment is one conflict-free 16-byte LDS read per
+//     lane; stages of 32 KiB ping-pong in LDS.
+#include "common.h"
+#include "plan.h"
+
+namespace fkm {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------------------------------
+// Centroid preparation.
+//   cprep (per problem, tile t of 32 centroids, group q < DP/(2*VW), lane l = i + 32h):
+//     16 bytes = -c~[32t+i][h*DP/2 + q*VW + e], e < VW  (VW = 8 for 2-byte types, 4 for fp32)
+//   cnh[b][k] = ||c~_k||^2 / 2 in fp32 (+inf for the padding rows k >= K)
+// c~ = dtype(c) with round-to-nearest-even.  Zero padding for d >= D and k >= K.
+// ------------------------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(256) void prep_centroids_kernel(const float *__restrict__ C, u32x4 *__restrict__ cprep,
+                                                             float *__restrict__ cnh, int K, int D, int DP,
+                                                             int KT) {
+    constexpr int S = DT == DT_F32 ? 4 : 2;
+    constexpr int VW = 16 / S;
+    const int QG = DP / (2 * VW);
+    const int bt = blockIdx.x;  // b * KT + t
+    const int b = bt / KT, t = bt - b * KT;
+    const int i = threadIdx.x >> 3, part = threadIdx.x & 7;
+    const int k = t * 32 + i;
+    const bool valid_k = k < K;
+    const float *row = C + ((size_t)b * K + (valid_k ? k : 0)) * D;
+    float ss = 0.f;
+    const int groups = DP / VW;
+    for (int g = part; g < groups; g += 8) {
+        const int d0 = g * VW;
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < VW; ++e) {
+            const int d = d0 + e;
+            float v = (valid_k && d < D) ? row[d] : 0.f;
+            uint32_t bits;
+            float r;
+            if constexpr (DT == DT_F32) {
+                r = v;
+                bits = __float_as_uint(-r);
+            } else if constexpr (DT == DT_F16) {
+                const uint32_t hb = f32_to_f16_bits(v);
+                r = f16_bits_to_f32(hb);
+                bits = hb ^ 0x8000u;  // exact negation
+            } else {
+                const uint32_t bb = f32_to_bf16_bits(v);
+                r = bf16_bits_to_f32(bb);
+                bits = bb ^ 0x8000u;
+            }
+            ss += r * r;
+            if constexpr (S == 4) {
+                w[e] = bits;
+            } else {
+                w[e >> 1] |= (bits & 0xFFFFu) << ((e & 1) * 16);
+            }
+        }
+        const int h = d0 / (DP / 2);
+        const int q = (d0 - h * (DP / 2)) / VW;
+        const size_t off = (((size_t)b * KT + t) * QG + q) * 64 + i + 32 * h;
+        cprep[off] = u32x4{w[0], w[1], w[2], w[3]};
+    }
+    ss += __shfl_xor(ss, 1);
+    ss += __shfl_xor(ss, 2);
+    ss += __shfl_xor(ss, 4);
+    if (part == 0) cnh[(size_t)b * KT * 32 + k] = valid_k ? 0.5f * ss : __builtin_inff();
+}
+
+// ------------------------------------------------------------------------------------------
+// shared pieces of the assign kernels
+// ------------------------------------------------------------------------------------------
+// One 16-byte group of a point row: elements d0 .. d0+VW-1 (zeros past D or past N).
+template <int DT>
+__device__ inline u32x4 load_x_group(const void *x, size_t row_elem0, int d0, int D, bool valid_pt) {
+    constexpr int S = DT == DT_F32 ? 4 : 2;
+    constexpr int VW = 16 / S;
+    if (!valid_pt || d0 >= D) return u32x4{0u, 0u, 0u, 0u};
+    if ((D % VW) == 0) {
+        return *(const u32x4 *)((const char *)x + (row_elem0 + d0) * S);
+    }
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < VW; ++e) {
+        const int d = d0 + e;
+        if (d < D) {
+            if constexpr (S == 4) {
+                w[e] = ((const uint32_t *)x)[row_elem0 + d];
+            } else {
+                w[e >> 1] |= (uint32_t)((const uint16_t *)x)[row_elem0 + d] << ((e & 1) * 16);
+            }
+        }
+    }
+    return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// acc += A(32 centroids) x B(32 points) over one 16-byte group per lane.
+template <int DT>
+__device__ inline f32x16 mfma_group(const u32x4 &a, const u32x4 &bx, f32x16 acc) {
+    if constexpr (DT == DT_BF16) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, bx),
+                                                       acc, 0, 0, 0);
+    } else if constexpr (DT == DT_F16) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, bx),
+                                                      acc, 0, 0, 0);
+    } else {
+        const f32x4 af = __builtin_bit_cast(f32x4, a), bf = __builtin_bit_cast(f32x4, bx);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(af[0], bf[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(af[1], bf[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(af[2], bf[2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(af[3], bf[3], acc, 0, 0, 0);
+        return acc;
+    }
+}
+
+// Running arg-min state of one lane for one 32-point block.
+struct ArgminState {
+    float run_min;
+    int run_tile;
+    f32x16 best;
+};
+
+__device__ inline void argmin_init(ArgminState &s) {
+    s.run_min = __builtin_inff();
+    s.run_tile = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s.best[r] = __builtin_inff();
+}
+
+// Fold one tile's 16 scores (this lane's rows of the tile) into the running state.
+__device__ inline void argmin_fold(ArgminState &s, const f32x16 &acc, int tile) {
+    float m01 = fminf(acc[0], acc[1]), m23 = fminf(acc[2], acc[3]);
+    float m45 = fminf(acc[4], acc[5]), m67 = fminf(acc[6], acc[7]);
+    float m89 = fminf(acc[8], acc[9]), mab = fminf(acc[10], acc[11]);
+    float mcd = fminf(acc[12], acc[13]), mef = fminf(acc[14], acc[15]);
+    float m = fminf(fminf(fminf(m01, m23), fminf(m45, m67)), fminf(fminf(m89, mab), fminf(mcd, mef)));
+    const bool imp = m < s.run_min;
+    s.run_min = imp ? m : s.run_min;
+    s.run_tile = imp ? tile : s.run_tile;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s.best[r] = imp ? acc[r] : s.best[r];
+}
+
+// Resolve the winning centroid of this lane, merge with the partner lane (lane ^ 32, same
+// point, the other 16 rows of every tile) and write.  Accumulator r of lane (j, h) holds row
+// 8*(r/4) + 4*h + (r%4) of the 32-centroid tile (MFMA 32x32 output layout).
+__device__ inline void argmin_finish(const ArgminState &s, int h, bool write, int64_t out_i, int32_t *out_a,
+                                     float *out_d, const float *xnorm) {
+    int slot = 15;
+#pragma unroll
+    for (int r = 15; r >= 0; --r) slot = (s.best[r] == s.run_min) ? r : slot;
+    int k = s.run_tile * 32 + 8 * (slot >> 2) + 4 * h + (slot & 3);
+    float sc = s.run_min;
+    const float osc = __shfl_xor(sc, 32);
+    const int ok = __shfl_xor(k, 32);
+    if (osc < sc || (osc == sc && ok < k)) {
+        sc = osc;
+        k = ok;
+    }
+    if (write) {
+        out_a[out_i] = k;
+        if (out_d) out_d[out_i] = xnorm[out_i] + 2.0f * sc;
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Small-D assign: each wave keeps PB blocks of 32 points in VGPRs (B operand) for the whole
+// scan; centroid tiles stream through LDS in stages of TPS tiles, double buffered.
+// grid = B * ceil(N / block_n) workgroups of 256 threads.
+// ------------------------------------------------------------------------------------------
+template <int DT, int DP>
+__global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restrict__ x,
+                                                             const u32x4 *__restrict__ cprep,
+                                                             const float *__restrict__ cnh,
+                                                             const float *__restrict__ xnorm,
+                                                             int32_t *__restrict__ out_a, float *__restrict__ out_d,
+                                                             int N, int D, int KT, int wgs_per_b) {
+    constexpr int S = DT == DT_F32 ? 4 : 2;
+    constexpr int VW = 16 / S;
+    constexpr int QG = DP / (2 * VW);
+    constexpr int PB = small_d_pb(DT, DP);
+    constexpr int TPS = small_d_tps(DT, DP);
+    constexpr int TILE_U4 = QG * 64;
+    constexpr int STAGE_U4 = TPS * TILE_U4;
+    constexpr int PF = STAGE_U4 / 256;
+    static_assert(STAGE_U4 % 256 == 0, "stage must split evenly over 256 threads");
+    static_assert(TPS * 8 <= 256, "norm copy uses one float4 per thread");
+
+    __shared__ u32x4 s_c[2][STAGE_U4];
+    __shared__ float s_n[2][TPS * 32];
+
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    const int b = wg / wgs_per_b;
+    const int tn = wg - b * wgs_per_b;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int j = lane & 31, h = lane >> 5;
+    const int pbase = tn * (ASSIGN_WAVES * PB * 32) + w * PB * 32;
+
+    u32x4 xr[PB][QG];
+#pragma unroll
+    for (int p = 0; p < PB; ++p) {
+        const int pt = pbase + p * 32 + j;
+        const bool vp = pt < N;
+        const size_t row0 = ((size_t)b * N + (vp ? pt : 0)) * D;
+#pragma unroll
+        for (int q = 0; q < QG; ++q) xr[p][q] = load_x_group<DT>(x, row0, h * (DP / 2) + q * VW, D, vp);
+    }
+
+    const u32x4 *cb = cprep + (size_t)b * KT * TILE_U4;
+    const float *nb = cnh + (size_t)b * KT * 32;
+    const int nst = (KT + TPS - 1) / TPS;
+
+    u32x4 pf[PF];
+    f32x4 pn;
+    auto gload = [&](int st) {
+        const int t0 = st * TPS;
+        const int nt = min(TPS, KT - t0);
+        const u32x4 *src = cb + (size_t)t0 * TILE_U4;
+#pragma unroll
+        for (int r = 0; r < PF; ++r) {
+            const int i = tid + r * 256;
+            pf[r] = i < nt * TILE_U4 ? src[i] : u32x4{0u, 0u, 0u, 0u};
+        }
+        pn = tid < nt * 8 ? ((const f32x4 *)(nb + (size_t)t0 * 32))[tid] : f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    auto swrite = [&](int buf) {
+#pragma unroll
+        for (int r = 0; r < PF; ++r) s_c[buf][tid + r * 256] = pf[r];
+        if (tid < TPS * 8) ((f32x4 *)s_n[buf])[tid] = pn;
+    };
+
+    gload(0);
+    swrite(0);
+    __syncthreads();
+
+    ArgminState st[PB];
+#pragma unroll
+    for (int p = 0; p < PB; ++p) argmin_init(st[p]);
+
+    for (int s = 0; s < nst; ++s) {
+        const int buf = s & 1;
+        if (s + 1 < nst) gload(s + 1);
+        const int nt = min(TPS, KT - s * TPS);
+        for (int tt = 0; tt < nt; ++tt) {
+            const int tile = s * TPS + tt;
+            f32x16 acc[PB];
+            {
+                const float *nrm = &s_n[buf][tt * 32 + 4 * h];
+                const f32x4 c0 = *(const f32x4 *)(nrm + 0), c1 = *(const f32x4 *)(nrm + 8);
+                const f32x4 c2 = *(const f32x4 *)(nrm + 16), c3 = *(const f32x4 *)(nrm + 24);
+                const f32x16 cn = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3],
+                                   c2[0], c2[1], c2[2], c2[3], c3[0], c3[1], c3[2], c3[3]};
+#pragma unroll
+                for (int p = 0; p < PB; ++p) acc[p] = cn;
+            }
+            const u32x4 *at = &s_c[buf][tt * TILE_U4 + lane];
+#pragma unroll
+            for (int q = 0; q < QG; ++q) {
+                const u32x4 a = at[q * 64];
+#pragma unroll
+                for (int p = 0; p < PB; ++p) acc[p] = mfma_group<DT>(a, xr[p][q], acc[p]);
+            }
+#pragma unroll
+            for (int p = 0; p < PB; ++p) argmin_fold(st[p], acc[p], tile);
+        }
+        if (s + 1 < nst) swrite(buf ^ 1);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int p = 0; p < PB; ++p) {
+        const int pt = pbase + p * 32 + j;
+        argmin_finish(st[p], h, h == 0 && pt < N, (int64_t)b * N + pt, out_a, out_d, xnorm);
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Split-D assign (README, "Large-D and dtype support": outer K loop, inner D loop, the
+// (points x centroids) accumulator held in registers across the D loop).  Workgroup = 128
+// points (4 waves x 32); register group = SPLITD_KB tiles (128 centroids); D streamed in
+// chunks of BD elements: x chunk and centroid chunk staged together in LDS, double buffered.
+// ------------------------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(256) void assign_split_d_kernel(const void *__restrict__ x,
+                                                             const u32x4 *__restrict__ cprep,
+                                                             const float *__restrict__ cnh,
+                                                             const float *__restrict__ xnorm,
+                                                             int32_t *__restrict__ out_a, float *__restrict__ out_d,
+                                                             int N, int D, int DP, int KT, int wgs_per_b) {
+    constexpr int S = DT == DT_F32 ? 4 : 2;
+    constexpr int VW = 16 / S;
+    constexpr int BD = splitd_bd(DT);
+    constexpr int QC = BD / (2 * VW);         // 16-byte groups per lane per chunk (= 4)
+    constexpr int KB = SPLITD_KB;
+    constexpr int XU4 = ASSIGN_WAVES * QC * 64;  // x chunk words
+    constexpr int CU4 = KB * QC * 64;            // centroid chunk words
+    constexpr int PFX = XU4 / 256, PFC = CU4 / 256;
+    static_assert(XU4 % 256 == 0 && CU4 % 256 == 0, "chunks split evenly");
+
+    __shared__ u32x4 s_x[2][XU4];
+    __shared__ u32x4 s_c[2][CU4];
+
+    const int QG = DP / (2 * VW);
+    const int NC = DP / BD;
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    const int b = wg / wgs_per_b;
+    const int tn = wg - b * wgs_per_b;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int h = lane >> 5;
+    const int pbase = tn * (ASSIGN_WAVES * 32);
+    const int ngroups = (KT + KB - 1) / KB;
+    const int nstage = ngroups * NC;
+    const u32x4 *cb = cprep + (size_t)b * KT * QG * 64;
+    const float *nb = cnh + (size_t)b * KT * 32;
+
+    u32x4 pfx[PFX], pfc[PFC];
+    auto gload = [&](int s) {
+        const int g = s / NC, dc = s - g * NC;
+#pragma unroll
+        for (int r = 0; r < PFX; ++r) {
+            const int i = tid + r * 256;
+            const int pb = i / (QC * 64), rem = i - pb * (QC * 64);
+            const int q = rem >> 6, ln = rem & 63;
+            const int pt = pbase + pb * 32 + (ln & 31);
+            const bool vp = pt < N;
+            const int d0 = (ln >> 5) * (DP / 2) + dc * (BD / 2) + q * VW;
+            pfx[r] = load_x_group<DT>(x, ((size_t)b * N + (vp ? pt : 0)) * D, d0, D, vp);
+        }
+#pragma unroll
+        for (int r = 0; r < PFC; ++r) {
+            const int i = tid + r * 256;
+            const int t = i / (QC * 64), rem = i - t * (QC * 64);
+            const int q = rem >> 6, ln = rem & 63;
+            const int tile = g * KB + t;
+            pfc[r] = tile < KT ? cb[((size_t)tile * QG + dc * QC + q) * 64 + ln] : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto swrite = [&](int buf) {
+#pragma unroll
+        for (int r = 0; r < PFX; ++r) s_x[buf][tid + r * 256] = pfx[r];
+#pragma unroll
+        for (int r = 0; r < PFC; ++r) s_c[buf][tid + r * 256] = pfc[r];
+    };
+
+    ArgminState st;
+    argmin_init(st);
+    f32x16 acc[KB];
+
+    gload(0);
+    swrite(0);
+    __syncthreads();
+    for (int s = 0; s < nstage; ++s) {
+        const int buf = s & 1;
+        const int g = s / NC, dc = s - g * NC;
+        if (s + 1 < nstage) gload(s + 1);
+        if (dc == 0) {
+#pragma unroll
+            for (int t = 0; t < KB; ++t) {
+                const int tile = g * KB + t;
+                const int tl = tile < KT ? tile : 0;
+                const float *nrm = nb + (size_t)tl * 32 + 4 * h;
+                const f32x4 c0 = *(const f32x4 *)(nrm + 0), c1 = *(const f32x4 *)(nrm + 8);
+                const f32x4 c2 = *(const f32x4 *)(nrm + 16), c3 = *(const f32x4 *)(nrm + 24);
+                acc[t] = f32x16{c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3],
+                                c2[0], c2[1], c2[2], c2[3], c3[0], c3[1], c3[2], c3[3]};
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < QC; ++q) {
+            const u32x4 xb = s_x[buf][(w * QC + q) * 64 + lane];
+#pragma unroll
+            for (int t = 0; t < KB; ++t) acc[t] = mfma_group<DT>(s_c[buf][(t * QC + q) * 64 + lane], xb, acc[t]);
+        }
+        if (dc == NC - 1) {
+#pragma unroll
+            for (int t = 0; t < KB; ++t) {
+                const int tile = g * KB + t;
+                if (tile < KT) argmin_fold(st, acc[t], tile);
+            }
+        }
+        if (s + 1 < nstage) swrite(buf ^ 1);
+        __syncthreads();
+    }
+    const int pt = pbase + w * 32 + (lane & 31);
+    argmin_finish(st, h, h == 0 && pt < N, (int64_t)b * N + pt, out_a, out_d, xnorm);
+}
+
+// ------------------------------------------------------------------------------------------
+// host launchers
+// ------------------------------------------------------------------------------------------
+hipError_t launch_prep_centroids(int dt, const float *C, void *cprep, float *cnh, int B, int K, int D, int DP,
+                                 hipStream_t stream) {
+    const int KT = (K + 31) / 32;
+    dim3 grid(B * KT), block(256);
+    if (dt == DT_F32)
+        prep_centroids_kernel<DT_F32><<<grid, block, 0, stream>>>(C, (u32x4 *)cprep, cnh, K, D, DP, KT);
+    else if (dt == DT_F16)
+        prep_centroids_kernel<DT_F16><<<grid, block, 0, stream>>>(C, (u32x4 *)cprep, cnh, K, D, DP, KT);
+    else
+        prep_centroids_kernel<DT_BF16><<<grid, block, 0, stream>>>(C, (u32x4 *)cprep, cnh, K, D, DP, KT);
+    return hipGetLastError();
+}
+
+template <int DT, int DP>
+static hipError_t launch_small(const void *x, const void *cprep, const float *cnh, const float *xn, int32_t *a,
+                               float *md, int B, int N, int D, int K, hipStream_t stream) {
+    constexpr int PB = small_d_pb(DT, DP);
+    const int KT = (K + 31) / 32;
+    const int bn = ASSIGN_WAVES * PB * 32;
+    const int wpb = (N + bn - 1) / bn;
+    assign_small_d_kernel<DT, DP><<<dim3(B * wpb), dim3(256), 0, stream>>>(x, (const u32x4 *)cprep, cnh, xn, a, md,
+                                                                           N, D, KT, wpb);
+    return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t launch_small_dt(int DP, const void *x, const void *cprep, const float *cnh, const float *xn,
+                                  int32_t *a, float *md, int B, int N, int D, int K, hipStream_t s) {
+    if constexpr (DT == DT_F32) {
+        switch (DP) {
+            case 8: return launch_small<DT, 8>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
+            case 16: return launch_small<DT, 16>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
+            case 32: return launch_small<DT, 32>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
+            case 64: return launch_small<DT, 64>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
+            case 128: return launch_small<DT, 128>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
+            case 256: return launch_small<DT, 256>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
+        }
+    } else {
+        switch (DP) {
+            case 16: return launch_small<DT, 16>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
+            case 32: return launch_small<DT, 32>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
+            case 64: return launch_small<DT, 64>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
+            case 128: return launch_small<DT, 128>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
+            case 256: return launch_small<DT, 256>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
+            case 512: return launch_small<DT, 512>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_assign(int dt, const AssignCfg &cfg, const void *x, const void *cprep, const float *cnh,
+                         const float *xn, int32_t *a, float *md, int B, int N, int D, int K, hipStream_t s) {
+    if (cfg.path == 0) {
+        if (dt == DT_F32) return launch_small_dt<DT_F32>(cfg.d_pad, x, cprep, cnh, xn, a, md, B, N, D, K, s);
+        if (dt == DT_F16) return launch_small_dt<DT_F16>(cfg.d_pad, x, cprep, cnh, xn, a, md, B, N, D, K, s);
+        return launch_small_dt<DT_BF16>(cfg.d_pad, x, cprep, cnh, xn, a, md, B, N, D, K, s);
+    }
+    const int KT = (K + 31) / 32;
+    const int bn = ASSIGN_WAVES * 32;
+    const int wpb = (N + bn - 1) / bn;
+    dim3 grid(B * wpb), block(256);
+    if (dt == DT_F32)
+        assign_split_d_kernel<DT_F32><<<grid, block, 0, s>>>(x, (const u32x4 *)cprep, cnh, xn, a, md, N, D, cfg.d_pad,
+                                                             KT, wpb);
+    else if (dt == DT_F16)
+        assign_split_d_kernel<DT_F16><<<grid, block, 0, s>>>(x, (const u32x4 *)cprep, cnh, xn, a, md, N, D, cfg.d_pad,
+                                                             KT, wpb);
+    else
+        assign_split_d_kernel<DT_BF16><<<grid, block, 0, s>>>(x, (const u32x4 *)cprep, cnh, xn, a, md, N, D,
+                                                              cfg.d_pad, KT, wpb);
+    return hipGetLastError();
+}
+
+}  // namespace fkm

@@ -1,0 +1,106 @@
+// Row norms (paper digest, "方法步骤详情" step (1): ||x_i||^2 precomputed before the centroid
+// scan) and the fp64 reductions behind the loop control (inertia and centroid shift).
+#include "common.h"
+#include "plan.h"
+
+namespace fkm {
+
+// One row per `lanes` lanes; each lane sums squares of 16-byte vectors (or scalars) of the row
+// in fp32, then a butterfly over the row's lanes.  Rows are dispatched in waves of 64/lanes.
+template <int DT, int V>
+__global__ __launch_bounds__(256) void row_norms_kernel(const void *__restrict__ x, float *__restrict__ out,
+                                                        int64_t rows, int D, int lanes) {
+    const int lane = threadIdx.x & 63;
+    const int G = 64 / lanes;
+    const int g = lane / lanes, r = lane - g * lanes;
+    const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * G + g;
+    const bool ok = row < rows;
+    const size_t e0 = (size_t)(ok ? row : 0) * D;
+    float s = 0.f;
+    if (ok) {
+        if constexpr (V == 1) {
+            for (int d = r; d < D; d += lanes) {
+                const float v = load_elem<DT>(x, e0 + d);
+                s += v * v;
+            }
+        } else {
+            constexpr int S = DT == DT_F32 ? 4 : 2;
+            for (int d = r * V; d < D; d += lanes * V) {
+                const uint4 u = *(const uint4 *)((const char *)x + (e0 + d) * S);
+                float f[V];
+                widen16<DT>(u, f);
+#pragma unroll
+                for (int e = 0; e < V; ++e) s += f[e] * f[e];
+            }
+        }
+    }
+    for (int off = 1; off < lanes; off <<= 1) s += __shfl_xor(s, off);
+    if (ok && r == 0) out[row] = s;
+}
+
+hipError_t launch_row_norms(int dt, const void *x, float *out, int64_t rows, int D, hipStream_t s) {
+    const int v16 = dt == DT_F32 ? 4 : 8;
+    const bool vec = (D % v16) == 0;
+    const int nvec = vec ? D / v16 : D;
+    int lanes = 1;
+    while (lanes < nvec && lanes < 64) lanes <<= 1;
+    const int G = 64 / lanes;
+    const int64_t waves = (rows + G - 1) / G;
+    dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+    if (dt == DT_F32) {
+        if (vec) row_norms_kernel<DT_F32, 4><<<grid, block, 0, s>>>(x, out, rows, D, lanes);
+        else row_norms_kernel<DT_F32, 1><<<grid, block, 0, s>>>(x, out, rows, D, lanes);
+    } else if (dt == DT_F16) {
+        if (vec) row_norms_kernel<DT_F16, 8><<<grid, block, 0, s>>>(x, out, rows, D, lanes);
+        else row_norms_kernel<DT_F16, 1><<<grid, block, 0, s>>>(x, out, rows, D, lanes);
+    } else {
+        if (vec) row_norms_kernel<DT_BF16, 8><<<grid, block, 0, s>>>(x, out, rows, D, lanes);
+        else row_norms_kernel<DT_BF16, 1><<<grid, block, 0, s>>>(x, out, rows, D, lanes);
+    }
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// Deterministic fp64 sums of float arrays, segmented by problem: level 1 writes one partial per
+// (problem, block) in a fixed order, level 2 adds the partials of a problem in order.
+// ------------------------------------------------------------------------------------------
+constexpr int RED_BLOCKS = 64;
+
+__global__ __launch_bounds__(256) void sum_f32_level1_kernel(const float *__restrict__ v, int64_t n,
+                                                             double *__restrict__ part) {
+    __shared__ double s[256];
+    const int b = blockIdx.y, blk = blockIdx.x;
+    const float *vb = v + (size_t)b * n;
+    const int64_t per = (n + RED_BLOCKS - 1) / RED_BLOCKS;
+    const int64_t lo = blk * per, hi = lo + per < n ? lo + per : n;
+    double acc = 0.0;
+    for (int64_t i = lo + threadIdx.x; i < hi; i += 256) acc += (double)vb[i];
+    s[threadIdx.x] = acc;
+    __syncthreads();
+    for (int off = 128; off >= 1; off >>= 1) {
+        if ((int)threadIdx.x < off) s[threadIdx.x] += s[threadIdx.x + off];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) part[(size_t)b * RED_BLOCKS + blk] = s[0];
+}
+
+// out[b] (= or +=) sum of the problem's partials.
+__global__ void sum_level2_kernel(const double *__restrict__ part, double *__restrict__ out, int accumulate) {
+    if (threadIdx.x != 0) return;
+    const int b = blockIdx.x;
+    double acc = 0.0;
+    for (int i = 0; i < RED_BLOCKS; ++i) acc += part[(size_t)b * RED_BLOCKS + i];
+    out[b] = accumulate ? out[b] + acc : acc;
+}
+
+size_t reduce_ws_bytes(int64_t B) { return align256((size_t)B * RED_BLOCKS * 8); }
+
+// out[b] = sum_i v[b*n + i] (fp64), or out[b] += ... when accumulate.
+hipError_t launch_sum_f32(const float *v, int B, int64_t n, double *out, int accumulate, void *ws, hipStream_t s) {
+    double *part = (double *)ws;
+    sum_f32_level1_kernel<<<dim3(RED_BLOCKS, B), dim3(256), 0, s>>>(v, n, part);
+    sum_level2_kernel<<<dim3(B), dim3(64), 0, s>>>(part, out, accumulate);
+    return hipGetLastError();
+}
+
+}  // namespace fkm

@@ -1,0 +1,226 @@
+// Stable arg-sort of the assignment vector on gfx950 (paper digest, "argsort与分段规约": only
+// the 1-D vector of cluster ids is sorted, the N x D points are never permuted; the digest's
+// "独立分析的弱点" suggests a radix sort for this key range).
+//
+// LSD counting passes over digits of the cluster id.  Per pass:
+//   1. hist:    each workgroup counts the digits of its tile of 4096 keys in LDS and writes
+//               one column of the [bins][tiles] table of its problem;
+//   2. scan:    one workgroup per problem turns the table into exclusive offsets, in
+//               (digit-major, tile-minor) order, so equal digits keep tile order;
+//   3. scatter: each wave ranks its keys 64 at a time, in index order: lanes holding the same
+//               digit are found with one ballot per digit bit; a lane's rank = earlier peers
+//               in the round + the wave's running count of that digit (LDS).  Waves are then
+//               offset by the counts of earlier waves of the tile.  Result: stable.
+// The single-pass case (all of the id in one digit) also yields the per-cluster counts.
+#include "common.h"
+#include "plan.h"
+
+namespace fkm {
+
+constexpr int SORT_WAVES = 4;
+constexpr int SORT_ROUNDS = SORT_TILE / (SORT_WAVES * 64);  // 16
+
+__global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t *__restrict__ keys, int N, int ntiles,
+                                                        int shift, int bins, int32_t *__restrict__ hist) {
+    extern __shared__ int32_t s_h[];
+    const int b = blockIdx.x / ntiles, t = blockIdx.x - b * ntiles;
+    for (int i = threadIdx.x; i < bins; i += 256) s_h[i] = 0;
+    __syncthreads();
+    const int32_t *kb = keys + (size_t)b * N;
+    const int lo = t * SORT_TILE, hi = min(N, lo + SORT_TILE);
+    const uint32_t mask = (uint32_t)bins - 1u;
+    for (int i = lo + threadIdx.x; i < hi; i += 256) atomicAdd(&s_h[((uint32_t)kb[i] >> shift) & mask], 1);
+    __syncthreads();
+    int32_t *hb = hist + (size_t)b * bins * ntiles;
+    for (int i = threadIdx.x; i < bins; i += 256) hb[(size_t)i * ntiles + t] = s_h[i];
+}
+
+// Exclusive scan of one problem's [bins][tiles] table, in place.
+__global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t *__restrict__ hist, int entries) {
+    __shared__ int32_t s_part[1024];
+    int32_t *hb = hist + (size_t)blockIdx.x * entries;
+    const int per = (entries + 1023) / 1024;
+    const int lo = min(entries, threadIdx.x * per), hi = min(entries, lo + per);
+    int32_t sum = 0;
+    for (int i = lo; i < hi; ++i) sum += hb[i];
+    s_part[threadIdx.x] = sum;
+    __syncthreads();
+    // Hillis-Steele inclusive scan over the 1024 partial sums
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int32_t v = threadIdx.x >= off ? s_part[threadIdx.x - off] : 0;
+        __syncthreads();
+        s_part[threadIdx.x] += v;
+        __syncthreads();
+    }
+    int32_t run = s_part[threadIdx.x] - sum;
+    for (int i = lo; i < hi; ++i) {
+        const int32_t v = hb[i];
+        hb[i] = run;
+        run += v;
+    }
+}
+
+// Per-bin totals of a scanned table (= counts per cluster when one digit is the whole id).
+__global__ __launch_bounds__(256) void counts_from_offsets_kernel(const int32_t *__restrict__ hist, int entries,
+                                                                  int ntiles, int K, int N,
+                                                                  int32_t *__restrict__ counts) {
+    const int b = blockIdx.y;
+    const int k = blockIdx.x * 256 + threadIdx.x;
+    if (k >= K) return;
+    const int32_t *hb = hist + (size_t)b * entries;
+    const int32_t start = hb[(size_t)k * ntiles];
+    const int32_t end = (k + 1) * ntiles < entries ? hb[(size_t)(k + 1) * ntiles] : N;
+    counts[(size_t)b * K + k] = end - start;
+}
+
+// Stable scatter of one pass.  vals_in == NULL means the values are the point indices.
+__global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__restrict__ keys_in,
+                                                           const int32_t *__restrict__ vals_in,
+                                                           const int32_t *__restrict__ hist, int N, int ntiles,
+                                                           int shift, int bits, int32_t *__restrict__ keys_out,
+                                                           int32_t *__restrict__ vals_out) {
+    extern __shared__ int32_t s_mem[];
+    const int bins = 1 << bits;
+    int32_t *s_wc = s_mem;                       // [SORT_WAVES][bins] running counts, then prefixes
+    int32_t *s_off = s_mem + SORT_WAVES * bins;  // [bins] this tile's global offsets
+    const int b = blockIdx.x / ntiles, t = blockIdx.x - b * ntiles;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int32_t *hb = hist + (size_t)b * bins * ntiles;
+    for (int i = tid; i < bins; i += 256) {
+        s_off[i] = hb[(size_t)i * ntiles + t];
+#pragma unroll
+        for (int ww = 0; ww < SORT_WAVES; ++ww) s_wc[ww * bins + i] = 0;
+    }
+    __syncthreads();
+
+    const size_t base = (size_t)b * N;
+    const int tile0 = t * SORT_TILE + w * (SORT_ROUNDS * 64);
+    const uint32_t mask = (uint32_t)bins - 1u;
+    int32_t key[SORT_ROUNDS], val[SORT_ROUNDS], pos[SORT_ROUNDS];
+#pragma unroll
+    for (int r = 0; r < SORT_ROUNDS; ++r) {
+        const int i = tile0 + r * 64 + lane;
+        const bool ok = i < N;
+        key[r] = ok ? keys_in[base + i] : 0;
+        val[r] = ok ? (vals_in ? vals_in[base + i] : i) : 0;
+    }
+    const uint64_t lt = lanemask_lt();
+    int32_t *wc = s_wc + w * bins;
+#pragma unroll
+    for (int r = 0; r < SORT_ROUNDS; ++r) {
+        const int i = tile0 + r * 64 + lane;
+        const bool ok = i < N;
+        const uint32_t dg = ((uint32_t)key[r] >> shift) & mask;
+        uint64_t peers = __ballot(ok);
+        for (int bit = 0; bit < bits; ++bit) {
+            const bool set = (dg >> bit) & 1u;
+            const uint64_t bal = __ballot(set);
+            peers &= set ? bal : ~bal;
+        }
+        const int before = __popcll(peers & lt);
+        // LDS accesses of one wave complete in order and the store depends on the load, so
+        // every lane reads its base before the group's lowest lane bumps it.
+        const int32_t wbase = ok ? wc[dg] : 0;
+        if (ok && before == 0) wc[dg] = wbase + __popcll(peers);
+        pos[r] = wbase + before;
+    }
+    __syncthreads();
+    // exclusive prefix over waves, per digit
+    for (int i = tid; i < bins; i += 256) {
+        int32_t run = 0;
+#pragma unroll
+        for (int ww = 0; ww < SORT_WAVES; ++ww) {
+            const int32_t v = s_wc[ww * bins + i];
+            s_wc[ww * bins + i] = run;
+            run += v;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < SORT_ROUNDS; ++r) {
+        const int i = tile0 + r * 64 + lane;
+        if (i < N) {
+            const uint32_t dg = ((uint32_t)key[r] >> shift) & mask;
+            const int32_t dst = s_off[dg] + wc[dg] + pos[r];
+            keys_out[base + dst] = key[r];
+            vals_out[base + dst] = val[r];
+        }
+    }
+}
+
+// Counts per cluster from the sorted ids: +end at a segment's last position, -start at its
+// first (each cluster gets exactly one of each, so integer atomics give an exact result).
+__global__ __launch_bounds__(256) void segment_counts_kernel(const int32_t *__restrict__ sids, int64_t total, int N,
+                                                             int K, int32_t *__restrict__ counts) {
+    const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gi >= total) return;
+    const int64_t b = gi / N;
+    const int p = (int)(gi - b * N);
+    const int32_t k = sids[gi];
+    if (k < 0 || k >= K) return;
+    int32_t *cb = counts + b * K;
+    if (p == N - 1 || sids[gi + 1] != k) atomicAdd(&cb[k], p + 1);
+    if (p == 0 || sids[gi - 1] != k) atomicSub(&cb[k], p);
+}
+
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t *__restrict__ p, int64_t n, int32_t v) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    fill_i32_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(p, n, v);
+    return hipGetLastError();
+}
+
+size_t sort_ws_bytes(int64_t B, int64_t N, int64_t K) {
+    const SortCfg c = plan_sort(N, K);
+    size_t bytes = align256((size_t)B * c.bins * c.ntiles * 4);
+    if (c.passes > 1) bytes += 2 * align256((size_t)B * N * 4);
+    return bytes;
+}
+
+// keys [B][N] -> sorted keys / point indices; counts optional.
+hipError_t launch_argsort(const int32_t *keys, int B, int N, int K, int32_t *out_keys, int32_t *out_vals,
+                          int32_t *counts, void *ws, hipStream_t s) {
+    const SortCfg c = plan_sort(N, K);
+    char *wp = (char *)ws;
+    int32_t *hist = (int32_t *)wp;
+    wp += align256((size_t)B * c.bins * c.ntiles * 4);
+    int32_t *tk = nullptr, *tv = nullptr;
+    if (c.passes > 1) {
+        tk = (int32_t *)wp;
+        wp += align256((size_t)B * N * 4);
+        tv = (int32_t *)wp;
+    }
+    const int entries = c.bins * c.ntiles;
+    const int32_t *kin = keys;
+    const int32_t *vin = nullptr;
+    for (int pass = 0; pass < c.passes; ++pass) {
+        const int shift = pass * c.bits;
+        // the last pass writes the outputs; earlier passes alternate so that holds
+        const bool to_out = ((c.passes - 1 - pass) % 2) == 0;
+        int32_t *ko = to_out ? out_keys : tk;
+        int32_t *vo = to_out ? out_vals : tv;
+        sort_hist_kernel<<<dim3(B * c.ntiles), dim3(256), c.bins * 4, s>>>(kin, N, c.ntiles, shift, c.bins, hist);
+        sort_scan_kernel<<<dim3(B), dim3(1024), 0, s>>>(hist, entries);
+        if (counts && c.passes == 1)
+            counts_from_offsets_kernel<<<dim3((K + 255) / 256, B), dim3(256), 0, s>>>(hist, entries, c.ntiles, K, N,
+                                                                                   counts);
+        sort_scatter_kernel<<<dim3(B * c.ntiles), dim3(256), (SORT_WAVES + 1) * c.bins * 4, s>>>(
+            kin, vin, hist, N, c.ntiles, shift, c.bits, ko, vo);
+        kin = ko;
+        vin = vo;
+    }
+    if (counts && c.passes > 1) {
+        hipError_t e = launch_fill_i32(counts, (int64_t)B * K, 0, s);
+        if (e != hipSuccess) return e;
+        const int64_t total = (int64_t)B * N;
+        segment_counts_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s>>>(out_keys, total, N, K,
+                                                                                         counts);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace fkm

@@ -1,0 +1,115 @@
+// Analytic tile plan (paper summary, "Key claims": a cache-aware heuristic picks the kernel
+// configuration from on-chip sizes and (N, K, D, B) instead of an exhaustive autotune).
+//
+// Everything here is arithmetic on gfx950 resource sizes; nothing is timed.
+//
+// Assign, small-D path (x tile kept in VGPRs for the whole centroid scan):
+//   * D is padded to DP in {16,...,512} (2-byte types) or {8,...,256} (fp32): the MFMA k-step
+//     is 16 (bf16/fp16 32x32x16) or 2 (fp32 32x32x2), and each lane holds half of every row.
+//   * VGPRs per lane ~= PB * (x: DP*s/8 + acc 16 + best 16) + prefetch 32 + c-norm 16 + 32.
+//     PB (32-point blocks per wave) is the largest of {4,2,1} keeping this <= 256, so two
+//     waves share a SIMD: one wave's compare/select work overlaps the other's MFMA.
+//   * Centroid stages of 32 KiB ping-pong in LDS: 2 x (32 KiB + norms) = 72 KiB per
+//     workgroup, two workgroups per CU within 160 KiB.
+//   * Every workgroup re-reads all K centroids from L2: the arithmetic intensity of that
+//     stream is 2*block_n*D FLOP per D*s bytes = block_n FLOP/B (bf16), >= 128 for
+//     block_n >= 128, above what L2 must feed MFMA (~2.5 PF / ~40 TB/s ~= 64 FLOP/B).
+//   * Workgroups of one problem are mapped onto one XCD so its centroids (K*D*s bytes,
+//     256 KiB at K=1024, D=128, bf16) stay in that XCD's 4 MiB L2.
+// Assign, split-D path (D above the register budget, README "Large-D and dtype support"):
+//   * point block of 128 (4 waves x 32), 4 centroid tiles (128 centroids) of accumulators per
+//     wave, D streamed through LDS in chunks of 64 (2-byte) / 32 (fp32) elements so one stage
+//     of x chunk + centroid chunk is 32 KiB, double buffered.
+// Arg-sort: counting passes over digits of the cluster id; one pass when the per-problem scan
+//   table (bins x tiles of 4096 keys) stays <= 2^20 entries and bins <= 4096 (the per-wave
+//   counters, 4 x bins x 4 B, fit LDS); otherwise balanced multi-pass LSD digits.
+// Update: rows are gathered with 16-byte vector loads when D allows; a row is covered by a
+//   power-of-two number of lanes so one wave load instruction moves 64 x 16 B from 64/lanes
+//   rows; each wave takes `rows` consecutive sorted positions, sized so ~8 waves per SIMD
+//   are in flight over the whole launch.
+#include "plan.h"
+
+#include <algorithm>
+
+namespace fkm {
+
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+static int pow2_ceil(int64_t v) {
+    int p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+static int log2_floor(int64_t v) {
+    int r = -1;
+    while (v > 0) { v >>= 1; ++r; }
+    return r;
+}
+
+AssignCfg plan_assign(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
+    AssignCfg c{};
+    const int s = dt == 0 ? 4 : 2;
+    const int dmin = dt == 0 ? 8 : 16;
+    if (D <= small_d_max(dt)) {
+        int dp = dmin;
+        while (dp < D) dp <<= 1;
+        c.path = 0;
+        c.d_pad = dp;
+        c.pb = small_d_pb(dt, dp);
+        c.tps = small_d_tps(dt, dp);
+        c.bd = 0;
+        c.block_n = ASSIGN_WAVES * c.pb * 32;
+        c.lds = 2 * (c.tps * 32 * dp * s + c.tps * 32 * 4);
+        c.vgpr = c.pb * (dp * s / 8 + 32) + 32 + 16 + 32;
+    } else {
+        const int bd = splitd_bd(dt);
+        c.path = 1;
+        c.d_pad = (int)((D + bd - 1) / bd * bd);
+        c.pb = 1;
+        c.tps = SPLITD_KB;
+        c.bd = bd;
+        c.block_n = ASSIGN_WAVES * 32;
+        c.lds = 2 * (c.block_n * bd * s + SPLITD_KB * 32 * bd * s) + SPLITD_KB * 32 * 4;
+        c.vgpr = SPLITD_KB * 16 + 16 + 32 + 16 + 48;
+    }
+    (void)K;
+    (void)B;
+    (void)N;
+    return c;
+}
+
+SortCfg plan_sort(int64_t N, int64_t K) {
+    SortCfg c{};
+    const int kbits = std::max(1, log2_floor(std::max<int64_t>(1, K - 1)) + 1);
+    c.ntiles = (int)cdiv(N, SORT_TILE);
+    int bmax = log2_floor(std::max<int64_t>(1, SORT_MAX_SCAN / c.ntiles));
+    bmax = std::max(1, std::min(SORT_MAX_BITS, bmax));
+    c.passes = (kbits + bmax - 1) / bmax;
+    c.bits = (kbits + c.passes - 1) / c.passes;
+    c.bins = 1 << c.bits;
+    return c;
+}
+
+UpdCfg plan_update(int dt, int64_t B, int64_t N, int64_t D) {
+    UpdCfg c{};
+    const int s = dt == 0 ? 4 : 2;
+    const int v16 = 16 / s;
+    c.vec = (D % v16 == 0) ? v16 : 1;
+    const int64_t nvec = D / c.vec;
+    c.lanes = std::min(64, pow2_ceil(nvec));
+    c.groups = 64 / c.lanes;
+    const int64_t vpl_all = cdiv(nvec, c.lanes);
+    c.vpl = (int)std::min<int64_t>(UPD_VPL_MAX, pow2_ceil(vpl_all));
+    c.cb_elems = c.lanes * c.vpl * c.vec;
+    c.ncb = (int)cdiv(D, c.cb_elems);
+    // ~8 resident waves per SIMD over the whole launch
+    const int64_t target_waves = (int64_t)Gfx950::cus * Gfx950::simds_per_cu * 8;
+    int64_t rows = (B * N) / std::max<int64_t>(1, target_waves / c.ncb);
+    rows = std::max<int64_t>(64, std::min<int64_t>(4096, rows));
+    c.rows = pow2_ceil(rows);
+    c.nch = cdiv(N, c.rows);
+    return c;
+}
+
+}  // namespace fkm

@@ -1,0 +1,73 @@
+// Analytic tile plan for the gfx950 kernels (host only).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/flashkm.h"
+
+namespace fkm {
+
+// gfx950 resources the plan is derived from.
+struct Gfx950 {
+    static constexpr int cus = 256;
+    static constexpr int simds_per_cu = 4;
+    static constexpr int lds_bytes_per_cu = 160 * 1024;
+    static constexpr int vgprs_per_lane = 512;       // arch + acc, per SIMD lane
+    static constexpr int l2_bytes_per_xcd = 4 << 20;
+    static constexpr int target_waves_per_simd = 2;  // lets one wave's compares overlap another's MFMA
+};
+
+// Kernel-side constants the plan and the launchers agree on.
+constexpr int ASSIGN_WAVES = 4;          // waves per assign workgroup
+constexpr int STAGE_BYTES = 32 * 1024;   // centroid bytes per LDS stage (double buffered)
+constexpr int SPLITD_KB = 4;             // split-D: 32-centroid tiles per register group
+constexpr int SORT_TILE = 4096;          // keys per sort workgroup (4 waves x 16 rounds x 64)
+constexpr int SORT_MAX_BITS = 11;        // <= 2048 bins per counting pass (LDS: 5 x bins x 4 B)
+constexpr int SORT_MAX_SCAN = 1 << 20;   // bins x tiles entries per problem for one scan workgroup
+constexpr int UPD_VPL_MAX = 4;           // 16-byte (or scalar) vectors per lane per row in the update
+
+struct AssignCfg {
+    int path;      // 0 small-D, 1 split-D
+    int d_pad;
+    int pb;        // point blocks per wave
+    int tps;       // tiles per LDS stage (small-D)
+    int bd;        // split-D chunk of D
+    int block_n;
+    int lds;
+    int vgpr;
+};
+
+struct SortCfg {
+    int bits, passes, ntiles, bins;
+};
+
+struct UpdCfg {
+    int rows;      // sorted rows per wave chunk
+    int vec;       // elements per vector
+    int lanes;     // lanes per row (power of two)
+    int groups;    // rows per step = 64 / lanes
+    int vpl;       // vectors per lane per row within one column block
+    int ncb;       // column blocks
+    int cb_elems;  // elements per column block
+    int64_t nch;   // chunks per problem
+};
+
+AssignCfg plan_assign(int dt, int64_t B, int64_t N, int64_t D, int64_t K);
+SortCfg plan_sort(int64_t N, int64_t K);
+UpdCfg plan_update(int dt, int64_t B, int64_t N, int64_t D);
+
+// Small-D register tile chosen for (dtype, padded D); shared with the kernel templates.
+constexpr int small_d_pb(int dt, int dp) {
+    return dt == 0 ? (dp <= 16 ? 4 : (dp <= 64 ? 2 : 1))
+                   : (dp <= 32 ? 4 : (dp <= 128 ? 2 : 1));
+}
+constexpr int small_d_tps(int dt, int dp) {
+    return STAGE_BYTES / (32 * dp * (dt == 0 ? 4 : 2)) > 0 ? STAGE_BYTES / (32 * dp * (dt == 0 ? 4 : 2)) : 1;
+}
+constexpr int splitd_bd(int dt) { return dt == 0 ? 32 : 64; }
+
+// Largest D handled by the small-D path (x tile kept in registers).
+constexpr int small_d_max(int dt) { return dt == 0 ? 256 : 512; }
+
+}  // namespace fkm

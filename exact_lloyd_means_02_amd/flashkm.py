@@ -1,0 +1,242 @@
+"""Thin ctypes binding of libflashkm (include/flashkm.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP kernels.  Torch
+tensors supply device memory and the current HIP stream; the workspace the C-ABI asks for is
+a torch uint8 tensor (the library itself allocates nothing).  If the library is missing the
+import raises: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libflashkm.so")
+
+KM_F32, KM_F16, KM_BF16 = 0, 1, 2
+KM_OK, KM_ERR_INVALID, KM_ERR_UNSUPPORTED, KM_ERR_WORKSPACE, KM_ERR_HIP = 0, -1, -2, -3, -4
+KM_OP_ASSIGN, KM_OP_ARGSORT, KM_OP_UPDATE, KM_OP_FIT, KM_OP_FIT_HOST = 1, 2, 3, 4, 5
+STATUS_NAMES = {0: "KM_OK", -1: "KM_ERR_INVALID", -2: "KM_ERR_UNSUPPORTED", -3: "KM_ERR_WORKSPACE", -4: "KM_ERR_HIP"}
+
+# every symbol the header declares
+EXPORTS = ["kmeans_plan", "kmeans_workspace_bytes", "kmeans_row_norms", "kmeans_assign", "kmeans_argsort_ids",
+           "kmeans_update", "kmeans_fit", "kmeans_last_error"]
+
+
+class KmPlan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "path", "d_pad", "point_blocks", "waves", "block_n", "block_k", "block_d", "lds_bytes", "vgpr_est",
+        "assign_wgs", "sort_bits", "sort_passes", "sort_tile", "upd_rows", "upd_vec", "upd_lanes")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class FlashKMError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("%s: %s" % (STATUS_NAMES.get(status, status), msg))
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libflashkm.so is not built (%s); run exact_lloyd_means_02_amd.build" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.kmeans_plan.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.POINTER(KmPlan)]
+    lib.kmeans_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, i64, i64]
+    lib.kmeans_workspace_bytes.restype = sz
+    lib.kmeans_row_norms.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp]
+    lib.kmeans_assign.argtypes = [vp, ctypes.c_int, vp, i64, i64, i64, i64, vp, vp, vp, vp, sz, vp]
+    lib.kmeans_argsort_ids.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, sz, vp]
+    lib.kmeans_update.argtypes = [vp, ctypes.c_int, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, sz, vp]
+    lib.kmeans_fit.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, i32, f32, i64, vp, vp, vp, vp, vp, sz, vp]
+    for n in ("kmeans_plan", "kmeans_row_norms", "kmeans_assign", "kmeans_argsort_ids", "kmeans_update",
+              "kmeans_fit"):
+        getattr(lib, n).restype = ctypes.c_int
+    lib.kmeans_last_error.argtypes = []
+    lib.kmeans_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+LIB = _load()
+
+
+def last_error() -> str:
+    return LIB.kmeans_last_error().decode()
+
+
+def _check(st: int):
+    if st != KM_OK:
+        raise FlashKMError(st, last_error())
+
+
+# ------------------------------------------------------------------------------------------------
+# torch marshalling
+# ------------------------------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: KM_F32, torch.float16: KM_F16, torch.bfloat16: KM_BF16}
+    if t.dtype not in m:
+        raise TypeError("unsupported dtype %s" % t.dtype)
+    return m[t.dtype]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t, stream=None):
+    torch = _torch()
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    if t.is_cuda:
+        return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+_WS = {}
+
+
+def workspace(op: int, dt: int, B: int, N: int, D: int, K: int, device, chunk_points: int = 0):
+    """A cached uint8 device tensor of the size the C-ABI asks for."""
+    torch = _torch()
+    nbytes = LIB.kmeans_workspace_bytes(op, dt, B, N, D, K, chunk_points)
+    if nbytes == 0:
+        raise FlashKMError(KM_ERR_INVALID, last_error() or "bad shape for workspace")
+    key = (op, str(device))
+    ws = _WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        _WS[key] = ws
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + nbytes]
+
+
+def clear_workspaces():
+    _WS.clear()
+
+
+def kmeans_plan(dt: int, B: int, N: int, D: int, K: int) -> dict:
+    p = KmPlan()
+    _check(LIB.kmeans_plan(dt, B, N, D, K, ctypes.byref(p)))
+    return p.as_dict()
+
+
+def kmeans_workspace_bytes(op: int, dt: int, B: int, N: int, D: int, K: int, chunk_points: int = 0) -> int:
+    return int(LIB.kmeans_workspace_bytes(op, dt, B, N, D, K, chunk_points))
+
+
+def kmeans_row_norms(x, out=None, stream=None):
+    torch = _torch()
+    _need(x.dim() == 3 and x.is_contiguous(), "x must be a contiguous [B, N, D] tensor")
+    B, N, D = x.shape
+    if out is None:
+        out = torch.empty((B, N), dtype=torch.float32, device=x.device)
+    _need(out.is_contiguous() and out.dtype == torch.float32 and tuple(out.shape) == (B, N), "bad out")
+    _check(LIB.kmeans_row_norms(_ptr(x), dtype_code(x), B, N, D, _ptr(out), _stream(x, stream)))
+    return out
+
+
+def kmeans_assign(x, centroids, x_norms=None, assign=None, min_dist=None, want_min_dist=False, stream=None):
+    """Returns (assign int32 [B,N], min_dist float32 [B,N] or None)."""
+    torch = _torch()
+    _need(x.dim() == 3 and x.is_contiguous(), "x must be a contiguous [B, N, D] tensor")
+    B, N, D = x.shape
+    _need(centroids.dim() == 3 and centroids.is_contiguous() and centroids.dtype == torch.float32
+          and centroids.shape[0] == B and centroids.shape[2] == D, "centroids must be contiguous f32 [B, K, D]")
+    K = centroids.shape[1]
+    if assign is None:
+        assign = torch.empty((B, N), dtype=torch.int32, device=x.device)
+    if want_min_dist and min_dist is None:
+        min_dist = torch.empty((B, N), dtype=torch.float32, device=x.device)
+    dt = dtype_code(x)
+    ws = workspace(KM_OP_ASSIGN, dt, B, N, D, K, x.device)
+    _check(LIB.kmeans_assign(_ptr(x), dt, _ptr(centroids), B, N, D, K, _ptr(x_norms), _ptr(assign), _ptr(min_dist),
+                             _ptr(ws), ws.numel(), _stream(x, stream)))
+    return assign, min_dist
+
+
+def kmeans_argsort_ids(assign, K: int, sorted_ids=None, sorted_idx=None, counts=None, want_counts=True,
+                       stream=None):
+    """Returns (sorted_ids, sorted_idx, counts or None), all int32."""
+    torch = _torch()
+    _need(assign.dim() == 2 and assign.is_contiguous() and assign.dtype == torch.int32, "assign: int32 [B, N]")
+    B, N = assign.shape
+    if sorted_ids is None:
+        sorted_ids = torch.empty_like(assign)
+    if sorted_idx is None:
+        sorted_idx = torch.empty_like(assign)
+    if want_counts and counts is None:
+        counts = torch.empty((B, K), dtype=torch.int32, device=assign.device)
+    ws = workspace(KM_OP_ARGSORT, KM_F32, B, N, 1, K, assign.device)
+    _check(LIB.kmeans_argsort_ids(_ptr(assign), B, N, K, _ptr(sorted_ids), _ptr(sorted_idx), _ptr(counts),
+                                  _ptr(ws), ws.numel(), _stream(assign, stream)))
+    return sorted_ids, sorted_idx, counts
+
+
+def kmeans_update(x, sorted_ids, sorted_idx, counts, centroids, shift=None, want_shift=False, stream=None):
+    """Updates `centroids` (f32 [B,K,D]) in place; returns shift (float64 [B]) or None."""
+    torch = _torch()
+    _need(x.dim() == 3 and x.is_contiguous(), "x must be a contiguous [B, N, D] tensor")
+    B, N, D = x.shape
+    _need(centroids.dim() == 3 and centroids.is_contiguous() and centroids.dtype == torch.float32, "centroids")
+    K = centroids.shape[1]
+    if want_shift and shift is None:
+        shift = torch.empty((B,), dtype=torch.float64, device=x.device)
+    dt = dtype_code(x)
+    ws = workspace(KM_OP_UPDATE, dt, B, N, D, K, x.device)
+    _check(LIB.kmeans_update(_ptr(x), dt, _ptr(sorted_ids), _ptr(sorted_idx), _ptr(counts), B, N, D, K,
+                             _ptr(centroids), _ptr(shift), _ptr(ws), ws.numel(), _stream(x, stream)))
+    return shift
+
+
+def kmeans_fit(x, centroids, iters: int, tol: float = 0.0, chunk_points: int = 0, assign=None,
+               want_assign=True, device=None, stream=None):
+    """Lloyd's loop.  x: device tensor, or pinned host tensor (streamed path).  `centroids` (device
+    f32 [B,K,D]) holds the init and receives the result.  Returns (assign, inertia [iters_done, B]
+    numpy float64, iters_done)."""
+    torch = _torch()
+    import numpy as np
+    _need(x.dim() == 3 and x.is_contiguous(), "x must be a contiguous [B, N, D] tensor")
+    B, N, D = x.shape
+    _need(centroids.is_cuda and centroids.dtype == torch.float32 and centroids.is_contiguous(), "centroids")
+    K = centroids.shape[1]
+    dev = centroids.device
+    if want_assign and assign is None:
+        assign = torch.empty((B, N), dtype=torch.int32, device=dev)
+    dt = dtype_code(x)
+    op = KM_OP_FIT if x.is_cuda else KM_OP_FIT_HOST
+    ws = workspace(op, dt, B, N, D, K, dev, chunk_points)
+    inertia = np.zeros((iters, B), dtype=np.float64)
+    done = ctypes.c_int32(0)
+    _check(LIB.kmeans_fit(_ptr(x), dt, B, N, D, K, int(iters), float(tol), int(chunk_points), _ptr(centroids),
+                          _ptr(assign), inertia.ctypes.data_as(ctypes.c_void_p), ctypes.byref(done), _ptr(ws),
+                          ws.numel(), _stream(centroids, stream)))
+    return assign, inertia[: done.value], done.value
+
+
+def batch_kmeans_euclid(x, n_clusters: int, max_iters: int = 100, tol: float = 0.0, init_centroids=None,
+                        chunk_points: int = 0, seed: int = 0):
+    """README-style entry (flash-kmeans README, "Usage"): returns (cluster_ids, centers, inertia).
+    Without init_centroids, K distinct points per problem are drawn with torch's generator."""
+    torch = _torch()
+    B, N, D = x.shape
+    dev = x.device if x.is_cuda else torch.device("cuda")
+    if init_centroids is None:
+        g = torch.Generator(device="cpu").manual_seed(seed)
+        idx = torch.stack([torch.randperm(N, generator=g)[:n_clusters] for _ in range(B)])
+        init_centroids = torch.stack([x[b].index_select(0, idx[b].to(x.device)) for b in range(B)]).float()
+    c = init_centroids.to(dev, dtype=torch.float32).contiguous().clone()
+    ids, inertia, _ = kmeans_fit(x, c, max_iters, tol, chunk_points)
+    return ids, c, inertia

@@ -1,0 +1,201 @@
+/*
+ * flashkm.h -- C-ABI of an MI355X (gfx950) library for batched Lloyd k-means:
+ * FlashAssign (streaming x.c^T contraction with an online arg-min) and the
+ * sort-inverse update (stable arg-sort of the assignment vector, segmented
+ * per-cluster sums, one write per segment).
+ *
+ * Sources are the Flash-KMeans pages:
+ *   - paper summary "Flash-KMeans: Fast and Memory-Efficient Exact K-Means",
+ *     sections "Key claims" and "Method";
+ *   - paper digest "Flash-KMeans：快速且内存高效精确K-Means聚类", sections
+ *     "argsort与分段规约", "核心方法" and "方法步骤详情" (steps (1)-(3));
+ *   - the flash-kmeans README, sections "Usage", "Large tensor Benchmark" and
+ *     "Large-D and dtype support".
+ *
+ * Conventions shared by every call:
+ *   - Arrays are dense, row-major, C-contiguous.  "Device" means memory the
+ *     GPU can address directly (hipMalloc / PyTorch CUDA tensors); "pinned
+ *     host" means page-locked host memory from hipHostMalloc or
+ *     torch.empty(..., pin_memory=True).
+ *   - B independent problems share K.  Shapes: x [B, N, D]; centroids
+ *     [B, K, D] float32; assign / sorted arrays [B, N] int32; counts [B, K]
+ *     int32.
+ *   - The caller owns every buffer.  The library allocates no device memory:
+ *     temporary storage comes from the caller's workspace `ws` of `ws_bytes`
+ *     bytes, sized by kmeans_workspace_bytes() and 256-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue their
+ *     kernels on it and return without waiting, except kmeans_fit (see there).
+ *   - Errors are explicit: every call returns a km_status_t; there is no
+ *     silent fallback.  Argument validation happens before any HIP call, so
+ *     invalid arguments are reported even on a machine without a GPU.
+ *     kmeans_last_error() returns a message for the calling thread's last
+ *     non-OK status.
+ *   - Preconditions the library does not check: finite input values; for the
+ *     arg-sort and update calls, 0 <= assign < K and sorted arrays / counts
+ *     produced by kmeans_argsort_ids from that assignment.  Kernels clamp
+ *     indices so that violating them gives wrong numbers, not out-of-bounds
+ *     accesses.
+ *   - Limits: 1 <= B, 1 <= K <= N < 2^31, 1 <= D <= 4096, B*N < 2^31,
+ *     K <= 2^24.
+ */
+#ifndef FLASHKM_H
+#define FLASHKM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KM_F32 = 0, KM_F16 = 1, KM_BF16 = 2 } km_dtype_t;
+
+typedef enum {
+    KM_OK = 0,
+    KM_ERR_INVALID = -1,      /* bad shape, null required pointer, unknown dtype/op, bad iters/tol */
+    KM_ERR_UNSUPPORTED = -2,  /* e.g. pageable host memory, host pointer where device memory is required */
+    KM_ERR_WORKSPACE = -3,    /* ws too small or misaligned */
+    KM_ERR_HIP = -4           /* a HIP runtime call failed; message carries hipGetErrorString */
+} km_status_t;
+
+typedef enum {
+    KM_OP_ASSIGN = 1,
+    KM_OP_ARGSORT = 2,
+    KM_OP_UPDATE = 3,
+    KM_OP_FIT = 4,            /* kmeans_fit with device-resident x */
+    KM_OP_FIT_HOST = 5        /* kmeans_fit with x in pinned host memory (streamed path) */
+} km_op_t;
+
+/*
+ * Tile plan chosen by the analytic heuristic (paper summary, "Key claims": a
+ * cache-aware heuristic picks kernel configurations from cache sizes and the
+ * problem shape instead of an exhaustive autotune).  Derived from gfx950 LDS
+ * (160 KiB per CU), register file (512 VGPRs per lane per SIMD), L2 (4 MiB
+ * per XCD) and (B, N, K, D, dtype); no timing runs.
+ */
+typedef struct {
+    int32_t path;          /* 0: small-D (points held in registers); 1: split-D (D tiled through LDS) */
+    int32_t d_pad;         /* D rounded up to the kernel's register tile */
+    int32_t point_blocks;  /* 32-point MFMA column blocks per wave */
+    int32_t waves;         /* waves per workgroup */
+    int32_t block_n;       /* points per workgroup */
+    int32_t block_k;       /* centroids per LDS stage (small-D) or per register group (split-D) */
+    int32_t block_d;       /* split-D: elements of D per LDS stage; 0 for small-D */
+    int32_t lds_bytes;     /* LDS per assign workgroup */
+    int32_t vgpr_est;      /* estimated VGPRs per lane of the assign kernel */
+    int32_t assign_wgs;    /* assign workgroups per launch */
+    int32_t sort_bits;     /* radix digit width */
+    int32_t sort_passes;   /* counting-sort passes */
+    int32_t sort_tile;     /* keys per sort workgroup */
+    int32_t upd_rows;      /* sorted rows per update wave */
+    int32_t upd_vec;       /* elements per update vector load */
+    int32_t upd_lanes;     /* lanes covering one row in the update */
+} km_plan_t;
+
+/* Fill *out with the plan for this problem.  Host only; no HIP call. */
+km_status_t kmeans_plan(km_dtype_t dt, int64_t B, int64_t N, int64_t D, int64_t K, km_plan_t *out);
+
+/*
+ * Workspace bytes needed by `op` (a km_op_t) for this shape.  `chunk_points`
+ * is used by KM_OP_FIT_HOST only (0 = default of 2^24 points, clamped to N).
+ * Returns 0 for invalid arguments.  Host only; no HIP call.
+ */
+size_t kmeans_workspace_bytes(int op, km_dtype_t dt, int64_t B, int64_t N, int64_t D, int64_t K,
+                              int64_t chunk_points);
+
+/*
+ * ||x_i||^2 for every point (paper digest, "方法步骤详情" step (1): the squared
+ * norms of the points are computed before the centroid scan).
+ *   x        device [B, N, D] of dtype dt
+ *   x_norms  device [B, N] float32 out (fp32 accumulation)
+ */
+km_status_t kmeans_row_norms(const void *x, km_dtype_t dt, int64_t B, int64_t N, int64_t D,
+                             float *x_norms, void *stream);
+
+/*
+ * FlashAssign (paper summary, "Method"; paper digest, "核心方法" and step (1)):
+ * for every point, a_i = argmin_k ||c~_k||^2 - 2 x_i . c~_k, scanning
+ * centroids tile by tile with a running (min, index) per point, never
+ * writing the N x K distance matrix.  c~ = dtype(fp32 centroids), rounded to
+ * nearest even; the contraction runs on MFMA in dt with fp32 accumulation.
+ * Ties go to the lowest centroid index.
+ *   x          device [B, N, D] dtype dt
+ *   centroids  device [B, K, D] float32 (the master copy; read only)
+ *   x_norms    device [B, N] float32 or NULL; required when min_dist != NULL
+ *   assign     device [B, N] int32 out
+ *   min_dist   device [B, N] float32 out or NULL: x_norms_i + min score
+ *              (the squared distance to the chosen centroid, in fp32)
+ *   ws         workspace >= kmeans_workspace_bytes(KM_OP_ASSIGN, ...)
+ */
+km_status_t kmeans_assign(const void *x, km_dtype_t dt, const float *centroids, int64_t B, int64_t N,
+                          int64_t D, int64_t K, const float *x_norms, int32_t *assign,
+                          float *min_dist, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Stable ascending arg-sort of each problem's assignment vector (paper
+ * digest, "argsort与分段规约": [3,1,2,1,3,2] -> ids [1,1,2,2,3,3], indices
+ * [1,3,2,5,0,4]); a hand-written LDS counting/radix sort keyed by cluster id.
+ *   assign      device [B, N] int32, values in [0, K)
+ *   sorted_ids  device [B, N] int32 out: assign[b, sorted_idx[b, j]]
+ *   sorted_idx  device [B, N] int32 out: 0-based point indices, equal ids in
+ *               increasing index order
+ *   counts      device [B, K] int32 out or NULL: points per cluster
+ */
+km_status_t kmeans_argsort_ids(const int32_t *assign, int64_t B, int64_t N, int64_t K,
+                               int32_t *sorted_ids, int32_t *sorted_idx, int32_t *counts, void *ws,
+                               size_t ws_bytes, void *stream);
+
+/*
+ * Sort-inverse update (paper summary, "Method"; paper digest, step (2)):
+ * each wave takes a contiguous chunk of the sorted order, gathers the rows
+ * of the unpermuted x through sorted_idx, sums each cluster-id segment on
+ * chip in fp32, and writes once per segment; segments cut by a chunk edge
+ * are combined in chunk order (deterministic, no float atomics).  Then
+ * c_k <- s_k / n_k; a cluster with n_k == 0 keeps its centroid.
+ *   x           device [B, N, D] dtype dt
+ *   sorted_ids, sorted_idx, counts   from kmeans_argsort_ids for the same
+ *               assignment
+ *   centroids   device [B, K, D] float32 in: C_t, out: C_{t+1}
+ *   shift       device [B] double out or NULL: sum_k ||C_{t+1,k} - C_{t,k}||^2
+ */
+km_status_t kmeans_update(const void *x, km_dtype_t dt, const int32_t *sorted_ids,
+                          const int32_t *sorted_idx, const int32_t *counts, int64_t B, int64_t N,
+                          int64_t D, int64_t K, float *centroids, double *shift, void *ws,
+                          size_t ws_bytes, void *stream);
+
+/*
+ * Lloyd's loop (README, "Usage": batch_kmeans_Euclid(x, n_clusters,
+ * max_iters, tol, init_centroids)): row norms once, then per iteration
+ * assign -> inertia -> arg-sort -> update.  With tol > 0 the run stops after
+ * iteration t when max_b shift_t[b] < tol (one host read per iteration);
+ * with tol == 0 all `iters` iterations run without a host wait until the end.
+ * If x is pinned host memory, the streamed path runs instead (README,
+ * "Large tensor Benchmark"; paper digest, step (3)): each iteration streams
+ * x in chunks of `chunk_points` points with hipMemcpyAsync into two device
+ * staging buffers, overlapping the copy of chunk i+1 with assign / arg-sort
+ * / partial update of chunk i, and divides after the last chunk.  x is never
+ * cached on the device across iterations.
+ *   x            device or pinned host [B, N, D] dtype dt (pageable host
+ *                memory -> KM_ERR_UNSUPPORTED)
+ *   iters        maximum iterations (>= 1); tol >= 0
+ *   chunk_points streamed path only (0 = 2^24, clamped to N)
+ *   centroids    device [B, K, D] float32 in: init, out: final
+ *   assign       device [B, N] int32 out or NULL: labels of the last assignment
+ *   inertia      host double [iters * B] out or NULL: per iteration and
+ *                problem, sum_i ||x_i - c~_{a_i}||^2 (fp32 terms, fp64 sum)
+ *   iters_done   host int32 out or NULL
+ * Returns after the work has finished (it synchronises `stream`).
+ */
+km_status_t kmeans_fit(const void *x, km_dtype_t dt, int64_t B, int64_t N, int64_t D, int64_t K,
+                       int32_t iters, float tol, int64_t chunk_points, float *centroids,
+                       int32_t *assign, double *inertia, int32_t *iters_done, void *ws,
+                       size_t ws_bytes, void *stream);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char *kmeans_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHKM_H */

@@ -1,0 +1,170 @@
+"""Stage parity on the GPU: every call goes through the C-ABI (libflashkm) and is compared
+with the fp64 oracle on the same seeded inputs (teacher forced: each stage takes the GPU's
+own inputs from the previous stage)."""
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from exact_lloyd_means_02_amd import workloads as W
+
+from helpers import (check_argsort, check_assign, check_inertia, check_update, device, make_inputs,
+                     operand)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fk():
+    from exact_lloyd_means_02_amd import flashkm
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return flashkm
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# small shapes spanning several tiles with ragged tails (N % 256, K % 32, D padding)
+ASSIGN_CASES = [
+    ("headline_bf16", dict(B=2, N=1000, K=100)),
+    ("headline_bf16", dict(B=1, N=700, K=1, M=1)),
+    ("batched_f16", dict(B=3, N=777, K=70)),
+    ("tiny_f32", dict()),
+    ("tiny_f32", dict(N=3000, D=37, K=45, M=20)),
+    ("headline_bf16", dict(B=2, N=600, D=96, K=64)),
+    ("batched_f16", dict(B=1, N=500, D=100, K=33)),
+    ("headline_bf16", dict(B=1, N=300, D=512, K=40)),
+    ("batched_f16", dict(B=2, N=400, D=24, K=300)),
+    ("splitd_f32", dict(N=700, K=150)),
+    ("headline_bf16", dict(B=1, N=520, D=768, K=70)),
+    ("batched_f16", dict(B=1, N=300, D=1000, K=40)),
+    ("splitd_f32", dict(N=400, D=300, K=64)),
+]
+
+
+@pytest.mark.parametrize("name,kw", ASSIGN_CASES, ids=[f"{n}-{kw}" for n, kw in ASSIGN_CASES])
+def test_row_norms_and_assign(fk, name, kw):
+    w = W.small(name, **kw)
+    _say(f"case {w}")
+    x, x64, c0, xt, ct = make_inputs(w)
+    xn = fk.kmeans_row_norms(xt)
+    a, md = fk.kmeans_assign(xt, ct, x_norms=xn, want_min_dist=True)
+    torch.cuda.synchronize()
+    xn_ref = oracle.row_norms(x64)
+    assert np.allclose(xn.cpu().numpy(), xn_ref, rtol=(w.D + 4) * 2.0 ** -24, atol=1e-30)
+    check_assign(x64, operand(c0, w.dtype), a.cpu().numpy(), md.cpu().numpy())
+
+
+def test_assign_exact_ties_go_to_lowest_index(fk):
+    """Duplicate centroids give bit-identical scores; the lowest index must win."""
+    w = W.small("headline_bf16", B=1, N=2000, K=64)
+    x, x64, c0, xt, ct = make_inputs(w)
+    c = c0.copy()
+    c[0, 40:] = c[0, 8:32]              # clusters 40..63 duplicate 8..31 (other tiles, other lanes)
+    c[0, 5] = c[0, 3]                   # same tile, same lane half
+    c[0, 7] = c[0, 2]                   # same tile, other lane half
+    a, _ = fk.kmeans_assign(xt, torch.from_numpy(c).to(device()))
+    a = a.cpu().numpy()[0]
+    assert not np.isin(a, [5, 7] + list(range(40, 64))).any()
+    check_assign(x64, operand(c, w.dtype), a[None])
+
+
+def test_assign_k_equals_n(fk):
+    w = W.small("headline_bf16", B=2, N=300, K=300)
+    x, x64, c0, xt, ct = make_inputs(w)
+    c = W.storage_to_f32(x, w.dtype)            # every point is a centroid
+    a, _ = fk.kmeans_assign(xt, torch.from_numpy(c).to(device()))
+    assert (a.cpu().numpy() == np.arange(300)[None]).all()
+
+
+def test_argsort_worked_example(fk, golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "argsort_worked_example.json")))
+    a = torch.tensor([g["assign"]], dtype=torch.int32, device=device())
+    s, i, c = fk.kmeans_argsort_ids(a, g["K"])
+    assert s.cpu().tolist()[0] == g["sorted_ids"]
+    assert i.cpu().tolist()[0] == g["sorted_idx"]
+    assert c.cpu().tolist()[0] == g["counts"]
+
+
+SORT_CASES = [(1, 1, 1), (3, 10000, 1000), (2, 4097, 8), (1, 65536, 1024), (2, 1 << 17, 32768),
+              (1, 1 << 20, 4096), (4, 12345, 2048), (1, 5000, 5000)]
+
+
+@pytest.mark.parametrize("B,N,K", SORT_CASES)
+def test_argsort(fk, B, N, K):
+    _say(f"argsort B={B} N={N} K={K} plan={fk.kmeans_plan(0, B, N, 1, K)['sort_passes']} passes")
+    rng = np.random.default_rng(N + K)
+    a = rng.integers(0, K, size=(B, N)).astype(np.int32)
+    if K > 4:
+        a[:, : N // 3] = rng.integers(0, 3, size=(B, N // 3))      # hot clusters
+    at = torch.from_numpy(a).to(device())
+    s, i, c = fk.kmeans_argsort_ids(at, K)
+    check_argsort(a, K, s.cpu().numpy(), i.cpu().numpy(), c.cpu().numpy())
+
+
+UPDATE_CASES = [
+    ("headline_bf16", dict(B=2, N=3000, K=100)),
+    ("batched_f16", dict(B=2, N=5000, K=37)),
+    ("tiny_f32", dict()),
+    ("tiny_f32", dict(N=3000, D=37, K=45, M=20)),
+    ("batched_f16", dict(B=1, N=2000, D=100, K=50)),
+    ("splitd_f32", dict(N=3000, K=20)),
+    ("headline_bf16", dict(B=1, N=2000, D=4096, K=10)),
+    ("skew_bf16_k64", dict(N=200000, K=64)),
+]
+
+
+@pytest.mark.parametrize("name,kw", UPDATE_CASES, ids=[f"{n}-{kw}" for n, kw in UPDATE_CASES])
+def test_update_teacher_forced(fk, name, kw):
+    w = W.small(name, **kw)
+    _say(f"case {w}")
+    x, x64, c0, xt, ct = make_inputs(w)
+    a, _ = fk.kmeans_assign(xt, ct)
+    s, i, c = fk.kmeans_argsort_ids(a, w.K)
+    cnew = ct.clone()
+    shift = fk.kmeans_update(xt, s, i, c, cnew, want_shift=True)
+    torch.cuda.synchronize()
+    an = a.cpu().numpy()
+    check_argsort(an, w.K, s.cpu().numpy(), i.cpu().numpy(), c.cpu().numpy())
+    check_update(x64, an, c0, cnew.cpu().numpy(), w.dtype, shift.cpu().numpy())
+
+
+def test_update_keeps_empty_clusters(fk):
+    w = W.small("headline_bf16", B=2, N=2000, K=50)
+    x, x64, c0, xt, ct = make_inputs(w)
+    rng = np.random.default_rng(3)
+    a = rng.integers(0, 25, size=(2, 2000)).astype(np.int32)        # clusters 25..49 empty
+    a[1, :1500] = 7                                                  # one hot cluster
+    at = torch.from_numpy(a).to(device())
+    s, i, c = fk.kmeans_argsort_ids(at, w.K)
+    cnew = ct.clone()
+    fk.kmeans_update(xt, s, i, c, cnew)
+    check_update(x64, a, c0, cnew.cpu().numpy(), w.dtype)
+
+
+def test_update_is_deterministic(fk):
+    w = W.small("skew_bf16_k64", N=300000, K=64)
+    x, x64, c0, xt, ct = make_inputs(w)
+    a, _ = fk.kmeans_assign(xt, ct)
+    s, i, c = fk.kmeans_argsort_ids(a, w.K)
+    outs = []
+    for _ in range(3):
+        cn = ct.clone()
+        fk.kmeans_update(xt, s, i, c, cn)
+        outs.append(cn.cpu().numpy())
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+def test_inertia_matches_oracle(fk):
+    w = W.small("headline_bf16", B=3, N=4000, K=128)
+    x, x64, c0, xt, ct = make_inputs(w)
+    xn = fk.kmeans_row_norms(xt)
+    a, md = fk.kmeans_assign(xt, ct, x_norms=xn, want_min_dist=True)
+    J = md.double().sum(dim=1).cpu().numpy()
+    check_inertia(x64, operand(c0, w.dtype), a.cpu().numpy(), J)
