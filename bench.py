@@ -1,0 +1,179 @@
+#!/usr/bin/env python3
+"""Benchmark: one batched Lloyd iteration on one MI355X.
+
+A step is one Lloyd iteration of the whole path (centroid preparation, FlashAssign with the
+per-point minimum distance, inertia, arg-sort, sort-inverse update with the shift), run by
+kmeans_fit on the headline workload (B=32, N=65536, D=128, K=1024, bf16; inputs resident in
+HBM).  The timed region is one kmeans_fit call of `--steps` iterations (the point norms are
+computed once inside it, as in any fit).  Per-stage times come from HIP events recorded on
+the stream the stages run on.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "ms per Lloyd iteration at B=32,N=65536,K=1024,D=128 bf16; % MFMA and % HBM peak"
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--workload", default="headline_bf16")
+    p.add_argument("--stage-reps", type=int, default=10)
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def algorithmic(w):
+    """Per-iteration algorithmic work (see the design notes): assign FLOP on MFMA, assign bytes,
+    update bytes (arg-sort + segmented reduction + centroid write)."""
+    from exact_lloyd_means_02_amd.workloads import ELEM_BYTES
+    s = ELEM_BYTES[w.dtype]
+    B, N, D, K = w.B, w.N, w.D, w.K
+    flops = 2.0 * B * N * K * D
+    assign_bytes = B * N * D * s + B * K * D * s + 4 * B * K + 8 * B * N
+    update_bytes = 20 * B * N + B * N * D * s + 8 * B * K * (D + 1) + B * K * D * (4 + s) + 4 * B * K
+    return flops, assign_bytes, update_bytes
+
+
+def cpu_baseline(w, x, c0, target_s):
+    """The fp64 oracle (as it stands) on a bounded sample of the same workload: one Lloyd
+    iteration on the first `n` points of the first `p` problems against all K centroids,
+    grown until it takes ~0.6 * target_s (or covers everything), then scaled to B*N points."""
+    import numpy as np
+    import oracle
+    from exact_lloyd_means_02_amd import workloads as W
+    n, p = min(w.N, 2048), 1
+    while True:
+        xs = W.storage_to_f64(x[:p, :n], w.dtype)
+        t0 = time.perf_counter()
+        oracle.lloyd_iteration(xs, c0[:p].astype(np.float64), dtype=w.dtype, mode="modelled")
+        dt = time.perf_counter() - t0
+        if dt >= 0.6 * target_s or (n >= w.N and p >= w.B):
+            break
+        grow = max(1.5, min(8.0, 0.7 * target_s / max(dt, 1e-3)))
+        if n < w.N:
+            n = min(w.N, int(n * grow))
+        else:
+            p = min(w.B, max(p + 1, int(p * grow)))
+    scale = (w.B * w.N) / (p * n)
+    return {"value": round(dt * scale * 1e3, 3), "unit": "ms", "cores": oracle.threads(), "kind": "oracle",
+            "sample": "one fp64 oracle Lloyd iteration on %d of %d points (%d problem(s) x %d points, all K=%d "
+                      "centroids) took %.2f s; scaled by %.1fx to the full iteration" % (
+                          p * n, w.B * w.N, p, n, w.K, dt, scale)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); --gpus %d is not supported"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from exact_lloyd_means_02_amd import flashkm as fk
+    from exact_lloyd_means_02_amd import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    if w.host:
+        print("bench.py: streamed workloads are timed by their own script", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    print("bench: generating %s" % (w,), file=sys.stderr, flush=True)
+    x, c0, _ = W.make(w)
+    xt = W.to_torch(x, w.dtype).to(dev)
+    c0t = torch.from_numpy(c0).to(dev)
+    c = c0t.clone()
+    stream = torch.cuda.current_stream(dev)
+
+    # ---- warmup (untimed): W iterations
+    fk.kmeans_fit(xt, c, max(1, args.warmup), 0.0)
+    torch.cuda.synchronize()
+
+    # ---- timed: exactly `steps` Lloyd iterations in one fit
+    c.copy_(c0t)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    _, inertia, done = fk.kmeans_fit(xt, c, args.steps, 0.0)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    assert done == args.steps
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    print("bench: %d iterations in %.3f ms" % (args.steps, (t1 - t0) * 1e3), file=sys.stderr, flush=True)
+
+    # ---- per-stage times (HIP events on the stages' stream), teacher forced from c0
+    xn = fk.kmeans_row_norms(xt)
+    a, md = fk.kmeans_assign(xt, c0t, x_norms=xn, want_min_dist=True)
+    s_ids, s_idx, counts = fk.kmeans_argsort_ids(a, w.K)
+    cu = c0t.clone()
+    torch.cuda.synchronize()
+    R = args.stage_reps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    times = {"row_norms": [], "assign": [], "argsort": [], "update": []}
+    for _ in range(R):
+        cu.copy_(c0t)
+        ev[0].record(stream)
+        fk.kmeans_row_norms(xt, out=xn)
+        ev[1].record(stream)
+        fk.kmeans_assign(xt, c0t, x_norms=xn, assign=a, min_dist=md)
+        ev[2].record(stream)
+        fk.kmeans_argsort_ids(a, w.K, sorted_ids=s_ids, sorted_idx=s_idx, counts=counts)
+        ev[3].record(stream)
+        fk.kmeans_update(xt, s_ids, s_idx, counts, cu)
+        ev[4].record(stream)
+        torch.cuda.synchronize()
+        for k, (i, j) in zip(times, [(0, 1), (1, 2), (2, 3), (3, 4)]):
+            times[k].append(ev[i].elapsed_time(ev[j]))
+    st = {k: float(np.median(v)) for k, v in times.items()}
+    flops, abytes, ubytes = algorithmic(w)
+    peak = PEAK_TFLOPS[w.dtype]
+    assign_tflops = flops / (st["assign"] * 1e-3) / 1e12
+    upd_ms = st["argsort"] + st["update"]
+    upd_gbs = ubytes / (upd_ms * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC if w.name == "headline_bf16" else "ms per Lloyd iteration (%s)" % w.name,
+        "value": round(ms_per_step, 4),
+        "unit": "ms",
+        "higher_is_better": False,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "D": w.D, "K": w.K, "iters": args.steps, "tol": 0.0,
+                   "inputs": "HBM-resident"},
+        "roofline": {"bound": "mfma", "achieved": round(assign_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(assign_tflops / peak, 4), "traffic": None,
+                     "kernel": "assign_small_d_kernel (event time of kmeans_assign: centroid prep + FlashAssign)",
+                     "flop_per_launch": flops},
+        "stages_ms": {k: round(v, 4) for k, v in st.items()},
+        "update": {"bound": "hbm", "achieved": round(upd_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                   "frac": round(upd_gbs / PEAK_HBM_GBS, 4), "bytes_per_iter": ubytes,
+                   "stages": "kmeans_argsort_ids + kmeans_update"},
+        "inertia_last": [float(v) for v in inertia[-1][:2]],
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the oracle sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, x, c0, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
