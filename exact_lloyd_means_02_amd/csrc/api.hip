@@ -92,7 +92,7 @@ km_status_t check_ws(const void *ws, size_t ws_bytes, size_t need) {
 // --------------------------------------------------------------------------------------------
 size_t assign_ws(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
     const AssignCfg c = plan_assign(dt, B, N, D, K);
-    const int64_t KT = ceil_div(K, 32);
+    const int64_t KT = (int64_t)assign_tiles(K);
     return align256((size_t)B * KT * 32 * c.d_pad * elem_bytes(dt)) + align256((size_t)B * KT * 32 * 4);
 }
 
@@ -230,7 +230,7 @@ km_status_t check_device_arch() {
 km_status_t do_assign(int dt, const void *x, const float *C, int64_t B, int64_t N, int64_t D, int64_t K,
                       const float *xn, int32_t *a, float *md, void *ws, hipStream_t s) {
     const AssignCfg cfg = plan_assign(dt, B, N, D, K);
-    const int64_t KT = ceil_div(K, 32);
+    const int64_t KT = (int64_t)assign_tiles(K);
     char *cprep = (char *)ws;
     float *cnh = (float *)(cprep + align256((size_t)B * KT * 32 * cfg.d_pad * elem_bytes(dt)));
     KM_HIP(launch_prep_centroids(dt, C, cprep, cnh, (int)B, (int)K, (int)D, cfg.d_pad, s));
@@ -455,7 +455,7 @@ km_status_t fit_host(int dt, const void *xh, int64_t B, int64_t N, int64_t D, in
     char *stage_buf[2] = {ws + L.stage_buf[0], ws + L.stage_buf[1]};
     char *cprep = ws + L.cprep;
     const AssignCfg cfg = plan_assign(dt, B, N, D, K);
-    const int64_t KT = ceil_div(K, 32);
+    const int64_t KT = (int64_t)assign_tiles(K);
     const size_t cprep_bytes = align256((size_t)B * KT * 32 * cfg.d_pad * es);
     float *cnh = (float *)(cprep + cprep_bytes);
     const size_t cprep_per_b = (size_t)KT * 32 * cfg.d_pad * es;

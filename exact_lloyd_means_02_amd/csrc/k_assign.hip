@@ -33,7 +33,10 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // ------------------------------------------------------------------------------------------
 // Centroid preparation.
 //   cprep (per problem, tile t of 32 centroids, group q < DP/(2*VW), lane l = i + 32h):
-//     16 bytes = -c~[32t+i][h*DP/2 + q*VW + e], e < VW  (VW = 8 for 2-byte types, 4 for fp32)
+//     16 bytes = -c~[32t+i][(2q+h)*VW + e], e < VW  (VW = 8 for 2-byte types, 4 for fp32)
+//   The contraction index is split so that the two lane halves (h) of one MFMA step hold
+//   adjacent 16-byte pieces of a row: the point rows are then read 32 contiguous bytes at a
+//   time (the same map is used for x, and only its consistency between A and B matters).
 //   cnh[b][k] = ||c~_k||^2 / 2 in fp32 (+inf for the padding rows k >= K)
 // c~ = dtype(c) with round-to-nearest-even.  Zero padding for d >= D and k >= K.
 // ------------------------------------------------------------------------------------------
@@ -80,8 +83,8 @@ __global__ __launch_bounds__(256) void prep_centroids_kernel(const float *__rest
                 w[e >> 1] |= (bits & 0xFFFFu) << ((e & 1) * 16);
             }
         }
-        const int h = d0 / (DP / 2);
-        const int q = (d0 - h * (DP / 2)) / VW;
+        const int h = (d0 / VW) & 1;
+        const int q = d0 / (2 * VW);
         const size_t off = (((size_t)b * KT + t) * QG + q) * 64 + i + 32 * h;
         cprep[off] = u32x4{w[0], w[1], w[2], w[3]};
     }
@@ -116,6 +119,12 @@ __device__ inline u32x4 load_x_group(const void *x, size_t row_elem0, int d0, in
         }
     }
     return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// Copy 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4): the
+// wave's 64 lanes fill the 1 KiB at `lds` (wave-uniform), lane l at bytes [16 l, 16 l + 16).
+__device__ inline void lds_dma16(const void *gptr, void *lds) {
+    __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
 }
 
 // acc += A(32 centroids) x B(32 points) over one 16-byte group per lane.
@@ -187,10 +196,34 @@ __device__ inline void argmin_finish(const ArgminState &s, int h, bool write, in
     }
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory loads are outstanding and all
+// LDS operations are done (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4]
+// in bits 15:14).
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | (7 << 4) | (0 << 8) | (((n >> 4) & 3) << 14); }
+
+// Workgroup barrier that leaves newer global->LDS copies in flight: this wave's LDS traffic
+// and all but its `n` youngest vector-memory loads are complete before the s_barrier.  The
+// empty asm statements keep the compiler from moving memory operations across it.
+template <int n>
+__device__ inline void stage_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(n));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // ------------------------------------------------------------------------------------------
 // Small-D assign: each wave keeps PB blocks of 32 points in VGPRs (B operand) for the whole
-// scan; centroid tiles stream through LDS in stages of TPS tiles, double buffered.
+// scan; centroid tiles stream through LDS in stages of two tiles, three buffers deep.
 // grid = B * ceil(N / block_n) workgroups of 256 threads.
+//
+// Per tile the wave issues PB x QG MFMAs.  Everything else is kept off their critical path:
+//   * the A fragments of tile t+1 are read from LDS while the MFMAs of tile t run (each
+//     fragment register is refilled right after its last MFMA of tile t);
+//   * the arg-min selects of tile t-1 (other accumulator set) fill the MFMA shadow;
+//   * the centroid norms of tile t+1 are read into the freed accumulator set;
+//   * stage s+2 is copied global->LDS while stage s is consumed; a barrier in the middle of
+//     each stage publishes stage s+1 before the first fragment of it is read.
 // ------------------------------------------------------------------------------------------
 template <int DT, int DP>
 __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restrict__ x,
@@ -203,15 +236,18 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
     constexpr int VW = 16 / S;
     constexpr int QG = DP / (2 * VW);
     constexpr int PB = small_d_pb(DT, DP);
-    constexpr int TPS = small_d_tps(DT, DP);
     constexpr int TILE_U4 = QG * 64;
+    constexpr int TPS = QG >= 2 ? 2 : 4;  // tiles per stage: at least 4 KiB, one per wave-copy
     constexpr int STAGE_U4 = TPS * TILE_U4;
-    constexpr int PF = STAGE_U4 / 256;
-    static_assert(STAGE_U4 % 256 == 0, "stage must split evenly over 256 threads");
-    static_assert(TPS * 8 <= 256, "norm copy uses one float4 per thread");
+    constexpr int PF = STAGE_U4 / 256;  // 1 KiB copy instructions per wave per stage
+    constexpr int NCOPY = PF + 1;       // ... plus one for the stage's norms
+    static_assert(STAGE_U4 % 256 == 0, "stage must split evenly over 4 waves");
+    static_assert(TPS % 2 == 0, "accumulator sets alternate per tile");
 
-    __shared__ u32x4 s_c[2][STAGE_U4];
-    __shared__ float s_n[2][TPS * 32];
+    // Three distinct LDS buffers: the compiler can then tell that the reads of one buffer
+    // never alias the global->LDS copies into another.
+    __shared__ u32x4 s_c0[STAGE_U4], s_c1[STAGE_U4], s_c2[STAGE_U4];
+    __shared__ __attribute__((aligned(16))) float s_n0[TPS * 32], s_n1[TPS * 32], s_n2[TPS * 32];
 
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
     const int b = wg / wgs_per_b;
@@ -227,69 +263,99 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
         const bool vp = pt < N;
         const size_t row0 = ((size_t)b * N + (vp ? pt : 0)) * D;
 #pragma unroll
-        for (int q = 0; q < QG; ++q) xr[p][q] = load_x_group<DT>(x, row0, h * (DP / 2) + q * VW, D, vp);
+        for (int q = 0; q < QG; ++q) xr[p][q] = load_x_group<DT>(x, row0, (2 * q + h) * VW, D, vp);
     }
 
     const u32x4 *cb = cprep + (size_t)b * KT * TILE_U4;
     const float *nb = cnh + (size_t)b * KT * 32;
-    const int nst = (KT + TPS - 1) / TPS;
+    const int nst = KT / TPS;  // KT is a multiple of 4
 
-    u32x4 pf[PF];
-    f32x4 pn;
-    auto gload = [&](int st) {
-        const int t0 = st * TPS;
-        const int nt = min(TPS, KT - t0);
-        const u32x4 *src = cb + (size_t)t0 * TILE_U4;
+    // Global -> LDS copy of stage st (TPS tiles and their norms).  Every wave issues exactly
+    // NCOPY copy instructions, so it can wait for an older stage with a fixed count.
+    auto stage_copy = [&](int st, u32x4 *sc, float *sn) {
+        const u32x4 *src = cb + (size_t)st * STAGE_U4;
 #pragma unroll
         for (int r = 0; r < PF; ++r) {
-            const int i = tid + r * 256;
-            pf[r] = i < nt * TILE_U4 ? src[i] : u32x4{0u, 0u, 0u, 0u};
+            const int chunk = r * ASSIGN_WAVES + w;
+            lds_dma16(src + chunk * 64 + lane, sc + chunk * 64);
         }
-        pn = tid < nt * 8 ? ((const f32x4 *)(nb + (size_t)t0 * 32))[tid] : f32x4{0.f, 0.f, 0.f, 0.f};
+        if (lane < 2 * TPS) lds_dma16(nb + (size_t)st * TPS * 32 + w * TPS * 8 + lane * 4, sn + w * TPS * 8);
     };
-    auto swrite = [&](int buf) {
-#pragma unroll
-        for (int r = 0; r < PF; ++r) s_c[buf][tid + r * 256] = pf[r];
-        if (tid < TPS * 8) ((f32x4 *)s_n[buf])[tid] = pn;
-    };
-
-    gload(0);
-    swrite(0);
-    __syncthreads();
 
     ArgminState st[PB];
 #pragma unroll
     for (int p = 0; p < PB; ++p) argmin_init(st[p]);
 
-    for (int s = 0; s < nst; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < nst) gload(s + 1);
-        const int nt = min(TPS, KT - s * TPS);
-        for (int tt = 0; tt < nt; ++tt) {
-            const int tile = s * TPS + tt;
-            f32x16 acc[PB];
-            {
-                const float *nrm = &s_n[buf][tt * 32 + 4 * h];
-                const f32x4 c0 = *(const f32x4 *)(nrm + 0), c1 = *(const f32x4 *)(nrm + 8);
-                const f32x4 c2 = *(const f32x4 *)(nrm + 16), c3 = *(const f32x4 *)(nrm + 24);
-                const f32x16 cn = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3],
-                                   c2[0], c2[1], c2[2], c2[3], c3[0], c3[1], c3[2], c3[3]};
+    u32x4 f[QG];  // A fragments of the tile being multiplied
+    f32x16 accA[PB], accB[PB];
+    auto load_norms = [&](f32x16 (&acc)[PB], const float *sn, int tt) {
+        const float *nrm = sn + tt * 32 + 4 * h;
+        const f32x4 c0 = *(const f32x4 *)(nrm + 0), c1 = *(const f32x4 *)(nrm + 8);
+        const f32x4 c2 = *(const f32x4 *)(nrm + 16), c3 = *(const f32x4 *)(nrm + 24);
+        const f32x16 cn = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3],
+                           c2[0], c2[1], c2[2], c2[3], c3[0], c3[1], c3[2], c3[3]};
 #pragma unroll
-                for (int p = 0; p < PB; ++p) acc[p] = cn;
-            }
-            const u32x4 *at = &s_c[buf][tt * TILE_U4 + lane];
+        for (int p = 0; p < PB; ++p) acc[p] = cn;
+    };
+    // One tile: multiply f into accC while refilling f with the next tile's fragments; fold
+    // accF (the previous tile), then load the next tile's norms into accF.  After the last
+    // tile the refills read a stale (in-bounds) buffer and are never used: no branches here.
+    auto step = [&](f32x16 (&accC)[PB], f32x16 (&accF)[PB], int tileF, const u32x4 *nsc, const float *nsn,
+                    int ntt) {
 #pragma unroll
-            for (int q = 0; q < QG; ++q) {
-                const u32x4 a = at[q * 64];
+        for (int q = 0; q < QG; ++q) {
 #pragma unroll
-                for (int p = 0; p < PB; ++p) acc[p] = mfma_group<DT>(a, xr[p][q], acc[p]);
-            }
-#pragma unroll
-            for (int p = 0; p < PB; ++p) argmin_fold(st[p], acc[p], tile);
+            for (int p = 0; p < PB; ++p) accC[p] = mfma_group<DT>(f[q], xr[p][q], accC[p]);
+            f[q] = nsc[ntt * TILE_U4 + q * 64 + lane];
         }
-        if (s + 1 < nst) swrite(buf ^ 1);
-        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < PB; ++p) argmin_fold(st[p], accF[p], tileF);
+        load_norms(accF, nsn, ntt);
+    };
+    // Stage s lives in X; stage s+1 in Y (copied earlier); stage s+2 is copied into Z, which
+    // nobody reads any more (its last reads happened before the previous mid-stage barrier).
+    // Tile t = TPS*s + i is multiplied into accA for even i, accB for odd i.
+    auto run_stage = [&](int s, u32x4 *xc, float *xn_, u32x4 *yc, float *yn, u32x4 *zc, float *zn) {
+        const bool copy2 = s + 2 < nst;
+        if (copy2) stage_copy(s + 2, zc, zn);
+        const int t0 = TPS * s;
+#pragma unroll
+        for (int i = 0; i + 2 < TPS; i += 2) {
+            step(accA, accB, t0 + i - 1, xc, xn_, i + 1);
+            step(accB, accA, t0 + i, xc, xn_, i + 2);
+        }
+        step(accA, accB, t0 + TPS - 3, xc, xn_, TPS - 1);  // prefetch the stage's last tile
+        const bool more = s + 1 < nst;
+        if (more) {
+            if (copy2) stage_barrier<NCOPY>();  // stage s+1 landed (this wave), then published
+            else stage_barrier<0>();
+        }
+        step(accB, accA, t0 + TPS - 2, yc, yn, 0);  // last tile; prefetch the next stage's first
+    };
+
+    // prologue: stages 0 and 1 in flight, stage 0 published, tile 0 loaded
+    stage_copy(0, s_c0, s_n0);
+    if (nst > 1) {
+        stage_copy(1, s_c1, s_n1);
+        stage_barrier<NCOPY>();
+    } else {
+        stage_barrier<0>();
     }
+#pragma unroll
+    for (int q = 0; q < QG; ++q) f[q] = s_c0[q * 64 + lane];
+    load_norms(accA, s_n0, 0);
+#pragma unroll
+    for (int p = 0; p < PB; ++p)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) accB[p][r] = __builtin_inff();  // "tile -1": a no-op fold
+
+    for (int s0 = 0; s0 < nst; s0 += 3) {
+        run_stage(s0, s_c0, s_n0, s_c1, s_n1, s_c2, s_n2);
+        if (s0 + 1 < nst) run_stage(s0 + 1, s_c1, s_n1, s_c2, s_n2, s_c0, s_n0);
+        if (s0 + 2 < nst) run_stage(s0 + 2, s_c2, s_n2, s_c0, s_n0, s_c1, s_n1);
+    }
+#pragma unroll
+    for (int p = 0; p < PB; ++p) argmin_fold(st[p], accB[p], KT - 1);
 
 #pragma unroll
     for (int p = 0; p < PB; ++p) {
@@ -347,7 +413,7 @@ __global__ __launch_bounds__(256) void assign_split_d_kernel(const void *__restr
             const int q = rem >> 6, ln = rem & 63;
             const int pt = pbase + pb * 32 + (ln & 31);
             const bool vp = pt < N;
-            const int d0 = (ln >> 5) * (DP / 2) + dc * (BD / 2) + q * VW;
+            const int d0 = dc * BD + (2 * q + (ln >> 5)) * VW;
             pfx[r] = load_x_group<DT>(x, ((size_t)b * N + (vp ? pt : 0)) * D, d0, D, vp);
         }
 #pragma unroll
@@ -414,7 +480,7 @@ __global__ __launch_bounds__(256) void assign_split_d_kernel(const void *__restr
 // ------------------------------------------------------------------------------------------
 hipError_t launch_prep_centroids(int dt, const float *C, void *cprep, float *cnh, int B, int K, int D, int DP,
                                  hipStream_t stream) {
-    const int KT = (K + 31) / 32;
+    const int KT = assign_tiles(K);
     dim3 grid(B * KT), block(256);
     if (dt == DT_F32)
         prep_centroids_kernel<DT_F32><<<grid, block, 0, stream>>>(C, (u32x4 *)cprep, cnh, K, D, DP, KT);
@@ -429,7 +495,7 @@ template <int DT, int DP>
 static hipError_t launch_small(const void *x, const void *cprep, const float *cnh, const float *xn, int32_t *a,
                                float *md, int B, int N, int D, int K, hipStream_t stream) {
     constexpr int PB = small_d_pb(DT, DP);
-    const int KT = (K + 31) / 32;
+    const int KT = assign_tiles(K);
     const int bn = ASSIGN_WAVES * PB * 32;
     const int wpb = (N + bn - 1) / bn;
     assign_small_d_kernel<DT, DP><<<dim3(B * wpb), dim3(256), 0, stream>>>(x, (const u32x4 *)cprep, cnh, xn, a, md,
@@ -447,7 +513,6 @@ static hipError_t launch_small_dt(int DP, const void *x, const void *cprep, cons
             case 32: return launch_small<DT, 32>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
             case 64: return launch_small<DT, 64>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
             case 128: return launch_small<DT, 128>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
-            case 256: return launch_small<DT, 256>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
         }
     } else {
         switch (DP) {
@@ -456,7 +521,6 @@ static hipError_t launch_small_dt(int DP, const void *x, const void *cprep, cons
             case 64: return launch_small<DT, 64>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
             case 128: return launch_small<DT, 128>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
             case 256: return launch_small<DT, 256>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
-            case 512: return launch_small<DT, 512>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
         }
     }
     return hipErrorInvalidValue;
@@ -469,7 +533,7 @@ hipError_t launch_assign(int dt, const AssignCfg &cfg, const void *x, const void
         if (dt == DT_F16) return launch_small_dt<DT_F16>(cfg.d_pad, x, cprep, cnh, xn, a, md, B, N, D, K, s);
         return launch_small_dt<DT_BF16>(cfg.d_pad, x, cprep, cnh, xn, a, md, B, N, D, K, s);
     }
-    const int KT = (K + 31) / 32;
+    const int KT = assign_tiles(K);
     const int bn = ASSIGN_WAVES * 32;
     const int wpb = (N + bn - 1) / bn;
     dim3 grid(B * wpb), block(256);

@@ -6,9 +6,10 @@
 // Assign, small-D path (x tile kept in VGPRs for the whole centroid scan):
 //   * D is padded to DP in {16,...,512} (2-byte types) or {8,...,256} (fp32): the MFMA k-step
 //     is 16 (bf16/fp16 32x32x16) or 2 (fp32 32x32x2), and each lane holds half of every row.
-//   * VGPRs per lane ~= PB * (x: DP*s/8 + acc 16 + best 16) + prefetch 32 + c-norm 16 + 32.
-//     PB (32-point blocks per wave) is the largest of {4,2,1} keeping this <= 256, so two
-//     waves share a SIMD: one wave's compare/select work overlaps the other's MFMA.
+//   * VGPRs per lane ~= PB * (x: DP*s/8 + two accumulator sets 32 + best 16) + prefetch 32
+//     + c-norm 16 + 32.  PB (32-point blocks per wave) is the largest of {2,1} keeping this
+//     <= 256, so two waves share a SIMD.  Within a wave the MFMAs of tile t+1 are interleaved
+//     with the arg-min selects of tile t (two accumulator sets).
 //   * Centroid stages of 32 KiB ping-pong in LDS: 2 x (32 KiB + norms) = 72 KiB per
 //     workgroup, two workgroups per CU within 160 KiB.
 //   * Every workgroup re-reads all K centroids from L2: the arithmetic intensity of that
@@ -61,7 +62,7 @@ AssignCfg plan_assign(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
         c.bd = 0;
         c.block_n = ASSIGN_WAVES * c.pb * 32;
         c.lds = 2 * (c.tps * 32 * dp * s + c.tps * 32 * 4);
-        c.vgpr = c.pb * (dp * s / 8 + 32) + 32 + 16 + 32;
+        c.vgpr = c.pb * (dp * s / 8 + 48) + 32 + 16 + 32;
     } else {
         const int bd = splitd_bd(dt);
         c.path = 1;

@@ -58,16 +58,20 @@ SortCfg plan_sort(int64_t N, int64_t K);
 UpdCfg plan_update(int dt, int64_t B, int64_t N, int64_t D);
 
 // Small-D register tile chosen for (dtype, padded D); shared with the kernel templates.
-constexpr int small_d_pb(int dt, int dp) {
-    return dt == 0 ? (dp <= 16 ? 4 : (dp <= 64 ? 2 : 1))
-                   : (dp <= 32 ? 4 : (dp <= 128 ? 2 : 1));
-}
+constexpr int small_d_pb(int dt, int dp) { return dt == 0 ? (dp <= 32 ? 2 : 1) : (dp <= 128 ? 2 : 1); }
+// Tiles per LDS stage: up to 32 KiB of centroids, between 2 and 8 tiles.
 constexpr int small_d_tps(int dt, int dp) {
-    return STAGE_BYTES / (32 * dp * (dt == 0 ? 4 : 2)) > 0 ? STAGE_BYTES / (32 * dp * (dt == 0 ? 4 : 2)) : 1;
+    return STAGE_BYTES / (32 * dp * (dt == 0 ? 4 : 2)) > 8   ? 8
+           : STAGE_BYTES / (32 * dp * (dt == 0 ? 4 : 2)) > 2 ? STAGE_BYTES / (32 * dp * (dt == 0 ? 4 : 2))
+                                                              : 2;
 }
 constexpr int splitd_bd(int dt) { return dt == 0 ? 32 : 64; }
 
+// 32-centroid tiles per problem in the prepared layout: padded to a multiple of 4 so the
+// assign kernels can stream whole stages of 2 or 4 tiles (padding tiles score +inf).
+inline int assign_tiles(int64_t K) { return 4 * (int)((K + 127) / 128); }
+
 // Largest D handled by the small-D path (x tile kept in registers).
-constexpr int small_d_max(int dt) { return dt == 0 ? 256 : 512; }
+constexpr int small_d_max(int dt) { return dt == 0 ? 128 : 256; }
 
 }  // namespace fkm
