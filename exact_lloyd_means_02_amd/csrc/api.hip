@@ -15,20 +15,23 @@ namespace fkm {
 hipError_t launch_prep_centroids(int dt, const float *C, void *cprep, float *cnh, int B, int K, int D, int DP,
                                  hipStream_t stream);
 hipError_t launch_assign(int dt, const AssignCfg &cfg, const void *x, const void *cprep, const float *cnh,
-                         const float *xn, int32_t *a, float *md, int B, int N, int D, int K, hipStream_t s);
+                         const float *xn, int32_t *a, float *md, double *wgi, int B, int N, int D, int K,
+                         hipStream_t s);
 size_t sort_ws_bytes(int64_t B, int64_t N, int64_t K);
 hipError_t launch_argsort(const int32_t *keys, int B, int N, int K, int32_t *out_keys, int32_t *out_vals,
                           int32_t *counts, void *ws, hipStream_t s);
 hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s);
 size_t update_ws_bytes(int dt, int64_t B, int64_t N, int64_t D, int64_t K);
+bool update_refreshes_prep(int dt, int64_t B, int64_t N, int64_t D);
 hipError_t launch_update(int dt, const void *x, const int32_t *sids, const int32_t *sidx, const int32_t *counts,
-                         int B, int N, int D, int K, int mode, float *C, float *sums, int32_t *cnt, void *ws,
-                         float **shiftk_out, int *ncb_out, hipStream_t s);
-hipError_t launch_finalize_acc(const float *sums, const int32_t *cnt, float *C, float *shiftk, int B, int K, int D,
-                               hipStream_t s);
+                         int B, int N, int D, int K, int mode, float *C, double *shift, float *sums, int32_t *cnt,
+                         const UpdRefresh &ref, void *ws, hipStream_t s);
+hipError_t launch_finalize_acc(int dt, const float *sums, const int32_t *cnt, float *C, double *shift, double *shk,
+                               const UpdRefresh &ref, int B, int K, int D, hipStream_t s);
 hipError_t launch_row_norms(int dt, const void *x, float *out, int64_t rows, int D, hipStream_t s);
 size_t reduce_ws_bytes(int64_t B);
 hipError_t launch_sum_f32(const float *v, int B, int64_t n, double *out, int accumulate, void *ws, hipStream_t s);
+hipError_t launch_sum_f64_rows(const double *part, int rows, int64_t len, double *out, hipStream_t s);
 }  // namespace fkm
 
 using namespace fkm;
@@ -58,7 +61,7 @@ km_status_t ok() { return KM_OK; }
 constexpr int64_t MAX_N = (int64_t)1 << 31;
 constexpr int64_t MAX_D = 4096;
 constexpr int64_t MAX_K = (int64_t)1 << 24;
-constexpr int RING = 256;  // iterations of inertia / shift kept on the device between host reads
+constexpr int RING = 16;  // iterations of inertia / shift kept on the device between host reads
 constexpr int64_t DEFAULT_CHUNK = (int64_t)1 << 24;
 
 bool dt_ok(int dt) { return dt == KM_F32 || dt == KM_F16 || dt == KM_BF16; }
@@ -98,44 +101,40 @@ size_t assign_ws(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
 
 size_t argsort_ws(int64_t B, int64_t N, int64_t K) { return sort_ws_bytes(B, N, K); }
 
-size_t update_ws(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
-    return update_ws_bytes(dt, B, N, D, K) + reduce_ws_bytes(B);
-}
+size_t update_ws(int dt, int64_t B, int64_t N, int64_t D, int64_t K) { return update_ws_bytes(dt, B, N, D, K); }
 
-size_t stage_max(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
-    size_t m = assign_ws(dt, B, N, D, K);
-    const size_t s2 = argsort_ws(B, N, K), s3 = update_ws(dt, B, N, D, K);
-    if (s2 > m) m = s2;
-    if (s3 > m) m = s3;
-    return m;
+int64_t assign_wgs_per_problem(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
+    return ceil_div(N, plan_assign(dt, B, N, D, K).block_n);
 }
 
 struct FitLayout {
-    size_t xn, md, a, sids, sidx, counts, ring_j, ring_s, red, stage, total;
+    size_t xn, a, sids, sidx, counts, prep, ring_part, ring_j, ring_s, scratch, total;
 };
 
-// Device-resident x.
+// Device-resident x.  The prepared centroids persist across iterations (the update refreshes
+// them); the arg-sort and update scratch share one region.
 FitLayout fit_layout(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
     FitLayout L{};
     size_t o = 0;
     const size_t bn4 = align256((size_t)B * N * 4);
     L.xn = o; o += bn4;
-    L.md = o; o += bn4;
     L.a = o; o += bn4;
     L.sids = o; o += bn4;
     L.sidx = o; o += bn4;
     L.counts = o; o += align256((size_t)B * K * 4);
+    L.prep = o; o += assign_ws(dt, B, N, D, K);
+    L.ring_part = o; o += align256((size_t)RING * B * assign_wgs_per_problem(dt, B, N, D, K) * 8);
     L.ring_j = o; o += align256((size_t)RING * B * 8);
     L.ring_s = o; o += align256((size_t)RING * B * 8);
-    L.red = o; o += reduce_ws_bytes(B);
-    L.stage = o; o += stage_max(dt, B, N, D, K);
+    L.scratch = o;
+    const size_t s2 = argsort_ws(B, N, K), s3 = update_ws(dt, B, N, D, K);
+    o += s2 > s3 ? s2 : s3;
     L.total = o;
     return L;
 }
 
 struct HostLayout {
-    size_t stage_buf[2], cprep, xn, md, a, sids, sidx, counts, sums, cnt, ring_j, ring_s, red, shiftk, scratch,
-        total;
+    size_t stage_buf[2], cprep, xn, md, a, sids, sidx, counts, sums, cnt, shk, ring_j, ring_s, red, scratch, total;
     int64_t chunk;
 };
 
@@ -164,10 +163,10 @@ HostLayout host_layout(int dt, int64_t B, int64_t N, int64_t D, int64_t K, int64
     L.counts = o; o += align256((size_t)K * 4);
     L.sums = o; o += align256((size_t)B * K * D * 4);
     L.cnt = o; o += align256((size_t)B * K * 4);
+    L.shk = o; o += align256((size_t)B * K * 8);
     L.ring_j = o; o += align256((size_t)RING * B * 8);
     L.ring_s = o; o += align256((size_t)RING * B * 8);
     L.red = o; o += reduce_ws_bytes(B);
-    L.shiftk = o; o += align256((size_t)B * K * 4);
     L.scratch = o;
     size_t sc = argsort_ws(1, c, K);
     const size_t u = update_ws(dt, 1, c, D, K);
@@ -234,20 +233,14 @@ km_status_t do_assign(int dt, const void *x, const float *C, int64_t B, int64_t 
     char *cprep = (char *)ws;
     float *cnh = (float *)(cprep + align256((size_t)B * KT * 32 * cfg.d_pad * elem_bytes(dt)));
     KM_HIP(launch_prep_centroids(dt, C, cprep, cnh, (int)B, (int)K, (int)D, cfg.d_pad, s));
-    KM_HIP(launch_assign(dt, cfg, x, cprep, cnh, xn, a, md, (int)B, (int)N, (int)D, (int)K, s));
+    KM_HIP(launch_assign(dt, cfg, x, cprep, cnh, xn, a, md, nullptr, (int)B, (int)N, (int)D, (int)K, s));
     return ok();
 }
 
 km_status_t do_update(int dt, const void *x, const int32_t *sids, const int32_t *sidx, const int32_t *counts,
                       int64_t B, int64_t N, int64_t D, int64_t K, float *C, double *shift, void *ws, hipStream_t s) {
-    float *shiftk = nullptr;
-    int ncb = 1;
-    KM_HIP(launch_update(dt, x, sids, sidx, counts, (int)B, (int)N, (int)D, (int)K, 0, C, nullptr, nullptr, ws,
-                         &shiftk, &ncb, s));
-    if (shift) {
-        void *red = (char *)ws + update_ws_bytes(dt, B, N, D, K);
-        KM_HIP(launch_sum_f32(shiftk, (int)B, (int64_t)ncb * K, shift, 0, red, s));
-    }
+    KM_HIP(launch_update(dt, x, sids, sidx, counts, (int)B, (int)N, (int)D, (int)K, 0, C, shift, nullptr, nullptr,
+                         UpdRefresh{}, ws, s));
     return ok();
 }
 
@@ -396,24 +389,37 @@ km_status_t read_shift_max(const double *dev, int64_t B, double *out, hipStream_
 km_status_t fit_device(int dt, const void *x, int64_t B, int64_t N, int64_t D, int64_t K, int iters, float tol,
                        float *C, int32_t *assign, double *inertia, int32_t *iters_done, char *ws, hipStream_t s) {
     const FitLayout L = fit_layout(dt, B, N, D, K);
+    const AssignCfg cfg = plan_assign(dt, B, N, D, K);
+    const int64_t KT = assign_tiles(K);
+    const int64_t wpb = assign_wgs_per_problem(dt, B, N, D, K);
     float *xn = (float *)(ws + L.xn);
-    float *md = (float *)(ws + L.md);
     int32_t *a = assign ? assign : (int32_t *)(ws + L.a);
     int32_t *sids = (int32_t *)(ws + L.sids);
     int32_t *sidx = (int32_t *)(ws + L.sidx);
     int32_t *counts = (int32_t *)(ws + L.counts);
+    char *cprep = ws + L.prep;
+    float *cnh = (float *)(cprep + align256((size_t)B * KT * 32 * cfg.d_pad * elem_bytes(dt)));
+    double *ring_part = (double *)(ws + L.ring_part);
     double *ring_j = (double *)(ws + L.ring_j);
     double *ring_s = (double *)(ws + L.ring_s);
-    void *red = ws + L.red;
-    void *stage = ws + L.stage;
+    void *scratch = ws + L.scratch;
+    const bool fused_prep = update_refreshes_prep(dt, B, N, D);
+    const UpdRefresh ref = fused_prep ? UpdRefresh{cprep, cnh, cfg.d_pad, (int)KT} : UpdRefresh{};
+
     KM_HIP(launch_row_norms(dt, x, xn, B * N, (int)D, s));
+    KM_HIP(launch_prep_centroids(dt, C, cprep, cnh, (int)B, (int)K, (int)D, cfg.d_pad, s));
     int done = 0, flushed = 0;
     for (int t = 0; t < iters; ++t) {
         const int slot = t - flushed;
-        KM_TRY(do_assign(dt, x, C, B, N, D, K, xn, a, md, stage, s));
-        KM_HIP(launch_sum_f32(md, (int)B, N, ring_j + (size_t)slot * B, 0, red, s));
-        KM_HIP(launch_argsort(a, (int)B, (int)N, (int)K, sids, sidx, counts, stage, s));
-        KM_TRY(do_update(dt, x, sids, sidx, counts, B, N, D, K, C, ring_s + (size_t)slot * B, stage, s));
+        // one iteration: assign (+ per-workgroup inertia partials), arg-sort, update (+ shift,
+        // + the next iteration's prepared centroids)
+        KM_HIP(launch_assign(dt, cfg, x, cprep, cnh, xn, a, nullptr, ring_part + (size_t)slot * B * wpb, (int)B,
+                             (int)N, (int)D, (int)K, s));
+        KM_HIP(launch_argsort(a, (int)B, (int)N, (int)K, sids, sidx, counts, scratch, s));
+        KM_HIP(launch_update(dt, x, sids, sidx, counts, (int)B, (int)N, (int)D, (int)K, 0, C,
+                             tol > 0.f ? ring_s + (size_t)slot * B : nullptr, nullptr, nullptr, ref, scratch, s));
+        if (!fused_prep && t + 1 < iters)
+            KM_HIP(launch_prep_centroids(dt, C, cprep, cnh, (int)B, (int)K, (int)D, cfg.d_pad, s));
         done = t + 1;
         bool stop = false;
         if (tol > 0.f) {
@@ -422,6 +428,7 @@ km_status_t fit_device(int dt, const void *x, int64_t B, int64_t N, int64_t D, i
             stop = smax < (double)tol;
         }
         if (slot + 1 == RING || stop || t + 1 == iters) {
+            KM_HIP(launch_sum_f64_rows(ring_part, (slot + 1) * (int)B, wpb, ring_j, s));
             KM_TRY(ring_to_host(ring_j, inertia, flushed, slot + 1, B, s));
             flushed = t + 1;
         }
@@ -470,8 +477,8 @@ km_status_t fit_host(int dt, const void *xh, int64_t B, int64_t N, int64_t D, in
     double *ring_j = (double *)(ws + L.ring_j);
     double *ring_s = (double *)(ws + L.ring_s);
     void *red = ws + L.red;
-    float *shiftk = (float *)(ws + L.shiftk);
     void *scratch = ws + L.scratch;
+    const UpdRefresh ref{cprep, cnh, cfg.d_pad, (int)KT};
 
     StreamedPipe P;
     KM_HIP(hipStreamCreateWithFlags(&P.cs, hipStreamNonBlocking));
@@ -501,11 +508,11 @@ km_status_t fit_host(int dt, const void *xh, int64_t B, int64_t N, int64_t D, in
     KM_HIP(hipEventRecord(P.ev_free[0], s));
     KM_HIP(hipEventRecord(P.ev_free[1], s));
     KM_TRY(issue_copy(0));
+    KM_HIP(launch_prep_centroids(dt, C, cprep, cnh, (int)B, (int)K, (int)D, cfg.d_pad, s));
     int64_t q = 0;
     int done = 0, flushed = 0;
     for (int t = 0; t < iters; ++t) {
         const int slot = t - flushed;
-        KM_HIP(launch_prep_centroids(dt, C, cprep, cnh, (int)B, (int)K, (int)D, cfg.d_pad, s));
         KM_HIP(launch_fill_i32((int32_t *)sums, B * K * D, 0, s));
         KM_HIP(launch_fill_i32(cnt, B * K, 0, s));
         KM_HIP(launch_fill_i32((int32_t *)(ring_j + (size_t)slot * B), 2 * B, 0, s));
@@ -520,15 +527,15 @@ km_status_t fit_host(int dt, const void *xh, int64_t B, int64_t N, int64_t D, in
             int32_t *ac = assign ? assign + (size_t)b * N + lo : a_ws;
             KM_HIP(launch_row_norms(dt, xc, xn, n, (int)D, s));
             KM_HIP(launch_assign(dt, cfg, xc, cprep + (size_t)b * cprep_per_b, cnh + (size_t)b * KT * 32, xn, ac, md,
-                                 1, (int)n, (int)D, (int)K, s));
+                                 nullptr, 1, (int)n, (int)D, (int)K, s));
             KM_HIP(launch_sum_f32(md, 1, n, ring_j + (size_t)slot * B + b, 1, red, s));
             KM_HIP(launch_argsort(ac, 1, (int)n, (int)K, sids, sidx, counts, scratch, s));
-            KM_HIP(launch_update(dt, xc, sids, sidx, counts, 1, (int)n, (int)D, (int)K, 1, nullptr,
-                                 sums + (size_t)b * K * D, cnt + (size_t)b * K, scratch, nullptr, nullptr, s));
+            KM_HIP(launch_update(dt, xc, sids, sidx, counts, 1, (int)n, (int)D, (int)K, 1, nullptr, nullptr,
+                                 sums + (size_t)b * K * D, cnt + (size_t)b * K, UpdRefresh{}, scratch, s));
             KM_HIP(hipEventRecord(P.ev_free[buf], s));
         }
-        KM_HIP(launch_finalize_acc(sums, cnt, C, shiftk, (int)B, (int)K, (int)D, s));
-        KM_HIP(launch_sum_f32(shiftk, (int)B, K, ring_s + (size_t)slot * B, 0, red, s));
+        KM_HIP(launch_finalize_acc(dt, sums, cnt, C, tol > 0.f ? ring_s + (size_t)slot * B : nullptr,
+                                   (double *)(ws + L.shk), ref, (int)B, (int)K, (int)D, s));
         done = t + 1;
         bool stop = false;
         if (tol > 0.f) {

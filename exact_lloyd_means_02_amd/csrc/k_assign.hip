@@ -177,8 +177,8 @@ __device__ inline void argmin_fold(ArgminState &s, const f32x16 &acc, int tile) 
 // Resolve the winning centroid of this lane, merge with the partner lane (lane ^ 32, same
 // point, the other 16 rows of every tile) and write.  Accumulator r of lane (j, h) holds row
 // 8*(r/4) + 4*h + (r%4) of the 32-centroid tile (MFMA 32x32 output layout).
-__device__ inline void argmin_finish(const ArgminState &s, int h, bool write, int64_t out_i, int32_t *out_a,
-                                     float *out_d, const float *xnorm) {
+__device__ inline float argmin_finish(const ArgminState &s, int h, bool write, int64_t out_i, int32_t *out_a,
+                                      float *out_d, const float *xnorm, bool want_d) {
     int slot = 15;
 #pragma unroll
     for (int r = 15; r >= 0; --r) slot = (s.best[r] == s.run_min) ? r : slot;
@@ -190,9 +190,30 @@ __device__ inline void argmin_finish(const ArgminState &s, int h, bool write, in
         sc = osc;
         k = ok;
     }
+    float d = 0.f;
     if (write) {
         out_a[out_i] = k;
-        if (out_d) out_d[out_i] = xnorm[out_i] + 2.0f * sc;
+        if (want_d) {
+            d = xnorm[out_i] + 2.0f * sc;  // squared distance to the chosen centroid (fp32)
+            if (out_d) out_d[out_i] = d;
+        }
+    }
+    return d;
+}
+
+// Sum of the workgroup's point distances in fp64, fixed order (lanes, then waves); thread 0
+// writes it.  Feeds the per-iteration inertia without a pass over min_dist.
+__device__ inline void workgroup_inertia(double v, double *dst) {
+    __shared__ double s_w[ASSIGN_WAVES];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double t = 0.0;
+#pragma unroll
+        for (int i = 0; i < ASSIGN_WAVES; ++i) t += s_w[i];
+        *dst = t;
     }
 }
 
@@ -231,6 +252,7 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
                                                              const float *__restrict__ cnh,
                                                              const float *__restrict__ xnorm,
                                                              int32_t *__restrict__ out_a, float *__restrict__ out_d,
+                                                             double *__restrict__ wg_inertia,
                                                              int N, int D, int KT, int wgs_per_b) {
     constexpr int S = DT == DT_F32 ? 4 : 2;
     constexpr int VW = 16 / S;
@@ -357,11 +379,14 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
 #pragma unroll
     for (int p = 0; p < PB; ++p) argmin_fold(st[p], accB[p], KT - 1);
 
+    const bool want_d = out_d != nullptr || wg_inertia != nullptr;
+    double dsum = 0.0;
 #pragma unroll
     for (int p = 0; p < PB; ++p) {
         const int pt = pbase + p * 32 + j;
-        argmin_finish(st[p], h, h == 0 && pt < N, (int64_t)b * N + pt, out_a, out_d, xnorm);
+        dsum += argmin_finish(st[p], h, h == 0 && pt < N, (int64_t)b * N + pt, out_a, out_d, xnorm, want_d);
     }
+    if (wg_inertia) workgroup_inertia(dsum, wg_inertia + (size_t)b * wgs_per_b + tn);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -376,6 +401,7 @@ __global__ __launch_bounds__(256) void assign_split_d_kernel(const void *__restr
                                                              const float *__restrict__ cnh,
                                                              const float *__restrict__ xnorm,
                                                              int32_t *__restrict__ out_a, float *__restrict__ out_d,
+                                                             double *__restrict__ wg_inertia,
                                                              int N, int D, int DP, int KT, int wgs_per_b) {
     constexpr int S = DT == DT_F32 ? 4 : 2;
     constexpr int VW = 16 / S;
@@ -472,7 +498,9 @@ __global__ __launch_bounds__(256) void assign_split_d_kernel(const void *__restr
         __syncthreads();
     }
     const int pt = pbase + w * 32 + (lane & 31);
-    argmin_finish(st, h, h == 0 && pt < N, (int64_t)b * N + pt, out_a, out_d, xnorm);
+    const float d = argmin_finish(st, h, h == 0 && pt < N, (int64_t)b * N + pt, out_a, out_d, xnorm,
+                                  out_d != nullptr || wg_inertia != nullptr);
+    if (wg_inertia) workgroup_inertia((double)d, wg_inertia + (size_t)b * wgs_per_b + tn);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -493,58 +521,60 @@ hipError_t launch_prep_centroids(int dt, const float *C, void *cprep, float *cnh
 
 template <int DT, int DP>
 static hipError_t launch_small(const void *x, const void *cprep, const float *cnh, const float *xn, int32_t *a,
-                               float *md, int B, int N, int D, int K, hipStream_t stream) {
+                               float *md, double *wgi, int B, int N, int D, int K, hipStream_t stream) {
     constexpr int PB = small_d_pb(DT, DP);
     const int KT = assign_tiles(K);
     const int bn = ASSIGN_WAVES * PB * 32;
     const int wpb = (N + bn - 1) / bn;
     assign_small_d_kernel<DT, DP><<<dim3(B * wpb), dim3(256), 0, stream>>>(x, (const u32x4 *)cprep, cnh, xn, a, md,
-                                                                           N, D, KT, wpb);
+                                                                           wgi, N, D, KT, wpb);
     return hipGetLastError();
 }
 
 template <int DT>
 static hipError_t launch_small_dt(int DP, const void *x, const void *cprep, const float *cnh, const float *xn,
-                                  int32_t *a, float *md, int B, int N, int D, int K, hipStream_t s) {
+                                  int32_t *a, float *md, double *wgi, int B, int N, int D, int K, hipStream_t s) {
     if constexpr (DT == DT_F32) {
         switch (DP) {
-            case 8: return launch_small<DT, 8>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
-            case 16: return launch_small<DT, 16>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
-            case 32: return launch_small<DT, 32>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
-            case 64: return launch_small<DT, 64>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
-            case 128: return launch_small<DT, 128>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
+            case 8: return launch_small<DT, 8>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
+            case 16: return launch_small<DT, 16>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
+            case 32: return launch_small<DT, 32>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
+            case 64: return launch_small<DT, 64>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
+            case 128: return launch_small<DT, 128>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
         }
     } else {
         switch (DP) {
-            case 16: return launch_small<DT, 16>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
-            case 32: return launch_small<DT, 32>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
-            case 64: return launch_small<DT, 64>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
-            case 128: return launch_small<DT, 128>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
-            case 256: return launch_small<DT, 256>(x, cprep, cnh, xn, a, md, B, N, D, K, s);
+            case 16: return launch_small<DT, 16>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
+            case 32: return launch_small<DT, 32>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
+            case 64: return launch_small<DT, 64>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
+            case 128: return launch_small<DT, 128>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
+            case 256: return launch_small<DT, 256>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
         }
     }
     return hipErrorInvalidValue;
 }
 
+// wgi (optional): per-workgroup fp64 sums of the chosen distances, [B][assign_wgs_per_problem].
 hipError_t launch_assign(int dt, const AssignCfg &cfg, const void *x, const void *cprep, const float *cnh,
-                         const float *xn, int32_t *a, float *md, int B, int N, int D, int K, hipStream_t s) {
+                         const float *xn, int32_t *a, float *md, double *wgi, int B, int N, int D, int K,
+                         hipStream_t s) {
     if (cfg.path == 0) {
-        if (dt == DT_F32) return launch_small_dt<DT_F32>(cfg.d_pad, x, cprep, cnh, xn, a, md, B, N, D, K, s);
-        if (dt == DT_F16) return launch_small_dt<DT_F16>(cfg.d_pad, x, cprep, cnh, xn, a, md, B, N, D, K, s);
-        return launch_small_dt<DT_BF16>(cfg.d_pad, x, cprep, cnh, xn, a, md, B, N, D, K, s);
+        if (dt == DT_F32) return launch_small_dt<DT_F32>(cfg.d_pad, x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
+        if (dt == DT_F16) return launch_small_dt<DT_F16>(cfg.d_pad, x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
+        return launch_small_dt<DT_BF16>(cfg.d_pad, x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
     }
     const int KT = assign_tiles(K);
     const int bn = ASSIGN_WAVES * 32;
     const int wpb = (N + bn - 1) / bn;
     dim3 grid(B * wpb), block(256);
     if (dt == DT_F32)
-        assign_split_d_kernel<DT_F32><<<grid, block, 0, s>>>(x, (const u32x4 *)cprep, cnh, xn, a, md, N, D, cfg.d_pad,
-                                                             KT, wpb);
+        assign_split_d_kernel<DT_F32><<<grid, block, 0, s>>>(x, (const u32x4 *)cprep, cnh, xn, a, md, wgi, N, D,
+                                                             cfg.d_pad, KT, wpb);
     else if (dt == DT_F16)
-        assign_split_d_kernel<DT_F16><<<grid, block, 0, s>>>(x, (const u32x4 *)cprep, cnh, xn, a, md, N, D, cfg.d_pad,
-                                                             KT, wpb);
+        assign_split_d_kernel<DT_F16><<<grid, block, 0, s>>>(x, (const u32x4 *)cprep, cnh, xn, a, md, wgi, N, D,
+                                                             cfg.d_pad, KT, wpb);
     else
-        assign_split_d_kernel<DT_BF16><<<grid, block, 0, s>>>(x, (const u32x4 *)cprep, cnh, xn, a, md, N, D,
+        assign_split_d_kernel<DT_BF16><<<grid, block, 0, s>>>(x, (const u32x4 *)cprep, cnh, xn, a, md, wgi, N, D,
                                                               cfg.d_pad, KT, wpb);
     return hipGetLastError();
 }

@@ -95,6 +95,28 @@ __global__ void sum_level2_kernel(const double *__restrict__ part, double *__res
 
 size_t reduce_ws_bytes(int64_t B) { return align256((size_t)B * RED_BLOCKS * 8); }
 
+// out[r] = sum_j part[r * len + j] (fp64), one workgroup per row, fixed order.
+__global__ __launch_bounds__(256) void sum_f64_rows_kernel(const double *__restrict__ part, int64_t len,
+                                                           double *__restrict__ out) {
+    __shared__ double s[256];
+    const double *p = part + (size_t)blockIdx.x * len;
+    double acc = 0.0;
+    for (int64_t i = threadIdx.x; i < len; i += 256) acc += p[i];
+    s[threadIdx.x] = acc;
+    __syncthreads();
+    for (int off = 128; off >= 1; off >>= 1) {
+        if ((int)threadIdx.x < off) s[threadIdx.x] += s[threadIdx.x + off];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[blockIdx.x] = s[0];
+}
+
+hipError_t launch_sum_f64_rows(const double *part, int rows, int64_t len, double *out, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    sum_f64_rows_kernel<<<dim3(rows), dim3(256), 0, s>>>(part, len, out);
+    return hipGetLastError();
+}
+
 // out[b] = sum_i v[b*n + i] (fp64), or out[b] += ... when accumulate.
 hipError_t launch_sum_f32(const float *v, int B, int64_t n, double *out, int accumulate, void *ws, hipStream_t s) {
     double *part = (double *)ws;

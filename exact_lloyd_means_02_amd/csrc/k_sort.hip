@@ -35,42 +35,59 @@ __global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t *__restric
     for (int i = threadIdx.x; i < bins; i += 256) hb[(size_t)i * ntiles + t] = s_h[i];
 }
 
-// Exclusive scan of one problem's [bins][tiles] table, in place.
-__global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t *__restrict__ hist, int entries) {
-    __shared__ int32_t s_part[1024];
-    int32_t *hb = hist + (size_t)blockIdx.x * entries;
-    const int per = (entries + 1023) / 1024;
-    const int lo = min(entries, threadIdx.x * per), hi = min(entries, lo + per);
-    int32_t sum = 0;
-    for (int i = lo; i < hi; ++i) sum += hb[i];
-    s_part[threadIdx.x] = sum;
-    __syncthreads();
-    // Hillis-Steele inclusive scan over the 1024 partial sums
-    for (int off = 1; off < 1024; off <<= 1) {
-        const int32_t v = threadIdx.x >= off ? s_part[threadIdx.x - off] : 0;
-        __syncthreads();
-        s_part[threadIdx.x] += v;
-        __syncthreads();
-    }
-    int32_t run = s_part[threadIdx.x] - sum;
-    for (int i = lo; i < hi; ++i) {
-        const int32_t v = hb[i];
-        hb[i] = run;
-        run += v;
-    }
-}
+// Exclusive scan of one problem's [bins][tiles] table, in place.  1024 threads; each pass
+// covers 1024 x 8 consecutive entries (8 independent loads per thread), scanned with wave
+// shuffles and one LDS step, carried to the next pass.
+constexpr int SCAN_ITEMS = 8;
 
-// Per-bin totals of a scanned table (= counts per cluster when one digit is the whole id).
-__global__ __launch_bounds__(256) void counts_from_offsets_kernel(const int32_t *__restrict__ hist, int entries,
-                                                                  int ntiles, int K, int N,
-                                                                  int32_t *__restrict__ counts) {
-    const int b = blockIdx.y;
-    const int k = blockIdx.x * 256 + threadIdx.x;
-    if (k >= K) return;
-    const int32_t *hb = hist + (size_t)b * entries;
-    const int32_t start = hb[(size_t)k * ntiles];
-    const int32_t end = (k + 1) * ntiles < entries ? hb[(size_t)(k + 1) * ntiles] : N;
-    counts[(size_t)b * K + k] = end - start;
+// When `counts` is given (single pass: the digit is the whole id) it also writes the per-bin
+// totals for bins < K from the scanned table.
+__global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t *__restrict__ hist, int entries, int ntiles,
+                                                         int32_t *__restrict__ counts, int K, int N) {
+    __shared__ int32_t s_wave[16];
+    __shared__ int32_t s_carry;
+    int32_t *hb = hist + (size_t)blockIdx.x * entries;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    if (t == 0) s_carry = 0;
+    __syncthreads();
+    for (int base = 0; base < entries; base += 1024 * SCAN_ITEMS) {
+        const int lo = base + t * SCAN_ITEMS;
+        int32_t v[SCAN_ITEMS];
+#pragma unroll
+        for (int i = 0; i < SCAN_ITEMS; ++i) v[i] = lo + i < entries ? hb[lo + i] : 0;
+        int32_t sum = 0;
+#pragma unroll
+        for (int i = 0; i < SCAN_ITEMS; ++i) sum += v[i];
+        // inclusive scan of the thread sums within the wave
+        int32_t inc = sum;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int32_t o = __shfl_up(inc, off);
+            if (lane >= off) inc += o;
+        }
+        if (lane == 63) s_wave[w] = inc;
+        __syncthreads();
+        int32_t wbase = 0;
+        for (int i = 0; i < w; ++i) wbase += s_wave[i];
+        int32_t run = s_carry + wbase + inc - sum;
+#pragma unroll
+        for (int i = 0; i < SCAN_ITEMS; ++i) {
+            if (lo + i < entries) hb[lo + i] = run;
+            run += v[i];
+        }
+        __syncthreads();
+        if (t == 1023) s_carry = run;
+        __syncthreads();
+    }
+    if (counts) {
+        // the table written above by this workgroup is visible after the barrier
+        int32_t *cb = counts + (size_t)blockIdx.x * K;
+        for (int k = t; k < K; k += 1024) {
+            const int32_t start = hb[(size_t)k * ntiles];
+            const int32_t end = (k + 1) * ntiles < entries ? hb[(size_t)(k + 1) * ntiles] : N;
+            cb[k] = end - start;
+        }
+    }
 }
 
 // Stable scatter of one pass.  vals_in == NULL means the values are the point indices.
@@ -204,10 +221,8 @@ hipError_t launch_argsort(const int32_t *keys, int B, int N, int K, int32_t *out
         int32_t *ko = to_out ? out_keys : tk;
         int32_t *vo = to_out ? out_vals : tv;
         sort_hist_kernel<<<dim3(B * c.ntiles), dim3(256), c.bins * 4, s>>>(kin, N, c.ntiles, shift, c.bins, hist);
-        sort_scan_kernel<<<dim3(B), dim3(1024), 0, s>>>(hist, entries);
-        if (counts && c.passes == 1)
-            counts_from_offsets_kernel<<<dim3((K + 255) / 256, B), dim3(256), 0, s>>>(hist, entries, c.ntiles, K, N,
-                                                                                   counts);
+        sort_scan_kernel<<<dim3(B), dim3(1024), 0, s>>>(hist, entries, c.ntiles,
+                                                        (counts && c.passes == 1) ? counts : nullptr, K, N);
         sort_scatter_kernel<<<dim3(B * c.ntiles), dim3(256), (SORT_WAVES + 1) * c.bins * 4, s>>>(
             kin, vin, hist, N, c.ntiles, shift, c.bits, ko, vo);
         kin = ko;

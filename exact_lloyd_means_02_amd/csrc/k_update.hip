@@ -16,20 +16,94 @@
 
 namespace fkm {
 
-constexpr int UPD_UNROLL = 4;
+hipError_t launch_sum_f64_rows(const double *part, int rows, int64_t len, double *out, hipStream_t s);
+
+// Row loads issued before any is consumed: 16 vectors per lane in flight (16 KiB per wave).
+template <int VPL>
+constexpr int upd_unroll() { return 16 / VPL; }
 
 struct UpdArgs {
     const void *x;
     const int32_t *sids, *sidx, *counts;
     int N, D, K, R, nch, lanes, ncb, cb_elems;
     int mode;          // 0: finish c_k in place; 1: accumulate into sums / cnt (streamed chunks)
+    int dt;
     float *C;          // [B][K][D] in/out (mode 0)
-    float *shiftk;     // [B][ncb][K] (mode 0; zeroed by the caller)
+    // optional fp64 partials of sum_k ||c_new - c_old||^2, each written once (no atomics):
+    // mode 0: [B*nch][ncb + 1] (column block of a chunk's wave; last slot: the chunk's cut
+    // segment, finished by the combine kernel); finalize: [B][K], one per cluster.
+    double *shp;
     float *sums;       // [B][K][D] (mode 1)
     int32_t *cnt;      // [B][K]    (mode 1)
     float *part;       // [B*nch][2][D]
     int32_t *rec;      // [B*nch][4]: cluster of slot 0 (cut on entry), of slot 1 (cut on exit), start of slot 1
+    // optional (mode 0): refresh the assign kernels' prepared centroids for every finished
+    // cluster (same layout as the prep kernel); clusters without points keep theirs.
+    void *cprep;
+    float *cnh;
+    int DP, KT;
 };
+
+// Store element d of -c~ (c~ = dtype(c), nearest even) into the prepared layout; returns c~^2.
+__device__ inline float prep_store_elem(const UpdArgs &a, int b, int k, int d, float c) {
+    const int VW = a.dt == DT_F32 ? 4 : 8;
+    const int gi = d / VW;
+    const int q = gi >> 1, hh = gi & 1, e = d - gi * VW;
+    const size_t word = (((size_t)b * a.KT + (k >> 5)) * (a.DP / (2 * VW)) + q) * 64 + (k & 31) + 32 * hh;
+    float r;
+    if (a.dt == DT_F32) {
+        r = c;
+        ((float *)a.cprep)[word * 4 + e] = -r;
+    } else if (a.dt == DT_F16) {
+        const uint32_t hb = f32_to_f16_bits(c);
+        r = f16_bits_to_f32(hb);
+        ((uint16_t *)a.cprep)[word * 8 + e] = (uint16_t)(hb ^ 0x8000u);
+    } else {
+        const uint32_t bb = f32_to_bf16_bits(c);
+        r = bf16_bits_to_f32(bb);
+        ((uint16_t *)a.cprep)[word * 8 + e] = (uint16_t)(bb ^ 0x8000u);
+    }
+    return r * r;
+}
+
+// Same for a whole 16-byte group starting at element d0 (d0 % VW == 0, all in range).
+template <int DT>
+__device__ inline float prep_store_group(const UpdArgs &a, int b, int k, int d0, const float *c) {
+    constexpr int VW = DT == DT_F32 ? 4 : 8;
+    const int gi = d0 / VW;
+    const int q = gi >> 1, hh = gi & 1;
+    const size_t word = (((size_t)b * a.KT + (k >> 5)) * (a.DP / (2 * VW)) + q) * 64 + (k & 31) + 32 * hh;
+    uint32_t w[4];
+    float ss = 0.f;
+    if constexpr (DT == DT_F32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            w[e] = __float_as_uint(-c[e]);
+            ss += c[e] * c[e];
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            uint32_t lo, hi;
+            float rl, rh;
+            if constexpr (DT == DT_F16) {
+                lo = f32_to_f16_bits(c[2 * e]);
+                hi = f32_to_f16_bits(c[2 * e + 1]);
+                rl = f16_bits_to_f32(lo);
+                rh = f16_bits_to_f32(hi);
+            } else {
+                lo = f32_to_bf16_bits(c[2 * e]);
+                hi = f32_to_bf16_bits(c[2 * e + 1]);
+                rl = bf16_bits_to_f32(lo);
+                rh = bf16_bits_to_f32(hi);
+            }
+            w[e] = ((lo ^ 0x8000u) & 0xFFFFu) | (((hi ^ 0x8000u) & 0xFFFFu) << 16);
+            ss += rl * rl + rh * rh;
+        }
+    }
+    ((uint4 *)a.cprep)[word] = make_uint4(w[0], w[1], w[2], w[3]);
+    return ss;
+}
 
 // Load the lane's vectors of row `row` within column block starting at element `c0`.
 template <int DT, int V, int VPL>
@@ -52,29 +126,43 @@ __device__ inline void load_row(const UpdArgs &a, size_t row_elem0, int c0, int 
 }
 
 // Finish cluster k from the row sum held by the lanes of one row group (lane index r < lanes).
-// mode 0: c_k <- s / n (fp32, IEEE division), shift_k contribution = sum (c_new - c_old)^2.
+// mode 0: c_k <- s / n (fp32, IEEE division); returns sum (c_new - c_old)^2 over the lane's
+//         columns and adds sum c~^2 to cn2 when the prepared centroids are refreshed.
 // mode 1: sums_k += s, cnt_k += n.
-template <int V, int VPL>
+template <int DT, int V, int VPL>
 __device__ inline float finish_cluster(const UpdArgs &a, int b, int k, int c0, int r, const float (&s)[VPL][V], int n,
-                                       bool write_cnt) {
+                                       bool write_cnt, float &cn2) {
     float d2 = 0.f;
     const size_t rowo = ((size_t)b * a.K + k) * a.D;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const int e0 = c0 + (r + i * a.lanes) * V;
+        if (a.mode == 0) {
+            float nw[V];
 #pragma unroll
-        for (int e = 0; e < V; ++e) {
-            const int d = e0 + e;
-            if (d < a.D) {
-                if (a.mode == 0) {
+            for (int e = 0; e < V; ++e) {
+                const int d = e0 + e;
+                nw[e] = 0.f;
+                if (d < a.D) {
                     const float old = a.C[rowo + d];
-                    const float nw = s[i][e] / (float)n;
-                    a.C[rowo + d] = nw;
-                    const float df = nw - old;
+                    nw[e] = s[i][e] / (float)n;
+                    a.C[rowo + d] = nw[e];
+                    const float df = nw[e] - old;
                     d2 += df * df;
-                } else {
-                    a.sums[rowo + d] += s[i][e];
                 }
+            }
+            if (a.cprep) {
+                if constexpr (V > 1) {
+                    if (e0 < a.D) cn2 += prep_store_group<DT>(a, b, k, e0, nw);
+                } else {
+                    if (e0 < a.D) cn2 += prep_store_elem(a, b, k, e0, nw[0]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const int d = e0 + e;
+                if (d < a.D) a.sums[rowo + d] += s[i][e];
             }
         }
     }
@@ -105,6 +193,7 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
     bool cin = p0 > 0 && sb[p0 - 1] == kraw;
     int seg_start = p0;
     int rec0 = -1, rec1 = -1, recps = 0;
+    float d2acc = 0.f;
     float acc[VPL][V];
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
@@ -118,22 +207,48 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
         const int idx = have ? ib[pos] : 0;
         const uint64_t eq = __ballot(have && sid == kraw);
         const int m = (~eq == 0ull) ? 64 : (int)__builtin_ctzll(~eq);
-        for (int base = 0; base < m; base += G * UPD_UNROLL) {
-            float tmp[UPD_UNROLL][VPL][V];
+        constexpr int U = upd_unroll<VPL>();
+        for (int base = 0; base < m; base += G * U) {
+            if constexpr (V == 1) {
+                float tmp[U][VPL][V];
 #pragma unroll
-            for (int u = 0; u < UPD_UNROLL; ++u) {
-                const int rr = base + u * G + g;
-                const bool ok = rr < m;
-                int row = __shfl(idx, rr & 63);
-                row = row < 0 ? 0 : (row >= N ? N - 1 : row);
-                load_row<DT, V, VPL>(a, (xb + row) * a.D, c0, r, tmp[u], ok);
+                for (int u = 0; u < U; ++u) {
+                    const int rr = base + u * G + g;
+                    int row = __shfl(idx, rr & 63);
+                    row = row < 0 ? 0 : (row >= N ? N - 1 : row);
+                    load_row<DT, V, VPL>(a, (xb + row) * a.D, c0, r, tmp[u], rr < m);
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int i = 0; i < VPL; ++i) acc[i][0] += tmp[u][i][0];
+            } else {
+                // keep the raw 16-byte vectors in flight; widen while accumulating
+                uint4 raw[U][VPL];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int rr = base + u * G + g;
+                    int row = __shfl(idx, rr & 63);
+                    row = row < 0 ? 0 : (row >= N ? N - 1 : row);
+                    const size_t e_row = (xb + row) * a.D;
+#pragma unroll
+                    for (int i = 0; i < VPL; ++i) {
+                        const int e0 = c0 + (r + i * a.lanes) * V;
+                        raw[u][i] = (rr < m && e0 < a.D)
+                                        ? *(const uint4 *)((const char *)a.x + (e_row + e0) * (DT == DT_F32 ? 4 : 2))
+                                        : make_uint4(0u, 0u, 0u, 0u);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int i = 0; i < VPL; ++i) {
+                        float f[V];
+                        widen16<DT>(raw[u][i], f);
+#pragma unroll
+                        for (int e = 0; e < V; ++e) acc[i][e] += f[e];
+                    }
             }
-#pragma unroll
-            for (int u = 0; u < UPD_UNROLL; ++u)
-#pragma unroll
-                for (int i = 0; i < VPL; ++i)
-#pragma unroll
-                    for (int e = 0; e < V; ++e) acc[i][e] += tmp[u][i][e];
         }
         p += m;
         const bool ended = (m < 64) || (p >= p1);
@@ -149,11 +264,11 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
             const bool cout = (p >= p1) && (p1 < N) && (sb[p1] == kraw);
             const int n = p - seg_start;
             if (!cin && !cout) {
-                float d2 = 0.f;
-                if (g == 0) d2 = finish_cluster<V, VPL>(a, b, k, c0, r, acc, n, cbi == 0);
-                if (a.mode == 0) {
-                    for (int off = 1; off < a.lanes; off <<= 1) d2 += __shfl_xor(d2, off);
-                    if (lane == 0) a.shiftk[((size_t)b * a.ncb + cbi) * a.K + k] = d2;
+                float cn2 = 0.f;
+                if (g == 0) d2acc += finish_cluster<DT, V, VPL>(a, b, k, c0, r, acc, n, cbi == 0, cn2);
+                if (a.cprep) {  // mode 0, ncb == 1
+                    for (int off = 1; off < a.lanes; off <<= 1) cn2 += __shfl_xor(cn2, off);
+                    if (lane == 0) a.cnh[(size_t)b * a.KT * 32 + k] = 0.5f * cn2;
                 }
             } else {
                 const int slot = cin ? 0 : 1;
@@ -179,6 +294,11 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
                 for (int e = 0; e < V; ++e) acc[i][e] = 0.f;
         }
     }
+    if (a.shp) {  // mode 0
+        double d = (double)d2acc;
+        for (int off = 1; off < 64; off <<= 1) d += __shfl_xor(d, off);
+        if (lane == 0) a.shp[(size_t)chunk * (a.ncb + 1) + cbi] = d;
+    }
     if (cbi == 0 && lane == 0) {
         int32_t *rc = a.rec + chunk * 4;
         rc[0] = rec0;
@@ -188,101 +308,161 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
     }
 }
 
-// One workgroup per chunk: if a segment starts in this chunk and runs past its end, add the
-// chunk partials of that segment in chunk order and finish the cluster.
-__global__ __launch_bounds__(256) void upd_combine_kernel(UpdArgs a) {
+// Finish column d of cluster k of problem b from its sum `s`, within a combine kernel.
+__device__ inline float combine_finish_col(const UpdArgs &a, int b, int k, size_t rowo, int d, float s, int nk,
+                                           float &cn2) {
+    if (a.mode == 0) {
+        const float old = a.C[rowo + d];
+        const float nw = s / (float)nk;
+        a.C[rowo + d] = nw;
+        if (a.cprep) cn2 += prep_store_elem(a, b, k, d, nw);
+        return (nw - old) * (nw - old);
+    }
+    a.sums[rowo + d] += s;
+    return 0.f;
+}
+
+// Segments that start in a chunk and run past its end: add the chunk partials in chunk order
+// and finish the cluster.  A workgroup covers 4 consecutive chunks.  A segment spread over at
+// most 8 chunks is finished by one wave (lanes over columns, pieces in order); a longer one
+// by the whole workgroup (piece groups x columns, fixed-order tree).  Deterministic either way.
+constexpr int COMBINE_WAVE_MAX = 8;
+
+__global__ __launch_bounds__(256) void upd_combine_kernel(UpdArgs a, int64_t nchunks) {
     __shared__ float s_red[256];
-    const int64_t chunk = blockIdx.x;
-    const int32_t *rc = a.rec + chunk * 4;
-    const int k = rc[1];
-    if (k < 0) return;
-    const int b = (int)(chunk / a.nch);
-    const int c = (int)(chunk - (int64_t)b * a.nch);
-    const int ps = rc[2];
-    int nk = a.counts[(size_t)b * a.K + k];
-    if (nk < 1) nk = 1;
-    int c_last = (int)(((int64_t)ps + nk - 1) / a.R);
-    if (c_last > a.nch - 1) c_last = a.nch - 1;
-    if (c_last < c) c_last = c;
-    const int npieces = c_last - c + 1;
-    const int D = a.D;
-    // threads = PG piece groups x DC columns
-    int DC = 1;
-    while (DC < D && DC < 256) DC <<= 1;
-    const int PG = 256 / DC;
-    const int t = threadIdx.x, pg = t / DC, dcol = t - pg * DC;
-    const size_t rowo = ((size_t)b * a.K + k) * D;
-    float d2 = 0.f;
-    for (int d = dcol; d < ((D + DC - 1) / DC) * DC; d += DC) {
-        float sum = 0.f;
-        if (d < D) {
-            for (int j = pg; j < npieces; j += PG) {
-                const int slot = j == 0 ? 1 : 0;
-                sum += a.part[((size_t)(chunk + j) * 2 + slot) * D + d];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int64_t chunk0 = (int64_t)blockIdx.x * 4;
+    int kk[4], np[4], nkk[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        kk[i] = -1;
+        np[i] = 0;
+        nkk[i] = 1;
+        const int64_t chunk = chunk0 + i;
+        if (chunk < nchunks) {
+            const int32_t *rc = a.rec + chunk * 4;
+            const int k = rc[1];
+            if (k >= 0) {
+                const int b = (int)(chunk / a.nch);
+                const int c = (int)(chunk - (int64_t)b * a.nch);
+                int nk = a.counts[(size_t)b * a.K + k];
+                nk = nk < 1 ? 1 : nk;
+                int c_last = (int)(((int64_t)rc[2] + nk - 1) / a.R);
+                c_last = c_last > a.nch - 1 ? a.nch - 1 : (c_last < c ? c : c_last);
+                kk[i] = k;
+                np[i] = c_last - c + 1;
+                nkk[i] = nk;
             }
         }
-        s_red[t] = sum;
-        __syncthreads();
-        for (int off = PG / 2; off >= 1; off >>= 1) {
-            if (pg < off) s_red[t] += s_red[t + off * DC];
+    }
+    const int D = a.D;
+    // long segments: the whole workgroup
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (kk[i] < 0 || np[i] <= COMBINE_WAVE_MAX) continue;  // uniform over the workgroup
+        const int64_t chunk = chunk0 + i;
+        const int b = (int)(chunk / a.nch);
+        const size_t rowo = ((size_t)b * a.K + kk[i]) * D;
+        int DC = 1;
+        while (DC < D && DC < 256) DC <<= 1;
+        const int PG = 256 / DC;
+        const int pg = t / DC, dcol = t - pg * DC;
+        float d2 = 0.f, cn2 = 0.f;
+        for (int d = dcol; d < ((D + DC - 1) / DC) * DC; d += DC) {
+            float sum = 0.f;
+            if (d < D) {
+                for (int j = pg; j < np[i]; j += PG) sum += a.part[((size_t)(chunk + j) * 2 + (j == 0 ? 1 : 0)) * D + d];
+            }
+            s_red[t] = sum;
+            __syncthreads();
+            for (int off = PG / 2; off >= 1; off >>= 1) {
+                if (pg < off) s_red[t] += s_red[t + off * DC];
+                __syncthreads();
+            }
+            if (pg == 0 && d < D) d2 += combine_finish_col(a, b, kk[i], rowo, d, s_red[dcol], nkk[i], cn2);
             __syncthreads();
         }
-        if (pg == 0 && d < D) {
-            const float s = s_red[dcol];
-            if (a.mode == 0) {
-                const float old = a.C[rowo + d];
-                const float nw = s / (float)nk;
-                a.C[rowo + d] = nw;
-                d2 += (nw - old) * (nw - old);
-            } else {
-                a.sums[rowo + d] += s;
+        if (a.mode == 0) {
+            s_red[t] = d2;
+            __syncthreads();
+            for (int off = 128; off >= 1; off >>= 1) {
+                if (t < off) s_red[t] += s_red[t + off];
+                __syncthreads();
             }
+            if (t == 0 && a.shp) a.shp[(size_t)chunk * (a.ncb + 1) + a.ncb] = (double)s_red[0];
+            __syncthreads();
+            s_red[t] = cn2;
+            __syncthreads();
+            for (int off = 128; off >= 1; off >>= 1) {
+                if (t < off) s_red[t] += s_red[t + off];
+                __syncthreads();
+            }
+            if (t == 0 && a.cprep) a.cnh[(size_t)b * a.KT * 32 + kk[i]] = 0.5f * s_red[0];
+            __syncthreads();
+        } else if (t == 0) {
+            a.cnt[(size_t)b * a.K + kk[i]] += nkk[i];
         }
-        __syncthreads();
+    }
+    // short segments: one wave each
+    const int64_t chunk = chunk0 + w;
+    if (kk[w] < 0 && chunk < nchunks && a.shp && lane == 0) a.shp[(size_t)chunk * (a.ncb + 1) + a.ncb] = 0.0;
+    if (kk[w] < 0 || np[w] > COMBINE_WAVE_MAX) return;
+    const int b = (int)(chunk / a.nch);
+    const size_t rowo = ((size_t)b * a.K + kk[w]) * D;
+    float d2 = 0.f, cn2 = 0.f;
+    for (int d = lane; d < D; d += 64) {
+        float sum = a.part[((size_t)chunk * 2 + 1) * D + d];
+        for (int j = 1; j < np[w]; ++j) sum += a.part[((size_t)(chunk + j) * 2) * D + d];
+        d2 += combine_finish_col(a, b, kk[w], rowo, d, sum, nkk[w], cn2);
     }
     if (a.mode == 0) {
-        s_red[t] = pg == 0 ? d2 : 0.f;
-        __syncthreads();
-        for (int off = 128; off >= 1; off >>= 1) {
-            if (t < off) s_red[t] += s_red[t + off];
-            __syncthreads();
+        for (int off = 1; off < 64; off <<= 1) {
+            d2 += __shfl_xor(d2, off);
+            cn2 += __shfl_xor(cn2, off);
         }
-        if (t == 0) a.shiftk[((size_t)b * a.ncb) * a.K + k] = s_red[0];
-    } else if (t == 0) {
-        a.cnt[(size_t)b * a.K + k] += a.counts[(size_t)b * a.K + k];
+        if (lane == 0 && a.shp) a.shp[(size_t)chunk * (a.ncb + 1) + a.ncb] = (double)d2;
+        if (lane == 0 && a.cprep) a.cnh[(size_t)b * a.KT * 32 + kk[w]] = 0.5f * cn2;
+    } else if (lane == 0) {
+        a.cnt[(size_t)b * a.K + kk[w]] += nkk[w];
     }
 }
 
 // Streamed path, after the last chunk: c_k <- sums_k / cnt_k where cnt_k > 0 (else keep),
-// shift_k = ||c_new - c_old||^2.  One wave per cluster.
-__global__ __launch_bounds__(256) void upd_finalize_acc_kernel(const float *__restrict__ sums,
-                                                               const int32_t *__restrict__ cnt, float *__restrict__ C,
-                                                               float *__restrict__ shiftk, int64_t rows, int D) {
+// shift += ||c_new - c_old||^2, prepared centroids refreshed.  One wave per cluster.
+__global__ __launch_bounds__(256) void upd_finalize_acc_kernel(UpdArgs a, int64_t rows) {
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= rows) return;
-    const int n = cnt[row];
-    float d2 = 0.f;
-    if (n > 0) {
-        for (int d = lane; d < D; d += 64) {
-            const float old = C[row * D + d];
-            const float nw = sums[row * D + d] / (float)n;
-            C[row * D + d] = nw;
-            d2 += (nw - old) * (nw - old);
-        }
+    const int b = (int)(row / a.K), k = (int)(row - (int64_t)b * a.K);
+    const int n = a.cnt[row];
+    if (n <= 0) {  // wave-uniform: the centroid is kept
+        if (lane == 0 && a.shp) a.shp[row] = 0.0;
+        return;
     }
-    for (int off = 1; off < 64; off <<= 1) d2 += __shfl_xor(d2, off);
-    if (lane == 0) shiftk[row] = d2;
+    const int D = a.D;
+    float d2 = 0.f, cn2 = 0.f;
+    for (int d = lane; d < D; d += 64) {
+        const float old = a.C[row * D + d];
+        const float nw = a.sums[row * D + d] / (float)n;
+        a.C[row * D + d] = nw;
+        d2 += (nw - old) * (nw - old);
+        if (a.cprep) cn2 += prep_store_elem(a, b, k, d, nw);
+    }
+    for (int off = 1; off < 64; off <<= 1) {
+        d2 += __shfl_xor(d2, off);
+        cn2 += __shfl_xor(cn2, off);
+    }
+    if (lane == 0 && a.shp) a.shp[row] = (double)d2;
+    if (lane == 0 && a.cprep) a.cnh[(size_t)b * a.KT * 32 + k] = 0.5f * cn2;
 }
 
 size_t update_ws_bytes(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
     const UpdCfg u = plan_update(dt, B, N, D);
     const int64_t chunks = B * u.nch;
+    (void)K;
     return align256((size_t)chunks * 2 * D * 4) + align256((size_t)chunks * 4 * 4) +
-           align256((size_t)B * u.ncb * K * 4);
+           align256((size_t)chunks * (u.ncb + 1) * 8);
 }
-
-hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s);
 
 template <int DT>
 static hipError_t launch_segsum_dt(const UpdArgs &a, int vec, int vpl, int64_t waves, hipStream_t s) {
@@ -300,21 +480,18 @@ static hipError_t launch_segsum_dt(const UpdArgs &a, int vec, int vpl, int64_t w
     return hipGetLastError();
 }
 
-// mode 0: in-core update of C (shiftk gets per-cluster shifts); mode 1: accumulate into sums / cnt.
-hipError_t launch_update(int dt, const void *x, const int32_t *sids, const int32_t *sidx, const int32_t *counts,
-                         int B, int N, int D, int K, int mode, float *C, float *sums, int32_t *cnt, void *ws,
-                         float **shiftk_out, int *ncb_out, hipStream_t s) {
+static UpdArgs make_args(int dt, const void *x, const int32_t *sids, const int32_t *sidx, const int32_t *counts,
+                         int B, int N, int D, int K, int mode, float *C, bool want_shift, float *sums, int32_t *cnt,
+                         const UpdRefresh &ref, void *ws) {
     const UpdCfg u = plan_update(dt, B, N, D);
     const int64_t chunks = (int64_t)B * u.nch;
     char *wp = (char *)ws;
-    float *part = (float *)wp;
+    UpdArgs a{};
+    a.part = (float *)wp;
     wp += align256((size_t)chunks * 2 * D * 4);
-    int32_t *rec = (int32_t *)wp;
+    a.rec = (int32_t *)wp;
     wp += align256((size_t)chunks * 4 * 4);
-    float *shiftk = (float *)wp;
-    if (shiftk_out) *shiftk_out = shiftk;
-    if (ncb_out) *ncb_out = u.ncb;
-    UpdArgs a;
+    a.shp = (mode == 0 && want_shift) ? (double *)wp : nullptr;
     a.x = x;
     a.sids = sids;
     a.sidx = sidx;
@@ -328,31 +505,62 @@ hipError_t launch_update(int dt, const void *x, const int32_t *sids, const int32
     a.ncb = u.ncb;
     a.cb_elems = u.cb_elems;
     a.mode = mode;
+    a.dt = dt;
     a.C = C;
-    a.shiftk = shiftk;
     a.sums = sums;
     a.cnt = cnt;
-    a.part = part;
-    a.rec = rec;
+    // the fused refresh needs one column block per row (each cluster finished by one lane group)
+    a.cprep = (ref.cprep && u.ncb == 1) ? ref.cprep : nullptr;
+    a.cnh = ref.cnh;
+    a.DP = ref.DP;
+    a.KT = ref.KT;
+    return a;
+}
+
+bool update_refreshes_prep(int dt, int64_t B, int64_t N, int64_t D) { return plan_update(dt, B, N, D).ncb == 1; }
+
+// mode 0: in-core update of C; shift (optional, [B]) receives sum_k ||c_new - c_old||^2 in fp64,
+// summed in a fixed order.  mode 1: accumulate into sums / cnt.  `ref` optionally names the
+// prepared centroids to refresh.
+hipError_t launch_update(int dt, const void *x, const int32_t *sids, const int32_t *sidx, const int32_t *counts,
+                         int B, int N, int D, int K, int mode, float *C, double *shift, float *sums, int32_t *cnt,
+                         const UpdRefresh &ref, void *ws, hipStream_t s) {
+    const UpdCfg u = plan_update(dt, B, N, D);
+    const int64_t chunks = (int64_t)B * u.nch;
+    const UpdArgs a = make_args(dt, x, sids, sidx, counts, B, N, D, K, mode, C, shift != nullptr, sums, cnt,
+                                mode == 0 ? ref : UpdRefresh{}, ws);
     hipError_t e;
-    if (mode == 0) {
-        e = launch_fill_i32((int32_t *)shiftk, (int64_t)B * u.ncb * K, 0, s);  // 0.0f has all-zero bits
-        if (e != hipSuccess) return e;
-    }
     const int64_t waves = chunks * u.ncb;
     if (dt == DT_F32) e = launch_segsum_dt<DT_F32>(a, u.vec, u.vpl, waves, s);
     else if (dt == DT_F16) e = launch_segsum_dt<DT_F16>(a, u.vec, u.vpl, waves, s);
     else e = launch_segsum_dt<DT_BF16>(a, u.vec, u.vpl, waves, s);
     if (e != hipSuccess) return e;
-    upd_combine_kernel<<<dim3((unsigned)chunks), dim3(256), 0, s>>>(a);
-    return hipGetLastError();
+    upd_combine_kernel<<<dim3((unsigned)((chunks + 3) / 4)), dim3(256), 0, s>>>(a, chunks);
+    e = hipGetLastError();
+    if (e != hipSuccess || !a.shp) return e;
+    return launch_sum_f64_rows(a.shp, B, u.nch * (u.ncb + 1), shift, s);
 }
 
-hipError_t launch_finalize_acc(const float *sums, const int32_t *cnt, float *C, float *shiftk, int B, int K, int D,
-                               hipStream_t s) {
+// shk: [B][K] doubles of scratch for the per-cluster shifts (optional, with shift).
+hipError_t launch_finalize_acc(int dt, const float *sums, const int32_t *cnt, float *C, double *shift, double *shk,
+                               const UpdRefresh &ref, int B, int K, int D, hipStream_t s) {
+    UpdArgs a{};
+    a.dt = dt;
+    a.D = D;
+    a.K = K;
+    a.C = C;
+    a.shp = shift ? shk : nullptr;
+    a.sums = (float *)sums;
+    a.cnt = (int32_t *)cnt;
+    a.cprep = ref.cprep;
+    a.cnh = ref.cnh;
+    a.DP = ref.DP;
+    a.KT = ref.KT;
     const int64_t rows = (int64_t)B * K;
-    upd_finalize_acc_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(sums, cnt, C, shiftk, rows, D);
-    return hipGetLastError();
+    upd_finalize_acc_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(a, rows);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !shift) return e;
+    return launch_sum_f64_rows(shk, B, K, shift, s);
 }
 
 }  // namespace fkm

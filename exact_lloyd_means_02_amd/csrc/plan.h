@@ -53,6 +53,14 @@ struct UpdCfg {
     int64_t nch;   // chunks per problem
 };
 
+// Prepared centroids (assign layout) that an update refreshes from the new centroids, or
+// all-null for no refresh.
+struct UpdRefresh {
+    void *cprep = nullptr;
+    float *cnh = nullptr;
+    int DP = 0, KT = 0;
+};
+
 AssignCfg plan_assign(int dt, int64_t B, int64_t N, int64_t D, int64_t K);
 SortCfg plan_sort(int64_t N, int64_t K);
 UpdCfg plan_update(int dt, int64_t B, int64_t N, int64_t D);

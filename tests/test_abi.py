@@ -1,0 +1,143 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the header declares,
+rejects invalid arguments before touching HIP, sizes workspaces consistently and plans tiles
+that fit gfx950 (LDS, VGPR) for every workload."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_lloyd_means_02_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flashkm.h")
+
+
+@pytest.fixture(scope="module")
+def fk():
+    from exact_lloyd_means_02_amd import flashkm
+    return flashkm
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kmeans_\w+)\s*\(", text)))
+
+
+def test_exports_match_header(fk):
+    names = header_functions()
+    assert names == sorted(fk.EXPORTS)
+    for n in names:
+        assert hasattr(fk.LIB, n), n
+
+
+P = ctypes.c_void_p(256)   # a non-null pointer value: never dereferenced on the paths tested
+
+
+@pytest.mark.parametrize("args,err", [
+    ((None, 2, 1, 10, 10, P, None), "x is NULL"),
+    ((P, 7, 1, 10, 10, P, None), "unknown dtype"),
+    ((P, 2, 0, 10, 10, P, None), "bad shape"),
+    ((P, 2, 1, 10, 5000, P, None), "bad shape"),
+    ((P, 2, 1, 10, 10, None, None), "x_norms is NULL"),
+    ((ctypes.c_void_p(258), 2, 1, 10, 10, P, None), "16-byte aligned"),
+])
+def test_row_norms_validation(fk, args, err):
+    assert fk.LIB.kmeans_row_norms(*args) == fk.KM_ERR_INVALID
+    assert err in fk.last_error()
+
+
+def _assign(fk, **kw):
+    a = dict(x=P, dt=2, c=P, B=1, N=100, D=16, K=10, xn=None, out=P, md=None, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return fk.LIB.kmeans_assign(a["x"], a["dt"], a["c"], a["B"], a["N"], a["D"], a["K"], a["xn"], a["out"], a["md"],
+                                a["ws"], a["wsb"], None)
+
+
+def test_assign_validation(fk):
+    assert _assign(fk, K=101) == fk.KM_ERR_INVALID and "K (101) > N (100)" in fk.last_error()
+    assert _assign(fk, K=0) == fk.KM_ERR_INVALID
+    assert _assign(fk, N=1 << 31) == fk.KM_ERR_INVALID
+    assert _assign(fk, B=2, N=1 << 30) == fk.KM_ERR_INVALID
+    assert _assign(fk, D=4097) == fk.KM_ERR_INVALID
+    assert _assign(fk, dt=3) == fk.KM_ERR_INVALID
+    assert _assign(fk, c=None) == fk.KM_ERR_INVALID and "centroids" in fk.last_error()
+    assert _assign(fk, out=None) == fk.KM_ERR_INVALID
+    assert _assign(fk, md=P) == fk.KM_ERR_INVALID and "x_norms" in fk.last_error()
+    assert _assign(fk, ws=None) == fk.KM_ERR_WORKSPACE
+    assert _assign(fk, ws=ctypes.c_void_p(256 + 128)) == fk.KM_ERR_WORKSPACE
+    assert _assign(fk, wsb=16) == fk.KM_ERR_WORKSPACE and "too small" in fk.last_error()
+
+
+def test_argsort_update_fit_validation(fk):
+    L = fk.LIB
+    assert L.kmeans_argsort_ids(None, 1, 10, 3, P, P, None, P, 1 << 20, None) == fk.KM_ERR_INVALID
+    assert L.kmeans_argsort_ids(P, 1, 10, 11, P, P, None, P, 1 << 20, None) == fk.KM_ERR_INVALID
+    assert L.kmeans_argsort_ids(P, 1, 10, 3, P, P, None, P, 0, None) == fk.KM_ERR_WORKSPACE
+    assert L.kmeans_update(P, 2, P, P, None, 1, 10, 4, 3, P, None, P, 1 << 20, None) == fk.KM_ERR_INVALID
+    assert L.kmeans_update(P, 2, P, P, P, 1, 10, 4, 3, None, None, P, 1 << 20, None) == fk.KM_ERR_INVALID
+    assert L.kmeans_fit(P, 2, 1, 10, 4, 3, 0, 0.0, 0, P, None, None, None, P, 1 << 20, None) == fk.KM_ERR_INVALID
+    assert "iters" in fk.last_error()
+    assert L.kmeans_fit(P, 2, 1, 10, 4, 3, 5, -1.0, 0, P, None, None, None, P, 1 << 20, None) == fk.KM_ERR_INVALID
+    assert L.kmeans_fit(P, 2, 1, 10, 4, 3, 5, 0.0, -5, P, None, None, None, P, 1 << 20, None) == fk.KM_ERR_INVALID
+    assert L.kmeans_fit(P, 2, 1, 10, 4, 3, 5, 0.0, 0, P, None, None, None, None, 1 << 20, None) == fk.KM_ERR_WORKSPACE
+
+
+def test_workspace_sizes(fk):
+    for op in (fk.KM_OP_ASSIGN, fk.KM_OP_ARGSORT, fk.KM_OP_UPDATE, fk.KM_OP_FIT, fk.KM_OP_FIT_HOST):
+        assert fk.kmeans_workspace_bytes(op, 2, 1, 10, 4, 11) == 0          # K > N: invalid
+        small = fk.kmeans_workspace_bytes(op, 2, 1, 4096, 16, 8)
+        big = fk.kmeans_workspace_bytes(op, 2, 4, 65536, 128, 1024)
+        assert 0 < small <= big and small % 256 == 0
+    assert fk.kmeans_workspace_bytes(99, 2, 1, 10, 4, 3) == 0
+    # the fit workspace covers every stage's workspace
+    fit = fk.kmeans_workspace_bytes(fk.KM_OP_FIT, 2, 32, 65536, 128, 1024)
+    for op in (fk.KM_OP_ASSIGN, fk.KM_OP_ARGSORT, fk.KM_OP_UPDATE):
+        assert fk.kmeans_workspace_bytes(op, 2, 32, 65536, 128, 1024) < fit
+    # streamed: two staging buffers of chunk_points rows
+    host = fk.kmeans_workspace_bytes(fk.KM_OP_FIT_HOST, 1, 1, 1 << 26, 64, 32768, 1 << 24)
+    assert host >= 2 * (1 << 24) * 64 * 2
+
+
+DT = {"f32": 0, "f16": 1, "bf16": 2}
+
+
+@pytest.mark.parametrize("name", sorted(W.WORKLOADS))
+def test_plan_fits_gfx950(fk, name):
+    w = W.WORKLOADS[name]
+    n = min(w.N, w.chunk) if w.host else w.N
+    p = fk.kmeans_plan(DT[w.dtype], w.B, n, w.D, w.K)
+    assert p["lds_bytes"] <= 160 * 1024
+    assert p["vgpr_est"] <= 256
+    assert p["d_pad"] >= w.D
+    assert p["path"] == (0 if w.D <= (128 if w.dtype == "f32" else 256) else 1)
+    assert p["block_n"] == p["waves"] * p["point_blocks"] * 32
+    assert (1 << (p["sort_bits"] * p["sort_passes"])) >= w.K
+    assert p["sort_bits"] <= 11
+    assert p["upd_rows"] >= 64 and p["upd_lanes"] in (1, 2, 4, 8, 16, 32, 64)
+    assert p["assign_wgs"] == w.B * -(-n // p["block_n"])
+
+
+def test_plan_headline_values(fk):
+    p = fk.kmeans_plan(2, 32, 65536, 128, 1024)
+    assert (p["path"], p["d_pad"], p["point_blocks"], p["block_n"]) == (0, 128, 2, 256)
+    assert (p["sort_bits"], p["sort_passes"]) == (10, 1)
+    s = fk.kmeans_plan(0, 1, 262144, 1024, 512)      # split-D fp32
+    assert s["path"] == 1 and s["block_d"] == 32
+    c5 = fk.kmeans_plan(1, 1, 1 << 24, 64, 32768)    # one streamed chunk: two counting passes
+    assert c5["sort_passes"] == 2
+
+
+def test_workload_generators_are_seeded():
+    w = W.small("headline_bf16", B=2, N=500, K=20)
+    x1, c1, _ = W.make(w)
+    x2, c2, _ = W.make(w)
+    assert (x1 == x2).all() and (c1 == c2).all()
+    assert x1.dtype == W.NP_STORAGE["bf16"] and x1.shape == (2, 500, 128)
+    idx = W.init_indices(w)
+    assert all(len(set(r.tolist())) == w.K for r in idx)          # distinct init points
+    w2 = W.small("skew_bf16_k64", N=40000, K=64)
+    x, c, mu = W.make(w2)
+    assert mu is not None and abs(mu[0, :4].mean() - 64.0) < 2.0   # the +64 channels, centred away
+    assert abs(W.storage_to_f64(x, "bf16")[0, :, :4].mean()) < 0.5
