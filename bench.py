@@ -6,11 +6,16 @@ per-point minimum distance, inertia, arg-sort, sort-inverse update with the shif
 kmeans_fit on the headline workload (B=32, N=65536, D=128, K=1024, bf16; inputs resident in
 HBM).  The timed region is one kmeans_fit call of `--steps` iterations (the point norms are
 computed once inside it, as in any fit).  Per-stage times come from HIP events recorded on
-the stream the stages run on.  Prints one JSON line.
+the stream the stages run on; the FlashAssign kernel is timed on its own through
+kmeans_assign_prepared (one kernel launch per call).  Prints one JSON line.
+
+`--copy-calib` instead runs a plain device copy of known size (the reference for scaling the
+FETCH_SIZE / WRITE_SIZE counters into bytes) and prints its size.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -28,13 +33,53 @@ PEAK_HBM_GBS = 8000.0
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--workload", default="headline_bf16")
     p.add_argument("--stage-reps", type=int, default=10)
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calib", action="store_true", help="run a plain 1 GiB device copy and exit")
     return p.parse_args()
+
+
+ASSIGN_SRC = os.path.join(ROOT, "exact_lloyd_means_02_amd", "csrc", "k_assign.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "assign_small_d_headline_bf16_traffic.txt")
+
+
+def assign_source_hash() -> str:
+    return hashlib.sha256(open(ASSIGN_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per FlashAssign launch from the committed counter summary (FETCH_SIZE +
+    WRITE_SIZE, scaled by the copy-kernel factor), or None when the summary is missing or was
+    taken on another version of the kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("k_assign.hip sha256[:16]") != assign_source_hash():
+        return None
+    try:
+        return float(kv["traffic bytes per launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calib():
+    import torch
+    n = 1 << 28                                    # 2^28 float32 = 1 GiB read + 1 GiB written
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calib": {"bytes_read": 4 * n, "bytes_written": 4 * n, "launches": 3,
+                                     "read_kib": 4 * n / 1024}}), flush=True)
 
 
 def algorithmic(w):
@@ -82,6 +127,9 @@ def main():
         print("bench.py: this build runs on one GPU only (no multi-GPU path); --gpus %d is not supported"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.copy_calib:
+        copy_calib()
+        return
     import numpy as np
     import torch
     from exact_lloyd_means_02_amd import flashkm as fk
@@ -116,27 +164,31 @@ def main():
 
     # ---- per-stage times (HIP events on the stages' stream), teacher forced from c0
     xn = fk.kmeans_row_norms(xt)
-    a, md = fk.kmeans_assign(xt, c0t, x_norms=xn, want_min_dist=True)
+    prep = fk.kmeans_prepare_centroids(c0t, xt)
+    a, md = fk.kmeans_assign_prepared(xt, prep, x_norms=xn, want_min_dist=True)
     s_ids, s_idx, counts = fk.kmeans_argsort_ids(a, w.K)
     cu = c0t.clone()
     torch.cuda.synchronize()
     R = args.stage_reps
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-    times = {"row_norms": [], "assign": [], "argsort": [], "update": []}
+    names = ["row_norms", "prepare", "assign", "argsort", "update"]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    times = {k: [] for k in names}
     for _ in range(R):
         cu.copy_(c0t)
         ev[0].record(stream)
         fk.kmeans_row_norms(xt, out=xn)
         ev[1].record(stream)
-        fk.kmeans_assign(xt, c0t, x_norms=xn, assign=a, min_dist=md)
+        fk.kmeans_prepare_centroids(c0t, xt, out=prep.buf)
         ev[2].record(stream)
-        fk.kmeans_argsort_ids(a, w.K, sorted_ids=s_ids, sorted_idx=s_idx, counts=counts)
+        fk.kmeans_assign_prepared(xt, prep, x_norms=xn, assign=a, min_dist=md)
         ev[3].record(stream)
-        fk.kmeans_update(xt, s_ids, s_idx, counts, cu)
+        fk.kmeans_argsort_ids(a, w.K, sorted_ids=s_ids, sorted_idx=s_idx, counts=counts)
         ev[4].record(stream)
+        fk.kmeans_update(xt, s_ids, s_idx, counts, cu)
+        ev[5].record(stream)
         torch.cuda.synchronize()
-        for k, (i, j) in zip(times, [(0, 1), (1, 2), (2, 3), (3, 4)]):
-            times[k].append(ev[i].elapsed_time(ev[j]))
+        for i, k in enumerate(names):
+            times[k].append(ev[i].elapsed_time(ev[i + 1]))
     st = {k: float(np.median(v)) for k, v in times.items()}
     flops, abytes, ubytes = algorithmic(w)
     peak = PEAK_TFLOPS[w.dtype]
@@ -160,9 +212,10 @@ def main():
         "config": {"workload": w.name, "B": w.B, "N": w.N, "D": w.D, "K": w.K, "iters": args.steps, "tol": 0.0,
                    "inputs": "HBM-resident"},
         "roofline": {"bound": "mfma", "achieved": round(assign_tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(assign_tflops / peak, 4), "traffic": None,
-                     "kernel": "assign_small_d_kernel (event time of kmeans_assign: centroid prep + FlashAssign)",
-                     "flop_per_launch": flops},
+                     "frac": round(assign_tflops / peak, 4), "traffic": measured_traffic(),
+                     "kernel": "FlashAssign (small-D) kernel, one launch per kmeans_assign_prepared call",
+                     "kernel_ms": round(st["assign"], 4), "flop_per_launch": flops,
+                     "algorithmic_bytes_per_launch": abytes},
         "stages_ms": {k: round(v, 4) for k, v in st.items()},
         "update": {"bound": "hbm", "achieved": round(upd_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                    "frac": round(upd_gbs / PEAK_HBM_GBS, 4), "bytes_per_iter": ubytes,

@@ -226,15 +226,32 @@ km_status_t check_device_arch() {
 // --------------------------------------------------------------------------------------------
 // stage bodies (validated arguments)
 // --------------------------------------------------------------------------------------------
-km_status_t do_assign(int dt, const void *x, const float *C, int64_t B, int64_t N, int64_t D, int64_t K,
-                      const float *xn, int32_t *a, float *md, void *ws, hipStream_t s) {
+// The prepared operand: c~ in tile order, then ||c~||^2 / 2 (assign_ws bytes in all).
+float *prep_norms(int dt, char *cprep, int64_t B, int64_t D, int64_t K, int d_pad) {
+    (void)D;
+    return (float *)(cprep + align256((size_t)B * assign_tiles(K) * 32 * d_pad * elem_bytes(dt)));
+}
+
+km_status_t do_prepare(int dt, const float *C, int64_t B, int64_t N, int64_t D, int64_t K, void *cprep,
+                       hipStream_t s) {
     const AssignCfg cfg = plan_assign(dt, B, N, D, K);
-    const int64_t KT = (int64_t)assign_tiles(K);
-    char *cprep = (char *)ws;
-    float *cnh = (float *)(cprep + align256((size_t)B * KT * 32 * cfg.d_pad * elem_bytes(dt)));
-    KM_HIP(launch_prep_centroids(dt, C, cprep, cnh, (int)B, (int)K, (int)D, cfg.d_pad, s));
+    KM_HIP(launch_prep_centroids(dt, C, cprep, prep_norms(dt, (char *)cprep, B, D, K, cfg.d_pad), (int)B, (int)K,
+                                 (int)D, cfg.d_pad, s));
+    return ok();
+}
+
+km_status_t do_assign_prepared(int dt, const void *x, const void *cprep, int64_t B, int64_t N, int64_t D, int64_t K,
+                               const float *xn, int32_t *a, float *md, hipStream_t s) {
+    const AssignCfg cfg = plan_assign(dt, B, N, D, K);
+    const float *cnh = prep_norms(dt, (char *)cprep, B, D, K, cfg.d_pad);
     KM_HIP(launch_assign(dt, cfg, x, cprep, cnh, xn, a, md, nullptr, (int)B, (int)N, (int)D, (int)K, s));
     return ok();
+}
+
+km_status_t do_assign(int dt, const void *x, const float *C, int64_t B, int64_t N, int64_t D, int64_t K,
+                      const float *xn, int32_t *a, float *md, void *ws, hipStream_t s) {
+    KM_TRY(do_prepare(dt, C, B, N, D, K, ws, s));
+    return do_assign_prepared(dt, x, ws, B, N, D, K, xn, a, md, s);
 }
 
 km_status_t do_update(int dt, const void *x, const int32_t *sids, const int32_t *sidx, const int32_t *counts,
@@ -320,6 +337,37 @@ km_status_t kmeans_assign(const void *x, km_dtype_t dt, const float *centroids, 
     KM_TRY(require_device(x_norms, "x_norms"));
     KM_TRY(require_device(ws, "ws"));
     return do_assign(dt, x, centroids, B, N, D, K, x_norms, assign, min_dist, ws, (hipStream_t)stream);
+}
+
+km_status_t kmeans_prepare_centroids(const float *centroids, km_dtype_t dt, int64_t B, int64_t N, int64_t D,
+                                     int64_t K, void *c_prep, size_t c_prep_bytes, void *stream) {
+    KM_TRY(check_shape(dt, B, N, D, K));
+    KM_TRY(check_ptr(centroids, "centroids"));
+    KM_TRY(check_ptr(c_prep, "c_prep"));
+    KM_TRY(check_ws(c_prep, c_prep_bytes, assign_ws(dt, B, N, D, K)));
+    KM_TRY(check_device_arch());
+    KM_TRY(require_device(centroids, "centroids"));
+    KM_TRY(require_device(c_prep, "c_prep"));
+    return do_prepare(dt, centroids, B, N, D, K, c_prep, (hipStream_t)stream);
+}
+
+km_status_t kmeans_assign_prepared(const void *x, km_dtype_t dt, const void *c_prep, size_t c_prep_bytes, int64_t B,
+                                   int64_t N, int64_t D, int64_t K, const float *x_norms, int32_t *assign,
+                                   float *min_dist, void *stream) {
+    KM_TRY(check_shape(dt, B, N, D, K));
+    KM_TRY(check_ptr(x, "x"));
+    KM_TRY(check_ptr(c_prep, "c_prep"));
+    KM_TRY(check_ptr(assign, "assign"));
+    if (min_dist && !x_norms) return fail(KM_ERR_INVALID, "min_dist requires x_norms");
+    if (((uintptr_t)x & 15) != 0) return fail(KM_ERR_INVALID, "x must be 16-byte aligned");
+    KM_TRY(check_ws(c_prep, c_prep_bytes, assign_ws(dt, B, N, D, K)));
+    KM_TRY(check_device_arch());
+    KM_TRY(require_device(x, "x"));
+    KM_TRY(require_device(c_prep, "c_prep"));
+    KM_TRY(require_device(assign, "assign"));
+    KM_TRY(require_device(min_dist, "min_dist"));
+    KM_TRY(require_device(x_norms, "x_norms"));
+    return do_assign_prepared(dt, x, c_prep, B, N, D, K, x_norms, assign, min_dist, (hipStream_t)stream);
 }
 
 km_status_t kmeans_argsort_ids(const int32_t *assign, int64_t B, int64_t N, int64_t K, int32_t *sorted_ids,

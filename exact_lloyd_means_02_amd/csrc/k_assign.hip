@@ -22,7 +22,8 @@
 //     '<' over tiles in increasing order, lowest slot, lexicographic lane merge).
 //   * Centroid tiles are pre-laid-out in "MFMA-fragment" order (see prep kernel) so a stage
 //     is one contiguous copy and each A fragment is one conflict-free 16-byte LDS read per
-//     lane; stages of 32 KiB ping-pong in LDS.
+//     lane; stages rotate through three LDS buffers, filled by direct global->LDS copies
+//     two stages ahead of their use.
 #include "common.h"
 #include "plan.h"
 
@@ -259,7 +260,8 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
     constexpr int QG = DP / (2 * VW);
     constexpr int PB = small_d_pb(DT, DP);
     constexpr int TILE_U4 = QG * 64;
-    constexpr int TPS = QG >= 2 ? 2 : 4;  // tiles per stage: at least 4 KiB, one per wave-copy
+    constexpr int TPS = small_d_tps(DT, DP);  // tiles per stage: at least 4 KiB, one per wave-copy
+    static_assert(TPS == (QG >= 2 ? 2 : 4), "stage size");
     constexpr int STAGE_U4 = TPS * TILE_U4;
     constexpr int PF = STAGE_U4 / 256;  // 1 KiB copy instructions per wave per stage
     constexpr int NCOPY = PF + 1;       // ... plus one for the stage's norms

@@ -10,8 +10,9 @@
 //     + c-norm 16 + 32.  PB (32-point blocks per wave) is the largest of {2,1} keeping this
 //     <= 256, so two waves share a SIMD.  Within a wave the MFMAs of tile t+1 are interleaved
 //     with the arg-min selects of tile t (two accumulator sets).
-//   * Centroid stages of 32 KiB ping-pong in LDS: 2 x (32 KiB + norms) = 72 KiB per
-//     workgroup, two workgroups per CU within 160 KiB.
+//   * Centroid stages of 2 (or 4, for D*s < 64 B) tiles rotate through three LDS buffers,
+//     filled by direct global->LDS copies two stages ahead of use: ~49 KiB per workgroup at
+//     D=128 bf16, so three workgroups (12 waves) fit a CU's 160 KiB.
 //   * Every workgroup re-reads all K centroids from L2: the arithmetic intensity of that
 //     stream is 2*block_n*D FLOP per D*s bytes = block_n FLOP/B (bf16), >= 128 for
 //     block_n >= 128, above what L2 must feed MFMA (~2.5 PF / ~40 TB/s ~= 64 FLOP/B).
@@ -61,7 +62,7 @@ AssignCfg plan_assign(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
         c.tps = small_d_tps(dt, dp);
         c.bd = 0;
         c.block_n = ASSIGN_WAVES * c.pb * 32;
-        c.lds = 2 * (c.tps * 32 * dp * s + c.tps * 32 * 4);
+        c.lds = SMALL_D_STAGES * (c.tps * 32 * dp * s + c.tps * 32 * 4) + ASSIGN_WAVES * 8;
         c.vgpr = c.pb * (dp * s / 8 + 48) + 32 + 16 + 32;
     } else {
         const int bd = splitd_bd(dt);

@@ -20,7 +20,6 @@ struct Gfx950 {
 
 // Kernel-side constants the plan and the launchers agree on.
 constexpr int ASSIGN_WAVES = 4;          // waves per assign workgroup
-constexpr int STAGE_BYTES = 32 * 1024;   // centroid bytes per LDS stage (double buffered)
 constexpr int SPLITD_KB = 4;             // split-D: 32-centroid tiles per register group
 constexpr int SORT_TILE = 4096;          // keys per sort workgroup (4 waves x 16 rounds x 64)
 constexpr int SORT_MAX_BITS = 11;        // <= 2048 bins per counting pass (LDS: 5 x bins x 4 B)
@@ -67,12 +66,11 @@ UpdCfg plan_update(int dt, int64_t B, int64_t N, int64_t D);
 
 // Small-D register tile chosen for (dtype, padded D); shared with the kernel templates.
 constexpr int small_d_pb(int dt, int dp) { return dt == 0 ? (dp <= 32 ? 2 : 1) : (dp <= 128 ? 2 : 1); }
-// Tiles per LDS stage: up to 32 KiB of centroids, between 2 and 8 tiles.
-constexpr int small_d_tps(int dt, int dp) {
-    return STAGE_BYTES / (32 * dp * (dt == 0 ? 4 : 2)) > 8   ? 8
-           : STAGE_BYTES / (32 * dp * (dt == 0 ? 4 : 2)) > 2 ? STAGE_BYTES / (32 * dp * (dt == 0 ? 4 : 2))
-                                                              : 2;
-}
+// Tiles per LDS stage: 2 when a tile's 32 centroid rows span at least two 16-byte groups
+// per lane half (D*s >= 64 bytes), else 4, so one stage is at least 4 KiB (one 16-byte copy
+// per lane of every wave).  Three stages rotate in LDS.
+constexpr int small_d_tps(int dt, int dp) { return dp * (dt == 0 ? 4 : 2) >= 64 ? 2 : 4; }
+constexpr int SMALL_D_STAGES = 3;
 constexpr int splitd_bd(int dt) { return dt == 0 ? 32 : 64; }
 
 // 32-centroid tiles per problem in the prepared layout: padded to a multiple of 4 so the

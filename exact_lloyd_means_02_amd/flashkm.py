@@ -19,8 +19,8 @@ KM_OP_ASSIGN, KM_OP_ARGSORT, KM_OP_UPDATE, KM_OP_FIT, KM_OP_FIT_HOST = 1, 2, 3, 
 STATUS_NAMES = {0: "KM_OK", -1: "KM_ERR_INVALID", -2: "KM_ERR_UNSUPPORTED", -3: "KM_ERR_WORKSPACE", -4: "KM_ERR_HIP"}
 
 # every symbol the header declares
-EXPORTS = ["kmeans_plan", "kmeans_workspace_bytes", "kmeans_row_norms", "kmeans_assign", "kmeans_argsort_ids",
-           "kmeans_update", "kmeans_fit", "kmeans_last_error"]
+EXPORTS = ["kmeans_plan", "kmeans_workspace_bytes", "kmeans_row_norms", "kmeans_assign", "kmeans_prepare_centroids",
+           "kmeans_assign_prepared", "kmeans_argsort_ids", "kmeans_update", "kmeans_fit", "kmeans_last_error"]
 
 
 class KmPlan(ctypes.Structure):
@@ -48,11 +48,13 @@ def _load():
     lib.kmeans_workspace_bytes.restype = sz
     lib.kmeans_row_norms.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp]
     lib.kmeans_assign.argtypes = [vp, ctypes.c_int, vp, i64, i64, i64, i64, vp, vp, vp, vp, sz, vp]
+    lib.kmeans_prepare_centroids.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, vp, sz, vp]
+    lib.kmeans_assign_prepared.argtypes = [vp, ctypes.c_int, vp, sz, i64, i64, i64, i64, vp, vp, vp, vp]
     lib.kmeans_argsort_ids.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, sz, vp]
     lib.kmeans_update.argtypes = [vp, ctypes.c_int, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, sz, vp]
     lib.kmeans_fit.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, i32, f32, i64, vp, vp, vp, vp, vp, sz, vp]
-    for n in ("kmeans_plan", "kmeans_row_norms", "kmeans_assign", "kmeans_argsort_ids", "kmeans_update",
-              "kmeans_fit"):
+    for n in ("kmeans_plan", "kmeans_row_norms", "kmeans_assign", "kmeans_prepare_centroids",
+              "kmeans_assign_prepared", "kmeans_argsort_ids", "kmeans_update", "kmeans_fit"):
         getattr(lib, n).restype = ctypes.c_int
     lib.kmeans_last_error.argtypes = []
     lib.kmeans_last_error.restype = ctypes.c_char_p
@@ -164,6 +166,51 @@ def kmeans_assign(x, centroids, x_norms=None, assign=None, min_dist=None, want_m
     ws = workspace(KM_OP_ASSIGN, dt, B, N, D, K, x.device)
     _check(LIB.kmeans_assign(_ptr(x), dt, _ptr(centroids), B, N, D, K, _ptr(x_norms), _ptr(assign), _ptr(min_dist),
                              _ptr(ws), ws.numel(), _stream(x, stream)))
+    return assign, min_dist
+
+
+class PreparedCentroids:
+    """The assign kernel's centroid operand (opaque device bytes) for one (dtype, B, D, K)."""
+
+    def __init__(self, buf, dt: int, B: int, D: int, K: int):
+        self.buf, self.dt, self.B, self.D, self.K = buf, dt, B, D, K
+
+
+def kmeans_prepare_centroids(centroids, dtype, out=None, stream=None) -> PreparedCentroids:
+    """c~ = dtype(centroids) in the assign kernel's layout plus ||c~||^2 / 2.  `dtype` is the
+    points' torch dtype (or a tensor of it)."""
+    torch = _torch()
+    _need(centroids.dim() == 3 and centroids.is_contiguous() and centroids.dtype == torch.float32,
+          "centroids must be contiguous f32 [B, K, D]")
+    B, K, D = centroids.shape
+    dt = dtype_code(dtype) if hasattr(dtype, "dtype") else dtype_code(torch.empty(0, dtype=dtype))
+    nbytes = LIB.kmeans_workspace_bytes(KM_OP_ASSIGN, dt, B, K, D, K, 0)
+    if nbytes == 0:
+        raise FlashKMError(KM_ERR_INVALID, last_error() or "bad shape")
+    if out is None:
+        raw = torch.empty(nbytes + 256, dtype=torch.uint8, device=centroids.device)
+        off = (-raw.data_ptr()) % 256
+        out = raw[off:off + nbytes]
+    _need(out.dtype == torch.uint8 and out.numel() >= nbytes, "out: uint8 device buffer too small")
+    _check(LIB.kmeans_prepare_centroids(_ptr(centroids), dt, B, K, D, K, _ptr(out), out.numel(),
+                                        _stream(centroids, stream)))
+    return PreparedCentroids(out, dt, B, D, K)
+
+
+def kmeans_assign_prepared(x, prep: PreparedCentroids, x_norms=None, assign=None, min_dist=None,
+                           want_min_dist=False, stream=None):
+    """FlashAssign from prepared centroids.  Returns (assign, min_dist or None)."""
+    torch = _torch()
+    _need(x.dim() == 3 and x.is_contiguous(), "x must be a contiguous [B, N, D] tensor")
+    B, N, D = x.shape
+    dt = dtype_code(x)
+    _need((prep.dt, prep.B, prep.D) == (dt, B, D), "prepared centroids were made for another dtype/shape")
+    if assign is None:
+        assign = torch.empty((B, N), dtype=torch.int32, device=x.device)
+    if want_min_dist and min_dist is None:
+        min_dist = torch.empty((B, N), dtype=torch.float32, device=x.device)
+    _check(LIB.kmeans_assign_prepared(_ptr(x), dt, _ptr(prep.buf), prep.buf.numel(), B, N, D, prep.K, _ptr(x_norms),
+                                      _ptr(assign), _ptr(min_dist), _stream(x, stream)))
     return assign, min_dist
 
 

@@ -132,6 +132,29 @@ km_status_t kmeans_assign(const void *x, km_dtype_t dt, const float *centroids, 
                           float *min_dist, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * The two halves of kmeans_assign, for callers that assign repeatedly against
+ * the same centroids (and to time the FlashAssign kernel on its own).
+ *
+ * kmeans_prepare_centroids: the centroid side of the contraction (paper
+ * digest, "核心方法": ||x - c||^2 = ||x||^2 + ||c||^2 - 2 x.c, so only c~ and
+ * ||c~||^2 are needed per centroid): c~ = dtype(fp32 centroids) (nearest
+ * even), laid out in the assign kernel's tile order, followed by ||c~||^2 / 2
+ * in fp32 computed from c~.
+ *   centroids  device [B, K, D] float32 (read only)
+ *   c_prep     device out, opaque, c_prep_bytes >= kmeans_workspace_bytes(
+ *              KM_OP_ASSIGN, dt, B, N, D, K) (any N), 256-byte aligned; valid
+ *              for calls with the same (dt, B, D, K)
+ *
+ * kmeans_assign_prepared: FlashAssign as kmeans_assign, from a c_prep written
+ * by kmeans_prepare_centroids for the same (dt, B, D, K).
+ */
+km_status_t kmeans_prepare_centroids(const float *centroids, km_dtype_t dt, int64_t B, int64_t N, int64_t D,
+                                     int64_t K, void *c_prep, size_t c_prep_bytes, void *stream);
+km_status_t kmeans_assign_prepared(const void *x, km_dtype_t dt, const void *c_prep, size_t c_prep_bytes,
+                                   int64_t B, int64_t N, int64_t D, int64_t K, const float *x_norms,
+                                   int32_t *assign, float *min_dist, void *stream);
+
+/*
  * Stable ascending arg-sort of each problem's assignment vector (paper
  * digest, "argsort与分段规约": [3,1,2,1,3,2] -> ids [1,1,2,2,3,3], indices
  * [1,3,2,5,0,4]); a hand-written LDS counting/radix sort keyed by cluster id.

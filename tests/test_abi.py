@@ -70,6 +70,23 @@ def test_assign_validation(fk):
     assert _assign(fk, wsb=16) == fk.KM_ERR_WORKSPACE and "too small" in fk.last_error()
 
 
+def test_prepared_assign_validation(fk):
+    L = fk.LIB
+    assert L.kmeans_prepare_centroids(None, 2, 1, 100, 16, 10, P, 1 << 20, None) == fk.KM_ERR_INVALID
+    assert L.kmeans_prepare_centroids(P, 2, 1, 100, 16, 10, None, 1 << 20, None) == fk.KM_ERR_INVALID
+    assert L.kmeans_prepare_centroids(P, 2, 1, 100, 16, 10, P, 16, None) == fk.KM_ERR_WORKSPACE
+    assert L.kmeans_prepare_centroids(P, 2, 1, 100, 16, 101, P, 1 << 20, None) == fk.KM_ERR_INVALID
+    args = [P, 2, P, 1 << 20, 1, 100, 16, 10, None, P, None, None]
+    bad = list(args); bad[2] = None
+    assert L.kmeans_assign_prepared(*bad) == fk.KM_ERR_INVALID and "c_prep" in fk.last_error()
+    bad = list(args); bad[3] = 16
+    assert L.kmeans_assign_prepared(*bad) == fk.KM_ERR_WORKSPACE
+    bad = list(args); bad[10] = P
+    assert L.kmeans_assign_prepared(*bad) == fk.KM_ERR_INVALID and "x_norms" in fk.last_error()
+    bad = list(args); bad[0] = ctypes.c_void_p(258)
+    assert L.kmeans_assign_prepared(*bad) == fk.KM_ERR_INVALID
+
+
 def test_argsort_update_fit_validation(fk):
     L = fk.LIB
     assert L.kmeans_argsort_ids(None, 1, 10, 3, P, P, None, P, 1 << 20, None) == fk.KM_ERR_INVALID

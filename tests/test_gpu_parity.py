@@ -61,6 +61,21 @@ def test_row_norms_and_assign(fk, name, kw):
     check_assign(x64, operand(c0, w.dtype), a.cpu().numpy(), md.cpu().numpy())
 
 
+def test_assign_prepared_equals_assign(fk):
+    w = W.small("headline_bf16", B=3, N=5000, K=300)
+    _say(f"assign_prepared {w.name} B={w.B} N={w.N} K={w.K}")
+    x, c0, _ = W.make(w)
+    xt = W.to_torch(x, w.dtype).to(device())
+    ct = torch.from_numpy(c0).to(device())
+    xn = fk.kmeans_row_norms(xt)
+    a1, m1 = fk.kmeans_assign(xt, ct, x_norms=xn, want_min_dist=True)
+    prep = fk.kmeans_prepare_centroids(ct, xt)
+    a2, m2 = fk.kmeans_assign_prepared(xt, prep, x_norms=xn, want_min_dist=True)
+    a3, _ = fk.kmeans_assign_prepared(xt, prep)                  # reused, no min_dist
+    assert torch.equal(a1, a2) and torch.equal(a1, a3)
+    assert torch.equal(m1, m2)
+
+
 def test_assign_exact_ties_go_to_lowest_index(fk):
     """Duplicate centroids give bit-identical scores; the lowest index must win."""
     w = W.small("headline_bf16", B=1, N=2000, K=64)
