@@ -59,8 +59,8 @@ def measured_traffic():
         return None
     kv = {}
     for line in open(TRAFFIC_FILE):
-        if ":" in line and not line.startswith("#"):
-            k, v = line.split(":", 1)
+        if ": " in line and not line.startswith("#"):
+            k, v = line.split(": ", 1)
             kv[k.strip()] = v.strip()
     if kv.get("k_assign.hip sha256[:16]") != assign_source_hash():
         return None

@@ -91,6 +91,18 @@ __device__ inline int xcd_remap(int p, int grid) {
     return start + p / NUM_XCD;
 }
 
+// The same partition of logical ids over XCDs as xcd_remap, walked backwards in time: the
+// first workgroups an XCD runs take the end of its range.  A kernel launched after one that
+// used xcd_remap over the same data then starts on what the earlier kernel touched last
+// (still in the memory-side cache) and ends on what the next such kernel reads first.
+__device__ inline int xcd_remap_rev(int p, int grid) {
+    const int q = grid / NUM_XCD, r = grid % NUM_XCD;
+    const int x = p % NUM_XCD;
+    const int start = x * q + (x < r ? x : r);
+    const int count = q + (x < r ? 1 : 0);
+    return start + count - 1 - p / NUM_XCD;
+}
+
 __device__ inline uint64_t lanemask_lt() {
     const int lane = __lane_id();
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));

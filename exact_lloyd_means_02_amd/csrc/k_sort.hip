@@ -5,12 +5,17 @@
 // LSD counting passes over digits of the cluster id.  Per pass:
 //   1. hist:    each workgroup counts the digits of its tile of 4096 keys in LDS and writes
 //               one column of the [bins][tiles] table of its problem;
-//   2. scan:    one workgroup per problem turns the table into exclusive offsets, in
-//               (digit-major, tile-minor) order, so equal digits keep tile order;
+//   2. offsets: where a problem has few tiles (bins x tiles <= SORT_INLINE_MAX) every scatter
+//               workgroup derives its own offsets from the table (sum over earlier tiles plus
+//               an exclusive scan of the digit totals); otherwise one scan workgroup per problem
+//               turns the table into offsets in (digit-major, tile-minor) order first;
 //   3. scatter: each wave ranks its keys 64 at a time, in index order: lanes holding the same
 //               digit are found with one ballot per digit bit; a lane's rank = earlier peers
-//               in the round + the wave's running count of that digit (LDS).  Waves are then
-//               offset by the counts of earlier waves of the tile.  Result: stable.
+//               in the round + the wave's running count of that digit (LDS).  The tile is
+//               then laid out in LDS in (digit, index) order and written out with consecutive
+//               lanes on consecutive positions of each digit's run.  Result: stable.
+// All tiles of one problem run on one XCD, so the short runs that neighbouring tiles write
+// into the same cache lines meet in that XCD's L2 instead of being written back piecemeal.
 // The single-pass case (all of the id in one digit) also yields the per-cluster counts.
 #include "common.h"
 #include "plan.h"
@@ -23,7 +28,8 @@ constexpr int SORT_ROUNDS = SORT_TILE / (SORT_WAVES * 64);  // 16
 __global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t *__restrict__ keys, int N, int ntiles,
                                                         int shift, int bins, int32_t *__restrict__ hist) {
     extern __shared__ int32_t s_h[];
-    const int b = blockIdx.x / ntiles, t = blockIdx.x - b * ntiles;
+    const int lb = xcd_remap(blockIdx.x, gridDim.x);
+    const int b = lb / ntiles, t = lb - b * ntiles;
     for (int i = threadIdx.x; i < bins; i += 256) s_h[i] = 0;
     __syncthreads();
     const int32_t *kb = keys + (size_t)b * N;
@@ -90,23 +96,88 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t *__restrict__ h
     }
 }
 
+// In-place exclusive scan of s[0, n) (n <= 1024) by a 256-thread workgroup.
+static_assert(SORT_MAX_BITS <= 10, "block_exscan_1024 covers at most 1024 bins");
+
+__device__ inline void block_exscan_1024(int32_t *s, int n, int32_t *s_wsum) {
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    int32_t v[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = t * 4 + i;
+        v[i] = idx < n ? s[idx] : 0;
+        sum += v[i];
+    }
+    int32_t inc = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t o = __shfl_up(inc, off);
+        if (lane >= off) inc += o;
+    }
+    if (lane == 63) s_wsum[w] = inc;
+    __syncthreads();
+    int32_t run = inc - sum;
+    for (int i = 0; i < w; ++i) run += s_wsum[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = t * 4 + i;
+        if (idx < n) s[idx] = run;
+        run += v[i];
+    }
+    __syncthreads();
+}
+
 // Stable scatter of one pass.  vals_in == NULL means the values are the point indices.
+// INLINE: `hist` holds the raw [bins][tiles] counts and each workgroup derives its offsets
+// (and, for counts != NULL, the workgroup of tile 0 writes the per-bin totals); otherwise
+// `hist` holds the scanned offsets.
+template <bool INLINE>
 __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__restrict__ keys_in,
                                                            const int32_t *__restrict__ vals_in,
                                                            const int32_t *__restrict__ hist, int N, int ntiles,
                                                            int shift, int bits, int32_t *__restrict__ keys_out,
-                                                           int32_t *__restrict__ vals_out) {
+                                                           int32_t *__restrict__ vals_out,
+                                                           int32_t *__restrict__ counts, int K) {
     extern __shared__ int32_t s_mem[];
+    __shared__ int32_t s_wsum[SORT_WAVES];
     const int bins = 1 << bits;
-    int32_t *s_wc = s_mem;                       // [SORT_WAVES][bins] running counts, then prefixes
-    int32_t *s_off = s_mem + SORT_WAVES * bins;  // [bins] this tile's global offsets
-    const int b = blockIdx.x / ntiles, t = blockIdx.x - b * ntiles;
+    int32_t *s_wc = s_mem;                        // [SORT_WAVES][bins] running counts, then prefixes
+    int32_t *s_off = s_wc + SORT_WAVES * bins;    // [bins] this tile's global offset of each digit
+    int32_t *s_ls = s_off + bins;                 // [bins] start of each digit inside the tile
+    int32_t *s_k = s_ls + bins;                   // [SORT_TILE] keys in (digit, index) order
+    int32_t *s_v = s_k + SORT_TILE;               // [SORT_TILE] values, same order
+    const int lb = xcd_remap(blockIdx.x, gridDim.x);
+    const int b = lb / ntiles, t = lb - b * ntiles;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int32_t *hb = hist + (size_t)b * bins * ntiles;
-    for (int i = tid; i < bins; i += 256) {
-        s_off[i] = hb[(size_t)i * ntiles + t];
+    for (int i = tid; i < SORT_WAVES * bins; i += 256) s_wc[i] = 0;
+    if constexpr (INLINE) {
+        int32_t pre[4];
 #pragma unroll
-        for (int ww = 0; ww < SORT_WAVES; ++ww) s_wc[ww * bins + i] = 0;
+        for (int j = 0; j < 4; ++j) {
+            const int i = tid + 256 * j;
+            pre[j] = 0;
+            if (i < bins) {
+                int32_t tot = 0, pr = 0;
+                for (int tt = 0; tt < ntiles; ++tt) {
+                    const int32_t h = hb[(size_t)i * ntiles + tt];
+                    tot += h;
+                    pr += tt < t ? h : 0;
+                }
+                s_off[i] = tot;
+                pre[j] = pr;
+                if (counts && t == 0 && i < K) counts[(size_t)b * K + i] = tot;
+            }
+        }
+        __syncthreads();
+        block_exscan_1024(s_off, bins, s_wsum);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = tid + 256 * j;
+            if (i < bins) s_off[i] += pre[j];
+        }
+    } else {
+        for (int i = tid; i < bins; i += 256) s_off[i] = hb[(size_t)i * ntiles + t];
     }
     __syncthreads();
 
@@ -142,7 +213,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__rest
         pos[r] = wbase + before;
     }
     __syncthreads();
-    // exclusive prefix over waves, per digit
+    // exclusive prefix over waves, per digit; the digit's total in this tile
     for (int i = tid; i < bins; i += 256) {
         int32_t run = 0;
 #pragma unroll
@@ -151,17 +222,29 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__rest
             s_wc[ww * bins + i] = run;
             run += v;
         }
+        s_ls[i] = run;
     }
     __syncthreads();
+    block_exscan_1024(s_ls, bins, s_wsum);
+    // lay the tile out in (digit, index) order
 #pragma unroll
     for (int r = 0; r < SORT_ROUNDS; ++r) {
         const int i = tile0 + r * 64 + lane;
         if (i < N) {
             const uint32_t dg = ((uint32_t)key[r] >> shift) & mask;
-            const int32_t dst = s_off[dg] + wc[dg] + pos[r];
-            keys_out[base + dst] = key[r];
-            vals_out[base + dst] = val[r];
+            const int lp = s_ls[dg] + wc[dg] + pos[r];
+            s_k[lp] = key[r];
+            s_v[lp] = val[r];
         }
+    }
+    __syncthreads();
+    const int tile_n = min(SORT_TILE, N - t * SORT_TILE);
+    for (int e = tid; e < tile_n; e += 256) {
+        const int32_t k = s_k[e];
+        const uint32_t dg = ((uint32_t)k >> shift) & mask;
+        const int dst = s_off[dg] + (e - s_ls[dg]);
+        keys_out[base + dst] = k;
+        vals_out[base + dst] = s_v[e];
     }
 }
 
@@ -220,11 +303,17 @@ hipError_t launch_argsort(const int32_t *keys, int B, int N, int K, int32_t *out
         const bool to_out = ((c.passes - 1 - pass) % 2) == 0;
         int32_t *ko = to_out ? out_keys : tk;
         int32_t *vo = to_out ? out_vals : tv;
+        int32_t *cnt_out = (counts && c.passes == 1) ? counts : nullptr;
+        const size_t lds = ((size_t)(SORT_WAVES + 2) * c.bins + 2 * SORT_TILE) * 4;
         sort_hist_kernel<<<dim3(B * c.ntiles), dim3(256), c.bins * 4, s>>>(kin, N, c.ntiles, shift, c.bins, hist);
-        sort_scan_kernel<<<dim3(B), dim3(1024), 0, s>>>(hist, entries, c.ntiles,
-                                                        (counts && c.passes == 1) ? counts : nullptr, K, N);
-        sort_scatter_kernel<<<dim3(B * c.ntiles), dim3(256), (SORT_WAVES + 1) * c.bins * 4, s>>>(
-            kin, vin, hist, N, c.ntiles, shift, c.bits, ko, vo);
+        if (entries <= SORT_INLINE_MAX) {
+            sort_scatter_kernel<true><<<dim3(B * c.ntiles), dim3(256), lds, s>>>(kin, vin, hist, N, c.ntiles, shift,
+                                                                                c.bits, ko, vo, cnt_out, K);
+        } else {
+            sort_scan_kernel<<<dim3(B), dim3(1024), 0, s>>>(hist, entries, c.ntiles, cnt_out, K, N);
+            sort_scatter_kernel<false><<<dim3(B * c.ntiles), dim3(256), lds, s>>>(kin, vin, hist, N, c.ntiles, shift,
+                                                                                 c.bits, ko, vo, nullptr, K);
+        }
         kin = ko;
         vin = vo;
     }

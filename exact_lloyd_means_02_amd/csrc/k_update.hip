@@ -18,9 +18,11 @@ namespace fkm {
 
 hipError_t launch_sum_f64_rows(const double *part, int rows, int64_t len, double *out, hipStream_t s);
 
-// Row loads issued before any is consumed: 16 vectors per lane in flight (16 KiB per wave).
+// Row loads issued before any is consumed: 8 vectors per lane in flight (8 KiB per wave).  With
+// 16 the kernel needs more than 128 VGPRs and only 3 waves fit a SIMD instead of 4; more waves
+// with shallower queues gather faster (measured on the headline shape).
 template <int VPL>
-constexpr int upd_unroll() { return 16 / VPL; }
+constexpr int upd_unroll() { return 8 / VPL; }
 
 struct UpdArgs {
     const void *x;
@@ -173,7 +175,7 @@ __device__ inline float finish_cluster(const UpdArgs &a, int b, int k, int c0, i
 template <int DT, int V, int VPL>
 __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t total_waves) {
     const int lane = threadIdx.x & 63;
-    const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t gw = (int64_t)xcd_remap_rev(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
     if (gw >= total_waves) return;
     const int cbi = (int)(gw % a.ncb);
     const int64_t chunk = gw / a.ncb;
@@ -188,8 +190,20 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
     const int32_t *ib = a.sidx + (size_t)b * N;
     const size_t xb = (size_t)b * N;
 
+    // Sorted ids / indices are read through a sliding window of 128 positions held in two
+    // registers per lane ([wp, wp+64) and [wp+64, wp+128)); the next 64 are loaded as soon as
+    // the walk passes wp+64, so that load overlaps the row gathers of the segments in between.
+    int wp = p0;
+    int cs, ci, ns, ni;
+    {
+        const int q0 = wp + lane, q1 = wp + 64 + lane;
+        cs = q0 < p1 ? sb[q0] : -1;
+        ci = q0 < p1 ? ib[q0] : 0;
+        ns = q1 < p1 ? sb[q1] : -1;
+        ni = q1 < p1 ? ib[q1] : 0;
+    }
     int p = p0;
-    int kraw = sb[p0];
+    int kraw = __shfl(cs, 0);
     bool cin = p0 > 0 && sb[p0 - 1] == kraw;
     int seg_start = p0;
     int rec0 = -1, rec1 = -1, recps = 0;
@@ -201,10 +215,14 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
         for (int e = 0; e < V; ++e) acc[i][e] = 0.f;
 
     while (true) {
-        const int pos = p + lane;
-        const bool have = pos < p1;
-        const int sid = have ? sb[pos] : -1;
-        const int idx = have ? ib[pos] : 0;
+        // the 64 positions from p: lane l takes window slot o + l of the 128
+        const int o = p - wp;  // 0 <= o < 64
+        const int q = o + lane;
+        const int s_lo = __shfl(cs, q & 63), s_hi = __shfl(ns, q & 63);
+        const int i_lo = __shfl(ci, q & 63), i_hi = __shfl(ni, q & 63);
+        const int sid = q < 64 ? s_lo : s_hi;
+        const int idx = q < 64 ? i_lo : i_hi;
+        const bool have = p + lane < p1;
         const uint64_t eq = __ballot(have && sid == kraw);
         const int m = (~eq == 0ull) ? 64 : (int)__builtin_ctzll(~eq);
         constexpr int U = upd_unroll<VPL>();
@@ -251,6 +269,14 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
             }
         }
         p += m;
+        if (p - wp >= 64) {  // slide the window by 64 and prefetch the following 64
+            wp += 64;
+            cs = ns;
+            ci = ni;
+            const int q1 = wp + 64 + lane;
+            ns = q1 < p1 ? sb[q1] : -1;
+            ni = q1 < p1 ? ib[q1] : 0;
+        }
         const bool ended = (m < 64) || (p >= p1);
         if (ended) {
             // sum the row groups: lanes r, r + lanes, r + 2*lanes, ... hold the same columns

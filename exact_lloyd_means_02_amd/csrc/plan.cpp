@@ -22,9 +22,10 @@
 //   * point block of 128 (4 waves x 32), 4 centroid tiles (128 centroids) of accumulators per
 //     wave, D streamed through LDS in chunks of 64 (2-byte) / 32 (fp32) elements so one stage
 //     of x chunk + centroid chunk is 32 KiB, double buffered.
-// Arg-sort: counting passes over digits of the cluster id; one pass when the per-problem scan
-//   table (bins x tiles of 4096 keys) stays <= 2^20 entries and bins <= 4096 (the per-wave
-//   counters, 4 x bins x 4 B, fit LDS); otherwise balanced multi-pass LSD digits.
+// Arg-sort: counting passes over digits of the cluster id; one pass when the per-problem
+//   table (bins x tiles of 4096 keys) stays <= 2^20 entries and bins <= 1024 (LDS of a scatter
+//   workgroup: 6 x bins x 4 B of counters and offsets plus the 32 KiB staged tile); otherwise
+//   balanced multi-pass LSD digits.
 // Update: rows are gathered with 16-byte vector loads when D allows; a row is covered by a
 //   power-of-two number of lanes so one wave load instruction moves 64 x 16 B from 64/lanes
 //   rows; each wave takes `rows` consecutive sorted positions, sized so ~8 waves per SIMD

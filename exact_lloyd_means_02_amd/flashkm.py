@@ -11,7 +11,7 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libflashkm.so")
+LIB_PATH = os.environ.get("FLASHKM_LIB") or os.path.join(HERE, "libflashkm.so")
 
 KM_F32, KM_F16, KM_BF16 = 0, 1, 2
 KM_OK, KM_ERR_INVALID, KM_ERR_UNSUPPORTED, KM_ERR_WORKSPACE, KM_ERR_HIP = 0, -1, -2, -3, -4

@@ -131,7 +131,7 @@ def test_plan_fits_gfx950(fk, name):
     assert p["path"] == (0 if w.D <= (128 if w.dtype == "f32" else 256) else 1)
     assert p["block_n"] == p["waves"] * p["point_blocks"] * 32
     assert (1 << (p["sort_bits"] * p["sort_passes"])) >= w.K
-    assert p["sort_bits"] <= 11
+    assert p["sort_bits"] <= 10
     assert p["upd_rows"] >= 64 and p["upd_lanes"] in (1, 2, 4, 8, 16, 32, 64)
     assert p["assign_wgs"] == w.B * -(-n // p["block_n"])
 
