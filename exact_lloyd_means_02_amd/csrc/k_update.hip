@@ -128,12 +128,13 @@ __device__ inline void load_row(const UpdArgs &a, size_t row_elem0, int c0, int 
 }
 
 // Finish cluster k from the row sum held by the lanes of one row group (lane index r < lanes).
-// mode 0: c_k <- s / n (fp32, IEEE division); returns sum (c_new - c_old)^2 over the lane's
-//         columns and adds sum c~^2 to cn2 when the prepared centroids are refreshed.
+// mode 0: c_k <- s / n (fp32, IEEE division); when shift partials are wanted returns
+//         sum (c_new - c_old)^2 over the lane's columns (c_old prefetched in `cold`); adds
+//         sum c~^2 to cn2 when the prepared centroids are refreshed.
 // mode 1: sums_k += s, cnt_k += n.
-template <int DT, int V, int VPL>
+template <int DT, int V, int VPL, bool SHIFT>
 __device__ inline float finish_cluster(const UpdArgs &a, int b, int k, int c0, int r, const float (&s)[VPL][V], int n,
-                                       bool write_cnt, float &cn2) {
+                                       const float (&cold)[VPL][V], bool write_cnt, float &cn2) {
     float d2 = 0.f;
     const size_t rowo = ((size_t)b * a.K + k) * a.D;
 #pragma unroll
@@ -146,11 +147,12 @@ __device__ inline float finish_cluster(const UpdArgs &a, int b, int k, int c0, i
                 const int d = e0 + e;
                 nw[e] = 0.f;
                 if (d < a.D) {
-                    const float old = a.C[rowo + d];
                     nw[e] = s[i][e] / (float)n;
                     a.C[rowo + d] = nw[e];
-                    const float df = nw[e] - old;
-                    d2 += df * df;
+                    if (SHIFT) {
+                        const float df = nw[e] - cold[i][e];
+                        d2 += df * df;
+                    }
                 }
             }
             if (a.cprep) {
@@ -172,7 +174,9 @@ __device__ inline float finish_cluster(const UpdArgs &a, int b, int k, int c0, i
     return d2;
 }
 
-template <int DT, int V, int VPL>
+// SHIFT: a.shp is set (mode 0 with shift partials wanted); a separate instance keeps the
+// register budget of the common case free of the old-centroid prefetch.
+template <int DT, int V, int VPL, bool SHIFT>
 __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t total_waves) {
     const int lane = threadIdx.x & 63;
     const int64_t gw = (int64_t)xcd_remap_rev(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
@@ -205,6 +209,22 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
     int p = p0;
     int kraw = __shfl(cs, 0);
     bool cin = p0 > 0 && sb[p0 - 1] == kraw;
+    // old centroid columns of the current segment's cluster, fetched when the segment starts
+    // (only for the shift partials), so the read overlaps the segment's row gathers
+    float cold[VPL][V];
+    auto fetch_cold = [&](int kr) {
+        if (SHIFT && g == 0) {
+            const int kc = kr < 0 ? 0 : (kr >= a.K ? a.K - 1 : kr);
+            const size_t rowo = ((size_t)b * a.K + kc) * a.D;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                const int e0 = c0 + (r + i * a.lanes) * V;
+#pragma unroll
+                for (int e = 0; e < V; ++e) cold[i][e] = e0 + e < a.D ? a.C[rowo + e0 + e] : 0.f;
+            }
+        }
+    };
+    fetch_cold(kraw);
     int seg_start = p0;
     int rec0 = -1, rec1 = -1, recps = 0;
     float d2acc = 0.f;
@@ -291,7 +311,7 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
             const int n = p - seg_start;
             if (!cin && !cout) {
                 float cn2 = 0.f;
-                if (g == 0) d2acc += finish_cluster<DT, V, VPL>(a, b, k, c0, r, acc, n, cbi == 0, cn2);
+                if (g == 0) d2acc += finish_cluster<DT, V, VPL, SHIFT>(a, b, k, c0, r, acc, n, cold, cbi == 0, cn2);
                 if (a.cprep) {  // mode 0, ncb == 1
                     for (int off = 1; off < a.lanes; off <<= 1) cn2 += __shfl_xor(cn2, off);
                     if (lane == 0) a.cnh[(size_t)b * a.KT * 32 + k] = 0.5f * cn2;
@@ -312,6 +332,7 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
             }
             if (p >= p1) break;
             kraw = __shfl(sid, m & 63);
+            fetch_cold(kraw);
             cin = false;
             seg_start = p;
 #pragma unroll
@@ -320,7 +341,7 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
                 for (int e = 0; e < V; ++e) acc[i][e] = 0.f;
         }
     }
-    if (a.shp) {  // mode 0
+    if (SHIFT) {  // mode 0
         double d = (double)d2acc;
         for (int off = 1; off < 64; off <<= 1) d += __shfl_xor(d, off);
         if (lane == 0) a.shp[(size_t)chunk * (a.ncb + 1) + cbi] = d;
@@ -490,19 +511,25 @@ size_t update_ws_bytes(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
            align256((size_t)chunks * (u.ncb + 1) * 8);
 }
 
-template <int DT>
-static hipError_t launch_segsum_dt(const UpdArgs &a, int vec, int vpl, int64_t waves, hipStream_t s) {
+template <int DT, bool SHIFT>
+static void launch_segsum_shift(const UpdArgs &a, int vec, int vpl, int64_t waves, hipStream_t s) {
     dim3 grid((unsigned)((waves + 3) / 4)), block(256);
     constexpr int VV = DT == DT_F32 ? 4 : 8;
     if (vec == 1) {
-        if (vpl == 1) upd_segsum_kernel<DT, 1, 1><<<grid, block, 0, s>>>(a, waves);
-        else if (vpl == 2) upd_segsum_kernel<DT, 1, 2><<<grid, block, 0, s>>>(a, waves);
-        else upd_segsum_kernel<DT, 1, 4><<<grid, block, 0, s>>>(a, waves);
+        if (vpl == 1) upd_segsum_kernel<DT, 1, 1, SHIFT><<<grid, block, 0, s>>>(a, waves);
+        else if (vpl == 2) upd_segsum_kernel<DT, 1, 2, SHIFT><<<grid, block, 0, s>>>(a, waves);
+        else upd_segsum_kernel<DT, 1, 4, SHIFT><<<grid, block, 0, s>>>(a, waves);
     } else {
-        if (vpl == 1) upd_segsum_kernel<DT, VV, 1><<<grid, block, 0, s>>>(a, waves);
-        else if (vpl == 2) upd_segsum_kernel<DT, VV, 2><<<grid, block, 0, s>>>(a, waves);
-        else upd_segsum_kernel<DT, VV, 4><<<grid, block, 0, s>>>(a, waves);
+        if (vpl == 1) upd_segsum_kernel<DT, VV, 1, SHIFT><<<grid, block, 0, s>>>(a, waves);
+        else if (vpl == 2) upd_segsum_kernel<DT, VV, 2, SHIFT><<<grid, block, 0, s>>>(a, waves);
+        else upd_segsum_kernel<DT, VV, 4, SHIFT><<<grid, block, 0, s>>>(a, waves);
     }
+}
+
+template <int DT>
+static hipError_t launch_segsum_dt(const UpdArgs &a, int vec, int vpl, int64_t waves, hipStream_t s) {
+    if (a.shp) launch_segsum_shift<DT, true>(a, vec, vpl, waves, s);
+    else launch_segsum_shift<DT, false>(a, vec, vpl, waves, s);
     return hipGetLastError();
 }
 
