@@ -296,7 +296,7 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
 
     // Global -> LDS copy of stage st (TPS tiles and their norms).  Every wave issues exactly
     // NCOPY copy instructions, so it can wait for an older stage with a fixed count.
-    auto stage_copy = [&](int st, u32x4 *sc, float *sn) {
+    auto stage_copy = [&](int st, u32x4 *__restrict__ sc, float *__restrict__ sn) {
         const u32x4 *src = cb + (size_t)st * STAGE_U4;
 #pragma unroll
         for (int r = 0; r < PF; ++r) {
@@ -311,35 +311,40 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
     for (int p = 0; p < PB; ++p) argmin_init(st[p]);
 
     u32x4 f[QG];  // A fragments of the tile being multiplied
+    f32x16 cn;    // half-norms of the tile being multiplied (this lane's 16 rows)
     f32x16 accA[PB], accB[PB];
-    auto load_norms = [&](f32x16 (&acc)[PB], const float *sn, int tt) {
+    auto load_norms = [&](const float *sn, int tt) {
         const float *nrm = sn + tt * 32 + 4 * h;
         const f32x4 c0 = *(const f32x4 *)(nrm + 0), c1 = *(const f32x4 *)(nrm + 8);
         const f32x4 c2 = *(const f32x4 *)(nrm + 16), c3 = *(const f32x4 *)(nrm + 24);
-        const f32x16 cn = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3],
-                           c2[0], c2[1], c2[2], c2[3], c3[0], c3[1], c3[2], c3[3]};
-#pragma unroll
-        for (int p = 0; p < PB; ++p) acc[p] = cn;
+        cn = f32x16{c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3],
+                    c2[0], c2[1], c2[2], c2[3], c3[0], c3[1], c3[2], c3[3]};
     };
-    // One tile: multiply f into accC while refilling f with the next tile's fragments; fold
-    // accF (the previous tile), then load the next tile's norms into accF.  After the last
-    // tile the refills read a stale (in-bounds) buffer and are never used: no branches here.
-    auto step = [&](f32x16 (&accC)[PB], f32x16 (&accF)[PB], int tileF, const u32x4 *nsc, const float *nsn,
-                    int ntt) {
+    // One tile: multiply f into accC (starting from the norms in cn) while refilling f and cn
+    // with the next tile's fragments and norms, each right after its last use, so the LDS
+    // reads have a whole tile to land; fold accF (the previous tile) in the MFMA shadow.  After
+    // the last tile the refills read a stale (in-bounds) buffer and are never used: no
+    // branches here.
+    auto step = [&](f32x16 (&accC)[PB], f32x16 (&accF)[PB], int tileF, const u32x4 *__restrict__ nsc,
+                    const float *__restrict__ nsn, int ntt) {
 #pragma unroll
         for (int q = 0; q < QG; ++q) {
 #pragma unroll
-            for (int p = 0; p < PB; ++p) accC[p] = mfma_group<DT>(f[q], xr[p][q], accC[p]);
+            for (int p = 0; p < PB; ++p) accC[p] = mfma_group<DT>(f[q], xr[p][q], q == 0 ? cn : accC[p]);
             f[q] = nsc[ntt * TILE_U4 + q * 64 + lane];
+            if (q == 0) load_norms(nsn, ntt);
         }
 #pragma unroll
         for (int p = 0; p < PB; ++p) argmin_fold(st[p], accF[p], tileF);
-        load_norms(accF, nsn, ntt);
     };
     // Stage s lives in X; stage s+1 in Y (copied earlier); stage s+2 is copied into Z, which
     // nobody reads any more (its last reads happened before the previous mid-stage barrier).
     // Tile t = TPS*s + i is multiplied into accA for even i, accB for odd i.
-    auto run_stage = [&](int s, u32x4 *xc, float *xn_, u32x4 *yc, float *yn, u32x4 *zc, float *zn) {
+    // The buffer pointers are __restrict__: the alias scopes this gives the LDS reads and the
+    // global->LDS copies let the compiler wait for a copy only where its buffer is read, not
+    // before every LDS read after it (which would stall each stage on the newest copy).
+    auto run_stage = [&](int s, u32x4 *__restrict__ xc, float *__restrict__ xn_, u32x4 *__restrict__ yc,
+                         float *__restrict__ yn, u32x4 *__restrict__ zc, float *__restrict__ zn) {
         const bool copy2 = s + 2 < nst;
         if (copy2) stage_copy(s + 2, zc, zn);
         const int t0 = TPS * s;
@@ -367,7 +372,7 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
     }
 #pragma unroll
     for (int q = 0; q < QG; ++q) f[q] = s_c0[q * 64 + lane];
-    load_norms(accA, s_n0, 0);
+    load_norms(s_n0, 0);
 #pragma unroll
     for (int p = 0; p < PB; ++p)
 #pragma unroll

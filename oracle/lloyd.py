@@ -157,16 +157,21 @@ def argsort_ids(a: np.ndarray, K: int):
     return a[sidx], sidx, counts
 
 
+def segment_sums(x: np.ndarray, a: np.ndarray, K: int):
+    """One problem (or one block of its points): s_k = sum_{a_i = k} x_i and
+    n_k = |{i : a_i = k}|, in fp64.  Returns (sums [K, D], counts [K])."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.asarray(a, dtype=np.int64)
+    sums = np.zeros((K, x.shape[1]), dtype=np.float64)
+    np.add.at(sums, a, x)
+    return sums, np.bincount(a, minlength=K)
+
+
 def update(x: np.ndarray, a: np.ndarray, c_old: np.ndarray):
     """One problem: s_k = sum_{a_i = k} x_i, n_k = |{i : a_i = k}|,
     c_k = s_k / n_k, or the previous c_k when n_k == 0.  Returns (c_new, counts)."""
-    x = np.asarray(x, dtype=np.float64)
     c_old = np.asarray(c_old, dtype=np.float64)
-    a = np.asarray(a, dtype=np.int64)
-    K, D = c_old.shape
-    sums = np.zeros((K, D), dtype=np.float64)
-    np.add.at(sums, a, x)
-    counts = np.bincount(a, minlength=K)
+    sums, counts = segment_sums(x, a, c_old.shape[0])
     c_new = c_old.copy()
     nz = counts > 0
     c_new[nz] = sums[nz] / counts[nz, None]
@@ -237,6 +242,6 @@ def lloyd_fit(x: np.ndarray, c0: np.ndarray, iters: int, tol: float = 0.0, dtype
 
 
 __all__ = [
-    "centroid_operand", "row_norms", "assign", "assign_batched", "dist_to", "near_mask",
+    "centroid_operand", "row_norms", "assign", "assign_batched", "dist_to", "near_mask", "segment_sums",
     "argsort_ids", "update", "inertia", "shift", "lloyd_iteration", "lloyd_fit", "threads",
 ]

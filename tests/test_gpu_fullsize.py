@@ -1,0 +1,283 @@
+"""Parity at the workloads' full sizes, in the launch configuration the benchmark times.
+
+The HIP path runs on the full inputs.  The oracle then checks:
+- outputs it can compute one by one: sampled points for the assignment, sampled clusters
+  for the centroids;
+- outputs that are cheap in full: the arg-sort and the counts of every problem, and the
+  inertia as an O(N*D) sum;
+- properties that hold at any size: streamed vs device-resident labels.
+
+Stages are teacher forced: each stage takes the GPU's own inputs from the previous stage,
+as the parity protocol prescribes.
+"""
+import sys
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+from exact_lloyd_means_02_amd import workloads as W
+
+from helpers import CENTROID_TOL, INERTIA_TOL, check_argsort, check_assign, device, operand
+
+torch = pytest.importorskip("torch")
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+BLOCK = 1 << 20       # points per host-side conversion block
+
+
+@pytest.fixture(scope="module")
+def fk():
+    from exact_lloyd_means_02_amd import flashkm
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return flashkm
+
+
+T0 = time.time()
+
+
+def _say(msg):
+    print("[%6.1fs] %s" % (time.time() - T0, msg), flush=True)
+    sys.stdout.flush()
+
+
+def _rows64(x, w, b, idx):
+    return W.storage_to_f64(x[b, idx], w.dtype)
+
+
+def _inertia_oracle(x, w, ct64, a_np):
+    """sum_i ||x_i - c~_{a_i}||^2 per problem, in blocks (oracle.dist_to per block)."""
+    B, N = a_np.shape
+    J = np.zeros(B)
+    for b in range(B):
+        for lo in range(0, N, BLOCK):
+            xb = W.storage_to_f64(x[b, lo:lo + BLOCK], w.dtype)
+            J[b] += float(np.sum(oracle.dist_to(xb, ct64[b], a_np[b, lo:lo + BLOCK])))
+    return J
+
+
+def _check_cluster_sample(x, w, c_old, a_np, counts_gpu, c_new_gpu, ks_per_problem):
+    """Counts of every cluster; centroids of the sampled clusters (oracle segment sums over the
+    GPU's assignment); empty clusters bit-identical to the old centroids."""
+    B, K = counts_gpu.shape
+    tol = CENTROID_TOL[w.dtype]
+    worst = 0.0
+    for b in range(B):
+        n_or = np.bincount(a_np[b], minlength=K)
+        assert np.array_equal(n_or, counts_gpu[b]), "counts differ in problem %d" % b
+        empty = n_or == 0
+        assert np.array_equal(c_new_gpu[b][empty], c_old[b][empty]), "empty clusters changed"
+        for k in ks_per_problem[b]:
+            rows = np.nonzero(a_np[b] == k)[0]
+            if rows.size == 0:
+                continue
+            s = np.zeros(x.shape[2])
+            for lo in range(0, rows.size, BLOCK):
+                r = rows[lo:lo + BLOCK]
+                sk, nk = oracle.segment_sums(_rows64(x, w, b, r), np.zeros(r.size, dtype=np.int64), 1)
+                s += sk[0]
+            c_or = s / rows.size
+            rel = np.linalg.norm(c_new_gpu[b, k].astype(np.float64) - c_or) / max(np.linalg.norm(c_or), 1e-30)
+            worst = max(worst, rel)
+            assert rel <= tol, "problem %d cluster %d (n=%d): centroid rel err %g > %g" % (b, k, rows.size, rel, tol)
+    return worst
+
+
+def _stage_parity(fk, w, x, c0, xt, ct, n_assign, n_clusters, seed):
+    """One teacher-forced iteration at full size; returns the GPU labels (numpy)."""
+    B, N, D, K = w.B, w.N, w.D, w.K
+    ct64 = operand(c0, w.dtype)
+    xn = fk.kmeans_row_norms(xt)
+    prep = fk.kmeans_prepare_centroids(ct, xt)
+    a, md = fk.kmeans_assign_prepared(xt, prep, x_norms=xn, want_min_dist=True)
+    s, i, cnt = fk.kmeans_argsort_ids(a, K)
+    cu = ct.clone()
+    shift = fk.kmeans_update(xt, s, i, cnt, cu, want_shift=True)
+    torch.cuda.synchronize()
+    a_np, md_np = a.cpu().numpy(), md.cpu().numpy()
+    s_np, i_np, cnt_np = s.cpu().numpy(), i.cpu().numpy(), cnt.cpu().numpy()
+    c_new = cu.cpu().numpy()
+    shift_np = shift.cpu().numpy()
+    _say("GPU stages done")
+
+    rng = np.random.default_rng(seed)
+    samp = [np.sort(rng.choice(N, size=min(N, n_assign), replace=False)) for _ in range(B)]
+    x64s = np.stack([_rows64(x, w, b, samp[b]) for b in range(B)])
+    a_s = np.stack([a_np[b, samp[b]] for b in range(B)])
+    md_s = np.stack([md_np[b, samp[b]] for b in range(B)])
+    flips = check_assign(x64s, ct64, a_s, md_s)
+    _say("assign: %d sampled points per problem, %d near-tie flips" % (n_assign, flips))
+
+    check_argsort(a_np, K, s_np, i_np, cnt_np)
+    _say("arg-sort and counts: all %d problems bit-exact" % B)
+
+    ks = []
+    for b in range(B):
+        hot = np.argsort(-cnt_np[b], kind="stable")[:4]            # the largest segments
+        rnd = rng.choice(K, size=min(K, n_clusters), replace=False)
+        ks.append(np.unique(np.concatenate([hot, rnd])))
+    worst = _check_cluster_sample(x, w, c0, a_np, cnt_np, c_new, ks)
+    _say("update: %d sampled clusters per problem, worst rel err %.3g" % (len(ks[0]), worst))
+
+    # shift = sum_k ||c_new - c_old||^2 of the GPU's own centroids (fp64), per problem
+    for b in range(B):
+        s_or = float(np.sum((c_new[b].astype(np.float64) - c0[b].astype(np.float64)) ** 2))
+        assert abs(shift_np[b] - s_or) <= 1e-5 * max(s_or, 1e-30) + 1e-12
+    return a_np, ct64
+
+
+def _fit_inertia_check(fk, w, x, c0, xt, ct, a_stage):
+    """kmeans_fit for one iteration: same labels as the stage calls, inertia against the oracle."""
+    c = ct.clone()
+    a, J, done = fk.kmeans_fit(xt, c, 1, 0.0)
+    a_np = a.cpu().numpy()
+    assert done == 1
+    assert np.array_equal(a_np, a_stage), "kmeans_fit labels differ from the stage calls"
+    J_or = _inertia_oracle(x, w, operand(c0, w.dtype), a_np)
+    rel = np.abs(J[0] - J_or) / np.abs(J_or)
+    _say("fit inertia: max rel diff %.3g" % rel.max())
+    assert rel.max() <= INERTIA_TOL
+
+
+# ---------------------------------------------------------------------------------------------
+# headline: B=32, N=65536, D=128, K=1024, bf16 (the benchmark's workload)
+# ---------------------------------------------------------------------------------------------
+def test_headline_full(fk):
+    w = W.WORKLOADS["headline_bf16"]
+    _say("headline: generating %s" % (w,))
+    x, c0, _ = W.make(w)
+    xt = W.to_torch(x, w.dtype).to(device())
+    ct = torch.from_numpy(c0).to(device())
+    a_np, _ = _stage_parity(fk, w, x, c0, xt, ct, n_assign=512, n_clusters=32, seed=31)
+    _fit_inertia_check(fk, w, x, c0, xt, ct, a_np)
+    # free-running: two iterations of the fit against the oracle's loop in modelled mode
+    c = ct.clone()
+    _, J, done = fk.kmeans_fit(xt, c, 2, 0.0)
+    x64 = W.storage_to_f64(x, w.dtype)
+    ref = oracle.lloyd_fit(x64, c0, 2, 0.0, dtype=w.dtype, mode="modelled")
+    rel = np.abs(J - ref["inertia"]) / np.abs(ref["inertia"])
+    _say("free-running 2 iterations: max inertia rel diff %.3g" % rel.max())
+    assert done == 2 and rel.max() <= INERTIA_TOL
+
+
+# ---------------------------------------------------------------------------------------------
+# batched fp16: B=32, N=75600, D=128, K=1000, tol 1e-4
+# ---------------------------------------------------------------------------------------------
+def test_batched_f16_full(fk):
+    w = W.WORKLOADS["batched_f16"]
+    _say("batched f16: generating %s" % (w,))
+    x, c0, _ = W.make(w)
+    xt = W.to_torch(x, w.dtype).to(device())
+    ct = torch.from_numpy(c0).to(device())
+    a_np, _ = _stage_parity(fk, w, x, c0, xt, ct, n_assign=384, n_clusters=24, seed=32)
+    _fit_inertia_check(fk, w, x, c0, xt, ct, a_np)
+    # the stopping rule: run one iteration at a time and take the oracle's fp64 shift of the
+    # GPU's own centroids; the multi-iteration fit must stop after the first iteration whose
+    # shift is below tol (decided only where no shift lies within 1% of tol: the one-at-a-time
+    # run recomputes the prepared centroids, so its trajectory may differ in near ties)
+    c = ct.clone()
+    c_prev = c0.astype(np.float64)
+    shifts = []
+    for t in range(w.iters):
+        fk.kmeans_fit(xt, c, 1, 0.0)
+        c_now = c.cpu().numpy().astype(np.float64)
+        shifts.append(float(np.max(oracle.shift(c_now, c_prev))))
+        c_prev = c_now
+    _say("shift per iteration (oracle, fp64): %s, tol %g" % (["%.4g" % v for v in shifts], w.tol))
+    below = [t for t, v in enumerate(shifts) if v < w.tol]
+    expect = below[0] + 1 if below else w.iters
+    c = ct.clone()
+    _, J, done = fk.kmeans_fit(xt, c, w.iters, w.tol)
+    _say("fit with tol: %d iterations (expected %d)" % (done, expect))
+    if all(abs(v - w.tol) > 1e-2 * w.tol for v in shifts[:expect]):
+        assert done == expect
+
+
+# ---------------------------------------------------------------------------------------------
+# skewed large N: B=1, N=2^24, D=128, bf16, K in {64, 4096}, Zipf(1.2) clusters, centred
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["skew_bf16_k64", "skew_bf16_k4096"])
+def test_skew_full(fk, name):
+    w = W.WORKLOADS[name]
+    _say("skew: generating %s" % (w,))
+    x, c0, mu = W.make(w)
+    _say("centring translation, channels 0-3: %s" % np.round(mu[0, :4], 3).tolist())
+    xt = W.to_torch(x, w.dtype).to(device())
+    ct = torch.from_numpy(c0).to(device())
+    a_np, ct64 = _stage_parity(fk, w, x, c0, xt, ct, n_assign=8192, n_clusters=12, seed=33)
+    hot = np.bincount(a_np[0], minlength=w.K).max() / w.N
+    _say("largest cluster holds %.1f%% of the points" % (100 * hot))
+    _fit_inertia_check(fk, w, x, c0, xt, ct, a_np)
+    # the whole run: inertia non-increasing up to the bf16 rounding of the centroids
+    c = ct.clone()
+    _, J, done = fk.kmeans_fit(xt, c, w.iters, 0.0)
+    _say("fit %d iterations: inertia %s" % (done, np.round(J[:, 0], 1).tolist()))
+    assert done == w.iters and (J[1:, 0] <= J[:-1, 0] * (1 + 1e-3)).all()
+
+
+# ---------------------------------------------------------------------------------------------
+# split-D: B=1, N=262144, D=1024, K=512, fp32
+# ---------------------------------------------------------------------------------------------
+def test_splitd_full(fk):
+    w = W.WORKLOADS["splitd_f32"]
+    assert fk.kmeans_plan(0, w.B, w.N, w.D, w.K)["path"] == 1
+    _say("split-D: generating %s" % (w,))
+    x, c0, _ = W.make(w)
+    xt = W.to_torch(x, w.dtype).to(device())
+    ct = torch.from_numpy(c0).to(device())
+    a_np, _ = _stage_parity(fk, w, x, c0, xt, ct, n_assign=2048, n_clusters=48, seed=34)
+    _fit_inertia_check(fk, w, x, c0, xt, ct, a_np)
+    c = ct.clone()
+    _, J, done = fk.kmeans_fit(xt, c, w.iters, 0.0)
+    x64 = W.storage_to_f64(x, w.dtype)
+    ref = oracle.lloyd_fit(x64, c0, w.iters, 0.0, dtype=w.dtype, mode="modelled")
+    rel = np.abs(J - ref["inertia"]) / np.abs(ref["inertia"])
+    _say("free-running %d iterations: max inertia rel diff %.3g" % (w.iters, rel.max()))
+    assert done == w.iters and rel.max() <= INERTIA_TOL
+
+
+# ---------------------------------------------------------------------------------------------
+# streamed: D=64, K=32768, fp16 in pinned host memory, real 2^24-point chunks (two full chunks
+# and a ragged one; the full 2^30-point run differs only in the number of chunks)
+# ---------------------------------------------------------------------------------------------
+def test_streamed_real_chunks(fk):
+    w0 = W.WORKLOADS["streamed_f16"]
+    N = 2 * w0.chunk + 12345
+    w = W.small("streamed_f16", N=N, iters=1)
+    assert w.K == 32768 and w.D == 64 and w.chunk == 1 << 24
+    _say("streamed: generating %s" % (w,))
+    xh = torch.empty((w.B, w.N, w.D), dtype=W.torch_dtype(w.dtype), pin_memory=True)
+    x = W.from_torch(xh, w.dtype)                         # numpy view of the pinned buffer
+    W.generate_points(w, x)
+    c0 = W.init_centroids(w, x)
+    ct = torch.from_numpy(c0).to(device())
+    c_s = ct.clone()
+    a_s, J_s, done = fk.kmeans_fit(xh, c_s, 1, 0.0, chunk_points=w.chunk)
+    torch.cuda.synchronize()
+    _say("streamed fit done")
+    xt = xh.to(device())
+    c_d = ct.clone()
+    a_d, J_d, _ = fk.kmeans_fit(xt, c_d, 1, 0.0)
+    a_np = a_s.cpu().numpy()
+    # labels do not depend on the chunking: identical to the device-resident run
+    assert np.array_equal(a_np, a_d.cpu().numpy())
+    ct64 = operand(c0, w.dtype)
+    rng = np.random.default_rng(35)
+    samp = np.sort(rng.choice(w.N, size=1 << 12, replace=False))
+    flips = check_assign(_rows64(x, w, 0, samp)[None], ct64, a_np[:, samp])
+    _say("assign: 4096 sampled points, %d near-tie flips" % flips)
+    counts = np.bincount(a_np[0], minlength=w.K)[None].astype(np.int32)
+    ks = [np.unique(np.concatenate([np.argsort(-counts[0], kind="stable")[:4],
+                                    rng.choice(w.K, size=48, replace=False)]))]
+    worst = _check_cluster_sample(x, w, c0, a_np, counts, c_s.cpu().numpy(), ks)
+    _say("streamed update: worst rel err over %d clusters %.3g" % (len(ks[0]), worst))
+    J_or = _inertia_oracle(x, w, ct64, a_np)
+    rel = abs(J_s[0, 0] - J_or[0]) / J_or[0]
+    _say("streamed inertia rel diff %.3g (device-resident %.3g)" % (rel, abs(J_d[0, 0] - J_or[0]) / J_or[0]))
+    assert rel <= INERTIA_TOL
+    # the two runs sum the same points in different orders: centroids agree to fp32 rounding
+    cs, cd = c_s.cpu().numpy(), c_d.cpu().numpy()
+    num = np.linalg.norm(cs - cd, axis=2)
+    den = np.maximum(np.linalg.norm(cd, axis=2), 1e-30)
+    assert (num / den).max() <= 1e-5

@@ -248,3 +248,27 @@ def test_f16_and_f32_operand_rounding():
     assert oracle.centroid_operand(vals, "f32").tolist() == [float(np.float32(1 + 2 ** -11)), 2049.0,
                                                             1 + 2 ** -23]
     assert (oracle.centroid_operand(vals, "bf16", mode="pure") == vals).all()
+
+
+def test_segment_sums_brute_force_and_blocks():
+    """s_k and n_k by explicit loops on a tiny input; sums over disjoint blocks of points add up
+    to the sums over all points (the streamed and full-size checks rely on this)."""
+    rng = np.random.default_rng(11)
+    x = rng.normal(size=(37, 5))
+    a = rng.integers(0, 6, size=37)
+    a[a == 4] = 5                                     # cluster 4 empty
+    sums, counts = oracle.segment_sums(x, a, 6)
+    for k in range(6):
+        want = np.zeros(5)
+        n = 0
+        for i in range(37):
+            if a[i] == k:
+                want += x[i]
+                n += 1
+        assert counts[k] == n
+        assert np.allclose(sums[k], want, rtol=0, atol=1e-12)
+    assert counts[4] == 0 and not sums[4].any()
+    s1, n1 = oracle.segment_sums(x[:20], a[:20], 6)
+    s2, n2 = oracle.segment_sums(x[20:], a[20:], 6)
+    assert np.array_equal(n1 + n2, counts)
+    assert np.allclose(s1 + s2, sums, rtol=0, atol=1e-12)
