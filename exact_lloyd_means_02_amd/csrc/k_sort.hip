@@ -5,10 +5,11 @@
 // LSD counting passes over digits of the cluster id.  Per pass:
 //   1. hist:    each workgroup counts the digits of its tile of 4096 keys in LDS and writes
 //               one column of the [bins][tiles] table of its problem;
-//   2. offsets: where a problem has few tiles (bins x tiles <= SORT_INLINE_MAX) every scatter
-//               workgroup derives its own offsets from the table (sum over earlier tiles plus
-//               an exclusive scan of the digit totals); otherwise one scan workgroup per problem
-//               turns the table into offsets in (digit-major, tile-minor) order first;
+//   2. offsets: where a problem has few tiles (<= SORT_INLINE_TILES) the table is stored
+//               tile-major and every scatter workgroup derives its own offsets from it (sum over
+//               earlier tiles plus an exclusive scan of the digit totals); otherwise one scan
+//               workgroup per problem turns the digit-major table into offsets in (digit-major,
+//               tile-minor) order first;
 //   3. scatter: each wave ranks its keys 64 at a time, in index order: lanes holding the same
 //               digit are found with one ballot per digit bit; a lane's rank = earlier peers
 //               in the round + the wave's running count of that digit (LDS).  The tile is
@@ -25,8 +26,11 @@ namespace fkm {
 constexpr int SORT_WAVES = 4;
 constexpr int SORT_ROUNDS = SORT_TILE / (SORT_WAVES * 64);  // 16
 
+// tile_major: the table is [tiles][bins] (each workgroup writes one contiguous row); otherwise
+// [bins][tiles] (one column per workgroup, the order the scan kernel needs).
 __global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t *__restrict__ keys, int N, int ntiles,
-                                                        int shift, int bins, int32_t *__restrict__ hist) {
+                                                        int shift, int bins, int32_t *__restrict__ hist,
+                                                        int tile_major) {
     extern __shared__ int32_t s_h[];
     const int lb = xcd_remap(blockIdx.x, gridDim.x);
     const int b = lb / ntiles, t = lb - b * ntiles;
@@ -35,10 +39,23 @@ __global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t *__restric
     const int32_t *kb = keys + (size_t)b * N;
     const int lo = t * SORT_TILE, hi = min(N, lo + SORT_TILE);
     const uint32_t mask = (uint32_t)bins - 1u;
-    for (int i = lo + threadIdx.x; i < hi; i += 256) atomicAdd(&s_h[((uint32_t)kb[i] >> shift) & mask], 1);
+    // all 16 keys of the thread are loaded before the first count
+    constexpr int PER = SORT_TILE / 256;
+    int32_t kv[PER];
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+        const int i = lo + r * 256 + (int)threadIdx.x;
+        kv[r] = i < hi ? kb[i] : -1;
+    }
+#pragma unroll
+    for (int r = 0; r < PER; ++r)
+        if (kv[r] >= 0) atomicAdd(&s_h[((uint32_t)kv[r] >> shift) & mask], 1);
     __syncthreads();
     int32_t *hb = hist + (size_t)b * bins * ntiles;
-    for (int i = threadIdx.x; i < bins; i += 256) hb[(size_t)i * ntiles + t] = s_h[i];
+    if (tile_major)
+        for (int i = threadIdx.x; i < bins; i += 256) hb[(size_t)t * bins + i] = s_h[i];
+    else
+        for (int i = threadIdx.x; i < bins; i += 256) hb[(size_t)i * ntiles + t] = s_h[i];
 }
 
 // Exclusive scan of one problem's [bins][tiles] table, in place.  1024 threads; each pass
@@ -152,29 +169,42 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__rest
     const int32_t *hb = hist + (size_t)b * bins * ntiles;
     for (int i = tid; i < SORT_WAVES * bins; i += 256) s_wc[i] = 0;
     if constexpr (INLINE) {
-        int32_t pre[4];
+        // `hist` is [tiles][bins]: thread tid sums the rows of its four consecutive digits
+        // (16-byte loads, all issued before the sums): the total over all tiles and the sum over
+        // the tiles before this one
+        const int i0 = 4 * tid;
+        int32_t tot[4] = {0, 0, 0, 0}, pre[4] = {0, 0, 0, 0};
+        if (i0 < bins) {
+            for (int tt0 = 0; tt0 < ntiles; tt0 += 16) {
+                int4 hv[16];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int i = tid + 256 * j;
-            pre[j] = 0;
-            if (i < bins) {
-                int32_t tot = 0, pr = 0;
-                for (int tt = 0; tt < ntiles; ++tt) {
-                    const int32_t h = hb[(size_t)i * ntiles + tt];
-                    tot += h;
-                    pr += tt < t ? h : 0;
+                for (int u = 0; u < 16; ++u)
+                    hv[u] = tt0 + u < ntiles ? *(const int4 *)(hb + (size_t)(tt0 + u) * bins + i0)
+                                             : make_int4(0, 0, 0, 0);
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    const bool before = tt0 + u < t;
+                    tot[0] += hv[u].x;
+                    tot[1] += hv[u].y;
+                    tot[2] += hv[u].z;
+                    tot[3] += hv[u].w;
+                    pre[0] += before ? hv[u].x : 0;
+                    pre[1] += before ? hv[u].y : 0;
+                    pre[2] += before ? hv[u].z : 0;
+                    pre[3] += before ? hv[u].w : 0;
                 }
-                s_off[i] = tot;
-                pre[j] = pr;
-                if (counts && t == 0 && i < K) counts[(size_t)b * K + i] = tot;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                s_off[i0 + e] = tot[e];
+                if (counts && t == 0 && i0 + e < K) counts[(size_t)b * K + i0 + e] = tot[e];
             }
         }
         __syncthreads();
         block_exscan_1024(s_off, bins, s_wsum);
+        if (i0 < bins) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int i = tid + 256 * j;
-            if (i < bins) s_off[i] += pre[j];
+            for (int e = 0; e < 4; ++e) s_off[i0 + e] += pre[e];
         }
     } else {
         for (int i = tid; i < bins; i += 256) s_off[i] = hb[(size_t)i * ntiles + t];
@@ -305,8 +335,10 @@ hipError_t launch_argsort(const int32_t *keys, int B, int N, int K, int32_t *out
         int32_t *vo = to_out ? out_vals : tv;
         int32_t *cnt_out = (counts && c.passes == 1) ? counts : nullptr;
         const size_t lds = ((size_t)(SORT_WAVES + 2) * c.bins + 2 * SORT_TILE) * 4;
-        sort_hist_kernel<<<dim3(B * c.ntiles), dim3(256), c.bins * 4, s>>>(kin, N, c.ntiles, shift, c.bins, hist);
-        if (entries <= SORT_INLINE_MAX) {
+        const bool inline_offsets = c.bins >= 4 && c.ntiles <= SORT_INLINE_TILES;
+        sort_hist_kernel<<<dim3(B * c.ntiles), dim3(256), c.bins * 4, s>>>(kin, N, c.ntiles, shift, c.bins, hist,
+                                                                            inline_offsets ? 1 : 0);
+        if (inline_offsets) {
             sort_scatter_kernel<true><<<dim3(B * c.ntiles), dim3(256), lds, s>>>(kin, vin, hist, N, c.ntiles, shift,
                                                                                 c.bits, ko, vo, cnt_out, K);
         } else {

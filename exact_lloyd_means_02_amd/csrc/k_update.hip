@@ -458,8 +458,16 @@ __global__ __launch_bounds__(256) void upd_combine_kernel(UpdArgs a, int64_t nch
     const size_t rowo = ((size_t)b * a.K + kk[w]) * D;
     float d2 = 0.f, cn2 = 0.f;
     for (int d = lane; d < D; d += 64) {
-        float sum = a.part[((size_t)chunk * 2 + 1) * D + d];
-        for (int j = 1; j < np[w]; ++j) sum += a.part[((size_t)(chunk + j) * 2) * D + d];
+        // every piece is loaded before the in-order sum (the loads are independent)
+        float pv[COMBINE_WAVE_MAX];
+        pv[0] = a.part[((size_t)chunk * 2 + 1) * D + d];
+#pragma unroll
+        for (int j = 1; j < COMBINE_WAVE_MAX; ++j)
+            pv[j] = j < np[w] ? a.part[((size_t)(chunk + j) * 2) * D + d] : 0.f;
+        float sum = pv[0];
+#pragma unroll
+        for (int j = 1; j < COMBINE_WAVE_MAX; ++j)
+            if (j < np[w]) sum += pv[j];
         d2 += combine_finish_col(a, b, kk[w], rowo, d, sum, nkk[w], cn2);
     }
     if (a.mode == 0) {
