@@ -197,25 +197,83 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
     // Sorted ids / indices are read through a sliding window of 128 positions held in two
     // registers per lane ([wp, wp+64) and [wp+64, wp+128)); the next 64 are loaded as soon as
     // the walk passes wp+64, so that load overlaps the row gathers of the segments in between.
-    int wp = p0;
-    int cs, ci, ns, ni;
-    {
+    int wp = p0, cs, ci, ns, ni;
+    auto load_window = [&](int pos) {
+        wp = pos;
         const int q0 = wp + lane, q1 = wp + 64 + lane;
-        cs = q0 < p1 ? sb[q0] : -1;
-        ci = q0 < p1 ? ib[q0] : 0;
-        ns = q1 < p1 ? sb[q1] : -1;
-        ni = q1 < p1 ? ib[q1] : 0;
-    }
-    int p = p0;
-    int kraw = __shfl(cs, 0);
+        cs = q0 < N ? sb[q0] : -1;
+        ci = q0 < N ? ib[q0] : 0;
+        ns = q1 < N ? sb[q1] : -1;
+        ni = q1 < N ? ib[q1] : 0;
+    };
+    auto slide_if_past = [&](int pos) {  // keep pos - wp < 64 (pos advanced by at most 64)
+        if (pos - wp >= 64) {
+            wp += 64;
+            cs = ns;
+            ci = ni;
+            const int q1 = wp + 64 + lane;
+            ns = q1 < N ? sb[q1] : -1;
+            ni = q1 < N ? ib[q1] : 0;
+        }
+    };
+    // the 64 positions from pos: lane l takes window slot pos - wp + l of the 128
+    auto view = [&](int pos, int &sid, int &idx) {
+        const int q = pos - wp + lane;
+        const int s_lo = __shfl(cs, q & 63), s_hi = __shfl(ns, q & 63);
+        const int i_lo = __shfl(ci, q & 63), i_hi = __shfl(ni, q & 63);
+        sid = q < 64 ? s_lo : s_hi;
+        idx = q < 64 ? i_lo : i_hi;
+    };
+    // positions of id k from pos on (at most 64, stopping at lim), given the view at pos
+    auto run_len = [&](int pos, int sid, int k, int lim) -> int {
+        const uint64_t eq = __ballot(pos + lane < lim && sid == k);
+        return (~eq == 0ull) ? 64 : (int)__builtin_ctzll(~eq);
+    };
+    auto clampk = [&](int kr) { return kr < 0 ? 0 : (kr >= a.K ? a.K - 1 : kr); };
+
+    load_window(p0);
+    int p = p0, plim = p1;
+    int sid, idx;
+    view(p, sid, idx);
+    int kraw = __shfl(sid, 0);
     bool cin = p0 > 0 && sb[p0 - 1] == kraw;
+    // Segment ownership: a segment that ends within the chunk after the one where it starts is
+    // summed entirely by the wave of its first chunk (which runs past its chunk end for it);
+    // only segments spanning three or more chunks leave partials for the combine kernel.  A
+    // wave whose chunk starts inside a segment finds the segment's end from the ids alone and
+    // its start from the count, and skips it when the previous chunk's wave owns it.
+    bool done = false;
+    if (cin) {
+        int e = p;
+        while (true) {
+            const int m = run_len(e, sid, kraw, p1);
+            e += m;
+            slide_if_past(e);
+            if (m < 64 || e >= p1) break;
+            view(e, sid, idx);
+        }
+        const bool ends_here = e < p1 || p1 == N || sb[p1] != kraw;
+        const int s_start = e - a.counts[(size_t)b * a.K + clampk(kraw)];
+        if (ends_here && s_start >= p0 - a.R) {
+            p = e;
+            if (p >= p1) {
+                done = true;
+            } else {
+                view(p, sid, idx);
+                kraw = __shfl(sid, 0);
+                cin = false;
+            }
+        } else {
+            load_window(p0);  // shared segment: sum this chunk's part after all
+            view(p, sid, idx);
+        }
+    }
     // old centroid columns of the current segment's cluster, fetched when the segment starts
     // (only for the shift partials), so the read overlaps the segment's row gathers
     float cold[VPL][V];
     auto fetch_cold = [&](int kr) {
         if (SHIFT && g == 0) {
-            const int kc = kr < 0 ? 0 : (kr >= a.K ? a.K - 1 : kr);
-            const size_t rowo = ((size_t)b * a.K + kc) * a.D;
+            const size_t rowo = ((size_t)b * a.K + clampk(kr)) * a.D;
 #pragma unroll
             for (int i = 0; i < VPL; ++i) {
                 const int e0 = c0 + (r + i * a.lanes) * V;
@@ -225,7 +283,7 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
         }
     };
     fetch_cold(kraw);
-    int seg_start = p0;
+    int seg_start = p;
     int rec0 = -1, rec1 = -1, recps = 0;
     float d2acc = 0.f;
     float acc[VPL][V];
@@ -234,18 +292,43 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
 #pragma unroll
         for (int e = 0; e < V; ++e) acc[i][e] = 0.f;
 
-    while (true) {
-        // the 64 positions from p: lane l takes window slot o + l of the 128
-        const int o = p - wp;  // 0 <= o < 64
-        const int q = o + lane;
-        const int s_lo = __shfl(cs, q & 63), s_hi = __shfl(ns, q & 63);
-        const int i_lo = __shfl(ci, q & 63), i_hi = __shfl(ni, q & 63);
-        const int sid = q < 64 ? s_lo : s_hi;
-        const int idx = q < 64 ? i_lo : i_hi;
-        const bool have = p + lane < p1;
-        const uint64_t eq = __ballot(have && sid == kraw);
-        const int m = (~eq == 0ull) ? 64 : (int)__builtin_ctzll(~eq);
-        constexpr int U = upd_unroll<VPL>();
+    // The summed segment ends: add the row groups and finish the cluster, or leave a partial
+    // for the combine kernel when the segment is cut by a chunk edge (cin / cout).
+    auto end_segment = [&](int kr, int n, bool s_cout) {
+        // sum the row groups: lanes r, r + lanes, r + 2*lanes, ... hold the same columns
+        for (int off = a.lanes; off < 64; off <<= 1) {
+#pragma unroll
+            for (int i = 0; i < VPL; ++i)
+#pragma unroll
+                for (int e = 0; e < V; ++e) acc[i][e] += __shfl_xor(acc[i][e], off);
+        }
+        const int k = clampk(kr);
+        if (!cin && !s_cout) {
+            float cn2 = 0.f;
+            if (g == 0) d2acc += finish_cluster<DT, V, VPL, SHIFT>(a, b, k, c0, r, acc, n, cold, cbi == 0, cn2);
+            if (a.cprep) {  // mode 0, ncb == 1
+                for (int off = 1; off < a.lanes; off <<= 1) cn2 += __shfl_xor(cn2, off);
+                if (lane == 0) a.cnh[(size_t)b * a.KT * 32 + k] = 0.5f * cn2;
+            }
+        } else {
+            const int slot = cin ? 0 : 1;
+            if (g == 0) {
+                float *dst = a.part + ((size_t)chunk * 2 + slot) * a.D;
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) {
+                    const int e0 = c0 + (r + i * a.lanes) * V;
+#pragma unroll
+                    for (int e = 0; e < V; ++e)
+                        if (e0 + e < a.D) dst[e0 + e] = acc[i][e];
+                }
+            }
+            if (slot == 0) rec0 = k; else { rec1 = k; recps = seg_start; }
+        }
+    };
+    constexpr int U = upd_unroll<VPL>();
+
+    while (!done) {
+        const int m = run_len(p, sid, kraw, plim);
         for (int base = 0; base < m; base += G * U) {
             if constexpr (V == 1) {
                 float tmp[U][VPL][V];
@@ -281,57 +364,33 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
                 for (int u = 0; u < U; ++u)
 #pragma unroll
                     for (int i = 0; i < VPL; ++i) {
-                        float f[V];
-                        widen16<DT>(raw[u][i], f);
+                        float fv[V];
+                        widen16<DT>(raw[u][i], fv);
 #pragma unroll
-                        for (int e = 0; e < V; ++e) acc[i][e] += f[e];
+                        for (int e = 0; e < V; ++e) acc[i][e] += fv[e];
                     }
             }
         }
+        const int next_k = __shfl(sid, m & 63);  // id at p + m (when m < 64)
         p += m;
-        if (p - wp >= 64) {  // slide the window by 64 and prefetch the following 64
-            wp += 64;
-            cs = ns;
-            ci = ni;
-            const int q1 = wp + 64 + lane;
-            ns = q1 < p1 ? sb[q1] : -1;
-            ni = q1 < p1 ? ib[q1] : 0;
-        }
-        const bool ended = (m < 64) || (p >= p1);
-        if (ended) {
-            // sum the row groups: lanes r, r + lanes, r + 2*lanes, ... hold the same columns
-            for (int off = a.lanes; off < 64; off <<= 1) {
-#pragma unroll
-                for (int i = 0; i < VPL; ++i)
-#pragma unroll
-                    for (int e = 0; e < V; ++e) acc[i][e] += __shfl_xor(acc[i][e], off);
-            }
-            const int k = kraw < 0 ? 0 : (kraw >= a.K ? a.K - 1 : kraw);
-            const bool cout = (p >= p1) && (p1 < N) && (sb[p1] == kraw);
-            const int n = p - seg_start;
-            if (!cin && !cout) {
-                float cn2 = 0.f;
-                if (g == 0) d2acc += finish_cluster<DT, V, VPL, SHIFT>(a, b, k, c0, r, acc, n, cold, cbi == 0, cn2);
-                if (a.cprep) {  // mode 0, ncb == 1
-                    for (int off = 1; off < a.lanes; off <<= 1) cn2 += __shfl_xor(cn2, off);
-                    if (lane == 0) a.cnh[(size_t)b * a.KT * 32 + k] = 0.5f * cn2;
-                }
+        slide_if_past(p);
+        bool ended = (m < 64) || (p >= plim);
+        bool cout = false;
+        if (p >= plim && plim == p1 && p1 < N && sb[p1] == kraw) {
+            // the segment runs past the chunk end: take all of it when it ends within the
+            // next chunk and started in this one
+            const int e = seg_start + a.counts[(size_t)b * a.K + clampk(kraw)];
+            if (!cin && e <= p1 + a.R) {
+                plim = e;
+                ended = false;
             } else {
-                const int slot = cin ? 0 : 1;
-                if (g == 0) {
-                    float *dst = a.part + ((size_t)chunk * 2 + slot) * a.D;
-#pragma unroll
-                    for (int i = 0; i < VPL; ++i) {
-                        const int e0 = c0 + (r + i * a.lanes) * V;
-#pragma unroll
-                        for (int e = 0; e < V; ++e)
-                            if (e0 + e < a.D) dst[e0 + e] = acc[i][e];
-                    }
-                }
-                if (slot == 0) rec0 = k; else { rec1 = k; recps = seg_start; }
+                cout = true;
             }
-            if (p >= p1) break;
-            kraw = __shfl(sid, m & 63);
+        }
+        if (ended) {
+            end_segment(kraw, p - seg_start, cout);
+            if (p >= plim) break;
+            kraw = next_k;
             fetch_cold(kraw);
             cin = false;
             seg_start = p;
@@ -340,6 +399,7 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
 #pragma unroll
                 for (int e = 0; e < V; ++e) acc[i][e] = 0.f;
         }
+        view(p, sid, idx);
     }
     if (SHIFT) {  // mode 0
         double d = (double)d2acc;
@@ -369,23 +429,22 @@ __device__ inline float combine_finish_col(const UpdArgs &a, int b, int k, size_
     return 0.f;
 }
 
-// Segments that start in a chunk and run past its end: add the chunk partials in chunk order
-// and finish the cluster.  A workgroup covers 4 consecutive chunks.  A segment spread over at
-// most 8 chunks is finished by one wave (lanes over columns, pieces in order); a longer one
-// by the whole workgroup (piece groups x columns, fixed-order tree).  Deterministic either way.
+// Segments that span three or more chunks: add the chunk partials in chunk order and finish
+// the cluster.  A workgroup covers COMBINE_CHUNKS consecutive chunks; their records are read
+// at once (most chunks start no such segment).  A segment spread over at most 8 chunks is
+// finished by one wave (lanes over columns, pieces in order); a longer one by the whole
+// workgroup (piece groups x columns, fixed-order tree).  Deterministic either way.
 constexpr int COMBINE_WAVE_MAX = 8;
+constexpr int COMBINE_CHUNKS = 16;
 
 __global__ __launch_bounds__(256) void upd_combine_kernel(UpdArgs a, int64_t nchunks) {
     __shared__ float s_red[256];
+    __shared__ int s_kk[COMBINE_CHUNKS], s_np[COMBINE_CHUNKS], s_nk[COMBINE_CHUNKS];
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int64_t chunk0 = (int64_t)blockIdx.x * 4;
-    int kk[4], np[4], nkk[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        kk[i] = -1;
-        np[i] = 0;
-        nkk[i] = 1;
-        const int64_t chunk = chunk0 + i;
+    const int64_t chunk0 = (int64_t)blockIdx.x * COMBINE_CHUNKS;
+    if (t < COMBINE_CHUNKS) {
+        int kv = -1, npv = 0, nkv = 1;
+        const int64_t chunk = chunk0 + t;
         if (chunk < nchunks) {
             const int32_t *rc = a.rec + chunk * 4;
             const int k = rc[1];
@@ -396,20 +455,24 @@ __global__ __launch_bounds__(256) void upd_combine_kernel(UpdArgs a, int64_t nch
                 nk = nk < 1 ? 1 : nk;
                 int c_last = (int)(((int64_t)rc[2] + nk - 1) / a.R);
                 c_last = c_last > a.nch - 1 ? a.nch - 1 : (c_last < c ? c : c_last);
-                kk[i] = k;
-                np[i] = c_last - c + 1;
-                nkk[i] = nk;
+                kv = k;
+                npv = c_last - c + 1;
+                nkv = nk;
             }
         }
+        s_kk[t] = kv;
+        s_np[t] = npv;
+        s_nk[t] = nkv;
     }
+    __syncthreads();
     const int D = a.D;
     // long segments: the whole workgroup
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (kk[i] < 0 || np[i] <= COMBINE_WAVE_MAX) continue;  // uniform over the workgroup
+    for (int i = 0; i < COMBINE_CHUNKS; ++i) {
+        const int kk = s_kk[i], np = s_np[i], nkk = s_nk[i];
+        if (kk < 0 || np <= COMBINE_WAVE_MAX) continue;  // uniform over the workgroup
         const int64_t chunk = chunk0 + i;
         const int b = (int)(chunk / a.nch);
-        const size_t rowo = ((size_t)b * a.K + kk[i]) * D;
+        const size_t rowo = ((size_t)b * a.K + kk) * D;
         int DC = 1;
         while (DC < D && DC < 256) DC <<= 1;
         const int PG = 256 / DC;
@@ -418,7 +481,7 @@ __global__ __launch_bounds__(256) void upd_combine_kernel(UpdArgs a, int64_t nch
         for (int d = dcol; d < ((D + DC - 1) / DC) * DC; d += DC) {
             float sum = 0.f;
             if (d < D) {
-                for (int j = pg; j < np[i]; j += PG) sum += a.part[((size_t)(chunk + j) * 2 + (j == 0 ? 1 : 0)) * D + d];
+                for (int j = pg; j < np; j += PG) sum += a.part[((size_t)(chunk + j) * 2 + (j == 0 ? 1 : 0)) * D + d];
             }
             s_red[t] = sum;
             __syncthreads();
@@ -426,7 +489,7 @@ __global__ __launch_bounds__(256) void upd_combine_kernel(UpdArgs a, int64_t nch
                 if (pg < off) s_red[t] += s_red[t + off * DC];
                 __syncthreads();
             }
-            if (pg == 0 && d < D) d2 += combine_finish_col(a, b, kk[i], rowo, d, s_red[dcol], nkk[i], cn2);
+            if (pg == 0 && d < D) d2 += combine_finish_col(a, b, kk, rowo, d, s_red[dcol], nkk, cn2);
             __syncthreads();
         }
         if (a.mode == 0) {
@@ -444,41 +507,48 @@ __global__ __launch_bounds__(256) void upd_combine_kernel(UpdArgs a, int64_t nch
                 if (t < off) s_red[t] += s_red[t + off];
                 __syncthreads();
             }
-            if (t == 0 && a.cprep) a.cnh[(size_t)b * a.KT * 32 + kk[i]] = 0.5f * s_red[0];
+            if (t == 0 && a.cprep) a.cnh[(size_t)b * a.KT * 32 + kk] = 0.5f * s_red[0];
             __syncthreads();
         } else if (t == 0) {
-            a.cnt[(size_t)b * a.K + kk[i]] += nkk[i];
+            a.cnt[(size_t)b * a.K + kk] += nkk;
         }
     }
-    // short segments: one wave each
-    const int64_t chunk = chunk0 + w;
-    if (kk[w] < 0 && chunk < nchunks && a.shp && lane == 0) a.shp[(size_t)chunk * (a.ncb + 1) + a.ncb] = 0.0;
-    if (kk[w] < 0 || np[w] > COMBINE_WAVE_MAX) return;
-    const int b = (int)(chunk / a.nch);
-    const size_t rowo = ((size_t)b * a.K + kk[w]) * D;
-    float d2 = 0.f, cn2 = 0.f;
-    for (int d = lane; d < D; d += 64) {
-        // every piece is loaded before the in-order sum (the loads are independent)
-        float pv[COMBINE_WAVE_MAX];
-        pv[0] = a.part[((size_t)chunk * 2 + 1) * D + d];
-#pragma unroll
-        for (int j = 1; j < COMBINE_WAVE_MAX; ++j)
-            pv[j] = j < np[w] ? a.part[((size_t)(chunk + j) * 2) * D + d] : 0.f;
-        float sum = pv[0];
-#pragma unroll
-        for (int j = 1; j < COMBINE_WAVE_MAX; ++j)
-            if (j < np[w]) sum += pv[j];
-        d2 += combine_finish_col(a, b, kk[w], rowo, d, sum, nkk[w], cn2);
-    }
-    if (a.mode == 0) {
-        for (int off = 1; off < 64; off <<= 1) {
-            d2 += __shfl_xor(d2, off);
-            cn2 += __shfl_xor(cn2, off);
+    // short segments (and the shift slot of every chunk): one wave each
+    for (int i = w; i < COMBINE_CHUNKS; i += 4) {  // 4 waves per workgroup
+        const int64_t chunk = chunk0 + i;
+        if (chunk >= nchunks) break;
+        const int kk = s_kk[i], np = s_np[i], nkk = s_nk[i];
+        if (kk < 0) {
+            if (a.shp && lane == 0) a.shp[(size_t)chunk * (a.ncb + 1) + a.ncb] = 0.0;
+            continue;
         }
-        if (lane == 0 && a.shp) a.shp[(size_t)chunk * (a.ncb + 1) + a.ncb] = (double)d2;
-        if (lane == 0 && a.cprep) a.cnh[(size_t)b * a.KT * 32 + kk[w]] = 0.5f * cn2;
-    } else if (lane == 0) {
-        a.cnt[(size_t)b * a.K + kk[w]] += nkk[w];
+        if (np > COMBINE_WAVE_MAX) continue;
+        const int b = (int)(chunk / a.nch);
+        const size_t rowo = ((size_t)b * a.K + kk) * D;
+        float d2 = 0.f, cn2 = 0.f;
+        for (int d = lane; d < D; d += 64) {
+            // every piece is loaded before the in-order sum (the loads are independent)
+            float pv[COMBINE_WAVE_MAX];
+            pv[0] = a.part[((size_t)chunk * 2 + 1) * D + d];
+#pragma unroll
+            for (int j = 1; j < COMBINE_WAVE_MAX; ++j)
+                pv[j] = j < np ? a.part[((size_t)(chunk + j) * 2) * D + d] : 0.f;
+            float sum = pv[0];
+#pragma unroll
+            for (int j = 1; j < COMBINE_WAVE_MAX; ++j)
+                if (j < np) sum += pv[j];
+            d2 += combine_finish_col(a, b, kk, rowo, d, sum, nkk, cn2);
+        }
+        if (a.mode == 0) {
+            for (int off = 1; off < 64; off <<= 1) {
+                d2 += __shfl_xor(d2, off);
+                cn2 += __shfl_xor(cn2, off);
+            }
+            if (lane == 0 && a.shp) a.shp[(size_t)chunk * (a.ncb + 1) + a.ncb] = (double)d2;
+            if (lane == 0 && a.cprep) a.cnh[(size_t)b * a.KT * 32 + kk] = 0.5f * cn2;
+        } else if (lane == 0) {
+            a.cnt[(size_t)b * a.K + kk] += nkk;
+        }
     }
 }
 
@@ -596,7 +666,7 @@ hipError_t launch_update(int dt, const void *x, const int32_t *sids, const int32
     else if (dt == DT_F16) e = launch_segsum_dt<DT_F16>(a, u.vec, u.vpl, waves, s);
     else e = launch_segsum_dt<DT_BF16>(a, u.vec, u.vpl, waves, s);
     if (e != hipSuccess) return e;
-    upd_combine_kernel<<<dim3((unsigned)((chunks + 3) / 4)), dim3(256), 0, s>>>(a, chunks);
+    upd_combine_kernel<<<dim3((unsigned)((chunks + COMBINE_CHUNKS - 1) / COMBINE_CHUNKS)), dim3(256), 0, s>>>(a, chunks);
     e = hipGetLastError();
     if (e != hipSuccess || !a.shp) return e;
     return launch_sum_f64_rows(a.shp, B, u.nch * (u.ncb + 1), shift, s);
