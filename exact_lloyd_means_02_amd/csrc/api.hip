@@ -454,14 +454,17 @@ km_status_t fit_device(int dt, const void *x, int64_t B, int64_t N, int64_t D, i
     const bool fused_prep = update_refreshes_prep(dt, B, N, D);
     const UpdRefresh ref = fused_prep ? UpdRefresh{cprep, cnh, cfg.d_pad, (int)KT} : UpdRefresh{};
 
-    KM_HIP(launch_row_norms(dt, x, xn, B * N, (int)D, s));
+    // the small-D assign kernel computes the point norms it needs from its own registers; the
+    // split-D kernel reads them
+    const float *xn_in = cfg.path == 0 ? nullptr : xn;
+    if (xn_in) KM_HIP(launch_row_norms(dt, x, xn, B * N, (int)D, s));
     KM_HIP(launch_prep_centroids(dt, C, cprep, cnh, (int)B, (int)K, (int)D, cfg.d_pad, s));
     int done = 0, flushed = 0;
     for (int t = 0; t < iters; ++t) {
         const int slot = t - flushed;
         // one iteration: assign (+ per-workgroup inertia partials), arg-sort, update (+ shift,
         // + the next iteration's prepared centroids)
-        KM_HIP(launch_assign(dt, cfg, x, cprep, cnh, xn, a, nullptr, ring_part + (size_t)slot * B * wpb, (int)B,
+        KM_HIP(launch_assign(dt, cfg, x, cprep, cnh, xn_in, a, nullptr, ring_part + (size_t)slot * B * wpb, (int)B,
                              (int)N, (int)D, (int)K, s));
         KM_HIP(launch_argsort(a, (int)B, (int)N, (int)K, sids, sidx, counts, scratch, s));
         KM_HIP(launch_update(dt, x, sids, sidx, counts, (int)B, (int)N, (int)D, (int)K, 0, C,
@@ -573,8 +576,9 @@ km_status_t fit_host(int dt, const void *xh, int64_t B, int64_t N, int64_t D, in
             const void *xc = stage_buf[buf];
             KM_HIP(hipStreamWaitEvent(s, P.ev_copy[buf], 0));
             int32_t *ac = assign ? assign + (size_t)b * N + lo : a_ws;
-            KM_HIP(launch_row_norms(dt, xc, xn, n, (int)D, s));
-            KM_HIP(launch_assign(dt, cfg, xc, cprep + (size_t)b * cprep_per_b, cnh + (size_t)b * KT * 32, xn, ac, md,
+            if (cfg.path != 0) KM_HIP(launch_row_norms(dt, xc, xn, n, (int)D, s));
+            KM_HIP(launch_assign(dt, cfg, xc, cprep + (size_t)b * cprep_per_b, cnh + (size_t)b * KT * 32,
+                                 cfg.path == 0 ? nullptr : xn, ac, md,
                                  nullptr, 1, (int)n, (int)D, (int)K, s));
             KM_HIP(launch_sum_f32(md, 1, n, ring_j + (size_t)slot * B + b, 1, red, s));
             KM_HIP(launch_argsort(ac, 1, (int)n, (int)K, sids, sidx, counts, scratch, s));

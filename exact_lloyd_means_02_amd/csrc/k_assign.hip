@@ -178,8 +178,9 @@ __device__ inline void argmin_fold(ArgminState &s, const f32x16 &acc, int tile) 
 // Resolve the winning centroid of this lane, merge with the partner lane (lane ^ 32, same
 // point, the other 16 rows of every tile) and write.  Accumulator r of lane (j, h) holds row
 // 8*(r/4) + 4*h + (r%4) of the 32-centroid tile (MFMA 32x32 output layout).
+// xnorm == NULL: the point's squared norm is `own_norm` (computed by the caller).
 __device__ inline float argmin_finish(const ArgminState &s, int h, bool write, int64_t out_i, int32_t *out_a,
-                                      float *out_d, const float *xnorm, bool want_d) {
+                                      float *out_d, const float *xnorm, bool want_d, float own_norm = 0.f) {
     int slot = 15;
 #pragma unroll
     for (int r = 15; r >= 0; --r) slot = (s.best[r] == s.run_min) ? r : slot;
@@ -195,7 +196,7 @@ __device__ inline float argmin_finish(const ArgminState &s, int h, bool write, i
     if (write) {
         out_a[out_i] = k;
         if (want_d) {
-            d = xnorm[out_i] + 2.0f * sc;  // squared distance to the chosen centroid (fp32)
+            d = (xnorm ? xnorm[out_i] : own_norm) + 2.0f * sc;  // squared distance to the chosen centroid
             if (out_d) out_d[out_i] = d;
         }
     }
@@ -293,6 +294,7 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
     const u32x4 *cb = cprep + (size_t)b * KT * TILE_U4;
     const float *nb = cnh + (size_t)b * KT * 32;
     const int nst = KT / TPS;  // KT is a multiple of 4
+    const bool want_d = out_d != nullptr || wg_inertia != nullptr;
 
     // Global -> LDS copy of stage st (TPS tiles and their norms).  Every wave issues exactly
     // NCOPY copy instructions, so it can wait for an older stage with a fixed count.
@@ -386,12 +388,24 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
 #pragma unroll
     for (int p = 0; p < PB; ++p) argmin_fold(st[p], accB[p], KT - 1);
 
-    const bool want_d = out_d != nullptr || wg_inertia != nullptr;
     double dsum = 0.0;
 #pragma unroll
     for (int p = 0; p < PB; ++p) {
         const int pt = pbase + p * 32 + j;
-        dsum += argmin_finish(st[p], h, h == 0 && pt < N, (int64_t)b * N + pt, out_a, out_d, xnorm, want_d);
+        // without given point norms: ||x||^2 from the point's registers (this lane's half of the
+        // row, then the partner lane's), in fp32
+        float own = 0.f;
+        if (want_d && !xnorm) {
+#pragma unroll
+            for (int q = 0; q < QG; ++q) {
+                float fx[VW];
+                widen16<DT>(__builtin_bit_cast(uint4, xr[p][q]), fx);
+#pragma unroll
+                for (int e = 0; e < VW; ++e) own += fx[e] * fx[e];
+            }
+            own += __shfl_xor(own, 32);
+        }
+        dsum += argmin_finish(st[p], h, h == 0 && pt < N, (int64_t)b * N + pt, out_a, out_d, xnorm, want_d, own);
     }
     if (wg_inertia) workgroup_inertia(dsum, wg_inertia + (size_t)b * wgs_per_b + tn);
 }
@@ -562,6 +576,7 @@ static hipError_t launch_small_dt(int DP, const void *x, const void *cprep, cons
 }
 
 // wgi (optional): per-workgroup fp64 sums of the chosen distances, [B][assign_wgs_per_problem].
+// xn: point norms for the distances (md / wgi); the small-D kernel computes them itself when NULL.
 hipError_t launch_assign(int dt, const AssignCfg &cfg, const void *x, const void *cprep, const float *cnh,
                          const float *xn, int32_t *a, float *md, double *wgi, int B, int N, int D, int K,
                          hipStream_t s) {
