@@ -312,7 +312,13 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
 #pragma unroll
     for (int p = 0; p < PB; ++p) argmin_init(st[p]);
 
-    u32x4 f[QG];  // A fragments of the tile being multiplied
+    // A fragments: group q of the tile being multiplied lives in slot q % FR.  A slot is
+    // refilled right after group q's MFMAs with group q + FR: of the same tile while there is
+    // one, else of the next tile.  FR = QG (a whole tile ahead) unless that would cost more
+    // than 32 registers (D*s >= 512 bytes), where FR = 8 keeps the kernel at two waves per SIMD.
+    constexpr int FR = QG > 8 ? 8 : QG;
+    static_assert(QG % FR == 0, "fragment ring");
+    u32x4 f[FR];
     f32x16 cn;    // half-norms of the tile being multiplied (this lane's 16 rows)
     f32x16 accA[PB], accB[PB];
     auto load_norms = [&](const float *sn, int tt) {
@@ -327,13 +333,14 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
     // reads have a whole tile to land; fold accF (the previous tile) in the MFMA shadow.  After
     // the last tile the refills read a stale (in-bounds) buffer and are never used: no
     // branches here.
-    auto step = [&](f32x16 (&accC)[PB], f32x16 (&accF)[PB], int tileF, const u32x4 *__restrict__ nsc,
-                    const float *__restrict__ nsn, int ntt) {
+    auto step = [&](f32x16 (&accC)[PB], f32x16 (&accF)[PB], int tileF, const u32x4 *__restrict__ csc, int ctt,
+                    const u32x4 *__restrict__ nsc, const float *__restrict__ nsn, int ntt) {
 #pragma unroll
         for (int q = 0; q < QG; ++q) {
 #pragma unroll
-            for (int p = 0; p < PB; ++p) accC[p] = mfma_group<DT>(f[q], xr[p][q], q == 0 ? cn : accC[p]);
-            f[q] = nsc[ntt * TILE_U4 + q * 64 + lane];
+            for (int p = 0; p < PB; ++p) accC[p] = mfma_group<DT>(f[q % FR], xr[p][q], q == 0 ? cn : accC[p]);
+            if (q + FR < QG) f[q % FR] = csc[ctt * TILE_U4 + (q + FR) * 64 + lane];
+            else f[q % FR] = nsc[ntt * TILE_U4 + (q + FR - QG) * 64 + lane];
             if (q == 0) load_norms(nsn, ntt);
         }
 #pragma unroll
@@ -352,16 +359,16 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
         const int t0 = TPS * s;
 #pragma unroll
         for (int i = 0; i + 2 < TPS; i += 2) {
-            step(accA, accB, t0 + i - 1, xc, xn_, i + 1);
-            step(accB, accA, t0 + i, xc, xn_, i + 2);
+            step(accA, accB, t0 + i - 1, xc, i, xc, xn_, i + 1);
+            step(accB, accA, t0 + i, xc, i + 1, xc, xn_, i + 2);
         }
-        step(accA, accB, t0 + TPS - 3, xc, xn_, TPS - 1);  // prefetch the stage's last tile
+        step(accA, accB, t0 + TPS - 3, xc, TPS - 2, xc, xn_, TPS - 1);  // prefetch the stage's last tile
         const bool more = s + 1 < nst;
         if (more) {
             if (copy2) stage_barrier<NCOPY>();  // stage s+1 landed (this wave), then published
             else stage_barrier<0>();
         }
-        step(accB, accA, t0 + TPS - 2, yc, yn, 0);  // last tile; prefetch the next stage's first
+        step(accB, accA, t0 + TPS - 2, xc, TPS - 1, yc, yn, 0);  // last tile; prefetch the next stage's first
     };
 
     // prologue: stages 0 and 1 in flight, stage 0 published, tile 0 loaded
@@ -373,7 +380,7 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
         stage_barrier<0>();
     }
 #pragma unroll
-    for (int q = 0; q < QG; ++q) f[q] = s_c0[q * 64 + lane];
+    for (int q = 0; q < FR; ++q) f[q] = s_c0[q * 64 + lane];
     load_norms(s_n0, 0);
 #pragma unroll
     for (int p = 0; p < PB; ++p)

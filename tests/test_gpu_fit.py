@@ -30,6 +30,7 @@ FIT_CASES = [
     ("batched_f16", dict(B=2, N=5000, K=100)),                # tol = 1e-4
     ("headline_bf16", dict(B=2, N=8192, K=256)),
     ("splitd_f32", dict(N=4000, K=32)),
+    ("headline_bf16", dict(B=1, N=3000, D=240, K=48)),     # small-D at padded D = 256
 ]
 
 
