@@ -346,8 +346,11 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
 #pragma unroll
         for (int p = 0; p < PB; ++p) argmin_fold(st[p], accF[p], tileF);
     };
-    // Stage s lives in X; stage s+1 in Y (copied earlier); stage s+2 is copied into Z, which
-    // nobody reads any more (its last reads happened before the previous mid-stage barrier).
+    // Stage s lives in X; stage s+1 in Y (copied earlier); stage s+2 is copied into Z.  With a
+    // whole tile of fragments in flight (FR == QG) the last step of a stage reads only Y, so Z
+    // (stage s-1's buffer) is free from the start of stage s and the copy goes first.  With a
+    // ring (FR < QG) the last step of stage s-1 still read Z after its mid-stage barrier, so the
+    // copy waits for this stage's mid-stage barrier, which every wave passes only after it.
     // Tile t = TPS*s + i is multiplied into accA for even i, accB for odd i.
     // The buffer pointers are __restrict__: the alias scopes this gives the LDS reads and the
     // global->LDS copies let the compiler wait for a copy only where its buffer is read, not
@@ -355,7 +358,8 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
     auto run_stage = [&](int s, u32x4 *__restrict__ xc, float *__restrict__ xn_, u32x4 *__restrict__ yc,
                          float *__restrict__ yn, u32x4 *__restrict__ zc, float *__restrict__ zn) {
         const bool copy2 = s + 2 < nst;
-        if (copy2) stage_copy(s + 2, zc, zn);
+        constexpr bool early = FR == QG;
+        if (early && copy2) stage_copy(s + 2, zc, zn);
         const int t0 = TPS * s;
 #pragma unroll
         for (int i = 0; i + 2 < TPS; i += 2) {
@@ -365,9 +369,11 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
         step(accA, accB, t0 + TPS - 3, xc, TPS - 2, xc, xn_, TPS - 1);  // prefetch the stage's last tile
         const bool more = s + 1 < nst;
         if (more) {
-            if (copy2) stage_barrier<NCOPY>();  // stage s+1 landed (this wave), then published
+            // stage s+1 landed (this wave), then published
+            if (early && copy2) stage_barrier<NCOPY>();
             else stage_barrier<0>();
         }
+        if (!early && copy2) stage_copy(s + 2, zc, zn);
         step(accB, accA, t0 + TPS - 2, xc, TPS - 1, yc, yn, 0);  // last tile; prefetch the next stage's first
     };
 

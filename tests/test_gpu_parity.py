@@ -79,6 +79,29 @@ def test_assign_prepared_equals_assign(fk):
     assert torch.equal(m1, m2)
 
 
+@pytest.mark.parametrize("name,kw", [("headline_bf16", dict(B=4, N=32768, D=240, K=512)),
+                                     ("tiny_f32", dict(B=2, N=32768, D=120, K=512, M=64))])
+def test_assign_fragment_ring_large(fk, name, kw):
+    """Padded widths where a tile's A fragments go through the 8-group ring (the stage copy
+    then waits for the mid-stage barrier): many workgroups per CU over many stages; two runs
+    agree bit for bit and sampled points match the oracle."""
+    w = W.small(name, **kw)
+    _say(f"fragment ring {w.name} B={w.B} N={w.N} D={w.D} K={w.K}")
+    x, c0, _ = W.make(w)
+    xt = W.to_torch(x, w.dtype).to(device())
+    ct = torch.from_numpy(c0).to(device())
+    xn = fk.kmeans_row_norms(xt)
+    a1, m1 = fk.kmeans_assign(xt, ct, x_norms=xn, want_min_dist=True)
+    a2, m2 = fk.kmeans_assign(xt, ct, x_norms=xn, want_min_dist=True)
+    assert torch.equal(a1, a2) and torch.equal(m1, m2)
+    rng = np.random.default_rng(5)
+    samp = [np.sort(rng.choice(w.N, size=512, replace=False)) for _ in range(w.B)]
+    x64s = np.stack([W.storage_to_f64(x[b, samp[b]], w.dtype) for b in range(w.B)])
+    a_np, m_np = a1.cpu().numpy(), m1.cpu().numpy()
+    check_assign(x64s, operand(c0, w.dtype), np.stack([a_np[b, samp[b]] for b in range(w.B)]),
+                 np.stack([m_np[b, samp[b]] for b in range(w.B)]))
+
+
 def test_assign_exact_ties_go_to_lowest_index(fk):
     """Duplicate centroids give bit-identical scores; the lowest index must win."""
     w = W.small("headline_bf16", B=1, N=2000, K=64)
