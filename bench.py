@@ -40,6 +40,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calib", action="store_true", help="run a plain 1 GiB device copy and exit")
+    p.add_argument("--context", action="store_true",
+                   help="also time the standard path in plain PyTorch (materialised distances + argmin, "
+                        "scatter-add update) for the kernel ratios")
     return p.parse_args()
 
 
@@ -119,6 +122,59 @@ def cpu_baseline(w, x, c0, target_s):
             "sample": "one fp64 oracle Lloyd iteration on %d of %d points (%d problem(s) x %d points, all K=%d "
                       "centroids) took %.2f s; scaled by %.1fx to the full iteration" % (
                           p * n, w.B * w.N, p, n, w.K, dt, scale)}
+
+
+def standard_path(w, xt, c0t, reps, st):
+    """The standard path the method replaces, in plain PyTorch on the same GPU (context only):
+    assign materialises the B x N x K distance matrix (hipBLASLt batched product, fp32
+    distances, argmin over K); update scatter-adds every row into its cluster's fp32 sum
+    with atomics (index_add_) and divides by the bincount.  Returns medians in ms and the
+    label agreement with the FlashAssign labels of the same centroids."""
+    import numpy as np
+    import torch
+    from exact_lloyd_means_02_amd import flashkm as fk
+    B, N, D, K = w.B, w.N, w.D, w.K
+    stream = torch.cuda.current_stream()
+    c_lp = c0t.to(xt.dtype)
+    c_lp_t = c_lp.transpose(1, 2).contiguous()          # [B, D, K], contiguous right operand
+    cn = (c_lp.float() ** 2).sum(-1)                     # ||c~||^2 from the rounded centroids
+    xf = xt.view(B * N, D)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ta, tu = [], []
+    lab = None
+    gemm_out = "fp32"
+    for _ in range(reps):
+        ev[0].record(stream)
+        if gemm_out == "fp32":
+            try:
+                dots = torch.bmm(xt, c_lp_t, out_dtype=torch.float32)   # [B, N, K], fp32 accumulate and output
+            except (RuntimeError, TypeError):
+                gemm_out = "input dtype"
+        if gemm_out != "fp32":
+            dots = torch.bmm(xt, c_lp_t)                 # [B, N, K] in the input dtype
+        dist = cn[:, None, :] - 2.0 * dots.float()       # ||x||^2 dropped: constant per point
+        lab = torch.argmin(dist, dim=-1)
+        del dots, dist
+        ev[1].record(stream)
+        flat = (lab + torch.arange(B, device=xt.device)[:, None] * K).view(-1)
+        sums = torch.zeros(B * K, D, dtype=torch.float32, device=xt.device)
+        sums.index_add_(0, flat, xf.float())
+        cnt = torch.bincount(flat, minlength=B * K)
+        newc = torch.where(cnt[:, None] > 0, sums / cnt.clamp(min=1)[:, None].float(), c0t.view(B * K, D))
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        ta.append(ev[0].elapsed_time(ev[1]))
+        tu.append(ev[1].elapsed_time(ev[2]))
+        del sums, cnt, newc, flat
+    prep = fk.kmeans_prepare_centroids(c0t, xt)
+    a, _ = fk.kmeans_assign_prepared(xt, prep)
+    agree = float((a.long() == lab).float().mean().item())
+    ma, mu = float(np.median(ta)), float(np.median(tu))
+    return {"what": "plain PyTorch on the same GPU: bmm + fp32 distances + argmin; index_add_ scatter + bincount",
+            "gemm_output": gemm_out, "materialised_assign_ms": round(ma, 4), "scatter_update_ms": round(mu, 4),
+            "assign_speedup": round(ma / st["assign"], 2),
+            "update_speedup": round(mu / (st["argsort"] + st["update"]), 2),
+            "label_agreement": agree}
 
 
 def bench_streamed(args, w):
@@ -296,6 +352,9 @@ def main():
                    "stages": "kmeans_argsort_ids + kmeans_update"},
         "inertia_last": [float(v) for v in inertia[-1][:2]],
     }
+    if args.context:
+        print("bench: timing the standard path", file=sys.stderr, flush=True)
+        out["context"] = standard_path(w, xt, c0t, 5, st)
     if not args.no_cpu_baseline:
         print("bench: timing the oracle sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, x, c0, args.cpu_seconds)
