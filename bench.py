@@ -40,6 +40,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calib", action="store_true", help="run a plain 1 GiB device copy and exit")
+    p.add_argument("--metric", default="l2", choices=["l2", "dot", "cosine"],
+                   help="k-means variant: Lloyd (l2), dot-product or cosine (spherical) k-means")
     p.add_argument("--context", action="store_true",
                    help="also time the standard path in plain PyTorch (materialised distances + argmin, "
                         "scatter-add update) for the kernel ratios")
@@ -97,18 +99,24 @@ def algorithmic(w):
     return flops, assign_bytes, update_bytes
 
 
-def cpu_baseline(w, x, c0, target_s):
-    """The fp64 oracle (as it stands) on a bounded sample of the same workload: one Lloyd
-    iteration on the first `n` points of the first `p` problems against all K centroids,
-    grown until it takes ~0.6 * target_s (or covers everything), then scaled to B*N points."""
+def cpu_baseline(w, x, c0, target_s, metric="l2"):
+    """The fp64 oracle (as it stands) on a bounded sample of the same workload: one iteration
+    on the first `n` points of the first `p` problems against all K centroids, grown until it
+    takes ~0.6 * target_s (or covers everything), then scaled to B*N points."""
     import numpy as np
     import oracle
+    from oracle import similarity as sim
     from exact_lloyd_means_02_amd import workloads as W
     n, p = min(w.N, 2048), 1
     while True:
         xs = W.storage_to_f64(x[:p, :n], w.dtype)
         t0 = time.perf_counter()
-        oracle.lloyd_iteration(xs, c0[:p].astype(np.float64), dtype=w.dtype, mode="modelled")
+        if metric == "l2":
+            oracle.lloyd_iteration(xs, c0[:p].astype(np.float64), dtype=w.dtype, mode="modelled")
+        else:
+            if metric == "cosine":
+                xs = sim.round_to_dtype(sim.normalize_rows(xs), w.dtype)
+            sim.similarity_iteration(xs, c0[:p].astype(np.float64), metric, dtype=w.dtype, mode="modelled")
         dt = time.perf_counter() - t0
         if dt >= 0.6 * target_s or (n >= w.N and p >= w.B):
             break
@@ -119,7 +127,7 @@ def cpu_baseline(w, x, c0, target_s):
             p = min(w.B, max(p + 1, int(p * grow)))
     scale = (w.B * w.N) / (p * n)
     return {"value": round(dt * scale * 1e3, 3), "unit": "ms", "cores": oracle.threads(), "kind": "oracle",
-            "sample": "one fp64 oracle Lloyd iteration on %d of %d points (%d problem(s) x %d points, all K=%d "
+            "sample": "one fp64 oracle iteration on %d of %d points (%d problem(s) x %d points, all K=%d "
                       "centroids) took %.2f s; scaled by %.1fx to the full iteration" % (
                           p * n, w.B * w.N, p, n, w.K, dt, scale)}
 
@@ -277,15 +285,20 @@ def main():
     c = c0t.clone()
     stream = torch.cuda.current_stream(dev)
 
+    def fit(iters):
+        if args.metric == "l2":
+            return fk.kmeans_fit(xt, c, iters, 0.0)
+        return fk.kmeans_fit_metric(xt, c, args.metric, iters, 0.0)
+
     # ---- warmup (untimed): W iterations
-    fk.kmeans_fit(xt, c, max(1, args.warmup), 0.0)
+    fit(max(1, args.warmup))
     torch.cuda.synchronize()
 
-    # ---- timed: exactly `steps` Lloyd iterations in one fit
+    # ---- timed: exactly `steps` iterations in one fit
     c.copy_(c0t)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    _, inertia, done = fk.kmeans_fit(xt, c, args.steps, 0.0)
+    _, inertia, done = fit(args.steps)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     assert done == args.steps
@@ -294,7 +307,7 @@ def main():
 
     # ---- per-stage times (HIP events on the stages' stream), teacher forced from c0
     xn = fk.kmeans_row_norms(xt)
-    prep = fk.kmeans_prepare_centroids(c0t, xt)
+    prep = fk.kmeans_prepare_centroids(c0t, xt, metric=args.metric)
     a, md = fk.kmeans_assign_prepared(xt, prep, x_norms=xn, want_min_dist=True)
     s_ids, s_idx, counts = fk.kmeans_argsort_ids(a, w.K)
     cu = c0t.clone()
@@ -308,7 +321,7 @@ def main():
         ev[0].record(stream)
         fk.kmeans_row_norms(xt, out=xn)
         ev[1].record(stream)
-        fk.kmeans_prepare_centroids(c0t, xt, out=prep.buf)
+        fk.kmeans_prepare_centroids(c0t, xt, out=prep.buf, metric=args.metric)
         ev[2].record(stream)
         fk.kmeans_assign_prepared(xt, prep, x_norms=xn, assign=a, min_dist=md)
         ev[3].record(stream)
@@ -326,8 +339,10 @@ def main():
     upd_ms = st["argsort"] + st["update"]
     upd_gbs = ubytes / (upd_ms * 1e-3) / 1e9
 
+    headline = w.name == "headline_bf16" and args.metric == "l2"
     out = {
-        "metric": METRIC if w.name == "headline_bf16" else "ms per Lloyd iteration (%s)" % w.name,
+        "metric": METRIC if headline else "ms per %s k-means iteration (%s)" % (
+            {"l2": "Lloyd", "dot": "dot-product", "cosine": "cosine"}[args.metric], w.name),
         "value": round(ms_per_step, 4),
         "unit": "ms",
         "higher_is_better": False,
@@ -340,7 +355,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "N": w.N, "D": w.D, "K": w.K, "iters": args.steps, "tol": 0.0,
-                   "inputs": "HBM-resident"},
+                   "inputs": "HBM-resident", "metric": args.metric},
         "roofline": {"bound": "mfma", "achieved": round(assign_tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(assign_tflops / peak, 4), "traffic": measured_traffic(),
                      "kernel": "FlashAssign (small-D) kernel, one launch per kmeans_assign_prepared call",
@@ -350,14 +365,14 @@ def main():
         "update": {"bound": "hbm", "achieved": round(upd_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                    "frac": round(upd_gbs / PEAK_HBM_GBS, 4), "bytes_per_iter": ubytes,
                    "stages": "kmeans_argsort_ids + kmeans_update"},
-        "inertia_last": [float(v) for v in inertia[-1][:2]],
+        ("inertia_last" if args.metric == "l2" else "similarity_last"): [float(v) for v in inertia[-1][:2]],
     }
     if args.context:
         print("bench: timing the standard path", file=sys.stderr, flush=True)
         out["context"] = standard_path(w, xt, c0t, 5, st)
     if not args.no_cpu_baseline:
         print("bench: timing the oracle sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(w, x, c0, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, x, c0, args.cpu_seconds, args.metric)
     print(json.dumps(out), flush=True)
 
 

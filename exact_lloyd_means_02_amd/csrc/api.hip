@@ -13,7 +13,7 @@
 namespace fkm {
 // kernels (k_*.hip)
 hipError_t launch_prep_centroids(int dt, const float *C, void *cprep, float *cnh, int B, int K, int D, int DP,
-                                 hipStream_t stream);
+                                 hipStream_t stream, int zero_norm);
 hipError_t launch_assign(int dt, const AssignCfg &cfg, const void *x, const void *cprep, const float *cnh,
                          const float *xn, int32_t *a, float *md, double *wgi, int B, int N, int D, int K,
                          hipStream_t s);
@@ -27,8 +27,9 @@ hipError_t launch_update(int dt, const void *x, const int32_t *sids, const int32
                          int B, int N, int D, int K, int mode, float *C, double *shift, float *sums, int32_t *cnt,
                          const UpdRefresh &ref, void *ws, hipStream_t s);
 hipError_t launch_finalize_acc(int dt, const float *sums, const int32_t *cnt, float *C, double *shift, double *shk,
-                               const UpdRefresh &ref, int B, int K, int D, hipStream_t s);
+                               const UpdRefresh &ref, int B, int K, int D, hipStream_t s, int normalize);
 hipError_t launch_row_norms(int dt, const void *x, float *out, int64_t rows, int D, hipStream_t s);
+hipError_t launch_normalize_rows(int dt, const void *x, void *out, int64_t rows, int D, hipStream_t s);
 size_t reduce_ws_bytes(int64_t B);
 hipError_t launch_sum_f32(const float *v, int B, int64_t n, double *out, int accumulate, void *ws, hipStream_t s);
 hipError_t launch_sum_f64_rows(const double *part, int rows, int64_t len, double *out, hipStream_t s);
@@ -65,6 +66,7 @@ constexpr int RING = 16;  // iterations of inertia / shift kept on the device be
 constexpr int64_t DEFAULT_CHUNK = (int64_t)1 << 24;
 
 bool dt_ok(int dt) { return dt == KM_F32 || dt == KM_F16 || dt == KM_BF16; }
+bool metric_ok(int m) { return m == KM_METRIC_L2 || m == KM_METRIC_DOT || m == KM_METRIC_COSINE; }
 
 km_status_t check_shape(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
     if (!dt_ok(dt)) return fail(KM_ERR_INVALID, "unknown dtype %d", dt);
@@ -108,12 +110,14 @@ int64_t assign_wgs_per_problem(int dt, int64_t B, int64_t N, int64_t D, int64_t 
 }
 
 struct FitLayout {
-    size_t xn, a, sids, sidx, counts, prep, ring_part, ring_j, ring_s, scratch, total;
+    size_t xn, a, sids, sidx, counts, prep, ring_part, ring_j, ring_s, xhat, sums, cnt, shk, scratch, total;
 };
 
 // Device-resident x.  The prepared centroids persist across iterations (the update refreshes
-// them); the arg-sort and update scratch share one region.
-FitLayout fit_layout(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
+// them); the arg-sort and update scratch share one region.  Cosine k-means adds the unit rows
+// x^ [B][N][D] (input dtype) and the accumulating update's sums [B][K][D], counts [B][K] and
+// per-cluster shifts [B][K].
+FitLayout fit_layout(int dt, int64_t B, int64_t N, int64_t D, int64_t K, int metric = KM_METRIC_L2) {
     FitLayout L{};
     size_t o = 0;
     const size_t bn4 = align256((size_t)B * N * 4);
@@ -126,6 +130,12 @@ FitLayout fit_layout(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
     L.ring_part = o; o += align256((size_t)RING * B * assign_wgs_per_problem(dt, B, N, D, K) * 8);
     L.ring_j = o; o += align256((size_t)RING * B * 8);
     L.ring_s = o; o += align256((size_t)RING * B * 8);
+    if (metric == KM_METRIC_COSINE) {
+        L.xhat = o; o += align256((size_t)B * N * D * elem_bytes(dt));
+        L.sums = o; o += align256((size_t)B * K * D * 4);
+        L.cnt = o; o += align256((size_t)B * K * 4);
+        L.shk = o; o += align256((size_t)B * K * 8);
+    }
     L.scratch = o;
     const size_t s2 = argsort_ws(B, N, K), s3 = update_ws(dt, B, N, D, K);
     o += s2 > s3 ? s2 : s3;
@@ -233,10 +243,10 @@ float *prep_norms(int dt, char *cprep, int64_t B, int64_t D, int64_t K, int d_pa
 }
 
 km_status_t do_prepare(int dt, const float *C, int64_t B, int64_t N, int64_t D, int64_t K, void *cprep,
-                       hipStream_t s) {
+                       hipStream_t s, int metric = KM_METRIC_L2) {
     const AssignCfg cfg = plan_assign(dt, B, N, D, K);
     KM_HIP(launch_prep_centroids(dt, C, cprep, prep_norms(dt, (char *)cprep, B, D, K, cfg.d_pad), (int)B, (int)K,
-                                 (int)D, cfg.d_pad, s));
+                                 (int)D, cfg.d_pad, s, metric != KM_METRIC_L2));
     return ok();
 }
 
@@ -301,6 +311,8 @@ size_t kmeans_workspace_bytes(int op, km_dtype_t dt, int64_t B, int64_t N, int64
         case KM_OP_UPDATE: return update_ws(dt, B, N, D, K);
         case KM_OP_FIT: return fit_layout(dt, B, N, D, K).total;
         case KM_OP_FIT_HOST: return host_layout(dt, B, N, D, K, chunk_points).total;
+        case KM_OP_FIT_DOT: return fit_layout(dt, B, N, D, K, KM_METRIC_DOT).total;
+        case KM_OP_FIT_COSINE: return fit_layout(dt, B, N, D, K, KM_METRIC_COSINE).total;
         default: g_err = "unknown workspace op"; return 0;
     }
 }
@@ -370,6 +382,34 @@ km_status_t kmeans_assign_prepared(const void *x, km_dtype_t dt, const void *c_p
     return do_assign_prepared(dt, x, c_prep, B, N, D, K, x_norms, assign, min_dist, (hipStream_t)stream);
 }
 
+km_status_t kmeans_normalize_rows(const void *x, km_dtype_t dt, int64_t rows, int64_t D, void *out, void *stream) {
+    if (!dt_ok(dt)) return fail(KM_ERR_INVALID, "unknown dtype %d", dt);
+    if (rows < 1 || D < 1 || D > MAX_D || rows >= MAX_N) return fail(KM_ERR_INVALID, "bad shape");
+    KM_TRY(check_ptr(x, "x"));
+    KM_TRY(check_ptr(out, "out"));
+    if (((uintptr_t)x & 15) != 0 || ((uintptr_t)out & 15) != 0)
+        return fail(KM_ERR_INVALID, "x and out must be 16-byte aligned");
+    KM_TRY(check_device_arch());
+    KM_TRY(require_device(x, "x"));
+    KM_TRY(require_device(out, "out"));
+    KM_HIP(launch_normalize_rows(dt, x, out, rows, (int)D, (hipStream_t)stream));
+    return ok();
+}
+
+km_status_t kmeans_prepare_centroids_metric(const float *centroids, km_dtype_t dt, km_metric_t metric, int64_t B,
+                                            int64_t N, int64_t D, int64_t K, void *c_prep, size_t c_prep_bytes,
+                                            void *stream) {
+    if (!metric_ok(metric)) return fail(KM_ERR_INVALID, "unknown metric %d", (int)metric);
+    KM_TRY(check_shape(dt, B, N, D, K));
+    KM_TRY(check_ptr(centroids, "centroids"));
+    KM_TRY(check_ptr(c_prep, "c_prep"));
+    KM_TRY(check_ws(c_prep, c_prep_bytes, assign_ws(dt, B, N, D, K)));
+    KM_TRY(check_device_arch());
+    KM_TRY(require_device(centroids, "centroids"));
+    KM_TRY(require_device(c_prep, "c_prep"));
+    return do_prepare(dt, centroids, B, N, D, K, c_prep, (hipStream_t)stream, (int)metric);
+}
+
 km_status_t kmeans_argsort_ids(const int32_t *assign, int64_t B, int64_t N, int64_t K, int32_t *sorted_ids,
                                int32_t *sorted_idx, int32_t *counts, void *ws, size_t ws_bytes, void *stream) {
     KM_TRY(check_shape(KM_F32, B, N, 1, K));
@@ -434,9 +474,16 @@ km_status_t read_shift_max(const double *dev, int64_t B, double *out, hipStream_
     return ok();
 }
 
+// metric: KM_METRIC_L2 (Lloyd), KM_METRIC_DOT (similarity x.c, mean update) or KM_METRIC_COSINE
+// (unit rows, mean-direction update).  For the similarity metrics the assign kernels get zero
+// norm terms (scores -x.c~) and zero point norms, so their per-point "distance" is
+// -2 x.c~ and the per-iteration value returned is -1/2 of its sum: the total similarity.
 km_status_t fit_device(int dt, const void *x, int64_t B, int64_t N, int64_t D, int64_t K, int iters, float tol,
-                       float *C, int32_t *assign, double *inertia, int32_t *iters_done, char *ws, hipStream_t s) {
-    const FitLayout L = fit_layout(dt, B, N, D, K);
+                       float *C, int32_t *assign, double *inertia, int32_t *iters_done, char *ws, hipStream_t s,
+                       int metric = KM_METRIC_L2) {
+    const FitLayout L = fit_layout(dt, B, N, D, K, metric);
+    const bool simm = metric != KM_METRIC_L2;
+    const bool cosine = metric == KM_METRIC_COSINE;
     const AssignCfg cfg = plan_assign(dt, B, N, D, K);
     const int64_t KT = assign_tiles(K);
     const int64_t wpb = assign_wgs_per_problem(dt, B, N, D, K);
@@ -452,25 +499,47 @@ km_status_t fit_device(int dt, const void *x, int64_t B, int64_t N, int64_t D, i
     double *ring_s = (double *)(ws + L.ring_s);
     void *scratch = ws + L.scratch;
     const bool fused_prep = update_refreshes_prep(dt, B, N, D);
-    const UpdRefresh ref = fused_prep ? UpdRefresh{cprep, cnh, cfg.d_pad, (int)KT} : UpdRefresh{};
+    const UpdRefresh full_ref{cprep, cnh, cfg.d_pad, (int)KT, simm ? 1 : 0};
+    const UpdRefresh ref = fused_prep ? full_ref : UpdRefresh{};
 
+    // the points the iterations use: x, or its unit rows for cosine k-means (whose centroids
+    // are made unit rows too, in place)
+    const void *xa = x;
+    if (cosine) {
+        KM_HIP(launch_normalize_rows(dt, x, ws + L.xhat, B * N, (int)D, s));
+        KM_HIP(launch_normalize_rows(KM_F32, C, C, B * K, (int)D, s));
+        xa = ws + L.xhat;
+    }
     // the small-D assign kernel computes the point norms it needs from its own registers; the
-    // split-D kernel reads them
-    const float *xn_in = cfg.path == 0 ? nullptr : xn;
-    if (xn_in) KM_HIP(launch_row_norms(dt, x, xn, B * N, (int)D, s));
-    KM_HIP(launch_prep_centroids(dt, C, cprep, cnh, (int)B, (int)K, (int)D, cfg.d_pad, s));
+    // split-D kernel reads them.  The similarity metrics take zeros instead.
+    const float *xn_in = simm ? xn : (cfg.path == 0 ? nullptr : xn);
+    if (simm) KM_HIP(launch_fill_i32((int32_t *)xn, B * N, 0, s));
+    else if (xn_in) KM_HIP(launch_row_norms(dt, x, xn, B * N, (int)D, s));
+    KM_HIP(launch_prep_centroids(dt, C, cprep, cnh, (int)B, (int)K, (int)D, cfg.d_pad, s, simm ? 1 : 0));
     int done = 0, flushed = 0;
     for (int t = 0; t < iters; ++t) {
         const int slot = t - flushed;
         // one iteration: assign (+ per-workgroup inertia partials), arg-sort, update (+ shift,
         // + the next iteration's prepared centroids)
-        KM_HIP(launch_assign(dt, cfg, x, cprep, cnh, xn_in, a, nullptr, ring_part + (size_t)slot * B * wpb, (int)B,
+        KM_HIP(launch_assign(dt, cfg, xa, cprep, cnh, xn_in, a, nullptr, ring_part + (size_t)slot * B * wpb, (int)B,
                              (int)N, (int)D, (int)K, s));
         KM_HIP(launch_argsort(a, (int)B, (int)N, (int)K, sids, sidx, counts, scratch, s));
-        KM_HIP(launch_update(dt, x, sids, sidx, counts, (int)B, (int)N, (int)D, (int)K, 0, C,
-                             tol > 0.f ? ring_s + (size_t)slot * B : nullptr, nullptr, nullptr, ref, scratch, s));
-        if (!fused_prep && t + 1 < iters)
-            KM_HIP(launch_prep_centroids(dt, C, cprep, cnh, (int)B, (int)K, (int)D, cfg.d_pad, s));
+        if (cosine) {
+            // sums and counts per cluster, then the mean direction (with shift and refresh)
+            float *sums = (float *)(ws + L.sums);
+            int32_t *cnt = (int32_t *)(ws + L.cnt);
+            KM_HIP(launch_fill_i32((int32_t *)sums, B * K * D, 0, s));
+            KM_HIP(launch_fill_i32(cnt, B * K, 0, s));
+            KM_HIP(launch_update(dt, xa, sids, sidx, counts, (int)B, (int)N, (int)D, (int)K, 1, nullptr, nullptr,
+                                 sums, cnt, UpdRefresh{}, scratch, s));
+            KM_HIP(launch_finalize_acc(dt, sums, cnt, C, tol > 0.f ? ring_s + (size_t)slot * B : nullptr,
+                                       (double *)(ws + L.shk), full_ref, (int)B, (int)K, (int)D, s, 1));
+        } else {
+            KM_HIP(launch_update(dt, xa, sids, sidx, counts, (int)B, (int)N, (int)D, (int)K, 0, C,
+                                 tol > 0.f ? ring_s + (size_t)slot * B : nullptr, nullptr, nullptr, ref, scratch, s));
+            if (!fused_prep && t + 1 < iters)
+                KM_HIP(launch_prep_centroids(dt, C, cprep, cnh, (int)B, (int)K, (int)D, cfg.d_pad, s, simm ? 1 : 0));
+        }
         done = t + 1;
         bool stop = false;
         if (tol > 0.f) {
@@ -486,6 +555,8 @@ km_status_t fit_device(int dt, const void *x, int64_t B, int64_t N, int64_t D, i
         if (stop) break;
     }
     KM_HIP(hipStreamSynchronize(s));
+    if (simm && inertia)
+        for (int64_t i = 0; i < (int64_t)done * B; ++i) inertia[i] *= -0.5;
     if (iters_done) *iters_done = done;
     return ok();
 }
@@ -559,7 +630,7 @@ km_status_t fit_host(int dt, const void *xh, int64_t B, int64_t N, int64_t D, in
     KM_HIP(hipEventRecord(P.ev_free[0], s));
     KM_HIP(hipEventRecord(P.ev_free[1], s));
     KM_TRY(issue_copy(0));
-    KM_HIP(launch_prep_centroids(dt, C, cprep, cnh, (int)B, (int)K, (int)D, cfg.d_pad, s));
+    KM_HIP(launch_prep_centroids(dt, C, cprep, cnh, (int)B, (int)K, (int)D, cfg.d_pad, s, 0));
     int64_t q = 0;
     int done = 0, flushed = 0;
     for (int t = 0; t < iters; ++t) {
@@ -587,7 +658,7 @@ km_status_t fit_host(int dt, const void *xh, int64_t B, int64_t N, int64_t D, in
             KM_HIP(hipEventRecord(P.ev_free[buf], s));
         }
         KM_HIP(launch_finalize_acc(dt, sums, cnt, C, tol > 0.f ? ring_s + (size_t)slot * B : nullptr,
-                                   (double *)(ws + L.shk), ref, (int)B, (int)K, (int)D, s));
+                                   (double *)(ws + L.shk), ref, (int)B, (int)K, (int)D, s, 0));
         done = t + 1;
         bool stop = false;
         if (tol > 0.f) {
@@ -608,6 +679,32 @@ km_status_t fit_host(int dt, const void *xh, int64_t B, int64_t N, int64_t D, in
 }
 
 }  // namespace
+
+extern "C" km_status_t kmeans_fit_metric(const void *x, km_dtype_t dt, km_metric_t metric, int64_t B, int64_t N,
+                                         int64_t D, int64_t K, int32_t iters, float tol, float *centroids,
+                                         int32_t *assign, double *objective, int32_t *iters_done, void *ws,
+                                         size_t ws_bytes, void *stream) {
+    if (!metric_ok(metric)) return fail(KM_ERR_INVALID, "unknown metric %d", (int)metric);
+    if (metric == KM_METRIC_L2)
+        return kmeans_fit(x, dt, B, N, D, K, iters, tol, 0, centroids, assign, objective, iters_done, ws, ws_bytes,
+                          stream);
+    KM_TRY(check_shape(dt, B, N, D, K));
+    KM_TRY(check_ptr(x, "x"));
+    KM_TRY(check_ptr(centroids, "centroids"));
+    if (iters < 1) return fail(KM_ERR_INVALID, "iters must be >= 1");
+    if (!(tol >= 0.f)) return fail(KM_ERR_INVALID, "tol must be >= 0");
+    if (((uintptr_t)x & 15) != 0) return fail(KM_ERR_INVALID, "x must be 16-byte aligned");
+    if (!ws) return fail(KM_ERR_WORKSPACE, "workspace is NULL");
+    KM_TRY(check_device_arch());
+    if (pointer_kind(x) != PTR_DEVICE)
+        return fail(KM_ERR_UNSUPPORTED, "the dot-product and cosine metrics need device-resident x");
+    KM_TRY(require_device(centroids, "centroids"));
+    KM_TRY(require_device(assign, "assign"));
+    KM_TRY(require_device(ws, "ws"));
+    KM_TRY(check_ws(ws, ws_bytes, fit_layout(dt, B, N, D, K, (int)metric).total));
+    return fit_device(dt, x, B, N, D, K, iters, tol, centroids, assign, objective, iters_done, (char *)ws,
+                      (hipStream_t)stream, (int)metric);
+}
 
 extern "C" km_status_t kmeans_fit(const void *x, km_dtype_t dt, int64_t B, int64_t N, int64_t D, int64_t K,
                                   int32_t iters, float tol, int64_t chunk_points, float *centroids, int32_t *assign,

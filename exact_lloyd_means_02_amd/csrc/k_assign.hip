@@ -44,7 +44,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 template <int DT>
 __global__ __launch_bounds__(256) void prep_centroids_kernel(const float *__restrict__ C, u32x4 *__restrict__ cprep,
                                                              float *__restrict__ cnh, int K, int D, int DP,
-                                                             int KT) {
+                                                             int KT, int zero_norm) {
     constexpr int S = DT == DT_F32 ? 4 : 2;
     constexpr int VW = 16 / S;
     const int QG = DP / (2 * VW);
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void prep_centroids_kernel(const float *__rest
     ss += __shfl_xor(ss, 1);
     ss += __shfl_xor(ss, 2);
     ss += __shfl_xor(ss, 4);
-    if (part == 0) cnh[(size_t)b * KT * 32 + k] = valid_k ? 0.5f * ss : __builtin_inff();
+    if (part == 0) cnh[(size_t)b * KT * 32 + k] = valid_k ? (zero_norm ? 0.f : 0.5f * ss) : __builtin_inff();
 }
 
 // ------------------------------------------------------------------------------------------
@@ -540,16 +540,18 @@ __global__ __launch_bounds__(256) void assign_split_d_kernel(const void *__restr
 // ------------------------------------------------------------------------------------------
 // host launchers
 // ------------------------------------------------------------------------------------------
+// zero_norm: the similarity metrics (dot product, cosine) score -x.c~ alone, so the norm
+// terms of the real rows are 0 (the padding rows keep +inf).
 hipError_t launch_prep_centroids(int dt, const float *C, void *cprep, float *cnh, int B, int K, int D, int DP,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, int zero_norm) {
     const int KT = assign_tiles(K);
     dim3 grid(B * KT), block(256);
     if (dt == DT_F32)
-        prep_centroids_kernel<DT_F32><<<grid, block, 0, stream>>>(C, (u32x4 *)cprep, cnh, K, D, DP, KT);
+        prep_centroids_kernel<DT_F32><<<grid, block, 0, stream>>>(C, (u32x4 *)cprep, cnh, K, D, DP, KT, zero_norm);
     else if (dt == DT_F16)
-        prep_centroids_kernel<DT_F16><<<grid, block, 0, stream>>>(C, (u32x4 *)cprep, cnh, K, D, DP, KT);
+        prep_centroids_kernel<DT_F16><<<grid, block, 0, stream>>>(C, (u32x4 *)cprep, cnh, K, D, DP, KT, zero_norm);
     else
-        prep_centroids_kernel<DT_BF16><<<grid, block, 0, stream>>>(C, (u32x4 *)cprep, cnh, K, D, DP, KT);
+        prep_centroids_kernel<DT_BF16><<<grid, block, 0, stream>>>(C, (u32x4 *)cprep, cnh, K, D, DP, KT, zero_norm);
     return hipGetLastError();
 }
 

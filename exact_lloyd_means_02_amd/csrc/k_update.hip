@@ -44,7 +44,12 @@ struct UpdArgs {
     void *cprep;
     float *cnh;
     int DP, KT;
+    int zero_norm;     // similarity metrics: the refreshed norm terms are 0
+    int normalize;     // finalize (cosine k-means): c_k <- sums_k / ||sums_k|| instead of / cnt_k
 };
+
+// The half-norm term the assign kernels add to a refreshed centroid's scores.
+__device__ inline float refreshed_half_norm(const UpdArgs &a, float cn2) { return a.zero_norm ? 0.f : 0.5f * cn2; }
 
 // Store element d of -c~ (c~ = dtype(c), nearest even) into the prepared layout; returns c~^2.
 __device__ inline float prep_store_elem(const UpdArgs &a, int b, int k, int d, float c) {
@@ -308,7 +313,7 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
             if (g == 0) d2acc += finish_cluster<DT, V, VPL, SHIFT>(a, b, k, c0, r, acc, n, cold, cbi == 0, cn2);
             if (a.cprep) {  // mode 0, ncb == 1
                 for (int off = 1; off < a.lanes; off <<= 1) cn2 += __shfl_xor(cn2, off);
-                if (lane == 0) a.cnh[(size_t)b * a.KT * 32 + k] = 0.5f * cn2;
+                if (lane == 0) a.cnh[(size_t)b * a.KT * 32 + k] = refreshed_half_norm(a, cn2);
             }
         } else {
             const int slot = cin ? 0 : 1;
@@ -507,7 +512,7 @@ __global__ __launch_bounds__(256) void upd_combine_kernel(UpdArgs a, int64_t nch
                 if (t < off) s_red[t] += s_red[t + off];
                 __syncthreads();
             }
-            if (t == 0 && a.cprep) a.cnh[(size_t)b * a.KT * 32 + kk] = 0.5f * s_red[0];
+            if (t == 0 && a.cprep) a.cnh[(size_t)b * a.KT * 32 + kk] = refreshed_half_norm(a, s_red[0]);
             __syncthreads();
         } else if (t == 0) {
             a.cnt[(size_t)b * a.K + kk] += nkk;
@@ -545,30 +550,43 @@ __global__ __launch_bounds__(256) void upd_combine_kernel(UpdArgs a, int64_t nch
                 cn2 += __shfl_xor(cn2, off);
             }
             if (lane == 0 && a.shp) a.shp[(size_t)chunk * (a.ncb + 1) + a.ncb] = (double)d2;
-            if (lane == 0 && a.cprep) a.cnh[(size_t)b * a.KT * 32 + kk] = 0.5f * cn2;
+            if (lane == 0 && a.cprep) a.cnh[(size_t)b * a.KT * 32 + kk] = refreshed_half_norm(a, cn2);
         } else if (lane == 0) {
             a.cnt[(size_t)b * a.K + kk] += nkk;
         }
     }
 }
 
-// Streamed path, after the last chunk: c_k <- sums_k / cnt_k where cnt_k > 0 (else keep),
-// shift += ||c_new - c_old||^2, prepared centroids refreshed.  One wave per cluster.
+// After the accumulating update (streamed chunks, or the cosine fit): c_k <- sums_k / cnt_k
+// where cnt_k > 0 (else keep), shift += ||c_new - c_old||^2, prepared centroids refreshed.
+// With a.normalize (cosine k-means, the mean direction) c_k <- sums_k / ||sums_k|| (fp32 norm
+// over the row, IEEE division), and a cluster whose sum is the zero vector keeps its centroid
+// too.  One wave per cluster.
 __global__ __launch_bounds__(256) void upd_finalize_acc_kernel(UpdArgs a, int64_t rows) {
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= rows) return;
     const int b = (int)(row / a.K), k = (int)(row - (int64_t)b * a.K);
     const int n = a.cnt[row];
-    if (n <= 0) {  // wave-uniform: the centroid is kept
+    const int D = a.D;
+    float den = (float)n;
+    if (a.normalize && n > 0) {
+        float ss = 0.f;
+        for (int d = lane; d < D; d += 64) {
+            const float v = a.sums[row * D + d];
+            ss += v * v;
+        }
+        for (int off = 1; off < 64; off <<= 1) ss += __shfl_xor(ss, off);
+        den = sqrtf(ss);
+    }
+    if (n <= 0 || !(den > 0.f)) {  // wave-uniform: the centroid is kept
         if (lane == 0 && a.shp) a.shp[row] = 0.0;
         return;
     }
-    const int D = a.D;
     float d2 = 0.f, cn2 = 0.f;
     for (int d = lane; d < D; d += 64) {
         const float old = a.C[row * D + d];
-        const float nw = a.sums[row * D + d] / (float)n;
+        const float nw = a.sums[row * D + d] / den;
         a.C[row * D + d] = nw;
         d2 += (nw - old) * (nw - old);
         if (a.cprep) cn2 += prep_store_elem(a, b, k, d, nw);
@@ -578,7 +596,7 @@ __global__ __launch_bounds__(256) void upd_finalize_acc_kernel(UpdArgs a, int64_
         cn2 += __shfl_xor(cn2, off);
     }
     if (lane == 0 && a.shp) a.shp[row] = (double)d2;
-    if (lane == 0 && a.cprep) a.cnh[(size_t)b * a.KT * 32 + k] = 0.5f * cn2;
+    if (lane == 0 && a.cprep) a.cnh[(size_t)b * a.KT * 32 + k] = refreshed_half_norm(a, cn2);
 }
 
 size_t update_ws_bytes(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
@@ -645,6 +663,7 @@ static UpdArgs make_args(int dt, const void *x, const int32_t *sids, const int32
     a.cnh = ref.cnh;
     a.DP = ref.DP;
     a.KT = ref.KT;
+    a.zero_norm = ref.zero_norm;
     return a;
 }
 
@@ -674,8 +693,10 @@ hipError_t launch_update(int dt, const void *x, const int32_t *sids, const int32
 
 // shk: [B][K] doubles of scratch for the per-cluster shifts (optional, with shift).
 hipError_t launch_finalize_acc(int dt, const float *sums, const int32_t *cnt, float *C, double *shift, double *shk,
-                               const UpdRefresh &ref, int B, int K, int D, hipStream_t s) {
+                               const UpdRefresh &ref, int B, int K, int D, hipStream_t s, int normalize) {
     UpdArgs a{};
+    a.zero_norm = ref.zero_norm;
+    a.normalize = normalize;
     a.dt = dt;
     a.D = D;
     a.K = K;

@@ -59,6 +59,7 @@ struct UpdRefresh {
     void *cprep = nullptr;
     float *cnh = nullptr;
     int DP = 0, KT = 0;
+    int zero_norm = 0;  // similarity metrics: refreshed norm terms are 0
 };
 
 AssignCfg plan_assign(int dt, int64_t B, int64_t N, int64_t D, int64_t K);

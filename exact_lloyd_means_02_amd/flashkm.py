@@ -16,11 +16,15 @@ LIB_PATH = os.environ.get("FLASHKM_LIB") or os.path.join(HERE, "libflashkm.so")
 KM_F32, KM_F16, KM_BF16 = 0, 1, 2
 KM_OK, KM_ERR_INVALID, KM_ERR_UNSUPPORTED, KM_ERR_WORKSPACE, KM_ERR_HIP = 0, -1, -2, -3, -4
 KM_OP_ASSIGN, KM_OP_ARGSORT, KM_OP_UPDATE, KM_OP_FIT, KM_OP_FIT_HOST = 1, 2, 3, 4, 5
+KM_OP_FIT_DOT, KM_OP_FIT_COSINE = 6, 7
+KM_METRIC_L2, KM_METRIC_DOT, KM_METRIC_COSINE = 0, 1, 2
+METRICS = {"l2": KM_METRIC_L2, "euclid": KM_METRIC_L2, "dot": KM_METRIC_DOT, "cosine": KM_METRIC_COSINE}
 STATUS_NAMES = {0: "KM_OK", -1: "KM_ERR_INVALID", -2: "KM_ERR_UNSUPPORTED", -3: "KM_ERR_WORKSPACE", -4: "KM_ERR_HIP"}
 
 # every symbol the header declares
 EXPORTS = ["kmeans_plan", "kmeans_workspace_bytes", "kmeans_row_norms", "kmeans_assign", "kmeans_prepare_centroids",
-           "kmeans_assign_prepared", "kmeans_argsort_ids", "kmeans_update", "kmeans_fit", "kmeans_last_error"]
+           "kmeans_assign_prepared", "kmeans_argsort_ids", "kmeans_update", "kmeans_fit", "kmeans_normalize_rows",
+           "kmeans_prepare_centroids_metric", "kmeans_fit_metric", "kmeans_last_error"]
 
 
 class KmPlan(ctypes.Structure):
@@ -53,8 +57,13 @@ def _load():
     lib.kmeans_argsort_ids.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, sz, vp]
     lib.kmeans_update.argtypes = [vp, ctypes.c_int, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, sz, vp]
     lib.kmeans_fit.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, i32, f32, i64, vp, vp, vp, vp, vp, sz, vp]
+    lib.kmeans_normalize_rows.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp]
+    lib.kmeans_prepare_centroids_metric.argtypes = [vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64, vp, sz, vp]
+    lib.kmeans_fit_metric.argtypes = [vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64, i32, f32, vp, vp, vp, vp,
+                                      vp, sz, vp]
     for n in ("kmeans_plan", "kmeans_row_norms", "kmeans_assign", "kmeans_prepare_centroids",
-              "kmeans_assign_prepared", "kmeans_argsort_ids", "kmeans_update", "kmeans_fit"):
+              "kmeans_assign_prepared", "kmeans_argsort_ids", "kmeans_update", "kmeans_fit", "kmeans_normalize_rows",
+              "kmeans_prepare_centroids_metric", "kmeans_fit_metric"):
         getattr(lib, n).restype = ctypes.c_int
     lib.kmeans_last_error.argtypes = []
     lib.kmeans_last_error.restype = ctypes.c_char_p
@@ -176,9 +185,17 @@ class PreparedCentroids:
         self.buf, self.dt, self.B, self.D, self.K = buf, dt, B, D, K
 
 
-def kmeans_prepare_centroids(centroids, dtype, out=None, stream=None) -> PreparedCentroids:
-    """c~ = dtype(centroids) in the assign kernel's layout plus ||c~||^2 / 2.  `dtype` is the
-    points' torch dtype (or a tensor of it)."""
+def metric_code(metric) -> int:
+    if isinstance(metric, int) and metric in METRICS.values():
+        return metric
+    if metric not in METRICS:
+        raise ValueError("unknown metric %r (one of %s)" % (metric, sorted(METRICS)))
+    return METRICS[metric]
+
+
+def kmeans_prepare_centroids(centroids, dtype, out=None, stream=None, metric="l2") -> PreparedCentroids:
+    """c~ = dtype(centroids) in the assign kernel's layout plus ||c~||^2 / 2 (0 for the "dot" and
+    "cosine" metrics).  `dtype` is the points' torch dtype (or a tensor of it)."""
     torch = _torch()
     _need(centroids.dim() == 3 and centroids.is_contiguous() and centroids.dtype == torch.float32,
           "centroids must be contiguous f32 [B, K, D]")
@@ -192,9 +209,27 @@ def kmeans_prepare_centroids(centroids, dtype, out=None, stream=None) -> Prepare
         off = (-raw.data_ptr()) % 256
         out = raw[off:off + nbytes]
     _need(out.dtype == torch.uint8 and out.numel() >= nbytes, "out: uint8 device buffer too small")
-    _check(LIB.kmeans_prepare_centroids(_ptr(centroids), dt, B, K, D, K, _ptr(out), out.numel(),
-                                        _stream(centroids, stream)))
+    m = metric_code(metric)
+    if m == KM_METRIC_L2:
+        _check(LIB.kmeans_prepare_centroids(_ptr(centroids), dt, B, K, D, K, _ptr(out), out.numel(),
+                                            _stream(centroids, stream)))
+    else:
+        _check(LIB.kmeans_prepare_centroids_metric(_ptr(centroids), dt, m, B, K, D, K, _ptr(out), out.numel(),
+                                                   _stream(centroids, stream)))
     return PreparedCentroids(out, dt, B, D, K)
+
+
+def kmeans_normalize_rows(x, out=None, stream=None):
+    """Unit rows dtype(x_i / ||x_i||) over the last axis (zero rows stay zero); `out` may be `x`."""
+    torch = _torch()
+    _need(x.is_contiguous() and x.dim() >= 1, "x must be contiguous")
+    D = x.shape[-1]
+    rows = x.numel() // D
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out.shape == x.shape and out.dtype == x.dtype and out.is_contiguous(), "out: same shape and dtype")
+    _check(LIB.kmeans_normalize_rows(_ptr(x), dtype_code(x), rows, D, _ptr(out), _stream(x, stream)))
+    return out
 
 
 def kmeans_assign_prepared(x, prep: PreparedCentroids, x_norms=None, assign=None, min_dist=None,
@@ -271,6 +306,33 @@ def kmeans_fit(x, centroids, iters: int, tol: float = 0.0, chunk_points: int = 0
                           _ptr(assign), inertia.ctypes.data_as(ctypes.c_void_p), ctypes.byref(done), _ptr(ws),
                           ws.numel(), _stream(centroids, stream)))
     return assign, inertia[: done.value], done.value
+
+
+def kmeans_fit_metric(x, centroids, metric, iters: int, tol: float = 0.0, assign=None, want_assign=True,
+                      stream=None):
+    """k-means under `metric` ("l2", "dot" or "cosine") on device-resident x.  `centroids` (device f32
+    [B,K,D]) holds the init and receives the result (unit rows for cosine).  Returns (assign,
+    objective [iters_done, B] numpy float64: inertia for "l2", total similarity otherwise,
+    iters_done)."""
+    torch = _torch()
+    import numpy as np
+    m = metric_code(metric)
+    _need(x.dim() == 3 and x.is_contiguous(), "x must be a contiguous [B, N, D] tensor")
+    B, N, D = x.shape
+    _need(centroids.is_cuda and centroids.dtype == torch.float32 and centroids.is_contiguous(), "centroids")
+    K = centroids.shape[1]
+    dev = centroids.device
+    if want_assign and assign is None:
+        assign = torch.empty((B, N), dtype=torch.int32, device=dev)
+    dt = dtype_code(x)
+    op = {KM_METRIC_L2: KM_OP_FIT, KM_METRIC_DOT: KM_OP_FIT_DOT, KM_METRIC_COSINE: KM_OP_FIT_COSINE}[m]
+    ws = workspace(op, dt, B, N, D, K, dev)
+    obj = np.zeros((iters, B), dtype=np.float64)
+    done = ctypes.c_int32(0)
+    _check(LIB.kmeans_fit_metric(_ptr(x), dt, m, B, N, D, K, int(iters), float(tol), _ptr(centroids), _ptr(assign),
+                                 obj.ctypes.data_as(ctypes.c_void_p), ctypes.byref(done), _ptr(ws), ws.numel(),
+                                 _stream(centroids, stream)))
+    return assign, obj[: done.value], done.value
 
 
 def batch_kmeans_euclid(x, n_clusters: int, max_iters: int = 100, tol: float = 0.0, init_centroids=None,

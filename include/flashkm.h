@@ -63,8 +63,17 @@ typedef enum {
     KM_OP_ARGSORT = 2,
     KM_OP_UPDATE = 3,
     KM_OP_FIT = 4,            /* kmeans_fit with device-resident x */
-    KM_OP_FIT_HOST = 5        /* kmeans_fit with x in pinned host memory (streamed path) */
+    KM_OP_FIT_HOST = 5,       /* kmeans_fit with x in pinned host memory (streamed path) */
+    KM_OP_FIT_DOT = 6,        /* kmeans_fit_metric, KM_METRIC_DOT, device-resident x */
+    KM_OP_FIT_COSINE = 7      /* kmeans_fit_metric, KM_METRIC_COSINE, device-resident x */
 } km_op_t;
+
+/* Similarity of a point and a centroid (see kmeans_fit_metric). */
+typedef enum {
+    KM_METRIC_L2 = 0,         /* squared Euclidean distance: Lloyd's k-means */
+    KM_METRIC_DOT = 1,        /* dot product x.c, maximised */
+    KM_METRIC_COSINE = 2      /* cosine x.c / (||x|| ||c||), maximised (spherical k-means) */
+} km_metric_t;
 
 /*
  * Tile plan chosen by the analytic heuristic (paper summary, "Key claims": a
@@ -213,6 +222,46 @@ km_status_t kmeans_fit(const void *x, km_dtype_t dt, int64_t B, int64_t N, int64
                        int32_t iters, float tol, int64_t chunk_points, float *centroids,
                        int32_t *assign, double *inertia, int32_t *iters_done, void *ws,
                        size_t ws_bytes, void *stream);
+
+/*
+ * Dot-product and cosine k-means.  The project README ("CuTe backend") names
+ * both as modes of the library without defining them; the readings taken:
+ *   KM_METRIC_DOT: a_i = the lowest k maximising x_i.c~_k; the update is the
+ *     mean of the members (a cluster without points keeps its centroid).
+ *   KM_METRIC_COSINE (spherical k-means): the points are used as unit rows
+ *     x^_i = dtype(x_i / ||x_i||) (kmeans_normalize_rows; a zero row stays
+ *     zero) and the initial centroids are made unit rows in place; a_i = the
+ *     lowest k maximising x^_i.c~_k; the update is the mean direction
+ *     c_k = S_k / ||S_k||, S_k = sum_{a_i = k} x^_i (fp32), and a cluster
+ *     without points, or with S_k = 0, keeps its centroid.
+ *   KM_METRIC_L2: exactly kmeans_fit.
+ * Both similarity metrics run on the same kernels as Lloyd's loop: the
+ * assign kernels get zero norm terms, so they take the arg-max of x.c~ with
+ * ties to the lowest index.
+ *
+ * kmeans_normalize_rows: out_i = dtype(x_i / ||x_i||) for `rows` rows of D
+ *   elements (fp32 norm and IEEE division, nearest-even rounding); out may
+ *   equal x.  x and out: device, 16-byte aligned.
+ * kmeans_prepare_centroids_metric: kmeans_prepare_centroids with the norm
+ *   terms 0 for KM_METRIC_DOT / KM_METRIC_COSINE (the centroids are taken as
+ *   given: unit rows are the caller's business here); the result feeds
+ *   kmeans_assign_prepared, whose min_dist then holds x_norms_i - 2 x_i.c~_a.
+ * kmeans_fit_metric: kmeans_fit for a metric, device-resident x only
+ *   (pinned host x with a similarity metric -> KM_ERR_UNSUPPORTED); ws from
+ *   kmeans_workspace_bytes(KM_OP_FIT / KM_OP_FIT_DOT / KM_OP_FIT_COSINE).
+ *   `objective` (host double [iters * B] or NULL): for KM_METRIC_L2 the
+ *   inertia; otherwise the total similarity sum_i x_i.c~_{a_i} (x^ for
+ *   cosine) of each iteration's assignment (fp32 terms, fp64 sum).
+ */
+km_status_t kmeans_normalize_rows(const void *x, km_dtype_t dt, int64_t rows, int64_t D, void *out,
+                                  void *stream);
+km_status_t kmeans_prepare_centroids_metric(const float *centroids, km_dtype_t dt, km_metric_t metric,
+                                            int64_t B, int64_t N, int64_t D, int64_t K, void *c_prep,
+                                            size_t c_prep_bytes, void *stream);
+km_status_t kmeans_fit_metric(const void *x, km_dtype_t dt, km_metric_t metric, int64_t B, int64_t N,
+                              int64_t D, int64_t K, int32_t iters, float tol, float *centroids,
+                              int32_t *assign, double *objective, int32_t *iters_done, void *ws,
+                              size_t ws_bytes, void *stream);
 
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char *kmeans_last_error(void);

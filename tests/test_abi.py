@@ -158,3 +158,48 @@ def test_workload_generators_are_seeded():
     x, c, mu = W.make(w2)
     assert mu is not None and abs(mu[0, :4].mean() - 64.0) < 2.0   # the +64 channels, centred away
     assert abs(W.storage_to_f64(x, "bf16")[0, :, :4].mean()) < 0.5
+
+
+def test_metric_entry_validation(fk):
+    L = fk.LIB
+    # kmeans_normalize_rows(x, dt, rows, D, out, stream)
+    assert L.kmeans_normalize_rows(None, 2, 10, 16, P, None) == fk.KM_ERR_INVALID and "x is NULL" in fk.last_error()
+    assert L.kmeans_normalize_rows(P, 2, 10, 16, None, None) == fk.KM_ERR_INVALID
+    assert L.kmeans_normalize_rows(P, 9, 10, 16, P, None) == fk.KM_ERR_INVALID and "dtype" in fk.last_error()
+    assert L.kmeans_normalize_rows(P, 2, 0, 16, P, None) == fk.KM_ERR_INVALID
+    assert L.kmeans_normalize_rows(P, 2, 10, 5000, P, None) == fk.KM_ERR_INVALID
+    assert L.kmeans_normalize_rows(P, 2, 10, 16, ctypes.c_void_p(264), None) == fk.KM_ERR_INVALID
+    assert "aligned" in fk.last_error()
+    # kmeans_prepare_centroids_metric(c, dt, metric, B, N, D, K, c_prep, bytes, stream)
+    assert L.kmeans_prepare_centroids_metric(P, 2, 3, 1, 100, 16, 10, P, 1 << 20, None) == fk.KM_ERR_INVALID
+    assert "metric" in fk.last_error()
+    assert L.kmeans_prepare_centroids_metric(P, 2, 1, 1, 100, 16, 10, P, 16, None) == fk.KM_ERR_WORKSPACE
+    assert L.kmeans_prepare_centroids_metric(None, 2, 2, 1, 100, 16, 10, P, 1 << 20, None) == fk.KM_ERR_INVALID
+    # kmeans_fit_metric(x, dt, metric, B, N, D, K, iters, tol, C, assign, obj, done, ws, bytes, stream)
+    def fit(**kw):
+        a = dict(x=P, dt=2, m=1, B=1, N=10, D=4, K=3, it=5, tol=0.0, C=P, ws=P, wsb=1 << 20)
+        a.update(kw)
+        return L.kmeans_fit_metric(a["x"], a["dt"], a["m"], a["B"], a["N"], a["D"], a["K"], a["it"], a["tol"],
+                                   a["C"], None, None, None, a["ws"], a["wsb"], None)
+    assert fit(m=-1) == fk.KM_ERR_INVALID and "metric" in fk.last_error()
+    assert fit(it=0) == fk.KM_ERR_INVALID and "iters" in fk.last_error()
+    assert fit(tol=-1.0) == fk.KM_ERR_INVALID
+    assert fit(K=11) == fk.KM_ERR_INVALID
+    assert fit(C=None) == fk.KM_ERR_INVALID
+    assert fit(x=ctypes.c_void_p(258), m=2) == fk.KM_ERR_INVALID
+    assert fit(ws=None, m=2) == fk.KM_ERR_WORKSPACE
+    # the L2 metric is kmeans_fit: same validation
+    assert fit(m=0, it=0) == fk.KM_ERR_INVALID and "iters" in fk.last_error()
+
+
+def test_metric_workspace_sizes(fk):
+    B, N, D, K = 2, 5000, 64, 100
+    for dt, s in ((0, 4), (1, 2), (2, 2)):
+        base = fk.kmeans_workspace_bytes(fk.KM_OP_FIT, dt, B, N, D, K)
+        dot = fk.kmeans_workspace_bytes(fk.KM_OP_FIT_DOT, dt, B, N, D, K)
+        cos = fk.kmeans_workspace_bytes(fk.KM_OP_FIT_COSINE, dt, B, N, D, K)
+        assert dot == base
+        # the unit rows, sums, counts and per-cluster shifts come on top
+        assert cos >= base + B * N * D * s + B * K * D * 4 + B * K * 4 + B * K * 8
+        assert cos <= base + B * N * D * s + B * K * D * 4 + B * K * 4 + B * K * 8 + 4 * 256
+    assert fk.kmeans_workspace_bytes(99, 2, B, N, D, K) == 0
