@@ -343,9 +343,145 @@ def batch_kmeans_euclid(x, n_clusters: int, max_iters: int = 100, tol: float = 0
     B, N, D = x.shape
     dev = x.device if x.is_cuda else torch.device("cuda")
     if init_centroids is None:
-        g = torch.Generator(device="cpu").manual_seed(seed)
-        idx = torch.stack([torch.randperm(N, generator=g)[:n_clusters] for _ in range(B)])
-        init_centroids = torch.stack([x[b].index_select(0, idx[b].to(x.device)) for b in range(B)]).float()
+        init_centroids = _seeded_init(x, n_clusters, seed)
     c = init_centroids.to(dev, dtype=torch.float32).contiguous().clone()
     ids, inertia, _ = kmeans_fit(x, c, max_iters, tol, chunk_points)
     return ids, c, inertia
+
+
+def batch_kmeans_cosine(x, n_clusters: int, max_iters: int = 100, tol: float = 0.0, init_centroids=None, seed: int = 0):
+    """Cosine (spherical) k-means, README-style: returns (cluster_ids, unit centers, objective)."""
+    return _batch_metric(x, n_clusters, max_iters, tol, init_centroids, seed, "cosine")
+
+
+def batch_kmeans_dot(x, n_clusters: int, max_iters: int = 100, tol: float = 0.0, init_centroids=None, seed: int = 0):
+    """Dot-product k-means, README-style: returns (cluster_ids, centers, objective)."""
+    return _batch_metric(x, n_clusters, max_iters, tol, init_centroids, seed, "dot")
+
+
+def _seeded_init(x, n_clusters: int, seed: int):
+    """K distinct points per problem, drawn with torch's CPU generator (fp32 copies)."""
+    torch = _torch()
+    B, N, _ = x.shape
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    idx = torch.stack([torch.randperm(N, generator=g)[:n_clusters] for _ in range(B)])
+    return torch.stack([x[b].index_select(0, idx[b].to(x.device)) for b in range(B)]).float()
+
+
+def _batch_metric(x, n_clusters, max_iters, tol, init_centroids, seed, metric):
+    torch = _torch()
+    _need(x.is_cuda, "the dot-product and cosine metrics need x on the GPU")
+    if init_centroids is None:
+        init_centroids = _seeded_init(x, n_clusters, seed)
+    c = init_centroids.to(x.device, dtype=torch.float32).contiguous().clone()
+    ids, obj, _ = kmeans_fit_metric(x, c, metric, max_iters, tol)
+    return ids, c, obj
+
+
+class FlashKMeans:
+    """faiss / scikit-learn style k-means object over the C-ABI (README: "an API interface similar to
+    faiss/sklearn"; "FlashKMeans(d=..., k=..., niter=..., tol=..., dtype=...)", with train / fit /
+    predict / fit_predict and init_centroids).
+
+    Input: [N, d] (one problem) or [B, N, d] (B independent problems sharing k), on the GPU, or in
+    host memory.  Pinned host memory selects the streamed path (Euclidean metric); other host
+    tensors are copied to the GPU first.  `dtype` is the compute dtype the points are cast to.
+    After fitting: `centroids` (fp32 [B, k, d], or [k, d] for 2-D input), `labels_` (from the last
+    assignment), `obj` (per-iteration inertia, or total similarity for "dot" / "cosine"),
+    `iters_done`.  `cluster_centers_` and `inertia_` mirror scikit-learn's names."""
+
+    def __init__(self, d: int, k: int, niter: int = 25, tol: float = 0.0, dtype=None, metric: str = "l2",
+                 device=None, seed: int = 0, verbose: bool = False, chunk_points: int = 0):
+        torch = _torch()
+        _need(d >= 1 and k >= 1 and niter >= 1 and tol >= 0.0, "d, k, niter must be >= 1 and tol >= 0")
+        metric_code(metric)
+        self.d, self.k, self.niter, self.tol = int(d), int(k), int(niter), float(tol)
+        self.dtype = dtype if dtype is not None else torch.float16
+        _need(self.dtype in (torch.float32, torch.float16, torch.bfloat16), "dtype: float32, float16 or bfloat16")
+        self.metric = metric
+        self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        self.seed, self.verbose, self.chunk_points = int(seed), bool(verbose), int(chunk_points)
+        self.centroids = None
+        self.labels_ = None
+        self.obj = None
+        self.iters_done = 0
+        self._batched = True
+        self._prep = None
+
+    # -- input marshalling
+    def _points(self, x, fitting=False):
+        _need(x.dim() in (2, 3) and x.shape[-1] == self.d, "x must be [N, %d] or [B, N, %d]" % (self.d, self.d))
+        if fitting:
+            _need(self.k <= x.shape[-2], "k (%d) > number of points (%d)" % (self.k, x.shape[-2]))
+        batched = x.dim() == 3
+        x3 = x if batched else x.unsqueeze(0)
+        if x3.dtype != self.dtype:
+            x3 = x3.to(self.dtype)
+        if x3.is_cuda:
+            x3 = x3.to(self.device)
+        elif not (x3.is_pinned() and self.metric in ("l2", "euclid")):
+            x3 = x3.to(self.device)
+        return x3.contiguous(), batched
+
+    def _out(self, t, batched):
+        return t if batched else t[0]
+
+    # -- faiss names
+    def train(self, x, init_centroids=None):
+        """Fits the centroids; returns self."""
+        torch = _torch()
+        x3, batched = self._points(x, fitting=True)
+        B, N, _ = x3.shape
+        if init_centroids is None:
+            init = _seeded_init(x3, self.k, self.seed)
+        else:
+            init = init_centroids if init_centroids.dim() == 3 else init_centroids.unsqueeze(0)
+            _need(tuple(init.shape) == (B, self.k, self.d), "init_centroids must be [B, k, d] or [k, d]")
+        c = init.to(self.device, dtype=torch.float32).contiguous().clone()
+        if self.metric in ("l2", "euclid"):
+            a, obj, done = kmeans_fit(x3, c, self.niter, self.tol, self.chunk_points)
+        else:
+            a, obj, done = kmeans_fit_metric(x3, c, self.metric, self.niter, self.tol)
+        self.centroids = c
+        self.labels_ = a
+        self.obj = obj
+        self.iters_done = done
+        self._batched = batched
+        self._prep = None
+        if self.verbose:
+            for t in range(done):
+                print("iteration %d: %s" % (t, " ".join("%.6g" % v for v in obj[t])))
+        return self
+
+    def fit(self, x, init_centroids=None):
+        return self.train(x, init_centroids)
+
+    def predict(self, x):
+        """Nearest (or most similar) fitted centroid of every point, through FlashAssign."""
+        torch = _torch()
+        _need(self.centroids is not None, "call fit / train first")
+        x3, batched = self._points(x)
+        if not x3.is_cuda:
+            x3 = x3.to(self.device)
+        _need(x3.shape[0] == self.centroids.shape[0], "x has %d problems, the model %d" % (
+            x3.shape[0], self.centroids.shape[0]))
+        if self._prep is None:
+            self._prep = kmeans_prepare_centroids(self.centroids, x3.dtype, metric=self.metric)
+        if self.metric == "cosine":
+            x3 = kmeans_normalize_rows(x3)
+        a, _ = kmeans_assign_prepared(x3, self._prep)
+        return self._out(a, batched)
+
+    def fit_predict(self, x, init_centroids=None):
+        """Fits, then returns the labels of the last assignment."""
+        self.train(x, init_centroids)
+        return self._out(self.labels_, self._batched)
+
+    # -- scikit-learn names
+    @property
+    def cluster_centers_(self):
+        return None if self.centroids is None else self._out(self.centroids, self._batched)
+
+    @property
+    def inertia_(self):
+        return None if self.obj is None or len(self.obj) == 0 else self.obj[-1]

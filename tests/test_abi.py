@@ -203,3 +203,20 @@ def test_metric_workspace_sizes(fk):
         assert cos >= base + B * N * D * s + B * K * D * 4 + B * K * 4 + B * K * 8
         assert cos <= base + B * N * D * s + B * K * D * 4 + B * K * 4 + B * K * 8 + 4 * 256
     assert fk.kmeans_workspace_bytes(99, 2, B, N, D, K) == 0
+
+
+def test_wrapper_validation_without_gpu(fk):
+    import torch
+    km = fk.FlashKMeans(d=8, k=5, niter=2, dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(ValueError, match="must be"):
+        km.fit(torch.zeros(100, 7))
+    with pytest.raises(ValueError, match="k \\(5\\) > number of points"):
+        km.fit(torch.zeros(4, 8))
+    with pytest.raises(ValueError, match="fit / train first"):
+        km.predict(torch.zeros(10, 8))
+    with pytest.raises(ValueError, match="unknown metric"):
+        fk.FlashKMeans(d=8, k=5, metric="manhattan", device="cuda:0")
+    with pytest.raises(ValueError):
+        fk.FlashKMeans(d=8, k=0, device="cuda:0")
+    with pytest.raises(ValueError, match="dtype"):
+        fk.FlashKMeans(d=8, k=5, dtype=torch.float64, device="cuda:0")
