@@ -34,7 +34,8 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--warmup", type=int, default=50,
+                   help="untimed iterations first: the GPU takes a few tens of ms of work to reach its steady clocks")
     p.add_argument("--workload", default="headline_bf16")
     p.add_argument("--stage-reps", type=int, default=10)
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
