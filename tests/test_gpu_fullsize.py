@@ -281,3 +281,65 @@ def test_streamed_real_chunks(fk):
     num = np.linalg.norm(cs - cd, axis=2)
     den = np.maximum(np.linalg.norm(cd, axis=2), 1e-30)
     assert (num / den).max() <= 1e-5
+
+
+# ---------------------------------------------------------------------------------------------
+# dot-product and cosine k-means at the headline size (one iteration, teacher forced)
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("metric", ["dot", "cosine"])
+def test_headline_metric_full(fk, metric):
+    from oracle import similarity as sim
+    from helpers import NEAR
+    w = W.WORKLOADS["headline_bf16"]
+    B, N, D, K = w.B, w.N, w.D, w.K
+    _say("headline %s: generating %s" % (metric, w))
+    x, c0, _ = W.make(w)
+    xt = W.to_torch(x, w.dtype).to(device())
+    ct = torch.from_numpy(c0).to(device())
+    c = ct.clone()
+    a, obj, done = fk.kmeans_fit_metric(xt, c, metric, 1)
+    assert done == 1
+    if metric == "cosine":
+        xa_t = fk.kmeans_normalize_rows(xt)                 # the unit rows the fit used
+        c_start = fk.kmeans_normalize_rows(ct).cpu().numpy().astype(np.float64)
+        xa = W.from_torch(xa_t, w.dtype)
+    else:
+        xa, c_start = x, c0.astype(np.float64)
+    torch.cuda.synchronize()
+    a_np = a.cpu().numpy().astype(np.int64)
+    cg = c.cpu().numpy().astype(np.float64)
+    ct64 = operand(c_start, w.dtype)
+    _say("GPU fit done")
+    rng = np.random.default_rng(41)
+    flips = 0
+    for b in range(B):
+        samp = np.sort(rng.choice(N, size=512, replace=False))
+        xs = _rows64(xa, w, b, samp)
+        a_or, s1, s2, scale = sim.similarity_assign(xs, ct64[b])
+        bad = (a_np[b, samp] != a_or) & ~sim.similarity_near_mask(s1, s2, scale, NEAR)
+        assert not bad.any(), "problem %d: picks differ outside the near-tie band" % b
+        flips += int((a_np[b, samp] != a_or).sum())
+    _say("assign: 512 sampled points per problem, %d near-tie flips" % flips)
+    tol = CENTROID_TOL[w.dtype]
+    worst = 0.0
+    for b in range(B):
+        counts = np.bincount(a_np[b], minlength=K)
+        kept = counts == 0
+        assert np.array_equal(cg[b][kept], c_start[b][kept].astype(np.float32).astype(np.float64))
+        ks = np.unique(np.concatenate([np.argsort(-counts, kind="stable")[:4], rng.choice(K, 24, replace=False)]))
+        for k in ks:
+            rows = np.nonzero(a_np[b] == k)[0]
+            if rows.size == 0:
+                continue
+            s = _rows64(xa, w, b, rows).sum(axis=0)
+            c_or = s / rows.size if metric == "dot" else s / np.linalg.norm(s)
+            rel = np.linalg.norm(cg[b, k] - c_or) / max(np.linalg.norm(c_or), 1e-30)
+            worst = max(worst, rel)
+            assert rel <= tol, "problem %d cluster %d: rel err %g" % (b, k, rel)
+        # the objective in full: sum_i x_i . c~_{a_i}
+        j = 0.0
+        for lo in range(0, N, BLOCK):
+            xb = W.storage_to_f64(xa[b, lo:lo + BLOCK], w.dtype)
+            j += float(np.einsum("nd,nd->n", xb, ct64[b][a_np[b, lo:lo + BLOCK]]).sum())
+        assert abs(obj[0, b] - j) <= INERTIA_TOL * abs(j)
+    _say("update: sampled clusters, worst rel err %.3g; objective matches in full" % worst)
