@@ -57,11 +57,12 @@ def assign_source_hash() -> str:
     return hashlib.sha256(open(ASSIGN_SRC, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(workload: str):
     """HBM bytes per FlashAssign launch from the committed counter summary (FETCH_SIZE +
-    WRITE_SIZE, scaled by the copy-kernel factor), or None when the summary is missing or was
-    taken on another version of the kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+    WRITE_SIZE, scaled by the copy-kernel factor), or None when the summary is missing, was
+    taken on another version of the kernel source, or covers another workload (it covers the
+    headline one)."""
+    if workload != "headline_bf16" or not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
     for line in open(TRAFFIC_FILE):
@@ -358,8 +359,9 @@ def main():
         "config": {"workload": w.name, "B": w.B, "N": w.N, "D": w.D, "K": w.K, "iters": args.steps, "tol": 0.0,
                    "inputs": "HBM-resident", "metric": args.metric},
         "roofline": {"bound": "mfma", "achieved": round(assign_tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(assign_tflops / peak, 4), "traffic": measured_traffic(),
-                     "kernel": "FlashAssign (small-D) kernel, one launch per kmeans_assign_prepared call",
+                     "frac": round(assign_tflops / peak, 4), "traffic": measured_traffic(w.name),
+                     "kernel": "FlashAssign (%s) kernel, one launch per kmeans_assign_prepared call" % (
+                         "small-D" if fk.kmeans_plan(fk.dtype_code(xt), w.B, w.N, w.D, w.K)["path"] == 0 else "split-D"),
                      "kernel_ms": round(st["assign"], 4), "flop_per_launch": flops,
                      "algorithmic_bytes_per_launch": abytes},
         "stages_ms": {k: round(v, 4) for k, v in st.items()},
