@@ -50,11 +50,15 @@ def parse():
 
 
 ASSIGN_SRC = os.path.join(ROOT, "exact_lloyd_means_02_amd", "csrc", "k_assign.hip")
+BUILD_SCRIPT = os.path.join(ROOT, "exact_lloyd_means_02_amd", "build.py")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "assign_small_d_headline_bf16_traffic.txt")
 
 
 def assign_source_hash() -> str:
-    return hashlib.sha256(open(ASSIGN_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the FlashAssign source and of the build script (which holds its compiler flags)."""
+    h = hashlib.sha256(open(ASSIGN_SRC, "rb").read())
+    h.update(open(BUILD_SCRIPT, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
@@ -69,7 +73,7 @@ def measured_traffic(workload: str):
         if ": " in line and not line.startswith("#"):
             k, v = line.split(": ", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("k_assign.hip sha256[:16]") != assign_source_hash():
+    if kv.get("k_assign.hip + build.py sha256[:16]") != assign_source_hash():
         return None
     try:
         return float(kv["traffic bytes per launch"])

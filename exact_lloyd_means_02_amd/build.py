@@ -26,9 +26,11 @@ FLAGS = [
 
 # Per-file extras.  The assign kernels: scores are never NaN (finite inputs; padding is +inf), so
 # fminf needs no NaN quieting; MFMA results stay in VGPRs so the arg-min selects read them
-# directly instead of copying out of AGPRs.
+# directly instead of copying out of AGPRs; the memory-clause scheduling strategy keeps every
+# instance at the occupancy of the default one and runs the headline instance about 1% faster.
 EXTRA = {
-    "k_assign.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "k_assign.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form",
+                     "-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
 }
 
 
