@@ -574,10 +574,14 @@ struct StreamedPipe {
     }
 };
 
+// metric as in fit_device.  Cosine k-means turns each staged chunk into unit rows in place (the
+// staging buffer is a device copy of x) before its assign and update.
 km_status_t fit_host(int dt, const void *xh, int64_t B, int64_t N, int64_t D, int64_t K, int iters, float tol,
                      int64_t chunk_points, float *C, int32_t *assign, double *inertia, int32_t *iters_done, char *ws,
-                     hipStream_t s) {
+                     hipStream_t s, int metric = KM_METRIC_L2) {
     const HostLayout L = host_layout(dt, B, N, D, K, chunk_points);
+    const bool simm = metric != KM_METRIC_L2;
+    const bool cosine = metric == KM_METRIC_COSINE;
     const int64_t chunk = L.chunk;
     const int64_t nchunk = ceil_div(N, chunk);
     const size_t es = elem_bytes(dt);
@@ -600,7 +604,7 @@ km_status_t fit_host(int dt, const void *xh, int64_t B, int64_t N, int64_t D, in
     double *ring_s = (double *)(ws + L.ring_s);
     void *red = ws + L.red;
     void *scratch = ws + L.scratch;
-    const UpdRefresh ref{cprep, cnh, cfg.d_pad, (int)KT};
+    const UpdRefresh ref{cprep, cnh, cfg.d_pad, (int)KT, simm ? 1 : 0};
 
     StreamedPipe P;
     KM_HIP(hipStreamCreateWithFlags(&P.cs, hipStreamNonBlocking));
@@ -630,7 +634,10 @@ km_status_t fit_host(int dt, const void *xh, int64_t B, int64_t N, int64_t D, in
     KM_HIP(hipEventRecord(P.ev_free[0], s));
     KM_HIP(hipEventRecord(P.ev_free[1], s));
     KM_TRY(issue_copy(0));
-    KM_HIP(launch_prep_centroids(dt, C, cprep, cnh, (int)B, (int)K, (int)D, cfg.d_pad, s, 0));
+    if (cosine) KM_HIP(launch_normalize_rows(KM_F32, C, C, B * K, (int)D, s));
+    // the similarity metrics take zero point norms (their per-point value is then -2 x.c~)
+    if (simm) KM_HIP(launch_fill_i32((int32_t *)xn, chunk, 0, s));
+    KM_HIP(launch_prep_centroids(dt, C, cprep, cnh, (int)B, (int)K, (int)D, cfg.d_pad, s, simm ? 1 : 0));
     int64_t q = 0;
     int done = 0, flushed = 0;
     for (int t = 0; t < iters; ++t) {
@@ -647,9 +654,10 @@ km_status_t fit_host(int dt, const void *xh, int64_t B, int64_t N, int64_t D, in
             const void *xc = stage_buf[buf];
             KM_HIP(hipStreamWaitEvent(s, P.ev_copy[buf], 0));
             int32_t *ac = assign ? assign + (size_t)b * N + lo : a_ws;
-            if (cfg.path != 0) KM_HIP(launch_row_norms(dt, xc, xn, n, (int)D, s));
+            if (cosine) KM_HIP(launch_normalize_rows(dt, xc, stage_buf[buf], n, (int)D, s));
+            if (cfg.path != 0 && !simm) KM_HIP(launch_row_norms(dt, xc, xn, n, (int)D, s));
             KM_HIP(launch_assign(dt, cfg, xc, cprep + (size_t)b * cprep_per_b, cnh + (size_t)b * KT * 32,
-                                 cfg.path == 0 ? nullptr : xn, ac, md,
+                                 (cfg.path == 0 && !simm) ? nullptr : xn, ac, md,
                                  nullptr, 1, (int)n, (int)D, (int)K, s));
             KM_HIP(launch_sum_f32(md, 1, n, ring_j + (size_t)slot * B + b, 1, red, s));
             KM_HIP(launch_argsort(ac, 1, (int)n, (int)K, sids, sidx, counts, scratch, s));
@@ -658,7 +666,7 @@ km_status_t fit_host(int dt, const void *xh, int64_t B, int64_t N, int64_t D, in
             KM_HIP(hipEventRecord(P.ev_free[buf], s));
         }
         KM_HIP(launch_finalize_acc(dt, sums, cnt, C, tol > 0.f ? ring_s + (size_t)slot * B : nullptr,
-                                   (double *)(ws + L.shk), ref, (int)B, (int)K, (int)D, s, 0));
+                                   (double *)(ws + L.shk), ref, (int)B, (int)K, (int)D, s, cosine ? 1 : 0));
         done = t + 1;
         bool stop = false;
         if (tol > 0.f) {
@@ -674,6 +682,8 @@ km_status_t fit_host(int dt, const void *xh, int64_t B, int64_t N, int64_t D, in
     }
     KM_HIP(hipStreamSynchronize(s));
     KM_HIP(hipStreamSynchronize(P.cs));
+    if (simm && inertia)
+        for (int64_t i = 0; i < (int64_t)done * B; ++i) inertia[i] *= -0.5;
     if (iters_done) *iters_done = done;
     return ok();
 }
@@ -681,29 +691,36 @@ km_status_t fit_host(int dt, const void *xh, int64_t B, int64_t N, int64_t D, in
 }  // namespace
 
 extern "C" km_status_t kmeans_fit_metric(const void *x, km_dtype_t dt, km_metric_t metric, int64_t B, int64_t N,
-                                         int64_t D, int64_t K, int32_t iters, float tol, float *centroids,
-                                         int32_t *assign, double *objective, int32_t *iters_done, void *ws,
-                                         size_t ws_bytes, void *stream) {
+                                         int64_t D, int64_t K, int32_t iters, float tol, int64_t chunk_points,
+                                         float *centroids, int32_t *assign, double *objective, int32_t *iters_done,
+                                         void *ws, size_t ws_bytes, void *stream) {
     if (!metric_ok(metric)) return fail(KM_ERR_INVALID, "unknown metric %d", (int)metric);
     if (metric == KM_METRIC_L2)
-        return kmeans_fit(x, dt, B, N, D, K, iters, tol, 0, centroids, assign, objective, iters_done, ws, ws_bytes,
-                          stream);
+        return kmeans_fit(x, dt, B, N, D, K, iters, tol, chunk_points, centroids, assign, objective, iters_done, ws,
+                          ws_bytes, stream);
     KM_TRY(check_shape(dt, B, N, D, K));
     KM_TRY(check_ptr(x, "x"));
     KM_TRY(check_ptr(centroids, "centroids"));
     if (iters < 1) return fail(KM_ERR_INVALID, "iters must be >= 1");
     if (!(tol >= 0.f)) return fail(KM_ERR_INVALID, "tol must be >= 0");
+    if (chunk_points < 0) return fail(KM_ERR_INVALID, "chunk_points must be >= 0");
     if (((uintptr_t)x & 15) != 0) return fail(KM_ERR_INVALID, "x must be 16-byte aligned");
     if (!ws) return fail(KM_ERR_WORKSPACE, "workspace is NULL");
     KM_TRY(check_device_arch());
-    if (pointer_kind(x) != PTR_DEVICE)
-        return fail(KM_ERR_UNSUPPORTED, "the dot-product and cosine metrics need device-resident x");
+    const PtrKind xk = pointer_kind(x);
+    if (xk == PTR_PAGEABLE)
+        return fail(KM_ERR_UNSUPPORTED, "x is pageable host memory; pass device memory or pinned host memory");
     KM_TRY(require_device(centroids, "centroids"));
     KM_TRY(require_device(assign, "assign"));
     KM_TRY(require_device(ws, "ws"));
-    KM_TRY(check_ws(ws, ws_bytes, fit_layout(dt, B, N, D, K, (int)metric).total));
-    return fit_device(dt, x, B, N, D, K, iters, tol, centroids, assign, objective, iters_done, (char *)ws,
-                      (hipStream_t)stream, (int)metric);
+    if (xk == PTR_DEVICE) {
+        KM_TRY(check_ws(ws, ws_bytes, fit_layout(dt, B, N, D, K, (int)metric).total));
+        return fit_device(dt, x, B, N, D, K, iters, tol, centroids, assign, objective, iters_done, (char *)ws,
+                          (hipStream_t)stream, (int)metric);
+    }
+    KM_TRY(check_ws(ws, ws_bytes, host_layout(dt, B, N, D, K, chunk_points).total));
+    return fit_host(dt, x, B, N, D, K, iters, tol, chunk_points, centroids, assign, objective, iters_done,
+                    (char *)ws, (hipStream_t)stream, (int)metric);
 }
 
 extern "C" km_status_t kmeans_fit(const void *x, km_dtype_t dt, int64_t B, int64_t N, int64_t D, int64_t K,

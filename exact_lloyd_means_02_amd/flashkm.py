@@ -59,8 +59,8 @@ def _load():
     lib.kmeans_fit.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, i32, f32, i64, vp, vp, vp, vp, vp, sz, vp]
     lib.kmeans_normalize_rows.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp]
     lib.kmeans_prepare_centroids_metric.argtypes = [vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64, vp, sz, vp]
-    lib.kmeans_fit_metric.argtypes = [vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64, i32, f32, vp, vp, vp, vp,
-                                      vp, sz, vp]
+    lib.kmeans_fit_metric.argtypes = [vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64, i32, f32, i64, vp, vp, vp,
+                                      vp, vp, sz, vp]
     for n in ("kmeans_plan", "kmeans_row_norms", "kmeans_assign", "kmeans_prepare_centroids",
               "kmeans_assign_prepared", "kmeans_argsort_ids", "kmeans_update", "kmeans_fit", "kmeans_normalize_rows",
               "kmeans_prepare_centroids_metric", "kmeans_fit_metric"):
@@ -308,12 +308,12 @@ def kmeans_fit(x, centroids, iters: int, tol: float = 0.0, chunk_points: int = 0
     return assign, inertia[: done.value], done.value
 
 
-def kmeans_fit_metric(x, centroids, metric, iters: int, tol: float = 0.0, assign=None, want_assign=True,
-                      stream=None):
-    """k-means under `metric` ("l2", "dot" or "cosine") on device-resident x.  `centroids` (device f32
-    [B,K,D]) holds the init and receives the result (unit rows for cosine).  Returns (assign,
-    objective [iters_done, B] numpy float64: inertia for "l2", total similarity otherwise,
-    iters_done)."""
+def kmeans_fit_metric(x, centroids, metric, iters: int, tol: float = 0.0, chunk_points: int = 0, assign=None,
+                      want_assign=True, stream=None):
+    """k-means under `metric` ("l2", "dot" or "cosine").  x: device tensor, or pinned host tensor
+    (streamed path).  `centroids` (device f32 [B,K,D]) holds the init and receives the result (unit
+    rows for cosine).  Returns (assign, objective [iters_done, B] numpy float64: inertia for "l2",
+    total similarity otherwise, iters_done)."""
     torch = _torch()
     import numpy as np
     m = metric_code(metric)
@@ -325,13 +325,16 @@ def kmeans_fit_metric(x, centroids, metric, iters: int, tol: float = 0.0, assign
     if want_assign and assign is None:
         assign = torch.empty((B, N), dtype=torch.int32, device=dev)
     dt = dtype_code(x)
-    op = {KM_METRIC_L2: KM_OP_FIT, KM_METRIC_DOT: KM_OP_FIT_DOT, KM_METRIC_COSINE: KM_OP_FIT_COSINE}[m]
-    ws = workspace(op, dt, B, N, D, K, dev)
+    if x.is_cuda:
+        op = {KM_METRIC_L2: KM_OP_FIT, KM_METRIC_DOT: KM_OP_FIT_DOT, KM_METRIC_COSINE: KM_OP_FIT_COSINE}[m]
+    else:
+        op = KM_OP_FIT_HOST
+    ws = workspace(op, dt, B, N, D, K, dev, chunk_points)
     obj = np.zeros((iters, B), dtype=np.float64)
     done = ctypes.c_int32(0)
-    _check(LIB.kmeans_fit_metric(_ptr(x), dt, m, B, N, D, K, int(iters), float(tol), _ptr(centroids), _ptr(assign),
-                                 obj.ctypes.data_as(ctypes.c_void_p), ctypes.byref(done), _ptr(ws), ws.numel(),
-                                 _stream(centroids, stream)))
+    _check(LIB.kmeans_fit_metric(_ptr(x), dt, m, B, N, D, K, int(iters), float(tol), int(chunk_points),
+                                 _ptr(centroids), _ptr(assign), obj.ctypes.data_as(ctypes.c_void_p),
+                                 ctypes.byref(done), _ptr(ws), ws.numel(), _stream(centroids, stream)))
     return assign, obj[: done.value], done.value
 
 
@@ -370,7 +373,7 @@ def _seeded_init(x, n_clusters: int, seed: int):
 
 def _batch_metric(x, n_clusters, max_iters, tol, init_centroids, seed, metric):
     torch = _torch()
-    _need(x.is_cuda, "the dot-product and cosine metrics need x on the GPU")
+    _need(x.is_cuda or x.is_pinned(), "x must be on the GPU or in pinned host memory")
     if init_centroids is None:
         init_centroids = _seeded_init(x, n_clusters, seed)
     c = init_centroids.to(x.device, dtype=torch.float32).contiguous().clone()
@@ -384,8 +387,8 @@ class FlashKMeans:
     predict / fit_predict and init_centroids).
 
     Input: [N, d] (one problem) or [B, N, d] (B independent problems sharing k), on the GPU, or in
-    host memory.  Pinned host memory selects the streamed path (Euclidean metric); other host
-    tensors are copied to the GPU first.  `dtype` is the compute dtype the points are cast to.
+    host memory.  Pinned host memory selects the streamed path; other host tensors are copied to
+    the GPU first.  `dtype` is the compute dtype the points are cast to.
     After fitting: `centroids` (fp32 [B, k, d], or [k, d] for 2-D input), `labels_` (from the last
     assignment), `obj` (per-iteration inertia, or total similarity for "dot" / "cosine"),
     `iters_done`.  `cluster_centers_` and `inertia_` mirror scikit-learn's names."""
@@ -417,9 +420,7 @@ class FlashKMeans:
         x3 = x if batched else x.unsqueeze(0)
         if x3.dtype != self.dtype:
             x3 = x3.to(self.dtype)
-        if x3.is_cuda:
-            x3 = x3.to(self.device)
-        elif not (x3.is_pinned() and self.metric in ("l2", "euclid")):
+        if x3.is_cuda or not x3.is_pinned():
             x3 = x3.to(self.device)
         return x3.contiguous(), batched
 
@@ -438,10 +439,7 @@ class FlashKMeans:
             init = init_centroids if init_centroids.dim() == 3 else init_centroids.unsqueeze(0)
             _need(tuple(init.shape) == (B, self.k, self.d), "init_centroids must be [B, k, d] or [k, d]")
         c = init.to(self.device, dtype=torch.float32).contiguous().clone()
-        if self.metric in ("l2", "euclid"):
-            a, obj, done = kmeans_fit(x3, c, self.niter, self.tol, self.chunk_points)
-        else:
-            a, obj, done = kmeans_fit_metric(x3, c, self.metric, self.niter, self.tol)
+        a, obj, done = kmeans_fit_metric(x3, c, self.metric, self.niter, self.tol, self.chunk_points)
         self.centroids = c
         self.labels_ = a
         self.obj = obj

@@ -246,9 +246,11 @@ km_status_t kmeans_fit(const void *x, km_dtype_t dt, int64_t B, int64_t N, int64
  *   terms 0 for KM_METRIC_DOT / KM_METRIC_COSINE (the centroids are taken as
  *   given: unit rows are the caller's business here); the result feeds
  *   kmeans_assign_prepared, whose min_dist then holds x_norms_i - 2 x_i.c~_a.
- * kmeans_fit_metric: kmeans_fit for a metric, device-resident x only
- *   (pinned host x with a similarity metric -> KM_ERR_UNSUPPORTED); ws from
- *   kmeans_workspace_bytes(KM_OP_FIT / KM_OP_FIT_DOT / KM_OP_FIT_COSINE).
+ * kmeans_fit_metric: kmeans_fit for a metric, with the same arguments.
+ *   Device-resident x takes ws from kmeans_workspace_bytes(KM_OP_FIT /
+ *   KM_OP_FIT_DOT / KM_OP_FIT_COSINE). Pinned host x selects the streamed
+ *   path, which takes ws from KM_OP_FIT_HOST; cosine then turns each staged
+ *   chunk into unit rows in place.
  *   `objective` (host double [iters * B] or NULL): for KM_METRIC_L2 the
  *   inertia; otherwise the total similarity sum_i x_i.c~_{a_i} (x^ for
  *   cosine) of each iteration's assignment (fp32 terms, fp64 sum).
@@ -259,9 +261,9 @@ km_status_t kmeans_prepare_centroids_metric(const float *centroids, km_dtype_t d
                                             int64_t B, int64_t N, int64_t D, int64_t K, void *c_prep,
                                             size_t c_prep_bytes, void *stream);
 km_status_t kmeans_fit_metric(const void *x, km_dtype_t dt, km_metric_t metric, int64_t B, int64_t N,
-                              int64_t D, int64_t K, int32_t iters, float tol, float *centroids,
-                              int32_t *assign, double *objective, int32_t *iters_done, void *ws,
-                              size_t ws_bytes, void *stream);
+                              int64_t D, int64_t K, int32_t iters, float tol, int64_t chunk_points,
+                              float *centroids, int32_t *assign, double *objective,
+                              int32_t *iters_done, void *ws, size_t ws_bytes, void *stream);
 
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char *kmeans_last_error(void);

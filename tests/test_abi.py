@@ -175,12 +175,12 @@ def test_metric_entry_validation(fk):
     assert "metric" in fk.last_error()
     assert L.kmeans_prepare_centroids_metric(P, 2, 1, 1, 100, 16, 10, P, 16, None) == fk.KM_ERR_WORKSPACE
     assert L.kmeans_prepare_centroids_metric(None, 2, 2, 1, 100, 16, 10, P, 1 << 20, None) == fk.KM_ERR_INVALID
-    # kmeans_fit_metric(x, dt, metric, B, N, D, K, iters, tol, C, assign, obj, done, ws, bytes, stream)
+    # kmeans_fit_metric(x, dt, metric, B, N, D, K, iters, tol, chunk_points, C, assign, obj, done, ws, bytes, stream)
     def fit(**kw):
         a = dict(x=P, dt=2, m=1, B=1, N=10, D=4, K=3, it=5, tol=0.0, C=P, ws=P, wsb=1 << 20)
         a.update(kw)
         return L.kmeans_fit_metric(a["x"], a["dt"], a["m"], a["B"], a["N"], a["D"], a["K"], a["it"], a["tol"],
-                                   a["C"], None, None, None, a["ws"], a["wsb"], None)
+                                   a.get("cp", 0), a["C"], None, None, None, a["ws"], a["wsb"], None)
     assert fit(m=-1) == fk.KM_ERR_INVALID and "metric" in fk.last_error()
     assert fit(it=0) == fk.KM_ERR_INVALID and "iters" in fk.last_error()
     assert fit(tol=-1.0) == fk.KM_ERR_INVALID
@@ -188,6 +188,7 @@ def test_metric_entry_validation(fk):
     assert fit(C=None) == fk.KM_ERR_INVALID
     assert fit(x=ctypes.c_void_p(258), m=2) == fk.KM_ERR_INVALID
     assert fit(ws=None, m=2) == fk.KM_ERR_WORKSPACE
+    assert fit(cp=-1, m=1) == fk.KM_ERR_INVALID and "chunk_points" in fk.last_error()
     # the L2 metric is kmeans_fit: same validation
     assert fit(m=0, it=0) == fk.KM_ERR_INVALID and "iters" in fk.last_error()
 

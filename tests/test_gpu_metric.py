@@ -252,3 +252,26 @@ def test_cosine_zero_rows_and_repeat(fk):
     assert (runs[0][0][0, :50] == 0).all()
     assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1])
     assert np.array_equal(runs[0][2], runs[1][2])
+
+
+@pytest.mark.parametrize("metric", ["cosine", "dot"])
+def test_streamed_metric_matches_device(fk, metric):
+    """Pinned host x (streamed in chunks, cosine: unit rows made per staged chunk) against the
+    device-resident fit: the first assignment is identical (same points, same centroids); the
+    centroids after it differ only by the fp32 order of the per-chunk sums."""
+    w = W.small("headline_bf16", B=2, N=9000, K=48)
+    _say(f"streamed {metric} {w}")
+    x, x64, c0, xt, ct = make_inputs(w)
+    xh = xt.cpu().pin_memory()
+    c_d, c_h = ct.clone(), ct.clone()
+    a_d, o_d, _ = fk.kmeans_fit_metric(xt, c_d, metric, 1)
+    a_h, o_h, _ = fk.kmeans_fit_metric(xh, c_h, metric, 1, chunk_points=4000)
+    assert torch.equal(a_d, a_h)
+    rel = (c_d - c_h).norm(dim=-1) / c_d.norm(dim=-1).clamp_min(1e-30)
+    assert rel.max().item() < 1e-5
+    assert np.abs(o_d - o_h).max() <= 1e-6 * np.abs(o_d).max()
+    # a few more iterations: the objectives stay together
+    c_d, c_h = ct.clone(), ct.clone()
+    _, o_d, _ = fk.kmeans_fit_metric(xt, c_d, metric, 4)
+    _, o_h, _ = fk.kmeans_fit_metric(xh, c_h, metric, 4, chunk_points=4000)
+    assert (np.abs(o_d - o_h) / np.abs(o_d)).max() < 1e-4
