@@ -7,9 +7,10 @@
 //               one column of the [bins][tiles] table of its problem;
 //   2. offsets: where a problem has few tiles (<= SORT_INLINE_TILES) the table is stored
 //               tile-major and every scatter workgroup derives its own offsets from it (sum over
-//               earlier tiles plus an exclusive scan of the digit totals); otherwise one scan
-//               workgroup per problem turns the digit-major table into offsets in (digit-major,
-//               tile-minor) order first;
+//               earlier tiles plus an exclusive scan of the digit totals); otherwise the table is
+//               digit-major, one scan workgroup per (problem, digit) turns its row into the
+//               digit's offsets over the tiles and records the digit's total, and every scatter
+//               workgroup adds the exclusive scan of the totals;
 //   3. scatter: each wave ranks its keys 64 at a time, in index order: lanes holding the same
 //               digit are found with one ballot per digit bit; a lane's rank = earlier peers
 //               in the round + the wave's running count of that digit (LDS).  The tile is
@@ -58,26 +59,26 @@ __global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t *__restric
         for (int i = threadIdx.x; i < bins; i += 256) hb[(size_t)i * ntiles + t] = s_h[i];
 }
 
-// Exclusive scan of one problem's [bins][tiles] table, in place.  1024 threads; each pass
-// covers 1024 x 8 consecutive entries (8 independent loads per thread), scanned with wave
+// Exclusive scan of one row of a problem's digit-major [bins][tiles] table, in place; the row's
+// total goes to totals[problem][digit].  One 256-thread workgroup per (problem, digit); each pass
+// covers 256 x 8 consecutive entries (8 independent loads per thread), scanned with wave
 // shuffles and one LDS step, carried to the next pass.
 constexpr int SCAN_ITEMS = 8;
 
-// When `counts` is given (single pass: the digit is the whole id) it also writes the per-bin
-// totals for bins < K from the scanned table.
-__global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t *__restrict__ hist, int entries, int ntiles,
-                                                         int32_t *__restrict__ counts, int K, int N) {
-    __shared__ int32_t s_wave[16];
+__global__ __launch_bounds__(256) void sort_rowscan_kernel(int32_t *__restrict__ hist, int bins, int ntiles,
+                                                           int32_t *__restrict__ totals) {
+    __shared__ int32_t s_wave[4];
     __shared__ int32_t s_carry;
-    int32_t *hb = hist + (size_t)blockIdx.x * entries;
+    const int row = blockIdx.x;  // problem * bins + digit
+    int32_t *hb = hist + (size_t)row * ntiles;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     if (t == 0) s_carry = 0;
     __syncthreads();
-    for (int base = 0; base < entries; base += 1024 * SCAN_ITEMS) {
+    for (int base = 0; base < ntiles; base += 256 * SCAN_ITEMS) {
         const int lo = base + t * SCAN_ITEMS;
         int32_t v[SCAN_ITEMS];
 #pragma unroll
-        for (int i = 0; i < SCAN_ITEMS; ++i) v[i] = lo + i < entries ? hb[lo + i] : 0;
+        for (int i = 0; i < SCAN_ITEMS; ++i) v[i] = lo + i < ntiles ? hb[lo + i] : 0;
         int32_t sum = 0;
 #pragma unroll
         for (int i = 0; i < SCAN_ITEMS; ++i) sum += v[i];
@@ -95,22 +96,15 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t *__restrict__ h
         int32_t run = s_carry + wbase + inc - sum;
 #pragma unroll
         for (int i = 0; i < SCAN_ITEMS; ++i) {
-            if (lo + i < entries) hb[lo + i] = run;
+            if (lo + i < ntiles) hb[lo + i] = run;
             run += v[i];
         }
         __syncthreads();
-        if (t == 1023) s_carry = run;
+        if (t == 255) s_carry = run;
         __syncthreads();
     }
-    if (counts) {
-        // the table written above by this workgroup is visible after the barrier
-        int32_t *cb = counts + (size_t)blockIdx.x * K;
-        for (int k = t; k < K; k += 1024) {
-            const int32_t start = hb[(size_t)k * ntiles];
-            const int32_t end = (k + 1) * ntiles < entries ? hb[(size_t)(k + 1) * ntiles] : N;
-            cb[k] = end - start;
-        }
-    }
+    if (t == 0) totals[row] = s_carry;
+    (void)bins;
 }
 
 // In-place exclusive scan of s[0, n) (n <= 1024) by a 256-thread workgroup.
@@ -145,13 +139,15 @@ __device__ inline void block_exscan_1024(int32_t *s, int n, int32_t *s_wsum) {
 }
 
 // Stable scatter of one pass.  vals_in == NULL means the values are the point indices.
-// INLINE: `hist` holds the raw [bins][tiles] counts and each workgroup derives its offsets
-// (and, for counts != NULL, the workgroup of tile 0 writes the per-bin totals); otherwise
-// `hist` holds the scanned offsets.
+// INLINE: `hist` holds the raw [tiles][bins] counts and each workgroup derives its offsets;
+// otherwise `hist` holds each digit's offsets over the tiles ([bins][tiles], scanned per row)
+// and `totals` the digit totals, whose exclusive scan each workgroup adds.  For counts != NULL
+// the workgroup of tile 0 writes the per-bin totals.
 template <bool INLINE>
 __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__restrict__ keys_in,
                                                            const int32_t *__restrict__ vals_in,
-                                                           const int32_t *__restrict__ hist, int N, int ntiles,
+                                                           const int32_t *__restrict__ hist,
+                                                           const int32_t *__restrict__ totals, int N, int ntiles,
                                                            int shift, int bits, int32_t *__restrict__ keys_out,
                                                            int32_t *__restrict__ vals_out,
                                                            int32_t *__restrict__ counts, int K) {
@@ -207,7 +203,14 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__rest
             for (int e = 0; e < 4; ++e) s_off[i0 + e] += pre[e];
         }
     } else {
-        for (int i = tid; i < bins; i += 256) s_off[i] = hb[(size_t)i * ntiles + t];
+        const int32_t *tb = totals + (size_t)b * bins;
+        for (int i = tid; i < bins; i += 256) {
+            s_off[i] = tb[i];
+            if (counts && t == 0 && i < K) counts[(size_t)b * K + i] = tb[i];
+        }
+        __syncthreads();
+        block_exscan_1024(s_off, bins, s_wsum);
+        for (int i = tid; i < bins; i += 256) s_off[i] += hb[(size_t)i * ntiles + t];
     }
     __syncthreads();
 
@@ -306,7 +309,7 @@ hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s) {
 
 size_t sort_ws_bytes(int64_t B, int64_t N, int64_t K) {
     const SortCfg c = plan_sort(N, K);
-    size_t bytes = align256((size_t)B * c.bins * c.ntiles * 4);
+    size_t bytes = align256((size_t)B * c.bins * c.ntiles * 4) + align256((size_t)B * c.bins * 4);
     if (c.passes > 1) bytes += 2 * align256((size_t)B * N * 4);
     return bytes;
 }
@@ -318,13 +321,14 @@ hipError_t launch_argsort(const int32_t *keys, int B, int N, int K, int32_t *out
     char *wp = (char *)ws;
     int32_t *hist = (int32_t *)wp;
     wp += align256((size_t)B * c.bins * c.ntiles * 4);
+    int32_t *totals = (int32_t *)wp;
+    wp += align256((size_t)B * c.bins * 4);
     int32_t *tk = nullptr, *tv = nullptr;
     if (c.passes > 1) {
         tk = (int32_t *)wp;
         wp += align256((size_t)B * N * 4);
         tv = (int32_t *)wp;
     }
-    const int entries = c.bins * c.ntiles;
     const int32_t *kin = keys;
     const int32_t *vin = nullptr;
     for (int pass = 0; pass < c.passes; ++pass) {
@@ -339,12 +343,14 @@ hipError_t launch_argsort(const int32_t *keys, int B, int N, int K, int32_t *out
         sort_hist_kernel<<<dim3(B * c.ntiles), dim3(256), c.bins * 4, s>>>(kin, N, c.ntiles, shift, c.bins, hist,
                                                                             inline_offsets ? 1 : 0);
         if (inline_offsets) {
-            sort_scatter_kernel<true><<<dim3(B * c.ntiles), dim3(256), lds, s>>>(kin, vin, hist, N, c.ntiles, shift,
-                                                                                c.bits, ko, vo, cnt_out, K);
+            sort_scatter_kernel<true><<<dim3(B * c.ntiles), dim3(256), lds, s>>>(kin, vin, hist, nullptr, N,
+                                                                                c.ntiles, shift, c.bits, ko, vo,
+                                                                                cnt_out, K);
         } else {
-            sort_scan_kernel<<<dim3(B), dim3(1024), 0, s>>>(hist, entries, c.ntiles, cnt_out, K, N);
-            sort_scatter_kernel<false><<<dim3(B * c.ntiles), dim3(256), lds, s>>>(kin, vin, hist, N, c.ntiles, shift,
-                                                                                 c.bits, ko, vo, nullptr, K);
+            sort_rowscan_kernel<<<dim3(B * c.bins), dim3(256), 0, s>>>(hist, c.bins, c.ntiles, totals);
+            sort_scatter_kernel<false><<<dim3(B * c.ntiles), dim3(256), lds, s>>>(kin, vin, hist, totals, N,
+                                                                                 c.ntiles, shift, c.bits, ko, vo,
+                                                                                 cnt_out, K);
         }
         kin = ko;
         vin = vo;

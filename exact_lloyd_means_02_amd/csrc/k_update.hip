@@ -486,7 +486,19 @@ __global__ __launch_bounds__(256) void upd_combine_kernel(UpdArgs a, int64_t nch
         for (int d = dcol; d < ((D + DC - 1) / DC) * DC; d += DC) {
             float sum = 0.f;
             if (d < D) {
-                for (int j = pg; j < np; j += PG) sum += a.part[((size_t)(chunk + j) * 2 + (j == 0 ? 1 : 0)) * D + d];
+                // pieces pg, pg + PG, ... in order; eight loads in flight before they are added
+                int j = pg;
+                for (; j + 7 * PG < np; j += 8 * PG) {
+                    float pv[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const int jj = j + u * PG;
+                        pv[u] = a.part[((size_t)(chunk + jj) * 2 + (jj == 0 ? 1 : 0)) * D + d];
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) sum += pv[u];
+                }
+                for (; j < np; j += PG) sum += a.part[((size_t)(chunk + j) * 2 + (j == 0 ? 1 : 0)) * D + d];
             }
             s_red[t] = sum;
             __syncthreads();

@@ -86,7 +86,7 @@ SortCfg plan_sort(int64_t N, int64_t K) {
     SortCfg c{};
     const int kbits = std::max(1, log2_floor(std::max<int64_t>(1, K - 1)) + 1);
     c.ntiles = (int)cdiv(N, SORT_TILE);
-    int bmax = log2_floor(std::max<int64_t>(1, SORT_MAX_SCAN / c.ntiles));
+    int bmax = log2_floor(std::max<int64_t>(1, SORT_MAX_TABLE / c.ntiles));
     bmax = std::max(1, std::min(SORT_MAX_BITS, bmax));
     c.passes = (kbits + bmax - 1) / bmax;
     c.bits = (kbits + c.passes - 1) / c.passes;

@@ -24,7 +24,7 @@ constexpr int SPLITD_KB = 4;             // split-D: 32-centroid tiles per regis
 constexpr int SORT_TILE = 4096;          // keys per sort workgroup (4 waves x 16 rounds x 64)
 constexpr int SORT_MAX_BITS = 10;        // <= 1024 bins per counting pass (LDS: 6 x bins x 4 B + 32 KiB tile)
 constexpr int SORT_INLINE_TILES = 64;    // tiles per problem up to which every scatter workgroup reads the table
-constexpr int SORT_MAX_SCAN = 1 << 20;   // bins x tiles entries per problem for one scan workgroup
+constexpr int SORT_MAX_TABLE = 1 << 24;  // bins x tiles entries per problem in one pass's table
 constexpr int UPD_VPL_MAX = 4;           // 16-byte (or scalar) vectors per lane per row in the update
 
 struct AssignCfg {

@@ -134,7 +134,8 @@ def test_argsort_worked_example(fk, golden_dir):
 
 
 SORT_CASES = [(1, 1, 1), (3, 10000, 1000), (2, 4097, 8), (1, 65536, 1024), (2, 1 << 17, 32768),
-              (1, 1 << 20, 4096), (4, 12345, 2048), (1, 5000, 5000), (1, 1 << 20, 1000), (3, 70000, 1024)]
+              (1, 1 << 20, 4096), (4, 12345, 2048), (1, 5000, 5000), (1, 1 << 20, 1000), (3, 70000, 1024),
+              (2, 300000, 700), (1, 1 << 22, 64)]
 
 
 @pytest.mark.parametrize("B,N,K", SORT_CASES)
