@@ -240,11 +240,12 @@ __device__ inline void stage_barrier() {
 // scan; centroid tiles stream through LDS in stages of two tiles, three buffers deep.
 // grid = B * ceil(N / block_n) workgroups of 256 threads.
 //
-// Per tile the wave issues PB x QG MFMAs.  Everything else is kept off their critical path:
-//   * the A fragments of tile t+1 are read from LDS while the MFMAs of tile t run (each
-//     fragment register is refilled right after its last MFMA of tile t);
-//   * the arg-min selects of tile t-1 (other accumulator set) fill the MFMA shadow;
-//   * the centroid norms of tile t+1 are read into the freed accumulator set;
+// Per tile the wave issues PB x QG MFMAs, then folds the tile's scores into its running
+// arg-min; the two waves of a SIMD interleave, so one wave's fold runs beside the other's
+// MFMAs.  Around them:
+//   * the A fragments are read from LDS ahead of use through a 4-group register ring (each
+//     slot refilled right after its last MFMA);
+//   * the centroid norms of tile t+1 are read while the MFMAs of tile t run;
 //   * stage s+2 is copied global->LDS while stage s is consumed; a barrier in the middle of
 //     each stage publishes stage s+1 before the first fragment of it is read.
 // ------------------------------------------------------------------------------------------
@@ -267,7 +268,6 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
     constexpr int PF = STAGE_U4 / 256;  // 1 KiB copy instructions per wave per stage
     constexpr int NCOPY = PF + 1;       // ... plus one for the stage's norms
     static_assert(STAGE_U4 % 256 == 0, "stage must split evenly over 4 waves");
-    static_assert(TPS % 2 == 0, "accumulator sets alternate per tile");
 
     // Three distinct LDS buffers: the compiler can then tell that the reads of one buffer
     // never alias the global->LDS copies into another.
@@ -314,13 +314,13 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
 
     // A fragments: group q of the tile being multiplied lives in slot q % FR.  A slot is
     // refilled right after group q's MFMAs with group q + FR: of the same tile while there is
-    // one, else of the next tile.  FR = QG (a whole tile ahead) unless that would cost more
-    // than 32 registers (D*s >= 512 bytes), where FR = 8 keeps the kernel at two waves per SIMD.
-    constexpr int FR = QG > 8 ? 8 : QG;
+    // one, else of the next tile.  A ring of 4 groups (16 registers) is as fast as a whole tile
+    // of them and leaves the registers for the other wave of the SIMD.
+    constexpr int FR = QG > 4 ? 4 : QG;
     static_assert(QG % FR == 0, "fragment ring");
     u32x4 f[FR];
     f32x16 cn;    // half-norms of the tile being multiplied (this lane's 16 rows)
-    f32x16 accA[PB], accB[PB];
+    f32x16 acc[PB];
     auto load_norms = [&](const float *sn, int tt) {
         const float *nrm = sn + tt * 32 + 4 * h;
         const f32x4 c0 = *(const f32x4 *)(nrm + 0), c1 = *(const f32x4 *)(nrm + 8);
@@ -328,30 +328,30 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
         cn = f32x16{c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3],
                     c2[0], c2[1], c2[2], c2[3], c3[0], c3[1], c3[2], c3[3]};
     };
-    // One tile: multiply f into accC (starting from the norms in cn) while refilling f and cn
-    // with the next tile's fragments and norms, each right after its last use, so the LDS
-    // reads have a whole tile to land; fold accF (the previous tile) in the MFMA shadow.  After
-    // the last tile the refills read a stale (in-bounds) buffer and are never used: no
-    // branches here.
-    auto step = [&](f32x16 (&accC)[PB], f32x16 (&accF)[PB], int tileF, const u32x4 *__restrict__ csc, int ctt,
-                    const u32x4 *__restrict__ nsc, const float *__restrict__ nsn, int ntt) {
+    // One tile: multiply f into acc (starting from the norms in cn) while refilling f and cn
+    // with the following fragments and norms, each right after its last use, then fold the
+    // tile's scores.  One accumulator set: the fold of one wave overlaps the MFMAs of the other
+    // wave of the SIMD (two accumulator sets alternating inside a wave measured 2-3% slower:
+    // the extra 32 registers cost more than the overlap gains).  After the last tile the
+    // refills read a stale (in-bounds) buffer and are never used: no branches here.
+    auto step = [&](int tile, const u32x4 *__restrict__ csc, int ctt, const u32x4 *__restrict__ nsc,
+                    const float *__restrict__ nsn, int ntt) {
 #pragma unroll
         for (int q = 0; q < QG; ++q) {
 #pragma unroll
-            for (int p = 0; p < PB; ++p) accC[p] = mfma_group<DT>(f[q % FR], xr[p][q], q == 0 ? cn : accC[p]);
+            for (int p = 0; p < PB; ++p) acc[p] = mfma_group<DT>(f[q % FR], xr[p][q], q == 0 ? cn : acc[p]);
             if (q + FR < QG) f[q % FR] = csc[ctt * TILE_U4 + (q + FR) * 64 + lane];
             else f[q % FR] = nsc[ntt * TILE_U4 + (q + FR - QG) * 64 + lane];
             if (q == 0) load_norms(nsn, ntt);
         }
 #pragma unroll
-        for (int p = 0; p < PB; ++p) argmin_fold(st[p], accF[p], tileF);
+        for (int p = 0; p < PB; ++p) argmin_fold(st[p], acc[p], tile);
     };
     // Stage s lives in X; stage s+1 in Y (copied earlier); stage s+2 is copied into Z.  With a
     // whole tile of fragments in flight (FR == QG) the last step of a stage reads only Y, so Z
     // (stage s-1's buffer) is free from the start of stage s and the copy goes first.  With a
     // ring (FR < QG) the last step of stage s-1 still read Z after its mid-stage barrier, so the
     // copy waits for this stage's mid-stage barrier, which every wave passes only after it.
-    // Tile t = TPS*s + i is multiplied into accA for even i, accB for odd i.
     // The buffer pointers are __restrict__: the alias scopes this gives the LDS reads and the
     // global->LDS copies let the compiler wait for a copy only where its buffer is read, not
     // before every LDS read after it (which would stall each stage on the newest copy).
@@ -362,11 +362,7 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
         if (early && copy2) stage_copy(s + 2, zc, zn);
         const int t0 = TPS * s;
 #pragma unroll
-        for (int i = 0; i + 2 < TPS; i += 2) {
-            step(accA, accB, t0 + i - 1, xc, i, xc, xn_, i + 1);
-            step(accB, accA, t0 + i, xc, i + 1, xc, xn_, i + 2);
-        }
-        step(accA, accB, t0 + TPS - 3, xc, TPS - 2, xc, xn_, TPS - 1);  // prefetch the stage's last tile
+        for (int i = 0; i + 1 < TPS; ++i) step(t0 + i, xc, i, xc, xn_, i + 1);  // refills from this stage
         const bool more = s + 1 < nst;
         if (more) {
             // stage s+1 landed (this wave), then published
@@ -374,7 +370,7 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
             else stage_barrier<0>();
         }
         if (!early && copy2) stage_copy(s + 2, zc, zn);
-        step(accB, accA, t0 + TPS - 2, xc, TPS - 1, yc, yn, 0);  // last tile; prefetch the next stage's first
+        step(t0 + TPS - 1, xc, TPS - 1, yc, yn, 0);  // last tile; refills from the next stage
     };
 
     // prologue: stages 0 and 1 in flight, stage 0 published, tile 0 loaded
@@ -388,18 +384,12 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
 #pragma unroll
     for (int q = 0; q < FR; ++q) f[q] = s_c0[q * 64 + lane];
     load_norms(s_n0, 0);
-#pragma unroll
-    for (int p = 0; p < PB; ++p)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) accB[p][r] = __builtin_inff();  // "tile -1": a no-op fold
 
     for (int s0 = 0; s0 < nst; s0 += 3) {
         run_stage(s0, s_c0, s_n0, s_c1, s_n1, s_c2, s_n2);
         if (s0 + 1 < nst) run_stage(s0 + 1, s_c1, s_n1, s_c2, s_n2, s_c0, s_n0);
         if (s0 + 2 < nst) run_stage(s0 + 2, s_c2, s_n2, s_c0, s_n0, s_c1, s_n1);
     }
-#pragma unroll
-    for (int p = 0; p < PB; ++p) argmin_fold(st[p], accB[p], KT - 1);
 
     double dsum = 0.0;
 #pragma unroll

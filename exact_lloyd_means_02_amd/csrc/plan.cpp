@@ -64,7 +64,10 @@ AssignCfg plan_assign(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
         c.bd = 0;
         c.block_n = ASSIGN_WAVES * c.pb * 32;
         c.lds = SMALL_D_STAGES * (c.tps * 32 * dp * s + c.tps * 32 * 4) + ASSIGN_WAVES * 8;
-        c.vgpr = c.pb * (dp * s / 8 + 48) + 32 + 16 + 32;
+        // per point block: x (dp*s/8), accumulators (16), best tile copy (16); then the fragment
+        // ring (at most 4 groups of 4), the norms (16) and addressing / fold temporaries (~48)
+        const int qg = dp * s / 32;
+        c.vgpr = c.pb * (dp * s / 8 + 32) + (qg < 4 ? qg : 4) * 4 + 16 + 48;
     } else {
         const int bd = splitd_bd(dt);
         c.path = 1;
