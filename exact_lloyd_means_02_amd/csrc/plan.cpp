@@ -67,7 +67,7 @@ AssignCfg plan_assign(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
         // per point block: x (dp*s/8), accumulators (16), best tile copy (16); then the fragment
         // ring (at most 4 groups of 4), the norms (16) and addressing / fold temporaries (~48)
         const int qg = dp * s / 32;
-        c.vgpr = c.pb * (dp * s / 8 + 32) + (qg < 4 ? qg : 4) * 4 + 16 + 48;
+        c.vgpr = c.pb * (dp * s / 8 + 32) + (qg > 4 ? 4 : (qg == 4 ? 2 : qg)) * 4 + 16 + 48;
     } else {
         const int bd = splitd_bd(dt);
         c.path = 1;
