@@ -263,7 +263,7 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
     constexpr int PB = small_d_pb(DT, DP);
     constexpr int TILE_U4 = QG * 64;
     constexpr int TPS = small_d_tps(DT, DP);  // tiles per stage: at least 4 KiB, one per wave-copy
-    static_assert(TPS == (QG >= 2 ? 2 : 4), "stage size");
+    static_assert(TPS == (QG >= 16 ? 1 : (QG >= 2 ? 2 : 4)), "stage size");
     constexpr int STAGE_U4 = TPS * TILE_U4;
     constexpr int PF = STAGE_U4 / 256;  // 1 KiB copy instructions per wave per stage
     constexpr int NCOPY = PF + 1;       // ... plus one for the stage's norms

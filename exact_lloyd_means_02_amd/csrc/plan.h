@@ -70,8 +70,12 @@ UpdCfg plan_update(int dt, int64_t B, int64_t N, int64_t D);
 constexpr int small_d_pb(int dt, int dp) { return dt == 0 ? (dp <= 32 ? 2 : 1) : (dp <= 128 ? 2 : 1); }
 // Tiles per LDS stage: 2 when a tile's 32 centroid rows span at least two 16-byte groups
 // per lane half (D*s >= 64 bytes), else 4, so one stage is at least 4 KiB (one 16-byte copy
-// per lane of every wave).  Three stages rotate in LDS.
-constexpr int small_d_tps(int dt, int dp) { return dp * (dt == 0 ? 4 : 2) >= 64 ? 2 : 4; }
+// per lane of every wave); 1 for rows of 512 bytes or more (fp32 D = 128, 2-byte D = 256),
+// where one tile is 16 KiB and three such stages let three workgroups share a CU's LDS.
+// Three stages rotate in LDS.
+constexpr int small_d_tps(int dt, int dp) {
+    return dp * (dt == 0 ? 4 : 2) >= 512 ? 1 : (dp * (dt == 0 ? 4 : 2) >= 64 ? 2 : 4);
+}
 constexpr int SMALL_D_STAGES = 3;
 constexpr int splitd_bd(int dt) { return dt == 0 ? 32 : 64; }
 
