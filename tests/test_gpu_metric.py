@@ -275,3 +275,38 @@ def test_streamed_metric_matches_device(fk, metric):
     _, o_d, _ = fk.kmeans_fit_metric(xt, c_d, metric, 4)
     _, o_h, _ = fk.kmeans_fit_metric(xh, c_h, metric, 4, chunk_points=4000)
     assert (np.abs(o_d - o_h) / np.abs(o_d)).max() < 1e-4
+
+
+def test_metric_degenerate_k(fk):
+    """K = 1: every label 0; the centroid is the mean (dot) or the mean direction of the unit rows
+    (cosine).  Cosine with K = N and the points as centroids: each point picks itself."""
+    w = W.small("headline_bf16", B=2, N=2000, K=1)
+    x, x64, c0, xt, ct = make_inputs(w)
+    for metric in ("dot", "cosine"):
+        c = ct.clone()
+        a, obj, _ = fk.kmeans_fit_metric(xt, c, metric, 1)
+        assert (a == 0).all()
+        cg = c.cpu().numpy().astype(np.float64)
+        xa = x64 if metric == "dot" else _f64(fk.kmeans_normalize_rows(xt))
+        for b in range(w.B):
+            want = xa[b].mean(axis=0) if metric == "dot" else xa[b].sum(axis=0) / np.linalg.norm(xa[b].sum(axis=0))
+            assert np.linalg.norm(cg[b, 0] - want) / np.linalg.norm(want) < 1e-3
+    w = W.small("headline_bf16", B=1, N=512, K=512)
+    x, x64, c0, xt, ct = make_inputs(w)
+    c = xt.float().contiguous().clone()                     # the points themselves as centroids
+    a, _, _ = fk.kmeans_fit_metric(xt, c, "cosine", 1)
+    assert torch.equal(a[0].cpu(), torch.arange(w.N, dtype=torch.int32))
+
+
+def test_metric_tol_stop(fk):
+    """The stopping rule is the same as Lloyd's: stop after iteration t when max_b shift_t < tol."""
+    w = W.small("headline_bf16", B=2, N=4000, K=64)
+    x, x64, c0, xt, ct = make_inputs(w)
+    for metric in ("dot", "cosine"):
+        c = ct.clone()
+        _, obj, done = fk.kmeans_fit_metric(xt, c, metric, 5, tol=1e30)
+        assert done == 1 and obj.shape == (1, w.B)
+        # after the first iteration the centroids have moved off the sampled points: no stop
+        c = ct.clone()
+        _, obj, done = fk.kmeans_fit_metric(xt, c, metric, 2, tol=1e-30)
+        assert done == 2
