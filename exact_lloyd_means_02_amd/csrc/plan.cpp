@@ -6,13 +6,13 @@
 // Assign, small-D path (x tile kept in VGPRs for the whole centroid scan):
 //   * D is padded to DP in {16,...,512} (2-byte types) or {8,...,256} (fp32): the MFMA k-step
 //     is 16 (bf16/fp16 32x32x16) or 2 (fp32 32x32x2), and each lane holds half of every row.
-//   * VGPRs per lane ~= PB * (x: DP*s/8 + two accumulator sets 32 + best 16) + prefetch 32
-//     + c-norm 16 + 32.  PB (32-point blocks per wave) is the largest of {2,1} keeping this
-//     <= 256, so two waves share a SIMD.  Within a wave the MFMAs of tile t+1 are interleaved
-//     with the arg-min selects of tile t (two accumulator sets).
-//   * Centroid stages of 2 (or 4, for D*s < 64 B) tiles rotate through three LDS buffers,
-//     filled by direct global->LDS copies two stages ahead of use: ~49 KiB per workgroup at
-//     D=128 bf16, so three workgroups (12 waves) fit a CU's 160 KiB.
+//   * VGPRs per lane ~= PB * (x: DP*s/8 + accumulators 16 + best 16) + fragment ring (<= 16)
+//     + c-norm 16 + ~48.  PB (32-point blocks per wave) is the largest of {2,1} keeping this
+//     <= 256, so at least two waves share a SIMD; the fold of one wave runs beside the MFMAs
+//     of the other.
+//   * Centroid stages of 2 tiles (4 for D*s < 64 B, 1 for D*s >= 512 B) rotate through three
+//     LDS buffers, filled by direct global->LDS copies two stages ahead of use: ~49 KiB per
+//     workgroup, so three workgroups (12 waves) fit a CU's 160 KiB.
 //   * Every workgroup re-reads all K centroids from L2: the arithmetic intensity of that
 //     stream is 2*block_n*D FLOP per D*s bytes = block_n FLOP/B (bf16), >= 128 for
 //     block_n >= 128, above what L2 must feed MFMA (~2.5 PF / ~40 TB/s ~= 64 FLOP/B).
@@ -23,7 +23,7 @@
 //     wave, D streamed through LDS in chunks of 64 (2-byte) / 32 (fp32) elements so one stage
 //     of x chunk + centroid chunk is 32 KiB, double buffered.
 // Arg-sort: counting passes over digits of the cluster id; one pass when the per-problem
-//   table (bins x tiles of 4096 keys) stays <= 2^20 entries and bins <= 1024 (LDS of a scatter
+//   table (bins x tiles of 4096 keys) stays <= 2^24 entries and bins <= 1024 (LDS of a scatter
 //   workgroup: 6 x bins x 4 B of counters and offsets plus the 32 KiB staged tile); otherwise
 //   balanced multi-pass LSD digits.
 // Update: rows are gathered with 16-byte vector loads when D allows; a row is covered by a
