@@ -436,6 +436,7 @@ km_status_t kmeans_update(const void *x, km_dtype_t dt, const int32_t *sorted_id
     KM_TRY(check_ptr(sorted_idx, "sorted_idx"));
     KM_TRY(check_ptr(counts, "counts"));
     KM_TRY(check_ptr(centroids, "centroids"));
+    if (((uintptr_t)centroids & 15) != 0) return fail(KM_ERR_INVALID, "centroids must be 16-byte aligned");
     if (((uintptr_t)x & 15) != 0) return fail(KM_ERR_INVALID, "x must be 16-byte aligned");
     KM_TRY(check_ws(ws, ws_bytes, update_ws(dt, B, N, D, K)));
     KM_TRY(check_device_arch());
@@ -704,6 +705,7 @@ extern "C" km_status_t kmeans_fit_metric(const void *x, km_dtype_t dt, km_metric
     if (iters < 1) return fail(KM_ERR_INVALID, "iters must be >= 1");
     if (!(tol >= 0.f)) return fail(KM_ERR_INVALID, "tol must be >= 0");
     if (chunk_points < 0) return fail(KM_ERR_INVALID, "chunk_points must be >= 0");
+    if (((uintptr_t)centroids & 15) != 0) return fail(KM_ERR_INVALID, "centroids must be 16-byte aligned");
     if (((uintptr_t)x & 15) != 0) return fail(KM_ERR_INVALID, "x must be 16-byte aligned");
     if (!ws) return fail(KM_ERR_WORKSPACE, "workspace is NULL");
     KM_TRY(check_device_arch());
@@ -732,6 +734,7 @@ extern "C" km_status_t kmeans_fit(const void *x, km_dtype_t dt, int64_t B, int64
     if (iters < 1) return fail(KM_ERR_INVALID, "iters must be >= 1");
     if (!(tol >= 0.f)) return fail(KM_ERR_INVALID, "tol must be >= 0");
     if (chunk_points < 0) return fail(KM_ERR_INVALID, "chunk_points must be >= 0");
+    if (((uintptr_t)centroids & 15) != 0) return fail(KM_ERR_INVALID, "centroids must be 16-byte aligned");
     if (((uintptr_t)x & 15) != 0) return fail(KM_ERR_INVALID, "x must be 16-byte aligned");
     if (!ws) return fail(KM_ERR_WORKSPACE, "workspace is NULL");
     KM_TRY(check_device_arch());

@@ -145,7 +145,26 @@ __device__ inline float finish_cluster(const UpdArgs &a, int b, int k, int c0, i
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const int e0 = c0 + (r + i * a.lanes) * V;
-        if (a.mode == 0) {
+        if (a.mode == 0 && V > 1) {
+            // whole 16-byte vectors (D is a multiple of V here): the new row goes out with
+            // 16-byte stores
+            if (e0 < a.D) {
+                float nw[V];
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    nw[e] = s[i][e] / (float)n;
+                    if (SHIFT) {
+                        const float df = nw[e] - cold[i][e];
+                        d2 += df * df;
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < V / 4; ++q)
+                    *(float4 *)(a.C + rowo + e0 + 4 * q) =
+                        make_float4(nw[4 * q], nw[4 * q + 1], nw[4 * q + 2], nw[4 * q + 3]);
+                if (a.cprep) cn2 += prep_store_group<DT>(a, b, k, e0, nw);
+            }
+        } else if (a.mode == 0) {
             float nw[V];
 #pragma unroll
             for (int e = 0; e < V; ++e) {
@@ -160,13 +179,7 @@ __device__ inline float finish_cluster(const UpdArgs &a, int b, int k, int c0, i
                     }
                 }
             }
-            if (a.cprep) {
-                if constexpr (V > 1) {
-                    if (e0 < a.D) cn2 += prep_store_group<DT>(a, b, k, e0, nw);
-                } else {
-                    if (e0 < a.D) cn2 += prep_store_elem(a, b, k, e0, nw[0]);
-                }
-            }
+            if (a.cprep && e0 < a.D) cn2 += prep_store_elem(a, b, k, e0, nw[0]);  // V == 1 here
         } else {
 #pragma unroll
             for (int e = 0; e < V; ++e) {
@@ -333,6 +346,8 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
     constexpr int U = upd_unroll<VPL>();
 
     while (!done) {
+        // m == 0 is a normal case: a segment whose length is a multiple of 64 ends at a window
+        // boundary, and the next view starts on the next segment's id
         const int m = run_len(p, sid, kraw, plim);
         for (int base = 0; base < m; base += G * U) {
             if constexpr (V == 1) {

@@ -19,7 +19,8 @@
  *     torch.empty(..., pin_memory=True).
  *   - B independent problems share K.  Shapes: x [B, N, D]; centroids
  *     [B, K, D] float32; assign / sorted arrays [B, N] int32; counts [B, K]
- *     int32.
+ *     int32.  x, and the centroids that an update or a fit writes, are
+ *     16-byte aligned.
  *   - The caller owns every buffer.  The library allocates no device memory:
  *     temporary storage comes from the caller's workspace `ws` of `ws_bytes`
  *     bytes, sized by kmeans_workspace_bytes() and 256-byte aligned.

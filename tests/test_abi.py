@@ -221,3 +221,14 @@ def test_wrapper_validation_without_gpu(fk):
         fk.FlashKMeans(d=8, k=0, device="cuda:0")
     with pytest.raises(ValueError, match="dtype"):
         fk.FlashKMeans(d=8, k=5, dtype=torch.float64, device="cuda:0")
+
+
+def test_centroid_alignment_validation(fk):
+    L = fk.LIB
+    C = ctypes.c_void_p(256 + 4)
+    assert L.kmeans_update(P, 2, P, P, P, 1, 10, 8, 3, C, None, P, 1 << 20, None) == fk.KM_ERR_INVALID
+    assert "centroids must be 16-byte aligned" in fk.last_error()
+    assert L.kmeans_fit(P, 2, 1, 10, 8, 3, 2, 0.0, 0, C, None, None, None, P, 1 << 20, None) == fk.KM_ERR_INVALID
+    assert "centroids" in fk.last_error()
+    assert L.kmeans_fit_metric(P, 2, 2, 1, 10, 8, 3, 2, 0.0, 0, C, None, None, None, P, 1 << 20,
+                               None) == fk.KM_ERR_INVALID

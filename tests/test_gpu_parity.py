@@ -190,6 +190,26 @@ def test_update_keeps_empty_clusters(fk):
     check_update(x64, a, c0, cnew.cpu().numpy(), w.dtype)
 
 
+@pytest.mark.parametrize("N", [1 << 14, 1 << 17, 1 << 20])
+def test_update_segments_on_window_edges(fk, N):
+    """Segment lengths that are multiples of the 64-position id window (and of the chunk length),
+    so segment ends fall exactly on window and chunk edges; plus lengths one off those."""
+    K = 64
+    w = W.small("headline_bf16", B=1, N=N, K=K)
+    x, x64, c0, xt, ct = make_inputs(w)
+    sizes = [64, 128, 192, 256, 512, 63, 65, 127, 129, 1, 2]
+    lens = [sizes[k % len(sizes)] for k in range(K - 1)]
+    lens.append(N - sum(lens))                                  # the rest into the last cluster
+    assert lens[-1] > 0
+    a = np.repeat(np.arange(K, dtype=np.int32), lens)
+    a = np.random.default_rng(N).permutation(a)[None, :].astype(np.int32)
+    at = torch.from_numpy(a).to(device())
+    s, i, c = fk.kmeans_argsort_ids(at, K)
+    cnew = ct.clone()
+    fk.kmeans_update(xt, s, i, c, cnew)
+    check_update(x64, a, c0, cnew.cpu().numpy(), w.dtype)
+
+
 def test_update_is_deterministic(fk):
     w = W.small("skew_bf16_k64", N=300000, K=64)
     x, x64, c0, xt, ct = make_inputs(w)
