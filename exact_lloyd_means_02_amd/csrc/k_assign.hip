@@ -15,8 +15,9 @@
 //     exact), so acc = ||c~||^2/2 - x.c~ = (||c~||^2 - 2 x.c~)/2 with no add per score and
 //     no risk of overflowing -2c~ in fp16.  Halving commutes with rounding, so comparisons
 //     are those of the full scores.
-//   * Per 32-centroid tile and lane: one min over the 16 scores, one compare with the
-//     running min, and (selects) a copy of the tile's 16 scores when it improves.  The slot
+//   * Per 32-centroid tile and lane: one min over the 16 scores (eight 3-input minima), one
+//     compare with the running min, and a copy of the tile's 16 scores when it improves
+//     (eight 64-bit moves under the mask of improving lanes).  The slot
 //     inside the winning tile is found once at the end by equality with the running min.
 //     Result: the exact arg-min of the fp32 scores with ties to the lowest index (strict
 //     '<' over tiles in increasing order, lowest slot, lexicographic lane merge).
@@ -163,16 +164,41 @@ __device__ inline void argmin_init(ArgminState &s) {
 
 // Fold one tile's 16 scores (this lane's rows of the tile) into the running state.
 __device__ inline void argmin_fold(ArgminState &s, const f32x16 &acc, int tile) {
-    float m01 = fminf(acc[0], acc[1]), m23 = fminf(acc[2], acc[3]);
-    float m45 = fminf(acc[4], acc[5]), m67 = fminf(acc[6], acc[7]);
-    float m89 = fminf(acc[8], acc[9]), mab = fminf(acc[10], acc[11]);
-    float mcd = fminf(acc[12], acc[13]), mef = fminf(acc[14], acc[15]);
-    float m = fminf(fminf(fminf(m01, m23), fminf(m45, m67)), fminf(fminf(m89, mab), fminf(mcd, mef)));
+    // eight three-input minima: five over triples, two over their results and the last
+    // score, one over those two
+    const float t0 = fminf(fminf(acc[0], acc[1]), acc[2]), t1 = fminf(fminf(acc[3], acc[4]), acc[5]);
+    const float t2 = fminf(fminf(acc[6], acc[7]), acc[8]), t3 = fminf(fminf(acc[9], acc[10]), acc[11]);
+    const float t4 = fminf(fminf(acc[12], acc[13]), acc[14]);
+    const float u0 = fminf(fminf(t0, t1), t2), u1 = fminf(fminf(t3, t4), acc[15]);
+    const float m = fminf(u0, u1);
     const bool imp = m < s.run_min;
     s.run_min = imp ? m : s.run_min;
     s.run_tile = imp ? tile : s.run_tile;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s.best[r] = imp ? acc[r] : s.best[r];
+    // copy the tile's scores where the lane improved: eight 64-bit moves under the lane mask
+    // (instead of sixteen selects).  Every accumulator register was already read by the
+    // minima above, so the MFMA results are complete here.
+    typedef unsigned long long u64x8 __attribute__((ext_vector_type(8)));
+    const unsigned long long mask = __builtin_amdgcn_ballot_w64(imp);
+    u64x8 bb = __builtin_bit_cast(u64x8, s.best);
+    const u64x8 aa = __builtin_bit_cast(u64x8, acc);
+    unsigned long long b0 = bb[0], b1 = bb[1], b2 = bb[2], b3 = bb[3], b4 = bb[4], b5 = bb[5], b6 = bb[6], b7 = bb[7];
+    unsigned long long sv;
+    asm volatile(
+        "s_and_saveexec_b64 %0, %17\n\t"
+        "v_mov_b64 %1, %9\n\t"
+        "v_mov_b64 %2, %10\n\t"
+        "v_mov_b64 %3, %11\n\t"
+        "v_mov_b64 %4, %12\n\t"
+        "v_mov_b64 %5, %13\n\t"
+        "v_mov_b64 %6, %14\n\t"
+        "v_mov_b64 %7, %15\n\t"
+        "v_mov_b64 %8, %16\n\t"
+        "s_mov_b64 exec, %0"
+        : "=&s"(sv), "+v"(b0), "+v"(b1), "+v"(b2), "+v"(b3), "+v"(b4), "+v"(b5), "+v"(b6), "+v"(b7)
+        : "v"(aa[0]), "v"(aa[1]), "v"(aa[2]), "v"(aa[3]), "v"(aa[4]), "v"(aa[5]), "v"(aa[6]), "v"(aa[7]), "s"(mask)
+        : "scc");
+    bb = u64x8{b0, b1, b2, b3, b4, b5, b6, b7};
+    s.best = __builtin_bit_cast(f32x16, bb);
 }
 
 // Resolve the winning centroid of this lane, merge with the partner lane (lane ^ 32, same
@@ -241,22 +267,19 @@ __device__ inline void stage_barrier() {
 // grid = B * ceil(N / block_n) workgroups of 256 threads.
 //
 // Per tile the wave issues PB x QG MFMAs, then folds the tile's scores into its running
-// arg-min; the two waves of a SIMD interleave, so one wave's fold runs beside the other's
-// MFMAs.  Around them:
-//   * the A fragments are read from LDS ahead of use through a 4-group register ring (each
+// arg-min; at least three waves share a SIMD (at most 168 registers), so one wave's fold runs
+// beside the others' MFMAs.  Around them:
+//   * the A fragments are read from LDS ahead of use through a 2-group register ring (each
 //     slot refilled right after its last MFMA);
-//   * the centroid norms of tile t+1 are read while the MFMAs of tile t run;
+//   * the tile's centroid norms are read into an accumulator set just before its MFMAs;
 //   * stage s+2 is copied global->LDS while stage s is consumed; a barrier in the middle of
 //     each stage publishes stage s+1 before the first fragment of it is read.
 // ------------------------------------------------------------------------------------------
 template <int DT, int DP>
-__global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restrict__ x,
-                                                             const u32x4 *__restrict__ cprep,
-                                                             const float *__restrict__ cnh,
-                                                             const float *__restrict__ xnorm,
-                                                             int32_t *__restrict__ out_a, float *__restrict__ out_d,
-                                                             double *__restrict__ wg_inertia,
-                                                             int N, int D, int KT, int wgs_per_b) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void assign_small_d_kernel(
+    const void *__restrict__ x, const u32x4 *__restrict__ cprep, const float *__restrict__ cnh,
+    const float *__restrict__ xnorm, int32_t *__restrict__ out_a, float *__restrict__ out_d,
+    double *__restrict__ wg_inertia, int N, int D, int KT, int wgs_per_b) {
     constexpr int S = DT == DT_F32 ? 4 : 2;
     constexpr int VW = 16 / S;
     constexpr int QG = DP / (2 * VW);
@@ -277,7 +300,10 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
     const int b = wg / wgs_per_b;
     const int tn = wg - b * wgs_per_b;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // the wave index is uniform: held in a scalar register, the copy addresses derived from it
+    // (global source bases and LDS destinations) stay scalar too
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 31, h = lane >> 5;
     const int pbase = tn * (ASSIGN_WAVES * PB * 32) + w * PB * 32;
 
@@ -314,40 +340,43 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
 
     // A fragments: group q of the tile being multiplied lives in slot q % FR.  A slot is
     // refilled right after group q's MFMAs with group q + FR: of the same tile while there is
-    // one, else of the next tile.  A ring of 4 groups (16 registers) is as fast as a whole tile
-    // of them and leaves the registers for the other wave of the SIMD.  For 4-group tiles
-    // (2-byte D = 64, fp32 D = 32) a ring of 2 brings the kernel to 3 waves per SIMD (13%
-    // faster at K = 1024, 3% at K = 32768).
-    constexpr int FR = QG > 4 ? 4 : (QG == 4 ? 2 : QG);
+    // one, else of the next tile.  A ring of 2 groups (8 registers) leaves room for three waves
+    // per SIMD at 2-byte D = 128 (168 registers): 3.7% faster there than a ring of 4 at two
+    // waves per SIMD, and 13% faster at 2-byte D = 64 than a ring of 4.
+    constexpr int FR = QG >= 4 ? 2 : QG;
     static_assert(QG % FR == 0, "fragment ring");
     u32x4 f[FR];
-    f32x16 cn;    // half-norms of the tile being multiplied (this lane's 16 rows)
     f32x16 acc[PB];
+    // The tile's half-norms (this lane's 16 rows) go into the last accumulator set, which the
+    // first MFMA of every point block takes as its C operand: no registers of their own.
     auto load_norms = [&](const float *sn, int tt) {
         const float *nrm = sn + tt * 32 + 4 * h;
         const f32x4 c0 = *(const f32x4 *)(nrm + 0), c1 = *(const f32x4 *)(nrm + 8);
         const f32x4 c2 = *(const f32x4 *)(nrm + 16), c3 = *(const f32x4 *)(nrm + 24);
-        cn = f32x16{c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3],
-                    c2[0], c2[1], c2[2], c2[3], c3[0], c3[1], c3[2], c3[3]};
+        acc[PB - 1] = f32x16{c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3],
+                             c2[0], c2[1], c2[2], c2[3], c3[0], c3[1], c3[2], c3[3]};
     };
-    // One tile: multiply f into acc (starting from the norms in cn) while refilling f and cn
-    // with the following fragments and norms, each right after its last use, then fold the
-    // tile's scores.  One accumulator set: the fold of one wave overlaps the MFMAs of the other
-    // wave of the SIMD (two accumulator sets alternating inside a wave measured 2-3% slower:
-    // the extra 32 registers cost more than the overlap gains).  After the last tile the
-    // refills read a stale (in-bounds) buffer and are never used: no branches here.
-    auto step = [&](int tile, const u32x4 *__restrict__ csc, int ctt, const u32x4 *__restrict__ nsc,
-                    const float *__restrict__ nsn, int ntt) {
+    // One tile (its norms already in acc[PB - 1]): multiply f into acc while refilling f with
+    // the following fragments, each right after its last use, then fold the tile's scores.
+    // One accumulator set: the fold of one wave overlaps the MFMAs of the other waves of the
+    // SIMD (two accumulator sets alternating inside a wave measured 2-3% slower: the extra 32
+    // registers cost more than the overlap gains).  After the last tile the refills read a
+    // stale (in-bounds) buffer and are never used: no branches here.
+    auto step = [&](int tile, const u32x4 *__restrict__ csc, int ctt, const u32x4 *__restrict__ nsc, int ntt) {
 #pragma unroll
         for (int q = 0; q < QG; ++q) {
 #pragma unroll
-            for (int p = 0; p < PB; ++p) acc[p] = mfma_group<DT>(f[q % FR], xr[p][q], q == 0 ? cn : acc[p]);
+            for (int p = 0; p < PB; ++p) acc[p] = mfma_group<DT>(f[q % FR], xr[p][q], q == 0 ? acc[PB - 1] : acc[p]);
             if (q + FR < QG) f[q % FR] = csc[ctt * TILE_U4 + (q + FR) * 64 + lane];
             else f[q % FR] = nsc[ntt * TILE_U4 + (q + FR - QG) * 64 + lane];
-            if (q == 0) load_norms(nsn, ntt);
         }
 #pragma unroll
-        for (int p = 0; p < PB; ++p) argmin_fold(st[p], acc[p], tile);
+        for (int p = 0; p < PB; ++p) {
+            argmin_fold(st[p], acc[p], tile);
+            // the fold completes here: left free to sink into the next tile it would keep a
+            // second accumulator set live
+            asm volatile("" : "+v"(st[p].best), "+v"(st[p].run_min), "+v"(st[p].run_tile));
+        }
     };
     // Stage s lives in X; stage s+1 in Y (copied earlier); stage s+2 is copied into Z.  With a
     // whole tile of fragments in flight (FR == QG) the last step of a stage reads only Y, so Z
@@ -364,7 +393,13 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
         if (early && copy2) stage_copy(s + 2, zc, zn);
         const int t0 = TPS * s;
 #pragma unroll
-        for (int i = 0; i + 1 < TPS; ++i) step(t0 + i, xc, i, xc, xn_, i + 1);  // refills from this stage
+        for (int i = 0; i + 1 < TPS; ++i) {
+            load_norms(xn_, i);
+            step(t0 + i, xc, i, xc, i + 1);  // refills from this stage
+        }
+        // the last tile's norms are read before the barrier, after which a faster wave may
+        // already copy into this buffer
+        load_norms(xn_, TPS - 1);
         const bool more = s + 1 < nst;
         if (more) {
             // stage s+1 landed (this wave), then published
@@ -372,7 +407,7 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
             else stage_barrier<0>();
         }
         if (!early && copy2) stage_copy(s + 2, zc, zn);
-        step(t0 + TPS - 1, xc, TPS - 1, yc, yn, 0);  // last tile; refills from the next stage
+        step(t0 + TPS - 1, xc, TPS - 1, yc, 0);  // last tile; refills from the next stage
     };
 
     // prologue: stages 0 and 1 in flight, stage 0 published, tile 0 loaded
@@ -385,7 +420,6 @@ __global__ __launch_bounds__(256) void assign_small_d_kernel(const void *__restr
     }
 #pragma unroll
     for (int q = 0; q < FR; ++q) f[q] = s_c0[q * 64 + lane];
-    load_norms(s_n0, 0);
 
     for (int s0 = 0; s0 < nst; s0 += 3) {
         run_stage(s0, s_c0, s_n0, s_c1, s_n1, s_c2, s_n2);

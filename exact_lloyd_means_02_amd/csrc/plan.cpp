@@ -6,10 +6,10 @@
 // Assign, small-D path (x tile kept in VGPRs for the whole centroid scan):
 //   * D is padded to DP in {16,...,512} (2-byte types) or {8,...,256} (fp32): the MFMA k-step
 //     is 16 (bf16/fp16 32x32x16) or 2 (fp32 32x32x2), and each lane holds half of every row.
-//   * VGPRs per lane ~= PB * (x: DP*s/8 + accumulators 16 + best 16) + fragment ring (<= 16)
-//     + c-norm 16 + ~48.  PB (32-point blocks per wave) is the largest of {2,1} keeping this
-//     <= 256, so at least two waves share a SIMD; the fold of one wave runs beside the MFMAs
-//     of the other.
+//   * VGPRs per lane ~= PB * (x: DP*s/8 + accumulators 16 + best 16) + fragment ring (<= 8)
+//     + ~24 (the tile's norms load into an accumulator set).  PB (32-point blocks per wave)
+//     is 2 up to 256-byte rows, else 1: at most 168 registers, so three waves share a SIMD and
+//     the fold of one wave runs beside the MFMAs of the others.
 //   * Centroid stages of 2 tiles (4 for D*s < 64 B, 1 for D*s >= 512 B) rotate through three
 //     LDS buffers, filled by direct global->LDS copies two stages ahead of use: ~49 KiB per
 //     workgroup, so three workgroups (12 waves) fit a CU's 160 KiB.
@@ -65,9 +65,9 @@ AssignCfg plan_assign(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
         c.block_n = ASSIGN_WAVES * c.pb * 32;
         c.lds = SMALL_D_STAGES * (c.tps * 32 * dp * s + c.tps * 32 * 4) + ASSIGN_WAVES * 8;
         // per point block: x (dp*s/8), accumulators (16), best tile copy (16); then the fragment
-        // ring (at most 4 groups of 4), the norms (16) and addressing / fold temporaries (~48)
+        // ring (at most 2 groups of 4) and addressing / fold temporaries (~24)
         const int qg = dp * s / 32;
-        c.vgpr = c.pb * (dp * s / 8 + 32) + (qg > 4 ? 4 : (qg == 4 ? 2 : qg)) * 4 + 16 + 48;
+        c.vgpr = c.pb * (dp * s / 8 + 32) + (qg >= 4 ? 2 : qg) * 4 + 24;
     } else {
         const int bd = splitd_bd(dt);
         c.path = 1;
