@@ -24,7 +24,7 @@
 //   * Centroid tiles are pre-laid-out in "MFMA-fragment" order (see prep kernel) so a stage
 //     is one contiguous copy and each A fragment is one conflict-free 16-byte LDS read per
 //     lane; stages rotate through three LDS buffers, filled by direct global->LDS copies
-//     two stages ahead of their use.
+//     (buffer loads into LDS, addressed from scalar registers) two stages ahead of their use.
 #include "common.h"
 #include "plan.h"
 
@@ -123,10 +123,18 @@ __device__ inline u32x4 load_x_group(const void *x, size_t row_elem0, int d0, in
     return u32x4{w[0], w[1], w[2], w[3]};
 }
 
-// Copy 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4): the
-// wave's 64 lanes fill the 1 KiB at `lds` (wave-uniform), lane l at bytes [16 l, 16 l + 16).
-__device__ inline void lds_dma16(const void *gptr, void *lds) {
-    __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+// Raw buffer descriptor over `bytes` bytes at `base` (fourth word: 32-bit data format, the
+// value gfx9-family parts expect for untyped loads).  Built in scalar registers.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+
+// Copy 16 bytes per lane from a buffer straight into LDS (buffer_load_dwordx4 ... lds): lane l
+// reads the buffer at byte voff + soff (voff per lane, soff wave-uniform) and the wave's 64
+// lanes fill the 1 KiB at `lds` (wave-uniform), lane l at bytes [16 l, 16 l + 16).  The
+// buffer form keeps all address arithmetic in scalar registers.
+__device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, int voff, int soff, void *lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
 }
 
 // acc += A(32 centroids) x B(32 points) over one 16-byte group per lane.
@@ -323,15 +331,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     const bool want_d = out_d != nullptr || wg_inertia != nullptr;
 
     // Global -> LDS copy of stage st (TPS tiles and their norms).  Every wave issues exactly
-    // NCOPY copy instructions, so it can wait for an older stage with a fixed count.
+    // NCOPY copy instructions, so it can wait for an older stage with a fixed count.  The
+    // descriptors are based at the stage, so every offset is small; each lane's offset is the
+    // constant 16 * lane, and each 1 KiB piece adds a scalar offset.
+    const int lane_off = lane * 16;
     auto stage_copy = [&](int st, u32x4 *__restrict__ sc, float *__restrict__ sn) {
-        const u32x4 *src = cb + (size_t)st * STAGE_U4;
+        const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(cb + (size_t)st * STAGE_U4, STAGE_U4 * 16);
 #pragma unroll
         for (int r = 0; r < PF; ++r) {
             const int chunk = r * ASSIGN_WAVES + w;
-            lds_dma16(src + chunk * 64 + lane, sc + chunk * 64);
+            lds_dma16(rc, lane_off, chunk * 1024, sc + chunk * 64);
         }
-        if (lane < 2 * TPS) lds_dma16(nb + (size_t)st * TPS * 32 + w * TPS * 8 + lane * 4, sn + w * TPS * 8);
+        if (lane < 2 * TPS) lds_dma16(buffer_rsrc(nb + (size_t)st * TPS * 32, TPS * 32 * 4), lane_off, w * TPS * 32, sn + w * TPS * 8);
     };
 
     ArgminState st[PB];
