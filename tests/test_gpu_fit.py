@@ -65,6 +65,35 @@ def test_fit_inertia_never_rises_much(fk):
     assert (J[1:] <= J[:-1] * (1 + 1e-3)).all()
 
 
+@pytest.mark.parametrize("name,kw", [("headline_bf16", dict(B=2, N=8192, K=256)), ("tiny_f32", dict())])
+def test_fit_resumes_from_its_centroids(fk, name, kw):
+    """The whole state of Lloyd's loop is the centroid set, so resuming is calling the fit again with
+    the centroids it returned: three iterations, then two more, match five in one call.  Not bit for
+    bit: a call's first iteration takes ||c~||^2 from the prepare kernel, while inside a fit the
+    update refreshes it with another fp32 summation order, so the norms may differ in the last bit."""
+    w = W.small(name, **kw)
+    _say(f"case {w}")
+    x, x64, c0, xt, ct = make_inputs(w)
+    c5 = ct.clone()
+    a5, J5, d5 = fk.kmeans_fit(xt, c5, 5, 0.0)
+    c3 = ct.clone()
+    _, J3, d3 = fk.kmeans_fit(xt, c3, 3, 0.0)
+    a2, J2, d2 = fk.kmeans_fit(xt, c3, 2, 0.0)
+    assert (d5, d3, d2) == (5, 3, 2)
+    flips = (a5.cpu().numpy() != a2.cpu().numpy()).mean()
+    Jr = np.concatenate([J3, J2])
+    rel = np.abs(Jr - J5) / np.abs(J5)
+    cg5 = c5.cpu().numpy().astype(np.float64)
+    cg = c3.cpu().numpy().astype(np.float64)
+    crel = (np.linalg.norm(cg - cg5, axis=2) / np.maximum(np.linalg.norm(cg5, axis=2), 1e-30)).max()
+    _say(f"label flips {flips:.3g}, objective rel {rel.max():.3g}, centroid rel {crel:.3g}, "
+         f"bit-identical {bool(flips == 0 and crel == 0)}")
+    assert flips < 1e-3
+    assert rel.max() <= INERTIA_TOL
+    if flips == 0:
+        assert crel <= CENTROID_TOL[w.dtype]
+
+
 def test_fit_tol_stops_early(fk):
     w = W.small("tiny_f32", iters=50)
     x, x64, c0, xt, ct = make_inputs(w)
