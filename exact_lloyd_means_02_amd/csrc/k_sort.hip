@@ -276,8 +276,12 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__rest
         const int32_t k = s_k[e];
         const uint32_t dg = ((uint32_t)k >> shift) & mask;
         const int dst = s_off[dg] + (e - s_ls[dg]);
-        keys_out[base + dst] = k;
-        vals_out[base + dst] = s_v[e];
+        // in range whenever the table counts these keys; the check keeps a table that does not
+        // (keys changed between the passes by a concurrent writer) from writing outside the rows
+        if ((unsigned)dst < (unsigned)N) {
+            keys_out[base + dst] = k;
+            vals_out[base + dst] = s_v[e];
+        }
     }
 }
 

@@ -119,15 +119,23 @@ def _need(cond, msg):
 _WS = {}
 
 
-def workspace(op: int, dt: int, B: int, N: int, D: int, K: int, device, chunk_points: int = 0):
-    """A cached uint8 device tensor of the size the C-ABI asks for."""
+def workspace(op: int, dt: int, B: int, N: int, D: int, K: int, device, chunk_points: int = 0, stream=None):
+    """A cached uint8 device tensor of the size the C-ABI asks for.
+
+    One cache entry per (operation, device, stream): calls queued on one stream run in order and
+    may share scratch memory, calls on different streams may run at the same time and must not.
+    A growing entry replaces the old tensor only after the device has drained, so no queued kernel
+    still uses the memory the allocator takes back."""
     torch = _torch()
     nbytes = LIB.kmeans_workspace_bytes(op, dt, B, N, D, K, chunk_points)
     if nbytes == 0:
         raise FlashKMError(KM_ERR_INVALID, last_error() or "bad shape for workspace")
-    key = (op, str(device))
+    sid = stream.value if isinstance(stream, ctypes.c_void_p) else stream
+    key = (op, str(device), sid)
     ws = _WS.get(key)
     if ws is None or ws.numel() < nbytes:
+        if ws is not None:
+            torch.cuda.synchronize(ws.device)
         ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
         _WS[key] = ws
     off = (-ws.data_ptr()) % 256
@@ -172,9 +180,10 @@ def kmeans_assign(x, centroids, x_norms=None, assign=None, min_dist=None, want_m
     if want_min_dist and min_dist is None:
         min_dist = torch.empty((B, N), dtype=torch.float32, device=x.device)
     dt = dtype_code(x)
-    ws = workspace(KM_OP_ASSIGN, dt, B, N, D, K, x.device)
+    st = _stream(x, stream)
+    ws = workspace(KM_OP_ASSIGN, dt, B, N, D, K, x.device, stream=st)
     _check(LIB.kmeans_assign(_ptr(x), dt, _ptr(centroids), B, N, D, K, _ptr(x_norms), _ptr(assign), _ptr(min_dist),
-                             _ptr(ws), ws.numel(), _stream(x, stream)))
+                             _ptr(ws), ws.numel(), st))
     return assign, min_dist
 
 
@@ -261,9 +270,10 @@ def kmeans_argsort_ids(assign, K: int, sorted_ids=None, sorted_idx=None, counts=
         sorted_idx = torch.empty_like(assign)
     if want_counts and counts is None:
         counts = torch.empty((B, K), dtype=torch.int32, device=assign.device)
-    ws = workspace(KM_OP_ARGSORT, KM_F32, B, N, 1, K, assign.device)
+    st = _stream(assign, stream)
+    ws = workspace(KM_OP_ARGSORT, KM_F32, B, N, 1, K, assign.device, stream=st)
     _check(LIB.kmeans_argsort_ids(_ptr(assign), B, N, K, _ptr(sorted_ids), _ptr(sorted_idx), _ptr(counts),
-                                  _ptr(ws), ws.numel(), _stream(assign, stream)))
+                                  _ptr(ws), ws.numel(), st))
     return sorted_ids, sorted_idx, counts
 
 
@@ -277,9 +287,10 @@ def kmeans_update(x, sorted_ids, sorted_idx, counts, centroids, shift=None, want
     if want_shift and shift is None:
         shift = torch.empty((B,), dtype=torch.float64, device=x.device)
     dt = dtype_code(x)
-    ws = workspace(KM_OP_UPDATE, dt, B, N, D, K, x.device)
+    st = _stream(x, stream)
+    ws = workspace(KM_OP_UPDATE, dt, B, N, D, K, x.device, stream=st)
     _check(LIB.kmeans_update(_ptr(x), dt, _ptr(sorted_ids), _ptr(sorted_idx), _ptr(counts), B, N, D, K,
-                             _ptr(centroids), _ptr(shift), _ptr(ws), ws.numel(), _stream(x, stream)))
+                             _ptr(centroids), _ptr(shift), _ptr(ws), ws.numel(), st))
     return shift
 
 
@@ -299,12 +310,13 @@ def kmeans_fit(x, centroids, iters: int, tol: float = 0.0, chunk_points: int = 0
         assign = torch.empty((B, N), dtype=torch.int32, device=dev)
     dt = dtype_code(x)
     op = KM_OP_FIT if x.is_cuda else KM_OP_FIT_HOST
-    ws = workspace(op, dt, B, N, D, K, dev, chunk_points)
+    st = _stream(centroids, stream)
+    ws = workspace(op, dt, B, N, D, K, dev, chunk_points, stream=st)
     inertia = np.zeros((iters, B), dtype=np.float64)
     done = ctypes.c_int32(0)
     _check(LIB.kmeans_fit(_ptr(x), dt, B, N, D, K, int(iters), float(tol), int(chunk_points), _ptr(centroids),
                           _ptr(assign), inertia.ctypes.data_as(ctypes.c_void_p), ctypes.byref(done), _ptr(ws),
-                          ws.numel(), _stream(centroids, stream)))
+                          ws.numel(), st))
     return assign, inertia[: done.value], done.value
 
 
@@ -329,12 +341,13 @@ def kmeans_fit_metric(x, centroids, metric, iters: int, tol: float = 0.0, chunk_
         op = {KM_METRIC_L2: KM_OP_FIT, KM_METRIC_DOT: KM_OP_FIT_DOT, KM_METRIC_COSINE: KM_OP_FIT_COSINE}[m]
     else:
         op = KM_OP_FIT_HOST
-    ws = workspace(op, dt, B, N, D, K, dev, chunk_points)
+    st = _stream(centroids, stream)
+    ws = workspace(op, dt, B, N, D, K, dev, chunk_points, stream=st)
     obj = np.zeros((iters, B), dtype=np.float64)
     done = ctypes.c_int32(0)
     _check(LIB.kmeans_fit_metric(_ptr(x), dt, m, B, N, D, K, int(iters), float(tol), int(chunk_points),
                                  _ptr(centroids), _ptr(assign), obj.ctypes.data_as(ctypes.c_void_p),
-                                 ctypes.byref(done), _ptr(ws), ws.numel(), _stream(centroids, stream)))
+                                 ctypes.byref(done), _ptr(ws), ws.numel(), st))
     return assign, obj[: done.value], done.value
 
 

@@ -232,3 +232,18 @@ def test_centroid_alignment_validation(fk):
     assert "centroids" in fk.last_error()
     assert L.kmeans_fit_metric(P, 2, 2, 1, 10, 8, 3, 2, 0.0, 0, C, None, None, None, P, 1 << 20,
                                None) == fk.KM_ERR_INVALID
+
+
+def test_workspace_cache_is_per_stream(fk):
+    """Calls on different streams may overlap, so the binding never hands them the same scratch
+    memory; calls on one stream run in order and share it (host tensors stand in for the device)."""
+    fk.clear_workspaces()
+    try:
+        a = fk.workspace(fk.KM_OP_FIT, fk.KM_BF16, 2, 4096, 64, 32, "cpu", stream=ctypes.c_void_p(0x1000))
+        b = fk.workspace(fk.KM_OP_FIT, fk.KM_BF16, 2, 4096, 64, 32, "cpu", stream=ctypes.c_void_p(0x2000))
+        a2 = fk.workspace(fk.KM_OP_FIT, fk.KM_BF16, 2, 4096, 64, 32, "cpu", stream=ctypes.c_void_p(0x1000))
+        assert a.untyped_storage().data_ptr() != b.untyped_storage().data_ptr()
+        assert a.untyped_storage().data_ptr() == a2.untyped_storage().data_ptr()
+        assert a.data_ptr() % 256 == 0 and b.data_ptr() % 256 == 0
+    finally:
+        fk.clear_workspaces()
