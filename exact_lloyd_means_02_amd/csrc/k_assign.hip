@@ -156,6 +156,18 @@ __device__ inline f32x16 mfma_group(const u32x4 &a, const u32x4 &bx, f32x16 acc)
     }
 }
 
+// acc + a.lo^2 + a.hi^2 for a word holding two 2-byte values (v_dot2_f32_{bf16,f16}).
+template <int DT>
+__device__ inline float dot2_self(uint32_t w, float acc) {
+    if constexpr (DT == DT_BF16) {
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w), __builtin_bit_cast(b2, w), acc, false);
+    } else {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w), __builtin_bit_cast(h2, w), acc, false);
+    }
+}
+
 // Running arg-min state of one lane for one 32-point block.
 struct ArgminState {
     float run_min;
@@ -448,10 +460,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
         if (want_d && !xnorm) {
 #pragma unroll
             for (int q = 0; q < QG; ++q) {
-                float fx[VW];
-                widen16<DT>(__builtin_bit_cast(uint4, xr[p][q]), fx);
+                if constexpr (DT == DT_F32) {
+                    float fx[VW];
+                    widen16<DT>(__builtin_bit_cast(uint4, xr[p][q]), fx);
 #pragma unroll
-                for (int e = 0; e < VW; ++e) own += fx[e] * fx[e];
+                    for (int e = 0; e < VW; ++e) own += fx[e] * fx[e];
+                } else {
+                    // two squares per instruction (exact products, fp32 sum), no widening
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) own = dot2_self<DT>(xr[p][q][e], own);
+                }
             }
             own += __shfl_xor(own, 32);
         }
