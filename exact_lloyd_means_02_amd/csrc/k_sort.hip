@@ -12,7 +12,8 @@
 //               digit's offsets over the tiles and records the digit's total, and every scatter
 //               workgroup adds the exclusive scan of the totals;
 //   3. scatter: each wave ranks its keys 64 at a time, in index order: lanes holding the same
-//               digit are found with one ballot per digit bit; a lane's rank = earlier peers
+//               digit are found with one ballot per digit bit (the digit width is a template
+//               parameter, so these unroll); a lane's rank = earlier peers
 //               in the round + the wave's running count of that digit (LDS).  The tile is
 //               then laid out in LDS in (digit, index) order and written out with consecutive
 //               lanes on consecutive positions of each digit's run.  Result: stable.
@@ -143,7 +144,7 @@ __device__ inline void block_exscan_1024(int32_t *s, int n, int32_t *s_wsum) {
 // otherwise `hist` holds each digit's offsets over the tiles ([bins][tiles], scanned per row)
 // and `totals` the digit totals, whose exclusive scan each workgroup adds.  For counts != NULL
 // the workgroup of tile 0 writes the per-bin totals.
-template <bool INLINE>
+template <bool INLINE, int BITS>
 __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__restrict__ keys_in,
                                                            const int32_t *__restrict__ vals_in,
                                                            const int32_t *__restrict__ hist,
@@ -232,12 +233,18 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__rest
         const int i = tile0 + r * 64 + lane;
         const bool ok = i < N;
         const uint32_t dg = ((uint32_t)key[r] >> shift) & mask;
-        uint64_t peers = __ballot(ok);
-        for (int bit = 0; bit < bits; ++bit) {
-            const bool set = (dg >> bit) & 1u;
-            const uint64_t bal = __ballot(set);
-            peers &= set ? bal : ~bal;
+        // peers: the lanes whose digit equals this lane's, one ballot per digit bit; a lane
+        // keeps the ballot where its bit is set and its complement where it is clear
+        const uint64_t okm = __ballot(ok);
+        uint32_t p_lo = (uint32_t)okm, p_hi = (uint32_t)(okm >> 32);
+#pragma unroll
+        for (int bit = 0; bit < BITS; ++bit) {
+            const uint32_t sx = (uint32_t)__builtin_amdgcn_sbfe((int)dg, bit, 1);  // 0 or all ones
+            const uint64_t bal = __ballot(sx != 0u);
+            p_lo &= ~((uint32_t)bal ^ sx);
+            p_hi &= ~((uint32_t)(bal >> 32) ^ sx);
         }
+        const uint64_t peers = ((uint64_t)p_hi << 32) | p_lo;
         const int before = __popcll(peers & lt);
         // LDS accesses of one wave complete in order and the store depends on the load, so
         // every lane reads its base before the group's lowest lane bumps it.
@@ -272,6 +279,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__rest
     }
     __syncthreads();
     const int tile_n = min(SORT_TILE, N - t * SORT_TILE);
+#pragma unroll 4
     for (int e = tid; e < tile_n; e += 256) {
         const int32_t k = s_k[e];
         const uint32_t dg = ((uint32_t)k >> shift) & mask;
@@ -311,6 +319,26 @@ hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s) {
     return hipGetLastError();
 }
 
+// The scatter kernel for `bits` bits per digit (1..SORT_MAX_BITS): the ballot loop unrolls.
+template <bool INLINE>
+static hipError_t launch_scatter(int bits, dim3 grid, size_t lds, hipStream_t s, const int32_t *kin, const int32_t *vin,
+                           const int32_t *hist, const int32_t *totals, int N, int ntiles, int shift, int32_t *ko,
+                           int32_t *vo, int32_t *cnt, int K) {
+#define FKM_SCATTER(B_)                                                                                            \
+    case B_:                                                                                                       \
+        sort_scatter_kernel<INLINE, B_><<<grid, dim3(256), lds, s>>>(kin, vin, hist, totals, N, ntiles, shift, bits, \
+                                                                      ko, vo, cnt, K);                             \
+        break;
+    static_assert(SORT_MAX_BITS == 10, "one instance per digit width");
+    switch (bits) {
+        FKM_SCATTER(1) FKM_SCATTER(2) FKM_SCATTER(3) FKM_SCATTER(4) FKM_SCATTER(5)
+        FKM_SCATTER(6) FKM_SCATTER(7) FKM_SCATTER(8) FKM_SCATTER(9) FKM_SCATTER(10)
+        default: return hipErrorInvalidValue;  // the plan never asks for another width
+    }
+#undef FKM_SCATTER
+    return hipGetLastError();
+}
+
 size_t sort_ws_bytes(int64_t B, int64_t N, int64_t K) {
     const SortCfg c = plan_sort(N, K);
     size_t bytes = align256((size_t)B * c.bins * c.ntiles * 4) + align256((size_t)B * c.bins * 4);
@@ -347,14 +375,14 @@ hipError_t launch_argsort(const int32_t *keys, int B, int N, int K, int32_t *out
         sort_hist_kernel<<<dim3(B * c.ntiles), dim3(256), c.bins * 4, s>>>(kin, N, c.ntiles, shift, c.bins, hist,
                                                                             inline_offsets ? 1 : 0);
         if (inline_offsets) {
-            sort_scatter_kernel<true><<<dim3(B * c.ntiles), dim3(256), lds, s>>>(kin, vin, hist, nullptr, N,
-                                                                                c.ntiles, shift, c.bits, ko, vo,
-                                                                                cnt_out, K);
+            const hipError_t e = launch_scatter<true>(c.bits, dim3(B * c.ntiles), lds, s, kin, vin, hist, nullptr, N,
+                                                      c.ntiles, shift, ko, vo, cnt_out, K);
+            if (e != hipSuccess) return e;
         } else {
             sort_rowscan_kernel<<<dim3(B * c.bins), dim3(256), 0, s>>>(hist, c.bins, c.ntiles, totals);
-            sort_scatter_kernel<false><<<dim3(B * c.ntiles), dim3(256), lds, s>>>(kin, vin, hist, totals, N,
-                                                                                 c.ntiles, shift, c.bits, ko, vo,
-                                                                                 cnt_out, K);
+            const hipError_t e = launch_scatter<false>(c.bits, dim3(B * c.ntiles), lds, s, kin, vin, hist, totals, N,
+                                                       c.ntiles, shift, ko, vo, cnt_out, K);
+            if (e != hipSuccess) return e;
         }
         kin = ko;
         vin = vo;
