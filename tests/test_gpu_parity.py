@@ -44,6 +44,13 @@ ASSIGN_CASES = [
     ("splitd_f32", dict(N=700, K=150)),
     ("headline_bf16", dict(B=1, N=520, D=768, K=70)),
     ("batched_f16", dict(B=1, N=300, D=1000, K=40)),
+    # one case per remaining small-D instance (padded D): 2-byte 16, 64, 256; fp32 8, 32, 128
+    ("headline_bf16", dict(B=1, N=900, D=10, K=50)),
+    ("batched_f16", dict(B=1, N=800, D=64, K=130)),
+    ("headline_bf16", dict(B=1, N=700, D=256, K=90)),
+    ("tiny_f32", dict(N=1500, D=8, K=33, M=12)),
+    ("tiny_f32", dict(N=1200, D=32, K=70, M=30)),
+    ("tiny_f32", dict(N=1000, D=128, K=200, M=40)),
     ("splitd_f32", dict(N=400, D=300, K=64)),
     ("headline_bf16", dict(B=1, N=700, D=200, K=70)),      # 2-byte, padded D = 256 (fragment ring)
     ("batched_f16", dict(B=2, N=500, D=256, K=40)),
@@ -135,7 +142,9 @@ def test_argsort_worked_example(fk, golden_dir):
 
 SORT_CASES = [(1, 1, 1), (3, 10000, 1000), (2, 4097, 8), (1, 65536, 1024), (2, 1 << 17, 32768),
               (1, 1 << 20, 4096), (4, 12345, 2048), (1, 5000, 5000), (1, 1 << 20, 1000), (3, 70000, 1024),
-              (2, 300000, 700), (1, 1 << 22, 64)]
+              (2, 300000, 700), (1, 1 << 22, 64),
+              # every digit width has its own scatter instance: 2, 4, 5 and 9 bits
+              (2, 5000, 3), (1, 9000, 16), (2, 6000, 31), (1, 20000, 300)]
 
 
 @pytest.mark.parametrize("B,N,K", SORT_CASES)
