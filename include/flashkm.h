@@ -23,7 +23,10 @@
  *     16-byte aligned.
  *   - The caller owns every buffer.  The library allocates no device memory:
  *     temporary storage comes from the caller's workspace `ws` of `ws_bytes`
- *     bytes, sized by kmeans_workspace_bytes() and 256-byte aligned.
+ *     bytes, sized by kmeans_workspace_bytes() and 256-byte aligned.  Calls on
+ *     one stream run in order and may share one workspace; calls that may run
+ *     at the same time (other streams) need workspaces of their own, as their
+ *     intermediate arrays (labels, digit tables, partial sums) live there.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue their
  *     kernels on it and return without waiting, except kmeans_fit (see there).
  *   - Errors are explicit: every call returns a km_status_t; there is no
