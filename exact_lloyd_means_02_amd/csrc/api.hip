@@ -25,7 +25,7 @@ size_t update_ws_bytes(int dt, int64_t B, int64_t N, int64_t D, int64_t K);
 bool update_refreshes_prep(int dt, int64_t B, int64_t N, int64_t D);
 hipError_t launch_update(int dt, const void *x, const int32_t *sids, const int32_t *sidx, const int32_t *counts,
                          int B, int N, int D, int K, int mode, float *C, double *shift, float *sums, int32_t *cnt,
-                         const UpdRefresh &ref, void *ws, hipStream_t s);
+                         const UpdRefresh &ref, void *ws, hipStream_t s, int normalize = 0);
 hipError_t launch_finalize_acc(int dt, const float *sums, const int32_t *cnt, float *C, double *shift, double *shk,
                                const UpdRefresh &ref, int B, int K, int D, hipStream_t s, int normalize);
 hipError_t launch_row_norms(int dt, const void *x, float *out, int64_t rows, int D, hipStream_t s);
@@ -525,7 +525,13 @@ km_status_t fit_device(int dt, const void *x, int64_t B, int64_t N, int64_t D, i
         KM_HIP(launch_assign(dt, cfg, xa, cprep, cnh, xn_in, a, nullptr, ring_part + (size_t)slot * B * wpb, (int)B,
                              (int)N, (int)D, (int)K, s));
         KM_HIP(launch_argsort(a, (int)B, (int)N, (int)K, sids, sidx, counts, scratch, s));
-        if (cosine) {
+        if (cosine && fused_prep) {
+            // one column block per row: the update finishes each cluster in place with the mean
+            // direction s_k / ||s_k|| (and the shift and the refresh), like the Euclidean finish
+            KM_HIP(launch_update(dt, xa, sids, sidx, counts, (int)B, (int)N, (int)D, (int)K, 0, C,
+                                 tol > 0.f ? ring_s + (size_t)slot * B : nullptr, nullptr, nullptr, full_ref, scratch,
+                                 s, 1));
+        } else if (cosine) {
             // sums and counts per cluster, then the mean direction (with shift and refresh)
             float *sums = (float *)(ws + L.sums);
             int32_t *cnt = (int32_t *)(ws + L.cnt);

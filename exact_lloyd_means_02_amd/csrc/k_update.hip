@@ -137,11 +137,28 @@ __device__ inline void load_row(const UpdArgs &a, size_t row_elem0, int c0, int 
 //         sum (c_new - c_old)^2 over the lane's columns (c_old prefetched in `cold`); adds
 //         sum c~^2 to cn2 when the prepared centroids are refreshed.
 // mode 1: sums_k += s, cnt_k += n.
+// With a.normalize (mode 0, cosine k-means) c_k <- s / ||s|| (fp32 norm over the row, IEEE
+// division) instead of s / n, and a cluster whose sum is the zero vector keeps its centroid.  The
+// norm is reduced over the row group's lanes, so it needs one column block per row (ncb == 1).
 template <int DT, int V, int VPL, bool SHIFT>
 __device__ inline float finish_cluster(const UpdArgs &a, int b, int k, int c0, int r, const float (&s)[VPL][V], int n,
                                        const float (&cold)[VPL][V], bool write_cnt, float &cn2) {
     float d2 = 0.f;
     const size_t rowo = ((size_t)b * a.K + k) * a.D;
+    float den = (float)n;
+    if (a.mode == 0 && a.normalize) {
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const int e0 = c0 + (r + i * a.lanes) * V;
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+                if (e0 + e < a.D) ss += s[i][e] * s[i][e];
+        }
+        for (int off = 1; off < a.lanes; off <<= 1) ss += __shfl_xor(ss, off);  // the row group's lanes
+        den = sqrtf(ss);
+        if (!(den > 0.f)) return 0.f;  // uniform over the row group: the centroid is kept
+    }
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const int e0 = c0 + (r + i * a.lanes) * V;
@@ -152,7 +169,7 @@ __device__ inline float finish_cluster(const UpdArgs &a, int b, int k, int c0, i
                 float nw[V];
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
-                    nw[e] = s[i][e] / (float)n;
+                    nw[e] = s[i][e] / den;
                     if (SHIFT) {
                         const float df = nw[e] - cold[i][e];
                         d2 += df * df;
@@ -171,7 +188,7 @@ __device__ inline float finish_cluster(const UpdArgs &a, int b, int k, int c0, i
                 const int d = e0 + e;
                 nw[e] = 0.f;
                 if (d < a.D) {
-                    nw[e] = s[i][e] / (float)n;
+                    nw[e] = s[i][e] / den;
                     a.C[rowo + d] = nw[e];
                     if (SHIFT) {
                         const float df = nw[e] - cold[i][e];
@@ -436,11 +453,12 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
 }
 
 // Finish column d of cluster k of problem b from its sum `s`, within a combine kernel.
-__device__ inline float combine_finish_col(const UpdArgs &a, int b, int k, size_t rowo, int d, float s, int nk,
+// den: n_k, or ||s_k|| with a.normalize (mode 0).
+__device__ inline float combine_finish_col(const UpdArgs &a, int b, int k, size_t rowo, int d, float s, float den,
                                            float &cn2) {
     if (a.mode == 0) {
         const float old = a.C[rowo + d];
-        const float nw = s / (float)nk;
+        const float nw = s / den;
         a.C[rowo + d] = nw;
         if (a.cprep) cn2 += prep_store_elem(a, b, k, d, nw);
         return (nw - old) * (nw - old);
@@ -497,8 +515,8 @@ __global__ __launch_bounds__(256) void upd_combine_kernel(UpdArgs a, int64_t nch
         while (DC < D && DC < 256) DC <<= 1;
         const int PG = 256 / DC;
         const int pg = t / DC, dcol = t - pg * DC;
-        float d2 = 0.f, cn2 = 0.f;
-        for (int d = dcol; d < ((D + DC - 1) / DC) * DC; d += DC) {
+        // column d's sum over the pieces, left in s_red[dcol] (fixed-order tree; every thread calls)
+        auto column_sum = [&](int d) {
             float sum = 0.f;
             if (d < D) {
                 // pieces pg, pg + PG, ... in order; eight loads in flight before they are added
@@ -521,7 +539,34 @@ __global__ __launch_bounds__(256) void upd_combine_kernel(UpdArgs a, int64_t nch
                 if (pg < off) s_red[t] += s_red[t + off * DC];
                 __syncthreads();
             }
-            if (pg == 0 && d < D) d2 += combine_finish_col(a, b, kk, rowo, d, s_red[dcol], nkk, cn2);
+        };
+        const int dend = ((D + DC - 1) / DC) * DC;
+        float den = (float)nkk;
+        if (a.mode == 0 && a.normalize) {
+            // the mean direction needs ||s|| first: one pass for the norm, then the same sums again
+            float ss = 0.f;
+            for (int d = dcol; d < dend; d += DC) {
+                column_sum(d);
+                if (pg == 0 && d < D) ss += s_red[dcol] * s_red[dcol];
+                __syncthreads();
+            }
+            s_red[t] = ss;
+            __syncthreads();
+            for (int off = 128; off >= 1; off >>= 1) {
+                if (t < off) s_red[t] += s_red[t + off];
+                __syncthreads();
+            }
+            den = sqrtf(s_red[0]);
+            __syncthreads();
+            if (!(den > 0.f)) {  // uniform: the zero sum keeps the centroid
+                if (t == 0 && a.shp) a.shp[(size_t)chunk * (a.ncb + 1) + a.ncb] = 0.0;
+                continue;
+            }
+        }
+        float d2 = 0.f, cn2 = 0.f;
+        for (int d = dcol; d < dend; d += DC) {
+            column_sum(d);
+            if (pg == 0 && d < D) d2 += combine_finish_col(a, b, kk, rowo, d, s_red[dcol], den, cn2);
             __syncthreads();
         }
         if (a.mode == 0) {
@@ -557,9 +602,8 @@ __global__ __launch_bounds__(256) void upd_combine_kernel(UpdArgs a, int64_t nch
         if (np > COMBINE_WAVE_MAX) continue;
         const int b = (int)(chunk / a.nch);
         const size_t rowo = ((size_t)b * a.K + kk) * D;
-        float d2 = 0.f, cn2 = 0.f;
-        for (int d = lane; d < D; d += 64) {
-            // every piece is loaded before the in-order sum (the loads are independent)
+        // column d's sum over the pieces, in chunk order; every piece is loaded before the sum
+        auto column_sum = [&](int d) {
             float pv[COMBINE_WAVE_MAX];
             pv[0] = a.part[((size_t)chunk * 2 + 1) * D + d];
 #pragma unroll
@@ -569,8 +613,24 @@ __global__ __launch_bounds__(256) void upd_combine_kernel(UpdArgs a, int64_t nch
 #pragma unroll
             for (int j = 1; j < COMBINE_WAVE_MAX; ++j)
                 if (j < np) sum += pv[j];
-            d2 += combine_finish_col(a, b, kk, rowo, d, sum, nkk, cn2);
+            return sum;
+        };
+        float den = (float)nkk;
+        if (a.mode == 0 && a.normalize) {
+            float ss = 0.f;
+            for (int d = lane; d < D; d += 64) {
+                const float sum = column_sum(d);
+                ss += sum * sum;
+            }
+            for (int off = 1; off < 64; off <<= 1) ss += __shfl_xor(ss, off);
+            den = sqrtf(ss);
+            if (!(den > 0.f)) {  // uniform: the zero sum keeps the centroid
+                if (lane == 0 && a.shp) a.shp[(size_t)chunk * (a.ncb + 1) + a.ncb] = 0.0;
+                continue;
+            }
         }
+        float d2 = 0.f, cn2 = 0.f;
+        for (int d = lane; d < D; d += 64) d2 += combine_finish_col(a, b, kk, rowo, d, column_sum(d), den, cn2);
         if (a.mode == 0) {
             for (int off = 1; off < 64; off <<= 1) {
                 d2 += __shfl_xor(d2, off);
@@ -699,13 +759,16 @@ bool update_refreshes_prep(int dt, int64_t B, int64_t N, int64_t D) { return pla
 // mode 0: in-core update of C; shift (optional, [B]) receives sum_k ||c_new - c_old||^2 in fp64,
 // summed in a fixed order.  mode 1: accumulate into sums / cnt.  `ref` optionally names the
 // prepared centroids to refresh.
+// normalize (mode 0, one column block per row): c_k <- s_k / ||s_k||, the cosine mean direction.
 hipError_t launch_update(int dt, const void *x, const int32_t *sids, const int32_t *sidx, const int32_t *counts,
                          int B, int N, int D, int K, int mode, float *C, double *shift, float *sums, int32_t *cnt,
-                         const UpdRefresh &ref, void *ws, hipStream_t s) {
+                         const UpdRefresh &ref, void *ws, hipStream_t s, int normalize) {
     const UpdCfg u = plan_update(dt, B, N, D);
     const int64_t chunks = (int64_t)B * u.nch;
-    const UpdArgs a = make_args(dt, x, sids, sidx, counts, B, N, D, K, mode, C, shift != nullptr, sums, cnt,
-                                mode == 0 ? ref : UpdRefresh{}, ws);
+    if (normalize && (mode != 0 || u.ncb != 1)) return hipErrorInvalidValue;
+    UpdArgs a = make_args(dt, x, sids, sidx, counts, B, N, D, K, mode, C, shift != nullptr, sums, cnt,
+                          mode == 0 ? ref : UpdRefresh{}, ws);
+    a.normalize = normalize;
     hipError_t e;
     const int64_t waves = chunks * u.ncb;
     if (dt == DT_F32) e = launch_segsum_dt<DT_F32>(a, u.vec, u.vpl, waves, s);
