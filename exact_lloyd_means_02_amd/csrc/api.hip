@@ -115,8 +115,8 @@ struct FitLayout {
 
 // Device-resident x.  The prepared centroids persist across iterations (the update refreshes
 // them); the arg-sort and update scratch share one region.  Cosine k-means adds the unit rows
-// x^ [B][N][D] (input dtype) and the accumulating update's sums [B][K][D], counts [B][K] and
-// per-cluster shifts [B][K].
+// x^ [B][N][D] (input dtype) and, where rows need several column blocks, the accumulating
+// update's sums [B][K][D], counts [B][K] and per-cluster shifts [B][K].
 FitLayout fit_layout(int dt, int64_t B, int64_t N, int64_t D, int64_t K, int metric = KM_METRIC_L2) {
     FitLayout L{};
     size_t o = 0;
@@ -132,9 +132,11 @@ FitLayout fit_layout(int dt, int64_t B, int64_t N, int64_t D, int64_t K, int met
     L.ring_s = o; o += align256((size_t)RING * B * 8);
     if (metric == KM_METRIC_COSINE) {
         L.xhat = o; o += align256((size_t)B * N * D * elem_bytes(dt));
-        L.sums = o; o += align256((size_t)B * K * D * 4);
-        L.cnt = o; o += align256((size_t)B * K * 4);
-        L.shk = o; o += align256((size_t)B * K * 8);
+        if (!update_refreshes_prep(dt, B, N, D)) {  // the accumulating update (wide rows) only
+            L.sums = o; o += align256((size_t)B * K * D * 4);
+            L.cnt = o; o += align256((size_t)B * K * 4);
+            L.shk = o; o += align256((size_t)B * K * 8);
+        }
     }
     L.scratch = o;
     const size_t s2 = argsort_ws(B, N, K), s3 = update_ws(dt, B, N, D, K);

@@ -194,16 +194,20 @@ def test_metric_entry_validation(fk):
 
 
 def test_metric_workspace_sizes(fk):
-    B, N, D, K = 2, 5000, 64, 100
-    for dt, s in ((0, 4), (1, 2), (2, 2)):
+    B, N, K = 2, 5000, 100
+    # (dtype, bytes per element, D, whether the update needs several column blocks per row):
+    # one block covers 64 lanes x 4 vectors x 16 bytes, i.e. 2048 2-byte or 1024 fp32 columns
+    for dt, s, D, wide in ((0, 4, 64, False), (1, 2, 64, False), (2, 2, 64, False), (2, 2, 4096, True),
+                           (0, 4, 2048, True)):
         base = fk.kmeans_workspace_bytes(fk.KM_OP_FIT, dt, B, N, D, K)
         dot = fk.kmeans_workspace_bytes(fk.KM_OP_FIT_DOT, dt, B, N, D, K)
         cos = fk.kmeans_workspace_bytes(fk.KM_OP_FIT_COSINE, dt, B, N, D, K)
         assert dot == base
-        # the unit rows, sums, counts and per-cluster shifts come on top
-        assert cos >= base + B * N * D * s + B * K * D * 4 + B * K * 4 + B * K * 8
-        assert cos <= base + B * N * D * s + B * K * D * 4 + B * K * 4 + B * K * 8 + 4 * 256
-    assert fk.kmeans_workspace_bytes(99, 2, B, N, D, K) == 0
+        # the unit rows come on top; the accumulating update's sums, counts and per-cluster shifts
+        # only where a row needs several column blocks (else the update finishes in place)
+        extra = B * N * D * s + ((B * K * D * 4 + B * K * 4 + B * K * 8) if wide else 0)
+        assert base + extra <= cos <= base + extra + 4 * 256
+    assert fk.kmeans_workspace_bytes(99, 2, B, N, 64, K) == 0
 
 
 def test_wrapper_validation_without_gpu(fk):
