@@ -188,6 +188,9 @@ FIT_CASES = [
     ("cosine", "headline_bf16", dict(B=2, N=8192, K=256), 6),
     ("cosine", "batched_f16", dict(B=2, N=5000, K=100), 4),
     ("cosine", "tiny_f32", dict(), 10),
+    # rows of 1100 fp32 columns need two column blocks in the update, so cosine takes the
+    # accumulating update and the mean-direction finalize instead of the in-place finish
+    ("cosine", "splitd_f32", dict(N=3000, D=1100, K=40), 3),
 ]
 
 
