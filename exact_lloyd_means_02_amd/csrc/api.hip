@@ -156,6 +156,25 @@ int64_t host_chunk(int64_t N, int64_t chunk_points) {
     return c;
 }
 
+// Scratch of the streamed path: the arg-sort tables or the update's chunk partials of one
+// staged chunk.  Chunks hold `c` points except the last, which holds N - (nchunk-1) c; the
+// update's plan is not monotonic in the point count (its rows per wave are a power of two
+// derived from the count, so a shorter chunk can have more partial records), so the region
+// covers both sizes.
+size_t host_scratch(int dt, int64_t N, int64_t D, int64_t K, int64_t c) {
+    auto need = [&](int64_t n) {
+        const size_t s2 = argsort_ws(1, n, K), s3 = update_ws(dt, 1, n, D, K);
+        return s2 > s3 ? s2 : s3;
+    };
+    size_t sc = need(c);
+    const int64_t last = N - (ceil_div(N, c) - 1) * c;
+    if (last != c) {
+        const size_t sl = need(last);
+        if (sl > sc) sc = sl;
+    }
+    return sc;
+}
+
 // Pinned-host x: two staging buffers, per-chunk arrays, [B][K][D] sums and [B][K] counts.
 HostLayout host_layout(int dt, int64_t B, int64_t N, int64_t D, int64_t K, int64_t chunk_points) {
     HostLayout L{};
@@ -180,10 +199,7 @@ HostLayout host_layout(int dt, int64_t B, int64_t N, int64_t D, int64_t K, int64
     L.ring_s = o; o += align256((size_t)RING * B * 8);
     L.red = o; o += reduce_ws_bytes(B);
     L.scratch = o;
-    size_t sc = argsort_ws(1, c, K);
-    const size_t u = update_ws(dt, 1, c, D, K);
-    if (u > sc) sc = u;
-    o += sc;
+    o += host_scratch(dt, N, D, K, c);
     L.total = o;
     return L;
 }

@@ -31,7 +31,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .lloyd import centroid_operand, segment_sums, argsort_ids
+from .lloyd import centroid_operand, segment_sums, argsort_ids, shift
 
 
 def normalize_rows(x: np.ndarray) -> np.ndarray:
@@ -134,11 +134,10 @@ def similarity_iteration(x: np.ndarray, c: np.ndarray, metric: str, dtype: str =
             c_new[b], _ = mean_direction(x[b], a[b], c[b])
     if mode == "modelled":
         c_new = c_new.astype(np.float32).astype(np.float64)   # the master is kept in fp32
-    diff = c_new - c
     return {
         "c_operand": ct, "a": a, "s1": s1, "s2": s2, "scale": scale, "objective": s1.sum(axis=1),
         "sorted_ids": sids, "sorted_idx": sidx, "counts": counts, "c_new": c_new,
-        "shift": np.sum(diff * diff, axis=(-1, -2)),
+        "shift": shift(c_new, c),
     }
 
 

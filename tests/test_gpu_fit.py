@@ -119,6 +119,25 @@ def test_fit_streamed_matches_device(fk, chunk):
     assert (np.abs(J_host - ref["inertia"]) / ref["inertia"]).max() <= INERTIA_TOL
 
 
+def test_fit_streamed_ragged_last_chunk_needs_more_scratch(fk):
+    """532480-point chunks with a last chunk of 2^19 points: the update plan of the shorter chunk
+    has more partial records than a full chunk's (the streamed workspace covers both sizes).
+    One iteration (the centroids of the two runs then differ in fp32 summation order only): labels
+    must equal the device-resident run's, the inertia the oracle's."""
+    w = W.small("headline_bf16", B=1, N=532480 + (1 << 19), K=64, iters=1)
+    _say(f"case {w}, chunk_points 532480")
+    x, x64, c0, xt, ct = make_inputs(w)
+    xh = W.to_torch(x, w.dtype).pin_memory()
+    c_dev, c_host = ct.clone(), ct.clone()
+    a_dev, J_dev, _ = fk.kmeans_fit(xt, c_dev, w.iters, 0.0)
+    a_host, J_host, done = fk.kmeans_fit(xh, c_host, w.iters, 0.0, chunk_points=532480)
+    assert done == w.iters
+    assert np.array_equal(a_host.cpu().numpy(), a_dev.cpu().numpy())
+    assert np.allclose(J_host, J_dev, rtol=1e-5)
+    ref = oracle.lloyd_fit(x64, c0, w.iters, 0.0, dtype=w.dtype, mode="modelled")
+    assert (np.abs(J_host - ref["inertia"]) / ref["inertia"]).max() <= INERTIA_TOL
+
+
 def test_fit_rejects_pageable_host(fk):
     w = W.small("tiny_f32")
     x, _, c0, _, ct = make_inputs(w)

@@ -159,6 +159,51 @@ def test_two_blobs_one_step():
     assert it["c_new"][0, :, 0].tolist() == [-11.0, 11.5]
     assert it["counts"][0].tolist() == [3, 2]
     assert it["inertia"][0] == 0 + 1 + 4 + 0 + 9
+    # the centroids moved by -1 and +1.5: shift = 1^2 + 1.5^2
+    assert it["shift"].tolist() == [3.25]
+    assert oracle.shift(it["c_new"], c0).tolist() == [3.25]
+
+
+# ---------------------------------------------------------------------------------------------
+# the shift and the stopping rule (tol semantics: a reading, so the pins below fix the reading's
+# arithmetic by hand-computed values; that the pages mean this rule stays unpinned)
+# ---------------------------------------------------------------------------------------------
+def test_shift_hand_values():
+    """sum over clusters of the squared Euclidean move, per problem: (3,4) and (1,0) -> 25 + 1.
+    Square roots (sqrt 26), norms (5 + 1), a mean (13) or a max (25) over clusters all differ."""
+    c_old = np.array([[[0.0, 0.0], [2.0, 5.0]], [[1.0, 1.0], [0.0, 0.0]]])
+    c_new = np.array([[[3.0, 4.0], [3.0, 5.0]], [[1.0, 1.0], [0.0, -2.0]]])
+    assert oracle.shift(c_new, c_old).tolist() == [26.0, 4.0]
+    assert oracle.shift(c_new[1], c_old[1]) == 4.0          # one problem -> a scalar
+    assert oracle.shift(c_old, c_old).tolist() == [0.0, 0.0]
+
+
+def _two_problem_blobs():
+    """Two 1-D problems of five points, K=2.  Problem 0: blobs at means -2 and 6, seeds -3 and 5
+    (each seed moves by 1: shift 2.0).  Problem 1: the two-blob example above (shift 3.25).  After
+    the first step both problems sit at their blob means: the second step's shift is 0."""
+    x = np.array([[[-1.0], [-2.0], [-3.0], [5.0], [7.0]],
+                  [[-10.0], [-11.0], [-12.0], [10.0], [13.0]]])
+    c0 = np.array([[[-3.0], [5.0]], [[-10.0], [10.0]]])
+    return x, c0
+
+
+def test_shift_per_problem_and_stop_on_max():
+    x, c0 = _two_problem_blobs()
+    it = oracle.lloyd_iteration(x, c0, mode="pure")
+    assert it["shift"].tolist() == [2.0, 3.25]
+    assert it["c_new"][:, :, 0].tolist() == [[-2.0, 6.0], [-11.0, 11.5]]
+    # the run stops after the first iteration whose max over problems is below tol (strict):
+    # tol=4: 3.25 < 4 -> stop after one; tol=3 and tol=3.25: go on, then 0 < tol -> stop after two.
+    # A sum over problems (5.25 >= 4), a mean or min over problems (2.625, 2.0 < 3), square roots
+    # (1.80 < 3), means or maxima over clusters (1.625, 2.25 < 3) or '<=' (3.25 <= 3.25) each
+    # change one of these counts.
+    f4 = oracle.lloyd_fit(x, c0, iters=5, tol=4.0, mode="pure")
+    assert f4["iters_done"] == 1 and f4["shift"].tolist() == [3.25]
+    for tol in (3.0, 3.25):
+        f = oracle.lloyd_fit(x, c0, iters=5, tol=tol, mode="pure")
+        assert f["iters_done"] == 2 and f["shift"].tolist() == [3.25, 0.0], tol
+    assert oracle.lloyd_fit(x, c0, iters=5, tol=0.0, mode="pure")["iters_done"] == 5
 
 
 # ---------------------------------------------------------------------------------------------

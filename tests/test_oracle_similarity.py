@@ -186,6 +186,22 @@ def test_cosine_two_directions_by_hand():
     assert f["objective"][-1].tolist() == [4.0]
 
 
+def test_dot_two_axes_by_hand():
+    """Dot product: (2,0), (4,0) pick c0=(1,0); (0,3), (0,5) pick c1=(0,1).  Means (3,0) and (0,4);
+    shift = 2^2 + 3^2 = 13; objective 2 + 4 + 3 + 5 = 14."""
+    x = np.array([[[2.0, 0.0], [4.0, 0.0], [0.0, 3.0], [0.0, 5.0]]])
+    c0 = np.array([[[1.0, 0.0], [0.0, 1.0]]])
+    it = sim.similarity_iteration(x, c0, "dot", mode="pure")
+    assert it["a"].tolist() == [[0, 0, 1, 1]]
+    assert it["c_new"].tolist() == [[[3.0, 0.0], [0.0, 4.0]]]
+    assert it["shift"].tolist() == [13.0]
+    assert it["objective"].tolist() == [14.0]
+    f = sim.similarity_fit(x, c0, "dot", iters=4, tol=13.5, mode="pure")
+    assert f["iters_done"] == 1                    # 13 < 13.5
+    f = sim.similarity_fit(x, c0, "dot", iters=4, tol=13.0, mode="pure")
+    assert f["iters_done"] == 2 and f["shift"].tolist() == [13.0, 0.0]
+
+
 def test_dot_k1_one_step():
     x = RNG.standard_normal((1, 300, 4))
     c0 = RNG.standard_normal((1, 1, 4))
