@@ -19,13 +19,17 @@ hipError_t launch_assign(int dt, const AssignCfg &cfg, const void *x, const void
                          hipStream_t s);
 size_t sort_ws_bytes(int64_t B, int64_t N, int64_t K);
 hipError_t launch_argsort(const int32_t *keys, int B, int N, int K, int32_t *out_keys, int32_t *out_vals,
-                          int32_t *counts, void *ws, hipStream_t s);
+                          int32_t *counts, int32_t *offs, int32_t *status, void *ws, hipStream_t s);
 hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s);
 size_t update_ws_bytes(int dt, int64_t B, int64_t N, int64_t D, int64_t K);
+size_t update_ctr_bytes(int dt, int64_t B, int64_t N, int64_t D, int64_t K);
+size_t update_scratch_bytes(int dt, int64_t B, int64_t N, int64_t D, int64_t K);
 bool update_refreshes_prep(int dt, int64_t B, int64_t N, int64_t D);
 hipError_t launch_update(int dt, const void *x, const int32_t *sids, const int32_t *sidx, const int32_t *counts,
                          int B, int N, int D, int K, int mode, float *C, double *shift, float *sums, int32_t *cnt,
-                         const UpdRefresh &ref, void *ws, hipStream_t s, int normalize = 0);
+                         const UpdRefresh &ref, const UpdMem &mem, hipStream_t s, int normalize = 0);
+hipError_t launch_update_ws(int dt, const void *x, const int32_t *sids, const int32_t *sidx, const int32_t *counts,
+                            int B, int N, int D, int K, float *C, double *shift, void *ws, hipStream_t s);
 hipError_t launch_finalize_acc(int dt, const float *sums, const int32_t *cnt, float *C, double *shift, double *shk,
                                const UpdRefresh &ref, int B, int K, int D, hipStream_t s, int normalize);
 hipError_t launch_row_norms(int dt, const void *x, float *out, int64_t rows, int D, hipStream_t s);
@@ -52,6 +56,15 @@ km_status_t fail(km_status_t st, const char *fmt, ...) {
 }
 
 km_status_t ok() { return KM_OK; }
+
+// The arg-sort's status word (see k_sort.hip): 0, or bits for labels outside [0, K) (1) and a
+// digit table that did not count the keys (2).
+km_status_t status_word(int32_t st, const char *who) {
+    if (st == 0) return KM_OK;
+    return fail(KM_ERR_INVALID, "%s met %s%s%s", who, (st & 1) ? "labels outside [0, K)" : "",
+                (st & 3) == 3 ? " and " : "",
+                (st & 2) ? "sorted destinations outside the rows (labels changed while it ran)" : "");
+}
 
 #define KM_HIP(call)                                                                                      \
     do {                                                                                                  \
@@ -101,7 +114,9 @@ size_t assign_ws(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
     return align256((size_t)B * KT * 32 * c.d_pad * elem_bytes(dt)) + align256((size_t)B * KT * 32 * 4);
 }
 
-size_t argsort_ws(int64_t B, int64_t N, int64_t K) { return sort_ws_bytes(B, N, K); }
+// A caller's arg-sort workspace: the status word (first 256 bytes), then the digit tables.
+constexpr size_t STATUS_BYTES = 256;
+size_t argsort_ws(int64_t B, int64_t N, int64_t K) { return STATUS_BYTES + sort_ws_bytes(B, N, K); }
 
 size_t update_ws(int dt, int64_t B, int64_t N, int64_t D, int64_t K) { return update_ws_bytes(dt, B, N, D, K); }
 
@@ -110,7 +125,8 @@ int64_t assign_wgs_per_problem(int dt, int64_t B, int64_t N, int64_t D, int64_t 
 }
 
 struct FitLayout {
-    size_t xn, a, sids, sidx, counts, prep, ring_part, ring_j, ring_s, xhat, sums, cnt, shk, scratch, total;
+    size_t xn, a, sids, sidx, counts, offs, status, updctr, prep, ring_part, ring_j, ring_s, xhat, sums, cnt, shk,
+        scratch, total;
 };
 
 // Device-resident x.  The prepared centroids persist across iterations (the update refreshes
@@ -126,6 +142,9 @@ FitLayout fit_layout(int dt, int64_t B, int64_t N, int64_t D, int64_t K, int met
     L.sids = o; o += bn4;
     L.sidx = o; o += bn4;
     L.counts = o; o += align256((size_t)B * K * 4);
+    L.offs = o; o += align256((size_t)B * K * 4);
+    L.status = o; o += STATUS_BYTES;
+    L.updctr = o; o += update_ctr_bytes(dt, B, N, D, K);
     L.prep = o; o += assign_ws(dt, B, N, D, K);
     L.ring_part = o; o += align256((size_t)RING * B * assign_wgs_per_problem(dt, B, N, D, K) * 8);
     L.ring_j = o; o += align256((size_t)RING * B * 8);
@@ -139,14 +158,15 @@ FitLayout fit_layout(int dt, int64_t B, int64_t N, int64_t D, int64_t K, int met
         }
     }
     L.scratch = o;
-    const size_t s2 = argsort_ws(B, N, K), s3 = update_ws(dt, B, N, D, K);
+    const size_t s2 = sort_ws_bytes(B, N, K), s3 = update_scratch_bytes(dt, B, N, D, K);
     o += s2 > s3 ? s2 : s3;
     L.total = o;
     return L;
 }
 
 struct HostLayout {
-    size_t stage_buf[2], cprep, xn, md, a, sids, sidx, counts, sums, cnt, shk, ring_j, ring_s, red, scratch, total;
+    size_t stage_buf[2], cprep, xn, md, a, sids, sidx, counts, offs, status, updctr, sums, cnt, shk, ring_j, ring_s,
+        red, scratch, total;
     int64_t chunk;
 };
 
@@ -156,20 +176,31 @@ int64_t host_chunk(int64_t N, int64_t chunk_points) {
     return c;
 }
 
-// Scratch of the streamed path: the arg-sort tables or the update's chunk partials of one
-// staged chunk.  Chunks hold `c` points except the last, which holds N - (nchunk-1) c; the
-// update's plan is not monotonic in the point count (its rows per wave are a power of two
-// derived from the count, so a shorter chunk can have more partial records), so the region
-// covers both sizes.
+// Per-chunk regions of the streamed path, sized for every chunk: chunks hold `c` points except
+// the last, which holds N - (nchunk-1) c.  The update's plan is not monotonic in the point count
+// (its rows per wave are a power of two derived from the count, so a shorter chunk can have more
+// partial records and counters), so each region covers both sizes.
+//   host_scratch: the arg-sort tables or the update's partial records of one staged chunk;
+//   host_updctr:  the update's arrival counters.
 size_t host_scratch(int dt, int64_t N, int64_t D, int64_t K, int64_t c) {
     auto need = [&](int64_t n) {
-        const size_t s2 = argsort_ws(1, n, K), s3 = update_ws(dt, 1, n, D, K);
+        const size_t s2 = sort_ws_bytes(1, n, K), s3 = update_scratch_bytes(dt, 1, n, D, K);
         return s2 > s3 ? s2 : s3;
     };
     size_t sc = need(c);
     const int64_t last = N - (ceil_div(N, c) - 1) * c;
     if (last != c) {
         const size_t sl = need(last);
+        if (sl > sc) sc = sl;
+    }
+    return sc;
+}
+
+size_t host_updctr(int dt, int64_t N, int64_t D, int64_t K, int64_t c) {
+    size_t sc = update_ctr_bytes(dt, 1, c, D, K);
+    const int64_t last = N - (ceil_div(N, c) - 1) * c;
+    if (last != c) {
+        const size_t sl = update_ctr_bytes(dt, 1, last, D, K);
         if (sl > sc) sc = sl;
     }
     return sc;
@@ -192,6 +223,9 @@ HostLayout host_layout(int dt, int64_t B, int64_t N, int64_t D, int64_t K, int64
     L.sids = o; o += c4;
     L.sidx = o; o += c4;
     L.counts = o; o += align256((size_t)K * 4);
+    L.offs = o; o += align256((size_t)K * 4);
+    L.status = o; o += STATUS_BYTES;
+    L.updctr = o; o += host_updctr(dt, N, D, K, c);
     L.sums = o; o += align256((size_t)B * K * D * 4);
     L.cnt = o; o += align256((size_t)B * K * 4);
     L.shk = o; o += align256((size_t)B * K * 8);
@@ -284,8 +318,7 @@ km_status_t do_assign(int dt, const void *x, const float *C, int64_t B, int64_t 
 
 km_status_t do_update(int dt, const void *x, const int32_t *sids, const int32_t *sidx, const int32_t *counts,
                       int64_t B, int64_t N, int64_t D, int64_t K, float *C, double *shift, void *ws, hipStream_t s) {
-    KM_HIP(launch_update(dt, x, sids, sidx, counts, (int)B, (int)N, (int)D, (int)K, 0, C, shift, nullptr, nullptr,
-                         UpdRefresh{}, ws, s));
+    KM_HIP(launch_update_ws(dt, x, sids, sidx, counts, (int)B, (int)N, (int)D, (int)K, C, shift, ws, s));
     return ok();
 }
 
@@ -441,8 +474,21 @@ km_status_t kmeans_argsort_ids(const int32_t *assign, int64_t B, int64_t N, int6
     KM_TRY(require_device(sorted_idx, "sorted_idx"));
     KM_TRY(require_device(counts, "counts"));
     KM_TRY(require_device(ws, "ws"));
-    KM_HIP(launch_argsort(assign, (int)B, (int)N, (int)K, sorted_ids, sorted_idx, counts, ws, (hipStream_t)stream));
+    KM_HIP(launch_argsort(assign, (int)B, (int)N, (int)K, sorted_ids, sorted_idx, counts, nullptr, (int32_t *)ws,
+                          (char *)ws + STATUS_BYTES, (hipStream_t)stream));
     return ok();
+}
+
+km_status_t kmeans_argsort_status(const void *ws, size_t ws_bytes, void *stream) {
+    KM_TRY(check_ptr(ws, "ws"));
+    if (((uintptr_t)ws & 255) != 0) return fail(KM_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (ws_bytes < STATUS_BYTES) return fail(KM_ERR_WORKSPACE, "workspace too small: %zu bytes", ws_bytes);
+    KM_TRY(check_device_arch());
+    KM_TRY(require_device(ws, "ws"));
+    int32_t st = 0;
+    KM_HIP(hipMemcpyAsync(&st, ws, 4, hipMemcpyDeviceToHost, (hipStream_t)stream));
+    KM_HIP(hipStreamSynchronize((hipStream_t)stream));
+    return status_word(st, "the arg-sort");
 }
 
 km_status_t kmeans_update(const void *x, km_dtype_t dt, const int32_t *sorted_ids, const int32_t *sorted_idx,
@@ -472,11 +518,13 @@ km_status_t kmeans_update(const void *x, km_dtype_t dt, const int32_t *sorted_id
 
 namespace {
 
-// Copy the first `n` iterations of a device ring [RING][B] into host[t0*B ...].
-km_status_t ring_to_host(const double *ring, double *host, int t0, int n, int64_t B, hipStream_t s) {
-    if (!host || n <= 0) return ok();
-    KM_HIP(hipMemcpyAsync(host + (size_t)t0 * B, ring, (size_t)n * B * 8, hipMemcpyDeviceToHost, s));
-    KM_HIP(hipStreamSynchronize(s));
+// Copy the first `n` iterations of a device ring [RING][B] into host[t0*B ...]; with `st_dev`,
+// also the arg-sort's status word into *st_host (one wait for both).
+km_status_t ring_to_host(const double *ring, double *host, int t0, int n, int64_t B, hipStream_t s,
+                         const int32_t *st_dev = nullptr, int32_t *st_host = nullptr) {
+    if (st_dev) KM_HIP(hipMemcpyAsync(st_host, st_dev, 4, hipMemcpyDeviceToHost, s));
+    if (host && n > 0) KM_HIP(hipMemcpyAsync(host + (size_t)t0 * B, ring, (size_t)n * B * 8, hipMemcpyDeviceToHost, s));
+    if (st_dev || (host && n > 0)) KM_HIP(hipStreamSynchronize(s));
     return ok();
 }
 
@@ -511,12 +559,17 @@ km_status_t fit_device(int dt, const void *x, int64_t B, int64_t N, int64_t D, i
     int32_t *sids = (int32_t *)(ws + L.sids);
     int32_t *sidx = (int32_t *)(ws + L.sidx);
     int32_t *counts = (int32_t *)(ws + L.counts);
+    int32_t *status = (int32_t *)(ws + L.status);
     char *cprep = ws + L.prep;
     float *cnh = (float *)(cprep + align256((size_t)B * KT * 32 * cfg.d_pad * elem_bytes(dt)));
     double *ring_part = (double *)(ws + L.ring_part);
     double *ring_j = (double *)(ws + L.ring_j);
     double *ring_s = (double *)(ws + L.ring_s);
     void *scratch = ws + L.scratch;
+    UpdMem mem;
+    mem.offs = (const int32_t *)(ws + L.offs);
+    mem.ctr = (int32_t *)(ws + L.updctr);
+    mem.scratch = scratch;
     const bool fused_prep = update_refreshes_prep(dt, B, N, D);
     const UpdRefresh full_ref{cprep, cnh, cfg.d_pad, (int)KT, simm ? 1 : 0};
     const UpdRefresh ref = fused_prep ? full_ref : UpdRefresh{};
@@ -535,19 +588,22 @@ km_status_t fit_device(int dt, const void *x, int64_t B, int64_t N, int64_t D, i
     if (simm) KM_HIP(launch_fill_i32((int32_t *)xn, B * N, 0, s));
     else if (xn_in) KM_HIP(launch_row_norms(dt, x, xn, B * N, (int)D, s));
     KM_HIP(launch_prep_centroids(dt, C, cprep, cnh, (int)B, (int)K, (int)D, cfg.d_pad, s, simm ? 1 : 0));
+    // the update's arrival counters start at zero; every update leaves them zero
+    KM_HIP(launch_fill_i32(mem.ctr, (int64_t)(update_ctr_bytes(dt, B, N, D, K) / 4), 0, s));
     int done = 0, flushed = 0;
+    int32_t st_host = 0;
     for (int t = 0; t < iters; ++t) {
         const int slot = t - flushed;
-        // one iteration: assign (+ per-workgroup inertia partials), arg-sort, update (+ shift,
-        // + the next iteration's prepared centroids)
+        // one iteration: assign (+ per-workgroup inertia partials), arg-sort (+ counts and the
+        // clusters' first positions), update (+ shift, + the next iteration's prepared centroids)
         KM_HIP(launch_assign(dt, cfg, xa, cprep, cnh, xn_in, a, nullptr, ring_part + (size_t)slot * B * wpb, (int)B,
                              (int)N, (int)D, (int)K, s));
-        KM_HIP(launch_argsort(a, (int)B, (int)N, (int)K, sids, sidx, counts, scratch, s));
+        KM_HIP(launch_argsort(a, (int)B, (int)N, (int)K, sids, sidx, counts, (int32_t *)mem.offs, status, scratch, s));
         if (cosine && fused_prep) {
             // one column block per row: the update finishes each cluster in place with the mean
             // direction s_k / ||s_k|| (and the shift and the refresh), like the Euclidean finish
             KM_HIP(launch_update(dt, xa, sids, sidx, counts, (int)B, (int)N, (int)D, (int)K, 0, C,
-                                 tol > 0.f ? ring_s + (size_t)slot * B : nullptr, nullptr, nullptr, full_ref, scratch,
+                                 tol > 0.f ? ring_s + (size_t)slot * B : nullptr, nullptr, nullptr, full_ref, mem,
                                  s, 1));
         } else if (cosine) {
             // sums and counts per cluster, then the mean direction (with shift and refresh)
@@ -556,12 +612,12 @@ km_status_t fit_device(int dt, const void *x, int64_t B, int64_t N, int64_t D, i
             KM_HIP(launch_fill_i32((int32_t *)sums, B * K * D, 0, s));
             KM_HIP(launch_fill_i32(cnt, B * K, 0, s));
             KM_HIP(launch_update(dt, xa, sids, sidx, counts, (int)B, (int)N, (int)D, (int)K, 1, nullptr, nullptr,
-                                 sums, cnt, UpdRefresh{}, scratch, s));
+                                 sums, cnt, UpdRefresh{}, mem, s));
             KM_HIP(launch_finalize_acc(dt, sums, cnt, C, tol > 0.f ? ring_s + (size_t)slot * B : nullptr,
                                        (double *)(ws + L.shk), full_ref, (int)B, (int)K, (int)D, s, 1));
         } else {
             KM_HIP(launch_update(dt, xa, sids, sidx, counts, (int)B, (int)N, (int)D, (int)K, 0, C,
-                                 tol > 0.f ? ring_s + (size_t)slot * B : nullptr, nullptr, nullptr, ref, scratch, s));
+                                 tol > 0.f ? ring_s + (size_t)slot * B : nullptr, nullptr, nullptr, ref, mem, s));
             if (!fused_prep && t + 1 < iters)
                 KM_HIP(launch_prep_centroids(dt, C, cprep, cnh, (int)B, (int)K, (int)D, cfg.d_pad, s, simm ? 1 : 0));
         }
@@ -573,8 +629,9 @@ km_status_t fit_device(int dt, const void *x, int64_t B, int64_t N, int64_t D, i
             stop = smax < (double)tol;
         }
         if (slot + 1 == RING || stop || t + 1 == iters) {
+            const bool last = stop || t + 1 == iters;
             KM_HIP(launch_sum_f64_rows(ring_part, (slot + 1) * (int)B, wpb, ring_j, s));
-            KM_TRY(ring_to_host(ring_j, inertia, flushed, slot + 1, B, s));
+            KM_TRY(ring_to_host(ring_j, inertia, flushed, slot + 1, B, s, last ? status : nullptr, &st_host));
             flushed = t + 1;
         }
         if (stop) break;
@@ -583,7 +640,7 @@ km_status_t fit_device(int dt, const void *x, int64_t B, int64_t N, int64_t D, i
     if (simm && inertia)
         for (int64_t i = 0; i < (int64_t)done * B; ++i) inertia[i] *= -0.5;
     if (iters_done) *iters_done = done;
-    return ok();
+    return status_word(st_host, "the fit's arg-sort");
 }
 
 struct StreamedPipe {
@@ -623,12 +680,17 @@ km_status_t fit_host(int dt, const void *xh, int64_t B, int64_t N, int64_t D, in
     int32_t *sids = (int32_t *)(ws + L.sids);
     int32_t *sidx = (int32_t *)(ws + L.sidx);
     int32_t *counts = (int32_t *)(ws + L.counts);
+    int32_t *status = (int32_t *)(ws + L.status);
     float *sums = (float *)(ws + L.sums);
     int32_t *cnt = (int32_t *)(ws + L.cnt);
     double *ring_j = (double *)(ws + L.ring_j);
     double *ring_s = (double *)(ws + L.ring_s);
     void *red = ws + L.red;
     void *scratch = ws + L.scratch;
+    UpdMem mem;
+    mem.offs = (const int32_t *)(ws + L.offs);
+    mem.ctr = (int32_t *)(ws + L.updctr);
+    mem.scratch = scratch;
     const UpdRefresh ref{cprep, cnh, cfg.d_pad, (int)KT, simm ? 1 : 0};
 
     StreamedPipe P;
@@ -663,8 +725,11 @@ km_status_t fit_host(int dt, const void *xh, int64_t B, int64_t N, int64_t D, in
     // the similarity metrics take zero point norms (their per-point value is then -2 x.c~)
     if (simm) KM_HIP(launch_fill_i32((int32_t *)xn, chunk, 0, s));
     KM_HIP(launch_prep_centroids(dt, C, cprep, cnh, (int)B, (int)K, (int)D, cfg.d_pad, s, simm ? 1 : 0));
+    // the update's arrival counters start at zero; every update leaves them zero
+    KM_HIP(launch_fill_i32(mem.ctr, (int64_t)(host_updctr(dt, N, D, K, chunk) / 4), 0, s));
     int64_t q = 0;
     int done = 0, flushed = 0;
+    int32_t st_host = 0;
     for (int t = 0; t < iters; ++t) {
         const int slot = t - flushed;
         KM_HIP(launch_fill_i32((int32_t *)sums, B * K * D, 0, s));
@@ -685,9 +750,9 @@ km_status_t fit_host(int dt, const void *xh, int64_t B, int64_t N, int64_t D, in
                                  (cfg.path == 0 && !simm) ? nullptr : xn, ac, md,
                                  nullptr, 1, (int)n, (int)D, (int)K, s));
             KM_HIP(launch_sum_f32(md, 1, n, ring_j + (size_t)slot * B + b, 1, red, s));
-            KM_HIP(launch_argsort(ac, 1, (int)n, (int)K, sids, sidx, counts, scratch, s));
+            KM_HIP(launch_argsort(ac, 1, (int)n, (int)K, sids, sidx, counts, (int32_t *)mem.offs, status, scratch, s));
             KM_HIP(launch_update(dt, xc, sids, sidx, counts, 1, (int)n, (int)D, (int)K, 1, nullptr, nullptr,
-                                 sums + (size_t)b * K * D, cnt + (size_t)b * K, UpdRefresh{}, scratch, s));
+                                 sums + (size_t)b * K * D, cnt + (size_t)b * K, UpdRefresh{}, mem, s));
             KM_HIP(hipEventRecord(P.ev_free[buf], s));
         }
         KM_HIP(launch_finalize_acc(dt, sums, cnt, C, tol > 0.f ? ring_s + (size_t)slot * B : nullptr,
@@ -700,7 +765,8 @@ km_status_t fit_host(int dt, const void *xh, int64_t B, int64_t N, int64_t D, in
             stop = smax < (double)tol;
         }
         if (slot + 1 == RING || stop || t + 1 == iters) {
-            KM_TRY(ring_to_host(ring_j, inertia, flushed, slot + 1, B, s));
+            const bool last = stop || t + 1 == iters;
+            KM_TRY(ring_to_host(ring_j, inertia, flushed, slot + 1, B, s, last ? status : nullptr, &st_host));
             flushed = t + 1;
         }
         if (stop) break;
@@ -710,7 +776,7 @@ km_status_t fit_host(int dt, const void *xh, int64_t B, int64_t N, int64_t D, in
     if (simm && inertia)
         for (int64_t i = 0; i < (int64_t)done * B; ++i) inertia[i] *= -0.5;
     if (iters_done) *iters_done = done;
-    return ok();
+    return status_word(st_host, "the fit's arg-sort");
 }
 
 }  // namespace

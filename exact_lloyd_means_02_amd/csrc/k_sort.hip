@@ -19,7 +19,14 @@
 //               lanes on consecutive positions of each digit's run.  Result: stable.
 // All tiles of one problem run on one XCD, so the short runs that neighbouring tiles write
 // into the same cache lines meet in that XCD's L2 instead of being written back piecemeal.
-// The single-pass case (all of the id in one digit) also yields the per-cluster counts.
+// The single-pass case (all of the id in one digit) also yields the per-cluster counts and
+// each cluster's first sorted position (the update's segment starts).
+//
+// Labels outside [0, K) are not sorted and not counted; the call cannot report them when it
+// returns (it does not wait for the GPU), so the kernels raise bits of a status word that the
+// first counting kernel of the call clears: 1 = a label outside [0, K), 2 = a destination outside
+// the output rows (a digit table that does not count the keys it is used with).  The output
+// positions past the sorted valid labels are then left unwritten.
 #include "common.h"
 #include "plan.h"
 
@@ -32,8 +39,9 @@ constexpr int SORT_ROUNDS = SORT_TILE / (SORT_WAVES * 64);  // 16
 // [bins][tiles] (one column per workgroup, the order the scan kernel needs).
 __global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t *__restrict__ keys, int N, int ntiles,
                                                         int shift, int bins, int32_t *__restrict__ hist,
-                                                        int tile_major) {
+                                                        int tile_major, int K, int32_t *__restrict__ status) {
     extern __shared__ int32_t s_h[];
+    if (status && shift == 0 && blockIdx.x == 0 && threadIdx.x == 0) *status = 0;  // the call's first kernel
     const int lb = xcd_remap(blockIdx.x, gridDim.x);
     const int b = lb / ntiles, t = lb - b * ntiles;
     for (int i = threadIdx.x; i < bins; i += 256) s_h[i] = 0;
@@ -51,7 +59,7 @@ __global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t *__restric
     }
 #pragma unroll
     for (int r = 0; r < PER; ++r)
-        if (kv[r] >= 0) atomicAdd(&s_h[((uint32_t)kv[r] >> shift) & mask], 1);
+        if ((uint32_t)kv[r] < (uint32_t)K) atomicAdd(&s_h[((uint32_t)kv[r] >> shift) & mask], 1);
     __syncthreads();
     int32_t *hb = hist + (size_t)b * bins * ntiles;
     if (tile_major)
@@ -151,9 +159,12 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__rest
                                                            const int32_t *__restrict__ totals, int N, int ntiles,
                                                            int shift, int bits, int32_t *__restrict__ keys_out,
                                                            int32_t *__restrict__ vals_out,
-                                                           int32_t *__restrict__ counts, int K) {
+                                                           int32_t *__restrict__ counts, int K,
+                                                           int32_t *__restrict__ offs,
+                                                           int32_t *__restrict__ status) {
     extern __shared__ int32_t s_mem[];
     __shared__ int32_t s_wsum[SORT_WAVES];
+    __shared__ int32_t s_nvalid;
     const int bins = 1 << bits;
     int32_t *s_wc = s_mem;                        // [SORT_WAVES][bins] running counts, then prefixes
     int32_t *s_off = s_wc + SORT_WAVES * bins;    // [bins] this tile's global offset of each digit
@@ -165,6 +176,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__rest
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int32_t *hb = hist + (size_t)b * bins * ntiles;
     for (int i = tid; i < SORT_WAVES * bins; i += 256) s_wc[i] = 0;
+    if (tid == 0) s_nvalid = 0;
     if constexpr (INLINE) {
         // `hist` is [tiles][bins]: thread tid sums the rows of its four consecutive digits
         // (16-byte loads, all issued before the sums): the total over all tiles and the sum over
@@ -214,6 +226,9 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__rest
         for (int i = tid; i < bins; i += 256) s_off[i] += hb[(size_t)i * ntiles + t];
     }
     __syncthreads();
+    // tile 0 starts every digit at its global offset: the clusters' first sorted positions
+    if (offs && t == 0)
+        for (int i = tid; i < bins && i < K; i += 256) offs[(size_t)b * K + i] = s_off[i];
 
     const size_t base = (size_t)b * N;
     const int tile0 = t * SORT_TILE + w * (SORT_ROUNDS * 64);
@@ -223,19 +238,23 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__rest
     for (int r = 0; r < SORT_ROUNDS; ++r) {
         const int i = tile0 + r * 64 + lane;
         const bool ok = i < N;
-        key[r] = ok ? keys_in[base + i] : 0;
+        key[r] = ok ? keys_in[base + i] : -1;
         val[r] = ok ? (vals_in ? vals_in[base + i] : i) : 0;
     }
     const uint64_t lt = lanemask_lt();
     int32_t *wc = s_wc + w * bins;
+    int nvalid = 0;
+    bool bad = false;
 #pragma unroll
     for (int r = 0; r < SORT_ROUNDS; ++r) {
         const int i = tile0 + r * 64 + lane;
-        const bool ok = i < N;
+        const bool ok = (uint32_t)key[r] < (uint32_t)K;  // in range (positions past N hold -1)
+        bad |= i < N && !ok;
         const uint32_t dg = ((uint32_t)key[r] >> shift) & mask;
         // peers: the lanes whose digit equals this lane's, one ballot per digit bit; a lane
         // keeps the ballot where its bit is set and its complement where it is clear
         const uint64_t okm = __ballot(ok);
+        nvalid += __popcll(okm);
         uint32_t p_lo = (uint32_t)okm, p_hi = (uint32_t)(okm >> 32);
 #pragma unroll
         for (int bit = 0; bit < BITS; ++bit) {
@@ -252,6 +271,8 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__rest
         if (ok && before == 0) wc[dg] = wbase + __popcll(peers);
         pos[r] = wbase + before;
     }
+    if (lane == 0) atomicAdd(&s_nvalid, nvalid);
+    if (status && __ballot(bad) != 0ull && lane == 0) atomicOr(status, 1);
     __syncthreads();
     // exclusive prefix over waves, per digit; the digit's total in this tile
     for (int i = tid; i < bins; i += 256) {
@@ -269,8 +290,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__rest
     // lay the tile out in (digit, index) order
 #pragma unroll
     for (int r = 0; r < SORT_ROUNDS; ++r) {
-        const int i = tile0 + r * 64 + lane;
-        if (i < N) {
+        if ((uint32_t)key[r] < (uint32_t)K) {
             const uint32_t dg = ((uint32_t)key[r] >> shift) & mask;
             const int lp = s_ls[dg] + wc[dg] + pos[r];
             s_k[lp] = key[r];
@@ -278,25 +298,30 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__rest
         }
     }
     __syncthreads();
-    const int tile_n = min(SORT_TILE, N - t * SORT_TILE);
+    const int tile_n = s_nvalid;  // the valid keys of the tile, laid out above
 #pragma unroll 4
     for (int e = tid; e < tile_n; e += 256) {
         const int32_t k = s_k[e];
         const uint32_t dg = ((uint32_t)k >> shift) & mask;
         const int dst = s_off[dg] + (e - s_ls[dg]);
-        // in range whenever the table counts these keys; the check keeps a table that does not
-        // (keys changed between the passes by a concurrent writer) from writing outside the rows
+        // in range whenever the table counts the keys it is used with; a table that does not
+        // (keys changed between the kernels by a concurrent writer) raises status bit 2 instead
+        // of writing outside the rows
         if ((unsigned)dst < (unsigned)N) {
             keys_out[base + dst] = k;
             vals_out[base + dst] = s_v[e];
+        } else if (status) {
+            atomicOr(status, 2);
         }
     }
 }
 
 // Counts per cluster from the sorted ids: +end at a segment's last position, -start at its
-// first (each cluster gets exactly one of each, so integer atomics give an exact result).
+// first (each cluster gets exactly one of each, so integer atomics give an exact result); the
+// first position itself is the cluster's segment start.
 __global__ __launch_bounds__(256) void segment_counts_kernel(const int32_t *__restrict__ sids, int64_t total, int N,
-                                                             int K, int32_t *__restrict__ counts) {
+                                                             int K, int32_t *__restrict__ counts,
+                                                             int32_t *__restrict__ offs) {
     const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (gi >= total) return;
     const int64_t b = gi / N;
@@ -305,7 +330,10 @@ __global__ __launch_bounds__(256) void segment_counts_kernel(const int32_t *__re
     if (k < 0 || k >= K) return;
     int32_t *cb = counts + b * K;
     if (p == N - 1 || sids[gi + 1] != k) atomicAdd(&cb[k], p + 1);
-    if (p == 0 || sids[gi - 1] != k) atomicSub(&cb[k], p);
+    if (p == 0 || sids[gi - 1] != k) {
+        atomicSub(&cb[k], p);
+        if (offs) offs[b * K + k] = p;
+    }
 }
 
 __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t *__restrict__ p, int64_t n, int32_t v) {
@@ -323,11 +351,11 @@ hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s) {
 template <bool INLINE>
 static hipError_t launch_scatter(int bits, dim3 grid, size_t lds, hipStream_t s, const int32_t *kin, const int32_t *vin,
                            const int32_t *hist, const int32_t *totals, int N, int ntiles, int shift, int32_t *ko,
-                           int32_t *vo, int32_t *cnt, int K) {
+                           int32_t *vo, int32_t *cnt, int K, int32_t *offs, int32_t *status) {
 #define FKM_SCATTER(B_)                                                                                            \
     case B_:                                                                                                       \
         sort_scatter_kernel<INLINE, B_><<<grid, dim3(256), lds, s>>>(kin, vin, hist, totals, N, ntiles, shift, bits, \
-                                                                      ko, vo, cnt, K);                             \
+                                                                      ko, vo, cnt, K, offs, status);               \
         break;
     static_assert(SORT_MAX_BITS == 10, "one instance per digit width");
     switch (bits) {
@@ -346,9 +374,10 @@ size_t sort_ws_bytes(int64_t B, int64_t N, int64_t K) {
     return bytes;
 }
 
-// keys [B][N] -> sorted keys / point indices; counts optional.
+// keys [B][N] -> sorted keys / point indices; counts, first positions ([B][K], only with
+// counts) and the status word optional.
 hipError_t launch_argsort(const int32_t *keys, int B, int N, int K, int32_t *out_keys, int32_t *out_vals,
-                          int32_t *counts, void *ws, hipStream_t s) {
+                          int32_t *counts, int32_t *offs, int32_t *status, void *ws, hipStream_t s) {
     const SortCfg c = plan_sort(N, K);
     char *wp = (char *)ws;
     int32_t *hist = (int32_t *)wp;
@@ -370,18 +399,20 @@ hipError_t launch_argsort(const int32_t *keys, int B, int N, int K, int32_t *out
         int32_t *ko = to_out ? out_keys : tk;
         int32_t *vo = to_out ? out_vals : tv;
         int32_t *cnt_out = (counts && c.passes == 1) ? counts : nullptr;
+        int32_t *offs_out = (offs && c.passes == 1) ? offs : nullptr;
+        int32_t *st = pass == 0 ? status : nullptr;
         const size_t lds = ((size_t)(SORT_WAVES + 2) * c.bins + 2 * SORT_TILE) * 4;
         const bool inline_offsets = c.bins >= 4 && c.ntiles <= SORT_INLINE_TILES;
         sort_hist_kernel<<<dim3(B * c.ntiles), dim3(256), c.bins * 4, s>>>(kin, N, c.ntiles, shift, c.bins, hist,
-                                                                            inline_offsets ? 1 : 0);
+                                                                            inline_offsets ? 1 : 0, K, st);
         if (inline_offsets) {
             const hipError_t e = launch_scatter<true>(c.bits, dim3(B * c.ntiles), lds, s, kin, vin, hist, nullptr, N,
-                                                      c.ntiles, shift, ko, vo, cnt_out, K);
+                                                      c.ntiles, shift, ko, vo, cnt_out, K, offs_out, st);
             if (e != hipSuccess) return e;
         } else {
             sort_rowscan_kernel<<<dim3(B * c.bins), dim3(256), 0, s>>>(hist, c.bins, c.ntiles, totals);
             const hipError_t e = launch_scatter<false>(c.bits, dim3(B * c.ntiles), lds, s, kin, vin, hist, totals, N,
-                                                       c.ntiles, shift, ko, vo, cnt_out, K);
+                                                       c.ntiles, shift, ko, vo, cnt_out, K, offs_out, st);
             if (e != hipSuccess) return e;
         }
         kin = ko;
@@ -392,7 +423,7 @@ hipError_t launch_argsort(const int32_t *keys, int B, int N, int K, int32_t *out
         if (e != hipSuccess) return e;
         const int64_t total = (int64_t)B * N;
         segment_counts_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s>>>(out_keys, total, N, K,
-                                                                                         counts);
+                                                                                         counts, offs);
     }
     return hipGetLastError();
 }

@@ -2,9 +2,13 @@
 // the sorted order is cut into chunks; each wave takes one chunk, walks its cluster-id
 // segments, gathers the rows of the unpermuted x through sorted_idx, sums each segment on
 // chip in fp32, and writes once per segment.  The digest issues one atomic per segment; here
-// a segment that lies inside one chunk is finished by its wave (c_k = s_k / n_k written
-// directly), and a segment cut by chunk edges leaves one fp32 partial per chunk that a
-// second kernel adds in chunk order.  No float atomics, so the result is deterministic.
+// a segment that lies inside one chunk (or ends in the next one) is finished by its wave
+// (c_k = s_k / n_k written directly).  A longer segment leaves one fp32 partial per chunk; the
+// waves of its chunks count their arrivals with an integer atomic per group of chunks, and the
+// last wave to arrive adds the group's partials in chunk order, then (for segments over more
+// than one group) the last group to arrive adds the group sums in group order and finishes the
+// cluster.  The order of every float sum is fixed by the chunk layout alone, not by which wave
+// arrives last, so the result is deterministic; there are no float atomics and no second kernel.
 //
 // Lane layout: a row is covered by `lanes` lanes (a power of two) holding 16-byte vectors
 // (or scalars when D is not a multiple of the vector width); one wave load instruction
@@ -32,13 +36,16 @@ struct UpdArgs {
     int dt;
     float *C;          // [B][K][D] in/out (mode 0)
     // optional fp64 partials of sum_k ||c_new - c_old||^2, each written once (no atomics):
-    // mode 0: [B*nch][ncb + 1] (column block of a chunk's wave; last slot: the chunk's cut
-    // segment, finished by the combine kernel); finalize: [B][K], one per cluster.
+    // mode 0: [B*nch][2*ncb]: slot cb, the clusters a chunk's wave finished in column block cb;
+    // slot ncb + cb, the long segment that starts in the chunk (written by the wave that
+    // finishes it, 0 when none starts there); finalize: [B][K], one per cluster.
     double *shp;
     float *sums;       // [B][K][D] (mode 1)
     int32_t *cnt;      // [B][K]    (mode 1)
-    float *part;       // [B*nch][2][D]
-    int32_t *rec;      // [B*nch][4]: cluster of slot 0 (cut on entry), of slot 1 (cut on exit), start of slot 1
+    float *part;       // [B*nch][2][D]: slot 0, the segment cut on entry; slot 1, cut on exit
+    const int32_t *offs;  // [B][K] first sorted position of each cluster's segment
+    int32_t *gcnt;     // [B*nch][2][ncb] arrivals per chunk group (zero between launches)
+    int32_t *scnt;     // [B][K][ncb] arrivals of group sums per long segment (zero between launches)
     // optional (mode 0): refresh the assign kernels' prepared centroids for every finished
     // cluster (same layout as the prep kernel); clusters without points keep theirs.
     void *cprep;
@@ -209,6 +216,140 @@ __device__ inline float finish_cluster(const UpdArgs &a, int b, int k, int c0, i
     return d2;
 }
 
+// Finish column d of cluster k of problem b from its sum `s` (a long segment's finishing wave).
+// den: n_k, or ||s_k|| with a.normalize (mode 0).  Returns (c_new - c_old)^2 (mode 0).
+__device__ inline float finish_col(const UpdArgs &a, int b, int k, size_t rowo, int d, float s, float den,
+                                   float &cn2) {
+    if (a.mode == 0) {
+        const float old = a.C[rowo + d];
+        const float nw = s / den;
+        a.C[rowo + d] = nw;
+        if (a.cprep) cn2 += prep_store_elem(a, b, k, d, nw);
+        return (nw - old) * (nw - old);
+    }
+    a.sums[rowo + d] += s;
+    return 0.f;
+}
+
+// Chunks per first-level group of a long segment's partials.
+constexpr int UPD_GROUP = 32;
+
+// Column d of the sum of m partial records: those of chunks first, first + stride, ... of the
+// problem whose chunk 0 is `cbase` (the segment's first chunk c_first holds it in slot 1, every
+// later chunk in slot 0), added in that order; eight loads in flight.
+__device__ inline float sum_pieces(const UpdArgs &a, size_t cbase, int c_first, int first, int stride, int m,
+                                   int d) {
+    float s = 0.f;
+    int i = 0;
+    for (; i + 8 <= m; i += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int ch = first + (i + u) * stride;
+            v[u] = a.part[((cbase + ch) * 2 + (ch == c_first ? 1 : 0)) * a.D + d];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; i < m; ++i) {
+        const int ch = first + i * stride;
+        s += a.part[((cbase + ch) * 2 + (ch == c_first ? 1 : 0)) * a.D + d];
+    }
+    return s;
+}
+
+// Finish long segment k (n points) in column block cbi from the sum of its m partial records
+// (first, stride as in sum_pieces).  The whole wave calls it; lanes take the block's columns.
+__device__ inline void finish_long(const UpdArgs &a, int b, int k, int cbi, int n, size_t cbase, int c_first,
+                                   int first, int stride, int m, int lane) {
+    const int c0 = cbi * a.cb_elems;
+    const int c1 = min(a.D, c0 + a.cb_elems);
+    const size_t rowo = ((size_t)b * a.K + k) * a.D;
+    double *shp_slot = a.shp ? a.shp + (cbase + c_first) * (2 * a.ncb) + a.ncb + cbi : nullptr;
+    float den = (float)n;
+    if (a.mode == 0 && a.normalize) {
+        // the mean direction needs ||s|| first (one column block per row here): one pass for the
+        // norm, then the same sums again
+        float ss = 0.f;
+        for (int d = c0 + lane; d < c1; d += 64) {
+            const float v = sum_pieces(a, cbase, c_first, first, stride, m, d);
+            ss += v * v;
+        }
+        for (int off = 1; off < 64; off <<= 1) ss += __shfl_xor(ss, off);
+        den = sqrtf(ss);
+        if (!(den > 0.f)) {  // uniform over the wave: the zero sum keeps the centroid
+            if (shp_slot && lane == 0) *shp_slot = 0.0;
+            return;
+        }
+    }
+    float d2 = 0.f, cn2 = 0.f;
+    for (int d = c0 + lane; d < c1; d += 64)
+        d2 += finish_col(a, b, k, rowo, d, sum_pieces(a, cbase, c_first, first, stride, m, d), den, cn2);
+    if (a.mode == 0) {
+        for (int off = 1; off < 64; off <<= 1) {
+            d2 += __shfl_xor(d2, off);
+            cn2 += __shfl_xor(cn2, off);
+        }
+        if (shp_slot && lane == 0) *shp_slot = (double)d2;
+        if (a.cprep && lane == 0) a.cnh[(size_t)b * a.KT * 32 + k] = refreshed_half_norm(a, cn2);
+    } else if (cbi == 0 && lane == 0) {
+        a.cnt[(size_t)b * a.K + k] += n;
+    }
+}
+
+// Called by the whole wave of chunk c (problem b, column block cbi) right after it wrote its
+// partial record of long segment k.  The segment's chunks c_first..c_last form groups of
+// UPD_GROUP; the last wave of a group to arrive adds the group's partials.  With one group that
+// wave finishes the cluster; otherwise it leaves the group sum in the record of the group's first
+// chunk, and the last group to arrive adds the group sums and finishes the cluster.  The release
+// fence before each arrival publishes the records written before it; the acquire fence after
+// it makes every record of the group visible to the wave that goes on.  The counters return to
+// zero for the next launch.
+__device__ inline void arrive_long(const UpdArgs &a, int b, int c, int cbi, int k, int lane) {
+    // counts and first positions come from the arg-sort of the same labels; clamped so that
+    // inconsistent inputs give wrong numbers, not accesses outside the records and counters
+    const int n = max(1, a.counts[(size_t)b * a.K + k]);
+    const int s0 = min(max(a.offs[(size_t)b * a.K + k], 0), a.N - 1);
+    const int c_first = s0 / a.R;
+    const int c_last = (int)min((int64_t)a.nch - 1, ((int64_t)s0 + n - 1) / a.R);
+    if (c < c_first || c > c_last) return;
+    const int P = c_last - c_first + 1;
+    const int j = (c - c_first) / UPD_GROUP;
+    const int gfirst = c_first + j * UPD_GROUP;
+    const int m = min(UPD_GROUP, P - j * UPD_GROUP);
+    const int gslot = j == 0 ? 1 : 0;
+    const size_t cbase = (size_t)b * a.nch;
+    int32_t *ctr = a.gcnt + ((cbase + gfirst) * 2 + gslot) * a.ncb + cbi;
+    __threadfence();
+    int old = 0;
+    if (lane == 0) old = atomicAdd(ctr, 1);
+    old = __shfl(old, 0);
+    if (old != m - 1) return;
+    __threadfence();
+    if (lane == 0) *ctr = 0;
+    const int ngroups = (P + UPD_GROUP - 1) / UPD_GROUP;
+    if (ngroups == 1) {
+        finish_long(a, b, k, cbi, n, cbase, c_first, c_first, 1, P, lane);
+        return;
+    }
+    const int c0 = cbi * a.cb_elems;
+    const int c1 = min(a.D, c0 + a.cb_elems);
+    float *grec = a.part + ((cbase + gfirst) * 2 + gslot) * a.D;
+    for (int d = c0 + lane; d < c1; d += 64) {
+        const float v = sum_pieces(a, cbase, c_first, gfirst, 1, m, d);
+        grec[d] = v;  // every piece of the group (this record too) was read above
+    }
+    __threadfence();
+    int32_t *sctr = a.scnt + ((size_t)b * a.K + k) * a.ncb + cbi;
+    old = 0;
+    if (lane == 0) old = atomicAdd(sctr, 1);
+    old = __shfl(old, 0);
+    if (old != ngroups - 1) return;
+    __threadfence();
+    if (lane == 0) *sctr = 0;
+    finish_long(a, b, k, cbi, n, cbase, c_first, c_first, UPD_GROUP, ngroups, lane);
+}
+
 // SHIFT: a.shp is set (mode 0 with shift partials wanted); a separate instance keeps the
 // register budget of the common case free of the old-centroid prefetch.
 template <int DT, int V, int VPL, bool SHIFT>
@@ -274,9 +415,9 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
     bool cin = p0 > 0 && sb[p0 - 1] == kraw;
     // Segment ownership: a segment that ends within the chunk after the one where it starts is
     // summed entirely by the wave of its first chunk (which runs past its chunk end for it);
-    // only segments spanning three or more chunks leave partials for the combine kernel.  A
-    // wave whose chunk starts inside a segment finds the segment's end from the ids alone and
-    // its start from the count, and skips it when the previous chunk's wave owns it.
+    // only segments spanning three or more chunks leave partials (the long segments).  A wave
+    // whose chunk starts inside a segment finds the segment's end from the ids alone and its
+    // start from the count, and skips it when the previous chunk's wave owns it.
     bool done = false;
     if (cin) {
         int e = p;
@@ -319,7 +460,9 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
     };
     fetch_cold(kraw);
     int seg_start = p;
-    int rec0 = -1, rec1 = -1, recps = 0;
+    // long segments this chunk holds a partial of: cut on entry (k_in), cut on exit (k_out); the
+    // wave arrives at them after its walk, when the walk's registers are free
+    int k_in = -1, k_out = -1;
     float d2acc = 0.f;
     float acc[VPL][V];
 #pragma unroll
@@ -327,8 +470,8 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
 #pragma unroll
         for (int e = 0; e < V; ++e) acc[i][e] = 0.f;
 
-    // The summed segment ends: add the row groups and finish the cluster, or leave a partial
-    // for the combine kernel when the segment is cut by a chunk edge (cin / cout).
+    // The summed segment ends: add the row groups and finish the cluster, or, for a segment cut
+    // by a chunk edge (cin / cout), write this chunk's partial.
     auto end_segment = [&](int kr, int n, bool s_cout) {
         // sum the row groups: lanes r, r + lanes, r + 2*lanes, ... hold the same columns
         for (int off = a.lanes; off < 64; off <<= 1) {
@@ -357,7 +500,8 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
                         if (e0 + e < a.D) dst[e0 + e] = acc[i][e];
                 }
             }
-            if (slot == 0) rec0 = k; else { rec1 = k; recps = seg_start; }
+            if (slot == 0) k_in = k;
+            else k_out = k;
         }
     };
     constexpr int U = upd_unroll<VPL>();
@@ -441,207 +585,14 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
     if (SHIFT) {  // mode 0
         double d = (double)d2acc;
         for (int off = 1; off < 64; off <<= 1) d += __shfl_xor(d, off);
-        if (lane == 0) a.shp[(size_t)chunk * (a.ncb + 1) + cbi] = d;
-    }
-    if (cbi == 0 && lane == 0) {
-        int32_t *rc = a.rec + chunk * 4;
-        rc[0] = rec0;
-        rc[1] = rec1;
-        rc[2] = recps;
-        rc[3] = 0;
-    }
-}
-
-// Finish column d of cluster k of problem b from its sum `s`, within a combine kernel.
-// den: n_k, or ||s_k|| with a.normalize (mode 0).
-__device__ inline float combine_finish_col(const UpdArgs &a, int b, int k, size_t rowo, int d, float s, float den,
-                                           float &cn2) {
-    if (a.mode == 0) {
-        const float old = a.C[rowo + d];
-        const float nw = s / den;
-        a.C[rowo + d] = nw;
-        if (a.cprep) cn2 += prep_store_elem(a, b, k, d, nw);
-        return (nw - old) * (nw - old);
-    }
-    a.sums[rowo + d] += s;
-    return 0.f;
-}
-
-// Segments that span three or more chunks: add the chunk partials in chunk order and finish
-// the cluster.  A workgroup covers COMBINE_CHUNKS consecutive chunks; their records are read
-// at once (most chunks start no such segment).  A segment spread over at most 8 chunks is
-// finished by one wave (lanes over columns, pieces in order); a longer one by the whole
-// workgroup (piece groups x columns, fixed-order tree).  Deterministic either way.
-constexpr int COMBINE_WAVE_MAX = 8;
-constexpr int COMBINE_CHUNKS = 16;
-
-__global__ __launch_bounds__(256) void upd_combine_kernel(UpdArgs a, int64_t nchunks) {
-    __shared__ float s_red[256];
-    __shared__ int s_kk[COMBINE_CHUNKS], s_np[COMBINE_CHUNKS], s_nk[COMBINE_CHUNKS];
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int64_t chunk0 = (int64_t)blockIdx.x * COMBINE_CHUNKS;
-    if (t < COMBINE_CHUNKS) {
-        int kv = -1, npv = 0, nkv = 1;
-        const int64_t chunk = chunk0 + t;
-        if (chunk < nchunks) {
-            const int32_t *rc = a.rec + chunk * 4;
-            const int k = rc[1];
-            if (k >= 0) {
-                const int b = (int)(chunk / a.nch);
-                const int c = (int)(chunk - (int64_t)b * a.nch);
-                int nk = a.counts[(size_t)b * a.K + k];
-                nk = nk < 1 ? 1 : nk;
-                int c_last = (int)(((int64_t)rc[2] + nk - 1) / a.R);
-                c_last = c_last > a.nch - 1 ? a.nch - 1 : (c_last < c ? c : c_last);
-                kv = k;
-                npv = c_last - c + 1;
-                nkv = nk;
-            }
-        }
-        s_kk[t] = kv;
-        s_np[t] = npv;
-        s_nk[t] = nkv;
-    }
-    __syncthreads();
-    const int D = a.D;
-    // long segments: the whole workgroup
-    for (int i = 0; i < COMBINE_CHUNKS; ++i) {
-        const int kk = s_kk[i], np = s_np[i], nkk = s_nk[i];
-        if (kk < 0 || np <= COMBINE_WAVE_MAX) continue;  // uniform over the workgroup
-        const int64_t chunk = chunk0 + i;
-        const int b = (int)(chunk / a.nch);
-        const size_t rowo = ((size_t)b * a.K + kk) * D;
-        int DC = 1;
-        while (DC < D && DC < 256) DC <<= 1;
-        const int PG = 256 / DC;
-        const int pg = t / DC, dcol = t - pg * DC;
-        // column d's sum over the pieces, left in s_red[dcol] (fixed-order tree; every thread calls)
-        auto column_sum = [&](int d) {
-            float sum = 0.f;
-            if (d < D) {
-                // pieces pg, pg + PG, ... in order; eight loads in flight before they are added
-                int j = pg;
-                for (; j + 7 * PG < np; j += 8 * PG) {
-                    float pv[8];
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        const int jj = j + u * PG;
-                        pv[u] = a.part[((size_t)(chunk + jj) * 2 + (jj == 0 ? 1 : 0)) * D + d];
-                    }
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) sum += pv[u];
-                }
-                for (; j < np; j += PG) sum += a.part[((size_t)(chunk + j) * 2 + (j == 0 ? 1 : 0)) * D + d];
-            }
-            s_red[t] = sum;
-            __syncthreads();
-            for (int off = PG / 2; off >= 1; off >>= 1) {
-                if (pg < off) s_red[t] += s_red[t + off * DC];
-                __syncthreads();
-            }
-        };
-        const int dend = ((D + DC - 1) / DC) * DC;
-        float den = (float)nkk;
-        if (a.mode == 0 && a.normalize) {
-            // the mean direction needs ||s|| first: one pass for the norm, then the same sums again
-            float ss = 0.f;
-            for (int d = dcol; d < dend; d += DC) {
-                column_sum(d);
-                if (pg == 0 && d < D) ss += s_red[dcol] * s_red[dcol];
-                __syncthreads();
-            }
-            s_red[t] = ss;
-            __syncthreads();
-            for (int off = 128; off >= 1; off >>= 1) {
-                if (t < off) s_red[t] += s_red[t + off];
-                __syncthreads();
-            }
-            den = sqrtf(s_red[0]);
-            __syncthreads();
-            if (!(den > 0.f)) {  // uniform: the zero sum keeps the centroid
-                if (t == 0 && a.shp) a.shp[(size_t)chunk * (a.ncb + 1) + a.ncb] = 0.0;
-                continue;
-            }
-        }
-        float d2 = 0.f, cn2 = 0.f;
-        for (int d = dcol; d < dend; d += DC) {
-            column_sum(d);
-            if (pg == 0 && d < D) d2 += combine_finish_col(a, b, kk, rowo, d, s_red[dcol], den, cn2);
-            __syncthreads();
-        }
-        if (a.mode == 0) {
-            s_red[t] = d2;
-            __syncthreads();
-            for (int off = 128; off >= 1; off >>= 1) {
-                if (t < off) s_red[t] += s_red[t + off];
-                __syncthreads();
-            }
-            if (t == 0 && a.shp) a.shp[(size_t)chunk * (a.ncb + 1) + a.ncb] = (double)s_red[0];
-            __syncthreads();
-            s_red[t] = cn2;
-            __syncthreads();
-            for (int off = 128; off >= 1; off >>= 1) {
-                if (t < off) s_red[t] += s_red[t + off];
-                __syncthreads();
-            }
-            if (t == 0 && a.cprep) a.cnh[(size_t)b * a.KT * 32 + kk] = refreshed_half_norm(a, s_red[0]);
-            __syncthreads();
-        } else if (t == 0) {
-            a.cnt[(size_t)b * a.K + kk] += nkk;
+        if (lane == 0) {
+            a.shp[(size_t)chunk * (2 * a.ncb) + cbi] = d;
+            // a long segment starting here has its shift written by the wave that finishes it
+            if (k_out < 0) a.shp[(size_t)chunk * (2 * a.ncb) + a.ncb + cbi] = 0.0;
         }
     }
-    // short segments (and the shift slot of every chunk): one wave each
-    for (int i = w; i < COMBINE_CHUNKS; i += 4) {  // 4 waves per workgroup
-        const int64_t chunk = chunk0 + i;
-        if (chunk >= nchunks) break;
-        const int kk = s_kk[i], np = s_np[i], nkk = s_nk[i];
-        if (kk < 0) {
-            if (a.shp && lane == 0) a.shp[(size_t)chunk * (a.ncb + 1) + a.ncb] = 0.0;
-            continue;
-        }
-        if (np > COMBINE_WAVE_MAX) continue;
-        const int b = (int)(chunk / a.nch);
-        const size_t rowo = ((size_t)b * a.K + kk) * D;
-        // column d's sum over the pieces, in chunk order; every piece is loaded before the sum
-        auto column_sum = [&](int d) {
-            float pv[COMBINE_WAVE_MAX];
-            pv[0] = a.part[((size_t)chunk * 2 + 1) * D + d];
-#pragma unroll
-            for (int j = 1; j < COMBINE_WAVE_MAX; ++j)
-                pv[j] = j < np ? a.part[((size_t)(chunk + j) * 2) * D + d] : 0.f;
-            float sum = pv[0];
-#pragma unroll
-            for (int j = 1; j < COMBINE_WAVE_MAX; ++j)
-                if (j < np) sum += pv[j];
-            return sum;
-        };
-        float den = (float)nkk;
-        if (a.mode == 0 && a.normalize) {
-            float ss = 0.f;
-            for (int d = lane; d < D; d += 64) {
-                const float sum = column_sum(d);
-                ss += sum * sum;
-            }
-            for (int off = 1; off < 64; off <<= 1) ss += __shfl_xor(ss, off);
-            den = sqrtf(ss);
-            if (!(den > 0.f)) {  // uniform: the zero sum keeps the centroid
-                if (lane == 0 && a.shp) a.shp[(size_t)chunk * (a.ncb + 1) + a.ncb] = 0.0;
-                continue;
-            }
-        }
-        float d2 = 0.f, cn2 = 0.f;
-        for (int d = lane; d < D; d += 64) d2 += combine_finish_col(a, b, kk, rowo, d, column_sum(d), den, cn2);
-        if (a.mode == 0) {
-            for (int off = 1; off < 64; off <<= 1) {
-                d2 += __shfl_xor(d2, off);
-                cn2 += __shfl_xor(cn2, off);
-            }
-            if (lane == 0 && a.shp) a.shp[(size_t)chunk * (a.ncb + 1) + a.ncb] = (double)d2;
-            if (lane == 0 && a.cprep) a.cnh[(size_t)b * a.KT * 32 + kk] = refreshed_half_norm(a, cn2);
-        } else if (lane == 0) {
-            a.cnt[(size_t)b * a.K + kk] += nkk;
-        }
-    }
+    if (k_in >= 0) arrive_long(a, b, c, cbi, k_in, lane);
+    if (k_out >= 0) arrive_long(a, b, c, cbi, k_out, lane);
 }
 
 // After the accumulating update (streamed chunks, or the cosine fit): c_k <- sums_k / cnt_k
@@ -686,12 +637,24 @@ __global__ __launch_bounds__(256) void upd_finalize_acc_kernel(UpdArgs a, int64_
     if (lane == 0 && a.cprep) a.cnh[(size_t)b * a.KT * 32 + k] = refreshed_half_norm(a, cn2);
 }
 
-size_t update_ws_bytes(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
+// Update memory: the arrival counters (zero between launches), the segments' first positions
+// and a scratch region for the partial records and shift partials.
+size_t update_ctr_bytes(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
+    const UpdCfg u = plan_update(dt, B, N, D);
+    const int64_t chunks = B * u.nch;
+    return align256((size_t)chunks * 2 * u.ncb * 4) + align256((size_t)B * K * u.ncb * 4);
+}
+
+size_t update_scratch_bytes(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
     const UpdCfg u = plan_update(dt, B, N, D);
     const int64_t chunks = B * u.nch;
     (void)K;
-    return align256((size_t)chunks * 2 * D * 4) + align256((size_t)chunks * 4 * 4) +
-           align256((size_t)chunks * (u.ncb + 1) * 8);
+    return align256((size_t)chunks * 2 * u.ncb * 8) + align256((size_t)chunks * 2 * D * 4);
+}
+
+// A caller's update workspace: counters, first positions [B][K], scratch.
+size_t update_ws_bytes(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
+    return update_ctr_bytes(dt, B, N, D, K) + align256((size_t)B * K * 4) + update_scratch_bytes(dt, B, N, D, K);
 }
 
 template <int DT, bool SHIFT>
@@ -718,16 +681,17 @@ static hipError_t launch_segsum_dt(const UpdArgs &a, int vec, int vpl, int64_t w
 
 static UpdArgs make_args(int dt, const void *x, const int32_t *sids, const int32_t *sidx, const int32_t *counts,
                          int B, int N, int D, int K, int mode, float *C, bool want_shift, float *sums, int32_t *cnt,
-                         const UpdRefresh &ref, void *ws) {
+                         const UpdRefresh &ref, const UpdMem &mem) {
     const UpdCfg u = plan_update(dt, B, N, D);
     const int64_t chunks = (int64_t)B * u.nch;
-    char *wp = (char *)ws;
+    char *wp = (char *)mem.scratch;
     UpdArgs a{};
-    a.part = (float *)wp;
-    wp += align256((size_t)chunks * 2 * D * 4);
-    a.rec = (int32_t *)wp;
-    wp += align256((size_t)chunks * 4 * 4);
     a.shp = (mode == 0 && want_shift) ? (double *)wp : nullptr;
+    wp += align256((size_t)chunks * 2 * u.ncb * 8);
+    a.part = (float *)wp;
+    a.gcnt = mem.ctr;
+    a.scnt = mem.ctr + align256((size_t)chunks * 2 * u.ncb * 4) / 4;
+    a.offs = mem.offs;
     a.x = x;
     a.sids = sids;
     a.sidx = sidx;
@@ -756,29 +720,69 @@ static UpdArgs make_args(int dt, const void *x, const int32_t *sids, const int32
 
 bool update_refreshes_prep(int dt, int64_t B, int64_t N, int64_t D) { return plan_update(dt, B, N, D).ncb == 1; }
 
+// Before an update whose caller has no first positions from the arg-sort: each cluster's first
+// sorted position (where the sorted id changes; clusters without points get none, and none is
+// read for them), and the arrival counters set to zero.
+__global__ __launch_bounds__(256) void upd_prologue_kernel(const int32_t *__restrict__ sids, int64_t total, int N,
+                                                           int K, int32_t *__restrict__ offs,
+                                                           int32_t *__restrict__ ctr, int64_t nctr) {
+    const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = gi; i < nctr; i += stride) ctr[i] = 0;
+    if (gi >= total) return;
+    const int64_t b = gi / N;
+    const int p = (int)(gi - b * N);
+    const int32_t k = sids[gi];
+    if (k < 0 || k >= K) return;
+    if (p == 0 || sids[gi - 1] != k) offs[b * K + k] = p;
+}
+
+hipError_t launch_update_prologue(const int32_t *sids, int B, int N, int K, int32_t *offs, int32_t *ctr,
+                                  size_t ctr_bytes, hipStream_t s) {
+    const int64_t total = (int64_t)B * N;
+    const int64_t nctr = (int64_t)(ctr_bytes / 4);
+    const int64_t work = total > nctr ? total : nctr;
+    const int64_t blocks = (work + 255) / 256 < 65536 ? (work + 255) / 256 : 65536;
+    upd_prologue_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(sids, total, N, K, offs, ctr, nctr);
+    return hipGetLastError();
+}
+
 // mode 0: in-core update of C; shift (optional, [B]) receives sum_k ||c_new - c_old||^2 in fp64,
 // summed in a fixed order.  mode 1: accumulate into sums / cnt.  `ref` optionally names the
-// prepared centroids to refresh.
+// prepared centroids to refresh.  mem: first positions (from the arg-sort or the prologue),
+// zeroed counters (left zero) and scratch.
 // normalize (mode 0, one column block per row): c_k <- s_k / ||s_k||, the cosine mean direction.
 hipError_t launch_update(int dt, const void *x, const int32_t *sids, const int32_t *sidx, const int32_t *counts,
                          int B, int N, int D, int K, int mode, float *C, double *shift, float *sums, int32_t *cnt,
-                         const UpdRefresh &ref, void *ws, hipStream_t s, int normalize) {
+                         const UpdRefresh &ref, const UpdMem &mem, hipStream_t s, int normalize) {
     const UpdCfg u = plan_update(dt, B, N, D);
     const int64_t chunks = (int64_t)B * u.nch;
     if (normalize && (mode != 0 || u.ncb != 1)) return hipErrorInvalidValue;
     UpdArgs a = make_args(dt, x, sids, sidx, counts, B, N, D, K, mode, C, shift != nullptr, sums, cnt,
-                          mode == 0 ? ref : UpdRefresh{}, ws);
+                          mode == 0 ? ref : UpdRefresh{}, mem);
     a.normalize = normalize;
     hipError_t e;
     const int64_t waves = chunks * u.ncb;
     if (dt == DT_F32) e = launch_segsum_dt<DT_F32>(a, u.vec, u.vpl, waves, s);
     else if (dt == DT_F16) e = launch_segsum_dt<DT_F16>(a, u.vec, u.vpl, waves, s);
     else e = launch_segsum_dt<DT_BF16>(a, u.vec, u.vpl, waves, s);
-    if (e != hipSuccess) return e;
-    upd_combine_kernel<<<dim3((unsigned)((chunks + COMBINE_CHUNKS - 1) / COMBINE_CHUNKS)), dim3(256), 0, s>>>(a, chunks);
-    e = hipGetLastError();
     if (e != hipSuccess || !a.shp) return e;
-    return launch_sum_f64_rows(a.shp, B, u.nch * (u.ncb + 1), shift, s);
+    return launch_sum_f64_rows(a.shp, B, u.nch * 2 * u.ncb, shift, s);
+}
+
+// A standalone update in a caller's workspace (update_ws_bytes): the prologue, then the update.
+hipError_t launch_update_ws(int dt, const void *x, const int32_t *sids, const int32_t *sidx, const int32_t *counts,
+                            int B, int N, int D, int K, float *C, double *shift, void *ws, hipStream_t s) {
+    const size_t cb = update_ctr_bytes(dt, B, N, D, K);
+    char *wp = (char *)ws;
+    UpdMem mem;
+    mem.ctr = (int32_t *)wp;
+    int32_t *offs = (int32_t *)(wp + cb);
+    mem.offs = offs;
+    mem.scratch = wp + cb + align256((size_t)B * K * 4);
+    hipError_t e = launch_update_prologue(sids, B, N, K, offs, mem.ctr, cb, s);
+    if (e != hipSuccess) return e;
+    return launch_update(dt, x, sids, sidx, counts, B, N, D, K, 0, C, shift, nullptr, nullptr, UpdRefresh{}, mem, s, 0);
 }
 
 // shk: [B][K] doubles of scratch for the per-cluster shifts (optional, with shift).

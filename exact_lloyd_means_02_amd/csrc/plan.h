@@ -62,6 +62,15 @@ struct UpdRefresh {
     int zero_norm = 0;  // similarity metrics: refreshed norm terms are 0
 };
 
+// Memory of one update launch: each cluster's first sorted position [B][K] (from the arg-sort
+// or the update's prologue), the arrival counters (zero on entry, left zero) and scratch for
+// partial records and shift partials.
+struct UpdMem {
+    const int32_t *offs = nullptr;
+    int32_t *ctr = nullptr;
+    void *scratch = nullptr;
+};
+
 AssignCfg plan_assign(int dt, int64_t B, int64_t N, int64_t D, int64_t K);
 SortCfg plan_sort(int64_t N, int64_t K);
 UpdCfg plan_update(int dt, int64_t B, int64_t N, int64_t D);

@@ -14,6 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("FLASHKM_LIB") or os.path.join(HERE, "libflashkm.so")
 
 KM_F32, KM_F16, KM_BF16 = 0, 1, 2
+DT_CODES = {"f32": KM_F32, "f16": KM_F16, "bf16": KM_BF16}
 KM_OK, KM_ERR_INVALID, KM_ERR_UNSUPPORTED, KM_ERR_WORKSPACE, KM_ERR_HIP = 0, -1, -2, -3, -4
 KM_OP_ASSIGN, KM_OP_ARGSORT, KM_OP_UPDATE, KM_OP_FIT, KM_OP_FIT_HOST = 1, 2, 3, 4, 5
 KM_OP_FIT_DOT, KM_OP_FIT_COSINE = 6, 7
@@ -23,8 +24,8 @@ STATUS_NAMES = {0: "KM_OK", -1: "KM_ERR_INVALID", -2: "KM_ERR_UNSUPPORTED", -3: 
 
 # every symbol the header declares
 EXPORTS = ["kmeans_plan", "kmeans_workspace_bytes", "kmeans_row_norms", "kmeans_assign", "kmeans_prepare_centroids",
-           "kmeans_assign_prepared", "kmeans_argsort_ids", "kmeans_update", "kmeans_fit", "kmeans_normalize_rows",
-           "kmeans_prepare_centroids_metric", "kmeans_fit_metric", "kmeans_last_error"]
+           "kmeans_assign_prepared", "kmeans_argsort_ids", "kmeans_argsort_status", "kmeans_update", "kmeans_fit",
+           "kmeans_normalize_rows", "kmeans_prepare_centroids_metric", "kmeans_fit_metric", "kmeans_last_error"]
 
 
 class KmPlan(ctypes.Structure):
@@ -55,6 +56,7 @@ def _load():
     lib.kmeans_prepare_centroids.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, vp, sz, vp]
     lib.kmeans_assign_prepared.argtypes = [vp, ctypes.c_int, vp, sz, i64, i64, i64, i64, vp, vp, vp, vp]
     lib.kmeans_argsort_ids.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, sz, vp]
+    lib.kmeans_argsort_status.argtypes = [vp, sz, vp]
     lib.kmeans_update.argtypes = [vp, ctypes.c_int, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, sz, vp]
     lib.kmeans_fit.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, i32, f32, i64, vp, vp, vp, vp, vp, sz, vp]
     lib.kmeans_normalize_rows.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp]
@@ -62,7 +64,7 @@ def _load():
     lib.kmeans_fit_metric.argtypes = [vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64, i32, f32, i64, vp, vp, vp,
                                       vp, vp, sz, vp]
     for n in ("kmeans_plan", "kmeans_row_norms", "kmeans_assign", "kmeans_prepare_centroids",
-              "kmeans_assign_prepared", "kmeans_argsort_ids", "kmeans_update", "kmeans_fit", "kmeans_normalize_rows",
+              "kmeans_assign_prepared", "kmeans_argsort_ids", "kmeans_argsort_status", "kmeans_update", "kmeans_fit", "kmeans_normalize_rows",
               "kmeans_prepare_centroids_metric", "kmeans_fit_metric"):
         getattr(lib, n).restype = ctypes.c_int
     lib.kmeans_last_error.argtypes = []
@@ -259,8 +261,9 @@ def kmeans_assign_prepared(x, prep: PreparedCentroids, x_norms=None, assign=None
 
 
 def kmeans_argsort_ids(assign, K: int, sorted_ids=None, sorted_idx=None, counts=None, want_counts=True,
-                       stream=None):
-    """Returns (sorted_ids, sorted_idx, counts or None), all int32."""
+                       stream=None, check=False):
+    """Returns (sorted_ids, sorted_idx, counts or None), all int32.  check=True waits for the
+    sort and raises FlashKMError when it met labels outside [0, K) (kmeans_argsort_status)."""
     torch = _torch()
     _need(assign.dim() == 2 and assign.is_contiguous() and assign.dtype == torch.int32, "assign: int32 [B, N]")
     B, N = assign.shape
@@ -274,6 +277,8 @@ def kmeans_argsort_ids(assign, K: int, sorted_ids=None, sorted_idx=None, counts=
     ws = workspace(KM_OP_ARGSORT, KM_F32, B, N, 1, K, assign.device, stream=st)
     _check(LIB.kmeans_argsort_ids(_ptr(assign), B, N, K, _ptr(sorted_ids), _ptr(sorted_idx), _ptr(counts),
                                   _ptr(ws), ws.numel(), st))
+    if check:
+        _check(LIB.kmeans_argsort_status(_ptr(ws), ws.numel(), st))
     return sorted_ids, sorted_idx, counts
 
 

@@ -34,11 +34,12 @@
  *     invalid arguments are reported even on a machine without a GPU.
  *     kmeans_last_error() returns a message for the calling thread's last
  *     non-OK status.
- *   - Preconditions the library does not check: finite input values; for the
- *     arg-sort and update calls, 0 <= assign < K and sorted arrays / counts
- *     produced by kmeans_argsort_ids from that assignment.  Kernels clamp
- *     indices so that violating them gives wrong numbers, not out-of-bounds
- *     accesses.
+ *   - Preconditions: finite input values (not checked).  The arg-sort skips
+ *     labels outside [0, K) and reports them through kmeans_argsort_status
+ *     (kmeans_fit through its return value).  kmeans_update needs sorted arrays
+ *     and counts produced by kmeans_argsort_ids from one assignment; it does
+ *     not check that, and clamps every index it derives from them, so
+ *     inconsistent inputs give wrong numbers, not accesses out of bounds.
  *   - Limits: 1 <= B, 1 <= K <= N < 2^31, 1 <= D <= 4096, B*N < 2^31,
  *     K <= 2^24.
  */
@@ -176,18 +177,35 @@ km_status_t kmeans_assign_prepared(const void *x, km_dtype_t dt, const void *c_p
  *   sorted_idx  device [B, N] int32 out: 0-based point indices, equal ids in
  *               increasing index order
  *   counts      device [B, K] int32 out or NULL: points per cluster
+ *   ws          workspace >= kmeans_workspace_bytes(KM_OP_ARGSORT, ...); its
+ *               first 4 bytes become the call's status word (below)
+ * Labels outside [0, K) are left out of the sort and the counts (the outputs
+ * are then unspecified, and no access leaves the output rows) and the status
+ * word records them.  The call returns without waiting for the GPU, so it
+ * cannot return that as its status; kmeans_argsort_status does.
  */
 km_status_t kmeans_argsort_ids(const int32_t *assign, int64_t B, int64_t N, int64_t K,
                                int32_t *sorted_ids, int32_t *sorted_idx, int32_t *counts, void *ws,
                                size_t ws_bytes, void *stream);
 
 /*
+ * Waits for `stream` and reports the status word of the last
+ * kmeans_argsort_ids call made with workspace `ws` on it: KM_OK, or
+ * KM_ERR_INVALID when that call met labels outside [0, K) (or a label array
+ * that changed while it ran).  Same digest section as kmeans_argsort_ids.
+ *   ws, ws_bytes  the workspace passed to kmeans_argsort_ids (device)
+ */
+km_status_t kmeans_argsort_status(const void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Sort-inverse update (paper summary, "Method"; paper digest, step (2)):
  * each wave takes a contiguous chunk of the sorted order, gathers the rows
  * of the unpermuted x through sorted_idx, sums each cluster-id segment on
- * chip in fp32, and writes once per segment; segments cut by a chunk edge
- * are combined in chunk order (deterministic, no float atomics).  Then
- * c_k <- s_k / n_k; a cluster with n_k == 0 keeps its centroid.
+ * chip in fp32, and writes once per segment; a segment spread over three or
+ * more chunks leaves one partial per chunk, and the last of its waves to
+ * finish adds them in chunk order (deterministic, no float atomics, one
+ * integer atomic per chunk of such a segment).  Then c_k <- s_k / n_k; a
+ * cluster with n_k == 0 keeps its centroid.
  *   x           device [B, N, D] dtype dt
  *   sorted_ids, sorted_idx, counts   from kmeans_argsort_ids for the same
  *               assignment
@@ -205,6 +223,9 @@ km_status_t kmeans_update(const void *x, km_dtype_t dt, const int32_t *sorted_id
  * assign -> inertia -> arg-sort -> update.  With tol > 0 the run stops after
  * iteration t when max_b shift_t[b] < tol (one host read per iteration);
  * with tol == 0 all `iters` iterations run without a host wait until the end.
+ * Returns KM_ERR_INVALID (after the run) if the arg-sort of the last
+ * iteration met labels outside [0, K), which the fit's own assignment never
+ * produces.
  * If x is pinned host memory, the streamed path runs instead (README,
  * "Large tensor Benchmark"; paper digest, step (3)): each iteration streams
  * x in chunks of `chunk_points` points with hipMemcpyAsync into two device
@@ -220,7 +241,9 @@ km_status_t kmeans_update(const void *x, km_dtype_t dt, const int32_t *sorted_id
  *   inertia      host double [iters * B] out or NULL: per iteration and
  *                problem, sum_i ||x_i - c~_{a_i}||^2 (fp32 terms, fp64 sum)
  *   iters_done   host int32 out or NULL
- * Returns after the work has finished (it synchronises `stream`).
+ * Returns after the work has finished (it synchronises `stream`).  The
+ * streamed path creates one copy stream and four events for the call and
+ * destroys them before it returns.
  */
 km_status_t kmeans_fit(const void *x, km_dtype_t dt, int64_t B, int64_t N, int64_t D, int64_t K,
                        int32_t iters, float tol, int64_t chunk_points, float *centroids,

@@ -94,3 +94,183 @@ def check_inertia(x64, ct64, a, J_gpu):
     for b in range(x64.shape[0]):
         J_or = oracle.inertia(x64[b], ct64[b], a[b])
         assert abs(J_gpu[b] - J_or) <= INERTIA_TOL * abs(J_or), "inertia %r vs oracle %r" % (J_gpu[b], J_or)
+
+
+def fit_trajectory(fk, xt, ct, T):
+    """The GPU fit's centroids after 0..T iterations (the fit is deterministic, so a fit of t
+    iterations ends where the first t iterations of a longer one do)."""
+    import torch
+    cs = [ct.cpu().numpy().astype(np.float64)]
+    for t in range(1, T + 1):
+        c = ct.clone()
+        fk.kmeans_fit(xt, c, t, 0.0)
+        torch.cuda.synchronize()
+        cs.append(c.cpu().numpy().astype(np.float64))
+    return cs
+
+
+BLOCK = 1 << 20          # points per block of the blocked oracle compositions below
+
+
+def _pool():
+    from concurrent.futures import ThreadPoolExecutor
+    return ThreadPoolExecutor(8)
+
+
+def oracle_iteration_blocked(x_store, dtype, c, problems, pool, block=BLOCK):
+    """One Lloyd iteration of the oracle in modelled mode (as oracle.lloyd_iteration), composed over
+    blocks of points to bound host memory: per block the oracle's assignment (labels, d1, d2) and
+    segment sums; the sums and counts of a problem are the sums over its blocks (the oracle's
+    segment sums are additive over disjoint blocks of points).  c [P, K, D] are the centroid masters
+    of `problems`.  Returns (labels [P, N], d1, d2, inertia [P], counts [P, K], c_new [P, K, D])."""
+    c = np.asarray(c, dtype=np.float64)
+    P, K, D = c.shape
+    N = x_store.shape[1]
+    ct = oracle.centroid_operand(c, dtype)
+    labels = np.empty((P, N), dtype=np.int64)
+    d1 = np.empty((P, N))
+    d2 = np.empty((P, N))
+    c_new = c.copy()
+    counts = np.zeros((P, K), dtype=np.int64)
+    for j, b in enumerate(problems):
+        futs = []
+        for lo in range(0, N, block):
+            hi = min(N, lo + block)
+            xb = W.storage_to_f64(x_store[b, lo:hi], dtype)
+            labels[j, lo:hi], d1[j, lo:hi], d2[j, lo:hi] = oracle.assign(xb, ct[j])
+            futs.append(pool.submit(oracle.segment_sums, xb, labels[j, lo:hi], K))
+        sums = np.zeros((K, D))
+        for f in futs:
+            sk, nk = f.result()
+            sums += sk
+            counts[j] += nk
+        nz = counts[j] > 0
+        c_new[j][nz] = sums[nz] / counts[j][nz, None]
+    c_new = c_new.astype(np.float32).astype(np.float64)       # the master is kept in fp32
+    return labels, d1, d2, d1.sum(axis=1), counts, c_new
+
+
+def check_fit(fk, w, x_store, c0, xt, ct, problems=None, say=print):
+    """Free-running kmeans_fit of w.iters iterations (tol w.tol) against the oracle, by the
+    parity protocol (x_store: the points in their storage dtype, [B, N, D]):
+      * the oracle's free-running Lloyd loop (modelled mode, same init) on `problems` (all by
+        default; problems are independent, so a subset runs the same per-problem trajectory):
+        per-iteration inertia within INERTIA_TOL, the same number of iterations, and where the
+        last labels of a cluster agree, its centroid within the dtype's tolerance;
+      * the last iteration teacher forced on every problem and point: the oracle's assignment
+        from the GPU's centroids before it (labels equal except near ties, the GPU's pick within
+        the band), and the oracle's update of those labels (every centroid within tolerance,
+        empty clusters bit-identical);
+      * the stopping rule (tol > 0): the fit stops after the first iteration whose shift, the
+        oracle's fp64 formula on the GPU's own centroids, is below tol (decided only where no
+        shift lies within 1e-3 * tol of it).
+    Returns a dict of what was measured."""
+    import torch
+    B, N, D = x_store.shape
+    c = ct.clone()
+    a, J, done = fk.kmeans_fit(xt, c, w.iters, w.tol)
+    torch.cuda.synchronize()
+    a_np = a.cpu().numpy().astype(np.int64)
+    c_T = c.cpu().numpy().astype(np.float64)
+    out = {"iters_done": done}
+    traj = fit_trajectory(fk, xt, ct, done)
+    assert np.array_equal(traj[-1], c_T), "a shorter fit did not follow the longer fit's trajectory"
+    if w.tol > 0:
+        shifts = [float(np.max(oracle.shift(traj[t], traj[t - 1]))) for t in range(1, done + 1)]
+        out["shifts"] = shifts
+        below = [t for t, v in enumerate(shifts) if v < w.tol]
+        expect = below[0] + 1 if below else w.iters
+        say("shift per iteration %s, tol %g: %d iterations (rule: %d)" % (
+            ["%.4g" % v for v in shifts], w.tol, done, expect))
+        if all(abs(v - w.tol) > 1e-3 * w.tol for v in shifts):
+            assert done == expect
+    tol = CENTROID_TOL[w.dtype]
+    with _pool() as pool:
+        # the last iteration, teacher forced on every problem and point
+        c_prev = traj[done - 1]
+        lab, d1, d2, _, cnt, c_or = oracle_iteration_blocked(x_store, w.dtype, c_prev, range(B), pool)
+        near = oracle.near_mask(d1, d2, NEAR)
+        mism = a_np != lab
+        bad = mism & ~near
+        assert not bad.any(), "last iteration: %d labels differ outside the near-tie band" % int(bad.sum())
+        flips = int(mism.sum())
+        if flips:  # the GPU's pick lies within the band of the best distance
+            ct64 = operand(c_prev.astype(np.float32), w.dtype)
+            for b in np.unique(np.nonzero(mism)[0]):
+                idx = np.nonzero(mism[b])[0]
+                dg = oracle.dist_to(W.storage_to_f64(x_store[b, idx], w.dtype), ct64[b], a_np[b, idx])
+                assert (dg <= d1[b, idx] * (1 + NEAR) + 1e-30).all()
+            # the update of the GPU's own labels
+            _, _, _, _, cnt, c_or = _update_of(x_store, w.dtype, a_np, c_prev, pool)
+        empty = cnt == 0
+        assert np.array_equal(c_T[empty], c_prev[empty]), "empty clusters changed"
+        num = np.linalg.norm(c_T - c_or, axis=2)[~empty]
+        den = np.maximum(np.linalg.norm(c_or, axis=2), 1e-30)[~empty]
+        last_worst = float((num / den).max()) if num.size else 0.0
+        assert last_worst <= tol, "last iteration: centroid rel err %g" % last_worst
+        out.update(last_iteration_near_tie_flips=flips, last_iteration_centroid_rel_max=last_worst)
+        # free running against the oracle
+        pb = list(range(B)) if problems is None else list(problems)
+        c_or = c0[pb].astype(np.float64)
+        J_or, S_or = [], []
+        t_or = 0
+        for t in range(w.iters):
+            lab_or, _, _, Jt, _, c_next = oracle_iteration_blocked(x_store, w.dtype, c_or, pb, pool)
+            J_or.append(Jt)
+            S_or.append(float(np.max(oracle.shift(c_next, c_or))))
+            c_or = c_next
+            t_or += 1
+            if problems is None and S_or[-1] < w.tol:
+                break
+            if problems is not None and t_or == done:
+                break
+    J_or = np.array(J_or)
+    assert t_or == done, "iterations: fit %d, oracle %d" % (done, t_or)
+    rel = np.abs(J[:, pb] - J_or) / np.abs(J_or)
+    out["inertia_rel_max"] = float(rel.max())
+    assert rel.max() <= INERTIA_TOL, "inertia rel diff %g" % rel.max()
+    agree_pts, agree_clusters, worst = 0, 0, 0.0
+    for j, b in enumerate(pb):
+        lo = lab_or[j]
+        same = a_np[b] == lo
+        agree_pts += int(same.sum())
+        # clusters whose member sets agree: no point enters or leaves them between the two runs
+        moved = np.zeros(c_T.shape[1], dtype=bool)
+        moved[a_np[b][~same]] = True
+        moved[lo[~same]] = True
+        ok = ~moved
+        if ok.any():
+            num = np.linalg.norm(c_T[b][ok] - c_or[j][ok], axis=1)
+            den = np.maximum(np.linalg.norm(c_or[j][ok], axis=1), 1e-30)
+            worst = max(worst, float((num / den).max()))
+            assert (num / den).max() <= tol, "problem %d: centroid rel err %g" % (b, (num / den).max())
+        agree_clusters += int(ok.sum())
+    out.update(free_label_agreement=agree_pts / (len(pb) * N), free_clusters_compared=agree_clusters,
+               free_centroid_rel_max=worst)
+    say("fit %s: %d iterations, inertia rel %.3g; last iteration: %d near-tie flips, centroid rel %.3g; "
+        "free-running (%d problems): labels agree %.6f, %d clusters compared, worst centroid rel %.3g" % (
+            w.name, done, out["inertia_rel_max"], flips, last_worst, len(pb), out["free_label_agreement"],
+            agree_clusters, worst))
+    return out
+
+
+def _update_of(x_store, dtype, labels, c_old, pool):
+    """The oracle's update of given labels (blocked segment sums): (None, None, None, None, counts,
+    c_new) with c_new rounded to the fp32 master."""
+    c_old = np.asarray(c_old, dtype=np.float64)
+    B, K, D = c_old.shape
+    N = x_store.shape[1]
+    counts = np.zeros((B, K), dtype=np.int64)
+    c_new = c_old.copy()
+    for b in range(B):
+        futs = [pool.submit(lambda lo: oracle.segment_sums(W.storage_to_f64(x_store[b, lo:lo + BLOCK], dtype),
+                                                           labels[b, lo:lo + BLOCK], K), lo)
+                for lo in range(0, N, BLOCK)]
+        sums = np.zeros((K, D))
+        for f in futs:
+            sk, nk = f.result()
+            sums += sk
+            counts[b] += nk
+        nz = counts[b] > 0
+        c_new[b][nz] = sums[nz] / counts[b][nz, None]
+    return None, None, None, None, counts, c_new.astype(np.float32).astype(np.float64)

@@ -117,37 +117,47 @@ def test_workspace_sizes(fk):
     assert host >= 2 * (1 << 24) * 64 * 2
 
 
-def _chunk_scratch_need(fk, dt, n, D, K):
-    return max(fk.kmeans_workspace_bytes(fk.KM_OP_ARGSORT, dt, 1, n, D, K),
-               fk.kmeans_workspace_bytes(fk.KM_OP_UPDATE, dt, 1, n, D, K))
+def _sort_need(fk, dt, n, D, K):
+    """Digit tables of one arg-sort of n labels (the standalone workspace less its status word)."""
+    return fk.kmeans_workspace_bytes(fk.KM_OP_ARGSORT, dt, 1, n, D, K) - 256
+
+
+def _update_need(fk, dt, n, D, K):
+    """Counters and scratch of one update of n points (the standalone workspace less the
+    clusters' first positions, which the streamed layout keeps at a fixed size)."""
+    return fk.kmeans_workspace_bytes(fk.KM_OP_UPDATE, dt, 1, n, D, K) - (-(-4 * K // 256) * 256)
 
 
 @pytest.mark.parametrize("dt,D,K", [(2, 128, 64), (1, 64, 512), (2, 256, 64), (0, 1024, 32), (1, 64, 32768)])
 def test_streamed_scratch_covers_the_last_chunk(fk, dt, D, K):
-    """The streamed path's scratch holds the arg-sort tables and the update's partials of one
-    staged chunk.  The update's plan is not monotonic in the point count, so a ragged last chunk
-    can need more than a full one: the workspace must cover both.  Only the scratch region of the
-    streamed layout depends on N (for a fixed chunk), so the growth of the workspace from N = m c
-    (all chunks full) to N = m c + r is at least what the r-point chunk needs beyond a full one."""
+    """The streamed path keeps the arg-sort tables, the update's partial records and its arrival
+    counters of one staged chunk.  The update's plan is not monotonic in the point count, so a
+    ragged last chunk can need more than a full one: the workspace must cover both.  Only those
+    regions of the streamed layout depend on N (for a fixed chunk), so the growth of the workspace
+    from N = m c (all chunks full) to N = m c + r bounds what the r-point chunk may need beyond a
+    full one: at least u(r) - u(c) - s(c) and s(r) - s(c) - u(c), with u the update's counters and
+    scratch and s the arg-sort's tables (the two share the scratch region)."""
     chunks = [1 << 14, 50000, 532480, 1 << 20, (1 << 24) - 4096, 1 << 24]
     rests = [1, 100, 12345, 31072, 262144, 524288, 532479, (1 << 20) - 1]
     checked = 0
     for c in chunks:
         for m in (1, 2):
             full = fk.kmeans_workspace_bytes(fk.KM_OP_FIT_HOST, dt, 1, m * c, D, K, c)
-            need_c = _chunk_scratch_need(fk, dt, c, D, K)
+            uc, sc = _update_need(fk, dt, c, D, K), _sort_need(fk, dt, c, D, K)
             for r in rests:
                 if r >= c or r < K:
                     continue
                 ws = fk.kmeans_workspace_bytes(fk.KM_OP_FIT_HOST, dt, 1, m * c + r, D, K, c)
-                need_r = _chunk_scratch_need(fk, dt, r, D, K)
-                assert ws - full >= need_r - need_c, (c, m, r, ws - full, need_r - need_c)
+                ur, sr = _update_need(fk, dt, r, D, K), _sort_need(fk, dt, r, D, K)
+                assert ws - full >= ur - uc - sc, (c, m, r, ws - full, ur - uc - sc)
+                assert ws - full >= sr - sc - uc, (c, m, r, ws - full, sr - sc - uc)
                 checked += 1
     assert checked > 0
-    # the case that exposed it: 532480-point chunks, a last chunk of 2^19 points, D=128, K=64
+    # the case that exposed it: 532480-point chunks, a last chunk of 2^19 points, D=128, K=64; the
+    # shorter chunk's update needs megabytes more than the full chunk's update and sort together
     if (dt, D, K) == (2, 128, 64):
         c, r = 532480, 1 << 19
-        assert _chunk_scratch_need(fk, dt, r, D, K) > _chunk_scratch_need(fk, dt, c, D, K)
+        assert _update_need(fk, dt, r, D, K) - _update_need(fk, dt, c, D, K) - _sort_need(fk, dt, c, D, K) > 1 << 20
 
 
 DT = {"f32": 0, "f16": 1, "bf16": 2}

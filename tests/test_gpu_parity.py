@@ -159,6 +159,26 @@ def test_argsort(fk, B, N, K):
     check_argsort(a, K, s.cpu().numpy(), i.cpu().numpy(), c.cpu().numpy())
 
 
+@pytest.mark.parametrize("K", [1000, 32768])
+def test_argsort_reports_labels_out_of_range(fk, K):
+    """Labels outside [0, K) are left out and reported by kmeans_argsort_status (the sort call
+    itself does not wait); the next call on the same workspace clears the report."""
+    N = 50000
+    rng = np.random.default_rng(K)
+    a = rng.integers(0, K, size=(2, N)).astype(np.int32)
+    a[0, 17] = -1
+    a[1, 4000] = K
+    a[1, 4001] = np.iinfo(np.int32).max
+    _say(f"argsort with out-of-range labels, K={K}, {fk.kmeans_plan(0, 2, N, 1, K)['sort_passes']} pass(es)")
+    at = torch.from_numpy(a).to(device())
+    with pytest.raises(fk.FlashKMError) as e:
+        fk.kmeans_argsort_ids(at, K, check=True)
+    assert e.value.status == fk.KM_ERR_INVALID and "outside [0, K)" in str(e.value)
+    good = rng.integers(0, K, size=(2, N)).astype(np.int32)
+    s, i, c = fk.kmeans_argsort_ids(torch.from_numpy(good).to(device()), K, check=True)
+    check_argsort(good, K, s.cpu().numpy(), i.cpu().numpy(), c.cpu().numpy())
+
+
 UPDATE_CASES = [
     ("headline_bf16", dict(B=2, N=3000, K=100)),
     ("batched_f16", dict(B=2, N=5000, K=37)),
@@ -217,6 +237,40 @@ def test_update_segments_on_window_edges(fk, N):
     cnew = ct.clone()
     fk.kmeans_update(xt, s, i, c, cnew)
     check_update(x64, a, c0, cnew.cpu().numpy(), w.dtype)
+
+
+# Segment lengths around the update's chunk groups: at B=1, N=2^17 a wave takes 64 sorted positions,
+# so a segment over P chunks has about 64 P points; the groups hold 32 chunks.
+LONG_LENS = [130, 192, 200, 1000, 31 * 64, 32 * 64, 32 * 64 + 1, 33 * 64, 64 * 64, 64 * 64 + 65, 20000, 3, 1, 64]
+
+
+@pytest.mark.parametrize("name,D", [("headline_bf16", 128), ("tiny_f32", 16), ("headline_bf16", 4096)])
+def test_update_long_segments(fk, name, D):
+    """Segments spread over 3..300 chunks (one group, a group boundary, several groups), whose
+    partials the last arriving waves add; every cluster against the oracle's means, the counts
+    bit-exact, and three runs bit-identical (the order of the sums must not depend on which wave
+    arrives last).  D=4096 takes two column blocks per row."""
+    N = 1 << 17 if D <= 128 else 1 << 15
+    K = len(LONG_LENS) + 1
+    w = W.small(name, B=1, N=N, D=D, K=K)
+    x, x64, c0, xt, ct = make_inputs(w)
+    lens = list(LONG_LENS) if D <= 128 else [max(1, v // 4) for v in LONG_LENS]
+    lens.append(N - sum(lens))
+    assert lens[-1] > 0
+    _say(f"case {w}, segment lengths {lens}, plan rows {fk.kmeans_plan(fk.DT_CODES[w.dtype], 1, N, D, K)['upd_rows']}")
+    a = np.repeat(np.arange(K, dtype=np.int32), lens)
+    a = np.random.default_rng(D).permutation(a)[None, :].astype(np.int32)
+    at = torch.from_numpy(a).to(device())
+    s, i, c = fk.kmeans_argsort_ids(at, K)
+    outs, shifts = [], []
+    for _ in range(3):
+        cn = ct.clone()
+        sh = fk.kmeans_update(xt, s, i, c, cn, want_shift=True)
+        outs.append(cn.cpu().numpy())
+        shifts.append(sh.cpu().numpy())
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+    assert all(np.array_equal(shifts[0], v) for v in shifts[1:])
+    check_update(x64, a, c0, outs[0], w.dtype, shifts[0])
 
 
 def test_update_is_deterministic(fk):

@@ -317,3 +317,31 @@ def test_segment_sums_brute_force_and_blocks():
     s2, n2 = oracle.segment_sums(x[20:], a[20:], 6)
     assert np.array_equal(n1 + n2, counts)
     assert np.allclose(s1 + s2, sums, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------------
+# the blocked composition the full-size GPU tests use (per block of points: the oracle's
+# assignment and segment sums; sums added over blocks) against the oracle's own iteration
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_blocked_iteration_equals_oracle_iteration(dtype):
+    from concurrent.futures import ThreadPoolExecutor
+    from exact_lloyd_means_02_amd import workloads as W
+    from helpers import oracle_iteration_blocked
+    x64 = _gmm(3, 5000, 8, 9, 21)
+    x_store = W.cast_f32(x64.astype(np.float32), dtype)
+    xs = W.storage_to_f64(x_store, dtype)
+    c = xs[:, 100:107].astype(np.float32).astype(np.float64)
+    ref = oracle.lloyd_iteration(xs, c, dtype=dtype, mode="modelled")
+    with ThreadPoolExecutor(4) as pool:
+        lab, d1, d2, J, cnt, c_new = oracle_iteration_blocked(x_store, dtype, c, [0, 1, 2], pool, block=777)
+    assert np.array_equal(lab, ref["a"]) and np.array_equal(cnt, ref["counts"])
+    np.testing.assert_allclose(d1, ref["d1"], rtol=1e-13)
+    np.testing.assert_allclose(d2, ref["d2"], rtol=1e-13)
+    np.testing.assert_allclose(J, ref["inertia"], rtol=1e-12)
+    # fp32 master: equal unless an fp64 sum order difference crosses an fp32 rounding boundary
+    assert np.max(np.abs(c_new - ref["c_new"]) / np.maximum(np.abs(ref["c_new"]), 1e-30)) <= 2 ** -23
+    # a subset of problems runs the same per-problem iteration
+    with ThreadPoolExecutor(4) as pool:
+        lab1, _, _, J1, _, c1 = oracle_iteration_blocked(x_store, dtype, c[[2]], [2], pool, block=1000)
+    assert np.array_equal(lab1[0], ref["a"][2]) and np.allclose(J1[0], ref["inertia"][2], rtol=1e-12)
