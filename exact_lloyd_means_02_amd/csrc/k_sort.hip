@@ -175,6 +175,17 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__rest
     const int b = lb / ntiles, t = lb - b * ntiles;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int32_t *hb = hist + (size_t)b * bins * ntiles;
+    // this wave's keys and values, loaded first: their memory latency overlaps the offsets below
+    const size_t base = (size_t)b * N;
+    const int tile0 = t * SORT_TILE + w * (SORT_ROUNDS * 64);
+    int32_t key[SORT_ROUNDS], val[SORT_ROUNDS], pos[SORT_ROUNDS];
+#pragma unroll
+    for (int r = 0; r < SORT_ROUNDS; ++r) {
+        const int i = tile0 + r * 64 + lane;
+        const bool ok = i < N;
+        key[r] = ok ? keys_in[base + i] : -1;
+        val[r] = ok ? (vals_in ? vals_in[base + i] : i) : 0;
+    }
     for (int i = tid; i < SORT_WAVES * bins; i += 256) s_wc[i] = 0;
     if (tid == 0) s_nvalid = 0;
     if constexpr (INLINE) {
@@ -230,17 +241,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__rest
     if (offs && t == 0)
         for (int i = tid; i < bins && i < K; i += 256) offs[(size_t)b * K + i] = s_off[i];
 
-    const size_t base = (size_t)b * N;
-    const int tile0 = t * SORT_TILE + w * (SORT_ROUNDS * 64);
     const uint32_t mask = (uint32_t)bins - 1u;
-    int32_t key[SORT_ROUNDS], val[SORT_ROUNDS], pos[SORT_ROUNDS];
-#pragma unroll
-    for (int r = 0; r < SORT_ROUNDS; ++r) {
-        const int i = tile0 + r * 64 + lane;
-        const bool ok = i < N;
-        key[r] = ok ? keys_in[base + i] : -1;
-        val[r] = ok ? (vals_in ? vals_in[base + i] : i) : 0;
-    }
     const uint64_t lt = lanemask_lt();
     int32_t *wc = s_wc + w * bins;
     int nvalid = 0;

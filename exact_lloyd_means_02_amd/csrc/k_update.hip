@@ -234,6 +234,29 @@ __device__ inline float finish_col(const UpdArgs &a, int b, int k, size_t rowo, 
 // Chunks per first-level group of a long segment's partials.
 constexpr int UPD_GROUP = 32;
 
+// The partial records and group sums pass between waves of different XCDs.  They are written and
+// read with device-scope (agent) atomic stores and loads, which the memory system keeps coherent
+// across the XCDs' L2 caches, so no device-wide cache write-back or invalidation is needed: a
+// wave waits until its record stores are acknowledged (vmcnt 0) before its arrival (an integer
+// atomic, also device scope), and the wave that sees the last arrival reads the records after it.
+// The empty asm statements keep the compiler from moving memory operations across these points.
+__device__ inline void rec_store(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float rec_load(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Count this wave's arrival (lane 0) once its earlier record stores are complete; returns the
+// count before it (wave-uniform).
+__device__ inline int arrive(int32_t *ctr, int lane) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    int old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __shfl(old, 0);
+    asm volatile("" ::: "memory");
+    return old;
+}
+
 // Column d of the sum of m partial records: those of chunks first, first + stride, ... of the
 // problem whose chunk 0 is `cbase` (the segment's first chunk c_first holds it in slot 1, every
 // later chunk in slot 0), added in that order; eight loads in flight.
@@ -246,14 +269,14 @@ __device__ inline float sum_pieces(const UpdArgs &a, size_t cbase, int c_first, 
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int ch = first + (i + u) * stride;
-            v[u] = a.part[((cbase + ch) * 2 + (ch == c_first ? 1 : 0)) * a.D + d];
+            v[u] = rec_load(a.part + ((cbase + ch) * 2 + (ch == c_first ? 1 : 0)) * a.D + d);
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) s += v[u];
     }
     for (; i < m; ++i) {
         const int ch = first + i * stride;
-        s += a.part[((cbase + ch) * 2 + (ch == c_first ? 1 : 0)) * a.D + d];
+        s += rec_load(a.part + ((cbase + ch) * 2 + (ch == c_first ? 1 : 0)) * a.D + d);
     }
     return s;
 }
@@ -301,10 +324,9 @@ __device__ inline void finish_long(const UpdArgs &a, int b, int k, int cbi, int 
 // partial record of long segment k.  The segment's chunks c_first..c_last form groups of
 // UPD_GROUP; the last wave of a group to arrive adds the group's partials.  With one group that
 // wave finishes the cluster; otherwise it leaves the group sum in the record of the group's first
-// chunk, and the last group to arrive adds the group sums and finishes the cluster.  The release
-// fence before each arrival publishes the records written before it; the acquire fence after
-// it makes every record of the group visible to the wave that goes on.  The counters return to
-// zero for the next launch.
+// chunk, and the last group to arrive adds the group sums and finishes the cluster.  Records
+// pass between the waves as rec_store / rec_load describe.  The counters return to zero for the
+// next launch.
 __device__ inline void arrive_long(const UpdArgs &a, int b, int c, int cbi, int k, int lane) {
     // counts and first positions come from the arg-sort of the same labels; clamped so that
     // inconsistent inputs give wrong numbers, not accesses outside the records and counters
@@ -320,12 +342,7 @@ __device__ inline void arrive_long(const UpdArgs &a, int b, int c, int cbi, int 
     const int gslot = j == 0 ? 1 : 0;
     const size_t cbase = (size_t)b * a.nch;
     int32_t *ctr = a.gcnt + ((cbase + gfirst) * 2 + gslot) * a.ncb + cbi;
-    __threadfence();
-    int old = 0;
-    if (lane == 0) old = atomicAdd(ctr, 1);
-    old = __shfl(old, 0);
-    if (old != m - 1) return;
-    __threadfence();
+    if (arrive(ctr, lane) != m - 1) return;
     if (lane == 0) *ctr = 0;
     const int ngroups = (P + UPD_GROUP - 1) / UPD_GROUP;
     if (ngroups == 1) {
@@ -337,15 +354,10 @@ __device__ inline void arrive_long(const UpdArgs &a, int b, int c, int cbi, int 
     float *grec = a.part + ((cbase + gfirst) * 2 + gslot) * a.D;
     for (int d = c0 + lane; d < c1; d += 64) {
         const float v = sum_pieces(a, cbase, c_first, gfirst, 1, m, d);
-        grec[d] = v;  // every piece of the group (this record too) was read above
+        rec_store(grec + d, v);  // every piece of the group (this record too) was read above
     }
-    __threadfence();
     int32_t *sctr = a.scnt + ((size_t)b * a.K + k) * a.ncb + cbi;
-    old = 0;
-    if (lane == 0) old = atomicAdd(sctr, 1);
-    old = __shfl(old, 0);
-    if (old != ngroups - 1) return;
-    __threadfence();
+    if (arrive(sctr, lane) != ngroups - 1) return;
     if (lane == 0) *sctr = 0;
     finish_long(a, b, k, cbi, n, cbase, c_first, c_first, UPD_GROUP, ngroups, lane);
 }
@@ -497,7 +509,7 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
                     const int e0 = c0 + (r + i * a.lanes) * V;
 #pragma unroll
                     for (int e = 0; e < V; ++e)
-                        if (e0 + e < a.D) dst[e0 + e] = acc[i][e];
+                        if (e0 + e < a.D) rec_store(dst + e0 + e, acc[i][e]);
                 }
             }
             if (slot == 0) k_in = k;
@@ -737,10 +749,58 @@ __global__ __launch_bounds__(256) void upd_prologue_kernel(const int32_t *__rest
     if (p == 0 || sids[gi - 1] != k) offs[b * K + k] = p;
 }
 
-hipError_t launch_update_prologue(const int32_t *sids, int B, int N, int K, int32_t *offs, int32_t *ctr,
-                                  size_t ctr_bytes, hipStream_t s) {
+// The same from the counts when the cluster table is small next to the points: one workgroup per
+// problem takes the exclusive scan of its counts (1024 at a time, carried), and every workgroup
+// clears a share of the counters.
+__global__ __launch_bounds__(256) void upd_prologue_counts_kernel(const int32_t *__restrict__ counts, int K,
+                                                                  int32_t *__restrict__ offs,
+                                                                  int32_t *__restrict__ ctr, int64_t nctr) {
+    __shared__ int32_t s_w[4];
+    __shared__ int32_t s_carry;
+    const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+    for (int64_t i = (int64_t)b * 256 + t; i < nctr; i += (int64_t)gridDim.x * 256) ctr[i] = 0;
+    const int32_t *cb = counts + (size_t)b * K;
+    int32_t *ob = offs + (size_t)b * K;
+    if (t == 0) s_carry = 0;
+    __syncthreads();
+    for (int k0 = 0; k0 < K; k0 += 1024) {
+        int32_t v[4], sum = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int k = k0 + 4 * t + i;
+            v[i] = k < K ? cb[k] : 0;
+            sum += v[i];
+        }
+        int32_t inc = sum;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int32_t o = __shfl_up(inc, off);
+            if (lane >= off) inc += o;
+        }
+        if (lane == 63) s_w[w] = inc;
+        __syncthreads();
+        int32_t run = s_carry + inc - sum;
+        for (int i = 0; i < w; ++i) run += s_w[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int k = k0 + 4 * t + i;
+            if (k < K) ob[k] = run;
+            run += v[i];
+        }
+        __syncthreads();
+        if (t == 255) s_carry = run;
+        __syncthreads();
+    }
+}
+
+hipError_t launch_update_prologue(const int32_t *sids, const int32_t *counts, int B, int N, int K, int32_t *offs,
+                                  int32_t *ctr, size_t ctr_bytes, hipStream_t s) {
     const int64_t total = (int64_t)B * N;
     const int64_t nctr = (int64_t)(ctr_bytes / 4);
+    if ((int64_t)K * 64 <= N) {  // scanning K counts per problem is cheaper than reading N ids
+        upd_prologue_counts_kernel<<<dim3((unsigned)B), dim3(256), 0, s>>>(counts, K, offs, ctr, nctr);
+        return hipGetLastError();
+    }
     const int64_t work = total > nctr ? total : nctr;
     const int64_t blocks = (work + 255) / 256 < 65536 ? (work + 255) / 256 : 65536;
     upd_prologue_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(sids, total, N, K, offs, ctr, nctr);
@@ -780,7 +840,7 @@ hipError_t launch_update_ws(int dt, const void *x, const int32_t *sids, const in
     int32_t *offs = (int32_t *)(wp + cb);
     mem.offs = offs;
     mem.scratch = wp + cb + align256((size_t)B * K * 4);
-    hipError_t e = launch_update_prologue(sids, B, N, K, offs, mem.ctr, cb, s);
+    hipError_t e = launch_update_prologue(sids, counts, B, N, K, offs, mem.ctr, cb, s);
     if (e != hipSuccess) return e;
     return launch_update(dt, x, sids, sidx, counts, B, N, D, K, 0, C, shift, nullptr, nullptr, UpdRefresh{}, mem, s, 0);
 }
