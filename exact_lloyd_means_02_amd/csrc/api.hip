@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/flashkm.h"
@@ -477,6 +478,67 @@ km_status_t kmeans_argsort_ids(const int32_t *assign, int64_t B, int64_t N, int6
     KM_HIP(launch_argsort(assign, (int)B, (int)N, (int)K, sorted_ids, sorted_idx, counts, nullptr, (int32_t *)ws,
                           (char *)ws + STATUS_BYTES, (hipStream_t)stream));
     return ok();
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------------------------------------
+// The assignment without a caller workspace, for callers that cannot allocate: its scratch (the
+// prepared centroid operand) lives in one static device array per GPU, whose address each device
+// gets once from hipGetSymbolAddress; host code passes only that address, never the array's name.
+// ------------------------------------------------------------------------------------------------
+namespace {
+
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES] = {};
+
+km_status_t scratch_for_current_device(void **out) {
+    int dev = 0;
+    KM_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= MAX_DEVICES) return fail(KM_ERR_UNSUPPORTED, "device index %d beyond %d", dev, MAX_DEVICES);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        KM_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (!p) return fail(KM_ERR_HIP, "hipGetSymbolAddress returned a null scratch address");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+km_status_t kmeans_assign_noalloc(const void *x, km_dtype_t dt, const float *centroids, int64_t B, int64_t N,
+                                  int64_t D, int64_t K, const float *x_norms, int32_t *assign, float *min_dist,
+                                  void *stream) {
+    KM_TRY(check_shape(dt, B, N, D, K));
+    KM_TRY(check_ptr(x, "x"));
+    KM_TRY(check_ptr(centroids, "centroids"));
+    KM_TRY(check_ptr(assign, "assign"));
+    if (min_dist && !x_norms) return fail(KM_ERR_INVALID, "min_dist requires x_norms");
+    if (((uintptr_t)x & 15) != 0) return fail(KM_ERR_INVALID, "x must be 16-byte aligned");
+    const size_t need = assign_ws(dt, B, N, D, K);
+    if (need > NOALLOC_SCRATCH_BYTES)
+        return fail(KM_ERR_WORKSPACE, "this shape needs %zu bytes of scratch; kmeans_assign_noalloc holds %zu",
+                    need, NOALLOC_SCRATCH_BYTES);
+    KM_TRY(check_device_arch());
+    KM_TRY(require_device(x, "x"));
+    KM_TRY(require_device(centroids, "centroids"));
+    KM_TRY(require_device(assign, "assign"));
+    KM_TRY(require_device(min_dist, "min_dist"));
+    KM_TRY(require_device(x_norms, "x_norms"));
+    void *ws = nullptr;
+    KM_TRY(scratch_for_current_device(&ws));
+    // the prepare kernel writes every byte of the operand the assign kernel reads (padding
+    // included), so nothing from an earlier call needs clearing
+    return do_assign(dt, x, centroids, B, N, D, K, x_norms, assign, min_dist, ws, (hipStream_t)stream);
 }
 
 km_status_t kmeans_argsort_status(const void *ws, size_t ws_bytes, void *stream) {

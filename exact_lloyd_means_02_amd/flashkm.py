@@ -23,7 +23,8 @@ METRICS = {"l2": KM_METRIC_L2, "euclid": KM_METRIC_L2, "dot": KM_METRIC_DOT, "co
 STATUS_NAMES = {0: "KM_OK", -1: "KM_ERR_INVALID", -2: "KM_ERR_UNSUPPORTED", -3: "KM_ERR_WORKSPACE", -4: "KM_ERR_HIP"}
 
 # every symbol the header declares
-EXPORTS = ["kmeans_plan", "kmeans_workspace_bytes", "kmeans_row_norms", "kmeans_assign", "kmeans_prepare_centroids",
+EXPORTS = ["kmeans_plan", "kmeans_workspace_bytes", "kmeans_row_norms", "kmeans_assign", "kmeans_assign_noalloc",
+           "kmeans_prepare_centroids",
            "kmeans_assign_prepared", "kmeans_argsort_ids", "kmeans_argsort_status", "kmeans_update", "kmeans_fit",
            "kmeans_normalize_rows", "kmeans_prepare_centroids_metric", "kmeans_fit_metric", "kmeans_last_error"]
 
@@ -53,6 +54,7 @@ def _load():
     lib.kmeans_workspace_bytes.restype = sz
     lib.kmeans_row_norms.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp]
     lib.kmeans_assign.argtypes = [vp, ctypes.c_int, vp, i64, i64, i64, i64, vp, vp, vp, vp, sz, vp]
+    lib.kmeans_assign_noalloc.argtypes = [vp, ctypes.c_int, vp, i64, i64, i64, i64, vp, vp, vp, vp]
     lib.kmeans_prepare_centroids.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, vp, sz, vp]
     lib.kmeans_assign_prepared.argtypes = [vp, ctypes.c_int, vp, sz, i64, i64, i64, i64, vp, vp, vp, vp]
     lib.kmeans_argsort_ids.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, sz, vp]
@@ -63,7 +65,7 @@ def _load():
     lib.kmeans_prepare_centroids_metric.argtypes = [vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64, vp, sz, vp]
     lib.kmeans_fit_metric.argtypes = [vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64, i32, f32, i64, vp, vp, vp,
                                       vp, vp, sz, vp]
-    for n in ("kmeans_plan", "kmeans_row_norms", "kmeans_assign", "kmeans_prepare_centroids",
+    for n in ("kmeans_plan", "kmeans_row_norms", "kmeans_assign", "kmeans_assign_noalloc", "kmeans_prepare_centroids",
               "kmeans_assign_prepared", "kmeans_argsort_ids", "kmeans_argsort_status", "kmeans_update", "kmeans_fit", "kmeans_normalize_rows",
               "kmeans_prepare_centroids_metric", "kmeans_fit_metric"):
         getattr(lib, n).restype = ctypes.c_int
@@ -186,6 +188,24 @@ def kmeans_assign(x, centroids, x_norms=None, assign=None, min_dist=None, want_m
     ws = workspace(KM_OP_ASSIGN, dt, B, N, D, K, x.device, stream=st)
     _check(LIB.kmeans_assign(_ptr(x), dt, _ptr(centroids), B, N, D, K, _ptr(x_norms), _ptr(assign), _ptr(min_dist),
                              _ptr(ws), ws.numel(), st))
+    return assign, min_dist
+
+
+def kmeans_assign_noalloc(x, centroids, x_norms=None, assign=None, min_dist=None, want_min_dist=False, stream=None):
+    """kmeans_assign without a workspace (the library's static per-GPU scratch; see the header).
+    Returns (assign int32 [B,N], min_dist float32 [B,N] or None)."""
+    torch = _torch()
+    _need(x.dim() == 3 and x.is_contiguous(), "x must be a contiguous [B, N, D] tensor")
+    B, N, D = x.shape
+    _need(centroids.dim() == 3 and centroids.is_contiguous() and centroids.dtype == torch.float32
+          and centroids.shape[0] == B and centroids.shape[2] == D, "centroids must be contiguous f32 [B, K, D]")
+    K = centroids.shape[1]
+    if assign is None:
+        assign = torch.empty((B, N), dtype=torch.int32, device=x.device)
+    if want_min_dist and min_dist is None:
+        min_dist = torch.empty((B, N), dtype=torch.float32, device=x.device)
+    _check(LIB.kmeans_assign_noalloc(_ptr(x), dtype_code(x), _ptr(centroids), B, N, D, K, _ptr(x_norms),
+                                     _ptr(assign), _ptr(min_dist), _stream(x, stream)))
     return assign, min_dist
 
 

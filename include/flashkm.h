@@ -146,6 +146,21 @@ km_status_t kmeans_assign(const void *x, km_dtype_t dt, const float *centroids, 
                           float *min_dist, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * kmeans_assign without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments and results as kmeans_assign, minus ws.
+ * Its scratch (the prepared centroids, kmeans_workspace_bytes(KM_OP_ASSIGN,
+ * ...) bytes) lives in one static device array of 32 MiB per GPU, which the
+ * library holds until the process ends; larger shapes return
+ * KM_ERR_WORKSPACE.  Every call on a GPU uses that GPU's array: calls that
+ * may overlap on one GPU (other streams, other threads) race and must not be
+ * made.  The call allocates nothing.
+ */
+km_status_t kmeans_assign_noalloc(const void *x, km_dtype_t dt, const float *centroids, int64_t B, int64_t N,
+                                  int64_t D, int64_t K, const float *x_norms, int32_t *assign,
+                                  float *min_dist, void *stream);
+
+/*
  * The two halves of kmeans_assign, for callers that assign repeatedly against
  * the same centroids (and to time the FlashAssign kernel on its own).
  *
