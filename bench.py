@@ -1,16 +1,28 @@
 #!/usr/bin/env python3
 """Benchmark: one batched Lloyd iteration on one MI355X.
 
-A step is one Lloyd iteration of the whole path (centroid preparation, FlashAssign with the
-per-point minimum distance, inertia, arg-sort, sort-inverse update with the shift), run by
-kmeans_fit on the headline workload (B=32, N=65536, D=128, K=1024, bf16; inputs resident in
-HBM).  The timed region is one kmeans_fit call of `--steps` iterations (the point norms are
-computed once inside it, as in any fit).  Per-stage times come from HIP events recorded on
-the stream the stages run on; the FlashAssign kernel is timed on its own through
-kmeans_assign_prepared (one kernel launch per call).  Prints one JSON line.
+A step is one Lloyd iteration of the whole path (FlashAssign with the per-point minimum
+distance and inertia partials, arg-sort, sort-inverse update with the refresh of the next
+iteration's centroid operand), run by kmeans_fit on the headline workload (B=32, N=65536,
+D=128, K=1024, bf16; inputs resident in HBM).  Order of the run:
 
-`--copy-calib` instead runs a plain device copy of known size (the reference for scaling the
-FETCH_SIZE / WRITE_SIZE counters into bytes) and prints its size.
+  1. per-stage timings: R teacher-forced repetitions of the stage calls (row norms, centroid
+     preparation, FlashAssign through kmeans_assign_prepared -- one kernel launch per call --,
+     arg-sort, update), each bracketed by HIP events on the stream the stages run on.  They run
+     first: the GPU leaves its idle clocks during the setup, and a few milliseconds of load after
+     that it passes through a power-management dip (FlashAssign 10-15% slower for about 10 ms,
+     see the design notes' trace); the stage timings take that load before the fit is timed.
+  2. `--warmup` untimed iterations as one fit;
+  3. the timed region: exactly `--steps` iterations as one kmeans_fit call, bracketed by device
+     synchronisations; `value` = its wall time / steps.  `--repeat` more timed fits follow and are
+     reported beside it (not in `value`).
+  4. the oracle on a bounded sample on the host (cpu_baseline).
+
+Prints one JSON line.  Other modes: `--copy-calib` (a plain device copy of known size, the
+reference for scaling the FETCH_SIZE / WRITE_SIZE counters), `--summarize-trace CSV` (the
+per-iteration summary of a rocprofv3 kernel trace of this script), `--context` /
+`--context-pages` (the standard path the method replaces, at the headline shape / at the pages'
+kernel-ratio shapes).
 """
 from __future__ import annotations
 
@@ -18,6 +30,8 @@ import argparse
 import hashlib
 import json
 import os
+import platform
+import subprocess
 import sys
 import time
 
@@ -34,8 +48,8 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=50,
-                   help="untimed iterations first: the GPU takes a few tens of ms of work to reach its steady clocks")
+    p.add_argument("--warmup", type=int, default=5, help="untimed iterations before the timed fit")
+    p.add_argument("--repeat", type=int, default=2, help="further timed fits reported beside `value`")
     p.add_argument("--workload", default="headline_bf16")
     p.add_argument("--stage-reps", type=int, default=10)
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
@@ -45,7 +59,11 @@ def parse():
                    help="k-means variant: Lloyd (l2), dot-product or cosine (spherical) k-means")
     p.add_argument("--context", action="store_true",
                    help="also time the standard path in plain PyTorch (materialised distances + argmin, "
-                        "scatter-add update) for the kernel ratios")
+                        "scatter-add update) at the workload's shape")
+    p.add_argument("--context-pages", action="store_true",
+                   help="time the standard path against this path at the pages' kernel-ratio shapes and exit")
+    p.add_argument("--summarize-trace", metavar="CSV",
+                   help="summarise a rocprofv3 kernel trace of this script (same --steps/--warmup/--stage-reps)")
     return p.parse_args()
 
 
@@ -105,10 +123,38 @@ def algorithmic(w):
     return flops, assign_bytes, update_bytes
 
 
+# ------------------------------------------------------------------------------------------------
+# host description and the oracle baseline
+# ------------------------------------------------------------------------------------------------
+def host_info():
+    """CPU model, sockets, cores and threads (lscpu), and the BLAS numpy is built with."""
+    info = {"cpu_count": os.cpu_count(), "machine": platform.machine()}
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if ":" not in line:
+                continue
+            k, v = [t.strip() for t in line.split(":", 1)]
+            if k in ("Model name", "Socket(s)", "Core(s) per socket", "Thread(s) per core", "CPU(s)"):
+                info[k] = v
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        import numpy as np
+        cfg = np.show_config(mode="dicts")
+        blas = cfg.get("Build Dependencies", {}).get("blas", {})
+        info["numpy_blas"] = "%s %s" % (blas.get("name", "?"), blas.get("version", ""))
+    except Exception:  # an older numpy without mode="dicts"
+        info["numpy_blas"] = "unknown"
+    return info
+
+
 def cpu_baseline(w, x, c0, target_s, metric="l2"):
     """The fp64 oracle (as it stands) on a bounded sample of the same workload: one iteration
     on the first `n` points of the first `p` problems against all K centroids, grown until it
-    takes ~0.6 * target_s (or covers everything), then scaled to B*N points."""
+    takes ~0.6 * target_s (or covers everything), then scaled to B*N points.  For Lloyd the
+    iteration is the oracle's own steps, timed apart: the assignment, then the arg-sort and the
+    update."""
     import numpy as np
     import oracle
     from oracle import similarity as sim
@@ -116,13 +162,20 @@ def cpu_baseline(w, x, c0, target_s, metric="l2"):
     n, p = min(w.N, 2048), 1
     while True:
         xs = W.storage_to_f64(x[:p, :n], w.dtype)
+        cs = c0[:p].astype(np.float64)
         t0 = time.perf_counter()
         if metric == "l2":
-            oracle.lloyd_iteration(xs, c0[:p].astype(np.float64), dtype=w.dtype, mode="modelled")
+            ct = oracle.centroid_operand(cs, w.dtype)
+            a, _, _ = oracle.assign_batched(xs, ct)
+            t1 = time.perf_counter()
+            for b in range(p):
+                oracle.argsort_ids(a[b], w.K)
+                oracle.update(xs[b], a[b], cs[b])
         else:
             if metric == "cosine":
                 xs = sim.round_to_dtype(sim.normalize_rows(xs), w.dtype)
-            sim.similarity_iteration(xs, c0[:p].astype(np.float64), metric, dtype=w.dtype, mode="modelled")
+            sim.similarity_iteration(xs, cs, metric, dtype=w.dtype, mode="modelled")
+            t1 = time.perf_counter()
         dt = time.perf_counter() - t0
         if dt >= 0.6 * target_s or (n >= w.N and p >= w.B):
             break
@@ -132,70 +185,260 @@ def cpu_baseline(w, x, c0, target_s, metric="l2"):
         else:
             p = min(w.B, max(p + 1, int(p * grow)))
     scale = (w.B * w.N) / (p * n)
-    return {"value": round(dt * scale * 1e3, 3), "unit": "ms", "cores": oracle.threads(), "kind": "oracle",
-            "sample": "one fp64 oracle iteration on %d of %d points (%d problem(s) x %d points, all K=%d "
-                      "centroids) took %.2f s; scaled by %.1fx to the full iteration" % (
-                          p * n, w.B * w.N, p, n, w.K, dt, scale)}
+    out = {"value": round(dt * scale * 1e3, 3), "unit": "ms", "cores": oracle.threads(), "kind": "oracle",
+           "sample": "one fp64 oracle iteration on %d of %d points (%d problem(s) x %d points, all K=%d "
+                     "centroids) took %.2f s; scaled by %.1fx to the full iteration" % (
+                         p * n, w.B * w.N, p, n, w.K, dt, scale),
+           "host": host_info()}
+    if metric == "l2":
+        out["assign_ms"] = round((t1 - t0) * scale * 1e3, 3)
+        out["update_ms"] = round((dt - (t1 - t0)) * scale * 1e3, 3)
+    return out
+
+
+# ------------------------------------------------------------------------------------------------
+# the standard path the method replaces (plain PyTorch; context only)
+# ------------------------------------------------------------------------------------------------
+def standard_assign(xt, c_master, chunk=None):
+    """Materialised-distance assignment: the [B, N, K] matrix of x.c~ from a batched product with
+    fp32 output (hipBLASLt), then ||c~||^2 - 2 x.c~ in fp32 and an argmin over K (the point norm is
+    a constant per point).  c~ is the centroid master cast to the points' dtype.  `chunk` splits N
+    (the matrix of one chunk is materialised at a time).  Returns int64 labels [B, N]."""
+    import torch
+    B, N, D = xt.shape
+    c_lp = c_master.to(xt.dtype)
+    c_lp_t = c_lp.transpose(1, 2).contiguous()          # [B, D, K], contiguous right operand
+    cn = (c_lp.float() ** 2).sum(-1)                     # ||c~||^2 from the rounded centroids
+    chunk = chunk or N
+    out = torch.empty((B, N), dtype=torch.int64, device=xt.device)
+    for lo in range(0, N, chunk):
+        xs = xt[:, lo:lo + chunk].contiguous()
+        try:
+            dots = torch.bmm(xs, c_lp_t, out_dtype=torch.float32)
+        except (RuntimeError, TypeError):
+            dots = torch.bmm(xs, c_lp_t).float()
+        dist = cn[:, None, :] - 2.0 * dots
+        del dots
+        out[:, lo:lo + chunk] = torch.argmin(dist, dim=-1)
+        del dist
+    return out
+
+
+def standard_update(xt, labels, c_old, chunk=1 << 22):
+    """Scatter-add update: every row added into its cluster's fp32 sum with atomics (index_add_),
+    counts by bincount, c = sum / n, empty clusters keep their centroid.  Returns (c_new [B, K, D]
+    fp32, counts [B, K])."""
+    import torch
+    B, N, D = xt.shape
+    K = c_old.shape[1]
+    flat = (labels + torch.arange(B, device=xt.device)[:, None] * K).reshape(-1)
+    xf = xt.reshape(B * N, D)
+    sums = torch.zeros(B * K, D, dtype=torch.float32, device=xt.device)
+    for lo in range(0, B * N, chunk):
+        sums.index_add_(0, flat[lo:lo + chunk], xf[lo:lo + chunk].float())
+    cnt = torch.bincount(flat, minlength=B * K)
+    newc = torch.where(cnt[:, None] > 0, sums / cnt.clamp(min=1)[:, None].float(), c_old.reshape(B * K, D))
+    return newc.view(B, K, D), cnt.view(B, K)
+
+
+def _event_ms(fn, reps, stream):
+    import numpy as np
+    import torch
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return float(np.median(ts))
 
 
 def standard_path(w, xt, c0t, reps, st):
-    """The standard path the method replaces, in plain PyTorch on the same GPU (context only):
-    assign materialises the B x N x K distance matrix (hipBLASLt batched product, fp32
-    distances, argmin over K); update scatter-adds every row into its cluster's fp32 sum
-    with atomics (index_add_) and divides by the bincount.  Returns medians in ms and the
-    label agreement with the FlashAssign labels of the same centroids."""
-    import numpy as np
+    """The standard path at the workload's shape, beside this path's stage times `st`."""
     import torch
     from exact_lloyd_means_02_amd import flashkm as fk
-    B, N, D, K = w.B, w.N, w.D, w.K
     stream = torch.cuda.current_stream()
-    c_lp = c0t.to(xt.dtype)
-    c_lp_t = c_lp.transpose(1, 2).contiguous()          # [B, D, K], contiguous right operand
-    cn = (c_lp.float() ** 2).sum(-1)                     # ||c~||^2 from the rounded centroids
-    xf = xt.view(B * N, D)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    ta, tu = [], []
-    lab = None
-    gemm_out = "fp32"
-    for _ in range(reps):
-        ev[0].record(stream)
-        if gemm_out == "fp32":
-            try:
-                dots = torch.bmm(xt, c_lp_t, out_dtype=torch.float32)   # [B, N, K], fp32 accumulate and output
-            except (RuntimeError, TypeError):
-                gemm_out = "input dtype"
-        if gemm_out != "fp32":
-            dots = torch.bmm(xt, c_lp_t)                 # [B, N, K] in the input dtype
-        dist = cn[:, None, :] - 2.0 * dots.float()       # ||x||^2 dropped: constant per point
-        lab = torch.argmin(dist, dim=-1)
-        del dots, dist
-        ev[1].record(stream)
-        flat = (lab + torch.arange(B, device=xt.device)[:, None] * K).view(-1)
-        sums = torch.zeros(B * K, D, dtype=torch.float32, device=xt.device)
-        sums.index_add_(0, flat, xf.float())
-        cnt = torch.bincount(flat, minlength=B * K)
-        newc = torch.where(cnt[:, None] > 0, sums / cnt.clamp(min=1)[:, None].float(), c0t.view(B * K, D))
-        ev[2].record(stream)
-        torch.cuda.synchronize()
-        ta.append(ev[0].elapsed_time(ev[1]))
-        tu.append(ev[1].elapsed_time(ev[2]))
-        del sums, cnt, newc, flat
+    lab = standard_assign(xt, c0t)
+    ma = _event_ms(lambda: standard_assign(xt, c0t), reps, stream)
+    mu = _event_ms(lambda: standard_update(xt, lab, c0t), reps, stream)
     prep = fk.kmeans_prepare_centroids(c0t, xt)
     a, _ = fk.kmeans_assign_prepared(xt, prep)
     agree = float((a.long() == lab).float().mean().item())
-    ma, mu = float(np.median(ta)), float(np.median(tu))
-    return {"what": "plain PyTorch on the same GPU: bmm + fp32 distances + argmin; index_add_ scatter + bincount",
-            "gemm_output": gemm_out, "materialised_assign_ms": round(ma, 4), "scatter_update_ms": round(mu, 4),
+    return {"what": "plain PyTorch on the same GPU: bmm (fp32 out) + fp32 distances + argmin; index_add_ "
+                    "scatter + bincount", "materialised_assign_ms": round(ma, 4), "scatter_update_ms": round(mu, 4),
             "assign_speedup": round(ma / st["assign"], 2),
-            "update_speedup": round(mu / (st["argsort"] + st["update"]), 2),
-            "label_agreement": agree}
+            "update_speedup": round(mu / (st["argsort"] + st["update"]), 2), "label_agreement": agree}
+
+
+def context_pages():
+    """The pages' kernel-ratio shapes (paper summary, "Key claims" and "Results"): assignment at
+    N = 2^20, K = 8192 (B = 1; D = 128, bf16: the pages state neither) and update at B = 1,
+    N = 2^25, K = 4096 (D = 128, bf16, 8.6 GB of points), the standard path against this path on
+    the same inputs, and the standard update's effective bandwidth (the pages quote about 50 GB/s
+    for the scatter-atomic update under hot-cluster contention on H200)."""
+    import numpy as np
+    import torch
+    from exact_lloyd_means_02_amd import flashkm as fk
+    from exact_lloyd_means_02_amd import workloads as W
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    out = {"what": "standard path (plain PyTorch) vs this path at the pages' kernel-ratio shapes, one MI355X"}
+    # assignment: B=1, N=2^20, K=8192, D=128 bf16 (GMM points, K seeded point picks)
+    wa = W.small("headline_bf16", B=1, N=1 << 20, K=8192, M=8192)
+    print("bench: context assign %s" % (wa,), file=sys.stderr, flush=True)
+    x, c0, _ = W.make(wa)
+    xt = W.to_torch(x, wa.dtype).to(dev)
+    ct = torch.from_numpy(c0).to(dev)
+    lab = standard_assign(xt, ct, chunk=1 << 18)
+    t_std = _event_ms(lambda: standard_assign(xt, ct, chunk=1 << 18), 3, stream)
+    prep = fk.kmeans_prepare_centroids(ct, xt)
+    a, _ = fk.kmeans_assign_prepared(xt, prep)
+    t_fa = _event_ms(lambda: fk.kmeans_assign_prepared(xt, prep, assign=a), 5, stream)
+    out["assign"] = {"B": 1, "N": wa.N, "K": wa.K, "D": wa.D, "dtype": wa.dtype,
+                     "standard_ms": round(t_std, 3), "flashassign_ms": round(t_fa, 3),
+                     "speedup": round(t_std / t_fa, 2),
+                     "label_agreement": float((a.long() == lab).float().mean().item()),
+                     "pages_H200": "122.5 ms -> 5.8 ms (21.2x)"}
+    del x, xt, lab, prep, a
+    torch.cuda.empty_cache()
+    # update: B=1, N=2^25, K=4096, D=128 bf16, Zipf(1.2) hot clusters (the skewed recipe)
+    wu = W.small("skew_bf16_k4096", N=1 << 25)
+    print("bench: context update %s" % (wu,), file=sys.stderr, flush=True)
+    x, c0, _ = W.make(wu)
+    xt = W.to_torch(x, wu.dtype).to(dev)
+    del x
+    ct = torch.from_numpy(c0).to(dev)
+    prep = fk.kmeans_prepare_centroids(ct, xt)
+    a, _ = fk.kmeans_assign_prepared(xt, prep)
+    t_std_u = _event_ms(lambda: standard_update(xt, a.long(), ct), 3, stream)
+    s_ids, s_idx, counts = fk.kmeans_argsort_ids(a, wu.K)
+    cu = ct.clone()
+
+    def ours():
+        fk.kmeans_argsort_ids(a, wu.K, sorted_ids=s_ids, sorted_idx=s_idx, counts=counts)
+        fk.kmeans_update(xt, s_ids, s_idx, counts, cu)
+    ours()
+    t_ours = _event_ms(ours, 5, stream)
+    nbytes = W.nbytes(wu)
+    out["update"] = {"B": 1, "N": wu.N, "K": wu.K, "D": wu.D, "dtype": wu.dtype, "points_GB": round(nbytes / 1e9, 2),
+                     "largest_cluster_share": round(float(counts.max().item()) / wu.N, 3),
+                     "standard_scatter_ms": round(t_std_u, 3), "argsort_plus_update_ms": round(t_ours, 3),
+                     "speedup": round(t_std_u / t_ours, 2),
+                     "standard_effective_GBs": round(nbytes / (t_std_u * 1e-3) / 1e9, 1),
+                     "ours_effective_GBs": round(nbytes / (t_ours * 1e-3) / 1e9, 1),
+                     "pages_H200": "up to 6.3x; scatter-atomic update about 50 GB/s"}
+    print(json.dumps(out), flush=True)
+
+
+# ------------------------------------------------------------------------------------------------
+# rocprofv3 kernel-trace summary
+# ------------------------------------------------------------------------------------------------
+KERNEL_TAGS = [("assign_small_d", "assign"), ("assign_split_d", "assign"), ("sort_hist", "hist"),
+               ("sort_scatter", "scatter"), ("sort_rowscan", "rowscan"), ("segment_counts", "segcounts"),
+               ("upd_segsum", "segsum"), ("upd_prologue", "prologue"), ("prep_centroids", "prep"),
+               ("rows_short", "rownorm"), ("row_norms", "rownorm"), ("fill_i32", "fill"),
+               ("sum_f64_rows", "sumrows"), ("copyBuffer", "copy"), ("upd_finalize", "finalize")]
+
+
+def summarize_trace(path, args):
+    """Per-iteration summary of a `rocprofv3 --kernel-trace` CSV of this script: the FlashAssign
+    launches of the per-stage timings (the launches `roofline` averages) and the timed fit's
+    iterations (kernel time, span from the first kernel's start to the last one's end, and the
+    idle gap before each iteration)."""
+    import csv
+    import numpy as np
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+
+    def tag(n):
+        for k, t in KERNEL_TAGS:
+            if k in n:
+                return t
+        return n[:24]
+    seq = [(tag(r["Kernel_Name"]), int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows]
+    names = [s[0] for s in seq]
+    # stage calls: row norms, prep, assign; the first such triple is the untimed priming call
+    stage_assign = [(seq[i + 2][2] - seq[i + 2][1]) / 1e3 for i in range(len(seq) - 2)
+                    if names[i] == "rownorm" and names[i + 1] == "prep" and names[i + 2] == "assign"][1:]
+    # fits: prep, fill, then iterations (each from an assign to the next one) until the next
+    # prep or row-norm kernel (another fit or stage call); the fit's inertia sums and copies to
+    # the host are not counted in an iteration's kernels
+    fits = []
+    i = 0
+    while i < len(seq) - 1:
+        if names[i] == "prep" and names[i + 1] == "fill":
+            its, j, cur = [], i + 2, []
+            while j < len(seq) and names[j] not in ("prep", "rownorm"):
+                if names[j] == "assign" and cur:
+                    its.append(cur)
+                    cur = []
+                if names[j] not in ("sumrows", "fill", "copy"):
+                    cur.append(seq[j])
+                j += 1
+            if cur:
+                its.append(cur)
+            fits.append(its)
+            i = j
+        else:
+            i += 1
+    lines = ["# rocprofv3 kernel trace summary (bench.py --summarize-trace)", "source: %s" % os.path.basename(path)]
+    lines.append("FlashAssign launches of the per-stage timings: %d, mean %.2f us, median %.2f us, min %.2f us" % (
+        len(stage_assign), np.mean(stage_assign), np.median(stage_assign), np.min(stage_assign)))
+    flops = 2.0 * 32 * 65536 * 1024 * 128
+    lines.append("  2*B*N*K*D / mean / 2.5 PFLOP/s = %.4f (headline shape)" % (flops / (np.mean(stage_assign) * 1e-6)
+                                                                              / 2.5e15))
+    lines.append("fits found: %d (iterations: %s)" % (len(fits), [len(f) for f in fits]))
+    if len(fits) >= 2:
+        timed = fits[1]
+        lines.append("timed fit (the second fit): %d iterations" % len(timed))
+        lines.append("  it  assign   hist  scatter  segsum | kernels   span   gap-before (us)")
+        prev_end = None
+        tot_k, tot_span, tot_gap = 0.0, 0.0, 0.0
+        per = {}
+        for t, it in enumerate(timed):
+            d = {}
+            for n, s0, e0 in it:
+                d[n] = d.get(n, 0.0) + (e0 - s0) / 1e3
+                per.setdefault(n, []).append((e0 - s0) / 1e3)
+            k = sum(d.values())
+            span = (it[-1][2] - it[0][1]) / 1e3
+            gap = (it[0][1] - prev_end) / 1e3 if prev_end is not None else 0.0
+            prev_end = it[-1][2]
+            tot_k += k
+            tot_span += span
+            tot_gap += gap if t > 0 else 0.0
+            lines.append("  %2d %7.1f %6.1f %7.1f %7.1f | %7.1f %7.1f %7.1f" % (
+                t, d.get("assign", 0), d.get("hist", 0), d.get("scatter", 0), d.get("segsum", 0), k, span, gap))
+        n = len(timed)
+        lines.append("  per iteration: kernels %.1f us, span %.1f us, gaps between iterations %.2f us" % (
+            tot_k / n, tot_span / n, tot_gap / max(1, n - 1)))
+        lines.append("  per kernel mean: " + ", ".join("%s %.1f" % (k, np.mean(v)) for k, v in per.items()))
+    print("\n".join(lines))
+
+
+# ------------------------------------------------------------------------------------------------
+# the streamed (pinned host) workload
+# ------------------------------------------------------------------------------------------------
+def pinned_blocks(w, block_points=1 << 27):
+    """The workload's points in pinned host blocks of `block_points` rows (the last one shorter),
+    generated in place (B = 1).  Returns (torch tensors, numpy views)."""
+    import torch
+    from exact_lloyd_means_02_amd import workloads as W
+    sizes = [min(block_points, w.N - lo) for lo in range(0, w.N, block_points)]
+    tb = [torch.empty((n, w.D), dtype=W.torch_dtype(w.dtype), pin_memory=True) for n in sizes]
+    # numpy views sharing the pinned memory (bf16 as its uint16 bit patterns)
+    nb = [t.view(torch.int16).numpy().view("uint16") if w.dtype == "bf16" else t.numpy() for t in tb]
+    W.generate_points(w, out_blocks=nb)
+    return tb, nb
 
 
 def bench_streamed(args, w):
-    """Host-resident workload: x in pinned host memory, streamed in chunks by kmeans_fit.  Reports
+    """Host-resident workload: x in pinned host memory (blocks of 2^27 points, so no single
+    allocation exceeds 16 GiB at D = 64 fp16), streamed in chunks by kmeans_fit_blocks.  Reports
     ms per Lloyd iteration, the plain host->device copy rate of the same chunks and the GPU time
     of one iteration on one device-resident chunk (the two legs the pipeline overlaps)."""
-    import numpy as np
     import torch
     from exact_lloyd_means_02_amd import flashkm as fk
     from exact_lloyd_means_02_amd import workloads as W
@@ -204,30 +447,31 @@ def bench_streamed(args, w):
     if n_override:
         w = W.small(w.name, N=n_override)
     steps = args.steps if args.steps != 20 else w.iters
-    print("bench: allocating %.1f GiB of pinned host memory for %s" % (W.nbytes(w) / 2 ** 30, w),
-          file=sys.stderr, flush=True)
+    print("bench: allocating %.1f GiB of pinned host memory (blocks of 2^27 points) for %s" % (
+        W.nbytes(w) / 2 ** 30, w), file=sys.stderr, flush=True)
     t0 = time.perf_counter()
-    xh = torch.empty((w.B, w.N, w.D), dtype=W.torch_dtype(w.dtype), pin_memory=True)
-    x = W.from_torch(xh, w.dtype)
-    print("bench: pinned in %.1f s; generating" % (time.perf_counter() - t0), file=sys.stderr, flush=True)
-    W.generate_points(w, x)
-    c0 = W.init_centroids(w, x)
+    tb, nb = pinned_blocks(w)
+    c0 = W.init_centroids_blocks(w, nb)
     dev = torch.device("cuda:0")
     c0t = torch.from_numpy(c0).to(dev)
-    print("bench: generated in %.1f s" % (time.perf_counter() - t0), file=sys.stderr, flush=True)
+    print("bench: pinned and generated in %.1f s (%d blocks)" % (time.perf_counter() - t0, len(tb)),
+          file=sys.stderr, flush=True)
 
     # leg 1: plain chunked host->device copies (two staging buffers, one stream)
     chunk = w.chunk
-    bufs = [torch.empty((chunk, w.D), dtype=xh.dtype, device=dev) for _ in range(2)]
+    bufs = [torch.empty((chunk, w.D), dtype=tb[0].dtype, device=dev) for _ in range(2)]
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    for q, lo in enumerate(range(0, w.N, chunk)):
-        n = min(chunk, w.N - lo)
-        bufs[q & 1][:n].copy_(xh[0, lo:lo + n], non_blocking=True)
+    q = 0
+    for t in tb:
+        for lo in range(0, t.shape[0], chunk):
+            n = min(chunk, t.shape[0] - lo)
+            bufs[q & 1][:n].copy_(t[lo:lo + n], non_blocking=True)
+            q += 1
     torch.cuda.synchronize()
     h2d_s = time.perf_counter() - t1
     # leg 2: one iteration on one device-resident chunk
-    xc = xh[:, :chunk].to(dev)
+    xc = tb[0][:chunk].to(dev)[None]
     cc = c0t.clone()
     fk.kmeans_fit(xc, cc, 1, 0.0)
     torch.cuda.synchronize()
@@ -243,7 +487,7 @@ def bench_streamed(args, w):
     c = c0t.clone()
     torch.cuda.synchronize()
     t3 = time.perf_counter()
-    _, inertia, done = fk.kmeans_fit(xh, c, steps, 0.0, chunk_points=chunk, want_assign=False)
+    _, inertia, done = fk.kmeans_fit_blocks(tb, c, steps, 0.0, chunk_points=chunk, want_assign=False)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t3) * 1e3 / steps
     nchunks = -(-w.N // chunk)
@@ -254,7 +498,7 @@ def bench_streamed(args, w):
         "warmup": 0, "ms_per_step": round(ms, 2), "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "N": w.N, "D": w.D, "K": w.K, "chunk_points": chunk,
-                   "chunks": nchunks, "iters": steps, "inputs": "pinned host"},
+                   "chunks": nchunks, "host_blocks": len(tb), "iters": steps, "inputs": "pinned host"},
         "assign_tflops_effective": round(flops / (ms * 1e-3) / 1e12, 1),
         "h2d_GBs_plain_copy": round(W.nbytes(w) / h2d_s / 1e9, 1),
         "h2d_ms_per_iteration": round(h2d_s * 1e3, 1),
@@ -265,14 +509,56 @@ def bench_streamed(args, w):
     print(json.dumps(out), flush=True)
 
 
+# ------------------------------------------------------------------------------------------------
+# the device-resident workloads
+# ------------------------------------------------------------------------------------------------
+def stage_times(fk, w, xt, c0t, reps, metric, stream):
+    """Teacher-forced stage calls from c0, each bracketed by HIP events on `stream`; returns the
+    medians (ms) and the FlashAssign launches' individual times."""
+    import numpy as np
+    import torch
+    xn = fk.kmeans_row_norms(xt)
+    prep = fk.kmeans_prepare_centroids(c0t, xt, metric=metric)
+    a, md = fk.kmeans_assign_prepared(xt, prep, x_norms=xn, want_min_dist=True)
+    s_ids, s_idx, counts = fk.kmeans_argsort_ids(a, w.K)
+    cu = c0t.clone()
+    torch.cuda.synchronize()
+    names = ["row_norms", "prepare", "assign", "argsort", "update"]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    times = {k: [] for k in names}
+    for _ in range(reps):
+        cu.copy_(c0t)
+        ev[0].record(stream)
+        fk.kmeans_row_norms(xt, out=xn)
+        ev[1].record(stream)
+        fk.kmeans_prepare_centroids(c0t, xt, out=prep.buf, metric=metric)
+        ev[2].record(stream)
+        fk.kmeans_assign_prepared(xt, prep, x_norms=xn, assign=a, min_dist=md)
+        ev[3].record(stream)
+        fk.kmeans_argsort_ids(a, w.K, sorted_ids=s_ids, sorted_idx=s_idx, counts=counts)
+        ev[4].record(stream)
+        fk.kmeans_update(xt, s_ids, s_idx, counts, cu)
+        ev[5].record(stream)
+        torch.cuda.synchronize()
+        for i, k in enumerate(names):
+            times[k].append(ev[i].elapsed_time(ev[i + 1]))
+    return {k: float(np.median(v)) for k, v in times.items()}, times["assign"]
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only (no multi-GPU path); --gpus %d is not supported"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args)
+        return
     if args.copy_calib:
         copy_calib()
+        return
+    if args.context_pages:
+        context_pages()
         return
     import numpy as np
     import torch
@@ -291,57 +577,40 @@ def main():
     c = c0t.clone()
     stream = torch.cuda.current_stream(dev)
 
+    # ---- 1. per-stage times (HIP events on the stages' stream), teacher forced from c0
+    st, assign_launches = stage_times(fk, w, xt, c0t, args.stage_reps, args.metric, stream)
+
     def fit(iters):
         if args.metric == "l2":
             return fk.kmeans_fit(xt, c, iters, 0.0)
         return fk.kmeans_fit_metric(xt, c, args.metric, iters, 0.0)
 
-    # ---- warmup (untimed): W iterations
-    fit(max(1, args.warmup))
+    # ---- 2. warmup (untimed): W iterations
+    if args.warmup > 0:
+        fit(args.warmup)
     torch.cuda.synchronize()
 
-    # ---- timed: exactly `steps` iterations in one fit
-    c.copy_(c0t)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    _, inertia, done = fit(args.steps)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    assert done == args.steps
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    print("bench: %d iterations in %.3f ms" % (args.steps, (t1 - t0) * 1e3), file=sys.stderr, flush=True)
-
-    # ---- per-stage times (HIP events on the stages' stream), teacher forced from c0
-    xn = fk.kmeans_row_norms(xt)
-    prep = fk.kmeans_prepare_centroids(c0t, xt, metric=args.metric)
-    a, md = fk.kmeans_assign_prepared(xt, prep, x_norms=xn, want_min_dist=True)
-    s_ids, s_idx, counts = fk.kmeans_argsort_ids(a, w.K)
-    cu = c0t.clone()
-    torch.cuda.synchronize()
-    R = args.stage_reps
-    names = ["row_norms", "prepare", "assign", "argsort", "update"]
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-    times = {k: [] for k in names}
-    for _ in range(R):
-        cu.copy_(c0t)
-        ev[0].record(stream)
-        fk.kmeans_row_norms(xt, out=xn)
-        ev[1].record(stream)
-        fk.kmeans_prepare_centroids(c0t, xt, out=prep.buf, metric=args.metric)
-        ev[2].record(stream)
-        fk.kmeans_assign_prepared(xt, prep, x_norms=xn, assign=a, min_dist=md)
-        ev[3].record(stream)
-        fk.kmeans_argsort_ids(a, w.K, sorted_ids=s_ids, sorted_idx=s_idx, counts=counts)
-        ev[4].record(stream)
-        fk.kmeans_update(xt, s_ids, s_idx, counts, cu)
-        ev[5].record(stream)
+    # ---- 3. timed: exactly `steps` iterations in one fit (then `repeat` more, reported apart)
+    runs = []
+    for r in range(1 + max(0, args.repeat)):
+        c.copy_(c0t)
         torch.cuda.synchronize()
-        for i, k in enumerate(names):
-            times[k].append(ev[i].elapsed_time(ev[i + 1]))
-    st = {k: float(np.median(v)) for k, v in times.items()}
+        t0 = time.perf_counter()
+        _, inertia, done = fit(args.steps)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        assert done == args.steps
+        runs.append((t1 - t0) * 1e3 / args.steps)
+        if r == 0:
+            inertia_first = inertia
+    ms_per_step = runs[0]
+    print("bench: %d iterations in %.3f ms (repeats: %s ms per iteration)" % (
+        args.steps, ms_per_step * args.steps, ["%.4f" % v for v in runs[1:]]), file=sys.stderr, flush=True)
+
     flops, abytes, ubytes = algorithmic(w)
     peak = PEAK_TFLOPS[w.dtype]
-    assign_tflops = flops / (st["assign"] * 1e-3) / 1e12
+    assign_ms = float(np.mean(assign_launches))      # the mean the kernel trace reproduces
+    assign_tflops = flops / (assign_ms * 1e-3) / 1e12
     upd_ms = st["argsort"] + st["update"]
     upd_gbs = ubytes / (upd_ms * 1e-3) / 1e9
 
@@ -362,17 +631,19 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "N": w.N, "D": w.D, "K": w.K, "iters": args.steps, "tol": 0.0,
                    "inputs": "HBM-resident", "metric": args.metric},
+        "repeat_ms_per_step": [round(v, 4) for v in runs[1:]],
         "roofline": {"bound": "mfma", "achieved": round(assign_tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(assign_tflops / peak, 4), "traffic": measured_traffic(w.name),
                      "kernel": "FlashAssign (%s) kernel, one launch per kmeans_assign_prepared call" % (
                          "small-D" if fk.kmeans_plan(fk.dtype_code(xt), w.B, w.N, w.D, w.K)["path"] == 0 else "split-D"),
-                     "kernel_ms": round(st["assign"], 4), "flop_per_launch": flops,
+                     "kernel_ms": round(assign_ms, 4), "kernel_ms_median": round(st["assign"], 4),
+                     "launches": len(assign_launches), "flop_per_launch": flops,
                      "algorithmic_bytes_per_launch": abytes},
         "stages_ms": {k: round(v, 4) for k, v in st.items()},
         "update": {"bound": "hbm", "achieved": round(upd_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                    "frac": round(upd_gbs / PEAK_HBM_GBS, 4), "bytes_per_iter": ubytes,
                    "stages": "kmeans_argsort_ids + kmeans_update"},
-        ("inertia_last" if args.metric == "l2" else "similarity_last"): [float(v) for v in inertia[-1][:2]],
+        ("inertia_last" if args.metric == "l2" else "similarity_last"): [float(v) for v in inertia_first[-1][:2]],
     }
     if args.context:
         print("bench: timing the standard path", file=sys.stderr, flush=True)

@@ -6,6 +6,7 @@
 
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/flashkm.h"
 #include "common.h"
@@ -718,9 +719,26 @@ struct StreamedPipe {
     }
 };
 
+// Where the streamed path finds the points: one contiguous pinned [B, N, D] array, or (B = 1) the
+// rows of one problem split over pinned blocks, block j holding rows [base[j], base[j+1]).
+struct HostSource {
+    const void *x = nullptr;            // contiguous, or nullptr
+    const void *const *blocks = nullptr;
+    const int64_t *base = nullptr;      // nblocks + 1 row offsets
+    int nblocks = 0;
+    size_t row_bytes = 0;
+    // rows [lo, lo + n) of problem b lie in one block (the blocks hold whole chunks)
+    const char *rows(int64_t b, int64_t N, int64_t lo) const {
+        if (x) return (const char *)x + ((size_t)b * N + lo) * row_bytes;
+        int j = 0;
+        while (j + 1 < nblocks && base[j + 1] <= lo) ++j;
+        return (const char *)blocks[j] + (size_t)(lo - base[j]) * row_bytes;
+    }
+};
+
 // metric as in fit_device.  Cosine k-means turns each staged chunk into unit rows in place (the
 // staging buffer is a device copy of x) before its assign and update.
-km_status_t fit_host(int dt, const void *xh, int64_t B, int64_t N, int64_t D, int64_t K, int iters, float tol,
+km_status_t fit_host(int dt, const HostSource &src, int64_t B, int64_t N, int64_t D, int64_t K, int iters, float tol,
                      int64_t chunk_points, float *C, int32_t *assign, double *inertia, int32_t *iters_done, char *ws,
                      hipStream_t s, int metric = KM_METRIC_L2) {
     const HostLayout L = host_layout(dt, B, N, D, K, chunk_points);
@@ -774,8 +792,7 @@ km_status_t fit_host(int dt, const void *xh, int64_t B, int64_t N, int64_t D, in
         chunk_rows(q, &b, &lo, &n);
         const int buf = (int)(q & 1);
         KM_HIP(hipStreamWaitEvent(P.cs, P.ev_free[buf], 0));
-        KM_HIP(hipMemcpyAsync(stage_buf[buf], (const char *)xh + ((size_t)b * N + lo) * D * es, (size_t)n * D * es,
-                              hipMemcpyHostToDevice, P.cs));
+        KM_HIP(hipMemcpyAsync(stage_buf[buf], src.rows(b, N, lo), (size_t)n * D * es, hipMemcpyHostToDevice, P.cs));
         KM_HIP(hipEventRecord(P.ev_copy[buf], P.cs));
         return ok();
     };
@@ -873,7 +890,10 @@ extern "C" km_status_t kmeans_fit_metric(const void *x, km_dtype_t dt, km_metric
                           (hipStream_t)stream, (int)metric);
     }
     KM_TRY(check_ws(ws, ws_bytes, host_layout(dt, B, N, D, K, chunk_points).total));
-    return fit_host(dt, x, B, N, D, K, iters, tol, chunk_points, centroids, assign, objective, iters_done,
+    HostSource src;
+    src.x = x;
+    src.row_bytes = (size_t)D * elem_bytes(dt);
+    return fit_host(dt, src, B, N, D, K, iters, tol, chunk_points, centroids, assign, objective, iters_done,
                     (char *)ws, (hipStream_t)stream, (int)metric);
 }
 
@@ -902,6 +922,54 @@ extern "C" km_status_t kmeans_fit(const void *x, km_dtype_t dt, int64_t B, int64
         return fit_device(dt, x, B, N, D, K, iters, tol, centroids, assign, inertia, iters_done, (char *)ws, s);
     }
     KM_TRY(check_ws(ws, ws_bytes, host_layout(dt, B, N, D, K, chunk_points).total));
-    return fit_host(dt, x, B, N, D, K, iters, tol, chunk_points, centroids, assign, inertia, iters_done, (char *)ws,
+    HostSource src;
+    src.x = x;
+    src.row_bytes = (size_t)D * elem_bytes(dt);
+    return fit_host(dt, src, B, N, D, K, iters, tol, chunk_points, centroids, assign, inertia, iters_done, (char *)ws,
                     s);
+}
+
+extern "C" km_status_t kmeans_fit_blocks(const void *const *x_blocks, const int64_t *block_points, int32_t nblocks,
+                                         km_dtype_t dt, int64_t D, int64_t K, int32_t iters, float tol,
+                                         int64_t chunk_points, float *centroids, int32_t *assign, double *inertia,
+                                         int32_t *iters_done, void *ws, size_t ws_bytes, void *stream) {
+    if (!x_blocks || !block_points) return fail(KM_ERR_INVALID, "x_blocks and block_points must not be NULL");
+    if (nblocks < 1 || nblocks > 4096) return fail(KM_ERR_INVALID, "nblocks must be in [1, 4096] (got %d)", nblocks);
+    if (chunk_points < 0) return fail(KM_ERR_INVALID, "chunk_points must be >= 0");
+    int64_t N = 0;
+    for (int j = 0; j < nblocks; ++j) {
+        if (!x_blocks[j]) return fail(KM_ERR_INVALID, "block %d is NULL", j);
+        if (block_points[j] < 1) return fail(KM_ERR_INVALID, "block %d holds %lld points", j, (long long)block_points[j]);
+        if (((uintptr_t)x_blocks[j] & 15) != 0) return fail(KM_ERR_INVALID, "block %d must be 16-byte aligned", j);
+        N += block_points[j];
+        if (N >= MAX_N) return fail(KM_ERR_INVALID, "the blocks hold 2^31 points or more");
+    }
+    KM_TRY(check_shape(dt, 1, N, D, K));
+    const int64_t c = host_chunk(N, chunk_points);
+    for (int j = 0; j + 1 < nblocks; ++j)
+        if (block_points[j] % c != 0)
+            return fail(KM_ERR_INVALID, "block %d holds %lld points, not a multiple of the %lld-point chunk", j,
+                        (long long)block_points[j], (long long)c);
+    KM_TRY(check_ptr(centroids, "centroids"));
+    if (iters < 1) return fail(KM_ERR_INVALID, "iters must be >= 1");
+    if (!(tol >= 0.f)) return fail(KM_ERR_INVALID, "tol must be >= 0");
+    if (((uintptr_t)centroids & 15) != 0) return fail(KM_ERR_INVALID, "centroids must be 16-byte aligned");
+    if (!ws) return fail(KM_ERR_WORKSPACE, "workspace is NULL");
+    KM_TRY(check_ws(ws, ws_bytes, host_layout(dt, 1, N, D, K, chunk_points).total));
+    KM_TRY(check_device_arch());
+    for (int j = 0; j < nblocks; ++j)
+        if (pointer_kind(x_blocks[j]) != PTR_PINNED_HOST)
+            return fail(KM_ERR_UNSUPPORTED, "block %d is not pinned host memory", j);
+    KM_TRY(require_device(centroids, "centroids"));
+    KM_TRY(require_device(assign, "assign"));
+    KM_TRY(require_device(ws, "ws"));
+    std::vector<int64_t> base((size_t)nblocks + 1, 0);
+    for (int j = 0; j < nblocks; ++j) base[(size_t)j + 1] = base[(size_t)j] + block_points[j];
+    HostSource src;
+    src.blocks = x_blocks;
+    src.base = base.data();
+    src.nblocks = nblocks;
+    src.row_bytes = (size_t)D * elem_bytes(dt);
+    return fit_host(dt, src, 1, N, D, K, iters, tol, chunk_points, centroids, assign, inertia, iters_done, (char *)ws,
+                    (hipStream_t)stream);
 }

@@ -24,9 +24,9 @@ STATUS_NAMES = {0: "KM_OK", -1: "KM_ERR_INVALID", -2: "KM_ERR_UNSUPPORTED", -3: 
 
 # every symbol the header declares
 EXPORTS = ["kmeans_plan", "kmeans_workspace_bytes", "kmeans_row_norms", "kmeans_assign", "kmeans_assign_noalloc",
-           "kmeans_prepare_centroids",
-           "kmeans_assign_prepared", "kmeans_argsort_ids", "kmeans_argsort_status", "kmeans_update", "kmeans_fit",
-           "kmeans_normalize_rows", "kmeans_prepare_centroids_metric", "kmeans_fit_metric", "kmeans_last_error"]
+           "kmeans_prepare_centroids", "kmeans_assign_prepared", "kmeans_argsort_ids", "kmeans_argsort_status",
+           "kmeans_update", "kmeans_fit", "kmeans_fit_blocks", "kmeans_normalize_rows",
+           "kmeans_prepare_centroids_metric", "kmeans_fit_metric", "kmeans_last_error"]
 
 
 class KmPlan(ctypes.Structure):
@@ -61,12 +61,15 @@ def _load():
     lib.kmeans_argsort_status.argtypes = [vp, sz, vp]
     lib.kmeans_update.argtypes = [vp, ctypes.c_int, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, sz, vp]
     lib.kmeans_fit.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, i32, f32, i64, vp, vp, vp, vp, vp, sz, vp]
+    lib.kmeans_fit_blocks.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(i64), i32, ctypes.c_int, i64, i64, i32, f32,
+                                      i64, vp, vp, vp, vp, vp, sz, vp]
     lib.kmeans_normalize_rows.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp]
     lib.kmeans_prepare_centroids_metric.argtypes = [vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64, vp, sz, vp]
     lib.kmeans_fit_metric.argtypes = [vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64, i32, f32, i64, vp, vp, vp,
                                       vp, vp, sz, vp]
     for n in ("kmeans_plan", "kmeans_row_norms", "kmeans_assign", "kmeans_assign_noalloc", "kmeans_prepare_centroids",
-              "kmeans_assign_prepared", "kmeans_argsort_ids", "kmeans_argsort_status", "kmeans_update", "kmeans_fit", "kmeans_normalize_rows",
+              "kmeans_assign_prepared", "kmeans_argsort_ids", "kmeans_argsort_status", "kmeans_update", "kmeans_fit",
+              "kmeans_fit_blocks", "kmeans_normalize_rows",
               "kmeans_prepare_centroids_metric", "kmeans_fit_metric"):
         getattr(lib, n).restype = ctypes.c_int
     lib.kmeans_last_error.argtypes = []
@@ -342,6 +345,39 @@ def kmeans_fit(x, centroids, iters: int, tol: float = 0.0, chunk_points: int = 0
     _check(LIB.kmeans_fit(_ptr(x), dt, B, N, D, K, int(iters), float(tol), int(chunk_points), _ptr(centroids),
                           _ptr(assign), inertia.ctypes.data_as(ctypes.c_void_p), ctypes.byref(done), _ptr(ws),
                           ws.numel(), st))
+    return assign, inertia[: done.value], done.value
+
+
+def kmeans_fit_blocks(blocks, centroids, iters: int, tol: float = 0.0, chunk_points: int = 0, assign=None,
+                      want_assign=True, stream=None):
+    """Lloyd's loop, streamed, for one problem whose points are split over pinned host tensors
+    `blocks` ([n_j, D] each, one dtype; every block but the last a multiple of the chunk).
+    `centroids` (device f32 [1, K, D]) holds the init and receives the result.  Returns (assign
+    [1, N] or None, inertia [iters_done, 1] numpy float64, iters_done)."""
+    torch = _torch()
+    import numpy as np
+    _need(len(blocks) >= 1, "at least one block")
+    D = blocks[0].shape[-1]
+    for t in blocks:
+        _need(t.dim() == 2 and t.shape[1] == D and t.is_contiguous() and t.dtype == blocks[0].dtype
+              and not t.is_cuda, "blocks: contiguous host [n, D] tensors of one dtype")
+    _need(centroids.is_cuda and centroids.dtype == torch.float32 and centroids.is_contiguous()
+          and centroids.dim() == 3 and centroids.shape[0] == 1, "centroids: device f32 [1, K, D]")
+    K = centroids.shape[1]
+    N = sum(int(t.shape[0]) for t in blocks)
+    dev = centroids.device
+    if want_assign and assign is None:
+        assign = torch.empty((1, N), dtype=torch.int32, device=dev)
+    dt = dtype_code(blocks[0])
+    st = _stream(centroids, stream)
+    ws = workspace(KM_OP_FIT_HOST, dt, 1, N, D, K, dev, chunk_points, stream=st)
+    ptrs = (ctypes.c_void_p * len(blocks))(*[t.data_ptr() for t in blocks])
+    npts = (ctypes.c_int64 * len(blocks))(*[int(t.shape[0]) for t in blocks])
+    inertia = np.zeros((iters, 1), dtype=np.float64)
+    done = ctypes.c_int32(0)
+    _check(LIB.kmeans_fit_blocks(ptrs, npts, len(blocks), dt, D, K, int(iters), float(tol), int(chunk_points),
+                                 _ptr(centroids), _ptr(assign), inertia.ctypes.data_as(ctypes.c_void_p),
+                                 ctypes.byref(done), _ptr(ws), ws.numel(), st))
     return assign, inertia[: done.value], done.value
 
 

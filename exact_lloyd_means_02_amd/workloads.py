@@ -179,14 +179,28 @@ def _threads() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
 
-def generate_points(w: Workload, out: np.ndarray | None = None) -> np.ndarray:
+def generate_points(w: Workload, out: np.ndarray | None = None, out_blocks=None) -> np.ndarray:
     """Points [B, N, D] in the storage dtype (uncentred).  `out` may be a preallocated
-    (e.g. pinned-host) numpy view of that shape."""
+    (e.g. pinned-host) numpy view of that shape.  With `out_blocks` (B = 1: a list of [n_j, D]
+    arrays holding consecutive rows, every one but the last a multiple of 2^20 rows) the same
+    points are written into the blocks instead, and the list is returned."""
     ss = np.random.SeedSequence(BASE_SEED + w.seed_id)
     ss_means, ss_data, _ = ss.spawn(3)
-    if out is None:
-        out = np.empty((w.B, w.N, w.D), dtype=NP_STORAGE[w.dtype])
-    assert out.shape == (w.B, w.N, w.D)
+    if out_blocks is not None:
+        assert w.B == 1 and sum(bl.shape[0] for bl in out_blocks) == w.N
+        assert all(bl.shape[0] % BLOCK_POINTS == 0 for bl in out_blocks[:-1])
+        starts = np.cumsum([0] + [bl.shape[0] for bl in out_blocks])
+
+        def dest(b, lo, hi):
+            j = int(np.searchsorted(starts, lo, side="right")) - 1
+            return out_blocks[j][lo - starts[j]:hi - starts[j]]
+    else:
+        if out is None:
+            out = np.empty((w.B, w.N, w.D), dtype=NP_STORAGE[w.dtype])
+        assert out.shape == (w.B, w.N, w.D)
+
+        def dest(b, lo, hi):
+            return out[b, lo:hi]
     p = _weights(w)
     jobs = []
     mean_children = ss_means.spawn(w.B)
@@ -203,11 +217,11 @@ def generate_points(w: Workload, out: np.ndarray | None = None) -> np.ndarray:
             jobs.append((blocks[j], hi - lo, means, b, lo, hi))
     if len(jobs) == 1:
         s, n, means, b, lo, hi = jobs[0]
-        _draw_block(s, n, w.D, means, p, w, out[b, lo:hi])
+        _draw_block(s, n, w.D, means, p, w, dest(b, lo, hi))
     else:
         with ThreadPoolExecutor(_threads()) as ex:
-            list(ex.map(lambda j: _draw_block(j[0], j[1], w.D, j[2], p, w, out[j[3], j[4]:j[5]]), jobs))
-    return out
+            list(ex.map(lambda j: _draw_block(j[0], j[1], w.D, j[2], p, w, dest(j[3], j[4], j[5])), jobs))
+    return out if out_blocks is None else out_blocks
 
 
 def center_points(w: Workload, x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
@@ -254,6 +268,23 @@ def init_centroids(w: Workload, x: np.ndarray) -> np.ndarray:
     return c
 
 
+def rows_of_blocks(blocks, idx: np.ndarray) -> np.ndarray:
+    """Rows `idx` (global row numbers, any order) of the points split over `blocks`."""
+    starts = np.cumsum([0] + [bl.shape[0] for bl in blocks])
+    j = np.searchsorted(starts, idx, side="right") - 1
+    out = np.empty((idx.size, blocks[0].shape[1]), dtype=blocks[0].dtype)
+    for jj in np.unique(j):
+        sel = j == jj
+        out[sel] = blocks[jj][idx[sel] - starts[jj]]
+    return out
+
+
+def init_centroids_blocks(w: Workload, blocks) -> np.ndarray:
+    """init_centroids for points split over blocks (B = 1)."""
+    idx = init_indices(w)
+    return storage_to_f32(rows_of_blocks(blocks, idx[0]), w.dtype)[None].astype(np.float32)
+
+
 def make(w: Workload, out: np.ndarray | None = None):
     """Points (storage dtype, centred if the workload says so), init centroids f32 and the
     centring translation (None when not centred)."""
@@ -284,5 +315,6 @@ def ceil_div(a: int, b: int) -> int:
 __all__ = [
     "Workload", "WORKLOADS", "make", "generate_points", "center_points", "init_indices", "init_centroids",
     "small", "cast_f32", "storage_to_f32", "storage_to_f64", "to_torch", "from_torch", "torch_dtype",
+    "rows_of_blocks", "init_centroids_blocks",
     "f32_to_bf16_bits", "bf16_bits_to_f32", "NP_STORAGE", "ELEM_BYTES", "nbytes", "ceil_div",
 ]

@@ -266,6 +266,27 @@ km_status_t kmeans_fit(const void *x, km_dtype_t dt, int64_t B, int64_t N, int64
                        size_t ws_bytes, void *stream);
 
 /*
+ * The streamed path for one problem whose points lie in several pinned host
+ * blocks, for point sets too large for one pinned allocation (README, "Large
+ * tensor Benchmark"; paper digest, step (3)).  The same as kmeans_fit on
+ * pinned host x with B = 1, where x is the concatenation of the blocks.
+ *   x_blocks      nblocks pointers to pinned host [block_points[j], D] arrays of
+ *                 dtype dt, 16-byte aligned; every block but the last holds a
+ *                 multiple of the chunk (chunk_points, 0 = 2^24, clamped to the
+ *                 total), so no staged chunk straddles two blocks
+ *   block_points  host int64 [nblocks]; their sum N < 2^31
+ *   centroids     device [1, K, D] float32 in: init, out: final
+ *   assign        device [1, N] int32 out or NULL (point order: block 0 first)
+ *   ws            >= kmeans_workspace_bytes(KM_OP_FIT_HOST, dt, 1, N, D, K,
+ *                 chunk_points)
+ * Other arguments and the return as kmeans_fit.
+ */
+km_status_t kmeans_fit_blocks(const void *const *x_blocks, const int64_t *block_points, int32_t nblocks,
+                              km_dtype_t dt, int64_t D, int64_t K, int32_t iters, float tol,
+                              int64_t chunk_points, float *centroids, int32_t *assign, double *inertia,
+                              int32_t *iters_done, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Dot-product and cosine k-means.  The project README ("CuTe backend") names
  * both as modes of the library without defining them; the readings taken:
  *   KM_METRIC_DOT: a_i = the lowest k maximising x_i.c~_k; the update is the

@@ -101,6 +101,27 @@ def test_argsort_update_fit_validation(fk):
     assert L.kmeans_fit(P, 2, 1, 10, 4, 3, 5, 0.0, 0, P, None, None, None, None, 1 << 20, None) == fk.KM_ERR_WORKSPACE
 
 
+def test_fit_blocks_validation(fk):
+    L = fk.LIB
+    VP, I64 = ctypes.c_void_p, ctypes.c_int64
+
+    def call(ptrs, npts, nb=None, chunk=0, K=3, iters=2, tol=0.0, ws=P):
+        pa = (VP * len(ptrs))(*ptrs)
+        na = (I64 * len(npts))(*npts)
+        return L.kmeans_fit_blocks(pa, na, len(ptrs) if nb is None else nb, 1, 8, K, iters, tol, chunk, P, None, None,
+                                   None, ws, 1 << 30, None)
+    assert call([256, 256], [4096, 100], nb=0) == fk.KM_ERR_INVALID and "nblocks" in fk.last_error()
+    assert call([256, None], [4096, 100]) == fk.KM_ERR_INVALID and "block 1 is NULL" in fk.last_error()
+    assert call([256, 256], [4096, 0]) == fk.KM_ERR_INVALID and "block 1 holds 0" in fk.last_error()
+    assert call([258, 256], [4096, 100]) == fk.KM_ERR_INVALID and "16-byte" in fk.last_error()
+    assert call([256, 256], [3000, 100], chunk=2048) == fk.KM_ERR_INVALID and "not a multiple" in fk.last_error()
+    assert call([256, 256], [1 << 30, 1 << 30]) == fk.KM_ERR_INVALID and "2^31" in fk.last_error()
+    assert call([256], [2], K=3) == fk.KM_ERR_INVALID and "K (3) > N (2)" in fk.last_error()
+    assert call([256], [4096], iters=0) == fk.KM_ERR_INVALID
+    assert call([256], [4096], tol=-1.0) == fk.KM_ERR_INVALID
+    assert call([256], [4096], ws=None) == fk.KM_ERR_WORKSPACE
+
+
 def test_workspace_sizes(fk):
     for op in (fk.KM_OP_ASSIGN, fk.KM_OP_ARGSORT, fk.KM_OP_UPDATE, fk.KM_OP_FIT, fk.KM_OP_FIT_HOST):
         assert fk.kmeans_workspace_bytes(op, 2, 1, 10, 4, 11) == 0          # K > N: invalid

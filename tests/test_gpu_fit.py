@@ -125,6 +125,35 @@ def test_fit_streamed_ragged_last_chunk_needs_more_scratch(fk):
     assert (np.abs(J_host - ref["inertia"]) / ref["inertia"]).max() <= INERTIA_TOL
 
 
+def test_fit_blocks_equals_contiguous(fk):
+    """The points split over pinned host blocks (every block but the last a multiple of the chunk):
+    the same chunk sequence as one contiguous pinned array, so the same labels, centroids and
+    inertia, bit for bit."""
+    chunk = 1 << 14
+    w = W.small("streamed_f16", N=3 * chunk + 2 * chunk + 777, K=256, M=256, iters=3)
+    x, x64, c0, xt, ct = make_inputs(w)
+    xh = W.to_torch(x, w.dtype).pin_memory()
+    sizes = [3 * chunk, 2 * chunk, 777]
+    blocks, lo = [], 0
+    for n in sizes:
+        blocks.append(xh[0, lo:lo + n].clone().pin_memory())
+        lo += n
+    c_blk, c_con = ct.clone(), ct.clone()
+    a_blk, J_blk, d_blk = fk.kmeans_fit_blocks(blocks, c_blk, w.iters, 0.0, chunk_points=chunk)
+    a_con, J_con, d_con = fk.kmeans_fit(xh, c_con, w.iters, 0.0, chunk_points=chunk)
+    assert d_blk == d_con == w.iters
+    assert np.array_equal(a_blk.cpu().numpy(), a_con.cpu().numpy())
+    assert np.array_equal(c_blk.cpu().numpy(), c_con.cpu().numpy())
+    assert np.array_equal(J_blk, J_con)
+    ref = oracle.lloyd_fit(x64, c0, w.iters, 0.0, dtype=w.dtype, mode="modelled")
+    assert (np.abs(J_blk - ref["inertia"]) / ref["inertia"]).max() <= INERTIA_TOL
+    # a block that is not a multiple of the chunk is refused
+    bad = [xh[0, :chunk + 1].clone().pin_memory(), xh[0, chunk + 1:].clone().pin_memory()]
+    with pytest.raises(fk.FlashKMError) as e:
+        fk.kmeans_fit_blocks(bad, ct.clone(), 1, 0.0, chunk_points=chunk)
+    assert e.value.status == fk.KM_ERR_INVALID
+
+
 def test_fit_rejects_pageable_host(fk):
     w = W.small("tiny_f32")
     x, _, c0, _, ct = make_inputs(w)

@@ -10,6 +10,7 @@ The HIP path runs on the full inputs.  The oracle then checks:
 Stages are teacher forced: each stage takes the GPU's own inputs from the previous stage,
 as the parity protocol prescribes.
 """
+import os
 import sys
 import time
 
@@ -265,6 +266,81 @@ def test_streamed_real_chunks(fk):
     num = np.linalg.norm(cs - cd, axis=2)
     den = np.maximum(np.linalg.norm(cd, axis=2), 1e-30)
     assert (num / den).max() <= 1e-5
+
+
+# ---------------------------------------------------------------------------------------------
+# streamed at its full size: N = 2^30, D = 64, K = 32768, fp16 in 8 pinned host blocks of 2^27
+# points (128 GiB), 3 iterations.  Needs that much pinned host memory and several minutes of host
+# time for the oracle, so it runs only when asked (FLASHKM_FULL_STREAMED=1).
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.skipif(os.environ.get("FLASHKM_FULL_STREAMED") != "1",
+                    reason="the 2^30-point streamed workload takes 128 GiB of pinned host memory and minutes of "
+                           "oracle time; set FLASHKM_FULL_STREAMED=1 to run it")
+def test_streamed_full_size(fk):
+    """Per iteration t (a fit of t+1 iterations; the fit is deterministic, so its first t are the
+    shorter fit's): the labels of 2^18 sampled points against the oracle's assignment from the
+    centroids before t (near-tie rule), the inertia of iteration t against the oracle's in full
+    (every point), every cluster's count (through the update: empty clusters keep their centroid)
+    and the centroids of sampled clusters against the oracle's means of the GPU's members."""
+    import bench
+    from concurrent.futures import ThreadPoolExecutor
+    w = W.WORKLOADS["streamed_f16"]
+    _say("streamed full size: pinning and generating %s" % (w,))
+    try:
+        tb, nb = bench.pinned_blocks(w)
+    except RuntimeError as e:
+        pytest.skip("pinned host allocation refused: %s" % e)
+    c0 = W.init_centroids_blocks(w, nb)
+    ct = torch.from_numpy(c0).to(device())
+    _say("generated; %d blocks" % len(tb))
+    rng = np.random.default_rng(36)
+    samp = np.sort(rng.choice(w.N, size=1 << 18, replace=False))
+    x_s = W.storage_to_f64(W.rows_of_blocks(nb, samp), w.dtype)
+    starts = np.cumsum([0] + [t.shape[0] for t in tb])
+    c_prev = c0.astype(np.float64)
+    tol = CENTROID_TOL[w.dtype]
+    for t in range(w.iters):
+        c = ct.clone()
+        a, J, done = fk.kmeans_fit_blocks(tb, c, t + 1, 0.0, chunk_points=w.chunk)
+        torch.cuda.synchronize()
+        assert done == t + 1
+        a_np = a.cpu().numpy()[0]
+        c_next = c.cpu().numpy().astype(np.float64)
+        del a
+        _say("iteration %d: GPU fit of %d iterations done, inertia %s" % (t, t + 1, J[:, 0].tolist()))
+        ct64 = operand(c_prev.astype(np.float32), w.dtype)
+        flips = check_assign(x_s[None], ct64, a_np[samp][None])
+        _say("  labels: %d sampled points, %d near-tie flips" % (samp.size, flips))
+
+        def block_dist(lo):
+            j = int(np.searchsorted(starts, lo, side="right")) - 1
+            xb = W.storage_to_f64(nb[j][lo - starts[j]:lo - starts[j] + BLOCK], w.dtype)
+            return float(np.sum(oracle.dist_to(xb, ct64[0], a_np[lo:lo + xb.shape[0]])))
+        with ThreadPoolExecutor(4) as ex:
+            J_or = sum(ex.map(block_dist, range(0, w.N, BLOCK)))
+        rel = abs(J[t, 0] - J_or) / J_or
+        _say("  inertia in full: rel diff %.3g" % rel)
+        assert rel <= INERTIA_TOL
+        counts = np.bincount(a_np, minlength=w.K)
+        empty = counts == 0
+        assert np.array_equal(c_next[0][empty], c_prev[0][empty]), "empty clusters changed"
+        ks = np.unique(np.concatenate([np.argsort(-counts, kind="stable")[:4], rng.choice(w.K, 28, replace=False)]))
+        ks = ks[counts[ks] > 0]
+        members = np.nonzero(np.isin(a_np, ks))[0]
+        lab_m = a_np[members]
+        worst = 0.0
+        for k in ks:
+            rows = members[lab_m == k]
+            xs = W.storage_to_f64(W.rows_of_blocks(nb, rows), w.dtype)
+            sk, nk = oracle.segment_sums(xs, np.zeros(rows.size, dtype=np.int64), 1)
+            c_or = sk[0] / rows.size
+            r = np.linalg.norm(c_next[0, k] - c_or) / max(np.linalg.norm(c_or), 1e-30)
+            worst = max(worst, r)
+            assert r <= tol, "cluster %d (n=%d): rel err %g" % (k, rows.size, r)
+        _say("  update: %d empty clusters kept, %d sampled clusters (largest n=%d), worst rel err %.3g" % (
+            int(empty.sum()), ks.size, int(counts.max()), worst))
+        c_prev = c_next
+        del a_np
 
 
 # ---------------------------------------------------------------------------------------------
