@@ -4,19 +4,22 @@
 A step is one Lloyd iteration of the whole path (FlashAssign with the per-point minimum
 distance and inertia partials, arg-sort, sort-inverse update with the refresh of the next
 iteration's centroid operand), run by kmeans_fit on the headline workload (B=32, N=65536,
-D=128, K=1024, bf16; inputs resident in HBM).  Order of the run:
+D=128, K=1024, bf16; inputs resident in HBM).  Every buffer (the fit's workspace included) is
+allocated before the first measurement, so the GPU never idles between the measurements.
+Order of the run:
 
-  1. per-stage timings: R teacher-forced repetitions of the stage calls (row norms, centroid
-     preparation, FlashAssign through kmeans_assign_prepared -- one kernel launch per call --,
-     arg-sort, update), each bracketed by HIP events on the stream the stages run on.  They run
-     first: the GPU leaves its idle clocks during the setup, and a few milliseconds of load after
-     that it passes through a power-management dip (FlashAssign 10-15% slower for about 10 ms,
-     see the design notes' trace); the stage timings take that load before the fit is timed.
+  1. per-stage timings, first pass ("stages_ms_first"): R teacher-forced repetitions of the stage
+     calls (row norms, centroid preparation, FlashAssign through kmeans_assign_prepared -- one
+     kernel launch per call --, arg-sort, update), each bracketed by HIP events on the stream the
+     stages run on.  A GPU that was idle during the setup passes through a power-management dip a
+     millisecond or two after its load starts (FlashAssign up to 30% slower for about 12 ms; see
+     the design notes' kernel trace); this pass takes that load, and its numbers show it.
   2. `--warmup` untimed iterations as one fit;
   3. the timed region: exactly `--steps` iterations as one kmeans_fit call, bracketed by device
      synchronisations; `value` = its wall time / steps.  `--repeat` more timed fits follow and are
      reported beside it (not in `value`).
-  4. the oracle on a bounded sample on the host (cpu_baseline).
+  4. per-stage timings, second pass ("stages_ms", the roofline and update figures).
+  5. the oracle on a bounded sample on the host (cpu_baseline).
 
 Prints one JSON line.  Other modes: `--copy-calib` (a plain device copy of known size, the
 reference for scaling the FETCH_SIZE / WRITE_SIZE counters), `--summarize-trace CSV` (the
@@ -359,9 +362,13 @@ def summarize_trace(path, args):
         return n[:24]
     seq = [(tag(r["Kernel_Name"]), int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows]
     names = [s[0] for s in seq]
-    # stage calls: row norms, prep, assign; the first such triple is the untimed priming call
-    stage_assign = [(seq[i + 2][2] - seq[i + 2][1]) / 1e3 for i in range(len(seq) - 2)
-                    if names[i] == "rownorm" and names[i + 1] == "prep" and names[i + 2] == "assign"][1:]
+    # stage calls: row norms, prep, assign, in two passes of 1 + R triples (the first triple of a
+    # pass is its untimed priming call); `roofline` averages the second pass
+    triples = [(seq[i + 2][2] - seq[i + 2][1]) / 1e3 for i in range(len(seq) - 2)
+               if names[i] == "rownorm" and names[i + 1] == "prep" and names[i + 2] == "assign"]
+    R = args.stage_reps
+    first_pass = triples[1:1 + R]
+    stage_assign = triples[2 + R:2 + 2 * R] if len(triples) >= 2 + 2 * R else first_pass
     # fits: prep, fill, then iterations (each from an assign to the next one) until the next
     # prep or row-norm kernel (another fit or stage call); the fit's inertia sums and copies to
     # the host are not counted in an iteration's kernels
@@ -384,8 +391,11 @@ def summarize_trace(path, args):
         else:
             i += 1
     lines = ["# rocprofv3 kernel trace summary (bench.py --summarize-trace)", "source: %s" % os.path.basename(path)]
-    lines.append("FlashAssign launches of the per-stage timings: %d, mean %.2f us, median %.2f us, min %.2f us" % (
-        len(stage_assign), np.mean(stage_assign), np.median(stage_assign), np.min(stage_assign)))
+    lines.append("FlashAssign launches of the first stage pass: %d, mean %.2f us" % (
+        len(first_pass), np.mean(first_pass)))
+    lines.append("FlashAssign launches of the second stage pass (the roofline's): %d, mean %.2f us, median %.2f us, "
+                 "min %.2f us" % (len(stage_assign), np.mean(stage_assign), np.median(stage_assign),
+                                  np.min(stage_assign)))
     flops = 2.0 * 32 * 65536 * 1024 * 128
     lines.append("  2*B*N*K*D / mean / 2.5 PFLOP/s = %.4f (headline shape)" % (flops / (np.mean(stage_assign) * 1e-6)
                                                                               / 2.5e15))
@@ -576,14 +586,20 @@ def main():
     c0t = torch.from_numpy(c0).to(dev)
     c = c0t.clone()
     stream = torch.cuda.current_stream(dev)
-
-    # ---- 1. per-stage times (HIP events on the stages' stream), teacher forced from c0
-    st, assign_launches = stage_times(fk, w, xt, c0t, args.stage_reps, args.metric, stream)
+    # the fit's workspace and label buffer, allocated now (the binding caches the workspace)
+    dt = fk.dtype_code(xt)
+    op = {"l2": fk.KM_OP_FIT, "dot": fk.KM_OP_FIT_DOT, "cosine": fk.KM_OP_FIT_COSINE}[args.metric]
+    fk.workspace(op, dt, w.B, w.N, w.D, w.K, dev, stream=fk._stream(c, None))
+    labels = torch.empty((w.B, w.N), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
 
     def fit(iters):
         if args.metric == "l2":
-            return fk.kmeans_fit(xt, c, iters, 0.0)
-        return fk.kmeans_fit_metric(xt, c, args.metric, iters, 0.0)
+            return fk.kmeans_fit(xt, c, iters, 0.0, assign=labels)
+        return fk.kmeans_fit_metric(xt, c, args.metric, iters, 0.0, assign=labels)
+
+    # ---- 1. per-stage times, first pass (HIP events on the stages' stream), teacher forced from c0
+    st_first, _ = stage_times(fk, w, xt, c0t, args.stage_reps, args.metric, stream)
 
     # ---- 2. warmup (untimed): W iterations
     if args.warmup > 0:
@@ -606,6 +622,9 @@ def main():
     ms_per_step = runs[0]
     print("bench: %d iterations in %.3f ms (repeats: %s ms per iteration)" % (
         args.steps, ms_per_step * args.steps, ["%.4f" % v for v in runs[1:]]), file=sys.stderr, flush=True)
+
+    # ---- 4. per-stage times, second pass
+    st, assign_launches = stage_times(fk, w, xt, c0t, args.stage_reps, args.metric, stream)
 
     flops, abytes, ubytes = algorithmic(w)
     peak = PEAK_TFLOPS[w.dtype]
@@ -640,6 +659,7 @@ def main():
                      "launches": len(assign_launches), "flop_per_launch": flops,
                      "algorithmic_bytes_per_launch": abytes},
         "stages_ms": {k: round(v, 4) for k, v in st.items()},
+        "stages_ms_first": {k: round(v, 4) for k, v in st_first.items()},
         "update": {"bound": "hbm", "achieved": round(upd_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                    "frac": round(upd_gbs / PEAK_HBM_GBS, 4), "bytes_per_iter": ubytes,
                    "stages": "kmeans_argsort_ids + kmeans_update"},
