@@ -34,6 +34,7 @@ import hashlib
 import json
 import os
 import platform
+import statistics
 import subprocess
 import sys
 import time
@@ -552,7 +553,9 @@ def stage_times(fk, w, xt, c0t, reps, metric, stream):
         torch.cuda.synchronize()
         for i, k in enumerate(names):
             times[k].append(ev[i].elapsed_time(ev[i + 1]))
-    return {k: float(np.median(v)) for k, v in times.items()}, times["assign"]
+    # plain-Python medians: a first np.median call spends tens of milliseconds of host time, which
+    # would leave the GPU idle between the measurements
+    return {k: float(statistics.median(v)) for k, v in times.items()}, times["assign"]
 
 
 def main():

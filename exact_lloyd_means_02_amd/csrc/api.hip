@@ -18,7 +18,7 @@ hipError_t launch_prep_centroids(int dt, const float *C, void *cprep, float *cnh
                                  hipStream_t stream, int zero_norm);
 hipError_t launch_assign(int dt, const AssignCfg &cfg, const void *x, const void *cprep, const float *cnh,
                          const float *xn, int32_t *a, float *md, double *wgi, int B, int N, int D, int K,
-                         hipStream_t s);
+                         hipStream_t s, const AssignSplit &sp);
 size_t sort_ws_bytes(int64_t B, int64_t N, int64_t K);
 hipError_t launch_argsort(const int32_t *keys, int B, int N, int K, int32_t *out_keys, int32_t *out_vals,
                           int32_t *counts, int32_t *offs, int32_t *status, void *ws, hipStream_t s);
@@ -110,10 +110,32 @@ km_status_t check_ws(const void *ws, size_t ws_bytes, size_t need) {
 // --------------------------------------------------------------------------------------------
 // workspace layouts
 // --------------------------------------------------------------------------------------------
-size_t assign_ws(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
+// The prepared centroid operand: c~ in tile order, then ||c~||^2 / 2.
+size_t prep_bytes(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
     const AssignCfg c = plan_assign(dt, B, N, D, K);
     const int64_t KT = (int64_t)assign_tiles(K);
     return align256((size_t)B * KT * 32 * c.d_pad * elem_bytes(dt)) + align256((size_t)B * KT * 32 * 4);
+}
+
+// Buffers of a K-split assign (see AssignSplit), 0 when the plan does not split.
+size_t split_bytes(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
+    if (plan_assign(dt, B, N, D, K).nsplit <= 1) return 0;
+    return align256((size_t)B * N * 8) + align256((size_t)B * N * 4);
+}
+
+// kmeans_assign's workspace: the prepared operand, then the split buffers.
+size_t assign_ws(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
+    return prep_bytes(dt, B, N, D, K) + split_bytes(dt, B, N, D, K);
+}
+
+AssignSplit split_at(int dt, int64_t B, int64_t N, int64_t D, int64_t K, char *buf) {
+    AssignSplit sp;
+    sp.nsplit = plan_assign(dt, B, N, D, K).nsplit;
+    if (sp.nsplit > 1) {
+        sp.packed = (unsigned long long *)buf;
+        sp.xn = (float *)(buf + align256((size_t)B * N * 8));
+    }
+    return sp;
 }
 
 // A caller's arg-sort workspace: the status word (first 256 bytes), then the digit tables.
@@ -127,8 +149,8 @@ int64_t assign_wgs_per_problem(int dt, int64_t B, int64_t N, int64_t D, int64_t 
 }
 
 struct FitLayout {
-    size_t xn, a, sids, sidx, counts, offs, status, updctr, prep, ring_part, ring_j, ring_s, xhat, sums, cnt, shk,
-        scratch, total;
+    size_t xn, a, sids, sidx, counts, offs, status, updctr, prep, split, ring_part, ring_j, ring_s, xhat, sums, cnt,
+        shk, scratch, total;
 };
 
 // Device-resident x.  The prepared centroids persist across iterations (the update refreshes
@@ -147,7 +169,8 @@ FitLayout fit_layout(int dt, int64_t B, int64_t N, int64_t D, int64_t K, int met
     L.offs = o; o += align256((size_t)B * K * 4);
     L.status = o; o += STATUS_BYTES;
     L.updctr = o; o += update_ctr_bytes(dt, B, N, D, K);
-    L.prep = o; o += assign_ws(dt, B, N, D, K);
+    L.prep = o; o += prep_bytes(dt, B, N, D, K);
+    L.split = o; o += split_bytes(dt, B, N, D, K);
     L.ring_part = o; o += align256((size_t)RING * B * assign_wgs_per_problem(dt, B, N, D, K) * 8);
     L.ring_j = o; o += align256((size_t)RING * B * 8);
     L.ring_s = o; o += align256((size_t)RING * B * 8);
@@ -217,7 +240,7 @@ HostLayout host_layout(int dt, int64_t B, int64_t N, int64_t D, int64_t K, int64
     const size_t sb = align256((size_t)c * D * elem_bytes(dt));
     L.stage_buf[0] = o; o += sb;
     L.stage_buf[1] = o; o += sb;
-    L.cprep = o; o += assign_ws(dt, B, N, D, K);
+    L.cprep = o; o += prep_bytes(dt, B, N, D, K);
     const size_t c4 = align256((size_t)c * 4);
     L.xn = o; o += c4;
     L.md = o; o += c4;
@@ -304,18 +327,24 @@ km_status_t do_prepare(int dt, const float *C, int64_t B, int64_t N, int64_t D, 
     return ok();
 }
 
+// sp: the K split and its buffers (nsplit 1: one scan per point tile, as kmeans_assign_prepared runs).
 km_status_t do_assign_prepared(int dt, const void *x, const void *cprep, int64_t B, int64_t N, int64_t D, int64_t K,
-                               const float *xn, int32_t *a, float *md, hipStream_t s) {
+                               const float *xn, int32_t *a, float *md, hipStream_t s,
+                               const AssignSplit &sp = AssignSplit{}) {
     const AssignCfg cfg = plan_assign(dt, B, N, D, K);
     const float *cnh = prep_norms(dt, (char *)cprep, B, D, K, cfg.d_pad);
-    KM_HIP(launch_assign(dt, cfg, x, cprep, cnh, xn, a, md, nullptr, (int)B, (int)N, (int)D, (int)K, s));
+    KM_HIP(launch_assign(dt, cfg, x, cprep, cnh, xn, a, md, nullptr, (int)B, (int)N, (int)D, (int)K, s, sp));
     return ok();
 }
 
+// kmeans_assign in workspace ws (assign_ws bytes): the prepared operand, then (for a K-split
+// plan) the keys, set to all ones here, and the norms.
 km_status_t do_assign(int dt, const void *x, const float *C, int64_t B, int64_t N, int64_t D, int64_t K,
                       const float *xn, int32_t *a, float *md, void *ws, hipStream_t s) {
     KM_TRY(do_prepare(dt, C, B, N, D, K, ws, s));
-    return do_assign_prepared(dt, x, ws, B, N, D, K, xn, a, md, s);
+    const AssignSplit sp = split_at(dt, B, N, D, K, (char *)ws + prep_bytes(dt, B, N, D, K));
+    if (sp.nsplit > 1) KM_HIP(launch_fill_i32((int32_t *)sp.packed, 2 * B * N, -1, s));
+    return do_assign_prepared(dt, x, ws, B, N, D, K, xn, a, md, s, sp);
 }
 
 km_status_t do_update(int dt, const void *x, const int32_t *sids, const int32_t *sidx, const int32_t *counts,
@@ -352,6 +381,7 @@ km_status_t kmeans_plan(km_dtype_t dt, int64_t B, int64_t N, int64_t D, int64_t 
     out->upd_rows = u.rows;
     out->upd_vec = u.vec;
     out->upd_lanes = u.lanes;
+    out->assign_splits = a.nsplit;
     return ok();
 }
 
@@ -409,7 +439,7 @@ km_status_t kmeans_prepare_centroids(const float *centroids, km_dtype_t dt, int6
     KM_TRY(check_shape(dt, B, N, D, K));
     KM_TRY(check_ptr(centroids, "centroids"));
     KM_TRY(check_ptr(c_prep, "c_prep"));
-    KM_TRY(check_ws(c_prep, c_prep_bytes, assign_ws(dt, B, N, D, K)));
+    KM_TRY(check_ws(c_prep, c_prep_bytes, prep_bytes(dt, B, N, D, K)));
     KM_TRY(check_device_arch());
     KM_TRY(require_device(centroids, "centroids"));
     KM_TRY(require_device(c_prep, "c_prep"));
@@ -425,7 +455,7 @@ km_status_t kmeans_assign_prepared(const void *x, km_dtype_t dt, const void *c_p
     KM_TRY(check_ptr(assign, "assign"));
     if (min_dist && !x_norms) return fail(KM_ERR_INVALID, "min_dist requires x_norms");
     if (((uintptr_t)x & 15) != 0) return fail(KM_ERR_INVALID, "x must be 16-byte aligned");
-    KM_TRY(check_ws(c_prep, c_prep_bytes, assign_ws(dt, B, N, D, K)));
+    KM_TRY(check_ws(c_prep, c_prep_bytes, prep_bytes(dt, B, N, D, K)));
     KM_TRY(check_device_arch());
     KM_TRY(require_device(x, "x"));
     KM_TRY(require_device(c_prep, "c_prep"));
@@ -456,7 +486,7 @@ km_status_t kmeans_prepare_centroids_metric(const float *centroids, km_dtype_t d
     KM_TRY(check_shape(dt, B, N, D, K));
     KM_TRY(check_ptr(centroids, "centroids"));
     KM_TRY(check_ptr(c_prep, "c_prep"));
-    KM_TRY(check_ws(c_prep, c_prep_bytes, assign_ws(dt, B, N, D, K)));
+    KM_TRY(check_ws(c_prep, c_prep_bytes, prep_bytes(dt, B, N, D, K)));
     KM_TRY(check_device_arch());
     KM_TRY(require_device(centroids, "centroids"));
     KM_TRY(require_device(c_prep, "c_prep"));
@@ -633,6 +663,7 @@ km_status_t fit_device(int dt, const void *x, int64_t B, int64_t N, int64_t D, i
     mem.offs = (const int32_t *)(ws + L.offs);
     mem.ctr = (int32_t *)(ws + L.updctr);
     mem.scratch = scratch;
+    const AssignSplit sp = split_at(dt, B, N, D, K, ws + L.split);
     const bool fused_prep = update_refreshes_prep(dt, B, N, D);
     const UpdRefresh full_ref{cprep, cnh, cfg.d_pad, (int)KT, simm ? 1 : 0};
     const UpdRefresh ref = fused_prep ? full_ref : UpdRefresh{};
@@ -651,8 +682,10 @@ km_status_t fit_device(int dt, const void *x, int64_t B, int64_t N, int64_t D, i
     if (simm) KM_HIP(launch_fill_i32((int32_t *)xn, B * N, 0, s));
     else if (xn_in) KM_HIP(launch_row_norms(dt, x, xn, B * N, (int)D, s));
     KM_HIP(launch_prep_centroids(dt, C, cprep, cnh, (int)B, (int)K, (int)D, cfg.d_pad, s, simm ? 1 : 0));
-    // the update's arrival counters start at zero; every update leaves them zero
+    // the update's arrival counters start at zero and the split assign's keys at all ones; every
+    // update and every split finish leave them so
     KM_HIP(launch_fill_i32(mem.ctr, (int64_t)(update_ctr_bytes(dt, B, N, D, K) / 4), 0, s));
+    if (sp.nsplit > 1) KM_HIP(launch_fill_i32((int32_t *)sp.packed, 2 * B * N, -1, s));
     int done = 0, flushed = 0;
     int32_t st_host = 0;
     for (int t = 0; t < iters; ++t) {
@@ -660,7 +693,7 @@ km_status_t fit_device(int dt, const void *x, int64_t B, int64_t N, int64_t D, i
         // one iteration: assign (+ per-workgroup inertia partials), arg-sort (+ counts and the
         // clusters' first positions), update (+ shift, + the next iteration's prepared centroids)
         KM_HIP(launch_assign(dt, cfg, xa, cprep, cnh, xn_in, a, nullptr, ring_part + (size_t)slot * B * wpb, (int)B,
-                             (int)N, (int)D, (int)K, s));
+                             (int)N, (int)D, (int)K, s, sp));
         KM_HIP(launch_argsort(a, (int)B, (int)N, (int)K, sids, sidx, counts, (int32_t *)mem.offs, status, scratch, s));
         if (cosine && fused_prep) {
             // one column block per row: the update finishes each cluster in place with the mean
@@ -825,9 +858,10 @@ km_status_t fit_host(int dt, const HostSource &src, int64_t B, int64_t N, int64_
             int32_t *ac = assign ? assign + (size_t)b * N + lo : a_ws;
             if (cosine) KM_HIP(launch_normalize_rows(dt, xc, stage_buf[buf], n, (int)D, s));
             if (cfg.path != 0 && !simm) KM_HIP(launch_row_norms(dt, xc, xn, n, (int)D, s));
+            // one scan per point tile: chunks of 2^24 points fill the chip by themselves
             KM_HIP(launch_assign(dt, cfg, xc, cprep + (size_t)b * cprep_per_b, cnh + (size_t)b * KT * 32,
                                  (cfg.path == 0 && !simm) ? nullptr : xn, ac, md,
-                                 nullptr, 1, (int)n, (int)D, (int)K, s));
+                                 nullptr, 1, (int)n, (int)D, (int)K, s, AssignSplit{}));
             KM_HIP(launch_sum_f32(md, 1, n, ring_j + (size_t)slot * B + b, 1, red, s));
             KM_HIP(launch_argsort(ac, 1, (int)n, (int)K, sids, sidx, counts, (int32_t *)mem.offs, status, scratch, s));
             KM_HIP(launch_update(dt, xc, sids, sidx, counts, 1, (int)n, (int)D, (int)K, 1, nullptr, nullptr,

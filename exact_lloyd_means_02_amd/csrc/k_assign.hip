@@ -221,23 +221,45 @@ __device__ inline void argmin_fold(ArgminState &s, const f32x16 &acc, int tile) 
     s.best = __builtin_bit_cast(f32x16, bb);
 }
 
-// Resolve the winning centroid of this lane, merge with the partner lane (lane ^ 32, same
-// point, the other 16 rows of every tile) and write.  Accumulator r of lane (j, h) holds row
-// 8*(r/4) + 4*h + (r%4) of the 32-centroid tile (MFMA 32x32 output layout).
-// xnorm == NULL: the point's squared norm is `own_norm` (computed by the caller).
-__device__ inline float argmin_finish(const ArgminState &s, int h, bool write, int64_t out_i, int32_t *out_a,
-                                      float *out_d, const float *xnorm, bool want_d, float own_norm = 0.f) {
+// Resolve the winning centroid of this lane and merge with the partner lane (lane ^ 32, same
+// point, the other 16 rows of every tile): the point's least (half) score and its lowest index.
+// Accumulator r of lane (j, h) holds row 8*(r/4) + 4*h + (r%4) of the 32-centroid tile (MFMA
+// 32x32 output layout).
+__device__ inline void argmin_resolve(const ArgminState &s, int h, float &sc, int &k) {
     int slot = 15;
 #pragma unroll
     for (int r = 15; r >= 0; --r) slot = (s.best[r] == s.run_min) ? r : slot;
-    int k = s.run_tile * 32 + 8 * (slot >> 2) + 4 * h + (slot & 3);
-    float sc = s.run_min;
+    k = s.run_tile * 32 + 8 * (slot >> 2) + 4 * h + (slot & 3);
+    sc = s.run_min;
     const float osc = __shfl_xor(sc, 32);
     const int ok = __shfl_xor(k, 32);
     if (osc < sc || (osc == sc && ok < k)) {
         sc = osc;
         k = ok;
     }
+}
+
+// A (score, index) pair as one 64-bit key whose unsigned order is (score, then index): the fp32
+// bits mapped to an order-preserving unsigned integer in the high word, the index in the low
+// word.  The least key over several partial scans is the least score with the lowest index.
+__device__ inline unsigned long long argmin_key(float sc, int k) {
+    uint32_t u = __float_as_uint(sc);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((unsigned long long)u << 32) | (uint32_t)k;
+}
+__device__ inline float argmin_key_score(unsigned long long key) {
+    uint32_t u = (uint32_t)(key >> 32);
+    u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+    return __uint_as_float(u);
+}
+
+// Write the merged pick of this lane (see argmin_resolve).
+// xnorm == NULL: the point's squared norm is `own_norm` (computed by the caller).
+__device__ inline float argmin_finish(const ArgminState &s, int h, bool write, int64_t out_i, int32_t *out_a,
+                                      float *out_d, const float *xnorm, bool want_d, float own_norm = 0.f) {
+    float sc;
+    int k;
+    argmin_resolve(s, h, sc, k);
     float d = 0.f;
     if (write) {
         out_a[out_i] = k;
@@ -295,11 +317,19 @@ __device__ inline void stage_barrier() {
 //   * stage s+2 is copied global->LDS while stage s is consumed; a barrier in the middle of
 //     each stage publishes stage s+1 before the first fragment of it is read.
 // ------------------------------------------------------------------------------------------
+//
+// K split (nsplit > 1, for grids too small to fill the chip): the workgroups of one point tile
+// scan disjoint ranges of centroid stages, and each point's pick leaves as an argmin_key through a
+// 64-bit atomic minimum into `packed` (the least key: the least score, ties to the lowest index,
+// the same pick as one scan of all stages).  The workgroup of the first range also writes the
+// points' squared norms to xn_out (when distances are wanted); split_finish_kernel turns the keys
+// into labels, distances and inertia partials.
 template <int DT, int DP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void assign_small_d_kernel(
     const void *__restrict__ x, const u32x4 *__restrict__ cprep, const float *__restrict__ cnh,
     const float *__restrict__ xnorm, int32_t *__restrict__ out_a, float *__restrict__ out_d,
-    double *__restrict__ wg_inertia, int N, int D, int KT, int wgs_per_b) {
+    double *__restrict__ wg_inertia, int N, int D, int KT, int wgs_per_b, int nsplit,
+    unsigned long long *__restrict__ packed, float *__restrict__ xn_out) {
     constexpr int S = DT == DT_F32 ? 4 : 2;
     constexpr int VW = 16 / S;
     constexpr int QG = DP / (2 * VW);
@@ -317,9 +347,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     __shared__ u32x4 s_c0[STAGE_U4], s_c1[STAGE_U4], s_c2[STAGE_U4];
     __shared__ __attribute__((aligned(16))) float s_n0[TPS * 32], s_n1[TPS * 32], s_n2[TPS * 32];
 
+    // consecutive logical workgroups (one XCD) take the K ranges of a point tile, then the next tile
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
-    const int b = wg / wgs_per_b;
-    const int tn = wg - b * wgs_per_b;
+    const int per_b = wgs_per_b * nsplit;
+    const int b = wg / per_b;
+    const int rb = wg - b * per_b;
+    const int tn = rb / nsplit;
+    const int sp = rb - tn * nsplit;
     const int tid = threadIdx.x, lane = tid & 63;
     // the wave index is uniform: held in a scalar register, the copy addresses derived from it
     // (global source bases and LDS destinations) stay scalar too
@@ -339,8 +373,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 
     const u32x4 *cb = cprep + (size_t)b * KT * TILE_U4;
     const float *nb = cnh + (size_t)b * KT * 32;
-    const int nst = KT / TPS;  // KT is a multiple of 4
-    const bool want_d = out_d != nullptr || wg_inertia != nullptr;
+    const int nst_all = KT / TPS;  // KT is a multiple of 4
+    // this workgroup's stages [s_beg, nst)
+    const int s_beg = sp * nst_all / nsplit;
+    const int nst = (sp + 1) * nst_all / nsplit;
+    const bool split = packed != nullptr;
+    const bool want_d = split ? (xn_out != nullptr && sp == 0) : (out_d != nullptr || wg_inertia != nullptr);
 
     // Global -> LDS copy of stage st (TPS tiles and their norms).  Every wave issues exactly
     // NCOPY copy instructions, so it can wait for an older stage with a fixed count.  The
@@ -433,10 +471,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
         step(t0 + TPS - 1, xc, TPS - 1, yc, 0);  // last tile; refills from the next stage
     };
 
-    // prologue: stages 0 and 1 in flight, stage 0 published, tile 0 loaded
-    stage_copy(0, s_c0, s_n0);
-    if (nst > 1) {
-        stage_copy(1, s_c1, s_n1);
+    // prologue: stages s_beg and s_beg + 1 in flight, the first published, its first tile loaded
+    stage_copy(s_beg, s_c0, s_n0);
+    if (nst > s_beg + 1) {
+        stage_copy(s_beg + 1, s_c1, s_n1);
         stage_barrier<NCOPY>();
     } else {
         stage_barrier<0>();
@@ -444,7 +482,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 #pragma unroll
     for (int q = 0; q < FR; ++q) f[q] = s_c0[q * 64 + lane];
 
-    for (int s0 = 0; s0 < nst; s0 += 3) {
+    for (int s0 = s_beg; s0 < nst; s0 += 3) {
         run_stage(s0, s_c0, s_n0, s_c1, s_n1, s_c2, s_n2);
         if (s0 + 1 < nst) run_stage(s0 + 1, s_c1, s_n1, s_c2, s_n2, s_c0, s_n0);
         if (s0 + 2 < nst) run_stage(s0 + 2, s_c2, s_n2, s_c0, s_n0, s_c1, s_n1);
@@ -473,7 +511,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
             }
             own += __shfl_xor(own, 32);
         }
-        dsum += argmin_finish(st[p], h, h == 0 && pt < N, (int64_t)b * N + pt, out_a, out_d, xnorm, want_d, own);
+        if (split) {
+            float sc;
+            int k;
+            argmin_resolve(st[p], h, sc, k);
+            if (h == 0 && pt < N) {
+                atomicMin(packed + (size_t)b * N + pt, argmin_key(sc, k));
+                if (want_d) xn_out[(size_t)b * N + pt] = own;
+            }
+        } else {
+            dsum += argmin_finish(st[p], h, h == 0 && pt < N, (int64_t)b * N + pt, out_a, out_d, xnorm, want_d, own);
+        }
+    }
+    if (!split && wg_inertia) workgroup_inertia(dsum, wg_inertia + (size_t)b * wgs_per_b + tn);
+}
+
+// After a K-split assign: each point's least key -> label (and distance xn + 2 score), with the
+// threads laid out as the assign workgroup's lanes (PB blocks of 32 points per wave, lanes h == 0
+// write), so the per-tile inertia partials add the same terms in the same order as the unsplit
+// kernel.  Resets the keys to all ones for the next use.
+template <int PB>
+__global__ __launch_bounds__(256) void split_finish_kernel(unsigned long long *__restrict__ packed,
+                                                           const float *__restrict__ xn, int32_t *__restrict__ out_a,
+                                                           float *__restrict__ out_d, double *__restrict__ wg_inertia,
+                                                           int N, int wgs_per_b) {
+    const int b = blockIdx.x / wgs_per_b, tn = blockIdx.x - b * wgs_per_b;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int j = lane & 31, h = lane >> 5;
+    const int pbase = tn * (ASSIGN_WAVES * PB * 32) + w * PB * 32;
+    const bool want_d = out_d != nullptr || wg_inertia != nullptr;
+    double dsum = 0.0;
+#pragma unroll
+    for (int p = 0; p < PB; ++p) {
+        const int pt = pbase + p * 32 + j;
+        if (h == 0 && pt < N) {
+            const size_t i = (size_t)b * N + pt;
+            const unsigned long long key = packed[i];
+            packed[i] = ~0ull;
+            out_a[i] = (int32_t)(uint32_t)key;
+            if (want_d) {
+                const float d = (xn ? xn[i] : 0.f) + 2.0f * argmin_key_score(key);
+                if (out_d) out_d[i] = d;
+                dsum += d;
+            }
+        }
     }
     if (wg_inertia) workgroup_inertia(dsum, wg_inertia + (size_t)b * wgs_per_b + tn);
 }
@@ -614,13 +695,26 @@ hipError_t launch_prep_centroids(int dt, const float *C, void *cprep, float *cnh
 
 template <int DT, int DP>
 static hipError_t launch_small(const void *x, const void *cprep, const float *cnh, const float *xn, int32_t *a,
-                               float *md, double *wgi, int B, int N, int D, int K, hipStream_t stream) {
+                               float *md, double *wgi, int B, int N, int D, int K, const AssignSplit &sp,
+                               hipStream_t stream) {
     constexpr int PB = small_d_pb(DT, DP);
     const int KT = assign_tiles(K);
     const int bn = ASSIGN_WAVES * PB * 32;
     const int wpb = (N + bn - 1) / bn;
-    assign_small_d_kernel<DT, DP><<<dim3(B * wpb), dim3(256), 0, stream>>>(x, (const u32x4 *)cprep, cnh, xn, a, md,
-                                                                           wgi, N, D, KT, wpb);
+    if (sp.nsplit <= 1) {
+        assign_small_d_kernel<DT, DP><<<dim3(B * wpb), dim3(256), 0, stream>>>(
+            x, (const u32x4 *)cprep, cnh, xn, a, md, wgi, N, D, KT, wpb, 1, nullptr, nullptr);
+        return hipGetLastError();
+    }
+    // the keys hold all ones on entry (the previous finish, or the caller's fill, left them so)
+    const bool want_d = md != nullptr || wgi != nullptr;
+    float *xn_out = (want_d && !xn) ? sp.xn : nullptr;
+    assign_small_d_kernel<DT, DP><<<dim3(B * wpb * sp.nsplit), dim3(256), 0, stream>>>(
+        x, (const u32x4 *)cprep, cnh, xn, a, md, wgi, N, D, KT, wpb, sp.nsplit, sp.packed, xn_out);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    split_finish_kernel<PB><<<dim3(B * wpb), dim3(256), 0, stream>>>(sp.packed, xn ? xn : xn_out, a, md, wgi, N,
+                                                                     wpb);
     return hipGetLastError();
 }
 
@@ -629,33 +723,36 @@ static hipError_t launch_small(const void *x, const void *cprep, const float *cn
 // faster there (K = 1024; 2% at K = 32768) than the memory-clause strategy used for the others,
 // which is the better one at the other widths.
 hipError_t launch_small_2byte_d64(int dt, const void *x, const void *cprep, const float *cnh, const float *xn,
-                                  int32_t *a, float *md, double *wgi, int B, int N, int D, int K, hipStream_t s);
+                                  int32_t *a, float *md, double *wgi, int B, int N, int D, int K,
+                                  const AssignSplit &sp, hipStream_t s);
 #ifdef FKM_ASSIGN_D64_UNIT
 hipError_t launch_small_2byte_d64(int dt, const void *x, const void *cprep, const float *cnh, const float *xn,
-                                  int32_t *a, float *md, double *wgi, int B, int N, int D, int K, hipStream_t s) {
-    if (dt == DT_F16) return launch_small<DT_F16, 64>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
-    if (dt == DT_BF16) return launch_small<DT_BF16, 64>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
+                                  int32_t *a, float *md, double *wgi, int B, int N, int D, int K,
+                                  const AssignSplit &sp, hipStream_t s) {
+    if (dt == DT_F16) return launch_small<DT_F16, 64>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, sp, s);
+    if (dt == DT_BF16) return launch_small<DT_BF16, 64>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, sp, s);
     return hipErrorInvalidValue;
 }
 #else
 template <int DT>
 static hipError_t launch_small_dt(int DP, const void *x, const void *cprep, const float *cnh, const float *xn,
-                                  int32_t *a, float *md, double *wgi, int B, int N, int D, int K, hipStream_t s) {
+                                  int32_t *a, float *md, double *wgi, int B, int N, int D, int K,
+                                  const AssignSplit &sp, hipStream_t s) {
     if constexpr (DT == DT_F32) {
         switch (DP) {
-            case 8: return launch_small<DT, 8>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
-            case 16: return launch_small<DT, 16>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
-            case 32: return launch_small<DT, 32>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
-            case 64: return launch_small<DT, 64>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
-            case 128: return launch_small<DT, 128>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
+            case 8: return launch_small<DT, 8>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, sp, s);
+            case 16: return launch_small<DT, 16>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, sp, s);
+            case 32: return launch_small<DT, 32>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, sp, s);
+            case 64: return launch_small<DT, 64>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, sp, s);
+            case 128: return launch_small<DT, 128>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, sp, s);
         }
     } else {
         switch (DP) {
-            case 16: return launch_small<DT, 16>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
-            case 32: return launch_small<DT, 32>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
-            case 64: return launch_small_2byte_d64(DT, x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
-            case 128: return launch_small<DT, 128>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
-            case 256: return launch_small<DT, 256>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
+            case 16: return launch_small<DT, 16>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, sp, s);
+            case 32: return launch_small<DT, 32>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, sp, s);
+            case 64: return launch_small_2byte_d64(DT, x, cprep, cnh, xn, a, md, wgi, B, N, D, K, sp, s);
+            case 128: return launch_small<DT, 128>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, sp, s);
+            case 256: return launch_small<DT, 256>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, sp, s);
         }
     }
     return hipErrorInvalidValue;
@@ -663,13 +760,14 @@ static hipError_t launch_small_dt(int DP, const void *x, const void *cprep, cons
 
 // wgi (optional): per-workgroup fp64 sums of the chosen distances, [B][assign_wgs_per_problem].
 // xn: point norms for the distances (md / wgi); the small-D kernel computes them itself when NULL.
+// sp: the K split (small-D path; nsplit 1 = one scan of all centroids per point tile).
 hipError_t launch_assign(int dt, const AssignCfg &cfg, const void *x, const void *cprep, const float *cnh,
                          const float *xn, int32_t *a, float *md, double *wgi, int B, int N, int D, int K,
-                         hipStream_t s) {
+                         hipStream_t s, const AssignSplit &sp) {
     if (cfg.path == 0) {
-        if (dt == DT_F32) return launch_small_dt<DT_F32>(cfg.d_pad, x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
-        if (dt == DT_F16) return launch_small_dt<DT_F16>(cfg.d_pad, x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
-        return launch_small_dt<DT_BF16>(cfg.d_pad, x, cprep, cnh, xn, a, md, wgi, B, N, D, K, s);
+        if (dt == DT_F32) return launch_small_dt<DT_F32>(cfg.d_pad, x, cprep, cnh, xn, a, md, wgi, B, N, D, K, sp, s);
+        if (dt == DT_F16) return launch_small_dt<DT_F16>(cfg.d_pad, x, cprep, cnh, xn, a, md, wgi, B, N, D, K, sp, s);
+        return launch_small_dt<DT_BF16>(cfg.d_pad, x, cprep, cnh, xn, a, md, wgi, B, N, D, K, sp, s);
     }
     const int KT = assign_tiles(K);
     const int bn = ASSIGN_WAVES * 32;

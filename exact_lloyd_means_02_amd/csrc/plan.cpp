@@ -18,6 +18,11 @@
 //     block_n >= 128, above what L2 must feed MFMA (~2.5 PF / ~40 TB/s ~= 64 FLOP/B).
 //   * Workgroups of one problem are mapped onto one XCD so its centroids (K*D*s bytes,
 //     256 KiB at K=1024, D=128, bf16) stay in that XCD's 4 MiB L2.
+//   * The grid must fill the chip: three workgroups per CU (the VGPR budget above) is 768
+//     workgroup slots.  When B * ceil(N / block_n) falls short of them, the centroid stages are
+//     split over nsplit workgroups per point tile (each scans a contiguous share, at least two
+//     stages, at most 8 shares), enough to fill the slots; their picks merge through a 64-bit
+//     atomic minimum of (score, index) keys, and a small kernel writes the labels.
 // Assign, split-D path (D above the register budget, README "Large-D and dtype support"):
 //   * point block of 128 (4 waves x 32), 4 centroid tiles (128 centroids) of accumulators per
 //     wave, D streamed through LDS in chunks of 64 (2-byte) / 32 (fp32) elements so one stage
@@ -31,6 +36,8 @@
 //   rows; each wave takes `rows` consecutive sorted positions, sized so ~8 waves per SIMD
 //   are in flight over the whole launch.
 #include "plan.h"
+
+#include <stdlib.h>
 
 #include <algorithm>
 
@@ -50,8 +57,16 @@ static int log2_floor(int64_t v) {
     return r;
 }
 
+// FLASHKM_ASSIGN_SPLIT=n (n >= 1) replaces the planned split of the small-D assign (a measuring
+// knob for comparing the plan with other splits; any n gives the same results).
+static int split_override() {
+    const char *e = getenv("FLASHKM_ASSIGN_SPLIT");
+    return e ? atoi(e) : 0;
+}
+
 AssignCfg plan_assign(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
     AssignCfg c{};
+    c.nsplit = 1;
     const int s = dt == 0 ? 4 : 2;
     const int dmin = dt == 0 ? 8 : 16;
     if (D <= small_d_max(dt)) {
@@ -68,6 +83,14 @@ AssignCfg plan_assign(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
         // ring (at most 2 groups of 4) and addressing / fold temporaries (~24)
         const int qg = dp * s / 32;
         c.vgpr = c.pb * (dp * s / 8 + 32) + (qg >= 4 ? 2 : qg) * 4 + 24;
+        const int64_t slots = (int64_t)Gfx950::cus * 3;
+        const int64_t wgs = B * cdiv(N, c.block_n);
+        const int nst = assign_tiles(K) / c.tps;
+        int ns = 1;
+        if (wgs < slots) ns = (int)std::min<int64_t>(8, cdiv(slots, wgs));
+        ns = std::max(1, std::min(ns, nst / 2));
+        if (split_override() > 0) ns = std::max(1, std::min(split_override(), nst));
+        c.nsplit = ns;
     } else {
         const int bd = splitd_bd(dt);
         c.path = 1;
@@ -79,9 +102,6 @@ AssignCfg plan_assign(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
         c.lds = 2 * (c.block_n * bd * s + SPLITD_KB * 32 * bd * s) + SPLITD_KB * 32 * 4;
         c.vgpr = SPLITD_KB * 16 + 16 + 32 + 16 + 48;
     }
-    (void)K;
-    (void)B;
-    (void)N;
     return c;
 }
 

@@ -36,6 +36,15 @@ struct AssignCfg {
     int block_n;
     int lds;
     int vgpr;
+    int nsplit;    // workgroups per point tile, each scanning a share of the centroid stages
+};
+
+// Buffers of a K-split assign (AssignCfg::nsplit > 1): one 64-bit (score, index) key per point,
+// all ones between launches, and the points' squared norms.
+struct AssignSplit {
+    int nsplit = 1;
+    unsigned long long *packed = nullptr;
+    float *xn = nullptr;
 };
 
 struct SortCfg {

@@ -32,7 +32,7 @@ EXPORTS = ["kmeans_plan", "kmeans_workspace_bytes", "kmeans_row_norms", "kmeans_
 class KmPlan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "path", "d_pad", "point_blocks", "waves", "block_n", "block_k", "block_d", "lds_bytes", "vgpr_est",
-        "assign_wgs", "sort_bits", "sort_passes", "sort_tile", "upd_rows", "upd_vec", "upd_lanes")]
+        "assign_wgs", "sort_bits", "sort_passes", "sort_tile", "upd_rows", "upd_vec", "upd_lanes", "assign_splits")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

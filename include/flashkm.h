@@ -104,6 +104,8 @@ typedef struct {
     int32_t upd_rows;      /* sorted rows per update wave */
     int32_t upd_vec;       /* elements per update vector load */
     int32_t upd_lanes;     /* lanes covering one row in the update */
+    int32_t assign_splits; /* small-D: workgroups per point tile, each scanning a share of the
+                              centroids (> 1 when B * ceil(N / block_n) cannot fill the chip) */
 } km_plan_t;
 
 /* Fill *out with the plan for this problem.  Host only; no HIP call. */
@@ -171,11 +173,13 @@ km_status_t kmeans_assign_noalloc(const void *x, km_dtype_t dt, const float *cen
  * in fp32 computed from c~.
  *   centroids  device [B, K, D] float32 (read only)
  *   c_prep     device out, opaque, c_prep_bytes >= kmeans_workspace_bytes(
- *              KM_OP_ASSIGN, dt, B, N, D, K) (any N), 256-byte aligned; valid
- *              for calls with the same (dt, B, D, K)
+ *              KM_OP_ASSIGN, dt, B, N, D, K) for any N (N = K is enough),
+ *              256-byte aligned; valid for calls with the same (dt, B, D, K)
  *
  * kmeans_assign_prepared: FlashAssign as kmeans_assign, from a c_prep written
- * by kmeans_prepare_centroids for the same (dt, B, D, K).
+ * by kmeans_prepare_centroids for the same (dt, B, D, K).  It always runs one
+ * scan of all centroids per point tile (no K split, see km_plan_t), so its
+ * result is the same as kmeans_assign's.
  */
 km_status_t kmeans_prepare_centroids(const float *centroids, km_dtype_t dt, int64_t B, int64_t N, int64_t D,
                                      int64_t K, void *c_prep, size_t c_prep_bytes, void *stream);

@@ -271,7 +271,8 @@ def test_streamed_real_chunks(fk):
 # ---------------------------------------------------------------------------------------------
 # streamed at its full size: N = 2^30, D = 64, K = 32768, fp16 in 8 pinned host blocks of 2^27
 # points (128 GiB), 3 iterations.  Needs that much pinned host memory and several minutes of host
-# time for the oracle, so it runs only when asked (FLASHKM_FULL_STREAMED=1).
+# time for the oracle, so it runs only when asked (FLASHKM_FULL_STREAMED=1); a host whose pinned
+# memory is capped lower runs it at FLASHKM_FULL_STREAMED_N points (a multiple of 2^27).
 # ---------------------------------------------------------------------------------------------
 @pytest.mark.skipif(os.environ.get("FLASHKM_FULL_STREAMED") != "1",
                     reason="the 2^30-point streamed workload takes 128 GiB of pinned host memory and minutes of "
@@ -285,6 +286,10 @@ def test_streamed_full_size(fk):
     import bench
     from concurrent.futures import ThreadPoolExecutor
     w = W.WORKLOADS["streamed_f16"]
+    n_env = int(os.environ.get("FLASHKM_FULL_STREAMED_N", "0"))
+    if n_env:
+        assert n_env % (1 << 27) == 0
+        w = W.small("streamed_f16", N=n_env)
     _say("streamed full size: pinning and generating %s" % (w,))
     try:
         tb, nb = bench.pinned_blocks(w)

@@ -109,6 +109,35 @@ def test_assign_fragment_ring_large(fk, name, kw):
                  np.stack([m_np[b, samp[b]] for b in range(w.B)]))
 
 
+SPLIT_CASES = [("headline_bf16", dict(B=1, N=20000, K=1024)), ("headline_bf16", dict(B=3, N=5001, K=300)),
+               ("batched_f16", dict(B=1, N=9000, D=64, K=2048)), ("tiny_f32", dict(N=7000, D=100, K=700, M=50)),
+               ("headline_bf16", dict(B=1, N=3000, D=256, K=200))]
+
+
+@pytest.mark.parametrize("name,kw", SPLIT_CASES, ids=[f"{n}-{kw}" for n, kw in SPLIT_CASES])
+def test_assign_k_split_equals_one_scan(fk, name, kw):
+    """Grids too small for the chip split the centroid scan over several workgroups per point
+    tile and merge (score, index) keys: kmeans_assign (split by the plan) must equal
+    kmeans_assign_prepared (one scan per tile) bit for bit, labels and distances, and the oracle
+    by the parity rule; a one-iteration fit takes the same labels."""
+    w = W.small(name, **kw)
+    x, x64, c0, xt, ct = make_inputs(w)
+    plan = fk.kmeans_plan(fk.DT_CODES[w.dtype], w.B, w.N, w.D, w.K)
+    _say(f"case {w}: plan {plan['assign_splits']} splits over {plan['assign_wgs']} point tiles")
+    assert plan["assign_splits"] > 1
+    xn = fk.kmeans_row_norms(xt)
+    a_s, md_s = fk.kmeans_assign(xt, ct, x_norms=xn, want_min_dist=True)
+    prep = fk.kmeans_prepare_centroids(ct, xt)
+    a_1, md_1 = fk.kmeans_assign_prepared(xt, prep, x_norms=xn, want_min_dist=True)
+    a_f, J, _ = fk.kmeans_fit(xt, ct.clone(), 1, 0.0)
+    torch.cuda.synchronize()
+    assert np.array_equal(a_s.cpu().numpy(), a_1.cpu().numpy())
+    assert np.array_equal(md_s.cpu().numpy(), md_1.cpu().numpy())
+    assert np.array_equal(a_f.cpu().numpy(), a_1.cpu().numpy())
+    check_assign(x64, operand(c0, w.dtype), a_s.cpu().numpy(), md_s.cpu().numpy())
+    check_inertia(x64, operand(c0, w.dtype), a_f.cpu().numpy(), J[0])
+
+
 def test_assign_exact_ties_go_to_lowest_index(fk):
     """Duplicate centroids give bit-identical scores; the lowest index must win."""
     w = W.small("headline_bf16", B=1, N=2000, K=64)
