@@ -66,6 +66,9 @@ def parse():
                         "scatter-add update) at the workload's shape")
     p.add_argument("--context-pages", action="store_true",
                    help="time the standard path against this path at the pages' kernel-ratio shapes and exit")
+    p.add_argument("--plan-regret", action="store_true",
+                   help="time kmeans_assign under the plan's K split and under other splits on a few shapes "
+                        "(the regret of the analytic plan) and exit")
     p.add_argument("--summarize-trace", metavar="CSV",
                    help="summarise a rocprofv3 kernel trace of this script (same --steps/--warmup/--stage-reps)")
     return p.parse_args()
@@ -337,6 +340,62 @@ def context_pages():
 
 
 # ------------------------------------------------------------------------------------------------
+# the analytic plan against alternatives
+# ------------------------------------------------------------------------------------------------
+REGRET_SHAPES = [  # (workload recipe, B, N, D, K)
+    ("headline_bf16", 1, 65536, 128, 1024), ("headline_bf16", 1, 65536, 128, 4096),
+    ("headline_bf16", 4, 32768, 128, 1024), ("headline_bf16", 1, 16384, 128, 8192),
+    ("batched_f16", 1, 262144, 64, 1024), ("headline_bf16", 32, 65536, 128, 1024)]
+REGRET_SPLITS = [1, 2, 3, 4, 6, 8]
+
+
+def plan_regret():
+    """kmeans_assign (prepare + FlashAssign [+ key merge]) timed with HIP events, median of 10, under
+    the plan's K split and under each alternative split (FLASHKM_ASSIGN_SPLIT, read by the plan at
+    every call); regret = time of the plan's choice / best time - 1."""
+    import torch
+    from exact_lloyd_means_02_amd import flashkm as fk
+    from exact_lloyd_means_02_amd import workloads as W
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    rows = []
+    for name, B, N, D, K in REGRET_SHAPES:
+        w = W.small(name, B=B, N=N, D=D, K=K)
+        x, c0, _ = W.make(w)
+        xt = W.to_torch(x, w.dtype).to(dev)
+        ct = torch.from_numpy(c0).to(dev)
+        os.environ.pop("FLASHKM_ASSIGN_SPLIT", None)
+        plan = fk.kmeans_plan(fk.DT_CODES[w.dtype], B, N, D, K)
+        ref = None
+        times = {}
+        for sp in REGRET_SPLITS:
+            os.environ["FLASHKM_ASSIGN_SPLIT"] = str(sp)
+            got = fk.kmeans_plan(fk.DT_CODES[w.dtype], B, N, D, K)["assign_splits"]
+            if got != sp:
+                continue                                   # more shares than stages
+            a, _ = fk.kmeans_assign(xt, ct)
+            for _ in range(3):
+                fk.kmeans_assign(xt, ct, assign=a)
+            times[sp] = _event_ms(lambda: fk.kmeans_assign(xt, ct, assign=a), 10, stream)
+            lab = a.cpu()
+            if ref is None:
+                ref = lab
+            assert torch.equal(lab, ref), "labels depend on the split"
+        os.environ.pop("FLASHKM_ASSIGN_SPLIT", None)
+        best = min(times, key=times.get)
+        chosen = plan["assign_splits"]
+        row = {"B": B, "N": N, "D": D, "K": K, "dtype": w.dtype, "point_tiles": plan["assign_wgs"],
+               "plan_splits": chosen, "ms": {str(k): round(v, 4) for k, v in times.items()}, "best_splits": best,
+               "regret": round(times[chosen] / times[best] - 1.0, 4)}
+        print(json.dumps(row), flush=True)
+        rows.append(row)
+        del xt, ct
+        torch.cuda.empty_cache()
+    print(json.dumps({"plan_regret_max": max(r["regret"] for r in rows),
+                      "plan_regret_mean": round(sum(r["regret"] for r in rows) / len(rows), 4)}), flush=True)
+
+
+# ------------------------------------------------------------------------------------------------
 # rocprofv3 kernel-trace summary
 # ------------------------------------------------------------------------------------------------
 KERNEL_TAGS = [("assign_small_d", "assign"), ("assign_split_d", "assign"), ("sort_hist", "hist"),
@@ -572,6 +631,9 @@ def main():
         return
     if args.context_pages:
         context_pages()
+        return
+    if args.plan_regret:
+        plan_regret()
         return
     import numpy as np
     import torch
