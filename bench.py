@@ -69,6 +69,9 @@ def parse():
     p.add_argument("--plan-regret", action="store_true",
                    help="time kmeans_assign under the plan's K split and under other splits on a few shapes "
                         "(the regret of the analytic plan) and exit")
+    p.add_argument("--summarize-counters", metavar="DIR",
+                   help="summarise rocprofv3 --pmc runs of this script kept under DIR (fetch/, write/, cfetch/, "
+                        "cwrite/, mfma/) into the HBM-traffic and MFMA summaries and exit")
     p.add_argument("--summarize-trace", metavar="CSV",
                    help="summarise a rocprofv3 kernel trace of this script (same --steps/--warmup/--stage-reps)")
     return p.parse_args()
@@ -396,6 +399,113 @@ def plan_regret():
 
 
 # ------------------------------------------------------------------------------------------------
+# rocprofv3 counter summaries
+# ------------------------------------------------------------------------------------------------
+COUNTER_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc %s --output-format csv -d <out>/%s -o run -- "
+               "python3 /root/repo/bench.py %s")
+BENCH_ARGS_COUNTERS = "--steps 1 --warmup 1 --stage-reps 2 --repeat 0 --no-cpu-baseline"
+
+
+def _counter_means(path):
+    """{kernel name: {counter: mean value per dispatch}} from a rocprofv3 counter_collection CSV."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(path)):
+        key = (r["Kernel_Name"], r["Counter_Name"])
+        per.setdefault(key, {}).setdefault(r["Dispatch_Id"], 0.0)
+        per[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    out = {}
+    for (k, c), d in per.items():
+        out.setdefault(k, {})[c] = (sum(d.values()) / len(d), len(d))
+    return out
+
+
+def _short(name):
+    return name.split("(")[0].replace("void ", "").replace("fkm::", "")
+
+
+def summarize_counters(root):
+    """HBM bytes per dispatch from FETCH_SIZE and WRITE_SIZE (each its own run), scaled by what the
+    same counters read for a plain 1 GiB device copy, against the algorithmic bytes of the
+    headline shape; MFMA counters of FlashAssign.  Prints the markdown summary, then writes the
+    FlashAssign traffic file bench.py reads (profiles/assign_small_d_headline_bf16_traffic.txt)."""
+    import glob
+    import numpy as np
+
+    def load(sub):
+        f = glob.glob(os.path.join(root, sub, "**", "*counter_collection.csv"), recursive=True)
+        return _counter_means(f[0]) if f else {}
+    fetch, write, cfetch, cwrite, mfma = (load(s) for s in ("fetch", "write", "cfetch", "cwrite", "mfma"))
+    copy = [k for k in cfetch if "copyBuffer" in k][0]
+    fscale = (1 << 30) / 1024 / cfetch[copy]["FETCH_SIZE"][0]
+    wscale = (1 << 30) / 1024 / cwrite[[k for k in cwrite if "copyBuffer" in k][0]]["WRITE_SIZE"][0]
+    B, N, D, K, s = 32, 65536, 128, 1024, 2
+    KT = 32
+    algo = {"assign_small_d_kernel": B * N * D * s + B * KT * 32 * D * s + 4 * B * KT * 32 + 8 * B * N,
+            "sort_hist_kernel": 4 * B * N, "sort_scatter_kernel": 16 * B * N,
+            "upd_segsum_kernel": B * N * D * s + 8 * B * N + B * K * D * (4 + 4 + s) + 4 * B * K}
+    lines = ["# HBM traffic per dispatch and FlashAssign MFMA counters: headline workload "
+             "(B=32, N=65536, D=128, K=1024, bf16)", "",
+             "Each counter set is its own run (the commands below; `<out>` = a scratch directory).  Values are",
+             "per dispatch, averaged over the dispatches of each kernel.", ""]
+    for c, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        lines.append("    " + COUNTER_CMD % (c, sub, BENCH_ARGS_COUNTERS))
+    for c, sub in (("FETCH_SIZE", "cfetch"), ("WRITE_SIZE", "cwrite")):
+        lines.append("    " + COUNTER_CMD % (c, sub, "--copy-calib"))
+    lines.append("    " + COUNTER_CMD % ("SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU "
+                                       "GRBM_GUI_ACTIVE", "mfma", BENCH_ARGS_COUNTERS))
+    lines += ["", "Scale (a plain 1 GiB device copy): FETCH_SIZE x %.4f, WRITE_SIZE x %.4f give bytes." % (fscale, wscale),
+              "", "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled bytes | algorithmic bytes | ratio |",
+              "|---|---:|---:|---:|---:|---:|---:|"]
+    assign_traffic = None
+    for k in sorted(fetch, key=lambda n: -fetch[n]["FETCH_SIZE"][0]):
+        f, n = fetch[k]["FETCH_SIZE"]
+        wv = write.get(k, {}).get("WRITE_SIZE", (float("nan"), 0))[0]
+        scaled = (f * fscale + wv * wscale) * 1024
+        a = next((v for key, v in algo.items() if key in k), None)
+        lines.append("| `%s` | %d | %.1f | %.1f | %.4g | %s | %s |" % (
+            _short(k), n, f, wv, scaled, "%.4g" % a if a else "-", "%.3f" % (scaled / a) if a else "-"))
+        if "assign_small_d_kernel" in k:
+            assign_traffic = (f, wv, scaled, n)
+    lines += ["", "Algorithmic bytes: assign = x (B N D 2) + prepared centroids (B KT 32 D 2) + their half-norms "
+              "(4 B KT 32) + labels and point norms (8 B N); hist = labels; scatter = labels and indices read, sorted "
+              "ids and indices written (16 B N); segsum = gathered rows + sorted ids and indices (8 B N) + old and new "
+              "centroids (f32) + refreshed operand (2 bytes) + half-norms."]
+    for k, v in mfma.items():
+        if "assign_small_d_kernel" not in k:
+            continue
+        mops = v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", (0, 0))[0]
+        busy = v.get("SQ_VALU_MFMA_BUSY_CYCLES", (0, 0))[0]
+        gui = v.get("GRBM_GUI_ACTIVE", (0, 0))[0]
+        valu = v.get("SQ_INSTS_VALU", (0, 0))[0]
+        flops = 2.0 * B * N * K * D
+        lines += ["", "FlashAssign MFMA counters (%d dispatches): SQ_INSTS_VALU_MFMA_MOPS_BF16 %.4g (x 512 = %.4g FLOP; "
+                  "2 B N K D = %.4g), SQ_VALU_MFMA_BUSY_CYCLES %.4g, GRBM_GUI_ACTIVE %.4g, SQ_INSTS_VALU %.4g "
+                  "(%.1f per 32-centroid tile and wave; the MFMA count per tile and wave is 16)." % (
+                      v["SQ_INSTS_VALU_MFMA_MOPS_BF16"][1], mops, mops * 512, flops, busy, gui, valu,
+                      valu / (B * N / 64 * KT) if valu else 0.0),
+                  "MFMA busy per SIMD cycle, busy / (GRBM_GUI_ACTIVE x 1024 SIMDs): %.3f" % (busy / (gui * 1024))
+                  if gui else ""]
+    print("\n".join(lines))
+    if assign_traffic:
+        f, wv, scaled, n = assign_traffic
+        txt = ["# FlashAssign (small-D kernel) HBM traffic, headline workload B=32 N=65536 D=128 K=1024 bf16",
+               "# read by bench.py for roofline.traffic; valid only for the kernel source whose hash is below",
+               "k_assign.hip + build.py sha256[:16]: %s" % assign_source_hash(),
+               "fetch command: " + COUNTER_CMD % ("FETCH_SIZE", "fetch", BENCH_ARGS_COUNTERS),
+               "write command: " + COUNTER_CMD % ("WRITE_SIZE", "write", BENCH_ARGS_COUNTERS),
+               "copy fetch command: " + COUNTER_CMD % ("FETCH_SIZE", "cfetch", "--copy-calib"),
+               "copy write command: " + COUNTER_CMD % ("WRITE_SIZE", "cwrite", "--copy-calib"),
+               "summary command: python3 bench.py --summarize-counters <out>",
+               "FETCH_SIZE KiB per dispatch: %.1f (%d dispatches)" % (f, n),
+               "WRITE_SIZE KiB per dispatch: %.1f" % wv,
+               "fetch scale (1 GiB copy): %.4f" % fscale, "write scale (1 GiB copy): %.4f" % wscale,
+               "traffic bytes per launch: %d" % round(scaled),
+               "algorithmic bytes per launch: %d" % algo["assign_small_d_kernel"]]
+        open(TRAFFIC_FILE, "w").write("\n".join(txt) + "\n")
+
+
+# ------------------------------------------------------------------------------------------------
 # rocprofv3 kernel-trace summary
 # ------------------------------------------------------------------------------------------------
 KERNEL_TAGS = [("assign_small_d", "assign"), ("assign_split_d", "assign"), ("sort_hist", "hist"),
@@ -625,6 +735,9 @@ def main():
         sys.exit(2)
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
         return
     if args.copy_calib:
         copy_calib()

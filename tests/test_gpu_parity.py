@@ -109,9 +109,10 @@ def test_assign_fragment_ring_large(fk, name, kw):
                  np.stack([m_np[b, samp[b]] for b in range(w.B)]))
 
 
-SPLIT_CASES = [("headline_bf16", dict(B=1, N=20000, K=1024)), ("headline_bf16", dict(B=3, N=5001, K=300)),
-               ("batched_f16", dict(B=1, N=9000, D=64, K=2048)), ("tiny_f32", dict(N=7000, D=100, K=700, M=50)),
-               ("headline_bf16", dict(B=1, N=3000, D=256, K=200))]
+# grids below 768 workgroups with at least 64 centroid tiles: 2, 3 (uneven shares of 50 stages), 4 splits
+SPLIT_CASES = [("headline_bf16", dict(B=1, N=20000, K=2048)), ("headline_bf16", dict(B=1, N=8000, K=3200)),
+               ("headline_bf16", dict(B=2, N=5001, K=4096)), ("batched_f16", dict(B=1, N=9000, D=64, K=2048)),
+               ("tiny_f32", dict(N=7000, D=100, K=2100, M=50)), ("headline_bf16", dict(B=1, N=5000, D=256, K=4100))]
 
 
 @pytest.mark.parametrize("name,kw", SPLIT_CASES, ids=[f"{n}-{kw}" for n, kw in SPLIT_CASES])
