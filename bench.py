@@ -484,8 +484,9 @@ def summarize_counters(root):
                   "(%.1f per 32-centroid tile and wave; the MFMA count per tile and wave is 16)." % (
                       v["SQ_INSTS_VALU_MFMA_MOPS_BF16"][1], mops, mops * 512, flops, busy, gui, valu,
                       valu / (B * N / 64 * KT) if valu else 0.0),
-                  "MFMA busy per SIMD cycle, busy / (GRBM_GUI_ACTIVE x 1024 SIMDs): %.3f" % (busy / (gui * 1024))
-                  if gui else ""]
+                  "SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE = %.1f (both summed over their counting units; the "
+                  "MFMA fraction of peak is taken from time instead: 2 B N K D / kernel time / 2.5 PFLOP/s)." % (
+                      busy / gui if gui else 0.0)]
     print("\n".join(lines))
     if assign_traffic:
         f, wv, scaled, n = assign_traffic

@@ -20,12 +20,13 @@
 //     256 KiB at K=1024, D=128, bf16) stay in that XCD's 4 MiB L2.
 //   * The grid must fill the chip: three workgroups per CU (the VGPR budget above) is 768
 //     workgroup slots.  When B * ceil(N / block_n) falls short of them, the centroid tiles are
-//     split over nsplit workgroups per point tile, enough to fill the slots (at most 8), each
-//     scanning a contiguous share; their picks merge through a 64-bit atomic minimum of
-//     (score, index) keys, and a small kernel writes the labels.  A workgroup has a fixed cost
-//     of about six tiles' worth of time (point tile load, pipeline fill, epilogue: measured from
-//     the efficiency at 32 and at 128 tiles per workgroup), and the merge adds a launch, so a
-//     share keeps at least 32 tiles (1024 centroids): below that the fixed costs eat the gain.
+//     split over nsplit workgroups per point tile, each scanning a contiguous share; their
+//     picks merge through a 64-bit atomic minimum of (score, index) keys, and a small kernel
+//     writes the labels.  A workgroup has a fixed cost of about six tiles' worth of time (point
+//     tile load, pipeline fill, epilogue: measured from the efficiency at 32 and at 128 tiles
+//     per workgroup), and the merge adds a launch, so a share keeps at least 32 tiles (1024
+//     centroids): below that the fixed costs eat the gain.  Within that floor the split goes as
+//     far as it can (at most 8): shorter shares also shorten the tail of the last round.
 // Assign, split-D path (D above the register budget, README "Large-D and dtype support"):
 //   * point block of 128 (4 waves x 32), 4 centroid tiles (128 centroids) of accumulators per
 //     wave, D streamed through LDS in chunks of 64 (2-byte) / 32 (fp32) elements so one stage
@@ -91,8 +92,7 @@ AssignCfg plan_assign(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
         const int KT = assign_tiles(K);
         const int nst = KT / c.tps;
         int ns = 1;
-        if (wgs < slots) ns = (int)std::min<int64_t>(8, cdiv(slots, wgs));
-        ns = std::max(1, std::min(ns, KT / 32));
+        if (wgs < slots) ns = std::max(1, std::min(8, KT / 32));
         if (split_override() > 0) ns = std::max(1, std::min(split_override(), nst));
         c.nsplit = ns;
     } else {
