@@ -59,6 +59,14 @@ __device__ inline float load_elem(const void *base, size_t i) {
     }
 }
 
+// 16-byte load marked nontemporal, for data a kernel reads once: the caches are told not to
+// keep it, and a stream of such row loads runs faster than plain loads.
+__device__ inline uint4 load16_nt(const void *p) {
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    const v4u t = __builtin_nontemporal_load((const v4u *)p);
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 // Widen a 16-byte vector holding 8 (2-byte types) or 4 (fp32) elements.
 template <int DT>
 __device__ inline void widen16(const uint4 &v, float *out) {

@@ -382,29 +382,30 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
     const int32_t *ib = a.sidx + (size_t)b * N;
     const size_t xb = (size_t)b * N;
 
-    // Sorted ids / indices are read through a sliding window of 128 positions held in two
-    // registers per lane ([wp, wp+64) and [wp+64, wp+128)); the next 64 are loaded as soon as
-    // the walk passes wp+64, so that load overlaps the row gathers of the segments in between.
-    int wp = p0, cs, ci, ns, ni;
-    auto load_window = [&](int pos) {
-        wp = pos;
-        const int q0 = wp + lane, q1 = wp + 64 + lane;
-        cs = q0 < N ? sb[q0] : -1;
-        ci = q0 < N ? ib[q0] : 0;
-        ns = q1 < N ? sb[q1] : -1;
-        ni = q1 < N ? ib[q1] : 0;
+    // Sorted ids / indices are read through a sliding window of 192 positions held in three
+    // register pairs per lane ([wp, wp+64), [wp+64, wp+128), [wp+128, wp+192)).  When the walk
+    // passes wp+64 the window moves on by 64 and the 64 positions after it are loaded: two
+    // windows ahead of their first read, so that load overlaps the row gathers in between
+    // instead of stalling the next view.
+    int wp = p0, cs, ci, ns, ni, fs, fi;
+    auto load_ids = [&](int q, int &s_, int &i_) {
+        s_ = q < N ? sb[q] : -1;
+        i_ = q < N ? ib[q] : 0;
     };
+    load_ids(p0 + lane, cs, ci);
+    load_ids(p0 + 64 + lane, ns, ni);
+    load_ids(p0 + 128 + lane, fs, fi);
     auto slide_if_past = [&](int pos) {  // keep pos - wp < 64 (pos advanced by at most 64)
         if (pos - wp >= 64) {
             wp += 64;
             cs = ns;
             ci = ni;
-            const int q1 = wp + 64 + lane;
-            ns = q1 < N ? sb[q1] : -1;
-            ni = q1 < N ? ib[q1] : 0;
+            ns = fs;
+            ni = fi;
+            load_ids(wp + 128 + lane, fs, fi);
         }
     };
-    // the 64 positions from pos: lane l takes window slot pos - wp + l of the 128
+    // the 64 positions from pos: lane l takes window slot pos - wp + l of the first 128
     auto view = [&](int pos, int &sid, int &idx) {
         const int q = pos - wp + lane;
         const int s_lo = __shfl(cs, q & 63), s_hi = __shfl(ns, q & 63);
@@ -419,30 +420,39 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
     };
     auto clampk = [&](int kr) { return kr < 0 ? 0 : (kr >= a.K ? a.K - 1 : kr); };
 
-    load_window(p0);
+    // The ids around the chunk edges, read with the first window: they settle which wave sums a
+    // segment cut by an edge without waiting for the walk to reach it.
+    const int id_prev = p0 > 0 ? sb[p0 - 1] : -1;                    // before the chunk
+    const int id_prev2 = p0 - a.R - 1 >= 0 ? sb[p0 - a.R - 1] : -1;  // before the previous chunk
+    const int id_last = sb[p1 - 1];                                  // the chunk's last
+    const int id_next = p1 < N ? sb[p1] : -1;                        // after the chunk
+    const bool next2_in = (int64_t)p1 + a.R < N;
+    const int id_next2 = next2_in ? sb[p1 + a.R] : -1;               // after the next chunk
+
     int p = p0, plim = p1;
     int sid, idx;
     view(p, sid, idx);
     int kraw = __shfl(sid, 0);
-    bool cin = p0 > 0 && sb[p0 - 1] == kraw;
+    bool cin = p0 > 0 && id_prev == kraw;
     // Segment ownership: a segment that ends within the chunk after the one where it starts is
     // summed entirely by the wave of its first chunk (which runs past its chunk end for it);
     // only segments spanning three or more chunks leave partials (the long segments).  A wave
-    // whose chunk starts inside a segment finds the segment's end from the ids alone and its
-    // start from the count, and skips it when the previous chunk's wave owns it.
+    // whose chunk starts inside a segment that began in the previous chunk (the id before that
+    // chunk differs) and ends in this one (the chunk's last id differs, or the id after it does)
+    // walks past it without gathering.
     bool done = false;
     if (cin) {
-        int e = p;
-        while (true) {
-            const int m = run_len(e, sid, kraw, p1);
-            e += m;
-            slide_if_past(e);
-            if (m < 64 || e >= p1) break;
-            view(e, sid, idx);
-        }
-        const bool ends_here = e < p1 || p1 == N || sb[p1] != kraw;
-        const int s_start = e - a.counts[(size_t)b * a.K + clampk(kraw)];
-        if (ends_here && s_start >= p0 - a.R) {
+        const bool ends_here = id_last != kraw || p1 == N || id_next != kraw;
+        const bool began_prev = !(p0 - a.R - 1 >= 0 && id_prev2 == kraw);
+        if (ends_here && began_prev) {
+            int e = p;
+            while (true) {
+                const int m = run_len(e, sid, kraw, p1);
+                e += m;
+                slide_if_past(e);
+                if (m < 64 || e >= p1) break;
+                view(e, sid, idx);
+            }
             p = e;
             if (p >= p1) {
                 done = true;
@@ -451,9 +461,6 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
                 kraw = __shfl(sid, 0);
                 cin = false;
             }
-        } else {
-            load_window(p0);  // shared segment: sum this chunk's part after all
-            view(p, sid, idx);
         }
     }
     // old centroid columns of the current segment's cluster, fetched when the segment starts
@@ -549,7 +556,7 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
                     for (int i = 0; i < VPL; ++i) {
                         const int e0 = c0 + (r + i * a.lanes) * V;
                         raw[u][i] = (rr < m && e0 < a.D)
-                                        ? *(const uint4 *)((const char *)a.x + (e_row + e0) * (DT == DT_F32 ? 4 : 2))
+                                        ? load16_nt((const char *)a.x + (e_row + e0) * (DT == DT_F32 ? 4 : 2))
                                         : make_uint4(0u, 0u, 0u, 0u);
                     }
                 }
@@ -569,12 +576,12 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
         slide_if_past(p);
         bool ended = (m < 64) || (p >= plim);
         bool cout = false;
-        if (p >= plim && plim == p1 && p1 < N && sb[p1] == kraw) {
-            // the segment runs past the chunk end: take all of it when it ends within the
-            // next chunk and started in this one
-            const int e = seg_start + a.counts[(size_t)b * a.K + clampk(kraw)];
-            if (!cin && e <= p1 + a.R) {
-                plim = e;
+        if (p >= plim && plim == p1 && p1 < N && id_next == kraw) {
+            // the segment runs past the chunk end: take all of it when it started in this chunk
+            // and ends within the next one (the id after the next chunk differs, or there is
+            // none); the walk then stops where the id changes
+            if (!cin && (!next2_in || id_next2 != kraw)) {
+                plim = next2_in ? p1 + a.R : N;
                 ended = false;
             } else {
                 cout = true;
@@ -582,7 +589,9 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
         }
         if (ended) {
             end_segment(kraw, p - seg_start, cout);
-            if (p >= plim) break;
+            // the chunk is done, or the segment taken past its end was (the walk stopped where
+            // its id changed, short of the limit)
+            if (p >= plim || plim != p1) break;
             kraw = next_k;
             fetch_cold(kraw);
             cin = false;

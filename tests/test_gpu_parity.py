@@ -269,6 +269,31 @@ def test_update_segments_on_window_edges(fk, N):
     check_update(x64, a, c0, cnew.cpu().numpy(), w.dtype)
 
 
+def test_update_chunk_edge_ownership(fk):
+    """Segments that start or end exactly on a chunk edge, one off it, fill a chunk, end inside
+    the next chunk or two chunks on (at B=2, N=2^14 a wave takes 64 sorted positions): which wave
+    sums a segment cut by a chunk edge is decided from the ids around the edges, and every cluster
+    must come out as the oracle's mean; the two problems take the lengths in different orders."""
+    B, N = 2, 1 << 14
+    R = fk.kmeans_plan(fk.DT_CODES["bf16"], B, N, 128, 2)["upd_rows"]
+    assert R == 64
+    base = [R, R, 2 * R, 1, R - 1, R, R + 1, R - 1, 2 * R - 1, 2 * R + 1, 2, R - 2, 3 * R, R, R // 2 - 1,
+            R // 2 + 1, 3 * R + 8, 1, 1, R - 2, 2 * R + 2, 2 * R - 2, 4 * R, R + R // 2, R // 2]
+    K = len(base) + 1
+    w = W.small("headline_bf16", B=B, N=N, K=K)
+    x, x64, c0, xt, ct = make_inputs(w)
+    a = np.empty((B, N), np.int32)
+    for b in range(B):
+        lens = base if b == 0 else base[::-1]
+        lens = list(lens) + [N - sum(lens)]
+        a[b] = np.random.default_rng(b).permutation(np.repeat(np.arange(K, dtype=np.int32), lens))
+    at = torch.from_numpy(a).to(device())
+    s, i, c = fk.kmeans_argsort_ids(at, K)
+    cnew = ct.clone()
+    shift = fk.kmeans_update(xt, s, i, c, cnew, want_shift=True)
+    check_update(x64, a, c0, cnew.cpu().numpy(), w.dtype, shift.cpu().numpy())
+
+
 # Segment lengths around the update's chunk groups: at B=1, N=2^17 a wave takes 64 sorted positions,
 # so a segment over P chunks has about 64 P points; the groups hold 32 chunks.
 LONG_LENS = [130, 192, 200, 1000, 31 * 64, 32 * 64, 32 * 64 + 1, 33 * 64, 64 * 64, 64 * 64 + 65, 20000, 3, 1, 64]
