@@ -32,8 +32,11 @@
 
 namespace fkm {
 
-constexpr int SORT_WAVES = 4;
-constexpr int SORT_ROUNDS = SORT_TILE / (SORT_WAVES * 64);  // 16
+// the scatter workgroup: 8 waves, each ranking 8 rounds of 64 keys of the tile
+constexpr int SORT_WAVES = 8;
+constexpr int SORT_THREADS = SORT_WAVES * 64;
+constexpr int SORT_ROUNDS = SORT_TILE / SORT_THREADS;  // 8
+static_assert(SORT_ROUNDS * SORT_THREADS == SORT_TILE, "a tile is whole rounds of the workgroup");
 
 // tile_major: the table is [tiles][bins] (each workgroup writes one contiguous row); otherwise
 // [bins][tiles] (one column per workgroup, the order the scan kernel needs).
@@ -116,15 +119,18 @@ __global__ __launch_bounds__(256) void sort_rowscan_kernel(int32_t *__restrict__
     (void)bins;
 }
 
-// In-place exclusive scan of s[0, n) (n <= 1024) by a 256-thread workgroup.
+// In-place exclusive scan of s[0, n) (n <= 1024) by a workgroup of NT threads.
 static_assert(SORT_MAX_BITS <= 10, "block_exscan_1024 covers at most 1024 bins");
 
+template <int NT>
 __device__ inline void block_exscan_1024(int32_t *s, int n, int32_t *s_wsum) {
+    static_assert(NT % 64 == 0 && 1024 % NT == 0, "whole waves, whole elements per thread");
+    constexpr int PER = 1024 / NT;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    int32_t v[4], sum = 0;
+    int32_t v[PER], sum = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int idx = t * 4 + i;
+    for (int i = 0; i < PER; ++i) {
+        const int idx = t * PER + i;
         v[i] = idx < n ? s[idx] : 0;
         sum += v[i];
     }
@@ -139,8 +145,8 @@ __device__ inline void block_exscan_1024(int32_t *s, int n, int32_t *s_wsum) {
     int32_t run = inc - sum;
     for (int i = 0; i < w; ++i) run += s_wsum[i];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int idx = t * 4 + i;
+    for (int i = 0; i < PER; ++i) {
+        const int idx = t * PER + i;
         if (idx < n) s[idx] = run;
         run += v[i];
     }
@@ -153,7 +159,7 @@ __device__ inline void block_exscan_1024(int32_t *s, int n, int32_t *s_wsum) {
 // and `totals` the digit totals, whose exclusive scan each workgroup adds.  For counts != NULL
 // the workgroup of tile 0 writes the per-bin totals.
 template <bool INLINE, int BITS>
-__global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__restrict__ keys_in,
+__global__ __launch_bounds__(SORT_THREADS) void sort_scatter_kernel(const int32_t *__restrict__ keys_in,
                                                            const int32_t *__restrict__ vals_in,
                                                            const int32_t *__restrict__ hist,
                                                            const int32_t *__restrict__ totals, int N, int ntiles,
@@ -166,8 +172,10 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__rest
     __shared__ int32_t s_wsum[SORT_WAVES];
     __shared__ int32_t s_nvalid;
     const int bins = 1 << bits;
-    int32_t *s_wc = s_mem;                        // [SORT_WAVES][bins] running counts, then prefixes
-    int32_t *s_off = s_wc + SORT_WAVES * bins;    // [bins] this tile's global offset of each digit
+    // [SORT_WAVES][bins] running counts of each wave, then their exclusive prefix over the waves
+    // (at most SORT_TILE, so 16 bits hold them)
+    uint16_t *s_wc = (uint16_t *)s_mem;
+    int32_t *s_off = s_mem + SORT_WAVES * bins / 2;  // [bins] this tile's global offset of each digit
     int32_t *s_ls = s_off + bins;                 // [bins] start of each digit inside the tile
     int32_t *s_k = s_ls + bins;                   // [SORT_TILE] keys in (digit, index) order
     int32_t *s_v = s_k + SORT_TILE;               // [SORT_TILE] values, same order
@@ -186,7 +194,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__rest
         key[r] = ok ? keys_in[base + i] : -1;
         val[r] = ok ? (vals_in ? vals_in[base + i] : i) : 0;
     }
-    for (int i = tid; i < SORT_WAVES * bins; i += 256) s_wc[i] = 0;
+    for (int i = tid; i < SORT_WAVES * bins / 2; i += SORT_THREADS) s_mem[i] = 0;  // s_wc
     if (tid == 0) s_nvalid = 0;
     if constexpr (INLINE) {
         // `hist` is [tiles][bins]: thread tid sums the rows of its four consecutive digits
@@ -221,29 +229,29 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__rest
             }
         }
         __syncthreads();
-        block_exscan_1024(s_off, bins, s_wsum);
+        block_exscan_1024<SORT_THREADS>(s_off, bins, s_wsum);
         if (i0 < bins) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) s_off[i0 + e] += pre[e];
         }
     } else {
         const int32_t *tb = totals + (size_t)b * bins;
-        for (int i = tid; i < bins; i += 256) {
+        for (int i = tid; i < bins; i += SORT_THREADS) {
             s_off[i] = tb[i];
             if (counts && t == 0 && i < K) counts[(size_t)b * K + i] = tb[i];
         }
         __syncthreads();
-        block_exscan_1024(s_off, bins, s_wsum);
-        for (int i = tid; i < bins; i += 256) s_off[i] += hb[(size_t)i * ntiles + t];
+        block_exscan_1024<SORT_THREADS>(s_off, bins, s_wsum);
+        for (int i = tid; i < bins; i += SORT_THREADS) s_off[i] += hb[(size_t)i * ntiles + t];
     }
     __syncthreads();
     // tile 0 starts every digit at its global offset: the clusters' first sorted positions
     if (offs && t == 0)
-        for (int i = tid; i < bins && i < K; i += 256) offs[(size_t)b * K + i] = s_off[i];
+        for (int i = tid; i < bins && i < K; i += SORT_THREADS) offs[(size_t)b * K + i] = s_off[i];
 
     const uint32_t mask = (uint32_t)bins - 1u;
     const uint64_t lt = lanemask_lt();
-    int32_t *wc = s_wc + w * bins;
+    uint16_t *wc = s_wc + w * bins;
     int nvalid = 0;
     bool bad = false;
 #pragma unroll
@@ -268,26 +276,26 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__rest
         const int before = __popcll(peers & lt);
         // LDS accesses of one wave complete in order and the store depends on the load, so
         // every lane reads its base before the group's lowest lane bumps it.
-        const int32_t wbase = ok ? wc[dg] : 0;
-        if (ok && before == 0) wc[dg] = wbase + __popcll(peers);
+        const int32_t wbase = ok ? (int32_t)wc[dg] : 0;
+        if (ok && before == 0) wc[dg] = (uint16_t)(wbase + __popcll(peers));
         pos[r] = wbase + before;
     }
     if (lane == 0) atomicAdd(&s_nvalid, nvalid);
     if (status && __ballot(bad) != 0ull && lane == 0) atomicOr(status, 1);
     __syncthreads();
     // exclusive prefix over waves, per digit; the digit's total in this tile
-    for (int i = tid; i < bins; i += 256) {
+    for (int i = tid; i < bins; i += SORT_THREADS) {
         int32_t run = 0;
 #pragma unroll
         for (int ww = 0; ww < SORT_WAVES; ++ww) {
             const int32_t v = s_wc[ww * bins + i];
-            s_wc[ww * bins + i] = run;
+            s_wc[ww * bins + i] = (uint16_t)run;
             run += v;
         }
         s_ls[i] = run;
     }
     __syncthreads();
-    block_exscan_1024(s_ls, bins, s_wsum);
+    block_exscan_1024<SORT_THREADS>(s_ls, bins, s_wsum);
     // lay the tile out in (digit, index) order
 #pragma unroll
     for (int r = 0; r < SORT_ROUNDS; ++r) {
@@ -301,7 +309,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__rest
     __syncthreads();
     const int tile_n = s_nvalid;  // the valid keys of the tile, laid out above
 #pragma unroll 4
-    for (int e = tid; e < tile_n; e += 256) {
+    for (int e = tid; e < tile_n; e += SORT_THREADS) {
         const int32_t k = s_k[e];
         const uint32_t dg = ((uint32_t)k >> shift) & mask;
         const int dst = s_off[dg] + (e - s_ls[dg]);
@@ -355,7 +363,7 @@ static hipError_t launch_scatter(int bits, dim3 grid, size_t lds, hipStream_t s,
                            int32_t *vo, int32_t *cnt, int K, int32_t *offs, int32_t *status) {
 #define FKM_SCATTER(B_)                                                                                            \
     case B_:                                                                                                       \
-        sort_scatter_kernel<INLINE, B_><<<grid, dim3(256), lds, s>>>(kin, vin, hist, totals, N, ntiles, shift, bits, \
+        sort_scatter_kernel<INLINE, B_><<<grid, dim3(SORT_THREADS), lds, s>>>(kin, vin, hist, totals, N, ntiles, shift, bits, \
                                                                       ko, vo, cnt, K, offs, status);               \
         break;
     static_assert(SORT_MAX_BITS == 10, "one instance per digit width");
@@ -402,7 +410,7 @@ hipError_t launch_argsort(const int32_t *keys, int B, int N, int K, int32_t *out
         int32_t *cnt_out = (counts && c.passes == 1) ? counts : nullptr;
         int32_t *offs_out = (offs && c.passes == 1) ? offs : nullptr;
         int32_t *st = pass == 0 ? status : nullptr;
-        const size_t lds = ((size_t)(SORT_WAVES + 2) * c.bins + 2 * SORT_TILE) * 4;
+        const size_t lds = (size_t)SORT_WAVES * c.bins * 2 + ((size_t)2 * c.bins + 2 * SORT_TILE) * 4;
         const bool inline_offsets = c.bins >= 4 && c.ntiles <= SORT_INLINE_TILES;
         sort_hist_kernel<<<dim3(B * c.ntiles), dim3(256), c.bins * 4, s>>>(kin, N, c.ntiles, shift, c.bins, hist,
                                                                             inline_offsets ? 1 : 0, K, st);

@@ -364,10 +364,17 @@ __device__ inline void arrive_long(const UpdArgs &a, int b, int c, int cbi, int 
 
 // SHIFT: a.shp is set (mode 0 with shift partials wanted); a separate instance keeps the
 // register budget of the common case free of the old-centroid prefetch.
-template <int DT, int V, int VPL, bool SHIFT>
+// BUF (16-byte vectors, a problem's rows at most 2 GiB): rows are gathered with raw buffer loads
+// over the problem's rows: 32-bit offsets, and a lane without a row takes an offset past the end,
+// which the buffer's range check turns into zeros without a memory access, so the loads of a
+// batch go out back to back with no branches around them.
+template <int DT, int V, int VPL, bool SHIFT, bool BUF>
 __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t total_waves) {
     const int lane = threadIdx.x & 63;
-    const int64_t gw = (int64_t)xcd_remap_rev(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
+    // the wave's index, in a scalar register: everything derived from it (problem, chunk,
+    // positions, the row buffer) is then wave-uniform to the compiler too
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int64_t gw = (int64_t)xcd_remap_rev(blockIdx.x, gridDim.x) * 4 + wave;
     if (gw >= total_waves) return;
     const int cbi = (int)(gw % a.ncb);
     const int64_t chunk = gw / a.ncb;
@@ -381,6 +388,14 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
     const int32_t *sb = a.sids + (size_t)b * N;
     const int32_t *ib = a.sidx + (size_t)b * N;
     const size_t xb = (size_t)b * N;
+    constexpr int ES = DT == DT_F32 ? 4 : 2;
+    const uint32_t rowbytes = (uint32_t)a.D * ES;
+    const uint32_t x_end = BUF ? (uint32_t)N * rowbytes : 0u;  // the problem's bytes: an offset there reads zeros
+    // the byte offsets of the rows at the 64 positions of the current view, one LDS row per wave
+    // (written and read by the same wave: its LDS accesses complete in order, no barrier)
+    __shared__ __align__(16) uint32_t s_xo[4][64];
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        (char *)const_cast<void *>(a.x) + xb * rowbytes, (short)0, (int)x_end, 0x00020000);
 
     // Sorted ids / indices are read through a sliding window of 192 positions held in three
     // register pairs per lane ([wp, wp+64), [wp+64, wp+128), [wp+128, wp+192)).  When the walk
@@ -529,6 +544,9 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
         // m == 0 is a normal case: a segment whose length is a multiple of 64 ends at a window
         // boundary, and the next view starts on the next segment's id
         const int m = run_len(p, sid, kraw, plim);
+        // the rows' byte offsets in the problem (buffer path; a garbage index wraps within the
+        // 32-bit offsets, and the range check keeps the load inside the problem's rows)
+        if constexpr (BUF && V > 1) s_xo[wave][lane] = (uint32_t)idx * rowbytes;
         for (int base = 0; base < m; base += G * U) {
             if constexpr (V == 1) {
                 float tmp[U][VPL][V];
@@ -543,6 +561,47 @@ __global__ __launch_bounds__(256) void upd_segsum_kernel(UpdArgs a, int64_t tota
                 for (int u = 0; u < U; ++u)
 #pragma unroll
                     for (int i = 0; i < VPL; ++i) acc[i][0] += tmp[u][i][0];
+            } else if constexpr (BUF) {
+                // row group g takes the U consecutive positions base + g*U ...: their byte offsets
+                // come from the wave's LDS row of offsets in one or two vector reads, then the
+                // loads go out back to back
+                uint32_t off[U];
+                const int i0 = (base + g * U) & 63;  // a multiple of U; rows at or past m are masked
+                if constexpr (U % 4 == 0) {
+#pragma unroll
+                    for (int q = 0; q < U / 4; ++q) {
+                        const uint4 v4 = *(const uint4 *)&s_xo[wave][i0 + 4 * q];
+                        off[4 * q] = v4.x;
+                        off[4 * q + 1] = v4.y;
+                        off[4 * q + 2] = v4.z;
+                        off[4 * q + 3] = v4.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) off[u] = s_xo[wave][i0 + u];
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) off[u] = base + g * U + u < m ? off[u] : x_end;
+                uint4 raw[U][VPL];
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int i = 0; i < VPL; ++i) {
+                        const int e0 = c0 + (r + i * a.lanes) * V;
+                        const uint32_t o = e0 < a.D ? off[u] + (uint32_t)e0 * ES : x_end;
+                        typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+                        const v4u t = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)o, 0, 2 /* nt */);
+                        raw[u][i] = make_uint4(t.x, t.y, t.z, t.w);
+                    }
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int i = 0; i < VPL; ++i) {
+                        float fv[V];
+                        widen16<DT>(raw[u][i], fv);
+#pragma unroll
+                        for (int e = 0; e < V; ++e) acc[i][e] += fv[e];
+                    }
             } else {
                 // keep the raw 16-byte vectors in flight; widen while accumulating
                 uint4 raw[U][VPL];
@@ -682,14 +741,20 @@ template <int DT, bool SHIFT>
 static void launch_segsum_shift(const UpdArgs &a, int vec, int vpl, int64_t waves, hipStream_t s) {
     dim3 grid((unsigned)((waves + 3) / 4)), block(256);
     constexpr int VV = DT == DT_F32 ? 4 : 8;
+    // the buffer path needs each problem's rows within 2 GiB (offsets plus a vector never wrap)
+    const bool buf = (int64_t)a.N * a.D * (DT == DT_F32 ? 4 : 2) <= ((int64_t)1 << 31);
     if (vec == 1) {
-        if (vpl == 1) upd_segsum_kernel<DT, 1, 1, SHIFT><<<grid, block, 0, s>>>(a, waves);
-        else if (vpl == 2) upd_segsum_kernel<DT, 1, 2, SHIFT><<<grid, block, 0, s>>>(a, waves);
-        else upd_segsum_kernel<DT, 1, 4, SHIFT><<<grid, block, 0, s>>>(a, waves);
+        if (vpl == 1) upd_segsum_kernel<DT, 1, 1, SHIFT, false><<<grid, block, 0, s>>>(a, waves);
+        else if (vpl == 2) upd_segsum_kernel<DT, 1, 2, SHIFT, false><<<grid, block, 0, s>>>(a, waves);
+        else upd_segsum_kernel<DT, 1, 4, SHIFT, false><<<grid, block, 0, s>>>(a, waves);
+    } else if (buf) {
+        if (vpl == 1) upd_segsum_kernel<DT, VV, 1, SHIFT, true><<<grid, block, 0, s>>>(a, waves);
+        else if (vpl == 2) upd_segsum_kernel<DT, VV, 2, SHIFT, true><<<grid, block, 0, s>>>(a, waves);
+        else upd_segsum_kernel<DT, VV, 4, SHIFT, true><<<grid, block, 0, s>>>(a, waves);
     } else {
-        if (vpl == 1) upd_segsum_kernel<DT, VV, 1, SHIFT><<<grid, block, 0, s>>>(a, waves);
-        else if (vpl == 2) upd_segsum_kernel<DT, VV, 2, SHIFT><<<grid, block, 0, s>>>(a, waves);
-        else upd_segsum_kernel<DT, VV, 4, SHIFT><<<grid, block, 0, s>>>(a, waves);
+        if (vpl == 1) upd_segsum_kernel<DT, VV, 1, SHIFT, false><<<grid, block, 0, s>>>(a, waves);
+        else if (vpl == 2) upd_segsum_kernel<DT, VV, 2, SHIFT, false><<<grid, block, 0, s>>>(a, waves);
+        else upd_segsum_kernel<DT, VV, 4, SHIFT, false><<<grid, block, 0, s>>>(a, waves);
     }
 }
 

@@ -33,7 +33,7 @@
 //     of x chunk + centroid chunk is 32 KiB, double buffered.
 // Arg-sort: counting passes over digits of the cluster id; one pass when the per-problem
 //   table (bins x tiles of 4096 keys) stays <= 2^24 entries and bins <= 1024 (LDS of a scatter
-//   workgroup: 6 x bins x 4 B of counters and offsets plus the 32 KiB staged tile); otherwise
+//   workgroup: 8 waves x bins 16-bit counters, 2 x bins offsets, the 32 KiB staged tile); otherwise
 //   balanced multi-pass LSD digits.
 // Update: rows are gathered with 16-byte vector loads when D allows; a row is covered by a
 //   power-of-two number of lanes so one wave load instruction moves 64 x 16 B from 64/lanes
