@@ -77,7 +77,11 @@ km_status_t status_word(int32_t st, const char *who) {
 constexpr int64_t MAX_N = (int64_t)1 << 31;
 constexpr int64_t MAX_D = 4096;
 constexpr int64_t MAX_K = (int64_t)1 << 24;
-constexpr int RING = 16;  // iterations of inertia / shift kept on the device between host reads
+// Iterations of inertia / shift kept on the device between host reads.  A read waits for the
+// stream to drain, and the next iteration's kernels are only launched after it, so each read
+// leaves the GPU idle for the host's round trip (about 75 us); 64 slots keep that to the end of
+// fits of up to 64 iterations (with tol = 0) for 8 * 64 * B * (workgroups per problem + 2) bytes.
+constexpr int RING = 64;
 constexpr int64_t DEFAULT_CHUNK = (int64_t)1 << 24;
 
 bool dt_ok(int dt) { return dt == KM_F32 || dt == KM_F16 || dt == KM_BF16; }

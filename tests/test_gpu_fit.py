@@ -81,6 +81,24 @@ def test_fit_resumes_from_its_centroids(fk, name, kw):
         assert crel <= CENTROID_TOL[w.dtype]
 
 
+def test_fit_inertia_across_device_ring_flushes(fk):
+    """150 iterations: the per-iteration inertia goes to the host in flushes of the device ring
+    (64 slots), so every slot of every flush must land at its own iteration: against the oracle's
+    Lloyd loop, and against a 100-iteration fit resumed for 50 more."""
+    w = W.small("tiny_f32", iters=150)
+    x, x64, c0, xt, ct = make_inputs(w)
+    c = ct.clone()
+    _, J, done = fk.kmeans_fit(xt, c, 150, 0.0)
+    assert done == 150 and J.shape[0] == 150
+    ref = oracle.lloyd_fit(x64, c0, 150, 0.0, dtype="f32", mode="modelled")
+    assert (np.abs(J - ref["inertia"]) / ref["inertia"]).max() <= INERTIA_TOL
+    c2 = ct.clone()
+    _, Ja, _ = fk.kmeans_fit(xt, c2, 100, 0.0)
+    _, Jb, _ = fk.kmeans_fit(xt, c2, 50, 0.0)
+    Jr = np.concatenate([Ja, Jb])
+    assert (np.abs(Jr - J) / J).max() <= INERTIA_TOL
+
+
 def test_fit_tol_stops_early(fk):
     w = W.small("tiny_f32", iters=50)
     x, x64, c0, xt, ct = make_inputs(w)
