@@ -8,12 +8,14 @@ D=128, K=1024, bf16; inputs resident in HBM).  Every buffer (the fit's workspace
 allocated before the first measurement, so the GPU never idles between the measurements.
 Order of the run:
 
-  1. per-stage timings, first pass ("stages_ms_first"): R teacher-forced repetitions of the stage
-     calls (row norms, centroid preparation, FlashAssign through kmeans_assign_prepared -- one
-     kernel launch per call --, arg-sort, update), each bracketed by HIP events on the stream the
-     stages run on.  A GPU that was idle during the setup passes through a power-management dip a
-     millisecond or two after its load starts (FlashAssign up to 30% slower for about 12 ms; see
-     the design notes' kernel trace); this pass takes that load, and its numbers show it.
+  1. per-stage timings, first pass ("stages_ms_first"): `--stage-reps-first` (40) teacher-forced
+     repetitions of the stage calls (row norms, centroid preparation, FlashAssign through
+     kmeans_assign_prepared -- one kernel launch per call --, arg-sort, update), each bracketed by
+     HIP events on the stream the stages run on.  A GPU that was idle during the setup runs its
+     first tens of milliseconds of load at lower clocks (FlashAssign up to 30% slower at first,
+     settling after 20-40 ms of load; see the design notes).  This pass (about 30 ms) takes that
+     load, and its numbers show it; a timed fit after 10 repetitions instead ran 2-3% slower per
+     iteration than the same fit repeated right after it.
   2. `--warmup` untimed iterations as one fit;
   3. the timed region: exactly `--steps` iterations as one kmeans_fit call, bracketed by device
      synchronisations; `value` = its wall time / steps.  `--repeat` more timed fits follow and are
@@ -55,7 +57,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5, help="untimed iterations before the timed fit")
     p.add_argument("--repeat", type=int, default=2, help="further timed fits reported beside `value`")
     p.add_argument("--workload", default="headline_bf16")
-    p.add_argument("--stage-reps", type=int, default=10)
+    p.add_argument("--stage-reps", type=int, default=10, help="repetitions of the second stage pass")
+    p.add_argument("--stage-reps-first", type=int, default=40,
+                   help="repetitions of the first stage pass (about 30 ms of load: the clocks settle in it)")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calib", action="store_true", help="run a plain 1 GiB device copy and exit")
@@ -403,7 +407,7 @@ def plan_regret():
 # ------------------------------------------------------------------------------------------------
 COUNTER_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc %s --output-format csv -d <out>/%s -o run -- "
                "python3 /root/repo/bench.py %s")
-BENCH_ARGS_COUNTERS = "--steps 1 --warmup 1 --stage-reps 2 --repeat 0 --no-cpu-baseline"
+BENCH_ARGS_COUNTERS = "--steps 1 --warmup 1 --stage-reps-first 2 --stage-reps 2 --repeat 0 --no-cpu-baseline"
 
 
 def _counter_means(path):
@@ -537,9 +541,9 @@ def summarize_trace(path, args):
     # pass is its untimed priming call); `roofline` averages the second pass
     triples = [(seq[i + 2][2] - seq[i + 2][1]) / 1e3 for i in range(len(seq) - 2)
                if names[i] == "rownorm" and names[i + 1] == "prep" and names[i + 2] == "assign"]
-    R = args.stage_reps
-    first_pass = triples[1:1 + R]
-    stage_assign = triples[2 + R:2 + 2 * R] if len(triples) >= 2 + 2 * R else first_pass
+    R1, R = args.stage_reps_first, args.stage_reps
+    first_pass = triples[1:1 + R1]
+    stage_assign = triples[2 + R1:2 + R1 + R] if len(triples) >= 2 + R1 + R else first_pass
     # fits: prep, fill, then iterations (each from an assign to the next one) until the next
     # prep or row-norm kernel (another fit or stage call); the fit's inertia sums and copies to
     # the host are not counted in an iteration's kernels
@@ -778,7 +782,7 @@ def main():
         return fk.kmeans_fit_metric(xt, c, args.metric, iters, 0.0, assign=labels)
 
     # ---- 1. per-stage times, first pass (HIP events on the stages' stream), teacher forced from c0
-    st_first, _ = stage_times(fk, w, xt, c0t, args.stage_reps, args.metric, stream)
+    st_first, _ = stage_times(fk, w, xt, c0t, args.stage_reps_first, args.metric, stream)
 
     # ---- 2. warmup (untimed): W iterations
     if args.warmup > 0:
