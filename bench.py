@@ -27,7 +27,9 @@ Prints one JSON line.  Other modes: `--copy-calib` (a plain device copy of known
 reference for scaling the FETCH_SIZE / WRITE_SIZE counters), `--summarize-trace CSV` (the
 per-iteration summary of a rocprofv3 kernel trace of this script), `--context` /
 `--context-pages` (the standard path the method replaces, at the headline shape / at the pages'
-kernel-ratio shapes).
+kernel-ratio shapes), `--plan-regret` (the K split of the plan against every alternative),
+`--summarize-counters DIR` (HBM traffic and MFMA counter summaries from rocprofv3 runs), `--clock-probe`
+(FlashAssign's shader clock and per-workgroup phase cycles from clock stamps).
 """
 from __future__ import annotations
 
@@ -61,6 +63,8 @@ def parse():
     p.add_argument("--stage-reps-first", type=int, default=40,
                    help="repetitions of the first stage pass (about 30 ms of load: the clocks settle in it)")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    p.add_argument("--clock-probe", nargs="*", metavar="B N D K [f16]",
+                   help="run the FlashAssign phase probe (clock stamps per workgroup; headline shape by default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calib", action="store_true", help="run a plain 1 GiB device copy and exit")
     p.add_argument("--metric", default="l2", choices=["l2", "dot", "cosine"],
@@ -174,7 +178,9 @@ def cpu_baseline(w, x, c0, target_s, metric="l2"):
     from oracle import similarity as sim
     from exact_lloyd_means_02_amd import workloads as W
     n, p = min(w.N, 2048), 1
-    while True:
+    per_run = target_s / 3.0   # the sample is grown to about this, then timed three times
+
+    def run_once():
         xs = W.storage_to_f64(x[:p, :n], w.dtype)
         cs = c0[:p].astype(np.float64)
         t0 = time.perf_counter()
@@ -190,23 +196,31 @@ def cpu_baseline(w, x, c0, target_s, metric="l2"):
                 xs = sim.round_to_dtype(sim.normalize_rows(xs), w.dtype)
             sim.similarity_iteration(xs, cs, metric, dtype=w.dtype, mode="modelled")
             t1 = time.perf_counter()
-        dt = time.perf_counter() - t0
-        if dt >= 0.6 * target_s or (n >= w.N and p >= w.B):
+        return time.perf_counter() - t0, t1 - t0
+
+    while True:
+        dt, ta = run_once()
+        if dt >= 0.6 * per_run or (n >= w.N and p >= w.B):
             break
-        grow = max(1.5, min(8.0, 0.7 * target_s / max(dt, 1e-3)))
+        grow = max(1.5, min(8.0, 0.7 * per_run / max(dt, 1e-3)))
         if n < w.N:
             n = min(w.N, int(n * grow))
         else:
             p = min(w.B, max(p + 1, int(p * grow)))
+    # the grown sample's run and two more: the median of the three
+    runs = [(dt, ta), run_once(), run_once()]
+    runs.sort()
+    dt, ta = runs[1]
     scale = (w.B * w.N) / (p * n)
     out = {"value": round(dt * scale * 1e3, 3), "unit": "ms", "cores": oracle.threads(), "kind": "oracle",
            "sample": "one fp64 oracle iteration on %d of %d points (%d problem(s) x %d points, all K=%d "
-                     "centroids) took %.2f s; scaled by %.1fx to the full iteration" % (
-                         p * n, w.B * w.N, p, n, w.K, dt, scale),
+                     "centroids), median of 3 runs %.2f s (runs %s s); scaled by %.1fx to the full "
+                     "iteration" % (p * n, w.B * w.N, p, n, w.K, dt, ["%.2f" % r[0] for r in runs], scale),
+           "runs_s": [round(r[0], 3) for r in runs],
            "host": host_info()}
     if metric == "l2":
-        out["assign_ms"] = round((t1 - t0) * scale * 1e3, 3)
-        out["update_ms"] = round((dt - (t1 - t0)) * scale * 1e3, 3)
+        out["assign_ms"] = round(ta * scale * 1e3, 3)
+        out["update_ms"] = round((dt - ta) * scale * 1e3, 3)
     return out
 
 
@@ -753,6 +767,14 @@ def main():
     if args.plan_regret:
         plan_regret()
         return
+    if args.clock_probe is not None:
+        # the probe executable built beside the library (its own compilation of the assign source
+        # with clock stamps); it prints its own summary
+        exe = os.path.join(ROOT, "exact_lloyd_means_02_amd", "probe_assign_clock")
+        if not os.path.exists(exe):
+            print("bench.py: %s is not built (build the package first)" % exe, file=sys.stderr)
+            sys.exit(2)
+        sys.exit(subprocess.call([exe] + list(args.clock_probe)))
     import numpy as np
     import torch
     from exact_lloyd_means_02_amd import flashkm as fk

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libflashkm.so")
 SOURCES = ["api.hip", "k_assign.hip", "k_assign_d64.hip", "k_sort.hip", "k_update.hip", "k_misc.hip", "plan.cpp"]
-HEADERS = ["common.h", "plan.h", os.path.join("..", "..", "include", "flashkm.h")]
+HEADERS = ["common.h", "plan.h", os.path.join("..", "..", "include", "flashkm.h"), "probe_assign_clock.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -46,6 +46,28 @@ def _compile(src: str) -> str:
     return obj
 
 
+PROBE_SRC = "probe_assign_clock.hip"
+PROBE = os.path.join(HERE, "probe_assign_clock")
+
+
+def _build_probe(objs) -> str:
+    """The FlashAssign phase probe (a measuring executable, not part of the library): its own compilation
+    of the assign source with clock stamps, linked with the plan and the D = 64 unit."""
+    obj = os.path.join(BUILD, "probe_assign_clock.o")
+    cmd = [HIPCC, *FLAGS, *EXTRA["k_assign.hip"], "-c", os.path.join(CSRC, PROBE_SRC), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (PROBE_SRC, " ".join(cmd), r.stderr))
+    deps = [o for o in objs if os.path.basename(o) in ("plan.o", "k_assign_d64.o")]
+    tmp = PROBE + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "--offload-arch=gfx950", obj, *deps, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
+    os.replace(tmp, PROBE)
+    return PROBE
+
+
 def build(force: bool = True, verbose: bool = False) -> str:
     """Compile every source for gfx950 and link libflashkm.so (always recompiles when force)."""
     os.makedirs(BUILD, exist_ok=True)
@@ -62,8 +84,9 @@ def build(force: bool = True, verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
     os.replace(tmp, LIB)
+    _build_probe(objs)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE)
     return LIB
 
 

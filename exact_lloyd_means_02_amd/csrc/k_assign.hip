@@ -32,6 +32,32 @@ namespace fkm {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// Clock stamps of the small-D kernel's phases, for the phase probe (probe_assign_clock.hip, which
+// defines FKM_CLOCK_STAMPS); compiled out of the library.  Thread 0 of workgroup w writes
+// fkm_stamps[w]: [0] start, [1] scan start (point tile and first stages in), [2] scan end, [3] end
+// (shader clock, s_memtime), [4] start and [5] end (the 100 MHz real-time counter).
+#ifdef FKM_CLOCK_STAMPS
+constexpr int FKM_STAMP_WGS = 1 << 14;
+__device__ unsigned long long fkm_stamps[FKM_STAMP_WGS][8];
+#define FKM_STAMP(i)                                                                      \
+    do {                                                                                  \
+        if (threadIdx.x == 0 && blockIdx.x < (unsigned)FKM_STAMP_WGS)                     \
+            fkm_stamps[blockIdx.x][i] = __builtin_amdgcn_s_memtime();                      \
+    } while (0)
+#define FKM_RSTAMP(i)                                                                     \
+    do {                                                                                  \
+        if (threadIdx.x == 0 && blockIdx.x < (unsigned)FKM_STAMP_WGS)                     \
+            fkm_stamps[blockIdx.x][i] = __builtin_amdgcn_s_memrealtime();                  \
+    } while (0)
+#else
+#define FKM_STAMP(i) \
+    do {             \
+    } while (0)
+#define FKM_RSTAMP(i) \
+    do {              \
+    } while (0)
+#endif
+
 // ------------------------------------------------------------------------------------------
 // Centroid preparation.
 //   cprep (per problem, tile t of 32 centroids, group q < DP/(2*VW), lane l = i + 32h):
@@ -347,6 +373,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     __shared__ u32x4 s_c0[STAGE_U4], s_c1[STAGE_U4], s_c2[STAGE_U4];
     __shared__ __attribute__((aligned(16))) float s_n0[TPS * 32], s_n1[TPS * 32], s_n2[TPS * 32];
 
+    FKM_RSTAMP(4);
+    FKM_STAMP(0);
     // consecutive logical workgroups (one XCD) take the K ranges of a point tile, then the next tile
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
     const int per_b = wgs_per_b * nsplit;
@@ -554,12 +582,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 #pragma unroll
     for (int q = 0; q < FR; ++q) f[q] = s_c0[q * 64 + lane];
 
+    FKM_STAMP(1);
     for (int s0 = s_beg; s0 < nst; s0 += 3) {
         run_stage(s0, s_c0, s_n0, s_c1, s_n1, s_c2, s_n2);
         if (s0 + 1 < nst) run_stage(s0 + 1, s_c1, s_n1, s_c2, s_n2, s_c0, s_n0);
         if (s0 + 2 < nst) run_stage(s0 + 2, s_c2, s_n2, s_c0, s_n0, s_c1, s_n1);
     }
 
+    FKM_STAMP(2);
     double dsum = 0.0;
 #pragma unroll
     for (int p = 0; p < PB; ++p) {
@@ -596,6 +626,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
         }
     }
     if (!split && wg_inertia) workgroup_inertia(dsum, wg_inertia + (size_t)b * wgs_per_b + tn);
+    FKM_STAMP(3);
+    FKM_RSTAMP(5);
 }
 
 // After a K-split assign: each point's least key -> label (and distance xn + 2 score), with the

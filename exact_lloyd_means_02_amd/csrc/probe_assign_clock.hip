@@ -1,0 +1,144 @@
+// Phase probe of the small-D FlashAssign kernel: the kernel built with FKM_CLOCK_STAMPS, launched on a
+// synthetic problem of the given shape, and every workgroup's clock stamps summarised:
+//   * the shader clock during the workgroups (s_memtime cycles over the 100 MHz real-time counter);
+//   * per workgroup, cycles from start to the scan (point tile in, first centroid stages in), in the
+//     scan (per 32-centroid tile too), and from the scan's end to the workgroup's end, split into the
+//     workgroups of the first round (started in the launch's first 2 us) and the later ones;
+//   * the launch time and its fraction of the nominal bf16/fp16 MFMA peak (2.5 PFLOP/s).
+// A measuring tool, not part of the library; built by build.py beside libflashkm.so and run by
+// `bench.py --clock-probe`.  Usage: probe_assign_clock [B N D K [dtype: bf16|f16]]
+#define FKM_CLOCK_STAMPS 1
+#include "k_assign.hip"
+
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <random>
+#include <string>
+#include <vector>
+
+#define CK(x)                                                                              \
+    do {                                                                                   \
+        hipError_t e_ = (x);                                                               \
+        if (e_ != hipSuccess) {                                                            \
+            std::printf("HIP error %s at line %d\n", hipGetErrorString(e_), __LINE__);     \
+            std::exit(1);                                                                  \
+        }                                                                                  \
+    } while (0)
+
+// host rounding of fp32 to the 2-byte types, nearest even (finite inputs)
+static uint16_t host_to_bf16(float f) {
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+static uint16_t host_to_f16(float f) {
+    const _Float16 h = (_Float16)f;
+    uint16_t u;
+    std::memcpy(&u, &h, 2);
+    return u;
+}
+
+static double pct(std::vector<double> v, double q) {
+    if (v.empty()) return 0.0;
+    std::sort(v.begin(), v.end());
+    return v[std::min(v.size() - 1, (size_t)(q * v.size()))];
+}
+
+int main(int argc, char **argv) {
+    using namespace fkm;
+    const int B = argc > 4 ? std::atoi(argv[1]) : 32, N = argc > 4 ? std::atoi(argv[2]) : 65536;
+    const int D = argc > 4 ? std::atoi(argv[3]) : 128, K = argc > 4 ? std::atoi(argv[4]) : 1024;
+    const bool f16 = argc > 5 && std::string(argv[5]) == "f16";
+    const int dt = f16 ? DT_F16 : DT_BF16;
+    const AssignCfg cfg = plan_assign(dt, B, N, D, K);
+    if (B < 1 || N < 1 || D < 1 || K < 1 || cfg.path != 0 || cfg.nsplit != 1) {
+        std::printf("the probe covers unsplit small-D plans of 2-byte inputs\n");
+        return 2;
+    }
+    const int KT = assign_tiles(K);
+    const int wpb = (N + cfg.block_n - 1) / cfg.block_n;
+    const long nwg = (long)B * wpb;
+    if (nwg > FKM_STAMP_WGS) {
+        std::printf("the probe records at most %d workgroups (this shape has %ld)\n", FKM_STAMP_WGS, nwg);
+        return 2;
+    }
+    std::printf("shape B=%d N=%d D=%d K=%d %s: %ld workgroups of %d points, %d centroid tiles each\n", B, N, D, K,
+                f16 ? "f16" : "bf16", nwg, cfg.block_n, KT);
+    // points ~ N(0, 1) rounded to the dtype, centroids ~ N(0, 1) in fp32
+    std::mt19937 rng(20260309);
+    std::normal_distribution<float> nd(0.f, 1.f);
+    std::vector<uint16_t> hx((size_t)B * N * D);
+    for (auto &v : hx) v = f16 ? host_to_f16(nd(rng)) : host_to_bf16(nd(rng));
+    std::vector<float> hc((size_t)B * K * D);
+    for (auto &v : hc) v = nd(rng);
+    void *x, *cprep;
+    float *C, *cnh;
+    int32_t *a;
+    double *wgi;
+    CK(hipMalloc(&x, hx.size() * 2));
+    CK(hipMemcpy(x, hx.data(), hx.size() * 2, hipMemcpyHostToDevice));
+    CK(hipMalloc(&C, hc.size() * 4));
+    CK(hipMemcpy(C, hc.data(), hc.size() * 4, hipMemcpyHostToDevice));
+    CK(hipMalloc(&cprep, (size_t)B * KT * 32 * cfg.d_pad * 2));
+    CK(hipMalloc(&cnh, (size_t)B * KT * 32 * 4));
+    CK(hipMalloc(&a, (size_t)B * N * 4));
+    CK(hipMalloc(&wgi, (size_t)B * wpb * 8));
+    CK(launch_prep_centroids(dt, C, cprep, cnh, B, K, D, cfg.d_pad, 0, 0));
+    hipEvent_t e0, e1;
+    CK(hipEventCreate(&e0));
+    CK(hipEventCreate(&e1));
+    // the launches of the fit's form (point norms from registers, inertia partials); about 40 ms of
+    // load first so that the clocks have settled, then the recorded launch
+    float ms = 0.f;
+    const long reps = std::max(20L, (long)(4.0e13 / (2.0 * B * N * K * D) * 1.0));
+    for (long it = 0; it < reps; ++it) {
+        CK(hipEventRecord(e0));
+        CK(launch_assign(dt, cfg, x, cprep, cnh, nullptr, a, nullptr, wgi, B, N, D, K, 0, AssignSplit{}));
+        CK(hipEventRecord(e1));
+        CK(hipEventSynchronize(e1));
+        CK(hipEventElapsedTime(&ms, e0, e1));
+    }
+    std::vector<unsigned long long> s((size_t)nwg * 8);
+    CK(hipMemcpyFromSymbol(s.data(), HIP_SYMBOL(fkm_stamps), s.size() * 8));
+    unsigned long long r0 = ~0ull, r1 = 0;
+    for (long w = 0; w < nwg; ++w) {
+        r0 = std::min(r0, s[w * 8 + 4]);
+        r1 = std::max(r1, s[w * 8 + 5]);
+    }
+    std::vector<double> clk, pro1, pro2, scan, epi, dur;
+    for (long w = 0; w < nwg; ++w) {
+        const unsigned long long *t = &s[w * 8];
+        const double rt = (double)(t[5] - t[4]);  // 10 ns units
+        if (rt > 0) clk.push_back((double)(t[3] - t[0]) / rt * 100.0);
+        const double start_us = (t[4] - r0) / 100.0;
+        (start_us < 2.0 ? pro1 : pro2).push_back((double)(t[1] - t[0]));
+        scan.push_back((double)(t[2] - t[1]));
+        epi.push_back((double)(t[3] - t[2]));
+        dur.push_back(rt / 100.0);
+    }
+    const double flop = 2.0 * B * N * (double)K * D;
+    std::printf("recorded launch: %.1f us, %.1f%% of 2.5 PFLOP/s (%ld launches of load before it)\n", ms * 1e3,
+                flop / (ms * 1e-3) / 2.5e15 * 100.0, reps - 1);
+    const double mhz = pct(clk, 0.5);
+    std::printf("shader clock during the workgroups: median %.0f MHz (p10 %.0f, p90 %.0f); at the median the\n"
+                "  MFMA peak is %.2f PFLOP/s and the launch runs at %.1f%% of it\n",
+                mhz, pct(clk, 0.1), pct(clk, 0.9), 2.5 * mhz / 2400.0,
+                flop / (ms * 1e-3) / (2.5e15 * mhz / 2400.0) * 100.0);
+    std::printf("workgroup duration: p50 %.2f us (min %.2f, max %.2f); span of the stamps %.1f us\n", pct(dur, 0.5),
+                pct(dur, 0.0), pct(dur, 1.0), (r1 - r0) / 100.0);
+    std::printf("shader cycles per workgroup (p10 / p50 / p90):\n");
+    std::printf("  to the scan, first round (%4zu wgs): %8.0f %8.0f %8.0f\n", pro1.size(), pct(pro1, 0.1), pct(pro1, 0.5),
+                pct(pro1, 0.9));
+    std::printf("  to the scan, later     (%5zu wgs): %8.0f %8.0f %8.0f\n", pro2.size(), pct(pro2, 0.1), pct(pro2, 0.5),
+                pct(pro2, 0.9));
+    std::printf("  scan                                 %8.0f %8.0f %8.0f   (per centroid tile %.0f at p50)\n",
+                pct(scan, 0.1), pct(scan, 0.5), pct(scan, 0.9), pct(scan, 0.5) / KT);
+    std::printf("  after the scan                       %8.0f %8.0f %8.0f\n", pct(epi, 0.1), pct(epi, 0.5),
+                pct(epi, 0.9));
+    const int mf = cfg.pb * (cfg.d_pad / 16);  // 32x32x16 MFMAs per tile and wave
+    std::printf("  (a tile's MFMA work per wave: %d MFMAs of 32 cycles = %d cycles; three waves per SIMD: %d)\n",
+                mf, mf * 32, 3 * mf * 32);
+    return 0;
+}
