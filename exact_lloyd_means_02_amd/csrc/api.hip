@@ -36,9 +36,8 @@ hipError_t launch_finalize_acc(int dt, const float *sums, const int32_t *cnt, fl
                                const UpdRefresh &ref, int B, int K, int D, hipStream_t s, int normalize);
 hipError_t launch_row_norms(int dt, const void *x, float *out, int64_t rows, int D, hipStream_t s);
 hipError_t launch_normalize_rows(int dt, const void *x, void *out, int64_t rows, int D, hipStream_t s);
-size_t reduce_ws_bytes(int64_t B);
-hipError_t launch_sum_f32(const float *v, int B, int64_t n, double *out, int accumulate, void *ws, hipStream_t s);
-hipError_t launch_sum_f64_rows(const double *part, int rows, int64_t len, double *out, hipStream_t s);
+hipError_t launch_sum_f64_rows(const double *part, int rows, int64_t len, double *out, hipStream_t s,
+                               int accumulate = 0);
 }  // namespace fkm
 
 using namespace fkm;
@@ -175,7 +174,7 @@ FitLayout fit_layout(int dt, int64_t B, int64_t N, int64_t D, int64_t K, int met
     L.updctr = o; o += update_ctr_bytes(dt, B, N, D, K);
     L.prep = o; o += prep_bytes(dt, B, N, D, K);
     L.split = o; o += split_bytes(dt, B, N, D, K);
-    L.ring_part = o; o += align256((size_t)RING * B * assign_wgs_per_problem(dt, B, N, D, K) * 8);
+    L.ring_part = o; o += align256((size_t)RING * B * assign_wgs_per_problem(dt, B, N, D, K) * ASSIGN_WAVES * 8);
     L.ring_j = o; o += align256((size_t)RING * B * 8);
     L.ring_s = o; o += align256((size_t)RING * B * 8);
     if (metric == KM_METRIC_COSINE) {
@@ -194,8 +193,8 @@ FitLayout fit_layout(int dt, int64_t B, int64_t N, int64_t D, int64_t K, int met
 }
 
 struct HostLayout {
-    size_t stage_buf[2], cprep, xn, md, a, sids, sidx, counts, offs, status, updctr, sums, cnt, shk, ring_j, ring_s,
-        red, scratch, total;
+    size_t stage_buf[2], cprep, xn, part, a, sids, sidx, counts, offs, status, updctr, sums, cnt, shk, ring_j,
+        ring_s, scratch, total;
     int64_t chunk;
 };
 
@@ -247,7 +246,8 @@ HostLayout host_layout(int dt, int64_t B, int64_t N, int64_t D, int64_t K, int64
     L.cprep = o; o += prep_bytes(dt, B, N, D, K);
     const size_t c4 = align256((size_t)c * 4);
     L.xn = o; o += c4;
-    L.md = o; o += c4;
+    // the assign's per-wave inertia partials of one chunk (a shorter last chunk has fewer)
+    L.part = o; o += align256((size_t)assign_wgs_per_problem(dt, 1, c, D, K) * ASSIGN_WAVES * 8);
     L.a = o; o += c4;
     L.sids = o; o += c4;
     L.sidx = o; o += c4;
@@ -260,7 +260,6 @@ HostLayout host_layout(int dt, int64_t B, int64_t N, int64_t D, int64_t K, int64
     L.shk = o; o += align256((size_t)B * K * 8);
     L.ring_j = o; o += align256((size_t)RING * B * 8);
     L.ring_s = o; o += align256((size_t)RING * B * 8);
-    L.red = o; o += reduce_ws_bytes(B);
     L.scratch = o;
     o += host_scratch(dt, N, D, K, c);
     L.total = o;
@@ -650,7 +649,7 @@ km_status_t fit_device(int dt, const void *x, int64_t B, int64_t N, int64_t D, i
     const bool cosine = metric == KM_METRIC_COSINE;
     const AssignCfg cfg = plan_assign(dt, B, N, D, K);
     const int64_t KT = assign_tiles(K);
-    const int64_t wpb = assign_wgs_per_problem(dt, B, N, D, K);
+    const int64_t wpb = assign_wgs_per_problem(dt, B, N, D, K) * ASSIGN_WAVES;  // inertia partials per problem
     float *xn = (float *)(ws + L.xn);
     int32_t *a = assign ? assign : (int32_t *)(ws + L.a);
     int32_t *sids = (int32_t *)(ws + L.sids);
@@ -694,7 +693,7 @@ km_status_t fit_device(int dt, const void *x, int64_t B, int64_t N, int64_t D, i
     int32_t st_host = 0;
     for (int t = 0; t < iters; ++t) {
         const int slot = t - flushed;
-        // one iteration: assign (+ per-workgroup inertia partials), arg-sort (+ counts and the
+        // one iteration: assign (+ per-wave inertia partials), arg-sort (+ counts and the
         // clusters' first positions), update (+ shift, + the next iteration's prepared centroids)
         KM_HIP(launch_assign(dt, cfg, xa, cprep, cnh, xn_in, a, nullptr, ring_part + (size_t)slot * B * wpb, (int)B,
                              (int)N, (int)D, (int)K, s, sp));
@@ -792,7 +791,7 @@ km_status_t fit_host(int dt, const HostSource &src, int64_t B, int64_t N, int64_
     float *cnh = (float *)(cprep + cprep_bytes);
     const size_t cprep_per_b = (size_t)KT * 32 * cfg.d_pad * es;
     float *xn = (float *)(ws + L.xn);
-    float *md = (float *)(ws + L.md);
+    double *part = (double *)(ws + L.part);
     int32_t *a_ws = (int32_t *)(ws + L.a);
     int32_t *sids = (int32_t *)(ws + L.sids);
     int32_t *sidx = (int32_t *)(ws + L.sidx);
@@ -802,7 +801,6 @@ km_status_t fit_host(int dt, const HostSource &src, int64_t B, int64_t N, int64_
     int32_t *cnt = (int32_t *)(ws + L.cnt);
     double *ring_j = (double *)(ws + L.ring_j);
     double *ring_s = (double *)(ws + L.ring_s);
-    void *red = ws + L.red;
     void *scratch = ws + L.scratch;
     UpdMem mem;
     mem.offs = (const int32_t *)(ws + L.offs);
@@ -864,9 +862,11 @@ km_status_t fit_host(int dt, const HostSource &src, int64_t B, int64_t N, int64_
             if (cfg.path != 0 && !simm) KM_HIP(launch_row_norms(dt, xc, xn, n, (int)D, s));
             // one scan per point tile: chunks of 2^24 points fill the chip by themselves
             KM_HIP(launch_assign(dt, cfg, xc, cprep + (size_t)b * cprep_per_b, cnh + (size_t)b * KT * 32,
-                                 (cfg.path == 0 && !simm) ? nullptr : xn, ac, md,
-                                 nullptr, 1, (int)n, (int)D, (int)K, s, AssignSplit{}));
-            KM_HIP(launch_sum_f32(md, 1, n, ring_j + (size_t)slot * B + b, 1, red, s));
+                                 (cfg.path == 0 && !simm) ? nullptr : xn, ac, nullptr, part, 1, (int)n, (int)D,
+                                 (int)K, s, AssignSplit{}));
+            // the chunk's inertia: its per-wave partials in order, added to the problem's sum
+            KM_HIP(launch_sum_f64_rows(part, 1, ceil_div(n, (int64_t)cfg.block_n) * ASSIGN_WAVES,
+                                       ring_j + (size_t)slot * B + b, s, 1));
             KM_HIP(launch_argsort(ac, 1, (int)n, (int)K, sids, sidx, counts, (int32_t *)mem.offs, status, scratch, s));
             KM_HIP(launch_update(dt, xc, sids, sidx, counts, 1, (int)n, (int)D, (int)K, 1, nullptr, nullptr,
                                  sums + (size_t)b * K * D, cnt + (size_t)b * K, UpdRefresh{}, mem, s));

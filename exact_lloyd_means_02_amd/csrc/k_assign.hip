@@ -297,20 +297,14 @@ __device__ inline float argmin_finish(const ArgminState &s, int h, bool write, i
     return d;
 }
 
-// Sum of the workgroup's point distances in fp64, fixed order (lanes, then waves); thread 0
-// writes it.  Feeds the per-iteration inertia without a pass over min_dist.
-__device__ inline void workgroup_inertia(double v, double *dst) {
-    __shared__ double s_w[ASSIGN_WAVES];
+// Sum of the wave's point distances in fp64, fixed order (a butterfly over the lanes); lane 0
+// writes it to dst[wave] (dst: the workgroup's ASSIGN_WAVES partials).  No workgroup barrier, so a
+// wave that finishes its scan early leaves without waiting for the others.  Feeds the
+// per-iteration inertia without a pass over min_dist.
+__device__ inline void wave_inertia(double v, double *dst) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = v;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        double t = 0.0;
-#pragma unroll
-        for (int i = 0; i < ASSIGN_WAVES; ++i) t += s_w[i];
-        *dst = t;
-    }
+    if ((threadIdx.x & 63) == 0) dst[threadIdx.x >> 6] = v;
 }
 
 // s_waitcnt immediate that waits until at most n vector-memory loads are outstanding and all
@@ -625,7 +619,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
             dsum += argmin_finish(st[p], h, h == 0 && pt < N, (int64_t)b * N + pt, out_a, out_d, xnorm, want_d, own);
         }
     }
-    if (!split && wg_inertia) workgroup_inertia(dsum, wg_inertia + (size_t)b * wgs_per_b + tn);
+    if (!split && wg_inertia) wave_inertia(dsum, wg_inertia + ((size_t)b * wgs_per_b + tn) * ASSIGN_WAVES);
     FKM_STAMP(3);
     FKM_RSTAMP(5);
 }
@@ -660,7 +654,7 @@ __global__ __launch_bounds__(256) void split_finish_kernel(unsigned long long *_
             }
         }
     }
-    if (wg_inertia) workgroup_inertia(dsum, wg_inertia + (size_t)b * wgs_per_b + tn);
+    if (wg_inertia) wave_inertia(dsum, wg_inertia + ((size_t)b * wgs_per_b + tn) * ASSIGN_WAVES);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -774,7 +768,7 @@ __global__ __launch_bounds__(256) void assign_split_d_kernel(const void *__restr
     const int pt = pbase + w * 32 + (lane & 31);
     const float d = argmin_finish(st, h, h == 0 && pt < N, (int64_t)b * N + pt, out_a, out_d, xnorm,
                                   out_d != nullptr || wg_inertia != nullptr);
-    if (wg_inertia) workgroup_inertia((double)d, wg_inertia + (size_t)b * wgs_per_b + tn);
+    if (wg_inertia) wave_inertia((double)d, wg_inertia + ((size_t)b * wgs_per_b + tn) * ASSIGN_WAVES);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -862,7 +856,7 @@ static hipError_t launch_small_dt(int DP, const void *x, const void *cprep, cons
     return hipErrorInvalidValue;
 }
 
-// wgi (optional): per-workgroup fp64 sums of the chosen distances, [B][assign_wgs_per_problem].
+// wgi (optional): per-wave fp64 sums of the chosen distances, [B][assign_wgs_per_problem][ASSIGN_WAVES].
 // xn: point norms for the distances (md / wgi); the small-D kernel computes them itself when NULL.
 // sp: the K split (small-D path; nsplit 1 = one scan of all centroids per point tile).
 hipError_t launch_assign(int dt, const AssignCfg &cfg, const void *x, const void *cprep, const float *cnh,

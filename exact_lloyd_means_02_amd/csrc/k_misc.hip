@@ -240,43 +240,12 @@ hipError_t launch_normalize_rows(int dt, const void *x, void *out, int64_t rows,
 }
 
 // ------------------------------------------------------------------------------------------
-// Deterministic fp64 sums of float arrays, segmented by problem: level 1 writes one partial per
-// (problem, block) in a fixed order, level 2 adds the partials of a problem in order.
+// Deterministic fp64 sums of partials, one row per workgroup in a fixed order.
 // ------------------------------------------------------------------------------------------
-constexpr int RED_BLOCKS = 64;
-
-__global__ __launch_bounds__(256) void sum_f32_level1_kernel(const float *__restrict__ v, int64_t n,
-                                                             double *__restrict__ part) {
-    __shared__ double s[256];
-    const int b = blockIdx.y, blk = blockIdx.x;
-    const float *vb = v + (size_t)b * n;
-    const int64_t per = (n + RED_BLOCKS - 1) / RED_BLOCKS;
-    const int64_t lo = blk * per, hi = lo + per < n ? lo + per : n;
-    double acc = 0.0;
-    for (int64_t i = lo + threadIdx.x; i < hi; i += 256) acc += (double)vb[i];
-    s[threadIdx.x] = acc;
-    __syncthreads();
-    for (int off = 128; off >= 1; off >>= 1) {
-        if ((int)threadIdx.x < off) s[threadIdx.x] += s[threadIdx.x + off];
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) part[(size_t)b * RED_BLOCKS + blk] = s[0];
-}
-
-// out[b] (= or +=) sum of the problem's partials.
-__global__ void sum_level2_kernel(const double *__restrict__ part, double *__restrict__ out, int accumulate) {
-    if (threadIdx.x != 0) return;
-    const int b = blockIdx.x;
-    double acc = 0.0;
-    for (int i = 0; i < RED_BLOCKS; ++i) acc += part[(size_t)b * RED_BLOCKS + i];
-    out[b] = accumulate ? out[b] + acc : acc;
-}
-
-size_t reduce_ws_bytes(int64_t B) { return align256((size_t)B * RED_BLOCKS * 8); }
-
-// out[r] = sum_j part[r * len + j] (fp64), one workgroup per row, fixed order.
+// out[r] = sum_j part[r * len + j] (fp64), one workgroup per row, fixed order; with accumulate,
+// out[r] += that sum.
 __global__ __launch_bounds__(256) void sum_f64_rows_kernel(const double *__restrict__ part, int64_t len,
-                                                           double *__restrict__ out) {
+                                                           double *__restrict__ out, int accumulate) {
     __shared__ double s[256];
     const double *p = part + (size_t)blockIdx.x * len;
     double acc = 0.0;
@@ -287,20 +256,13 @@ __global__ __launch_bounds__(256) void sum_f64_rows_kernel(const double *__restr
         if ((int)threadIdx.x < off) s[threadIdx.x] += s[threadIdx.x + off];
         __syncthreads();
     }
-    if (threadIdx.x == 0) out[blockIdx.x] = s[0];
+    if (threadIdx.x == 0) out[blockIdx.x] = accumulate ? out[blockIdx.x] + s[0] : s[0];
 }
 
-hipError_t launch_sum_f64_rows(const double *part, int rows, int64_t len, double *out, hipStream_t s) {
+hipError_t launch_sum_f64_rows(const double *part, int rows, int64_t len, double *out, hipStream_t s,
+                               int accumulate) {
     if (rows <= 0) return hipSuccess;
-    sum_f64_rows_kernel<<<dim3(rows), dim3(256), 0, s>>>(part, len, out);
-    return hipGetLastError();
-}
-
-// out[b] = sum_i v[b*n + i] (fp64), or out[b] += ... when accumulate.
-hipError_t launch_sum_f32(const float *v, int B, int64_t n, double *out, int accumulate, void *ws, hipStream_t s) {
-    double *part = (double *)ws;
-    sum_f32_level1_kernel<<<dim3(RED_BLOCKS, B), dim3(256), 0, s>>>(v, n, part);
-    sum_level2_kernel<<<dim3(B), dim3(64), 0, s>>>(part, out, accumulate);
+    sum_f64_rows_kernel<<<dim3(rows), dim3(256), 0, s>>>(part, len, out, accumulate);
     return hipGetLastError();
 }
 

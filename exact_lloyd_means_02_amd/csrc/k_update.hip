@@ -20,7 +20,8 @@
 
 namespace fkm {
 
-hipError_t launch_sum_f64_rows(const double *part, int rows, int64_t len, double *out, hipStream_t s);
+hipError_t launch_sum_f64_rows(const double *part, int rows, int64_t len, double *out, hipStream_t s,
+                               int accumulate = 0);
 
 // Row loads issued before any is consumed: 8 vectors per lane in flight (8 KiB per wave).  With
 // 16 the kernel needs more than 128 VGPRs and only 3 waves fit a SIMD instead of 4; more waves

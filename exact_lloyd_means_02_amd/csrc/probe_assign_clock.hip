@@ -84,7 +84,7 @@ int main(int argc, char **argv) {
     CK(hipMalloc(&cprep, (size_t)B * KT * 32 * cfg.d_pad * 2));
     CK(hipMalloc(&cnh, (size_t)B * KT * 32 * 4));
     CK(hipMalloc(&a, (size_t)B * N * 4));
-    CK(hipMalloc(&wgi, (size_t)B * wpb * 8));
+    CK(hipMalloc(&wgi, (size_t)B * wpb * ASSIGN_WAVES * 8));  // per-wave inertia partials
     CK(launch_prep_centroids(dt, C, cprep, cnh, B, K, D, cfg.d_pad, 0, 0));
     hipEvent_t e0, e1;
     CK(hipEventCreate(&e0));
