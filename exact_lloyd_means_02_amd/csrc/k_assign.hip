@@ -32,10 +32,11 @@ namespace fkm {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Clock stamps of the small-D kernel's phases, for the phase probe (probe_assign_clock.hip, which
+// Clock stamps of the assign kernels' phases, for the phase probe (probe_assign_clock.hip, which
 // defines FKM_CLOCK_STAMPS); compiled out of the library.  Thread 0 of workgroup w writes
-// fkm_stamps[w]: [0] start, [1] scan start (point tile and first stages in), [2] scan end, [3] end
-// (shader clock, s_memtime), [4] start and [5] end (the 100 MHz real-time counter).
+// fkm_stamps[w]: [0] start, [1] scan start (point tile and first stages in; split-D: the first
+// chunk pair in), [2] scan end, [3] end (shader clock, s_memtime), [4] start and [5] end (the
+// 100 MHz real-time counter).
 #ifdef FKM_CLOCK_STAMPS
 constexpr int FKM_STAMP_WGS = 1 << 14;
 __device__ unsigned long long fkm_stamps[FKM_STAMP_WGS][8];
@@ -684,6 +685,8 @@ __global__ __launch_bounds__(256) void assign_split_d_kernel(const void *__restr
     __shared__ u32x4 s_x[2][XU4];
     __shared__ u32x4 s_c[2][CU4];
 
+    FKM_RSTAMP(4);
+    FKM_STAMP(0);
     const int QG = DP / (2 * VW);
     const int NC = DP / BD;
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
@@ -733,6 +736,7 @@ __global__ __launch_bounds__(256) void assign_split_d_kernel(const void *__restr
     gload(0);
     swrite(0);
     __syncthreads();
+    FKM_STAMP(1);
     for (int s = 0; s < nstage; ++s) {
         const int buf = s & 1;
         const int g = s / NC, dc = s - g * NC;
@@ -765,10 +769,13 @@ __global__ __launch_bounds__(256) void assign_split_d_kernel(const void *__restr
         if (s + 1 < nstage) swrite(buf ^ 1);
         __syncthreads();
     }
+    FKM_STAMP(2);
     const int pt = pbase + w * 32 + (lane & 31);
     const float d = argmin_finish(st, h, h == 0 && pt < N, (int64_t)b * N + pt, out_a, out_d, xnorm,
                                   out_d != nullptr || wg_inertia != nullptr);
     if (wg_inertia) wave_inertia((double)d, wg_inertia + ((size_t)b * wgs_per_b + tn) * ASSIGN_WAVES);
+    FKM_STAMP(3);
+    FKM_RSTAMP(5);
 }
 
 // ------------------------------------------------------------------------------------------

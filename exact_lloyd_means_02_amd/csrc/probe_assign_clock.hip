@@ -1,12 +1,14 @@
-// Phase probe of the small-D FlashAssign kernel: the kernel built with FKM_CLOCK_STAMPS, launched on a
-// synthetic problem of the given shape, and every workgroup's clock stamps summarised:
+// Phase probe of the FlashAssign kernels: the kernel the plan picks (small-D or split-D) built with
+// FKM_CLOCK_STAMPS, launched on a synthetic problem of the given shape, and every workgroup's clock
+// stamps summarised:
 //   * the shader clock during the workgroups (s_memtime cycles over the 100 MHz real-time counter);
 //   * per workgroup, cycles from start to the scan (point tile in, first centroid stages in), in the
 //     scan (per 32-centroid tile too), and from the scan's end to the workgroup's end, split into the
 //     workgroups of the first round (started in the launch's first 2 us) and the later ones;
-//   * the launch time and its fraction of the nominal bf16/fp16 MFMA peak (2.5 PFLOP/s).
+//   * the launch time and its fraction of the nominal MFMA peak of the dtype (2.5 PFLOP/s bf16/fp16,
+//     157.3 TFLOP/s fp32), and of that peak at the measured clock.
 // A measuring tool, not part of the library; built by build.py beside libflashkm.so and run by
-// `bench.py --clock-probe`.  Usage: probe_assign_clock [B N D K [dtype: bf16|f16]]
+// `bench.py --clock-probe`.  Usage: probe_assign_clock [B N D K [dtype: bf16|f16|f32]]
 #define FKM_CLOCK_STAMPS 1
 #include "k_assign.hip"
 
@@ -50,11 +52,13 @@ int main(int argc, char **argv) {
     using namespace fkm;
     const int B = argc > 4 ? std::atoi(argv[1]) : 32, N = argc > 4 ? std::atoi(argv[2]) : 65536;
     const int D = argc > 4 ? std::atoi(argv[3]) : 128, K = argc > 4 ? std::atoi(argv[4]) : 1024;
-    const bool f16 = argc > 5 && std::string(argv[5]) == "f16";
-    const int dt = f16 ? DT_F16 : DT_BF16;
+    const std::string dts = argc > 5 ? std::string(argv[5]) : std::string("bf16");
+    const int dt = dts == "f16" ? DT_F16 : (dts == "f32" ? DT_F32 : DT_BF16);
+    const int es = dt == DT_F32 ? 4 : 2;
+    const double peak = dt == DT_F32 ? 157.3e12 : 2.5e15;
     const AssignCfg cfg = plan_assign(dt, B, N, D, K);
-    if (B < 1 || N < 1 || D < 1 || K < 1 || cfg.path != 0 || cfg.nsplit != 1) {
-        std::printf("the probe covers unsplit small-D plans of 2-byte inputs\n");
+    if (B < 1 || N < 1 || D < 1 || K < 1 || cfg.nsplit != 1) {
+        std::printf("the probe covers plans without a K split\n");
         return 2;
     }
     const int KT = assign_tiles(K);
@@ -64,24 +68,27 @@ int main(int argc, char **argv) {
         std::printf("the probe records at most %d workgroups (this shape has %ld)\n", FKM_STAMP_WGS, nwg);
         return 2;
     }
-    std::printf("shape B=%d N=%d D=%d K=%d %s: %ld workgroups of %d points, %d centroid tiles each\n", B, N, D, K,
-                f16 ? "f16" : "bf16", nwg, cfg.block_n, KT);
+    std::printf("shape B=%d N=%d D=%d K=%d %s, %s kernel: %ld workgroups of %d points, %d centroid tiles each\n", B, N,
+                D, K, dts.c_str(), cfg.path == 0 ? "small-D" : "split-D", nwg, cfg.block_n, KT);
     // points ~ N(0, 1) rounded to the dtype, centroids ~ N(0, 1) in fp32
     std::mt19937 rng(20260309);
     std::normal_distribution<float> nd(0.f, 1.f);
-    std::vector<uint16_t> hx((size_t)B * N * D);
-    for (auto &v : hx) v = f16 ? host_to_f16(nd(rng)) : host_to_bf16(nd(rng));
+    std::vector<uint16_t> hx(dt == DT_F32 ? 0 : (size_t)B * N * D);
+    std::vector<float> hxf(dt == DT_F32 ? (size_t)B * N * D : 0);
+    for (auto &v : hx) v = dt == DT_F16 ? host_to_f16(nd(rng)) : host_to_bf16(nd(rng));
+    for (auto &v : hxf) v = nd(rng);
     std::vector<float> hc((size_t)B * K * D);
     for (auto &v : hc) v = nd(rng);
     void *x, *cprep;
     float *C, *cnh;
     int32_t *a;
     double *wgi;
-    CK(hipMalloc(&x, hx.size() * 2));
-    CK(hipMemcpy(x, hx.data(), hx.size() * 2, hipMemcpyHostToDevice));
+    CK(hipMalloc(&x, (size_t)B * N * D * es));
+    if (dt == DT_F32) CK(hipMemcpy(x, hxf.data(), hxf.size() * 4, hipMemcpyHostToDevice));
+    else CK(hipMemcpy(x, hx.data(), hx.size() * 2, hipMemcpyHostToDevice));
     CK(hipMalloc(&C, hc.size() * 4));
     CK(hipMemcpy(C, hc.data(), hc.size() * 4, hipMemcpyHostToDevice));
-    CK(hipMalloc(&cprep, (size_t)B * KT * 32 * cfg.d_pad * 2));
+    CK(hipMalloc(&cprep, (size_t)B * KT * 32 * cfg.d_pad * es));
     CK(hipMalloc(&cnh, (size_t)B * KT * 32 * 4));
     CK(hipMalloc(&a, (size_t)B * N * 4));
     CK(hipMalloc(&wgi, (size_t)B * wpb * ASSIGN_WAVES * 8));  // per-wave inertia partials
@@ -92,7 +99,7 @@ int main(int argc, char **argv) {
     // the launches of the fit's form (point norms from registers, inertia partials); about 40 ms of
     // load first so that the clocks have settled, then the recorded launch
     float ms = 0.f;
-    const long reps = std::max(20L, (long)(4.0e13 / (2.0 * B * N * K * D) * 1.0));
+    const long reps = std::max(20L, (long)(0.04 * peak * 0.5 / (2.0 * B * N * (double)K * D)));
     for (long it = 0; it < reps; ++it) {
         CK(hipEventRecord(e0));
         CK(launch_assign(dt, cfg, x, cprep, cnh, nullptr, a, nullptr, wgi, B, N, D, K, 0, AssignSplit{}));
@@ -119,13 +126,13 @@ int main(int argc, char **argv) {
         dur.push_back(rt / 100.0);
     }
     const double flop = 2.0 * B * N * (double)K * D;
-    std::printf("recorded launch: %.1f us, %.1f%% of 2.5 PFLOP/s (%ld launches of load before it)\n", ms * 1e3,
-                flop / (ms * 1e-3) / 2.5e15 * 100.0, reps - 1);
+    std::printf("recorded launch: %.1f us, %.1f%% of the %s MFMA peak %.1f TFLOP/s (%ld launches of load before it)\n",
+                ms * 1e3, flop / (ms * 1e-3) / peak * 100.0, dts.c_str(), peak / 1e12, reps - 1);
     const double mhz = pct(clk, 0.5);
     std::printf("shader clock during the workgroups: median %.0f MHz (p10 %.0f, p90 %.0f); at the median the\n"
-                "  MFMA peak is %.2f PFLOP/s and the launch runs at %.1f%% of it\n",
-                mhz, pct(clk, 0.1), pct(clk, 0.9), 2.5 * mhz / 2400.0,
-                flop / (ms * 1e-3) / (2.5e15 * mhz / 2400.0) * 100.0);
+                "  MFMA peak is %.1f TFLOP/s and the launch runs at %.1f%% of it\n",
+                mhz, pct(clk, 0.1), pct(clk, 0.9), peak * mhz / 2400.0 / 1e12,
+                flop / (ms * 1e-3) / (peak * mhz / 2400.0) * 100.0);
     std::printf("workgroup duration: p50 %.2f us (min %.2f, max %.2f); span of the stamps %.1f us\n", pct(dur, 0.5),
                 pct(dur, 0.0), pct(dur, 1.0), (r1 - r0) / 100.0);
     std::printf("shader cycles per workgroup (p10 / p50 / p90):\n");
@@ -137,8 +144,10 @@ int main(int argc, char **argv) {
                 pct(scan, 0.1), pct(scan, 0.5), pct(scan, 0.9), pct(scan, 0.5) / KT);
     std::printf("  after the scan                       %8.0f %8.0f %8.0f\n", pct(epi, 0.1), pct(epi, 0.5),
                 pct(epi, 0.9));
-    const int mf = cfg.pb * (cfg.d_pad / 16);  // 32x32x16 MFMAs per tile and wave
-    std::printf("  (a tile's MFMA work per wave: %d MFMAs of 32 cycles = %d cycles; three waves per SIMD: %d)\n",
-                mf, mf * 32, 3 * mf * 32);
+    if (cfg.path == 0 && dt != DT_F32) {
+        const int mf = cfg.pb * (cfg.d_pad / 16);  // 32x32x16 MFMAs per tile and wave
+        std::printf("  (a tile's MFMA work per wave: %d MFMAs of 32 cycles = %d cycles; three waves per SIMD: %d)\n",
+                    mf, mf * 32, 3 * mf * 32);
+    }
     return 0;
 }
