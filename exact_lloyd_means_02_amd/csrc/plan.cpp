@@ -29,8 +29,10 @@
 //     far as it can (at most 8): shorter shares also shorten the tail of the last round.
 // Assign, split-D path (D above the register budget, README "Large-D and dtype support"):
 //   * point block of 128 (4 waves x 32), 4 centroid tiles (128 centroids) of accumulators per
-//     wave, D streamed through LDS in chunks of 64 (2-byte) / 32 (fp32) elements so one stage
-//     of x chunk + centroid chunk is 32 KiB, double buffered.
+//     wave, D streamed through LDS in chunks of 32 (2-byte) / 16 (fp32) elements so one stage
+//     of x chunk + centroid chunk is 16 KiB, double buffered: 32 KiB of LDS and at most 168
+//     registers, so three waves share a SIMD (chunks twice as wide held 64 KiB and 178 registers,
+//     two waves per SIMD, and ran 2% slower at D = 1024 fp32).
 // Arg-sort: counting passes over digits of the cluster id; one pass when the per-problem
 //   table (bins x tiles of 4096 keys) stays <= 2^24 entries and bins <= 1024 (LDS of a scatter
 //   workgroup: 8 waves x bins 16-bit counters, 2 x bins offsets, the 32 KiB staged tile); otherwise

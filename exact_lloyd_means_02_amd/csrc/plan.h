@@ -95,7 +95,7 @@ constexpr int small_d_tps(int dt, int dp) {
     return dp * (dt == 0 ? 4 : 2) >= 512 ? 1 : (dp * (dt == 0 ? 4 : 2) >= 64 ? 2 : 4);
 }
 constexpr int SMALL_D_STAGES = 3;
-constexpr int splitd_bd(int dt) { return dt == 0 ? 32 : 64; }
+constexpr int splitd_bd(int dt) { return dt == 0 ? 16 : 32; }
 
 // 32-centroid tiles per problem in the prepared layout: padded to a multiple of 4 so the
 // assign kernels can stream whole stages of 2 or 4 tiles (padding tiles score +inf).

@@ -205,7 +205,7 @@ def test_plan_headline_values(fk):
     assert (p["path"], p["d_pad"], p["point_blocks"], p["block_n"]) == (0, 128, 2, 256)
     assert (p["sort_bits"], p["sort_passes"]) == (10, 1)
     s = fk.kmeans_plan(0, 1, 262144, 1024, 512)      # split-D fp32
-    assert s["path"] == 1 and s["block_d"] == 32
+    assert s["path"] == 1 and s["block_d"] == 16    # 16 fp32 dimensions per LDS chunk
     c5 = fk.kmeans_plan(1, 1, 1 << 24, 64, 32768)    # one streamed chunk: two counting passes
     assert c5["sort_passes"] == 2
 
