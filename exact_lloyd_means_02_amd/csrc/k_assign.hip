@@ -36,7 +36,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // defines FKM_CLOCK_STAMPS); compiled out of the library.  Thread 0 of workgroup w writes
 // fkm_stamps[w]: [0] start, [1] scan start (point tile and first stages in; split-D: the first
 // chunk pair in), [2] scan end, [3] end (shader clock, s_memtime), [4] start and [5] end (the
-// 100 MHz real-time counter).
+// 100 MHz real-time counter), [6] the HW_ID hardware register at the start (which CU of the XCD,
+// SIMD and wave slot thread 0 runs on).
 #ifdef FKM_CLOCK_STAMPS
 constexpr int FKM_STAMP_WGS = 1 << 14;
 __device__ unsigned long long fkm_stamps[FKM_STAMP_WGS][8];
@@ -50,12 +51,21 @@ __device__ unsigned long long fkm_stamps[FKM_STAMP_WGS][8];
         if (threadIdx.x == 0 && blockIdx.x < (unsigned)FKM_STAMP_WGS)                     \
             fkm_stamps[blockIdx.x][i] = __builtin_amdgcn_s_memrealtime();                  \
     } while (0)
+// hwreg(HW_REG_HW_ID = 4, offset 0, 32 bits)
+#define FKM_HWSTAMP(i)                                                                    \
+    do {                                                                                  \
+        if (threadIdx.x == 0 && blockIdx.x < (unsigned)FKM_STAMP_WGS)                     \
+            fkm_stamps[blockIdx.x][i] = (unsigned)__builtin_amdgcn_s_getreg(4 | (31 << 11)); \
+    } while (0)
 #else
 #define FKM_STAMP(i) \
     do {             \
     } while (0)
 #define FKM_RSTAMP(i) \
     do {              \
+    } while (0)
+#define FKM_HWSTAMP(i) \
+    do {               \
     } while (0)
 #endif
 
@@ -369,6 +379,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     __shared__ __attribute__((aligned(16))) float s_n0[TPS * 32], s_n1[TPS * 32], s_n2[TPS * 32];
 
     FKM_RSTAMP(4);
+    FKM_HWSTAMP(6);
     FKM_STAMP(0);
     // consecutive logical workgroups (one XCD) take the K ranges of a point tile, then the next tile
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
@@ -518,10 +529,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
         u32x4 *xst = (w < 2 ? s_c1 : s_c2) + (w & 1) * (XBLK / 16);
         auto x_copy = [&](int p) {
             const int row0 = pbase + p * 32;
-            const int nrows = max(0, min(32, N - row0));
-            // the block's rows only: rows past N are outside the buffer and read as zeros
+            // the block's rows only: rows past N are outside the buffer and read as zeros.  The
+            // clamp compiles to a vector instruction; read back into a scalar register, the
+            // descriptor stays scalar (else every copy below becomes a loop over lane values)
+            const int nbytes = __builtin_amdgcn_readfirstlane(max(0, min(32, N - row0)) * D * S);
             const __amdgpu_buffer_rsrc_t rx =
-                buffer_rsrc((const char *)x + ((size_t)b * N + min(row0, N)) * D * S, nrows * D * S);
+                buffer_rsrc((const char *)x + ((size_t)b * N + min(row0, N)) * D * S, nbytes);
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 const int b0 = i * 1024 + lane * 16;
@@ -686,6 +699,7 @@ __global__ __launch_bounds__(256) void assign_split_d_kernel(const void *__restr
     __shared__ u32x4 s_c[2][CU4];
 
     FKM_RSTAMP(4);
+    FKM_HWSTAMP(6);
     FKM_STAMP(0);
     const int QG = DP / (2 * VW);
     const int NC = DP / BD;

@@ -6,7 +6,9 @@
 //     scan (per 32-centroid tile too), and from the scan's end to the workgroup's end, split into the
 //     workgroups of the first round (started in the launch's first 2 us) and the later ones;
 //   * the launch time and its fraction of the nominal MFMA peak of the dtype (2.5 PFLOP/s bf16/fp16,
-//     157.3 TFLOP/s fp32), and of that peak at the measured clock.
+//     157.3 TFLOP/s fp32), and of that peak at the measured clock;
+//   * per CU, the share of time with 0..3 of its workgroups resident and in their scan, and the gaps
+//     between successive workgroup starts on a CU.
 // A measuring tool, not part of the library; built by build.py beside libflashkm.so and run by
 // `bench.py --clock-probe`.  Usage: probe_assign_clock [B N D K [dtype: bf16|f16|f32]]
 #define FKM_CLOCK_STAMPS 1
@@ -144,6 +146,63 @@ int main(int argc, char **argv) {
                 pct(scan, 0.1), pct(scan, 0.5), pct(scan, 0.9), pct(scan, 0.5) / KT);
     std::printf("  after the scan                       %8.0f %8.0f %8.0f\n", pct(epi, 0.1), pct(epi, 0.5),
                 pct(epi, 0.9));
+    // Per CU: how many of its resident workgroups are in their scan at each instant.  A workgroup's CU
+    // is its XCD (workgroups go to the XCDs round-robin, so blockIdx mod 8) with the SE, SH and CU
+    // fields of HW_ID; shader-clock stamps are put on the real-time axis by each workgroup's own
+    // start/end pair.  Measured from the launch's first start to its last start (before the drain).
+    {
+        struct Ev { double t; int res, scan; };
+        std::vector<std::vector<Ev>> ev(8 * 256);
+        double t_last_start = 0;
+        for (long w = 0; w < nwg; ++w) {
+            const unsigned long long *t = &s[w * 8];
+            if (t[5] <= t[4] || t[3] <= t[0]) continue;
+            const unsigned hw = (unsigned)t[6];
+            const int key = (int)(w % 8) * 256 + (int)((hw >> 8) & 0xFFu);
+            const double a = (double)(t[4] - r0), rt = (double)(t[5] - t[4]), mt = (double)(t[3] - t[0]);
+            const double s1 = a + (double)(t[1] - t[0]) / mt * rt, s2 = a + (double)(t[2] - t[0]) / mt * rt;
+            ev[key].push_back({a, +1, 0});
+            ev[key].push_back({s1, 0, +1});
+            ev[key].push_back({s2, 0, -1});
+            ev[key].push_back({a + rt, -1, 0});
+            t_last_start = std::max(t_last_start, a);
+        }
+        double busy[5] = {0, 0, 0, 0, 0}, resw[5] = {0, 0, 0, 0, 0}, total = 0;
+        int cus = 0;
+        std::vector<double> gaps;
+        for (auto &e : ev) {
+            if (e.empty()) continue;
+            ++cus;
+            std::sort(e.begin(), e.end(), [](const Ev &x, const Ev &y) { return x.t < y.t; });
+            int res = 0, sc = 0;
+            double prev = 0, last_start = -1;
+            for (const Ev &x : e) {
+                const double t1 = std::min(x.t, t_last_start);
+                if (t1 > prev) {
+                    busy[std::min(sc, 4)] += t1 - prev;
+                    resw[std::min(res, 4)] += t1 - prev;
+                    total += t1 - prev;
+                }
+                prev = std::max(prev, t1);
+                if (x.res > 0) {
+                    if (last_start >= 0) gaps.push_back((x.t - last_start) / 100.0);
+                    last_start = x.t;
+                }
+                res += x.res;
+                sc += x.scan;
+            }
+        }
+        std::printf("per CU (%d CUs seen), time from the first start to the last start:\n", cus);
+        std::printf("  workgroups resident:  0: %4.1f%%  1: %4.1f%%  2: %4.1f%%  3: %4.1f%%  4+: %4.1f%%\n",
+                    100 * resw[0] / total, 100 * resw[1] / total, 100 * resw[2] / total, 100 * resw[3] / total,
+                    100 * resw[4] / total);
+        std::printf("  workgroups scanning:  0: %4.1f%%  1: %4.1f%%  2: %4.1f%%  3: %4.1f%%  4+: %4.1f%%\n",
+                    100 * busy[0] / total, 100 * busy[1] / total, 100 * busy[2] / total, 100 * busy[3] / total,
+                    100 * busy[4] / total);
+        std::printf("  gap between successive workgroup starts on a CU (us): p10 %.2f p25 %.2f p50 %.2f p75 %.2f "
+                    "p90 %.2f\n",
+                    pct(gaps, 0.1), pct(gaps, 0.25), pct(gaps, 0.5), pct(gaps, 0.75), pct(gaps, 0.9));
+    }
     if (cfg.path == 0 && dt != DT_F32) {
         const int mf = cfg.pb * (cfg.d_pad / 16);  // 32x32x16 MFMAs per tile and wave
         std::printf("  (a tile's MFMA work per wave: %d MFMAs of 32 cycles = %d cycles; three waves per SIMD: %d)\n",
