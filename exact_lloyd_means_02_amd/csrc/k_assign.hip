@@ -258,6 +258,16 @@ __device__ inline void argmin_fold(ArgminState &s, const f32x16 &acc, int tile) 
     s.best = __builtin_bit_cast(f32x16, bb);
 }
 
+// The value held by lane l ^ 32 (the lane of the same point that holds the other 16 rows of
+// each tile).  v_permlane32_swap trades lanes 32-63 of its first operand with lanes 0-31 of its
+// second; with both operands v, the second result holds the upper half's values in lanes 0-31
+// and the first the lower half's in lanes 32-63.  A VALU exchange, no LDS round trip.
+__device__ inline uint32_t partner32(uint32_t v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (threadIdx.x & 32) ? r[0] : r[1];
+}
+__device__ inline float partner32(float v) { return __uint_as_float(partner32(__float_as_uint(v))); }
+
 // Resolve the winning centroid of this lane and merge with the partner lane (lane ^ 32, same
 // point, the other 16 rows of every tile): the point's least (half) score and its lowest index.
 // Accumulator r of lane (j, h) holds row 8*(r/4) + 4*h + (r%4) of the 32-centroid tile (MFMA
@@ -268,8 +278,8 @@ __device__ inline void argmin_resolve(const ArgminState &s, int h, float &sc, in
     for (int r = 15; r >= 0; --r) slot = (s.best[r] == s.run_min) ? r : slot;
     k = s.run_tile * 32 + 8 * (slot >> 2) + 4 * h + (slot & 3);
     sc = s.run_min;
-    const float osc = __shfl_xor(sc, 32);
-    const int ok = __shfl_xor(k, 32);
+    const float osc = partner32(sc);
+    const int ok = (int)partner32((uint32_t)k);
     if (osc < sc || (osc == sc && ok < k)) {
         sc = osc;
         k = ok;
@@ -308,14 +318,35 @@ __device__ inline float argmin_finish(const ArgminState &s, int h, bool write, i
     return d;
 }
 
-// Sum of the wave's point distances in fp64, fixed order (a butterfly over the lanes); lane 0
-// writes it to dst[wave] (dst: the workgroup's ASSIGN_WAVES partials).  No workgroup barrier, so a
-// wave that finishes its scan early leaves without waiting for the others.  Feeds the
-// per-iteration inertia without a pass over min_dist.
+// A double moved across lanes by the DPP pattern CTRL (both 32-bit halves alike).
+template <int CTRL>
+__device__ inline double dpp_f64(double v) {
+    const unsigned long long b = __builtin_bit_cast(unsigned long long, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+__device__ inline double readlane_f64(double v, int l) {
+    const unsigned long long b = __builtin_bit_cast(unsigned long long, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+    return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+
+// Sum of the wave's point distances in fp64, fixed order; lane 0 writes it to dst[wave] (dst:
+// the workgroup's ASSIGN_WAVES partials).  Within each row of 16 lanes the partner of a step is
+// fixed by a DPP pattern (lane ^ 1, lane ^ 2, the other quad of the half-row, the other half of
+// the row), so every lane of a row ends with the row's sum; the four row sums are then added in
+// row order.  No LDS traffic and no workgroup barrier: a wave that finishes its scan early
+// leaves without waiting for the others.  Feeds the per-iteration inertia without a pass over
+// min_dist.
 __device__ inline void wave_inertia(double v, double *dst) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    if ((threadIdx.x & 63) == 0) dst[threadIdx.x >> 6] = v;
+    v += dpp_f64<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+    v += dpp_f64<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+    v += dpp_f64<0x141>(v);  // row_half_mirror
+    v += dpp_f64<0x140>(v);  // row_mirror
+    const double t = ((readlane_f64(v, 0) + readlane_f64(v, 16)) + readlane_f64(v, 32)) + readlane_f64(v, 48);
+    if ((threadIdx.x & 63) == 0) dst[threadIdx.x >> 6] = t;
 }
 
 // s_waitcnt immediate that waits until at most n vector-memory loads are outstanding and all
@@ -619,7 +650,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
                     for (int e = 0; e < 4; ++e) own = dot2_self<DT>(xr[p][q][e], own);
                 }
             }
-            own += __shfl_xor(own, 32);
+            own += partner32(own);
         }
         if (split) {
             float sc;
