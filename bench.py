@@ -63,7 +63,7 @@ def parse():
     p.add_argument("--stage-reps-first", type=int, default=40,
                    help="repetitions of the first stage pass (about 30 ms of load: the clocks settle in it)")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
-    p.add_argument("--clock-probe", nargs="*", metavar="B N D K [f16]",
+    p.add_argument("--clock-probe", nargs="*", metavar="B N D K [dtype [extra LDS]]",
                    help="run the FlashAssign phase probe (clock stamps per workgroup; headline shape by default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calib", action="store_true", help="run a plain 1 GiB device copy and exit")

@@ -10,7 +10,9 @@
 //   * per CU, the share of time with 0..3 of its workgroups resident and in their scan, and the gaps
 //     between successive workgroup starts on a CU.
 // A measuring tool, not part of the library; built by build.py beside libflashkm.so and run by
-// `bench.py --clock-probe`.  Usage: probe_assign_clock [B N D K [dtype: bf16|f16|f32]]
+// `bench.py --clock-probe`.  Usage: probe_assign_clock [B N D K [dtype: bf16|f16|f32 [extra LDS]]]
+// `extra LDS` (bytes of dynamic LDS per workgroup, 2-byte types at padded D = 128 only) lowers the
+// number of workgroups that share a CU: with 20000 two fit, with 40000 one (one wave per SIMD).
 #define FKM_CLOCK_STAMPS 1
 #include "k_assign.hip"
 
@@ -55,6 +57,7 @@ int main(int argc, char **argv) {
     const int B = argc > 4 ? std::atoi(argv[1]) : 32, N = argc > 4 ? std::atoi(argv[2]) : 65536;
     const int D = argc > 4 ? std::atoi(argv[3]) : 128, K = argc > 4 ? std::atoi(argv[4]) : 1024;
     const std::string dts = argc > 5 ? std::string(argv[5]) : std::string("bf16");
+    const int dyn = argc > 6 ? std::atoi(argv[6]) : 0;
     const int dt = dts == "f16" ? DT_F16 : (dts == "f32" ? DT_F32 : DT_BF16);
     const int es = dt == DT_F32 ? 4 : 2;
     const double peak = dt == DT_F32 ? 157.3e12 : 2.5e15;
@@ -63,6 +66,12 @@ int main(int argc, char **argv) {
         std::printf("the probe covers plans without a K split\n");
         return 2;
     }
+    if (dyn != 0 && (dyn < 0 || dyn > 100000 || dt == DT_F32 || cfg.path != 0 || cfg.d_pad != 128)) {
+        std::printf("extra LDS: 0 .. 100000 bytes, 2-byte types at padded D = 128 only\n");
+        return 2;
+    }
+    auto kern = dt == DT_F16 ? assign_small_d_kernel<DT_F16, 128> : assign_small_d_kernel<DT_BF16, 128>;
+    if (dyn > 0) CK(hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, dyn));
     const int KT = assign_tiles(K);
     const int wpb = (N + cfg.block_n - 1) / cfg.block_n;
     const long nwg = (long)B * wpb;
@@ -72,6 +81,7 @@ int main(int argc, char **argv) {
     }
     std::printf("shape B=%d N=%d D=%d K=%d %s, %s kernel: %ld workgroups of %d points, %d centroid tiles each\n", B, N,
                 D, K, dts.c_str(), cfg.path == 0 ? "small-D" : "split-D", nwg, cfg.block_n, KT);
+    if (dyn > 0) std::printf("extra dynamic LDS per workgroup: %d bytes\n", dyn);
     // points ~ N(0, 1) rounded to the dtype, centroids ~ N(0, 1) in fp32
     std::mt19937 rng(20260309);
     std::normal_distribution<float> nd(0.f, 1.f);
@@ -104,7 +114,13 @@ int main(int argc, char **argv) {
     const long reps = std::max(20L, (long)(0.04 * peak * 0.5 / (2.0 * B * N * (double)K * D)));
     for (long it = 0; it < reps; ++it) {
         CK(hipEventRecord(e0));
-        CK(launch_assign(dt, cfg, x, cprep, cnh, nullptr, a, nullptr, wgi, B, N, D, K, 0, AssignSplit{}));
+        if (dyn == 0) {
+            CK(launch_assign(dt, cfg, x, cprep, cnh, nullptr, a, nullptr, wgi, B, N, D, K, 0, AssignSplit{}));
+        } else {  // the same launch as launch_assign's, with the extra LDS
+            kern<<<dim3(B * wpb), dim3(256), dyn, 0>>>(x, (const u32x4 *)cprep, cnh, nullptr, a, nullptr, wgi, N, D,
+                                                       KT, wpb, 1, nullptr, nullptr);
+            CK(hipGetLastError());
+        }
         CK(hipEventRecord(e1));
         CK(hipEventSynchronize(e1));
         CK(hipEventElapsedTime(&ms, e0, e1));
