@@ -367,7 +367,7 @@ km_status_t kmeans_plan(km_dtype_t dt, int64_t B, int64_t N, int64_t D, int64_t 
     KM_TRY(check_ptr(out, "out"));
     const AssignCfg a = plan_assign(dt, B, N, D, K);
     const SortCfg so = plan_sort(N, K);
-    const UpdCfg u = plan_update(dt, B, N, D);
+    const UpdCfg u = plan_update(dt, B, N, D, K);
     out->path = a.path;
     out->d_pad = a.d_pad;
     out->point_blocks = a.pb;

@@ -721,13 +721,13 @@ __global__ __launch_bounds__(256) void upd_finalize_acc_kernel(UpdArgs a, int64_
 // Update memory: the arrival counters (zero between launches), the segments' first positions
 // and a scratch region for the partial records and shift partials.
 size_t update_ctr_bytes(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
-    const UpdCfg u = plan_update(dt, B, N, D);
+    const UpdCfg u = plan_update(dt, B, N, D, K);
     const int64_t chunks = B * u.nch;
     return align256((size_t)chunks * 2 * u.ncb * 4) + align256((size_t)B * K * u.ncb * 4);
 }
 
 size_t update_scratch_bytes(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
-    const UpdCfg u = plan_update(dt, B, N, D);
+    const UpdCfg u = plan_update(dt, B, N, D, K);
     const int64_t chunks = B * u.nch;
     (void)K;
     return align256((size_t)chunks * 2 * u.ncb * 8) + align256((size_t)chunks * 2 * D * 4);
@@ -769,7 +769,7 @@ static hipError_t launch_segsum_dt(const UpdArgs &a, int vec, int vpl, int64_t w
 static UpdArgs make_args(int dt, const void *x, const int32_t *sids, const int32_t *sidx, const int32_t *counts,
                          int B, int N, int D, int K, int mode, float *C, bool want_shift, float *sums, int32_t *cnt,
                          const UpdRefresh &ref, const UpdMem &mem) {
-    const UpdCfg u = plan_update(dt, B, N, D);
+    const UpdCfg u = plan_update(dt, B, N, D, K);
     const int64_t chunks = (int64_t)B * u.nch;
     char *wp = (char *)mem.scratch;
     UpdArgs a{};
@@ -805,7 +805,8 @@ static UpdArgs make_args(int dt, const void *x, const int32_t *sids, const int32
     return a;
 }
 
-bool update_refreshes_prep(int dt, int64_t B, int64_t N, int64_t D) { return plan_update(dt, B, N, D).ncb == 1; }
+// (the column blocks do not depend on K)
+bool update_refreshes_prep(int dt, int64_t B, int64_t N, int64_t D) { return plan_update(dt, B, N, D, 1).ncb == 1; }
 
 // Before an update whose caller has no first positions from the arg-sort: each cluster's first
 // sorted position (where the sorted id changes; clusters without points get none, and none is
@@ -890,7 +891,7 @@ hipError_t launch_update_prologue(const int32_t *sids, const int32_t *counts, in
 hipError_t launch_update(int dt, const void *x, const int32_t *sids, const int32_t *sidx, const int32_t *counts,
                          int B, int N, int D, int K, int mode, float *C, double *shift, float *sums, int32_t *cnt,
                          const UpdRefresh &ref, const UpdMem &mem, hipStream_t s, int normalize) {
-    const UpdCfg u = plan_update(dt, B, N, D);
+    const UpdCfg u = plan_update(dt, B, N, D, K);
     const int64_t chunks = (int64_t)B * u.nch;
     if (normalize && (mode != 0 || u.ncb != 1)) return hipErrorInvalidValue;
     UpdArgs a = make_args(dt, x, sids, sidx, counts, B, N, D, K, mode, C, shift != nullptr, sums, cnt,

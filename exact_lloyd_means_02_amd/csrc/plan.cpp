@@ -123,7 +123,7 @@ SortCfg plan_sort(int64_t N, int64_t K) {
     return c;
 }
 
-UpdCfg plan_update(int dt, int64_t B, int64_t N, int64_t D) {
+UpdCfg plan_update(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
     UpdCfg c{};
     const int s = dt == 0 ? 4 : 2;
     const int v16 = 16 / s;
@@ -135,11 +135,25 @@ UpdCfg plan_update(int dt, int64_t B, int64_t N, int64_t D) {
     c.vpl = (int)std::min<int64_t>(UPD_VPL_MAX, pow2_ceil(vpl_all));
     c.cb_elems = c.lanes * c.vpl * c.vec;
     c.ncb = (int)cdiv(D, c.cb_elems);
-    // ~8 resident waves per SIMD over the whole launch
-    const int64_t target_waves = (int64_t)Gfx950::cus * Gfx950::simds_per_cu * 8;
+    // About 4 waves per SIMD over the whole launch, which at the kernel's occupancy (6 waves per
+    // SIMD at 2-byte D = 128) runs in one round: fewer, longer chunks amortise each wave's start (its
+    // id window and the ids at its chunk edges) and its edge work.  Rounded to the nearest power of
+    // two.  Measured update times against the chunk length (MI355X): B=32 N=65536 K=1024, 101 us at
+    // 512 rows against 110 at 256 (8 waves per SIMD), 109 at 768 and 112 at 1024; B=32 N=75600
+    // K=1000, 125 us at 512 against 141 at 1024; one 2^24-point problem, K=64, 747 us at 4096 against
+    // 778 at 2048.
+    const int64_t target_waves = (int64_t)Gfx950::cus * Gfx950::simds_per_cu * 4;
     int64_t rows = (B * N) / std::max<int64_t>(1, target_waves / c.ncb);
     rows = std::max<int64_t>(64, std::min<int64_t>(4096, rows));
-    c.rows = pow2_ceil(rows);
+    int64_t p2 = pow2_ceil(rows);
+    if (p2 - rows > rows - p2 / 2) p2 /= 2;
+    // A chunk between a quarter of the mean segment (N / K) and twice it: the wave that owns a
+    // segment cut by its chunk's end walks on to the segment's end, up to a segment's length past
+    // its chunk, which unbalances the waves; such chunks are halved (one 2^24-point problem with
+    // K = 4096: 811 us at 2048 rows, 852 at 4096).
+    const int64_t mean_seg = N / std::max<int64_t>(1, K);
+    if (p2 > mean_seg / 4 && p2 <= 2 * mean_seg) p2 = std::max<int64_t>(64, p2 / 2);
+    c.rows = (int)p2;
     c.nch = cdiv(N, c.rows);
     return c;
 }

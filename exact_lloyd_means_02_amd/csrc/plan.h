@@ -82,7 +82,7 @@ struct UpdMem {
 
 AssignCfg plan_assign(int dt, int64_t B, int64_t N, int64_t D, int64_t K);
 SortCfg plan_sort(int64_t N, int64_t K);
-UpdCfg plan_update(int dt, int64_t B, int64_t N, int64_t D);
+UpdCfg plan_update(int dt, int64_t B, int64_t N, int64_t D, int64_t K);
 
 // Small-D register tile chosen for (dtype, padded D); shared with the kernel templates.
 constexpr int small_d_pb(int dt, int dp) { return dt == 0 ? (dp <= 32 ? 2 : 1) : (dp <= 128 ? 2 : 1); }

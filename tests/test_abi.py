@@ -158,8 +158,8 @@ def test_streamed_scratch_covers_the_last_chunk(fk, dt, D, K):
     from N = m c (all chunks full) to N = m c + r bounds what the r-point chunk may need beyond a
     full one: at least u(r) - u(c) - s(c) and s(r) - s(c) - u(c), with u the update's counters and
     scratch and s the arg-sort's tables (the two share the scratch region)."""
-    chunks = [1 << 14, 50000, 532480, 1 << 20, (1 << 24) - 4096, 1 << 24]
-    rests = [1, 100, 12345, 31072, 262144, 524288, 532479, (1 << 20) - 1]
+    chunks = [1 << 14, 50000, 532480, 786432, 1 << 20, (1 << 24) - 4096, 1 << 24]
+    rests = [1, 100, 12345, 31072, 262144, 524288, 532479, 782336, (1 << 20) - 1]
     checked = 0
     for c in chunks:
         for m in (1, 2):
@@ -174,10 +174,12 @@ def test_streamed_scratch_covers_the_last_chunk(fk, dt, D, K):
                 assert ws - full >= sr - sc - uc, (c, m, r, ws - full, sr - sc - uc)
                 checked += 1
     assert checked > 0
-    # the case that exposed it: 532480-point chunks, a last chunk of 2^19 points, D=128, K=64; the
-    # shorter chunk's update needs megabytes more than the full chunk's update and sort together
+    # a case where it matters: 786432-point chunks (192 points per wave slot, 256 rows per update
+    # chunk) and a last chunk of 782336 points (191 per slot, rounded to 128 rows: twice the
+    # chunks), D=128, K=64; the shorter chunk's update needs megabytes more than the full chunk's
+    # update and sort together
     if (dt, D, K) == (2, 128, 64):
-        c, r = 532480, 1 << 19
+        c, r = 786432, 782336
         assert _update_need(fk, dt, r, D, K) - _update_need(fk, dt, c, D, K) - _sort_need(fk, dt, c, D, K) > 1 << 20
 
 

@@ -125,17 +125,20 @@ def test_fit_streamed_matches_device(fk, chunk):
 
 
 def test_fit_streamed_ragged_last_chunk_needs_more_scratch(fk):
-    """532480-point chunks with a last chunk of 2^19 points: the update plan of the shorter chunk
-    has more partial records than a full chunk's (the streamed workspace covers both sizes).
-    One iteration (the centroids of the two runs then differ in fp32 summation order only): labels
-    must equal the device-resident run's, the inertia the oracle's."""
-    w = W.small("headline_bf16", B=1, N=532480 + (1 << 19), K=64, iters=1)
-    _say(f"case {w}, chunk_points 532480")
+    """786432-point chunks with a last chunk of 782336 points: the update plan of the shorter chunk
+    has twice the chunks, so more partial records, than a full chunk's (the streamed workspace
+    covers both sizes).  One iteration (the centroids of the two runs then differ in fp32 summation
+    order only): labels must equal the device-resident run's, the inertia the oracle's."""
+    c, r = 786432, 782336
+    assert fk.kmeans_plan(fk.DT_CODES["bf16"], 1, r, 128, 64)["upd_rows"] * 2 == \
+        fk.kmeans_plan(fk.DT_CODES["bf16"], 1, c, 128, 64)["upd_rows"]
+    w = W.small("headline_bf16", B=1, N=c + r, K=64, iters=1)
+    _say(f"case {w}, chunk_points {c}")
     x, x64, c0, xt, ct = make_inputs(w)
     xh = W.to_torch(x, w.dtype).pin_memory()
     c_dev, c_host = ct.clone(), ct.clone()
     a_dev, J_dev, _ = fk.kmeans_fit(xt, c_dev, w.iters, 0.0)
-    a_host, J_host, done = fk.kmeans_fit(xh, c_host, w.iters, 0.0, chunk_points=532480)
+    a_host, J_host, done = fk.kmeans_fit(xh, c_host, w.iters, 0.0, chunk_points=c)
     assert done == w.iters
     assert np.array_equal(a_host.cpu().numpy(), a_dev.cpu().numpy())
     assert np.allclose(J_host, J_dev, rtol=1e-5)
