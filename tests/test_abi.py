@@ -212,6 +212,21 @@ def test_plan_headline_values(fk):
     assert c5["sort_passes"] == 2
 
 
+def test_plan_update_rows(fk):
+    """The update's sorted positions per wave: about 4 waves per SIMD over the launch (1024 SIMDs),
+    to the nearest power of two, within 64..4096, halved when the chunk lies between a quarter of and
+    twice the mean segment length N/K."""
+    rows = lambda dt, B, N, D, K: fk.kmeans_plan(dt, B, N, D, K)["upd_rows"]
+    assert rows(2, 32, 65536, 128, 1024) == 512         # 2^21 / 4096 positions
+    assert rows(1, 32, 75600, 128, 1000) == 512         # 590.6 -> 512 (nearest power of two)
+    assert rows(2, 1, 1 << 24, 128, 64) == 4096         # mean segment 262144: no halving
+    assert rows(2, 1, 1 << 24, 128, 4096) == 2048       # mean segment 4096: 4096 halved
+    assert rows(0, 1, 262144, 1024, 512) == 64          # 64 (the floor)
+    assert rows(2, 1, 4096 * 255, 128, 64) == 256       # 255 -> 256
+    assert rows(2, 1, 4096 * 191, 128, 64) == 128       # 191 -> 128 (below three quarters of 256)
+    assert rows(2, 1, 1 << 30, 128, 2) == 4096          # the ceiling
+
+
 def test_workload_generators_are_seeded():
     w = W.small("headline_bf16", B=2, N=500, K=20)
     x1, c1, _ = W.make(w)
