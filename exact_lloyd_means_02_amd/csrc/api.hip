@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -191,6 +192,8 @@ FitLayout fit_layout(int dt, int64_t B, int64_t N, int64_t D, int64_t K, int met
     L.total = o;
     return L;
 }
+
+size_t fit_ws_bytes(int dt, int64_t B, int64_t N, int64_t D, int64_t K, int metric);
 
 struct HostLayout {
     size_t stage_buf[2], cprep, xn, part, a, sids, sidx, counts, offs, status, updctr, sums, cnt, shk, ring_j,
@@ -395,10 +398,10 @@ size_t kmeans_workspace_bytes(int op, km_dtype_t dt, int64_t B, int64_t N, int64
         case KM_OP_ASSIGN: return assign_ws(dt, B, N, D, K);
         case KM_OP_ARGSORT: return argsort_ws(B, N, K);
         case KM_OP_UPDATE: return update_ws(dt, B, N, D, K);
-        case KM_OP_FIT: return fit_layout(dt, B, N, D, K).total;
+        case KM_OP_FIT: return fit_ws_bytes(dt, B, N, D, K, KM_METRIC_L2);
         case KM_OP_FIT_HOST: return host_layout(dt, B, N, D, K, chunk_points).total;
-        case KM_OP_FIT_DOT: return fit_layout(dt, B, N, D, K, KM_METRIC_DOT).total;
-        case KM_OP_FIT_COSINE: return fit_layout(dt, B, N, D, K, KM_METRIC_COSINE).total;
+        case KM_OP_FIT_DOT: return fit_ws_bytes(dt, B, N, D, K, KM_METRIC_DOT);
+        case KM_OP_FIT_COSINE: return fit_ws_bytes(dt, B, N, D, K, KM_METRIC_COSINE);
         default: g_err = "unknown workspace op"; return 0;
     }
 }
@@ -637,109 +640,275 @@ km_status_t read_shift_max(const double *dev, int64_t B, double *out, hipStream_
     return ok();
 }
 
+// One chain of the device fit: a contiguous range of the problems with its own workspace layout
+// and stream.
+struct FitChain {
+    int64_t B = 0, b0 = 0;
+    hipStream_t s = nullptr;
+    FitLayout L{};
+    char *ws = nullptr;
+    AssignCfg cfg{};
+    int64_t wpb = 0;
+    const void *xa = nullptr;
+    float *C = nullptr, *xn = nullptr, *cnh = nullptr;
+    const float *xn_in = nullptr;
+    int32_t *a = nullptr, *sids = nullptr, *sidx = nullptr, *counts = nullptr, *status = nullptr;
+    char *cprep = nullptr;
+    double *ring_part = nullptr, *ring_j = nullptr, *ring_s = nullptr;
+    void *scratch = nullptr;
+    UpdMem mem;
+    AssignSplit sp;
+    bool fused_prep = false;
+    UpdRefresh full_ref{}, ref{};
+    int32_t st_host = 0;
+    std::vector<double> j_host;  // two chains: this chain's inertia rows, read at a flush
+};
+
+// Two half-batch chains (see fit_device) where the iterations stop at `iters` (tol = 0), the batch
+// has at least two problems, and each half runs the small-D assign without a K split (its grid
+// fills the chip).
+bool fit_two_chains(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
+    if (B < 2) return false;
+    for (const int64_t bh : {B / 2, B - B / 2}) {
+        const AssignCfg c = plan_assign(dt, bh, N, D, K);
+        if (c.path != 0 || c.nsplit != 1) return false;
+    }
+    return true;
+}
+
+// The device fit's workspace: one chain's layout, or, where two chains may run, the larger of that
+// and the two halves' layouts one after the other.
+size_t fit_ws_bytes(int dt, int64_t B, int64_t N, int64_t D, int64_t K, int metric) {
+    size_t t = fit_layout(dt, B, N, D, K, metric).total;
+    if (fit_two_chains(dt, B, N, D, K)) {
+        const size_t t2 = fit_layout(dt, B / 2, N, D, K, metric).total + fit_layout(dt, B - B / 2, N, D, K, metric).total;
+        t = t2 > t ? t2 : t;
+    }
+    return t;
+}
+
+// A chain's pointers, and its setup on its stream (point norms or unit rows, prepared centroids,
+// zeroed counters).
+km_status_t fit_chain_setup(FitChain &c, int dt, const void *x, int64_t B_all, int64_t N, int64_t D, int64_t K,
+                            float *C, int32_t *assign, int metric) {
+    const bool simm = metric != KM_METRIC_L2;
+    const bool cosine = metric == KM_METRIC_COSINE;
+    const int64_t B = c.B;
+    const FitLayout &L = c.L;
+    char *ws = c.ws;
+    c.cfg = plan_assign(dt, B, N, D, K);
+    const int64_t KT = assign_tiles(K);
+    c.wpb = assign_wgs_per_problem(dt, B, N, D, K) * ASSIGN_WAVES;  // inertia partials per problem
+    c.C = C + c.b0 * K * D;
+    c.xn = (float *)(ws + L.xn);
+    c.a = assign ? assign + c.b0 * N : (int32_t *)(ws + L.a);
+    c.sids = (int32_t *)(ws + L.sids);
+    c.sidx = (int32_t *)(ws + L.sidx);
+    c.counts = (int32_t *)(ws + L.counts);
+    c.status = (int32_t *)(ws + L.status);
+    c.cprep = ws + L.prep;
+    c.cnh = (float *)(c.cprep + align256((size_t)B * KT * 32 * c.cfg.d_pad * elem_bytes(dt)));
+    c.ring_part = (double *)(ws + L.ring_part);
+    c.ring_j = (double *)(ws + L.ring_j);
+    c.ring_s = (double *)(ws + L.ring_s);
+    c.scratch = ws + L.scratch;
+    c.mem.offs = (const int32_t *)(ws + L.offs);
+    c.mem.ctr = (int32_t *)(ws + L.updctr);
+    c.mem.scratch = c.scratch;
+    c.mem.plan_B = B_all;  // each problem's update chunked as in a launch over the whole batch
+    c.sp = split_at(dt, B, N, D, K, ws + L.split);
+    c.fused_prep = update_refreshes_prep(dt, B, N, D);
+    c.full_ref = UpdRefresh{c.cprep, c.cnh, c.cfg.d_pad, (int)KT, simm ? 1 : 0};
+    c.ref = c.fused_prep ? c.full_ref : UpdRefresh{};
+    const hipStream_t s = c.s;
+    const void *xc = (const char *)x + (size_t)c.b0 * N * D * elem_bytes(dt);
+    // the points the iterations use: x, or its unit rows for cosine k-means (whose centroids
+    // are made unit rows too, in place)
+    c.xa = xc;
+    if (cosine) {
+        KM_HIP(launch_normalize_rows(dt, xc, ws + L.xhat, B * N, (int)D, s));
+        KM_HIP(launch_normalize_rows(KM_F32, c.C, c.C, B * K, (int)D, s));
+        c.xa = ws + L.xhat;
+    }
+    // the small-D assign kernel computes the point norms it needs from its own registers; the
+    // split-D kernel reads them.  The similarity metrics take zeros instead.
+    c.xn_in = simm ? c.xn : (c.cfg.path == 0 ? nullptr : c.xn);
+    if (simm) KM_HIP(launch_fill_i32((int32_t *)c.xn, B * N, 0, s));
+    else if (c.xn_in) KM_HIP(launch_row_norms(dt, xc, c.xn, B * N, (int)D, s));
+    KM_HIP(launch_prep_centroids(dt, c.C, c.cprep, c.cnh, (int)B, (int)K, (int)D, c.cfg.d_pad, s, simm ? 1 : 0));
+    // the update's arrival counters start at zero and the split assign's keys at all ones; every
+    // update and every split finish leave them so
+    KM_HIP(launch_fill_i32(c.mem.ctr, (int64_t)(update_ctr_bytes(dt, B, N, D, K) / 4), 0, s));
+    if (c.sp.nsplit > 1) KM_HIP(launch_fill_i32((int32_t *)c.sp.packed, 2 * B * N, -1, s));
+    return ok();
+}
+
+// One Lloyd iteration of a chain after its assign: arg-sort (+ counts and the clusters' first
+// positions), update (+ shift, + the next iteration's prepared centroids).
+km_status_t fit_chain_rest(FitChain &c, int dt, int64_t N, int64_t D, int64_t K, float tol, int slot, bool more,
+                           int metric) {
+    const bool simm = metric != KM_METRIC_L2;
+    const bool cosine = metric == KM_METRIC_COSINE;
+    const int64_t B = c.B;
+    const hipStream_t s = c.s;
+    KM_HIP(launch_argsort(c.a, (int)B, (int)N, (int)K, c.sids, c.sidx, c.counts, (int32_t *)c.mem.offs, c.status,
+                          c.scratch, s));
+    double *shift = tol > 0.f ? c.ring_s + (size_t)slot * B : nullptr;
+    if (cosine && c.fused_prep) {
+        // one column block per row: the update finishes each cluster in place with the mean
+        // direction s_k / ||s_k|| (and the shift and the refresh), like the Euclidean finish
+        KM_HIP(launch_update(dt, c.xa, c.sids, c.sidx, c.counts, (int)B, (int)N, (int)D, (int)K, 0, c.C, shift,
+                             nullptr, nullptr, c.full_ref, c.mem, s, 1));
+    } else if (cosine) {
+        // sums and counts per cluster, then the mean direction (with shift and refresh)
+        float *sums = (float *)(c.ws + c.L.sums);
+        int32_t *cnt = (int32_t *)(c.ws + c.L.cnt);
+        KM_HIP(launch_fill_i32((int32_t *)sums, B * K * D, 0, s));
+        KM_HIP(launch_fill_i32(cnt, B * K, 0, s));
+        KM_HIP(launch_update(dt, c.xa, c.sids, c.sidx, c.counts, (int)B, (int)N, (int)D, (int)K, 1, nullptr, nullptr,
+                             sums, cnt, UpdRefresh{}, c.mem, s));
+        KM_HIP(launch_finalize_acc(dt, sums, cnt, c.C, shift, (double *)(c.ws + c.L.shk), c.full_ref, (int)B,
+                                   (int)K, (int)D, s, 1));
+    } else {
+        KM_HIP(launch_update(dt, c.xa, c.sids, c.sidx, c.counts, (int)B, (int)N, (int)D, (int)K, 0, c.C, shift,
+                             nullptr, nullptr, c.ref, c.mem, s));
+        if (!c.fused_prep && more)
+            KM_HIP(launch_prep_centroids(dt, c.C, c.cprep, c.cnh, (int)B, (int)K, (int)D, c.cfg.d_pad, s,
+                                         simm ? 1 : 0));
+    }
+    return ok();
+}
+
+// The second chain's stream: created once per device and kept until the process ends, so that its
+// hardware queue stays the same from call to call (a stream made per call can land on the queue of
+// the caller's stream, and the chains then run one after the other).  Fits that run at the same
+// time on one device share it: their second chains queue behind each other, each still waiting
+// only for its own events.
+std::mutex g_chain_mu;
+hipStream_t g_chain_stream[64] = {};
+
+km_status_t chain_stream(hipStream_t *out) {
+    int dev = 0;
+    KM_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= 64) return fail(KM_ERR_UNSUPPORTED, "device index %d beyond 64", dev);
+    std::lock_guard<std::mutex> lock(g_chain_mu);
+    if (!g_chain_stream[dev]) KM_HIP(hipStreamCreateWithFlags(&g_chain_stream[dev], hipStreamNonBlocking));
+    *out = g_chain_stream[dev];
+    return ok();
+}
+
+struct ChainSync {
+    hipStream_t s2 = nullptr;
+    hipEvent_t after_assign[2] = {nullptr, nullptr};
+    hipEvent_t done2 = nullptr;
+    ~ChainSync() {
+        for (auto &e : after_assign)
+            if (e) (void)hipEventDestroy(e);
+        if (done2) (void)hipEventDestroy(done2);
+    }
+};
+
 // metric: KM_METRIC_L2 (Lloyd), KM_METRIC_DOT (similarity x.c, mean update) or KM_METRIC_COSINE
 // (unit rows, mean-direction update).  For the similarity metrics the assign kernels get zero
 // norm terms (scores -x.c~) and zero point norms, so their per-point "distance" is
 // -2 x.c~ and the per-iteration value returned is -1/2 of its sum: the total similarity.
+//
+// The iterations of different problems are independent, so where fit_two_chains holds the batch
+// runs as two half-batch chains: the first on the caller's stream, the second on the library's
+// stream for the device (chain_stream), with three events of this call.  Their FlashAssign launches alternate (each waits for the other chain's previous one) and
+// never overlap, while each chain's arg-sort and update run beside the other chain's FlashAssign:
+// MFMA-bound and memory-bound work share the chip.  Per problem every kernel does the work of the
+// one-chain fit (the updates are planned for the whole batch), so the results are bit-identical.
 km_status_t fit_device(int dt, const void *x, int64_t B, int64_t N, int64_t D, int64_t K, int iters, float tol,
                        float *C, int32_t *assign, double *inertia, int32_t *iters_done, char *ws, hipStream_t s,
                        int metric = KM_METRIC_L2) {
-    const FitLayout L = fit_layout(dt, B, N, D, K, metric);
     const bool simm = metric != KM_METRIC_L2;
-    const bool cosine = metric == KM_METRIC_COSINE;
-    const AssignCfg cfg = plan_assign(dt, B, N, D, K);
-    const int64_t KT = assign_tiles(K);
-    const int64_t wpb = assign_wgs_per_problem(dt, B, N, D, K) * ASSIGN_WAVES;  // inertia partials per problem
-    float *xn = (float *)(ws + L.xn);
-    int32_t *a = assign ? assign : (int32_t *)(ws + L.a);
-    int32_t *sids = (int32_t *)(ws + L.sids);
-    int32_t *sidx = (int32_t *)(ws + L.sidx);
-    int32_t *counts = (int32_t *)(ws + L.counts);
-    int32_t *status = (int32_t *)(ws + L.status);
-    char *cprep = ws + L.prep;
-    float *cnh = (float *)(cprep + align256((size_t)B * KT * 32 * cfg.d_pad * elem_bytes(dt)));
-    double *ring_part = (double *)(ws + L.ring_part);
-    double *ring_j = (double *)(ws + L.ring_j);
-    double *ring_s = (double *)(ws + L.ring_s);
-    void *scratch = ws + L.scratch;
-    UpdMem mem;
-    mem.offs = (const int32_t *)(ws + L.offs);
-    mem.ctr = (int32_t *)(ws + L.updctr);
-    mem.scratch = scratch;
-    const AssignSplit sp = split_at(dt, B, N, D, K, ws + L.split);
-    const bool fused_prep = update_refreshes_prep(dt, B, N, D);
-    const UpdRefresh full_ref{cprep, cnh, cfg.d_pad, (int)KT, simm ? 1 : 0};
-    const UpdRefresh ref = fused_prep ? full_ref : UpdRefresh{};
-
-    // the points the iterations use: x, or its unit rows for cosine k-means (whose centroids
-    // are made unit rows too, in place)
-    const void *xa = x;
-    if (cosine) {
-        KM_HIP(launch_normalize_rows(dt, x, ws + L.xhat, B * N, (int)D, s));
-        KM_HIP(launch_normalize_rows(KM_F32, C, C, B * K, (int)D, s));
-        xa = ws + L.xhat;
+    const int nch = (tol <= 0.f && fit_two_chains(dt, B, N, D, K)) ? 2 : 1;
+    FitChain ch[2];
+    ChainSync sync;
+    if (nch == 1) {
+        ch[0].B = B;
+        ch[0].L = fit_layout(dt, B, N, D, K, metric);
+        ch[0].ws = ws;
+        ch[0].s = s;
+    } else {
+        ch[0].B = B / 2;
+        ch[1].B = B - B / 2;
+        ch[1].b0 = B / 2;
+        ch[0].L = fit_layout(dt, ch[0].B, N, D, K, metric);
+        ch[1].L = fit_layout(dt, ch[1].B, N, D, K, metric);
+        ch[0].ws = ws;
+        ch[1].ws = ws + ch[0].L.total;
+        ch[0].s = s;
+        KM_TRY(chain_stream(&sync.s2));
+        for (auto &e : sync.after_assign) KM_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+        KM_HIP(hipEventCreateWithFlags(&sync.done2, hipEventDisableTiming));
+        ch[1].s = sync.s2;
+        // the second chain starts after the caller's earlier work on its stream
+        KM_HIP(hipEventRecord(sync.done2, s));
+        KM_HIP(hipStreamWaitEvent(sync.s2, sync.done2, 0));
     }
-    // the small-D assign kernel computes the point norms it needs from its own registers; the
-    // split-D kernel reads them.  The similarity metrics take zeros instead.
-    const float *xn_in = simm ? xn : (cfg.path == 0 ? nullptr : xn);
-    if (simm) KM_HIP(launch_fill_i32((int32_t *)xn, B * N, 0, s));
-    else if (xn_in) KM_HIP(launch_row_norms(dt, x, xn, B * N, (int)D, s));
-    KM_HIP(launch_prep_centroids(dt, C, cprep, cnh, (int)B, (int)K, (int)D, cfg.d_pad, s, simm ? 1 : 0));
-    // the update's arrival counters start at zero and the split assign's keys at all ones; every
-    // update and every split finish leave them so
-    KM_HIP(launch_fill_i32(mem.ctr, (int64_t)(update_ctr_bytes(dt, B, N, D, K) / 4), 0, s));
-    if (sp.nsplit > 1) KM_HIP(launch_fill_i32((int32_t *)sp.packed, 2 * B * N, -1, s));
+    for (int h = 0; h < nch; ++h) KM_TRY(fit_chain_setup(ch[h], dt, x, B, N, D, K, C, assign, metric));
     int done = 0, flushed = 0;
-    int32_t st_host = 0;
     for (int t = 0; t < iters; ++t) {
         const int slot = t - flushed;
-        // one iteration: assign (+ per-wave inertia partials), arg-sort (+ counts and the
-        // clusters' first positions), update (+ shift, + the next iteration's prepared centroids)
-        KM_HIP(launch_assign(dt, cfg, xa, cprep, cnh, xn_in, a, nullptr, ring_part + (size_t)slot * B * wpb, (int)B,
-                             (int)N, (int)D, (int)K, s, sp));
-        KM_HIP(launch_argsort(a, (int)B, (int)N, (int)K, sids, sidx, counts, (int32_t *)mem.offs, status, scratch, s));
-        if (cosine && fused_prep) {
-            // one column block per row: the update finishes each cluster in place with the mean
-            // direction s_k / ||s_k|| (and the shift and the refresh), like the Euclidean finish
-            KM_HIP(launch_update(dt, xa, sids, sidx, counts, (int)B, (int)N, (int)D, (int)K, 0, C,
-                                 tol > 0.f ? ring_s + (size_t)slot * B : nullptr, nullptr, nullptr, full_ref, mem,
-                                 s, 1));
-        } else if (cosine) {
-            // sums and counts per cluster, then the mean direction (with shift and refresh)
-            float *sums = (float *)(ws + L.sums);
-            int32_t *cnt = (int32_t *)(ws + L.cnt);
-            KM_HIP(launch_fill_i32((int32_t *)sums, B * K * D, 0, s));
-            KM_HIP(launch_fill_i32(cnt, B * K, 0, s));
-            KM_HIP(launch_update(dt, xa, sids, sidx, counts, (int)B, (int)N, (int)D, (int)K, 1, nullptr, nullptr,
-                                 sums, cnt, UpdRefresh{}, mem, s));
-            KM_HIP(launch_finalize_acc(dt, sums, cnt, C, tol > 0.f ? ring_s + (size_t)slot * B : nullptr,
-                                       (double *)(ws + L.shk), full_ref, (int)B, (int)K, (int)D, s, 1));
-        } else {
-            KM_HIP(launch_update(dt, xa, sids, sidx, counts, (int)B, (int)N, (int)D, (int)K, 0, C,
-                                 tol > 0.f ? ring_s + (size_t)slot * B : nullptr, nullptr, nullptr, ref, mem, s));
-            if (!fused_prep && t + 1 < iters)
-                KM_HIP(launch_prep_centroids(dt, C, cprep, cnh, (int)B, (int)K, (int)D, cfg.d_pad, s, simm ? 1 : 0));
+        const bool more = t + 1 < iters;
+        for (int h = 0; h < nch; ++h) {
+            FitChain &c = ch[h];
+            // two chains: this FlashAssign after the other chain's latest one
+            if (nch == 2 && (h == 1 || t > 0)) KM_HIP(hipStreamWaitEvent(c.s, sync.after_assign[1 - h], 0));
+            KM_HIP(launch_assign(dt, c.cfg, c.xa, c.cprep, c.cnh, c.xn_in, c.a, nullptr,
+                                 c.ring_part + (size_t)slot * c.B * c.wpb, (int)c.B, (int)N, (int)D, (int)K, c.s,
+                                 c.sp));
+            if (nch == 2) KM_HIP(hipEventRecord(sync.after_assign[h], c.s));
+            KM_TRY(fit_chain_rest(c, dt, N, D, K, tol, slot, more, metric));
         }
         done = t + 1;
         bool stop = false;
-        if (tol > 0.f) {
+        if (tol > 0.f) {  // one chain
             double smax = 0.0;
-            KM_TRY(read_shift_max(ring_s + (size_t)slot * B, B, &smax, s));
+            KM_TRY(read_shift_max(ch[0].ring_s + (size_t)slot * B, B, &smax, s));
             stop = smax < (double)tol;
         }
         if (slot + 1 == RING || stop || t + 1 == iters) {
             const bool last = stop || t + 1 == iters;
-            KM_HIP(launch_sum_f64_rows(ring_part, (slot + 1) * (int)B, wpb, ring_j, s));
-            KM_TRY(ring_to_host(ring_j, inertia, flushed, slot + 1, B, s, last ? status : nullptr, &st_host));
+            for (int h = 0; h < nch; ++h) {
+                FitChain &c = ch[h];
+                KM_HIP(launch_sum_f64_rows(c.ring_part, (slot + 1) * (int)c.B, c.wpb, c.ring_j, c.s));
+                if (last) KM_HIP(hipMemcpyAsync(&c.st_host, c.status, 4, hipMemcpyDeviceToHost, c.s));
+                if (inertia && nch == 1)
+                    KM_HIP(hipMemcpyAsync(inertia + (size_t)flushed * B, c.ring_j, (size_t)(slot + 1) * B * 8,
+                                          hipMemcpyDeviceToHost, c.s));
+                else if (inertia) {
+                    // each chain into a host buffer of its own: copies from the two streams into
+                    // interleaved columns of the caller's (pageable) rows are staged by the runtime
+                    // and can overwrite each other's columns
+                    c.j_host.resize((size_t)(slot + 1) * c.B);
+                    KM_HIP(hipMemcpyAsync(c.j_host.data(), c.ring_j, (size_t)(slot + 1) * c.B * 8,
+                                          hipMemcpyDeviceToHost, c.s));
+                }
+            }
+            for (int h = 0; h < nch; ++h) KM_HIP(hipStreamSynchronize(ch[h].s));
+            if (inertia && nch == 2)  // the chains' columns of the [iteration][problem] rows
+                for (int h = 0; h < nch; ++h)
+                    for (int i = 0; i <= slot; ++i)
+                        std::copy_n(ch[h].j_host.data() + (size_t)i * ch[h].B, ch[h].B,
+                                    inertia + (size_t)(flushed + i) * B + ch[h].b0);
             flushed = t + 1;
         }
         if (stop) break;
+    }
+    if (nch == 2) {  // the caller's stream waits for the second chain
+        KM_HIP(hipEventRecord(sync.done2, sync.s2));
+        KM_HIP(hipStreamWaitEvent(s, sync.done2, 0));
     }
     KM_HIP(hipStreamSynchronize(s));
     if (simm && inertia)
         for (int64_t i = 0; i < (int64_t)done * B; ++i) inertia[i] *= -0.5;
     if (iters_done) *iters_done = done;
-    return status_word(st_host, "the fit's arg-sort");
+    int32_t st = 0;
+    for (int h = 0; h < nch; ++h) st |= ch[h].st_host;
+    return status_word(st, "the fit's arg-sort");
 }
 
 struct StreamedPipe {
@@ -923,7 +1092,7 @@ extern "C" km_status_t kmeans_fit_metric(const void *x, km_dtype_t dt, km_metric
     KM_TRY(require_device(assign, "assign"));
     KM_TRY(require_device(ws, "ws"));
     if (xk == PTR_DEVICE) {
-        KM_TRY(check_ws(ws, ws_bytes, fit_layout(dt, B, N, D, K, (int)metric).total));
+        KM_TRY(check_ws(ws, ws_bytes, fit_ws_bytes(dt, B, N, D, K, (int)metric)));
         return fit_device(dt, x, B, N, D, K, iters, tol, centroids, assign, objective, iters_done, (char *)ws,
                           (hipStream_t)stream, (int)metric);
     }
@@ -956,7 +1125,7 @@ extern "C" km_status_t kmeans_fit(const void *x, km_dtype_t dt, int64_t B, int64
     KM_TRY(require_device(ws, "ws"));
     hipStream_t s = (hipStream_t)stream;
     if (xk == PTR_DEVICE) {
-        KM_TRY(check_ws(ws, ws_bytes, fit_layout(dt, B, N, D, K).total));
+        KM_TRY(check_ws(ws, ws_bytes, fit_ws_bytes(dt, B, N, D, K, KM_METRIC_L2)));
         return fit_device(dt, x, B, N, D, K, iters, tol, centroids, assign, inertia, iters_done, (char *)ws, s);
     }
     KM_TRY(check_ws(ws, ws_bytes, host_layout(dt, B, N, D, K, chunk_points).total));

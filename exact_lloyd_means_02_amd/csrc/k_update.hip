@@ -769,7 +769,7 @@ static hipError_t launch_segsum_dt(const UpdArgs &a, int vec, int vpl, int64_t w
 static UpdArgs make_args(int dt, const void *x, const int32_t *sids, const int32_t *sidx, const int32_t *counts,
                          int B, int N, int D, int K, int mode, float *C, bool want_shift, float *sums, int32_t *cnt,
                          const UpdRefresh &ref, const UpdMem &mem) {
-    const UpdCfg u = plan_update(dt, B, N, D, K);
+    const UpdCfg u = plan_update(dt, mem.plan_B > B ? mem.plan_B : B, N, D, K);
     const int64_t chunks = (int64_t)B * u.nch;
     char *wp = (char *)mem.scratch;
     UpdArgs a{};
@@ -891,7 +891,7 @@ hipError_t launch_update_prologue(const int32_t *sids, const int32_t *counts, in
 hipError_t launch_update(int dt, const void *x, const int32_t *sids, const int32_t *sidx, const int32_t *counts,
                          int B, int N, int D, int K, int mode, float *C, double *shift, float *sums, int32_t *cnt,
                          const UpdRefresh &ref, const UpdMem &mem, hipStream_t s, int normalize) {
-    const UpdCfg u = plan_update(dt, B, N, D, K);
+    const UpdCfg u = plan_update(dt, mem.plan_B > B ? mem.plan_B : B, N, D, K);
     const int64_t chunks = (int64_t)B * u.nch;
     if (normalize && (mode != 0 || u.ncb != 1)) return hipErrorInvalidValue;
     UpdArgs a = make_args(dt, x, sids, sidx, counts, B, N, D, K, mode, C, shift != nullptr, sums, cnt,

@@ -78,6 +78,11 @@ struct UpdMem {
     const int32_t *offs = nullptr;
     int32_t *ctr = nullptr;
     void *scratch = nullptr;
+    // the batch size the update's chunk plan is made for (0: the launch's own); a launch over part
+    // of a batch then chunks (and adds) each problem as the whole batch's launch would.  At least
+    // the launch's problem count, so the chunks are no shorter and the counters and scratch sized
+    // for the launch suffice.
+    int64_t plan_B = 0;
 };
 
 AssignCfg plan_assign(int dt, int64_t B, int64_t N, int64_t D, int64_t K);

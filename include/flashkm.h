@@ -262,7 +262,12 @@ km_status_t kmeans_update(const void *x, km_dtype_t dt, const int32_t *sorted_id
  *   iters_done   host int32 out or NULL
  * Returns after the work has finished (it synchronises `stream`).  The
  * streamed path creates one copy stream and four events for the call and
- * destroys them before it returns.
+ * destroys them before it returns.  With device x, tol = 0 and a batch whose
+ * halves each fill the GPU, the fit runs the two halves as two chains (their
+ * assignments alternating, each half's arg-sort and update running beside
+ * the other half's assignment; the results are bit-identical to one chain):
+ * the second half on a stream the library creates once per device and keeps
+ * until the process ends, with three events created for the call.
  */
 km_status_t kmeans_fit(const void *x, km_dtype_t dt, int64_t B, int64_t N, int64_t D, int64_t K,
                        int32_t iters, float tol, int64_t chunk_points, float *centroids,

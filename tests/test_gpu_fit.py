@@ -99,6 +99,28 @@ def test_fit_inertia_across_device_ring_flushes(fk):
     assert (np.abs(Jr - J) / J).max() <= INERTIA_TOL
 
 
+@pytest.mark.parametrize("B", [3, 4])
+def test_fit_two_chains(fk, B):
+    """With tol = 0, a batch whose halves each fill the chip runs as two half-batch chains on two
+    streams (their FlashAssign launches alternating); tol > 0 runs one chain.  The two-chain fit
+    against the oracle's Lloyd loop by the parity protocol, and against the one-chain fit: per
+    problem the same work in the same order, so labels, centroids and inertia are bit-identical.
+    B = 3 splits unevenly (1 + 2 problems)."""
+    w = W.small("headline_bf16", B=B, N=1 << 18, K=256, iters=3)
+    for bh in (B // 2, B - B // 2):   # each half fills the chip without a K split
+        assert fk.kmeans_plan(fk.DT_CODES[w.dtype], bh, w.N, w.D, w.K)["assign_splits"] == 1
+    _say(f"case {w}")
+    x, x64, c0, xt, ct = make_inputs(w)
+    check_fit(fk, w, x, c0, xt, ct, say=_say)
+    c2, c1 = ct.clone(), ct.clone()
+    a2, J2, d2 = fk.kmeans_fit(xt, c2, w.iters, 0.0)
+    a1, J1, d1 = fk.kmeans_fit(xt, c1, w.iters, 1e-30)
+    assert d1 == d2 == w.iters
+    assert np.array_equal(J1, J2)
+    assert np.array_equal(a1.cpu().numpy(), a2.cpu().numpy())
+    assert np.array_equal(c1.cpu().numpy(), c2.cpu().numpy())
+
+
 def test_fit_tol_stops_early(fk):
     w = W.small("tiny_f32", iters=50)
     x, x64, c0, xt, ct = make_inputs(w)
