@@ -16,12 +16,17 @@ Order of the run:
      settling after 20-40 ms of load; see the design notes).  This pass (about 30 ms) takes that
      load, and its numbers show it; a timed fit after 10 repetitions instead ran 2-3% slower per
      iteration than the same fit repeated right after it.
-  2. `--warmup` untimed iterations as one fit;
-  3. the timed region: exactly `--steps` iterations as one kmeans_fit call, bracketed by device
+  2. `--settle-iters` (60) untimed iterations as one fit, about 35 ms of the timed workload's own
+     load.  Where the fit runs the batch as two half-batch chains (FlashAssign of one half beside
+     the arg-sort and update of the other), its mix of MFMA and memory work settles the clocks at
+     another point than the stage calls do: right after the first pass, the first timed fit ran
+     2-4% slower per iteration than the fits after it, for 30-40 ms.
+  3. `--warmup` untimed iterations as one fit;
+  4. the timed region: exactly `--steps` iterations as one kmeans_fit call, bracketed by device
      synchronisations; `value` = its wall time / steps.  `--repeat` more timed fits follow and are
      reported beside it (not in `value`).
-  4. per-stage timings, second pass ("stages_ms", the roofline and update figures).
-  5. the oracle on a bounded sample on the host (cpu_baseline).
+  5. per-stage timings, second pass ("stages_ms", the roofline and update figures).
+  6. the oracle on a bounded sample on the host (cpu_baseline).
 
 Prints one JSON line.  Other modes: `--copy-calib` (a plain device copy of known size, the
 reference for scaling the FETCH_SIZE / WRITE_SIZE counters), `--summarize-trace CSV` (the
@@ -60,6 +65,8 @@ def parse():
     p.add_argument("--repeat", type=int, default=2, help="further timed fits reported beside `value`")
     p.add_argument("--workload", default="headline_bf16")
     p.add_argument("--stage-reps", type=int, default=10, help="repetitions of the second stage pass")
+    p.add_argument("--settle-iters", type=int, default=60,
+                   help="untimed fit iterations before the warmup (the clocks settle under the fit's own load)")
     p.add_argument("--stage-reps-first", type=int, default=40,
                    help="repetitions of the first stage pass (about 30 ms of load: the clocks settle in it)")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
@@ -421,15 +428,24 @@ def plan_regret():
 # ------------------------------------------------------------------------------------------------
 COUNTER_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc %s --output-format csv -d <out>/%s -o run -- "
                "python3 /root/repo/bench.py %s")
-BENCH_ARGS_COUNTERS = "--steps 1 --warmup 1 --stage-reps-first 2 --stage-reps 2 --repeat 0 --no-cpu-baseline"
+BENCH_ARGS_COUNTERS = "--steps 1 --warmup 1 --settle-iters 0 --stage-reps-first 2 --stage-reps 2 --repeat 0 --no-cpu-baseline"
 
 
 def _counter_means(path):
-    """{kernel name: {counter: mean value per dispatch}} from a rocprofv3 counter_collection CSV."""
+    """{kernel name: {counter: mean value per dispatch}} from a rocprofv3 counter_collection CSV,
+    over each kernel's dispatches of its largest grid: the whole-batch launches of the stage calls
+    (a fit that runs two half-batch chains launches the same kernels over half the problems)."""
     import csv
-    per = {}
+    per, grid = {}, {}
     for r in csv.DictReader(open(path)):
-        key = (r["Kernel_Name"], r["Counter_Name"])
+        g = int(r.get("Grid_Size", 0) or 0)
+        k = r["Kernel_Name"]
+        if g < grid.get(k, 0):
+            continue
+        if g > grid.get(k, 0):
+            grid[k] = g
+            per = {key: v for key, v in per.items() if key[0] != k}
+        key = (k, r["Counter_Name"])
         per.setdefault(key, {}).setdefault(r["Dispatch_Id"], 0.0)
         per[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
     out = {}
@@ -537,8 +553,9 @@ KERNEL_TAGS = [("assign_small_d", "assign"), ("assign_split_d", "assign"), ("sor
 def summarize_trace(path, args):
     """Per-iteration summary of a `rocprofv3 --kernel-trace` CSV of this script: the FlashAssign
     launches of the per-stage timings (the launches `roofline` averages) and the timed fit's
-    iterations (kernel time, span from the first kernel's start to the last one's end, and the
-    idle gap before each iteration)."""
+    iterations.  A fit that runs two half-batch chains has two hardware queues; an iteration runs
+    from one FlashAssign launch of the first chain to its next, and its kernel times add both
+    chains' kernels (which overlap, so they may exceed the iteration's span)."""
     import csv
     import numpy as np
     rows = list(csv.DictReader(open(path)))
@@ -549,7 +566,8 @@ def summarize_trace(path, args):
             if k in n:
                 return t
         return n[:24]
-    seq = [(tag(r["Kernel_Name"]), int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows]
+    seq = [(tag(r["Kernel_Name"]), int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r.get("Queue_Id", "0"))
+           for r in rows]
     names = [s[0] for s in seq]
     # stage calls: row norms, prep, assign, in two passes of 1 + R triples (the first triple of a
     # pass is its untimed priming call); `roofline` averages the second pass
@@ -558,27 +576,40 @@ def summarize_trace(path, args):
     R1, R = args.stage_reps_first, args.stage_reps
     first_pass = triples[1:1 + R1]
     stage_assign = triples[2 + R1:2 + R1 + R] if len(triples) >= 2 + R1 + R else first_pass
-    # fits: prep, fill, then iterations (each from an assign to the next one) until the next
-    # prep or row-norm kernel (another fit or stage call); the fit's inertia sums and copies to
-    # the host are not counted in an iteration's kernels
+    # fits: each chain starts with prep then fill on its queue (two chains: two such starts within
+    # a millisecond); a fit's kernels run to the next fit or stage call (prep or row norms).  Its
+    # inertia sums, fills and copies to the host are not counted in the iterations.
+    starts = []
+    for i in range(len(seq)):
+        if names[i] != "prep":
+            continue
+        nxt = next((j for j in range(i + 1, len(seq)) if seq[j][3] == seq[i][3]), None)
+        if nxt is not None and names[nxt] == "fill":
+            if starts and seq[i][1] - seq[starts[-1]][1] < 1000000:
+                continue  # the second chain's start of the same fit
+            starts.append(i)
     fits = []
-    i = 0
-    while i < len(seq) - 1:
-        if names[i] == "prep" and names[i + 1] == "fill":
-            its, j, cur = [], i + 2, []
-            while j < len(seq) and names[j] not in ("prep", "rownorm"):
-                if names[j] == "assign" and cur:
-                    its.append(cur)
-                    cur = []
-                if names[j] not in ("sumrows", "fill", "copy"):
-                    cur.append(seq[j])
-                j += 1
-            if cur:
+    for fi, i in enumerate(starts):
+        end = starts[fi + 1] if fi + 1 < len(starts) else len(seq)
+        ks = []
+        for j in range(i, end):
+            if names[j] == "rownorm" or (names[j] == "prep" and j > i + 4 and not ks == []
+                                         and names[j - 1] not in ("fill", "prep")):
+                break
+            if names[j] not in ("sumrows", "fill", "copy", "prep"):
+                ks.append(seq[j])
+        if not ks:
+            continue
+        q0 = next(k[3] for k in ks if k[0] == "assign")
+        its, cur = [], []
+        for k in ks:
+            if k[0] == "assign" and k[3] == q0 and cur:
                 its.append(cur)
-            fits.append(its)
-            i = j
-        else:
-            i += 1
+                cur = []
+            cur.append(k)
+        if cur:
+            its.append(cur)
+        fits.append((its, len(set(k[3] for k in ks))))
     lines = ["# rocprofv3 kernel trace summary (bench.py --summarize-trace)", "source: %s" % os.path.basename(path)]
     lines.append("FlashAssign launches of the first stage pass: %d, mean %.2f us" % (
         len(first_pass), np.mean(first_pass)))
@@ -588,32 +619,30 @@ def summarize_trace(path, args):
     flops = 2.0 * 32 * 65536 * 1024 * 128
     lines.append("  2*B*N*K*D / mean / 2.5 PFLOP/s = %.4f (headline shape)" % (flops / (np.mean(stage_assign) * 1e-6)
                                                                               / 2.5e15))
-    lines.append("fits found: %d (iterations: %s)" % (len(fits), [len(f) for f in fits]))
-    if len(fits) >= 2:
-        timed = fits[1]
-        lines.append("timed fit (the second fit): %d iterations" % len(timed))
-        lines.append("  it  assign   hist  scatter  segsum | kernels   span   gap-before (us)")
-        prev_end = None
-        tot_k, tot_span, tot_gap = 0.0, 0.0, 0.0
+    lines.append("fits found: %d (iterations: %s; chains: %s)" % (
+        len(fits), [len(f[0]) for f in fits], [f[1] for f in fits]))
+    ti = (1 if getattr(args, "settle_iters", 0) > 0 else 0) + (1 if args.warmup > 0 else 0)
+    if len(fits) > ti:
+        timed, nchains = fits[ti]
+        lines.append("timed fit (fit %d): %d iterations, %d chain(s)" % (ti + 1, len(timed), nchains))
+        lines.append("  it  assign   hist  scatter  segsum | kernels   span (us)")
+        tot_k, tot_span = 0.0, 0.0
         per = {}
         for t, it in enumerate(timed):
             d = {}
-            for n, s0, e0 in it:
+            for n, s0, e0, _ in it:
                 d[n] = d.get(n, 0.0) + (e0 - s0) / 1e3
                 per.setdefault(n, []).append((e0 - s0) / 1e3)
             k = sum(d.values())
-            span = (it[-1][2] - it[0][1]) / 1e3
-            gap = (it[0][1] - prev_end) / 1e3 if prev_end is not None else 0.0
-            prev_end = it[-1][2]
+            end = timed[t + 1][0][1] if t + 1 < len(timed) else max(e0 for _, _, e0, _ in it)
+            span = (end - it[0][1]) / 1e3
             tot_k += k
             tot_span += span
-            tot_gap += gap if t > 0 else 0.0
-            lines.append("  %2d %7.1f %6.1f %7.1f %7.1f | %7.1f %7.1f %7.1f" % (
-                t, d.get("assign", 0), d.get("hist", 0), d.get("scatter", 0), d.get("segsum", 0), k, span, gap))
+            lines.append("  %2d %7.1f %6.1f %7.1f %7.1f | %7.1f %7.1f" % (
+                t, d.get("assign", 0), d.get("hist", 0), d.get("scatter", 0), d.get("segsum", 0), k, span))
         n = len(timed)
-        lines.append("  per iteration: kernels %.1f us, span %.1f us, gaps between iterations %.2f us" % (
-            tot_k / n, tot_span / n, tot_gap / max(1, n - 1)))
-        lines.append("  per kernel mean: " + ", ".join("%s %.1f" % (k, np.mean(v)) for k, v in per.items()))
+        lines.append("  per iteration: kernels %.1f us (both chains added), span %.1f us" % (tot_k / n, tot_span / n))
+        lines.append("  per kernel launch mean: " + ", ".join("%s %.1f" % (k, np.mean(v)) for k, v in per.items()))
     print("\n".join(lines))
 
 
@@ -806,12 +835,16 @@ def main():
     # ---- 1. per-stage times, first pass (HIP events on the stages' stream), teacher forced from c0
     st_first, _ = stage_times(fk, w, xt, c0t, args.stage_reps_first, args.metric, stream)
 
-    # ---- 2. warmup (untimed): W iterations
+    # ---- 2. settle (untimed): the fit's own load for about 35 ms
+    if args.settle_iters > 0:
+        fit(args.settle_iters)
+        c.copy_(c0t)
+    # ---- 3. warmup (untimed): W iterations
     if args.warmup > 0:
         fit(args.warmup)
     torch.cuda.synchronize()
 
-    # ---- 3. timed: exactly `steps` iterations in one fit (then `repeat` more, reported apart)
+    # ---- 4. timed: exactly `steps` iterations in one fit (then `repeat` more, reported apart)
     runs = []
     for r in range(1 + max(0, args.repeat)):
         c.copy_(c0t)
@@ -823,12 +856,16 @@ def main():
         assert done == args.steps
         runs.append((t1 - t0) * 1e3 / args.steps)
         if r == 0:
-            inertia_first = inertia
+            inertia_first = inertia.copy()
+            # every squared distance is positive on these inputs; a zero is a value never written
+            assert args.metric != "l2" or bool(np.all(inertia > 0)), "fit returned a non-positive inertia"
+        else:  # the same start, the same fixed-order sums: the same values to the bit
+            assert np.array_equal(inertia, inertia_first), "repeat fit's inertia differs from the first"
     ms_per_step = runs[0]
     print("bench: %d iterations in %.3f ms (repeats: %s ms per iteration)" % (
         args.steps, ms_per_step * args.steps, ["%.4f" % v for v in runs[1:]]), file=sys.stderr, flush=True)
 
-    # ---- 4. per-stage times, second pass
+    # ---- 5. per-stage times, second pass
     st, assign_launches = stage_times(fk, w, xt, c0t, args.stage_reps, args.metric, stream)
 
     flops, abytes, ubytes = algorithmic(w)
