@@ -481,7 +481,8 @@ def summarize_counters(root):
     lines = ["# HBM traffic per dispatch and FlashAssign MFMA counters: headline workload "
              "(B=32, N=65536, D=128, K=1024, bf16)", "",
              "Each counter set is its own run (the commands below; `<out>` = a scratch directory).  Values are",
-             "per dispatch, averaged over the dispatches of each kernel.", ""]
+             "per dispatch, averaged over each kernel's dispatches of its largest grid: the whole-batch stage",
+             "calls (the fit's half-batch launches, which share the chip with the other half, are left out).", ""]
     for c, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
         lines.append("    " + COUNTER_CMD % (c, sub, BENCH_ARGS_COUNTERS))
     for c, sub in (("FETCH_SIZE", "cfetch"), ("WRITE_SIZE", "cwrite")):
