@@ -554,7 +554,8 @@ KERNEL_TAGS = [("assign_small_d", "assign"), ("assign_split_d", "assign"), ("sor
 def summarize_trace(path, args):
     """Per-iteration summary of a `rocprofv3 --kernel-trace` CSV of this script: the FlashAssign
     launches of the per-stage timings (the launches `roofline` averages) and the timed fit's
-    iterations.  A fit that runs two half-batch chains has two hardware queues; an iteration runs
+    iterations.  A fit that runs two half-batch chains has two hardware queues (the FlashAssign
+    launches of both chains on one, their arg-sorts and updates on the other); an iteration runs
     from one FlashAssign launch of the first chain to its next, and its kernel times add both
     chains' kernels (which overlap, so they may exceed the iteration's span)."""
     import csv
@@ -601,16 +602,24 @@ def summarize_trace(path, args):
                 ks.append(seq[j])
         if not ks:
             continue
+        # chains: the prep launches before the first FlashAssign; an iteration has one FlashAssign
+        # per chain, on one queue or on one queue per chain
+        first_a = next(j for j in range(i, end) if names[j] == "assign")
+        nch = max(1, sum(1 for j in range(i, first_a) if names[j] == "prep"))
+        qa = set(k[3] for k in ks if k[0] == "assign")
+        per_it = max(1, nch // len(qa))
         q0 = next(k[3] for k in ks if k[0] == "assign")
-        its, cur = [], []
+        its, cur, na = [], [], 0
         for k in ks:
-            if k[0] == "assign" and k[3] == q0 and cur:
-                its.append(cur)
-                cur = []
+            if k[0] == "assign" and k[3] == q0:
+                if cur and na % per_it == 0:
+                    its.append(cur)
+                    cur = []
+                na += 1
             cur.append(k)
         if cur:
             its.append(cur)
-        fits.append((its, len(set(k[3] for k in ks))))
+        fits.append((its, nch))
     lines = ["# rocprofv3 kernel trace summary (bench.py --summarize-trace)", "source: %s" % os.path.basename(path)]
     lines.append("FlashAssign launches of the first stage pass: %d, mean %.2f us" % (
         len(first_pass), np.mean(first_pass)))
@@ -876,6 +885,17 @@ def main():
     upd_ms = st["argsort"] + st["update"]
     upd_gbs = ubytes / (upd_ms * 1e-3) / 1e9
 
+    # the assign's bound: the MFMA floor (flops / peak) or the HBM floor (algorithmic bytes / peak
+    # bandwidth), whichever is longer; K below about 300 makes it HBM-bound
+    if abytes / (PEAK_HBM_GBS * 1e9) > flops / (peak * 1e12):
+        assign_gbs = abytes / (assign_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(assign_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(assign_gbs / PEAK_HBM_GBS, 4),
+                "mfma": {"achieved": round(assign_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                         "frac": round(assign_tflops / peak, 4)}}
+    else:
+        roof = {"bound": "mfma", "achieved": round(assign_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(assign_tflops / peak, 4)}
     headline = w.name == "headline_bf16" and args.metric == "l2"
     out = {
         "metric": METRIC if headline else "ms per %s k-means iteration (%s)" % (
@@ -894,13 +914,13 @@ def main():
         "config": {"workload": w.name, "B": w.B, "N": w.N, "D": w.D, "K": w.K, "iters": args.steps, "tol": 0.0,
                    "inputs": "HBM-resident", "metric": args.metric},
         "repeat_ms_per_step": [round(v, 4) for v in runs[1:]],
-        "roofline": {"bound": "mfma", "achieved": round(assign_tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(assign_tflops / peak, 4), "traffic": measured_traffic(w.name),
+        "roofline": dict(roof, **{
+                     "traffic": measured_traffic(w.name),
                      "kernel": "FlashAssign (%s) kernel, one launch per kmeans_assign_prepared call" % (
                          "small-D" if fk.kmeans_plan(fk.dtype_code(xt), w.B, w.N, w.D, w.K)["path"] == 0 else "split-D"),
                      "kernel_ms": round(assign_ms, 4), "kernel_ms_median": round(st["assign"], 4),
                      "launches": len(assign_launches), "flop_per_launch": flops,
-                     "algorithmic_bytes_per_launch": abytes},
+                     "algorithmic_bytes_per_launch": abytes}),
         "stages_ms": {k: round(v, 4) for k, v in st.items()},
         "stages_ms_first": {k: round(v, 4) for k, v in st_first.items()},
         "update": {"bound": "hbm", "achieved": round(upd_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -243,26 +243,46 @@ hipError_t launch_normalize_rows(int dt, const void *x, void *out, int64_t rows,
 // Deterministic fp64 sums of partials, one row per workgroup in a fixed order.
 // ------------------------------------------------------------------------------------------
 // out[r] = sum_j part[r * len + j] (fp64), one workgroup per row, fixed order; with accumulate,
-// out[r] += that sum.
-__global__ __launch_bounds__(256) void sum_f64_rows_kernel(const double *__restrict__ part, int64_t len,
-                                                           double *__restrict__ out, int accumulate) {
-    __shared__ double s[256];
+// out[r] += that sum.  Rows run to a few hundred thousand partials (one per assign wave of a
+// 2^24-point problem), so each thread keeps SUM_U independent loads in flight (a strided slot
+// each: thread t, slot u reads j = t + 1024 (U i + u)) and adds them into SUM_U accumulators;
+// the accumulators, then the threads, are added in a fixed tree.  With one load in flight per
+// thread a 262144-partial row took about 400 us (latency-bound); the order depends on len only.
+constexpr int SUM_T = 1024, SUM_U = 16;
+__global__ __launch_bounds__(SUM_T) void sum_f64_rows_kernel(const double *__restrict__ part, int64_t len,
+                                                             double *__restrict__ out, int accumulate) {
+    __shared__ double s[SUM_T];
     const double *p = part + (size_t)blockIdx.x * len;
-    double acc = 0.0;
-    for (int64_t i = threadIdx.x; i < len; i += 256) acc += p[i];
-    s[threadIdx.x] = acc;
+    const int t = threadIdx.x;
+    double a[SUM_U];
+#pragma unroll
+    for (int u = 0; u < SUM_U; ++u) a[u] = 0.0;
+    int64_t i = t;
+    for (; i + (int64_t)(SUM_U - 1) * SUM_T < len; i += (int64_t)SUM_U * SUM_T) {
+        double v[SUM_U];
+#pragma unroll
+        for (int u = 0; u < SUM_U; ++u) v[u] = p[i + (int64_t)u * SUM_T];
+#pragma unroll
+        for (int u = 0; u < SUM_U; ++u) a[u] += v[u];
+    }
+    for (; i < len; i += SUM_T) a[0] += p[i];
+#pragma unroll
+    for (int w = SUM_U / 2; w >= 1; w >>= 1)
+#pragma unroll
+        for (int u = 0; u < w; ++u) a[u] += a[u + w];
+    s[t] = a[0];
     __syncthreads();
-    for (int off = 128; off >= 1; off >>= 1) {
-        if ((int)threadIdx.x < off) s[threadIdx.x] += s[threadIdx.x + off];
+    for (int off = SUM_T / 2; off >= 1; off >>= 1) {
+        if (t < off) s[t] += s[t + off];
         __syncthreads();
     }
-    if (threadIdx.x == 0) out[blockIdx.x] = accumulate ? out[blockIdx.x] + s[0] : s[0];
+    if (t == 0) out[blockIdx.x] = accumulate ? out[blockIdx.x] + s[0] : s[0];
 }
 
 hipError_t launch_sum_f64_rows(const double *part, int rows, int64_t len, double *out, hipStream_t s,
                                int accumulate) {
     if (rows <= 0) return hipSuccess;
-    sum_f64_rows_kernel<<<dim3(rows), dim3(256), 0, s>>>(part, len, out, accumulate);
+    sum_f64_rows_kernel<<<dim3(rows), dim3(SUM_T), 0, s>>>(part, len, out, accumulate);
     return hipGetLastError();
 }
 
