@@ -245,34 +245,38 @@ hipError_t launch_normalize_rows(int dt, const void *x, void *out, int64_t rows,
 // out[r] = sum_j part[r * len + j] (fp64), one workgroup per row, fixed order; with accumulate,
 // out[r] += that sum.  Rows run to a few hundred thousand partials (one per assign wave of a
 // 2^24-point problem), so each thread keeps SUM_U independent loads in flight (a strided slot
-// each: thread t, slot u reads j = t + 1024 (U i + u)) and adds them into SUM_U accumulators;
-// the accumulators, then the threads, are added in a fixed tree.  With one load in flight per
-// thread a 262144-partial row took about 400 us (latency-bound); the order depends on len only.
-constexpr int SUM_T = 1024, SUM_U = 16;
-__global__ __launch_bounds__(SUM_T) void sum_f64_rows_kernel(const double *__restrict__ part, int64_t len,
-                                                             double *__restrict__ out, int accumulate) {
-    __shared__ double s[SUM_T];
+// each: thread t, slot u reads j = t + T (U i + u)) and adds them into SUM_U accumulators; the
+// accumulators, then the threads, are added in a fixed tree.  With one load in flight per thread a
+// 262144-partial row took about 400 us (latency-bound).  Long rows take T = 1024 threads; short
+// ones T = 256 (four waves, which find room on a CU beside a running assign where sixteen do
+// not).  T is a function of len, so the order depends on len only.
+constexpr int SUM_U = 16;
+constexpr int64_t SUM_LONG = 16384;  // rows at least this long take 1024 threads
+template <int T>
+__global__ __launch_bounds__(T) void sum_f64_rows_kernel(const double *__restrict__ part, int64_t len,
+                                                         double *__restrict__ out, int accumulate) {
+    __shared__ double s[T];
     const double *p = part + (size_t)blockIdx.x * len;
     const int t = threadIdx.x;
     double a[SUM_U];
 #pragma unroll
     for (int u = 0; u < SUM_U; ++u) a[u] = 0.0;
     int64_t i = t;
-    for (; i + (int64_t)(SUM_U - 1) * SUM_T < len; i += (int64_t)SUM_U * SUM_T) {
+    for (; i + (int64_t)(SUM_U - 1) * T < len; i += (int64_t)SUM_U * T) {
         double v[SUM_U];
 #pragma unroll
-        for (int u = 0; u < SUM_U; ++u) v[u] = p[i + (int64_t)u * SUM_T];
+        for (int u = 0; u < SUM_U; ++u) v[u] = p[i + (int64_t)u * T];
 #pragma unroll
         for (int u = 0; u < SUM_U; ++u) a[u] += v[u];
     }
-    for (; i < len; i += SUM_T) a[0] += p[i];
+    for (; i < len; i += T) a[0] += p[i];
 #pragma unroll
     for (int w = SUM_U / 2; w >= 1; w >>= 1)
 #pragma unroll
         for (int u = 0; u < w; ++u) a[u] += a[u + w];
     s[t] = a[0];
     __syncthreads();
-    for (int off = SUM_T / 2; off >= 1; off >>= 1) {
+    for (int off = T / 2; off >= 1; off >>= 1) {
         if (t < off) s[t] += s[t + off];
         __syncthreads();
     }
@@ -282,7 +286,8 @@ __global__ __launch_bounds__(SUM_T) void sum_f64_rows_kernel(const double *__res
 hipError_t launch_sum_f64_rows(const double *part, int rows, int64_t len, double *out, hipStream_t s,
                                int accumulate) {
     if (rows <= 0) return hipSuccess;
-    sum_f64_rows_kernel<<<dim3(rows), dim3(SUM_T), 0, s>>>(part, len, out, accumulate);
+    if (len >= SUM_LONG) sum_f64_rows_kernel<1024><<<dim3(rows), dim3(1024), 0, s>>>(part, len, out, accumulate);
+    else sum_f64_rows_kernel<256><<<dim3(rows), dim3(256), 0, s>>>(part, len, out, accumulate);
     return hipGetLastError();
 }
 

@@ -199,6 +199,46 @@ def test_skew_full(fk, name):
         # all 5 iterations free running against the oracle's loop (blocked over points), the
         # last one teacher forced on every point
         check_fit(fk, w, x, c0, xt, ct, say=_say)
+    else:
+        # the oracle's free-running loop at K = 4096 takes minutes per iteration on the host:
+        # every iteration of the run teacher forced instead, from the GPU's own centroids
+        _check_each_iteration(fk, w, x, xt, ct, n_assign=8192, n_clusters=4, seed=35)
+
+
+def _check_each_iteration(fk, w, x, xt, ct, n_assign, n_clusters, seed):
+    """Every iteration t of a w.iters-iteration kmeans_fit, teacher forced: the fit of t + 1
+    iterations returns the labels of iteration t (made from the centroids C_t that the fit of t
+    iterations returns) and C_{t+1}.  Sampled labels against the oracle's assignment from C_t
+    (near-tie rule), the inertia of iteration t in full, C_{t+1} on the largest and on sampled
+    clusters against the oracle's means of the GPU's labels, empty clusters bit-identical; the
+    shorter fits follow the longer fit's trajectory bit for bit."""
+    B, N, K = w.B, w.N, w.K
+    rng = np.random.default_rng(seed)
+    c_full = ct.clone()
+    _, J_full, done = fk.kmeans_fit(xt, c_full, w.iters, 0.0)
+    assert done == w.iters
+    c_t = ct.cpu().numpy()
+    for t in range(w.iters):
+        c = ct.clone()
+        a, J, done = fk.kmeans_fit(xt, c, t + 1, 0.0)
+        torch.cuda.synchronize()
+        assert done == t + 1 and np.array_equal(J, J_full[:t + 1]), "fit of %d iterations left the trajectory" % (t + 1)
+        a_np, c_next = a.cpu().numpy(), c.cpu().numpy()
+        ct64 = operand(c_t, w.dtype)
+        samp = [np.sort(rng.choice(N, size=min(N, n_assign), replace=False)) for _ in range(B)]
+        x64s = np.stack([_rows64(x, w, b, samp[b]) for b in range(B)])
+        flips = check_assign(x64s, ct64, np.stack([a_np[b, samp[b]] for b in range(B)]))
+        J_or = _inertia_oracle(x, w, ct64, a_np)
+        rel = float(np.max(np.abs(J[t] - J_or) / np.abs(J_or)))
+        assert rel <= INERTIA_TOL, "iteration %d: inertia rel diff %g" % (t, rel)
+        cnt = np.stack([np.bincount(a_np[b], minlength=K) for b in range(B)])
+        ks = [np.unique(np.concatenate([np.argsort(-cnt[b], kind="stable")[:4],
+                                        rng.choice(K, size=n_clusters, replace=False)])) for b in range(B)]
+        worst = _check_cluster_sample(x, w, c_t, a_np, cnt, c_next, ks)
+        _say("iteration %d: %d sampled labels, %d near-tie flips; inertia rel %.3g; %d clusters, worst rel %.3g"
+             % (t, n_assign, flips, rel, len(ks[0]), worst))
+        c_t = c_next
+    assert np.array_equal(c_t, c_full.cpu().numpy()), "stepwise fits end away from the whole fit"
 
 
 # ---------------------------------------------------------------------------------------------
@@ -213,13 +253,9 @@ def test_splitd_full(fk):
     ct = torch.from_numpy(c0).to(device())
     a_np, _ = _stage_parity(fk, w, x, c0, xt, ct, n_assign=2048, n_clusters=48, seed=34)
     _fit_inertia_check(fk, w, x, c0, xt, ct, a_np)
-    c = ct.clone()
-    _, J, done = fk.kmeans_fit(xt, c, w.iters, 0.0)
-    x64 = W.storage_to_f64(x, w.dtype)
-    ref = oracle.lloyd_fit(x64, c0, w.iters, 0.0, dtype=w.dtype, mode="modelled")
-    rel = np.abs(J - ref["inertia"]) / np.abs(ref["inertia"])
-    _say("free-running %d iterations: max inertia rel diff %.3g" % (w.iters, rel.max()))
-    assert done == w.iters and rel.max() <= INERTIA_TOL
+    # all 3 iterations free running against the oracle's loop, the last one teacher forced on
+    # every point (labels, every centroid)
+    check_fit(fk, w, x, c0, xt, ct, say=_say)
 
 
 # ---------------------------------------------------------------------------------------------
