@@ -117,7 +117,7 @@ km_status_t check_ws(const void *ws, size_t ws_bytes, size_t need) {
 // The prepared centroid operand: c~ in tile order, then ||c~||^2 / 2.
 size_t prep_bytes(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
     const AssignCfg c = plan_assign(dt, B, N, D, K);
-    const int64_t KT = (int64_t)assign_tiles(K);
+    const int64_t KT = (int64_t)assign_tiles(dt, D, K);
     return align256((size_t)B * KT * 32 * c.d_pad * elem_bytes(dt)) + align256((size_t)B * KT * 32 * 4);
 }
 
@@ -321,8 +321,7 @@ km_status_t check_device_arch() {
 // --------------------------------------------------------------------------------------------
 // The prepared operand: c~ in tile order, then ||c~||^2 / 2 (assign_ws bytes in all).
 float *prep_norms(int dt, char *cprep, int64_t B, int64_t D, int64_t K, int d_pad) {
-    (void)D;
-    return (float *)(cprep + align256((size_t)B * assign_tiles(K) * 32 * d_pad * elem_bytes(dt)));
+    return (float *)(cprep + align256((size_t)B * assign_tiles(dt, D, K) * 32 * d_pad * elem_bytes(dt)));
 }
 
 km_status_t do_prepare(int dt, const float *C, int64_t B, int64_t N, int64_t D, int64_t K, void *cprep,
@@ -697,7 +696,7 @@ km_status_t fit_chain_setup(FitChain &c, int dt, const void *x, int64_t B_all, i
     const FitLayout &L = c.L;
     char *ws = c.ws;
     c.cfg = plan_assign(dt, B, N, D, K);
-    const int64_t KT = assign_tiles(K);
+    const int64_t KT = assign_tiles(dt, D, K);
     c.wpb = assign_wgs_per_problem(dt, B, N, D, K) * ASSIGN_WAVES;  // inertia partials per problem
     c.C = C + c.b0 * K * D;
     c.xn = (float *)(ws + L.xn);
@@ -955,7 +954,7 @@ km_status_t fit_host(int dt, const HostSource &src, int64_t B, int64_t N, int64_
     char *stage_buf[2] = {ws + L.stage_buf[0], ws + L.stage_buf[1]};
     char *cprep = ws + L.cprep;
     const AssignCfg cfg = plan_assign(dt, B, N, D, K);
-    const int64_t KT = (int64_t)assign_tiles(K);
+    const int64_t KT = (int64_t)assign_tiles(dt, D, K);
     const size_t cprep_bytes = align256((size_t)B * KT * 32 * cfg.d_pad * es);
     float *cnh = (float *)(cprep + cprep_bytes);
     const size_t cprep_per_b = (size_t)KT * 32 * cfg.d_pad * es;

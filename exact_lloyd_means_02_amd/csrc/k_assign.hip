@@ -831,7 +831,7 @@ __global__ __launch_bounds__(256) void assign_split_d_kernel(const void *__restr
 // terms of the real rows are 0 (the padding rows keep +inf).
 hipError_t launch_prep_centroids(int dt, const float *C, void *cprep, float *cnh, int B, int K, int D, int DP,
                                  hipStream_t stream, int zero_norm) {
-    const int KT = assign_tiles(K);
+    const int KT = assign_tiles(dt, D, K);
     dim3 grid(B * KT), block(256);
     if (dt == DT_F32)
         prep_centroids_kernel<DT_F32><<<grid, block, 0, stream>>>(C, (u32x4 *)cprep, cnh, K, D, DP, KT, zero_norm);
@@ -848,7 +848,7 @@ static hipError_t launch_small(const void *x, const void *cprep, const float *cn
                                float *md, double *wgi, int B, int N, int D, int K, const AssignSplit &sp,
                                hipStream_t stream) {
     constexpr int PB = small_d_pb(DT, DP);
-    const int KT = assign_tiles(K);
+    const int KT = assign_tiles(DT, D, K);
     const int bn = ASSIGN_WAVES * PB * 32;
     const int wpb = (N + bn - 1) / bn;
     if (sp.nsplit <= 1) {
@@ -919,7 +919,7 @@ hipError_t launch_assign(int dt, const AssignCfg &cfg, const void *x, const void
         if (dt == DT_F16) return launch_small_dt<DT_F16>(cfg.d_pad, x, cprep, cnh, xn, a, md, wgi, B, N, D, K, sp, s);
         return launch_small_dt<DT_BF16>(cfg.d_pad, x, cprep, cnh, xn, a, md, wgi, B, N, D, K, sp, s);
     }
-    const int KT = assign_tiles(K);
+    const int KT = assign_tiles(dt, D, K);
     const int bn = ASSIGN_WAVES * 32;
     const int wpb = (N + bn - 1) / bn;
     dim3 grid(B * wpb), block(256);

@@ -91,7 +91,7 @@ AssignCfg plan_assign(int dt, int64_t B, int64_t N, int64_t D, int64_t K) {
         c.vgpr = c.pb * (dp * s / 8 + 32) + (qg >= 4 ? 2 : qg) * 4 + 24;
         const int64_t slots = (int64_t)Gfx950::cus * 3;
         const int64_t wgs = B * cdiv(N, c.block_n);
-        const int KT = assign_tiles(K);
+        const int KT = assign_tiles(dt, D, K);
         const int nst = KT / c.tps;
         int ns = 1;
         if (wgs < slots) ns = std::max(1, std::min(8, KT / 32));

@@ -102,11 +102,22 @@ constexpr int small_d_tps(int dt, int dp) {
 constexpr int SMALL_D_STAGES = 3;
 constexpr int splitd_bd(int dt) { return dt == 0 ? 16 : 32; }
 
-// 32-centroid tiles per problem in the prepared layout: padded to a multiple of 4 so the
-// assign kernels can stream whole stages of 2 or 4 tiles (padding tiles score +inf).
-inline int assign_tiles(int64_t K) { return 4 * (int)((K + 127) / 128); }
-
 // Largest D handled by the small-D path (x tile kept in registers).
 constexpr int small_d_max(int dt) { return dt == 0 ? 128 : 256; }
+
+// 32-centroid tiles per problem in the prepared layout: padded to whole LDS stages of the small-D
+// kernel (small_d_tps tiles at the padded D), or to the split-D kernel's register group of
+// SPLITD_KB tiles; padding tiles score +inf.  (A multiple of 4 for every D doubled the scan at
+// K <= 64 where stages hold 2 tiles: 4 tiles for 2 of real centroids.)
+inline int assign_tiles(int dt, int64_t D, int64_t K) {
+    int mult = SPLITD_KB;
+    if (D <= small_d_max(dt)) {
+        int dp = dt == 0 ? 8 : 16;
+        while (dp < D) dp <<= 1;
+        mult = small_d_tps(dt, dp);
+    }
+    const int64_t t = (K + 31) / 32;
+    return (int)((t + mult - 1) / mult * mult);
+}
 
 }  // namespace fkm

@@ -72,7 +72,7 @@ int main(int argc, char **argv) {
     }
     auto kern = dt == DT_F16 ? assign_small_d_kernel<DT_F16, 128> : assign_small_d_kernel<DT_BF16, 128>;
     if (dyn > 0) CK(hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, dyn));
-    const int KT = assign_tiles(K);
+    const int KT = assign_tiles(dt, D, K);
     const int wpb = (N + cfg.block_n - 1) / cfg.block_n;
     const long nwg = (long)B * wpb;
     if (nwg > FKM_STAMP_WGS) {
