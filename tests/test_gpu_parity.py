@@ -55,6 +55,9 @@ ASSIGN_CASES = [
     ("headline_bf16", dict(B=1, N=700, D=200, K=70)),      # 2-byte, padded D = 256 (fragment ring)
     ("batched_f16", dict(B=2, N=500, D=256, K=40)),
     ("tiny_f32", dict(N=900, D=100, K=50, M=10)),          # fp32, padded D = 128 (fragment ring)
+    # one-tile stages with a single tile of centroids (one stage in all)
+    ("tiny_f32", dict(N=600, D=128, K=20, M=8)),
+    ("headline_bf16", dict(B=2, N=500, D=256, K=32)),
 ]
 
 
