@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libflashkm.so")
-SOURCES = ["api.hip", "k_assign.hip", "k_assign_d64.hip", "k_sort.hip", "k_update.hip", "k_misc.hip", "plan.cpp"]
+SOURCES = ["api.hip", "k_assign.hip", "k_assign_d64.hip", "k_assign_d128.hip", "k_sort.hip", "k_update.hip",
+           "k_misc.hip", "plan.cpp"]
 HEADERS = ["common.h", "plan.h", os.path.join("..", "..", "include", "flashkm.h"), "probe_assign_clock.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -33,6 +34,10 @@ EXTRA = {
                      "-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
     # the 2-byte D = 64 instance: the default scheduling strategy is 8% faster there
     "k_assign_d64.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+    # the 2-byte D = 128 instance (the headline width): the iterative ILP strategy is about 0.6% faster
+    # per launch there; under it the split-D kernel would run 18% slower, so it has a unit of its own
+    "k_assign_d128.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form",
+                          "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
 }
 
 
@@ -52,13 +57,16 @@ PROBE = os.path.join(HERE, "probe_assign_clock")
 
 def _build_probe(objs) -> str:
     """The FlashAssign phase probe (a measuring executable, not part of the library): its own compilation
-    of the assign source with clock stamps, linked with the plan and the D = 64 unit."""
+    of the assign source with clock stamps, linked with the plan and the D = 64 and D = 128 units.  It is
+    compiled with the D = 128 unit's flags, so that its stamped 2-byte D = 128 instance (the one it launches
+    itself) is scheduled as the library's is; its split-D and other instances then differ from the
+    library's in scheduling strategy."""
     obj = os.path.join(BUILD, "probe_assign_clock.o")
-    cmd = [HIPCC, *FLAGS, *EXTRA["k_assign.hip"], "-c", os.path.join(CSRC, PROBE_SRC), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA["k_assign_d128.hip"], "-c", os.path.join(CSRC, PROBE_SRC), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (PROBE_SRC, " ".join(cmd), r.stderr))
-    deps = [o for o in objs if os.path.basename(o) in ("plan.o", "k_assign_d64.o")]
+    deps = [o for o in objs if os.path.basename(o) in ("plan.o", "k_assign_d64.o", "k_assign_d128.o")]
     tmp = PROBE + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", obj, *deps, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

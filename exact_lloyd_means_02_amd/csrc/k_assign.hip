@@ -826,7 +826,7 @@ __global__ __launch_bounds__(256) void assign_split_d_kernel(const void *__restr
 // ------------------------------------------------------------------------------------------
 // host launchers
 // ------------------------------------------------------------------------------------------
-#ifndef FKM_ASSIGN_D64_UNIT
+#if !defined(FKM_ASSIGN_D64_UNIT) && !defined(FKM_ASSIGN_D128_UNIT)
 // zero_norm: the similarity metrics (dot product, cosine) score -x.c~ alone, so the norm
 // terms of the real rows are 0 (the padding rows keep +inf).
 hipError_t launch_prep_centroids(int dt, const float *C, void *cprep, float *cnh, int B, int K, int D, int DP,
@@ -868,19 +868,33 @@ static hipError_t launch_small(const void *x, const void *cprep, const float *cn
     return hipGetLastError();
 }
 
-// The 2-byte instance at padded D = 64 is compiled in a file of its own (k_assign_d64.hip, this
-// file with FKM_ASSIGN_D64_UNIT defined) under the compiler's default scheduling strategy: 8%
-// faster there (K = 1024; 2% at K = 32768) than the memory-clause strategy used for the others,
-// which is the better one at the other widths.
+// The 2-byte instances at padded D = 64 and D = 128 are compiled in files of their own
+// (k_assign_d64.hip and k_assign_d128.hip: this file with FKM_ASSIGN_D64_UNIT or
+// FKM_ASSIGN_D128_UNIT defined), each under the compiler scheduling strategy that runs it fastest:
+// at D = 64 the default one, 8% faster (K = 1024; 2% at K = 32768) than the memory-clause strategy
+// the other instances take; at D = 128 the iterative ILP one, about 0.6% faster per launch and 1% per
+// fit iteration at the headline shape (four same-box A/B pairs), which would make the split-D
+// kernel 18% slower.
 hipError_t launch_small_2byte_d64(int dt, const void *x, const void *cprep, const float *cnh, const float *xn,
                                   int32_t *a, float *md, double *wgi, int B, int N, int D, int K,
                                   const AssignSplit &sp, hipStream_t s);
-#ifdef FKM_ASSIGN_D64_UNIT
+hipError_t launch_small_2byte_d128(int dt, const void *x, const void *cprep, const float *cnh, const float *xn,
+                                   int32_t *a, float *md, double *wgi, int B, int N, int D, int K,
+                                   const AssignSplit &sp, hipStream_t s);
+#if defined(FKM_ASSIGN_D64_UNIT)
 hipError_t launch_small_2byte_d64(int dt, const void *x, const void *cprep, const float *cnh, const float *xn,
                                   int32_t *a, float *md, double *wgi, int B, int N, int D, int K,
                                   const AssignSplit &sp, hipStream_t s) {
     if (dt == DT_F16) return launch_small<DT_F16, 64>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, sp, s);
     if (dt == DT_BF16) return launch_small<DT_BF16, 64>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, sp, s);
+    return hipErrorInvalidValue;
+}
+#elif defined(FKM_ASSIGN_D128_UNIT)
+hipError_t launch_small_2byte_d128(int dt, const void *x, const void *cprep, const float *cnh, const float *xn,
+                                   int32_t *a, float *md, double *wgi, int B, int N, int D, int K,
+                                   const AssignSplit &sp, hipStream_t s) {
+    if (dt == DT_F16) return launch_small<DT_F16, 128>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, sp, s);
+    if (dt == DT_BF16) return launch_small<DT_BF16, 128>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, sp, s);
     return hipErrorInvalidValue;
 }
 #else
@@ -901,7 +915,7 @@ static hipError_t launch_small_dt(int DP, const void *x, const void *cprep, cons
             case 16: return launch_small<DT, 16>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, sp, s);
             case 32: return launch_small<DT, 32>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, sp, s);
             case 64: return launch_small_2byte_d64(DT, x, cprep, cnh, xn, a, md, wgi, B, N, D, K, sp, s);
-            case 128: return launch_small<DT, 128>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, sp, s);
+            case 128: return launch_small_2byte_d128(DT, x, cprep, cnh, xn, a, md, wgi, B, N, D, K, sp, s);
             case 256: return launch_small<DT, 256>(x, cprep, cnh, xn, a, md, wgi, B, N, D, K, sp, s);
         }
     }
@@ -934,6 +948,6 @@ hipError_t launch_assign(int dt, const AssignCfg &cfg, const void *x, const void
                                                               cfg.d_pad, KT, wpb);
     return hipGetLastError();
 }
-#endif  // FKM_ASSIGN_D64_UNIT
+#endif  // FKM_ASSIGN_D64_UNIT / FKM_ASSIGN_D128_UNIT
 
 }  // namespace fkm

@@ -51,7 +51,7 @@ def _kernels(asm, pattern):
 @pytest.fixture(scope="module")
 def assign_asm(tmp_path_factory):
     d = tmp_path_factory.mktemp("isa")
-    return _asm("k_assign.hip", d) + _asm("k_assign_d64.hip", d)
+    return _asm("k_assign.hip", d) + _asm("k_assign_d64.hip", d) + _asm("k_assign_d128.hip", d)
 
 
 @pytest.fixture(scope="module")
