@@ -73,6 +73,10 @@ def parse():
     p.add_argument("--clock-probe", nargs="*", metavar="B N D K [dtype [extra LDS]]",
                    help="run the FlashAssign phase probe (clock stamps per workgroup; headline shape by default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--streamed-source", default="auto", choices=["auto", "pinned", "pageable"],
+                   help="streamed workload: x in pinned host blocks (kmeans_fit_blocks) or in pageable host "
+                        "memory staged through a pinned buffer (kmeans_fit_staged); auto = pinned up to "
+                        "64 GiB (the pinned memory the GPU boxes allow one process), pageable above")
     p.add_argument("--copy-calib", action="store_true", help="run a plain 1 GiB device copy and exit")
     p.add_argument("--metric", default="l2", choices=["l2", "dot", "cosine"],
                    help="k-means variant: Lloyd (l2), dot-product or cosine (spherical) k-means")
@@ -672,11 +676,16 @@ def pinned_blocks(w, block_points=1 << 27):
     return tb, nb
 
 
+PINNED_CAP_BYTES = 64 << 30   # pinned host memory the GPU machines allow one process
+
+
 def bench_streamed(args, w):
-    """Host-resident workload: x in pinned host memory (blocks of 2^27 points, so no single
-    allocation exceeds 16 GiB at D = 64 fp16), streamed in chunks by kmeans_fit_blocks.  Reports
-    ms per Lloyd iteration, the plain host->device copy rate of the same chunks and the GPU time
-    of one iteration on one device-resident chunk (the two legs the pipeline overlaps)."""
+    """Host-resident workload, streamed in chunks: x in pinned host memory (blocks of 2^27
+    points, so no single allocation exceeds 16 GiB at D = 64 fp16) through kmeans_fit_blocks, or
+    (above the pinned cap, e.g. the stated N = 2^30, 128 GiB) in pageable host memory through
+    kmeans_fit_staged and its pinned staging buffer.  Reports ms per Lloyd iteration, the plain
+    host->device copy rate of the same chunks and the GPU time of one iteration on one
+    device-resident chunk (the legs the pipeline overlaps)."""
     import torch
     from exact_lloyd_means_02_amd import flashkm as fk
     from exact_lloyd_means_02_amd import workloads as W
@@ -685,14 +694,24 @@ def bench_streamed(args, w):
     if n_override:
         w = W.small(w.name, N=n_override)
     steps = args.steps if args.steps != 20 else w.iters
-    print("bench: allocating %.1f GiB of pinned host memory (blocks of 2^27 points) for %s" % (
-        W.nbytes(w) / 2 ** 30, w), file=sys.stderr, flush=True)
+    pageable = args.streamed_source == "pageable" or (args.streamed_source == "auto"
+                                                      and W.nbytes(w) > PINNED_CAP_BYTES)
     t0 = time.perf_counter()
-    tb, nb = pinned_blocks(w)
-    c0 = W.init_centroids_blocks(w, nb)
     dev = torch.device("cuda:0")
+    if pageable:
+        print("bench: generating %.1f GiB of points in pageable host memory for %s" % (
+            W.nbytes(w) / 2 ** 30, w), file=sys.stderr, flush=True)
+        x, c0, _ = W.make(w)
+        tb = [W.to_torch(x, w.dtype)[0]]          # one pageable [N, D] view
+        xp = W.to_torch(x, w.dtype)
+    else:
+        print("bench: allocating %.1f GiB of pinned host memory (blocks of 2^27 points) for %s" % (
+            W.nbytes(w) / 2 ** 30, w), file=sys.stderr, flush=True)
+        tb, nb = pinned_blocks(w)
+        c0 = W.init_centroids_blocks(w, nb)
     c0t = torch.from_numpy(c0).to(dev)
-    print("bench: pinned and generated in %.1f s (%d blocks)" % (time.perf_counter() - t0, len(tb)),
+    print("bench: generated in %.1f s (%s)" % (time.perf_counter() - t0,
+                                               "pageable" if pageable else "%d pinned blocks" % len(tb)),
           file=sys.stderr, flush=True)
 
     # leg 1: plain chunked host->device copies (two staging buffers, one stream)
@@ -723,20 +742,27 @@ def bench_streamed(args, w):
         W.nbytes(w) / h2d_s / 1e9, chunk_ms, steps), file=sys.stderr, flush=True)
 
     c = c0t.clone()
+    stage = fk.stage_buffer(fk.dtype_code(tb[0]), w.B, w.N, w.D, w.K, chunk) if pageable else None
     torch.cuda.synchronize()
     t3 = time.perf_counter()
-    _, inertia, done = fk.kmeans_fit_blocks(tb, c, steps, 0.0, chunk_points=chunk, want_assign=False)
+    if pageable:
+        _, inertia, done = fk.kmeans_fit_staged(xp, c, steps, 0.0, chunk_points=chunk, stage=stage,
+                                                want_assign=False)
+    else:
+        _, inertia, done = fk.kmeans_fit_blocks(tb, c, steps, 0.0, chunk_points=chunk, want_assign=False)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t3) * 1e3 / steps
     nchunks = -(-w.N // chunk)
     flops = 2.0 * w.B * w.N * w.K * w.D
     out = {
-        "metric": "ms per Lloyd iteration (%s, x streamed from pinned host memory)" % w.name,
+        "metric": "ms per Lloyd iteration (%s, x streamed from %s host memory)" % (
+            w.name, "pageable (staged through pinned buffers)" if pageable else "pinned"),
         "value": round(ms, 2), "unit": "ms", "higher_is_better": False, "n_gpus": 1, "steps": steps,
         "warmup": 0, "ms_per_step": round(ms, 2), "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "N": w.N, "D": w.D, "K": w.K, "chunk_points": chunk,
-                   "chunks": nchunks, "host_blocks": len(tb), "iters": steps, "inputs": "pinned host"},
+                   "chunks": nchunks, "host_blocks": len(tb), "iters": steps,
+                   "inputs": "pageable host, pinned staging" if pageable else "pinned host"},
         "assign_tflops_effective": round(flops / (ms * 1e-3) / 1e12, 1),
         "h2d_GBs_plain_copy": round(W.nbytes(w) / h2d_s / 1e9, 1),
         "h2d_ms_per_iteration": round(h2d_s * 1e3, 1),

@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <mutex>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "../../include/flashkm.h"
@@ -207,6 +208,11 @@ int64_t host_chunk(int64_t N, int64_t chunk_points) {
     return c;
 }
 
+// One half of kmeans_fit_staged's pinned buffer: a chunk of rows, rounded up to 256 bytes.
+size_t stage_half_bytes(int dt, int64_t N, int64_t D, int64_t chunk_points) {
+    return align256((size_t)host_chunk(N, chunk_points) * (size_t)D * elem_bytes(dt));
+}
+
 // Per-chunk regions of the streamed path, sized for every chunk: chunks hold `c` points except
 // the last, which holds N - (nchunk-1) c.  The update's plan is not monotonic in the point count
 // (its rows per wave are a power of two derived from the count, so a shorter chunk can have more
@@ -401,6 +407,7 @@ size_t kmeans_workspace_bytes(int op, km_dtype_t dt, int64_t B, int64_t N, int64
         case KM_OP_FIT_HOST: return host_layout(dt, B, N, D, K, chunk_points).total;
         case KM_OP_FIT_DOT: return fit_ws_bytes(dt, B, N, D, K, KM_METRIC_DOT);
         case KM_OP_FIT_COSINE: return fit_ws_bytes(dt, B, N, D, K, KM_METRIC_COSINE);
+        case KM_OP_STAGE_PINNED: return 2 * stage_half_bytes(dt, N, D, chunk_points);
         default: g_err = "unknown workspace op"; return 0;
     }
 }
@@ -914,10 +921,12 @@ struct StreamedPipe {
     hipStream_t cs = nullptr;
     hipEvent_t ev_copy[2] = {nullptr, nullptr};
     hipEvent_t ev_free[2] = {nullptr, nullptr};
+    hipEvent_t ev_pin[2] = {nullptr, nullptr};  // staged source: a pinned half's device copy done
     ~StreamedPipe() {
         for (int i = 0; i < 2; ++i) {
             if (ev_copy[i]) (void)hipEventDestroy(ev_copy[i]);
             if (ev_free[i]) (void)hipEventDestroy(ev_free[i]);
+            if (ev_pin[i]) (void)hipEventDestroy(ev_pin[i]);
         }
         if (cs) (void)hipStreamDestroy(cs);
     }
@@ -931,6 +940,9 @@ struct HostSource {
     const int64_t *base = nullptr;      // nblocks + 1 row offsets
     int nblocks = 0;
     size_t row_bytes = 0;
+    // staged source (pageable x): two pinned chunk buffers that host threads fill before each
+    // chunk's copy to the device; nullptr when x itself is pinned
+    char *pin[2] = {nullptr, nullptr};
     // rows [lo, lo + n) of problem b lie in one block (the blocks hold whole chunks)
     const char *rows(int64_t b, int64_t N, int64_t lo) const {
         if (x) return (const char *)x + ((size_t)b * N + lo) * row_bytes;
@@ -940,8 +952,32 @@ struct HostSource {
     }
 };
 
+// memcpy over up to 16 host threads (contiguous 4 KiB-aligned slices; one thread below 8 MiB).
+void parallel_copy(void *dst, const void *src, size_t bytes) {
+    const unsigned hw = std::thread::hardware_concurrency();
+    const size_t nt = std::max<size_t>(1, std::min<size_t>(16, hw ? hw : 1));
+    if (nt == 1 || bytes < ((size_t)8 << 20)) {
+        memcpy(dst, src, bytes);
+        return;
+    }
+    const size_t per = (bytes / nt + 4095) & ~(size_t)4095;
+    std::vector<std::thread> th;
+    for (size_t i = 0; i < nt && i * per < bytes; ++i) {
+        const size_t lo = i * per, n = std::min(per, bytes - lo);
+        th.emplace_back([=] { memcpy((char *)dst + lo, (const char *)src + lo, n); });
+    }
+    for (auto &t : th) t.join();
+}
+
 // metric as in fit_device.  Cosine k-means turns each staged chunk into unit rows in place (the
 // staging buffer is a device copy of x) before its assign and update.
+//
+// A staged source (src.pin set, x in pageable memory) runs two chunks ahead instead of one: right
+// after chunk q's kernels are queued, host threads copy chunk q + 2 into the pinned half that chunk
+// q's device copy has left (waiting for that copy to end), and its device copy is queued behind
+// chunk q's kernels, into the device buffer they free.  During chunk q's kernels the copy engine
+// moves chunk q + 1 and the host copies chunk q + 2, so the GPU waits only where one of the copies
+// takes longer than a chunk's kernels.
 km_status_t fit_host(int dt, const HostSource &src, int64_t B, int64_t N, int64_t D, int64_t K, int iters, float tol,
                      int64_t chunk_points, float *C, int32_t *assign, double *inertia, int32_t *iters_done, char *ws,
                      hipStream_t s, int metric = KM_METRIC_L2) {
@@ -978,9 +1014,14 @@ km_status_t fit_host(int dt, const HostSource &src, int64_t B, int64_t N, int64_
 
     StreamedPipe P;
     KM_HIP(hipStreamCreateWithFlags(&P.cs, hipStreamNonBlocking));
+    const bool staged = src.pin[0] != nullptr;
     for (int i = 0; i < 2; ++i) {
         KM_HIP(hipEventCreateWithFlags(&P.ev_copy[i], hipEventDisableTiming));
         KM_HIP(hipEventCreateWithFlags(&P.ev_free[i], hipEventDisableTiming));
+        if (staged) {
+            KM_HIP(hipEventCreateWithFlags(&P.ev_pin[i], hipEventDisableTiming));
+            KM_HIP(hipEventRecord(P.ev_pin[i], P.cs));  // both halves free at the start
+        }
     }
     // chunk sequence (iteration-major), copies run one chunk ahead, across iteration borders
     const int64_t per_iter = B * nchunk;
@@ -994,15 +1035,25 @@ km_status_t fit_host(int dt, const HostSource &src, int64_t B, int64_t N, int64_
         int64_t b, lo, n;
         chunk_rows(q, &b, &lo, &n);
         const int buf = (int)(q & 1);
+        const size_t bytes = (size_t)n * D * es;
+        const void *from = src.rows(b, N, lo);
+        if (staged) {  // into pinned half `buf`, once its previous device copy (chunk q - 2) is done
+            KM_HIP(hipEventSynchronize(P.ev_pin[buf]));
+            parallel_copy(src.pin[buf], from, bytes);
+            from = src.pin[buf];
+        }
         KM_HIP(hipStreamWaitEvent(P.cs, P.ev_free[buf], 0));
-        KM_HIP(hipMemcpyAsync(stage_buf[buf], src.rows(b, N, lo), (size_t)n * D * es, hipMemcpyHostToDevice, P.cs));
+        KM_HIP(hipMemcpyAsync(stage_buf[buf], from, bytes, hipMemcpyHostToDevice, P.cs));
         KM_HIP(hipEventRecord(P.ev_copy[buf], P.cs));
+        if (staged) KM_HIP(hipEventRecord(P.ev_pin[buf], P.cs));
         return ok();
     };
+    const int64_t total_q = (int64_t)iters * per_iter;  // chunks of a fit that runs all iterations
     // the copy stream must not start before work already queued on `s` that it depends on
     KM_HIP(hipEventRecord(P.ev_free[0], s));
     KM_HIP(hipEventRecord(P.ev_free[1], s));
     KM_TRY(issue_copy(0));
+    if (staged && total_q > 1) KM_TRY(issue_copy(1));
     if (cosine) KM_HIP(launch_normalize_rows(KM_F32, C, C, B * K, (int)D, s));
     // the similarity metrics take zero point norms (their per-point value is then -2 x.c~)
     if (simm) KM_HIP(launch_fill_i32((int32_t *)xn, chunk, 0, s));
@@ -1019,7 +1070,7 @@ km_status_t fit_host(int dt, const HostSource &src, int64_t B, int64_t N, int64_
         KM_HIP(launch_fill_i32((int32_t *)(ring_j + (size_t)slot * B), 2 * B, 0, s));
         for (int64_t i = 0; i < per_iter; ++i, ++q) {
             const bool more = (t + 1 < iters) || (i + 1 < per_iter);
-            if (more) KM_TRY(issue_copy(q + 1));
+            if (more && !staged) KM_TRY(issue_copy(q + 1));
             int64_t b, lo, n;
             chunk_rows(q, &b, &lo, &n);
             const int buf = (int)(q & 1);
@@ -1039,6 +1090,7 @@ km_status_t fit_host(int dt, const HostSource &src, int64_t B, int64_t N, int64_
             KM_HIP(launch_update(dt, xc, sids, sidx, counts, 1, (int)n, (int)D, (int)K, 1, nullptr, nullptr,
                                  sums + (size_t)b * K * D, cnt + (size_t)b * K, UpdRefresh{}, mem, s));
             KM_HIP(hipEventRecord(P.ev_free[buf], s));
+            if (staged && q + 2 < total_q) KM_TRY(issue_copy(q + 2));
         }
         KM_HIP(launch_finalize_acc(dt, sums, cnt, C, tol > 0.f ? ring_s + (size_t)slot * B : nullptr,
                                    (double *)(ws + L.shk), ref, (int)B, (int)K, (int)D, s, cosine ? 1 : 0));
@@ -1177,5 +1229,40 @@ extern "C" km_status_t kmeans_fit_blocks(const void *const *x_blocks, const int6
     src.nblocks = nblocks;
     src.row_bytes = (size_t)D * elem_bytes(dt);
     return fit_host(dt, src, 1, N, D, K, iters, tol, chunk_points, centroids, assign, inertia, iters_done, (char *)ws,
+                    (hipStream_t)stream);
+}
+
+extern "C" km_status_t kmeans_fit_staged(const void *x, km_dtype_t dt, int64_t B, int64_t N, int64_t D, int64_t K,
+                                         int32_t iters, float tol, int64_t chunk_points, void *pinned_stage,
+                                         size_t pinned_bytes, float *centroids, int32_t *assign, double *inertia,
+                                         int32_t *iters_done, void *ws, size_t ws_bytes, void *stream) {
+    KM_TRY(check_shape(dt, B, N, D, K));
+    KM_TRY(check_ptr(x, "x"));
+    KM_TRY(check_ptr(pinned_stage, "pinned_stage"));
+    KM_TRY(check_ptr(centroids, "centroids"));
+    if (iters < 1) return fail(KM_ERR_INVALID, "iters must be >= 1");
+    if (!(tol >= 0.f)) return fail(KM_ERR_INVALID, "tol must be >= 0");
+    if (chunk_points < 0) return fail(KM_ERR_INVALID, "chunk_points must be >= 0");
+    if (((uintptr_t)centroids & 15) != 0) return fail(KM_ERR_INVALID, "centroids must be 16-byte aligned");
+    if (((uintptr_t)x & 15) != 0) return fail(KM_ERR_INVALID, "x must be 16-byte aligned");
+    if (((uintptr_t)pinned_stage & 15) != 0) return fail(KM_ERR_INVALID, "pinned_stage must be 16-byte aligned");
+    const size_t half = stage_half_bytes(dt, N, D, chunk_points);
+    if (pinned_bytes < 2 * half)
+        return fail(KM_ERR_WORKSPACE, "pinned_stage too small: %zu < %zu bytes", pinned_bytes, 2 * half);
+    if (!ws) return fail(KM_ERR_WORKSPACE, "workspace is NULL");
+    KM_TRY(check_ws(ws, ws_bytes, host_layout(dt, B, N, D, K, chunk_points).total));
+    KM_TRY(check_device_arch());
+    if (pointer_kind(x) == PTR_DEVICE) return fail(KM_ERR_INVALID, "x must be host memory (got device memory)");
+    if (pointer_kind(pinned_stage) != PTR_PINNED_HOST)
+        return fail(KM_ERR_UNSUPPORTED, "pinned_stage is not pinned host memory");
+    KM_TRY(require_device(centroids, "centroids"));
+    KM_TRY(require_device(assign, "assign"));
+    KM_TRY(require_device(ws, "ws"));
+    HostSource src;
+    src.x = x;
+    src.row_bytes = (size_t)D * elem_bytes(dt);
+    src.pin[0] = (char *)pinned_stage;
+    src.pin[1] = (char *)pinned_stage + half;
+    return fit_host(dt, src, B, N, D, K, iters, tol, chunk_points, centroids, assign, inertia, iters_done, (char *)ws,
                     (hipStream_t)stream);
 }

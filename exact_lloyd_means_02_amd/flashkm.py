@@ -17,7 +17,7 @@ KM_F32, KM_F16, KM_BF16 = 0, 1, 2
 DT_CODES = {"f32": KM_F32, "f16": KM_F16, "bf16": KM_BF16}
 KM_OK, KM_ERR_INVALID, KM_ERR_UNSUPPORTED, KM_ERR_WORKSPACE, KM_ERR_HIP = 0, -1, -2, -3, -4
 KM_OP_ASSIGN, KM_OP_ARGSORT, KM_OP_UPDATE, KM_OP_FIT, KM_OP_FIT_HOST = 1, 2, 3, 4, 5
-KM_OP_FIT_DOT, KM_OP_FIT_COSINE = 6, 7
+KM_OP_FIT_DOT, KM_OP_FIT_COSINE, KM_OP_STAGE_PINNED = 6, 7, 8
 KM_METRIC_L2, KM_METRIC_DOT, KM_METRIC_COSINE = 0, 1, 2
 METRICS = {"l2": KM_METRIC_L2, "euclid": KM_METRIC_L2, "dot": KM_METRIC_DOT, "cosine": KM_METRIC_COSINE}
 STATUS_NAMES = {0: "KM_OK", -1: "KM_ERR_INVALID", -2: "KM_ERR_UNSUPPORTED", -3: "KM_ERR_WORKSPACE", -4: "KM_ERR_HIP"}
@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "KM_OK", -1: "KM_ERR_INVALID", -2: "KM_ERR_UNSUPPORTED", -3: 
 # every symbol the header declares
 EXPORTS = ["kmeans_plan", "kmeans_workspace_bytes", "kmeans_row_norms", "kmeans_assign", "kmeans_assign_noalloc",
            "kmeans_prepare_centroids", "kmeans_assign_prepared", "kmeans_argsort_ids", "kmeans_argsort_status",
-           "kmeans_update", "kmeans_fit", "kmeans_fit_blocks", "kmeans_normalize_rows",
+           "kmeans_update", "kmeans_fit", "kmeans_fit_blocks", "kmeans_fit_staged", "kmeans_normalize_rows",
            "kmeans_prepare_centroids_metric", "kmeans_fit_metric", "kmeans_last_error"]
 
 
@@ -63,13 +63,15 @@ def _load():
     lib.kmeans_fit.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, i32, f32, i64, vp, vp, vp, vp, vp, sz, vp]
     lib.kmeans_fit_blocks.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(i64), i32, ctypes.c_int, i64, i64, i32, f32,
                                       i64, vp, vp, vp, vp, vp, sz, vp]
+    lib.kmeans_fit_staged.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, i32, f32, i64, vp, sz, vp, vp, vp, vp,
+                                      vp, sz, vp]
     lib.kmeans_normalize_rows.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp]
     lib.kmeans_prepare_centroids_metric.argtypes = [vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64, vp, sz, vp]
     lib.kmeans_fit_metric.argtypes = [vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64, i32, f32, i64, vp, vp, vp,
                                       vp, vp, sz, vp]
     for n in ("kmeans_plan", "kmeans_row_norms", "kmeans_assign", "kmeans_assign_noalloc", "kmeans_prepare_centroids",
               "kmeans_assign_prepared", "kmeans_argsort_ids", "kmeans_argsort_status", "kmeans_update", "kmeans_fit",
-              "kmeans_fit_blocks", "kmeans_normalize_rows",
+              "kmeans_fit_blocks", "kmeans_fit_staged", "kmeans_normalize_rows",
               "kmeans_prepare_centroids_metric", "kmeans_fit_metric"):
         getattr(lib, n).restype = ctypes.c_int
     lib.kmeans_last_error.argtypes = []
@@ -377,6 +379,48 @@ def kmeans_fit_blocks(blocks, centroids, iters: int, tol: float = 0.0, chunk_poi
     done = ctypes.c_int32(0)
     _check(LIB.kmeans_fit_blocks(ptrs, npts, len(blocks), dt, D, K, int(iters), float(tol), int(chunk_points),
                                  _ptr(centroids), _ptr(assign), inertia.ctypes.data_as(ctypes.c_void_p),
+                                 ctypes.byref(done), _ptr(ws), ws.numel(), st))
+    return assign, inertia[: done.value], done.value
+
+
+def stage_buffer(dt: int, B: int, N: int, D: int, K: int, chunk_points: int = 0):
+    """A pinned host uint8 tensor of the size kmeans_fit_staged asks for (KM_OP_STAGE_PINNED)."""
+    torch = _torch()
+    nbytes = LIB.kmeans_workspace_bytes(KM_OP_STAGE_PINNED, dt, B, N, D, K, chunk_points)
+    if nbytes == 0:
+        raise FlashKMError(KM_ERR_INVALID, last_error() or "bad shape for the staging buffer")
+    buf = torch.empty(nbytes + 256, dtype=torch.uint8, pin_memory=True)
+    off = (-buf.data_ptr()) % 256
+    return buf[off:off + nbytes]
+
+
+def kmeans_fit_staged(x, centroids, iters: int, tol: float = 0.0, chunk_points: int = 0, stage=None, assign=None,
+                      want_assign=True, stream=None):
+    """Lloyd's loop, streamed from host memory that need not be pinned: x is a contiguous host
+    tensor [B, N, D] (pageable or pinned); chunks pass through the pinned tensor `stage` (from
+    stage_buffer, made here when None).  `centroids` (device f32 [B, K, D]) holds the init and
+    receives the result.  Returns (assign or None, inertia [iters_done, B] numpy float64,
+    iters_done)."""
+    torch = _torch()
+    import numpy as np
+    _need(x.dim() == 3 and x.is_contiguous() and not x.is_cuda, "x must be a contiguous host [B, N, D] tensor")
+    B, N, D = x.shape
+    _need(centroids.is_cuda and centroids.dtype == torch.float32 and centroids.is_contiguous()
+          and centroids.dim() == 3 and centroids.shape[0] == B and centroids.shape[2] == D,
+          "centroids: device f32 [B, K, D]")
+    K = centroids.shape[1]
+    dt = dtype_code(x)
+    dev = centroids.device
+    if stage is None:
+        stage = stage_buffer(dt, B, N, D, K, chunk_points)
+    if want_assign and assign is None:
+        assign = torch.empty((B, N), dtype=torch.int32, device=dev)
+    st = _stream(centroids, stream)
+    ws = workspace(KM_OP_FIT_HOST, dt, B, N, D, K, dev, chunk_points, stream=st)
+    inertia = np.zeros((iters, B), dtype=np.float64)
+    done = ctypes.c_int32(0)
+    _check(LIB.kmeans_fit_staged(_ptr(x), dt, B, N, D, K, int(iters), float(tol), int(chunk_points), _ptr(stage),
+                                 stage.numel(), _ptr(centroids), _ptr(assign), inertia.ctypes.data_as(ctypes.c_void_p),
                                  ctypes.byref(done), _ptr(ws), ws.numel(), st))
     return assign, inertia[: done.value], done.value
 

@@ -70,7 +70,9 @@ typedef enum {
     KM_OP_FIT = 4,            /* kmeans_fit with device-resident x */
     KM_OP_FIT_HOST = 5,       /* kmeans_fit with x in pinned host memory (streamed path) */
     KM_OP_FIT_DOT = 6,        /* kmeans_fit_metric, KM_METRIC_DOT, device-resident x */
-    KM_OP_FIT_COSINE = 7      /* kmeans_fit_metric, KM_METRIC_COSINE, device-resident x */
+    KM_OP_FIT_COSINE = 7,     /* kmeans_fit_metric, KM_METRIC_COSINE, device-resident x */
+    KM_OP_STAGE_PINNED = 8    /* kmeans_fit_staged: bytes of its pinned host staging buffer (its
+                                 device workspace is that of KM_OP_FIT_HOST) */
 } km_op_t;
 
 /* Similarity of a point and a centroid (see kmeans_fit_metric). */
@@ -293,6 +295,33 @@ km_status_t kmeans_fit(const void *x, km_dtype_t dt, int64_t B, int64_t N, int64
 km_status_t kmeans_fit_blocks(const void *const *x_blocks, const int64_t *block_points, int32_t nblocks,
                               km_dtype_t dt, int64_t D, int64_t K, int32_t iters, float tol,
                               int64_t chunk_points, float *centroids, int32_t *assign, double *inertia,
+                              int32_t *iters_done, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The streamed path for points in pageable host memory, staged through a
+ * pinned host buffer that the caller provides: for hosts that cannot pin the
+ * whole point set (README, "Large tensor Benchmark"; paper digest, step (3):
+ * data that does not fit the GPU streams through it chunk by chunk).  Host
+ * threads of the call copy chunk q + 2 into one half of the pinned buffer
+ * while the GPU works on chunk q and the copy engine moves chunk q + 1 to the
+ * device, so where those copies keep up the iteration tracks the GPU's work.
+ * The result is that of kmeans_fit on pinned host x with the same chunk,
+ * bit for bit.
+ *   x             host [B, N, D] of dtype dt (pageable or pinned), 16-byte
+ *                 aligned; read by host threads during the call
+ *   pinned_stage  pinned host memory (hipHostMalloc or a pinned allocation),
+ *                 16-byte aligned, of at least
+ *                 kmeans_workspace_bytes(KM_OP_STAGE_PINNED, dt, B, N, D, K,
+ *                 chunk_points) bytes: two chunk buffers; overwritten
+ *   ws            device, >= kmeans_workspace_bytes(KM_OP_FIT_HOST, ...)
+ * Other arguments and the return as kmeans_fit (KM_ERR_INVALID for device x,
+ * KM_ERR_UNSUPPORTED for a pinned_stage that is not pinned host memory).  It
+ * creates one copy stream and six events for the call, and up to 16 host
+ * threads per chunk copy, and returns after the work has finished.
+ */
+km_status_t kmeans_fit_staged(const void *x, km_dtype_t dt, int64_t B, int64_t N, int64_t D, int64_t K,
+                              int32_t iters, float tol, int64_t chunk_points, void *pinned_stage,
+                              size_t pinned_bytes, float *centroids, int32_t *assign, double *inertia,
                               int32_t *iters_done, void *ws, size_t ws_bytes, void *stream);
 
 /*

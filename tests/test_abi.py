@@ -122,6 +122,31 @@ def test_fit_blocks_validation(fk):
     assert call([256], [4096], ws=None) == fk.KM_ERR_WORKSPACE
 
 
+def test_fit_staged_validation(fk):
+    """kmeans_fit_staged rejects bad arguments before any HIP call; its pinned buffer holds two
+    chunks of rows, each rounded up to 256 bytes."""
+    L = fk.LIB
+    half = lambda n, d, c, es: -(-min(c if c > 0 else 1 << 24, n) * d * es // 256) * 256
+    assert fk.kmeans_workspace_bytes(fk.KM_OP_STAGE_PINNED, 1, 1, 1 << 20, 64, 100, 1 << 18) == 2 * half(1 << 20, 64, 1 << 18, 2)
+    assert fk.kmeans_workspace_bytes(fk.KM_OP_STAGE_PINNED, 0, 2, 5000, 37, 10, 0) == 2 * half(5000, 37, 0, 4)
+    need = fk.kmeans_workspace_bytes(fk.KM_OP_STAGE_PINNED, 2, 1, 4096, 16, 8, 0)
+
+    def call(x=P, iters=2, tol=0.0, chunk=0, stage=P, sbytes=None, ws=P, C=P, K=8):
+        return L.kmeans_fit_staged(x, 2, 1, 4096, 16, K, iters, tol, chunk, stage, need if sbytes is None else sbytes,
+                                   C, None, None, None, ws, 1 << 30, None)
+    assert call(x=None) == fk.KM_ERR_INVALID and "x" in fk.last_error()
+    assert call(stage=None) == fk.KM_ERR_INVALID and "pinned_stage" in fk.last_error()
+    assert call(C=None) == fk.KM_ERR_INVALID
+    assert call(K=5000) == fk.KM_ERR_INVALID and "K (5000) > N (4096)" in fk.last_error()
+    assert call(iters=0) == fk.KM_ERR_INVALID
+    assert call(tol=-1.0) == fk.KM_ERR_INVALID
+    assert call(chunk=-1) == fk.KM_ERR_INVALID
+    assert call(x=ctypes.c_void_p(264)) == fk.KM_ERR_INVALID and "16-byte" in fk.last_error()
+    assert call(stage=ctypes.c_void_p(264)) == fk.KM_ERR_INVALID and "16-byte" in fk.last_error()
+    assert call(sbytes=need - 1) == fk.KM_ERR_WORKSPACE and "pinned_stage too small" in fk.last_error()
+    assert call(ws=None) == fk.KM_ERR_WORKSPACE
+
+
 def test_workspace_sizes(fk):
     for op in (fk.KM_OP_ASSIGN, fk.KM_OP_ARGSORT, fk.KM_OP_UPDATE, fk.KM_OP_FIT, fk.KM_OP_FIT_HOST):
         assert fk.kmeans_workspace_bytes(op, 2, 1, 10, 4, 11) == 0          # K > N: invalid

@@ -168,6 +168,30 @@ def test_fit_streamed_ragged_last_chunk_needs_more_scratch(fk):
     assert (np.abs(J_host - ref["inertia"]) / ref["inertia"]).max() <= INERTIA_TOL
 
 
+@pytest.mark.parametrize("B,iters,tol", [(1, 3, 0.0), (2, 2, 0.0), (1, 4, 1e30)])
+def test_fit_staged_equals_pinned(fk, B, iters, tol):
+    """x in pageable host memory through the pinned staging buffer: the same chunk sequence as the
+    pinned streamed fit, so the same labels, centroids and inertia, bit for bit; a ragged last chunk,
+    chunks that run two ahead across iteration borders, and (tol = 1e30) a fit that stops after its
+    first iteration with copies of the next one already issued."""
+    chunk = 1 << 14
+    w = W.small("streamed_f16", B=B, N=5 * chunk + 333, K=256, M=256, iters=iters, tol=tol)
+    _say(f"case {w}, chunk_points {chunk}")
+    x, x64, c0, xt, ct = make_inputs(w)
+    xp = W.to_torch(x, w.dtype)                  # pageable
+    xh = xp.pin_memory()
+    assert not xp.is_pinned()
+    c_pin, c_stg = ct.clone(), ct.clone()
+    a_pin, J_pin, d_pin = fk.kmeans_fit(xh, c_pin, w.iters, w.tol, chunk_points=chunk)
+    a_stg, J_stg, d_stg = fk.kmeans_fit_staged(xp, c_stg, w.iters, w.tol, chunk_points=chunk)
+    assert d_stg == d_pin == (1 if tol > 0 else w.iters)
+    assert np.array_equal(a_stg.cpu().numpy(), a_pin.cpu().numpy())
+    assert np.array_equal(c_stg.cpu().numpy(), c_pin.cpu().numpy())
+    assert np.array_equal(J_stg, J_pin)
+    ref = oracle.lloyd_fit(x64, c0, d_stg, 0.0, dtype=w.dtype, mode="modelled")
+    assert (np.abs(J_stg - ref["inertia"]) / ref["inertia"]).max() <= INERTIA_TOL
+
+
 def test_fit_blocks_equals_contiguous(fk):
     """The points split over pinned host blocks (every block but the last a multiple of the chunk):
     the same chunk sequence as one contiguous pinned array, so the same labels, centroids and
