@@ -952,7 +952,8 @@ struct HostSource {
     }
 };
 
-// memcpy over up to 16 host threads (contiguous 4 KiB-aligned slices; one thread below 8 MiB).
+// memcpy over up to 16 host threads (contiguous 4 KiB-aligned slices; one thread below 8 MiB).  A
+// slice whose thread cannot be started is copied by the calling thread (no exception leaves here).
 void parallel_copy(void *dst, const void *src, size_t bytes) {
     const unsigned hw = std::thread::hardware_concurrency();
     const size_t nt = std::max<size_t>(1, std::min<size_t>(16, hw ? hw : 1));
@@ -962,9 +963,14 @@ void parallel_copy(void *dst, const void *src, size_t bytes) {
     }
     const size_t per = (bytes / nt + 4095) & ~(size_t)4095;
     std::vector<std::thread> th;
+    th.reserve(nt);
     for (size_t i = 0; i < nt && i * per < bytes; ++i) {
         const size_t lo = i * per, n = std::min(per, bytes - lo);
-        th.emplace_back([=] { memcpy((char *)dst + lo, (const char *)src + lo, n); });
+        try {
+            th.emplace_back([=] { memcpy((char *)dst + lo, (const char *)src + lo, n); });
+        } catch (...) {
+            memcpy((char *)dst + lo, (const char *)src + lo, n);
+        }
     }
     for (auto &t : th) t.join();
 }
