@@ -254,7 +254,7 @@ km_status_t kmeans_update(const void *x, km_dtype_t dt, const int32_t *sorted_id
  * / partial update of chunk i, and divides after the last chunk.  x is never
  * cached on the device across iterations.
  *   x            device or pinned host [B, N, D] dtype dt (pageable host
- *                memory -> KM_ERR_UNSUPPORTED)
+ *                memory -> KM_ERR_UNSUPPORTED; kmeans_fit_staged takes it)
  *   iters        maximum iterations (>= 1); tol >= 0
  *   chunk_points streamed path only (0 = 2^24, clamped to N)
  *   centroids    device [B, K, D] float32 in: init, out: final
