@@ -76,7 +76,7 @@ def parse():
     p.add_argument("--streamed-source", default="auto", choices=["auto", "pinned", "pageable"],
                    help="streamed workload: x in pinned host blocks (kmeans_fit_blocks) or in pageable host "
                         "memory staged through a pinned buffer (kmeans_fit_staged); auto = pinned up to "
-                        "64 GiB (the pinned memory the GPU boxes allow one process), pageable above")
+                        "64 GiB (the pinned memory the MI355X hosts measured allow one process), pageable above")
     p.add_argument("--copy-calib", action="store_true", help="run a plain 1 GiB device copy and exit")
     p.add_argument("--metric", default="l2", choices=["l2", "dot", "cosine"],
                    help="k-means variant: Lloyd (l2), dot-product or cosine (spherical) k-means")
@@ -676,7 +676,7 @@ def pinned_blocks(w, block_points=1 << 27):
     return tb, nb
 
 
-PINNED_CAP_BYTES = 64 << 30   # pinned host memory the GPU machines allow one process
+PINNED_CAP_BYTES = 64 << 30   # pinned host memory the MI355X hosts measured allow one process
 
 
 def bench_streamed(args, w):

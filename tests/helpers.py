@@ -8,7 +8,7 @@ import oracle
 from exact_lloyd_means_02_amd import workloads as W
 
 U32 = 2.0 ** -24          # fp32 unit roundoff
-NEAR = 1e-3               # near-tie band: top-2 gap below NEAR * best (spec rule)
+NEAR = 1e-3               # near-tie band: top-2 gap below NEAR * best (the parity rule for labels)
 CENTROID_TOL = {"f32": 1e-5, "f16": 1e-3, "bf16": 1e-3}
 INERTIA_TOL = 1e-4
 

@@ -309,7 +309,7 @@ def test_streamed_real_chunks(fk):
 # points (128 GiB), 3 iterations.  Needs that much pinned host memory and several minutes of host
 # time for the oracle, so it runs only when asked (FLASHKM_FULL_STREAMED=1); FLASHKM_FULL_STREAMED_N
 # points (a multiple of 2^27) instead of 2^30 when set.  Up to 64 GiB (the pinned host memory the
-# GPU machines allow one process) the points sit in pinned blocks (kmeans_fit_blocks); above, as at the
+# MI355X hosts measured allow one process) the points sit in pinned blocks (kmeans_fit_blocks); above, as at the
 # stated 2^30 points (128 GiB), in pageable memory staged through a pinned buffer (kmeans_fit_staged).
 # ---------------------------------------------------------------------------------------------
 @pytest.mark.skipif(os.environ.get("FLASHKM_FULL_STREAMED") != "1",
