@@ -1029,7 +1029,8 @@ km_status_t fit_host(int dt, const HostSource &src, int64_t B, int64_t N, int64_
             KM_HIP(hipEventRecord(P.ev_pin[i], P.cs));  // both halves free at the start
         }
     }
-    // chunk sequence (iteration-major), copies run one chunk ahead, across iteration borders
+    // chunk sequence (iteration-major); copies run one chunk ahead (two for a staged source), across
+    // iteration borders
     const int64_t per_iter = B * nchunk;
     auto chunk_rows = [&](int64_t q, int64_t *b, int64_t *lo, int64_t *n) {
         const int64_t r = q % per_iter;
