@@ -506,13 +506,16 @@ class FlashKMeans:
 
     Input: [N, d] (one problem) or [B, N, d] (B independent problems sharing k), on the GPU, or in
     host memory.  Pinned host memory selects the streamed path; other host tensors are copied to
-    the GPU first.  `dtype` is the compute dtype the points are cast to.
+    the GPU first, or, with `host_streaming=True` (Euclidean metric), fitted in place through the
+    staged streamed path (kmeans_fit_staged: for point sets larger than the GPU's memory).  `dtype`
+    is the compute dtype the points are cast to.
     After fitting: `centroids` (fp32 [B, k, d], or [k, d] for 2-D input), `labels_` (from the last
     assignment), `obj` (per-iteration inertia, or total similarity for "dot" / "cosine"),
     `iters_done`.  `cluster_centers_` and `inertia_` mirror scikit-learn's names."""
 
     def __init__(self, d: int, k: int, niter: int = 25, tol: float = 0.0, dtype=None, metric: str = "l2",
-                 device=None, seed: int = 0, verbose: bool = False, chunk_points: int = 0):
+                 device=None, seed: int = 0, verbose: bool = False, chunk_points: int = 0,
+                 host_streaming: bool = False):
         torch = _torch()
         _need(d >= 1 and k >= 1 and niter >= 1 and tol >= 0.0, "d, k, niter must be >= 1 and tol >= 0")
         metric_code(metric)
@@ -522,6 +525,8 @@ class FlashKMeans:
         self.metric = metric
         self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
         self.seed, self.verbose, self.chunk_points = int(seed), bool(verbose), int(chunk_points)
+        _need(not host_streaming or metric_code(metric) == KM_METRIC_L2, "host_streaming: Euclidean metric only")
+        self.host_streaming = bool(host_streaming)
         self.centroids = None
         self.labels_ = None
         self.obj = None
@@ -538,7 +543,7 @@ class FlashKMeans:
         x3 = x if batched else x.unsqueeze(0)
         if x3.dtype != self.dtype:
             x3 = x3.to(self.dtype)
-        if x3.is_cuda or not x3.is_pinned():
+        if not x3.is_cuda and not x3.is_pinned() and not (fitting and self.host_streaming):
             x3 = x3.to(self.device)
         return x3.contiguous(), batched
 
@@ -557,7 +562,10 @@ class FlashKMeans:
             init = init_centroids if init_centroids.dim() == 3 else init_centroids.unsqueeze(0)
             _need(tuple(init.shape) == (B, self.k, self.d), "init_centroids must be [B, k, d] or [k, d]")
         c = init.to(self.device, dtype=torch.float32).contiguous().clone()
-        a, obj, done = kmeans_fit_metric(x3, c, self.metric, self.niter, self.tol, self.chunk_points)
+        if not x3.is_cuda and not x3.is_pinned():   # host_streaming with pageable points
+            a, obj, done = kmeans_fit_staged(x3, c, self.niter, self.tol, self.chunk_points)
+        else:
+            a, obj, done = kmeans_fit_metric(x3, c, self.metric, self.niter, self.tol, self.chunk_points)
         self.centroids = c
         self.labels_ = a
         self.obj = obj

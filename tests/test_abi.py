@@ -331,6 +331,8 @@ def test_wrapper_validation_without_gpu(fk):
         fk.FlashKMeans(d=8, k=0, device="cuda:0")
     with pytest.raises(ValueError, match="dtype"):
         fk.FlashKMeans(d=8, k=5, dtype=torch.float64, device="cuda:0")
+    with pytest.raises(ValueError, match="host_streaming"):
+        fk.FlashKMeans(d=8, k=5, metric="cosine", host_streaming=True, device="cuda:0")
 
 
 def test_centroid_alignment_validation(fk):

@@ -84,6 +84,23 @@ def test_pinned_host_input_uses_streamed_path(fk):
     assert rel.max().item() < 1e-5
 
 
+def test_host_streaming_pageable_equals_pinned(fk):
+    """host_streaming=True fits pageable host points in place through the staged path: the same chunk
+    sequence as pinned host input, so the same labels and centroids, bit for bit."""
+    w = W.small("headline_bf16", B=2, N=9000, K=40)
+    _say(f"wrapper host streaming {w}")
+    x, x64, c0, xt, ct = make_inputs(w)
+    xp = xt.cpu()
+    assert not xp.is_pinned()
+    km_s = fk.FlashKMeans(d=w.D, k=w.K, niter=3, dtype=torch.bfloat16, chunk_points=4096, host_streaming=True)
+    lab_s = km_s.fit_predict(xp, init_centroids=ct)
+    km_p = fk.FlashKMeans(d=w.D, k=w.K, niter=3, dtype=torch.bfloat16, chunk_points=4096)
+    lab_p = km_p.fit_predict(xp.pin_memory(), init_centroids=ct)
+    assert torch.equal(lab_s.cpu(), lab_p.cpu())
+    assert torch.equal(km_s.centroids.cpu(), km_p.centroids.cpu())
+    assert np.array_equal(km_s.obj, km_p.obj)
+
+
 @pytest.mark.parametrize("metric", ["cosine", "dot"])
 def test_metric_wrapper(fk, metric):
     w = W.small("headline_bf16", B=2, N=4000, K=32)
