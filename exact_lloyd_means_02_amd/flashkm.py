@@ -459,14 +459,18 @@ def kmeans_fit_metric(x, centroids, metric, iters: int, tol: float = 0.0, chunk_
 def batch_kmeans_euclid(x, n_clusters: int, max_iters: int = 100, tol: float = 0.0, init_centroids=None,
                         chunk_points: int = 0, seed: int = 0):
     """README-style entry (flash-kmeans README, "Usage"): returns (cluster_ids, centers, inertia).
-    Without init_centroids, K distinct points per problem are drawn with torch's generator."""
+    Without init_centroids, K distinct points per problem are drawn with torch's generator.  x on
+    the GPU, or in host memory: pinned (streamed fit) or pageable (staged streamed fit)."""
     torch = _torch()
     B, N, D = x.shape
-    dev = x.device if x.is_cuda else torch.device("cuda")
+    dev = x.device if x.is_cuda else torch.device("cuda", torch.cuda.current_device())
     if init_centroids is None:
         init_centroids = _seeded_init(x, n_clusters, seed)
     c = init_centroids.to(dev, dtype=torch.float32).contiguous().clone()
-    ids, inertia, _ = kmeans_fit(x, c, max_iters, tol, chunk_points)
+    if not x.is_cuda and not x.is_pinned():
+        ids, inertia, _ = kmeans_fit_staged(x.contiguous(), c, max_iters, tol, chunk_points)
+    else:
+        ids, inertia, _ = kmeans_fit(x, c, max_iters, tol, chunk_points)
     return ids, c, inertia
 
 
@@ -490,12 +494,20 @@ def _seeded_init(x, n_clusters: int, seed: int):
 
 
 def _batch_metric(x, n_clusters, max_iters, tol, init_centroids, seed, metric):
+    """x on the GPU, in pinned host memory (streamed fit), or, for the Euclidean metric, in pageable
+    host memory (staged streamed fit); the centroids live on the GPU (the current device for host x)."""
     torch = _torch()
-    _need(x.is_cuda or x.is_pinned(), "x must be on the GPU or in pinned host memory")
+    pageable = not x.is_cuda and not x.is_pinned()
+    _need(not pageable or metric_code(metric) == KM_METRIC_L2,
+          "x must be on the GPU or in pinned host memory (pageable host memory: Euclidean metric only)")
     if init_centroids is None:
         init_centroids = _seeded_init(x, n_clusters, seed)
-    c = init_centroids.to(x.device, dtype=torch.float32).contiguous().clone()
-    ids, obj, _ = kmeans_fit_metric(x, c, metric, max_iters, tol)
+    dev = x.device if x.is_cuda else torch.device("cuda", torch.cuda.current_device())
+    c = init_centroids.to(dev, dtype=torch.float32).contiguous().clone()
+    if pageable:
+        ids, obj, _ = kmeans_fit_staged(x.contiguous(), c, max_iters, tol)
+    else:
+        ids, obj, _ = kmeans_fit_metric(x, c, metric, max_iters, tol)
     return ids, c, obj
 
 

@@ -132,3 +132,19 @@ def test_batch_kmeans_euclid_matches_fit(fk):
     c2 = ct.clone()
     a, J2, _ = fk.kmeans_fit(xt, c2, 3)
     assert torch.equal(ids, a) and torch.equal(c, c2) and np.array_equal(J, J2)
+
+
+def test_batch_kmeans_euclid_host_inputs(fk):
+    """Host x: pinned (streamed fit) and pageable (staged streamed fit) give the same result, bit for
+    bit (the same chunks), with the centroids returned on the GPU."""
+    w = W.small("batched_f16", B=2, N=3000, K=40)
+    x, x64, c0, xt, ct = make_inputs(w)
+    xp = xt.cpu()
+    ids_p, c_p, J_p = fk.batch_kmeans_euclid(xp.pin_memory(), w.K, max_iters=3, init_centroids=ct.cpu())
+    ids_s, c_s, J_s = fk.batch_kmeans_euclid(xp, w.K, max_iters=3, init_centroids=ct.cpu())
+    assert c_p.is_cuda and c_s.is_cuda
+    assert torch.equal(ids_p, ids_s) and torch.equal(c_p, c_s) and np.array_equal(J_p, J_s)
+    ref = oracle.lloyd_fit(x64, c0, 3, 0.0, dtype=w.dtype, mode="modelled")
+    assert (np.abs(J_s - ref["inertia"]) / ref["inertia"]).max() <= 1e-4
+    with pytest.raises(ValueError, match="Euclidean metric only"):
+        fk.batch_kmeans_cosine(xp, w.K, max_iters=1, init_centroids=ct.cpu())
